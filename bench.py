@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN token mixer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  leg "prefill_long32k": gdn_prefill_chunked on B=1, H=32, T=32768, d=128,
+                         bf16 q/k/v/out, f32 gates and state, chunk 64
+                         (512 sequential chunks per head; final state written)
+  leg "decode_b256":     the hybrid decode step on B=256, H=32, d=128:
+                         gdn_decode_step (in place, on the token leaving the
+                         512-token window) + gdn_swa_sink_decode (4 sinks +
+                         512 window slots, bf16 KV, writes the new token,
+                         adds into the same output); the f32 state comes from
+                         a GPU prefill of the 4096-token context (set-up)
+  leg "conv_qwen32b":    Qwen-32B-shaped layer with projection adaptation:
+                         gdn_short_conv_silu on q, k (with per-head L2 norm)
+                         and v, then gdn_prefill_chunked; B=2, H=40, T=16384
+
+The headline value is the prefill leg's throughput in tokens/s (B*T per call,
+all heads), with the decode leg's tokens/s (B per step) reported beside it.
+Inputs are resident in HBM before timing starts; every leg is timed with HIP
+events on the stream the kernels run on (torch's current stream).  The CPU
+oracle (plain C, f64) is timed on a bounded sample of the same workloads on
+this host's cores as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import gated_delta_rule_115_amd as gdn  # noqa: E402
+import synthetic  # noqa: E402
+
+# MI355X published peaks (dense).
+PEAK_BF16_FLOPS = 2.5e15
+PEAK_HBM_BPS = 8.0e12
+
+# Algorithmic work per unit (fixed definitions; d = Dk = Dv, chunk C = 64):
+#   prefill flops per token-head: dense-tile count of the chunked form
+#     2C(3d + 2d) + 6 d^2 = 180,224 at d = 128
+#   prefill bytes per token-head: bf16 q, k, v + f32 alpha, beta + bf16 out
+#     2(3d) + 8 + 2d = 1,032 at d = 128; plus the f32 final state per head.
+def prefill_flops_per_token_head(d, C=64):
+    return 2 * C * (3 * d + 2 * d) + 6 * d * d
+
+
+def prefill_bytes(B, T, H, d, esize=2):
+    return B * T * H * (esize * 3 * d + 8 + esize * d) + B * H * d * d * 4
+
+
+# Hybrid decode bytes per (b, h): GDN step reads and writes the f32 state,
+# reads bf16 q, k, v and f32 alpha, beta, writes bf16 out; the softmax path
+# streams the bf16 cache slots except the current one, reads and stores the
+# new k, v, reads q, and reads + writes the (bf16) output it adds into.
+def decode_gdn_bytes(d, esize=2):
+    return 8 * d * d + esize * 3 * d + 8 + esize * d
+
+
+def decode_swa_bytes(d, n_slots, esize=2):
+    return esize * (2 * d * (n_slots - 1) + 2 * d + 2 * d + d + 2 * d)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="prefill_long32k,decode_b256,conv_qwen32b")
+    return ap.parse_args()
+
+
+class Leg:
+    def __init__(self, name):
+        self.name = name
+        self.ms = []
+
+    def timed(self, fn, stream):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        return (a, b)
+
+
+def make_prefill_leg():
+    c = synthetic.CONFIGS["long32k"]
+    B, T, H, d = c["B"], c["T"], c["H"], c["Dk"]
+    x = synthetic.gdn_inputs(B, T, H, d, d, dtype="bf16", seed=c["seed"], device="cuda")
+    out = torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda")
+    st = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(B, T, H, d, d, 64), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        gdn.gdn_prefill_chunked(x["q"], x["k"], x["v"], x["alpha"], x["beta"], None,
+                                chunk=64, out=out, state_out=st, workspace=ws)
+
+    info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
+                flops=prefill_flops_per_token_head(d) * B * T * H,
+                bytes=prefill_bytes(B, T, H, d))
+    return run, info, x
+
+
+def make_decode_leg():
+    c = synthetic.CONFIGS["hybrid_decode"]
+    B, H, d, s, w, ctx = c["B"], c["H"], c["Dk"], c["n_sink"], c["window"], c["context"]
+    # f32 state from the GPU prefill of tokens s .. ctx-w-1 (the linear set of
+    # the 4096-token context before this step); set-up, not timed.
+    n_lin = ctx - w - s
+    pre = synthetic.gdn_inputs(B, n_lin, H, d, d, dtype="bf16", seed=c["seed"], device="cuda")
+    st = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    gdn.gdn_prefill_chunked(pre["q"], pre["k"], pre["v"], pre["alpha"], pre["beta"], None,
+                            chunk=64, state_out=st)
+    torch.cuda.synchronize()
+    del pre
+    torch.cuda.empty_cache()
+    tok = synthetic.gdn_inputs(B, 1, H, d, d, dtype="bf16", seed=c["seed"] + 100, device="cuda")
+    q, k, v = (tok[n][:, 0].contiguous() for n in ("q", "k", "v"))
+    a, b = (tok[n][:, 0].contiguous() for n in ("alpha", "beta"))
+    qs, kc, vc = synthetic.swa_inputs(B, H, d, s + w, dtype="bf16", seed=c["seed"] + 200,
+                                      device="cuda")
+    kn, vn = (z[:, :, 0].contiguous() for z in
+              synthetic.swa_inputs(B, H, d, 1, seed=c["seed"] + 300, device="cuda")[1:])
+    nt = torch.full((B,), ctx + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, H, d, dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        gdn.gdn_decode_step(q, k, v, a, b, st, state_out=st, out=out)
+        gdn.gdn_swa_sink_decode(qs, kc, vc, nt, n_sink=s, window=w, k_new=kn, v_new=vn,
+                                accumulate=True, out=out)
+
+    info = dict(B=B, H=H, d=d, tokens=B, n_slots=s + w,
+                bytes=B * H * (decode_gdn_bytes(d) + decode_swa_bytes(d, s + w)),
+                bytes_gdn=B * H * decode_gdn_bytes(d),
+                bytes_swa=B * H * decode_swa_bytes(d, s + w))
+    return run, info, dict(q=q, k=k, v=v, alpha=a, beta=b, state=st)
+
+
+def make_conv_leg():
+    c = synthetic.CONFIGS["qwen32b_conv"]
+    B, T, H, d = c["B"], c["T"], c["H"], c["Dk"]
+    g = synthetic.gdn_inputs(B, T, H, d, d, dtype="bf16", seed=c["seed"], normalise_qk=False,
+                             device="cuda")
+    raw = {n: g[n].reshape(B, T, H * d) for n in ("q", "k", "v")}
+    taps = {n: synthetic.conv_inputs(1, 1, H * d, 4, seed=c["seed"] * 10 + i, device="cuda")[1]
+            for i, n in enumerate(("q", "k", "v"))}
+    conv = {n: torch.empty_like(raw[n]) for n in raw}
+    out = torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda")
+    st = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(B, T, H, d, d, 64), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        for n, grp in (("q", d), ("k", d), ("v", 0)):
+            gdn.gdn_short_conv_silu(raw[n], taps[n], l2norm_group=grp, out=conv[n])
+        gdn.gdn_prefill_chunked(conv["q"].view(B, T, H, d), conv["k"].view(B, T, H, d),
+                                conv["v"].view(B, T, H, d), g["alpha"], g["beta"], None,
+                                chunk=64, out=out, state_out=st, workspace=ws)
+
+    info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
+                conv_bytes=3 * B * T * H * d * 2 * 2,
+                flops=prefill_flops_per_token_head(d) * B * T * H,
+                bytes=prefill_bytes(B, T, H, d))
+    return run, info
+
+
+def cpu_baseline(prefill_x, decode_x):
+    """The oracle as it stands, on a bounded sample of each workload."""
+    import numpy as np
+    import oracle
+
+    f64 = synthetic.to_f64
+    res = {}
+    # Prefill: all 32 heads of the first 8192 tokens of the 32k sequence.
+    Ts = 8192
+    ins = [f64(prefill_x[n][:, :Ts]) for n in ("q", "k", "v", "alpha", "beta")]
+    t0 = time.perf_counter()
+    oracle.gdn_recurrence(*ins)
+    dt = time.perf_counter() - t0
+    res["prefill"] = dict(value=Ts / dt, unit="tokens/s", seconds=dt,
+                          sample=f"all 32 heads x first {Ts} of 32768 tokens (B=1)")
+    # Decode: the GDN step of all 256 x 32 heads.
+    d_ins = [f64(decode_x[n]) for n in ("q", "k", "v", "alpha", "beta", "state")]
+    t0 = time.perf_counter()
+    oracle.decode_step(*d_ins)
+    dt = time.perf_counter() - t0
+    res["decode"] = dict(value=d_ins[0].shape[0] / dt, unit="tokens/s", seconds=dt,
+                         sample="GDN step of all 256 x 32 heads (softmax path not timed)")
+    res["cores"] = oracle.num_threads()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); every "
+              "(batch, head) of this workload is independent, so several GPUs would run "
+              "independent copies of this one-GPU measurement.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    legs_wanted = args.legs.split(",")
+
+    legs = {}
+    infos = {}
+    keep = {}
+    if "prefill_long32k" in legs_wanted:
+        run, info, x = make_prefill_leg()
+        legs["prefill_long32k"], infos["prefill_long32k"], keep["prefill"] = run, info, x
+    if "decode_b256" in legs_wanted:
+        run, info, x = make_decode_leg()
+        legs["decode_b256"], infos["decode_b256"], keep["decode"] = run, info, x
+    if "conv_qwen32b" in legs_wanted:
+        run, info = make_conv_leg()
+        legs["conv_qwen32b"], infos["conv_qwen32b"] = run, info
+    torch.cuda.synchronize()
+
+    def step(record):
+        evs = {}
+        for name, fn in legs.items():
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                evs[name] = (a, b)
+            else:
+                fn()
+        return evs
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    all_evs = [step(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    leg_ms = {n: [e[n][0].elapsed_time(e[n][1]) for e in all_evs] for n in legs}
+
+    out_legs = {}
+    for n, ms in leg_ms.items():
+        inf = infos[n]
+        avg = sum(ms) / len(ms)
+        sec = avg / 1e3
+        rec = dict(ms_avg=avg, ms_min=min(ms), tokens_per_s=inf["tokens"] / sec)
+        if "flops" in inf:
+            rec["tflops"] = inf["flops"] / sec / 1e12
+            rec["mfma_frac"] = inf["flops"] / sec / PEAK_BF16_FLOPS
+            rec["hbm_gbps_algorithmic"] = inf["bytes"] / sec / 1e9
+            rec["hbm_frac"] = inf["bytes"] / sec / PEAK_HBM_BPS
+        else:
+            rec["hbm_gbps_algorithmic"] = inf["bytes"] / sec / 1e9
+            rec["hbm_frac"] = inf["bytes"] / sec / PEAK_HBM_BPS
+        out_legs[n] = rec
+
+    head = out_legs.get("prefill_long32k")
+    value = head["tokens_per_s"] if head else None
+    roofline = None
+    if head:
+        inf = infos["prefill_long32k"]
+        sec = head["ms_avg"] / 1e3
+        roofline = dict(bound="mfma", kernel="gdn_prefill_chunked (chunk_prep + chunk_recur)",
+                        achieved=inf["flops"] / sec / 1e12, peak=PEAK_BF16_FLOPS / 1e12,
+                        unit="TFLOP/s", frac=inf["flops"] / sec / PEAK_BF16_FLOPS,
+                        traffic=None, flops_per_launch=inf["flops"],
+                        flops_per_token_head=prefill_flops_per_token_head(inf["d"]))
+    roof_dec = None
+    if "decode_b256" in out_legs:
+        inf = infos["decode_b256"]
+        sec = out_legs["decode_b256"]["ms_avg"] / 1e3
+        roof_dec = dict(bound="hbm", kernel="gdn_decode_step + gdn_swa_sink_decode",
+                        achieved=inf["bytes"] / sec / 1e9, peak=PEAK_HBM_BPS / 1e9,
+                        unit="GB/s", frac=inf["bytes"] / sec / PEAK_HBM_BPS, traffic=None,
+                        bytes_per_launch=inf["bytes"])
+
+    cpu = None
+    if not args.no_cpu_baseline and "prefill" in keep and "decode" in keep:
+        cb = cpu_baseline(keep["prefill"], keep["decode"])
+        cpu = dict(value=cb["prefill"]["value"], unit="tokens/s", cores=cb["cores"],
+                   kind="oracle", sample=cb["prefill"]["sample"],
+                   seconds=cb["prefill"]["seconds"],
+                   decode=dict(value=cb["decode"]["value"], unit="tokens/s",
+                               sample=cb["decode"]["sample"],
+                               seconds=cb["decode"]["seconds"]))
+
+    step_ms = wall * 1e3 / args.steps
+    line = {
+        "metric": "GDN layer tokens/s (prefill T=32k, decode B=256) + % MFMA / HBM peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded torch.Generator; Llama/Qwen-shaped layers, random init)",
+        "config": {
+            "workload": "long32k prefill (B1 H32 T32768 d128, chunk 64) + hybrid decode "
+                        "(B256 H32 d128, 4 sinks + 512 window) + qwen32b conv+prefill "
+                        "(B2 H40 T16384 d128)",
+            "global_batch": 1, "seq_len": 32768, "parallelism": "single-gpu",
+        },
+        "decode_tokens_per_s": out_legs.get("decode_b256", {}).get("tokens_per_s"),
+        "legs": out_legs,
+        "roofline": roofline,
+        "roofline_decode": roof_dec,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+"""MI355X (gfx950) Gated DeltaNet token mixer: thin Python binding of libgdn.so.
+
+The functions below carry the names of the C entry points declared in
+include/gdn.h and do argument marshalling only: they check device, dtype,
+shape and contiguity of torch tensors, allocate outputs / workspace when the
+caller does not pass them, and call the library on the current HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no
+CPU or PyTorch fallback.  If libgdn.so is missing or fails to load, every
+entry point raises.
+
+Operation ("The Key to Going Linear: Analysis-Driven Transformer
+Linearization", section 3.1.2): per (batch, head), a key-major f32 state
+S in R^{Dk x Dv} is updated per token as
+    S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+and read as out_t = scale * S_t^T q_t.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "GDN_BF16", "GDN_F32", "GdnError", "lib", "library_path",
+    "gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
+    "gdn_decode_step", "gdn_short_conv_silu", "gdn_swa_sink_decode",
+    "EXPORTED_SYMBOLS",
+]
+
+GDN_BF16 = 0
+GDN_F32 = 1
+_STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
+           3: "GDN_ERR_HIP"}
+
+# Every function the C header declares.
+EXPORTED_SYMBOLS = (
+    "gdn_abi_version", "gdn_last_error", "gdn_prefill_workspace_bytes",
+    "gdn_prefill_chunked", "gdn_decode_step", "gdn_short_conv_silu",
+    "gdn_swa_sink_decode",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libgdn.so")
+_lib = None
+
+
+class GdnError(RuntimeError):
+    """A library call returned a non-zero gdn_status."""
+
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so (built by gated_delta_rule_115_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with "
+            "`python -m gated_delta_rule_115_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(library_path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.gdn_abi_version.restype = i
+    L.gdn_last_error.restype = ctypes.c_char_p
+    L.gdn_prefill_workspace_bytes.restype = sz
+    L.gdn_prefill_workspace_bytes.argtypes = [i] * 7
+    L.gdn_prefill_chunked.restype = i
+    L.gdn_prefill_chunked.argtypes = [vp] * 8 + [i] * 8 + [f, vp, sz, vp]
+    L.gdn_decode_step.restype = i
+    L.gdn_decode_step.argtypes = [vp] * 8 + [i] * 6 + [f, vp]
+    L.gdn_short_conv_silu.restype = i
+    L.gdn_short_conv_silu.argtypes = [vp] * 3 + [i] * 5 + [f, i, i, vp]
+    L.gdn_swa_sink_decode.restype = i
+    L.gdn_swa_sink_decode.argtypes = [vp] * 6 + [i] * 5 + [f, i, vp, i, i, vp]
+    _lib = L
+    return L
+
+
+def gdn_abi_version() -> int:
+    return lib().gdn_abi_version()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise GdnError(fn, status, lib().gdn_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _out_dtype(x_dtype, out_dtype):
+    return x_dtype if out_dtype is None else out_dtype
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype=GDN_BF16) -> int:
+    return int(lib().gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype))
+
+
+def gdn_prefill_chunked(q, k, v, alpha, beta, state_in=None, *, chunk=64,
+                        scale=1.0, out=None, out_dtype=None, state_out=None,
+                        workspace=None, want_state=True, stream=None):
+    """Chunk-parallel prefill.  q, k [B,T,H,Dk], v [B,T,H,Dv] (bf16 or f32),
+    alpha, beta [B,T,H] f32, state_in [B,H,Dk,Dv] f32 or None.  out_dtype
+    (default: q's dtype) may be float32 with bf16 inputs.
+    Returns (out [B,T,H,Dv], state_out [B,H,Dk,Dv] or None)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = _dtype_code(q)
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, (B, T, H, Dk))
+    _dev(v, "v", q.dtype, (B, T, H, Dv))
+    _dev(alpha, "alpha", torch.float32, (B, T, H))
+    _dev(beta, "beta", torch.float32, (B, T, H))
+    _dev(state_in, "state_in", torch.float32, (B, H, Dk, Dv))
+    odt = _out_dtype(q.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=odt, device=q.device)
+    _dev(out, "out", odt, (B, T, H, Dv))
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _dev(state_out, "state_out", torch.float32, (B, H, Dk, Dv))
+    need = gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    st = lib().gdn_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
+        _ptr(state_out), _ptr(out), B, T, H, Dk, Dv, chunk, dt, _dtype_code(out),
+        float(scale), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("gdn_prefill_chunked", st)
+    return out, state_out
+
+
+def gdn_decode_step(q, k, v, alpha, beta, state_in, *, state_out=None,
+                    scale=1.0, out=None, out_dtype=None, stream=None):
+    """One token per sequence.  q, k [B,H,Dk], v [B,H,Dv], alpha, beta [B,H],
+    state_in [B,H,Dk,Dv] f32.  state_out=state_in updates in place.
+    Returns (out [B,H,Dv], state_out)."""
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = _dtype_code(q)
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, (B, H, Dk))
+    _dev(v, "v", q.dtype, (B, H, Dv))
+    _dev(alpha, "alpha", torch.float32, (B, H))
+    _dev(beta, "beta", torch.float32, (B, H))
+    _dev(state_in, "state_in", torch.float32, (B, H, Dk, Dv))
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    _dev(state_out, "state_out", torch.float32, (B, H, Dk, Dv))
+    odt = _out_dtype(q.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=odt, device=q.device)
+    _dev(out, "out", odt, (B, H, Dv))
+    st = lib().gdn_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
+        _ptr(state_out), _ptr(out), B, H, Dk, Dv, dt, _dtype_code(out),
+        float(scale), _stream(stream))
+    _check("gdn_decode_step", st)
+    return out, state_out
+
+
+def gdn_short_conv_silu(x, taps, *, l2norm_group=0, eps=1e-6, out=None,
+                        out_dtype=None, stream=None):
+    """Causal depthwise conv + SiLU (+ per-group L2 norm).  x [B,T,Ch],
+    taps [Ch,K] f32 (taps[:, K-1] on the current token).  Returns y [B,T,Ch]."""
+    B, T, Ch = x.shape
+    K = taps.shape[1]
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    _dev(taps, "taps", torch.float32, (Ch, K))
+    odt = _out_dtype(x.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        out = torch.empty((B, T, Ch), dtype=odt, device=x.device)
+    _dev(out, "out", odt, (B, T, Ch))
+    st = lib().gdn_short_conv_silu(_ptr(x), _ptr(taps), _ptr(out), B, T, Ch, K,
+                                   int(l2norm_group), float(eps), dt,
+                                   _dtype_code(out), _stream(stream))
+    _check("gdn_short_conv_silu", st)
+    return out
+
+
+def gdn_swa_sink_decode(q, k_cache, v_cache, n_tokens, *, n_sink, window,
+                        k_new=None, v_new=None, softmax_scale=None,
+                        accumulate=False, out=None, out_dtype=None, stream=None):
+    """Softmax over sinks + sliding window for the current token.
+    q [B,H,D]; k_cache, v_cache [B,H,n_sink+window,D]; n_tokens [B] int32
+    (tokens seen including the current).  k_new/v_new [B,H,D] are written
+    into the current slot first when given.  accumulate=True adds into out."""
+    B, H, D = q.shape
+    dt = _dtype_code(q)
+    nslot = n_sink + window
+    _dev(q, "q")
+    _dev(k_cache, "k_cache", q.dtype, (B, H, nslot, D))
+    _dev(v_cache, "v_cache", q.dtype, (B, H, nslot, D))
+    _dev(n_tokens, "n_tokens", torch.int32, (B,))
+    _dev(k_new, "k_new", q.dtype, (B, H, D))
+    _dev(v_new, "v_new", q.dtype, (B, H, D))
+    odt = _out_dtype(q.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs out")
+        out = torch.empty((B, H, D), dtype=odt, device=q.device)
+    _dev(out, "out", odt, (B, H, D))
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    st = lib().gdn_swa_sink_decode(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(n_tokens), B, H, D, int(n_sink), int(window), float(softmax_scale),
+        int(bool(accumulate)), _ptr(out), dt, _dtype_code(out), _stream(stream))
+    _check("gdn_swa_sink_decode", st)
+    return out

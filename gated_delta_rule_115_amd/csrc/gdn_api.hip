@@ -1,0 +1,228 @@
+// C ABI of the GDN library: host-side argument validation, then launch on the
+// caller's stream.  Nothing here allocates, frees or synchronises.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// dtype of the token inputs and of the output: (bf16, bf16), (bf16, f32) or
+// (f32, f32).
+int check_dtypes(int dtype, int out_dtype) {
+  if (dtype != GDN_BF16 && dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_ARG, "dtype %d is neither GDN_BF16 nor GDN_F32", dtype);
+  if (out_dtype != GDN_BF16 && out_dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_ARG, "out_dtype %d is neither GDN_BF16 nor GDN_F32",
+                out_dtype);
+  if (dtype == GDN_F32 && out_dtype == GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "f32 inputs with a bf16 output are not supported");
+  return GDN_OK;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t esize(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_DTYPES(dt, odt)                 \
+  do {                                          \
+    const int st_ = check_dtypes((dt), (odt));  \
+    if (st_ != GDN_OK) return st_;              \
+  } while (0)
+
+#define REQUIRE_PTR(p)                                                        \
+  do {                                                                        \
+    if ((p) == nullptr) return fail(GDN_ERR_INVALID_ARG, "%s is NULL", #p);   \
+    if (!aligned16(p))                                                        \
+      return fail(GDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p);      \
+  } while (0)
+
+#define REQUIRE_ALIGNED_OR_NULL(p)                                            \
+  do {                                                                        \
+    if ((p) != nullptr && !aligned16(p))                                      \
+      return fail(GDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p);      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv,
+                                   int chunk, int dtype) {
+  if (B < 0 || T < 0 || H < 1 || !is_head_dim(Dk) || !is_head_dim(Dv)) return 0;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
+  if (dtype != GDN_BF16 && dtype != GDN_F32) return 0;
+  return gdn::prefill_workspace_bytes(B, T, H, chunk, dtype == GDN_BF16);
+}
+
+int gdn_prefill_chunked(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        const float* state_in, float* state_out, void* out,
+                        int B, int T, int H, int Dk, int Dv, int chunk,
+                        int dtype, int out_dtype, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG,
+          "bad sizes B=%d T=%d H=%d", B, T, H);
+  REQUIRE(is_head_dim(Dk) && is_head_dim(Dv), GDN_ERR_UNSUPPORTED,
+          "head dims Dk=%d Dv=%d not in {16,32,64,128}", Dk, Dv);
+  REQUIRE(chunk == 16 || chunk == 32 || chunk == 64, GDN_ERR_UNSUPPORTED,
+          "chunk %d not in {16,32,64}", chunk);
+  const long long nc = ((long long)T + chunk - 1) / chunk;
+  REQUIRE((long long)B * H * nc < (1LL << 31) && (long long)B * H * 8 < (1LL << 31),
+          GDN_ERR_UNSUPPORTED, "grid too large");
+  if ((long long)B * H == 0) return ok();
+  REQUIRE_ALIGNED_OR_NULL(state_in);
+  REQUIRE_ALIGNED_OR_NULL(state_out);
+  if (T > 0) {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    REQUIRE(alpha != nullptr && beta != nullptr, GDN_ERR_INVALID_ARG,
+            "alpha/beta is NULL");
+    const size_t need = gdn::prefill_workspace_bytes(B, T, H, chunk, dtype == GDN_BF16);
+    REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
+    REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
+            "workspace is not 256-byte aligned");
+    REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG,
+            "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  }
+  gdn::PrefillArgs p;
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+  p.state_in = state_in; p.state_out = state_out; p.out = out;
+  p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = chunk;
+  p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16;
+  p.scale = scale; p.workspace = workspace; p.stream = stream;
+  return hip_status(gdn::launch_prefill(p), "gdn_prefill_chunked launch");
+}
+
+int gdn_decode_step(const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta,
+                    const float* state_in, float* state_out, void* out, int B,
+                    int H, int Dk, int Dv, int dtype, int out_dtype,
+                    float scale, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d H=%d", B, H);
+  REQUIRE(is_head_dim(Dk) && is_head_dim(Dv), GDN_ERR_UNSUPPORTED,
+          "head dims Dk=%d Dv=%d not in {16,32,64,128}", Dk, Dv);
+  REQUIRE((long long)B * H < (1LL << 31), GDN_ERR_UNSUPPORTED, "grid too large");
+  if (B == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(state_in);
+  REQUIRE_PTR(state_out);
+  REQUIRE(alpha != nullptr && beta != nullptr, GDN_ERR_INVALID_ARG,
+          "alpha/beta is NULL");
+  gdn::DecodeArgs p;
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+  p.state_in = state_in; p.state_out = state_out; p.out = out;
+  p.B = B; p.H = H; p.Dk = Dk; p.Dv = Dv;
+  p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16;
+  p.scale = scale; p.stream = stream;
+  return hip_status(gdn::launch_decode(p), "gdn_decode_step launch");
+}
+
+int gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
+                        int T, int Ch, int K, int l2norm_group, float eps,
+                        int dtype, int out_dtype, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && T >= 0 && Ch >= 1, GDN_ERR_INVALID_ARG,
+          "bad sizes B=%d T=%d Ch=%d", B, T, Ch);
+  REQUIRE(K >= 1 && K <= 8, GDN_ERR_UNSUPPORTED, "kernel size %d not in 1..8", K);
+  REQUIRE(Ch % 8 == 0, GDN_ERR_UNSUPPORTED, "Ch=%d is not a multiple of 8", Ch);
+  const int g = l2norm_group;
+  REQUIRE(g == 0 || (g >= 8 && g <= 512 && (g & (g - 1)) == 0 && Ch % g == 0),
+          GDN_ERR_UNSUPPORTED,
+          "l2norm_group %d must be 0 or a power of two in 8..512 dividing Ch", g);
+  REQUIRE(B <= 65535 && ((long long)T + 63) / 64 <= 65535, GDN_ERR_UNSUPPORTED,
+          "grid too large (B <= 65535, T <= 4194240)");
+  if ((long long)B * T == 0) return ok();
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(y);
+  REQUIRE(taps != nullptr, GDN_ERR_INVALID_ARG, "taps is NULL");
+  const size_t xbytes = (size_t)B * T * Ch * esize(dtype);
+  const size_t ybytes = (size_t)B * T * Ch * esize(out_dtype);
+  const char* xa = (const char*)x;
+  const char* ya = (const char*)y;
+  REQUIRE(ya + ybytes <= xa || xa + xbytes <= ya, GDN_ERR_INVALID_ARG,
+          "y overlaps x");
+  gdn::ConvArgs p;
+  p.x = x; p.taps = taps; p.y = y;
+  p.B = B; p.T = T; p.Ch = Ch; p.K = K; p.group = g; p.eps = eps;
+  p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16; p.stream = stream;
+  return hip_status(gdn::launch_conv(p), "gdn_short_conv_silu launch");
+}
+
+int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
+                        void* k_cache, void* v_cache, const int* n_tokens,
+                        int B, int H, int D, int n_sink, int window,
+                        float softmax_scale, int accumulate, void* out,
+                        int dtype, int out_dtype, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d H=%d", B, H);
+  REQUIRE(D == 64 || D == 128, GDN_ERR_UNSUPPORTED, "head dim %d not in {64,128}", D);
+  REQUIRE(n_sink >= 0 && window >= 1, GDN_ERR_INVALID_ARG,
+          "bad cache shape n_sink=%d window=%d", n_sink, window);
+  REQUIRE((long long)n_sink + window < (1LL << 24), GDN_ERR_UNSUPPORTED,
+          "cache too long");
+  REQUIRE(accumulate == 0 || accumulate == 1, GDN_ERR_INVALID_ARG,
+          "accumulate must be 0 or 1");
+  REQUIRE((k_new == nullptr) == (v_new == nullptr), GDN_ERR_INVALID_ARG,
+          "k_new and v_new must both be given or both be NULL");
+  REQUIRE((long long)B * H < (1LL << 31), GDN_ERR_UNSUPPORTED, "grid too large");
+  if (B == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(out);
+  REQUIRE_ALIGNED_OR_NULL(k_new);
+  REQUIRE_ALIGNED_OR_NULL(v_new);
+  REQUIRE(n_tokens != nullptr, GDN_ERR_INVALID_ARG, "n_tokens is NULL");
+  gdn::SwaArgs p;
+  p.q = q; p.k_new = k_new; p.v_new = v_new; p.k_cache = k_cache; p.v_cache = v_cache;
+  p.n_tokens = n_tokens; p.B = B; p.H = H; p.D = D; p.n_sink = n_sink;
+  p.window = window; p.softmax_scale = softmax_scale; p.accumulate = accumulate;
+  p.out = out; p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16;
+  p.stream = stream;
+  return hip_status(gdn::launch_swa(p), "gdn_swa_sink_decode launch");
+}
+
+}  // extern "C"

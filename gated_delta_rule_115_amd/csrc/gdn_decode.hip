@@ -1,0 +1,152 @@
+// Single-token GDN decode step for a batch of sequences, gfx950.
+//
+// "The Key to Going Linear: Analysis-Driven Transformer Linearization",
+// section 3.1.2 (recurrent form), one token per (b, h):
+//   S' = alpha (I - beta k k^T) S + beta k v^T,   out = scale * S'^T q.
+// Rewritten so the state is touched in ONE pass (read once, written once):
+//   u   = beta (v - alpha S^T k)                 [Dv]
+//   out = scale (alpha S^T q + (k . q) u)        [Dv]
+//   S'  = alpha S + k u^T
+// (expand S' and substitute; it is the same update exactly).
+//
+// The step is HBM-bound: 8*Dk*Dv bytes of f32 state per (b, h) against
+// ~4*Dk*Dv flops.  One work-group of 256 threads owns one (b, h); thread
+// (rg, cg) holds rows rg, rg+RG, ... and the float4 column group cg of S in
+// registers, so every state load/store is a 16-byte coalesced access and all
+// of a thread's loads are in flight before the first reduction.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+template <class TIn, class TOut, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k,
+    const TIn* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const float* state_in, float* state_out,
+    TOut* __restrict__ out, float scale) {
+  constexpr int NT = 256;
+  constexpr int CG = DV / 4;            // float4 column groups
+  constexpr int RG = NT / CG;           // row groups
+  constexpr int RPT = (DK + RG - 1) / RG;  // rows per thread
+  static_assert(NT % CG == 0, "DV/4 must divide 256");
+
+  __shared__ float ks[DK], qs[DK], vs[DV];
+  __shared__ float red_k[RG][DV + 4], red_q[RG][DV + 4];
+  __shared__ float red_kq[RG];
+  __shared__ float us[DV];
+
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG, rg = tid / CG;
+  const size_t sbase = (size_t)bh * DK * DV;
+
+  // State rows of this thread, all loads issued up front.
+  f32x4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + i * RG;
+    if (r < DK)
+      s[i] = *reinterpret_cast<const f32x4*>(state_in + sbase + (size_t)r * DV + cg * 4);
+    else
+      s[i] = zero4();
+  }
+
+  for (int i = tid; i < DK; i += NT) {
+    ks[i] = to_f32(k[(size_t)bh * DK + i]);
+    qs[i] = to_f32(q[(size_t)bh * DK + i]);
+  }
+  for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
+  const float a = alpha[bh];
+  const float b = beta[bh];
+  __syncthreads();
+
+  // Partial S^T k and S^T q over this thread's rows; k.q from column group 0.
+  float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+  float pkq = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + i * RG;
+    if (r < DK) {
+      const float kr = ks[r], qr = qs[r];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pk[c] += s[i][c] * kr;
+        pq[c] += s[i][c] * qr;
+      }
+      if (cg == 0) pkq += kr * qr;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    red_k[rg][cg * 4 + c] = pk[c];
+    red_q[rg][cg * 4 + c] = pq[c];
+  }
+  if (cg == 0) red_kq[rg] = pkq;
+  __syncthreads();
+
+  if (tid < DV) {
+    float sk = 0.f, sq = 0.f, kq = 0.f;
+    for (int g = 0; g < RG; ++g) {
+      sk += red_k[g][tid];
+      sq += red_q[g][tid];
+      kq += red_kq[g];
+    }
+    const float u = b * (vs[tid] - a * sk);
+    us[tid] = u;
+    out[(size_t)bh * DV + tid] = from_f32<TOut>(scale * (a * sq + kq * u));
+  }
+  __syncthreads();
+
+  const f32x4 u4 = *reinterpret_cast<const f32x4*>(&us[cg * 4]);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + i * RG;
+    if (r < DK) {
+      const float kr = ks[r];
+      f32x4 o;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = a * s[i][c] + kr * u4[c];
+      *reinterpret_cast<f32x4*>(state_out + sbase + (size_t)r * DV + cg * 4) = o;
+    }
+  }
+}
+
+template <class TIn, class TOut, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs& p) {
+  hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV>), dim3(p.B * p.H), dim3(256),
+                     0, (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k,
+                     (const TIn*)p.v, p.alpha, p.beta, p.state_in, p.state_out,
+                     (TOut*)p.out, p.scale);
+  return hipGetLastError();
+}
+
+template <class TIn, class TOut, int DK>
+static hipError_t launch_decode_dv(const DecodeArgs& p) {
+  switch (p.Dv) {
+    case 16: return launch_decode_t<TIn, TOut, DK, 16>(p);
+    case 32: return launch_decode_t<TIn, TOut, DK, 32>(p);
+    case 64: return launch_decode_t<TIn, TOut, DK, 64>(p);
+    case 128: return launch_decode_t<TIn, TOut, DK, 128>(p);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class TIn, class TOut>
+static hipError_t launch_decode_dk(const DecodeArgs& p) {
+  switch (p.Dk) {
+    case 16: return launch_decode_dv<TIn, TOut, 16>(p);
+    case 32: return launch_decode_dv<TIn, TOut, 32>(p);
+    case 64: return launch_decode_dv<TIn, TOut, 64>(p);
+    case 128: return launch_decode_dv<TIn, TOut, 128>(p);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& p) {
+  if (p.B * p.H == 0) return hipSuccess;
+  if (!p.bf16) return launch_decode_dk<float, float>(p);
+  return p.out_bf16 ? launch_decode_dk<bf16, bf16>(p) : launch_decode_dk<bf16, float>(p);
+}
+
+}  // namespace gdn

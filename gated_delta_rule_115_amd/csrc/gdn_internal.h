@@ -1,0 +1,71 @@
+// Host-side launch interfaces between the C ABI (gdn_api.hip) and the kernel
+// files.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gdn {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  const float* state_in;
+  float* state_out;
+  void* out;
+  int B, H, Dk, Dv;
+  bool bf16, out_bf16;
+  float scale;
+  void* stream;
+};
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  const float* state_in;
+  float* state_out;
+  void* out;
+  int B, T, H, Dk, Dv, chunk;
+  bool bf16, out_bf16;
+  float scale;
+  void* workspace;
+  void* stream;
+};
+
+struct ConvArgs {
+  const void* x;
+  const float* taps;
+  void* y;
+  int B, T, Ch, K, group;
+  float eps;
+  bool bf16, out_bf16;
+  void* stream;
+};
+
+struct SwaArgs {
+  const void* q;
+  const void *k_new, *v_new;
+  void *k_cache, *v_cache;
+  const int* n_tokens;
+  int B, H, D, n_sink, window;
+  float softmax_scale;
+  int accumulate;
+  void* out;
+  bool bf16, out_bf16;
+  void* stream;
+};
+
+// Per-chunk workspace layout of the prefill (one record per (b, h, chunk)):
+//   Tm    [C][C]  operand type: (I + A)^-1 of the chunk (unit lower)
+//   Pm    [C][C]  operand type: scale * exp(g_r - g_i) q_r.k_i for i <= r, else 0
+//   gam   [C]     f32: cumulative log gate within the chunk
+// Records are padded to 256 bytes.
+size_t prefill_record_bytes(int chunk, bool bf16);
+size_t prefill_workspace_bytes(int B, int T, int H, int chunk, bool bf16);
+
+hipError_t launch_decode(const DecodeArgs& p);
+hipError_t launch_prefill(const PrefillArgs& p);
+hipError_t launch_conv(const ConvArgs& p);
+hipError_t launch_swa(const SwaArgs& p);
+
+}  // namespace gdn

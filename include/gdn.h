@@ -1,0 +1,158 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet token-mixer library.
+ *
+ * The operation is the GDN layer of "The Key to Going Linear: Analysis-Driven
+ * Transformer Linearization" (Kuzina, Whatmough, Ehteshami Bejnordi):
+ *   section 3.1.2:  S_t = (I - beta_t k_t k_t^T) G_t S_{t-1} + beta_t k_t v_t^T,
+ *                   y_t = q_t^T S_t,
+ * with a scalar gate G_t = alpha_t I per (token, head), a key-major fp32 state
+ * S in R^{Dk x Dv}, and the read-out taken after token t is written:
+ *   out_t = scale * S_t^T q_t.
+ * Section 4 adds a disjoint softmax path over sink tokens and a sliding window
+ * ("Adding Sliding Window Attention") and causal short convolutions on q, k, v
+ * ("Adapting Q/K/V").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronises; every call is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and returns immediately.
+ *   - Tensors are dense row-major.  Token tensors are [B, T, H, D] (the
+ *     natural output of a [B, T, H*D] projection); states are [B, H, Dk, Dv]
+ *     float32; gates alpha/beta are [B, T, H] float32.
+ *   - `dtype` (gdn_dtype) is the element type of the token inputs (q, k, v,
+ *     x, KV caches): GDN_BF16 (bfloat16) or GDN_F32.  `out_dtype` is the
+ *     element type of `out` / `y`: the input dtype, or GDN_F32 with bf16
+ *     inputs (f32 results of bf16 inputs; a bf16 output is exactly that f32
+ *     result rounded once to nearest-even).  Gates, states and taps are
+ *     always f32.  In bf16 mode all arithmetic accumulates in f32 and the
+ *     matrix products take bf16 operands; in f32 mode every product is f32.
+ *   - Token/state pointers must be 16-byte aligned.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     failed check returns GDN_ERR_INVALID_ARG or GDN_ERR_UNSUPPORTED and
+ *     enqueues nothing; a launch failure returns GDN_ERR_HIP.  The message of
+ *     the last failure on the calling thread is gdn_last_error().  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - Data-dependent preconditions are documented, not checked: alpha in
+ *     (0, 1], beta in [0, 1], q and k of moderate norm (the workloads
+ *     L2-normalise them per token).
+ *   - Calls are thread-safe; there is no mutable global state besides the
+ *     per-thread error message.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misalignment, too small */
+  GDN_ERR_UNSUPPORTED = 2, /* valid request outside the supported shapes     */
+  GDN_ERR_HIP = 3          /* a HIP runtime call failed                       */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* ABI version of this header (incremented on any signature change). */
+#define GDN_ABI_VERSION 1
+int gdn_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+/*
+ * Workspace (bytes) that gdn_prefill_chunked needs for these sizes; 0 if the
+ * sizes are invalid.  The workspace holds, per chunk of `chunk` tokens, the
+ * chunk's triangular-solve matrix, its decay-masked query-key products and
+ * its cumulative log gates.
+ */
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv,
+                                   int chunk, int dtype);
+
+/*
+ * Chunk-parallel GDN prefill (section 3.1.2 recurrence, computed exactly up
+ * to rounding by a chunked WY/UT rewrite).  Equivalent to running the
+ * recurrence token by token over t = 0..T-1 for every (b, h):
+ *   q, k      [B, T, H, Dk]  dtype      alpha, beta [B, T, H]  f32
+ *   v         [B, T, H, Dv]  dtype      out         [B, T, H, Dv] out_dtype
+ *   state_in  [B, H, Dk, Dv] f32, or NULL for a zero initial state
+ *   state_out [B, H, Dk, Dv] f32, or NULL; may alias state_in (resume)
+ *   scale     multiplies every read-out (1.0 for the page's y_t = q_t^T S_t)
+ *   chunk     16, 32 or 64 tokens per chunk (a tuning choice: the result is
+ *             the same recurrence for any chunk, up to rounding)
+ *   workspace device scratch of at least gdn_prefill_workspace_bytes(...)
+ * Limits: B >= 0, T >= 0, H >= 1, Dk and Dv in {16, 32, 64, 128}.  T = 0
+ * copies state_in (or zeros) to state_out.  alpha must be > 0 (the kernels
+ * work with log alpha).
+ */
+int gdn_prefill_chunked(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        const float* state_in, float* state_out, void* out,
+                        int B, int T, int H, int Dk, int Dv, int chunk,
+                        int dtype, int out_dtype, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrence step for a batch of sequences (section 3.1.2 at a single
+ * token; the recurrent form used for generation):
+ *   q, k [B, H, Dk] dtype;  v [B, H, Dv] dtype;  alpha, beta [B, H] f32
+ *   state_in, state_out [B, H, Dk, Dv] f32 (may alias: in-place update)
+ *   out [B, H, Dv] out_dtype:   out = scale * S'^T q
+ * Each state is read once and written once.  Limits as for the prefill.
+ */
+int gdn_decode_step(const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta,
+                    const float* state_in, float* state_out, void* out, int B,
+                    int H, int Dk, int Dv, int dtype, int out_dtype,
+                    float scale, void* stream);
+
+/*
+ * Causal depthwise short convolution + SiLU on one projection output
+ * (section 4, "Adapting Q/K/V"), optionally followed by an L2 normalisation
+ * of every group of `l2norm_group` consecutive channels (one head), as the
+ * key normalisation k / (||k||_2 + eps) of appendix B.1:
+ *   x [B, T, Ch] dtype, y [B, T, Ch] out_dtype;  taps [Ch, K] f32,
+ *   taps[c][K-1] multiplies x_t
+ *   y_t[c] = SiLU(sum_j taps[c][j] * x_{t-K+1+j}[c]),  x_{<0} = 0
+ * Limits: K in 1..8; Ch a multiple of 8; l2norm_group 0 (off) or a power of
+ * two in 8..512 dividing Ch.  y must not overlap x.
+ */
+int gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
+                        int T, int Ch, int K, int l2norm_group, float eps,
+                        int dtype, int out_dtype, void* stream);
+
+/*
+ * Softmax decode step over sink tokens and a sliding window (section 4,
+ * "Adding Sliding Window Attention": I = sinks + window, logits scaled by
+ * softmax_scale, normally 1/sqrt(D)).
+ *   q        [B, H, D] dtype: the current token's softmax-path query
+ *   k_cache, v_cache [B, H, n_sink + window, D] dtype.  Slot i < n_sink holds
+ *            the token at 0-based position i; the token at position p >=
+ *            n_sink lives in slot n_sink + (p - n_sink) % window.
+ *   n_tokens [B] int32 (device): tokens seen including the current one, so
+ *            the current token is at position n_tokens[b] - 1 (>= 0 required,
+ *            n_tokens[b] >= 1).  The attended set is positions
+ *            {0..min(n_sink, t)-1} and {max(n_sink, t-window)..t-1}, t =
+ *            n_tokens[b]; each position at most once.
+ *   k_new, v_new [B, H, D] dtype or both NULL: when given, the current
+ *            token's key/value are first stored into its cache slot (this
+ *            overwrites the token leaving the window) and attended from there.
+ *   accumulate 0: out = y_swa; 1: out += y_swa (adds to the linear path's
+ *            read-out written earlier on the same stream).
+ *   out      [B, H, D] out_dtype.
+ * Limits: D in {64, 128}; n_sink >= 0; window >= 1.
+ */
+int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
+                        void* k_cache, void* v_cache, const int* n_tokens,
+                        int B, int H, int D, int n_sink, int window,
+                        float softmax_scale, int accumulate, void* out,
+                        int dtype, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,136 @@
+"""C-ABI contract on the CPU: the library loads, exports every function that
+include/gdn.h declares, and rejects bad arguments on the host with the
+documented status codes before anything touches a GPU.  No call here passes
+validation with real work, so no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_115_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+BF16, F32 = 0, 1
+A = 4096  # a 16-byte-aligned fake address (never dereferenced: validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 7
+    L = gdn.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(gdn.EXPORTED_SYMBOLS)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define\s+GDN_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert gdn.gdn_abi_version() == int(m.group(1))
+
+
+def _prefill(**kw):
+    a = dict(q=A, k=A, v=A, alpha=A, beta=A, s_in=None, s_out=None, out=A, B=1, T=64,
+             H=2, Dk=128, Dv=128, chunk=64, dt=BF16, odt=BF16, scale=1.0, ws=A,
+             wsb=1 << 40)
+    a.update(kw)
+    return gdn.lib().gdn_prefill_chunked(
+        a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s_in"], a["s_out"], a["out"],
+        a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["chunk"], a["dt"], a["odt"],
+        a["scale"], a["ws"], a["wsb"], None)
+
+
+def _err():
+    return gdn.lib().gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(Dk=100), UNSUPPORTED, "head dims"),
+    (dict(Dv=256), UNSUPPORTED, "head dims"),
+    (dict(chunk=48), UNSUPPORTED, "chunk"),
+    (dict(dt=7), INVALID, "dtype"),
+    (dict(odt=5), INVALID, "out_dtype"),
+    (dict(dt=F32, odt=BF16), UNSUPPORTED, "bf16 output"),
+    (dict(B=-1), INVALID, "bad sizes"),
+    (dict(H=0), INVALID, "bad sizes"),
+    (dict(q=None), INVALID, "q is NULL"),
+    (dict(out=None), INVALID, "out is NULL"),
+    (dict(k=A + 2), INVALID, "aligned"),
+    (dict(s_in=A + 4), INVALID, "aligned"),
+    (dict(alpha=None), INVALID, "alpha"),
+    (dict(ws=None), INVALID, "workspace is NULL"),
+    (dict(ws=A + 16), INVALID, "256-byte"),
+    (dict(wsb=100), INVALID, "too small"),
+])
+def test_prefill_validation(kw, code, msg):
+    assert _prefill(**kw) == code
+    assert msg in _err()
+
+
+def test_prefill_empty_batch_is_ok_without_gpu():
+    assert _prefill(B=0, q=None, k=None, v=None, out=None, ws=None) == OK
+    assert _err() == ""
+
+
+def test_workspace_bytes():
+    f = gdn.gdn_prefill_workspace_bytes
+    # per chunk: two C x C operand matrices + C f32 log gates, padded to 256 B
+    assert f(1, 64, 1, 128, 128, 64, BF16) == 2 * 64 * 64 * 2 + 256
+    assert f(2, 65, 3, 128, 128, 64, BF16) == 2 * 3 * 2 * (2 * 64 * 64 * 2 + 256)
+    assert f(1, 16, 1, 16, 16, 16, F32) == 2304
+    assert f(1, 16, 1, 100, 16, 16, F32) == 0
+
+
+def test_decode_validation():
+    L = gdn.lib()
+    call = lambda **kw: L.gdn_decode_step(
+        kw.get("q", A), A, A, A, A, kw.get("s", A), A, A, kw.get("B", 2), 2,
+        kw.get("Dk", 64), 64, kw.get("dt", BF16), kw.get("odt", BF16), 1.0, None)
+    assert call(Dk=48) == UNSUPPORTED
+    assert call(q=None) == INVALID and "q is NULL" in _err()
+    assert call(s=A + 8) == INVALID and "aligned" in _err()
+    assert call(dt=F32, odt=BF16) == UNSUPPORTED
+    assert call(B=0, q=None) == OK
+
+
+def test_conv_validation():
+    L = gdn.lib()
+    call = lambda **kw: L.gdn_short_conv_silu(
+        kw.get("x", A), A, kw.get("y", A + (1 << 30)), 1, kw.get("T", 10),
+        kw.get("Ch", 256), kw.get("K", 4), kw.get("g", 0), 1e-6, BF16, BF16, None)
+    assert call(K=9) == UNSUPPORTED
+    assert call(Ch=12) == UNSUPPORTED
+    assert call(g=24) == UNSUPPORTED
+    assert call(g=512, Ch=256) == UNSUPPORTED
+    assert call(y=A + 16) == INVALID and "overlaps" in _err()
+    assert call(x=None) == INVALID
+    assert call(T=0, x=None) == OK
+
+
+def test_swa_validation():
+    L = gdn.lib()
+    call = lambda **kw: L.gdn_swa_sink_decode(
+        A, kw.get("kn", None), kw.get("vn", None), A, A, kw.get("nt", A), 2, 2,
+        kw.get("D", 128), kw.get("s", 4), kw.get("w", 8), 0.1, kw.get("acc", 0), A,
+        BF16, BF16, None)
+    assert call(D=96) == UNSUPPORTED
+    assert call(w=0) == INVALID
+    assert call(s=-1) == INVALID
+    assert call(kn=A) == INVALID and "both" in _err()
+    assert call(acc=2) == INVALID
+    assert call(nt=None) == INVALID
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "library_path", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        gdn.lib()

@@ -1,0 +1,97 @@
+"""GPU parity: gdn_short_conv_silu against the oracle's direct loop
+("The Key to Going Linear: Analysis-Driven Transformer Linearization",
+section 4 "Adapting Q/K/V"; key normalisation of appendix B.1), and the
+conv -> prefill chain of the Qwen-32B-shaped layer against oracle conv ->
+oracle recurrence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_115_amd as gdn
+import oracle
+import synthetic
+from common import TOL, assert_bf16_is_rounded_f32, dev, err, f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,B,T,Ch,K,group", [
+    ("f32", 2, 100, 256, 4, 0), ("f32", 2, 100, 256, 4, 64),
+    ("f32", 1, 3, 64, 4, 32),          # T < K
+    ("f32", 1, 130, 128, 1, 128), ("f32", 1, 70, 96, 8, 32),
+    ("bf16", 2, 129, 512, 4, 128), ("bf16", 1, 64, 1024, 3, 0),
+])
+def test_conv_matches_oracle(dtype, B, T, Ch, K, group):
+    say(f"conv {dtype} B={B} T={T} Ch={Ch} K={K} group={group}")
+    x, taps = synthetic.conv_inputs(B, T, Ch, K, dtype=dtype, seed=T + Ch + K)
+    y = gdn.gdn_short_conv_silu(dev(x), dev(taps), l2norm_group=group, eps=1e-6,
+                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.short_conv_silu(f64(x), f64(taps), l2norm_group=group, eps=1e-6)
+    assert err(y, ref) <= TOL[dtype]
+    if dtype == "bf16":
+        yb = gdn.gdn_short_conv_silu(dev(x), dev(taps), l2norm_group=group, eps=1e-6)
+        torch.cuda.synchronize()
+        assert_bf16_is_rounded_f32(yb, y)
+
+
+def test_conv_full_qwen32b_projection():
+    """Full-size q projection of the Qwen-32B-shaped layer: B=2 T=16384 40x128."""
+    B, T, H, D = 2, 16384, 40, 128
+    x, taps = synthetic.conv_inputs(B, T, H * D, 4, dtype="bf16", seed=4, device="cuda")
+    y = gdn.gdn_short_conv_silu(x, taps, l2norm_group=D, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.short_conv_silu(f64(x), f64(taps), l2norm_group=D, eps=1e-6)
+    e = err(y, ref)
+    say(f"  full conv err {e:.3e}")
+    assert e <= TOL["bf16"]
+
+
+def test_conv_then_prefill_qwen32b_sampled():
+    """Qwen-32B-shaped layer with projection adaptation: conv -> SiLU -> L2 on
+    q, k (conv -> SiLU on v) then the GDN prefill; sampled heads checked
+    against oracle conv -> oracle recurrence on the same raw inputs.
+
+    The prefill consumes bf16 q, k, v, so the layer stores the conv outputs
+    in bf16 between the two calls.  The oracle chain applies that same
+    storage rounding (its own f64 conv output rounded to bf16) at the same
+    boundary: without it, the bf16 storage alone moves the f64 recurrence's
+    output by ~3e-2 of its RMS, more than the kernels' own error budget."""
+    c = synthetic.CONFIGS["qwen32b_conv"]
+    B, T, H, D = c["B"], c["T"], c["H"], c["Dk"]
+    say(f"qwen32b conv+prefill B={B} T={T} H={H}")
+    g = synthetic.gdn_inputs(B, T, H, D, D, dtype="bf16", seed=c["seed"],
+                             normalise_qk=False, device="cuda")
+    raw = {n: g[n].reshape(B, T, H * D) for n in ("q", "k", "v")}
+    taps = {n: synthetic.conv_inputs(1, 1, H * D, 4, seed=c["seed"] * 10 + i,
+                                     device="cuda")[1]
+            for i, n in enumerate(("q", "k", "v"))}
+    qc = gdn.gdn_short_conv_silu(raw["q"], taps["q"], l2norm_group=D)
+    kc = gdn.gdn_short_conv_silu(raw["k"], taps["k"], l2norm_group=D)
+    vc = gdn.gdn_short_conv_silu(raw["v"], taps["v"], l2norm_group=0)
+    o, s = gdn.gdn_prefill_chunked(qc.view(B, T, H, D), kc.view(B, T, H, D),
+                                   vc.view(B, T, H, D), g["alpha"], g["beta"], None,
+                                   chunk=c["chunk"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    picks = rng.choice(B * H, size=6, replace=False)
+    refs_o, refs_s, got_o, got_s = [], [], [], []
+    for p in picks:
+        b, h = int(p // H), int(p % H)
+        sl = slice(h * D, (h + 1) * D)
+        conv = {}
+        for n, grp in (("q", D), ("k", D), ("v", 0)):
+            c64 = oracle.short_conv_silu(f64(raw[n][b:b + 1, :, sl]),
+                                         f64(taps[n][sl]), l2norm_group=grp)
+            conv[n] = torch.from_numpy(c64).to(torch.bfloat16).double().numpy()
+        ro, rs = oracle.gdn_recurrence(conv["q"][:, :, None], conv["k"][:, :, None],
+                                       conv["v"][:, :, None],
+                                       f64(g["alpha"][b:b + 1, :, h:h + 1]),
+                                       f64(g["beta"][b:b + 1, :, h:h + 1]))
+        refs_o.append(ro[0, :, 0]); refs_s.append(rs[0, 0])
+        got_o.append(f64(o[b, :, h])); got_s.append(f64(s[b, h]))
+    eo = oracle.rms_normalised_max_error(np.stack(got_o), np.stack(refs_o))
+    es = oracle.rms_normalised_max_error(np.stack(got_s), np.stack(refs_s))
+    say(f"  sampled heads: out err {eo:.3e} state err {es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]

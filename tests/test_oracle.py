@@ -348,3 +348,12 @@ def test_error_statistics():
     assert abs(oracle.rms_normalised_max_error(got, ref) - 0.1) < 1e-15
     # appendix B.1: nMSE = MSE / Var(ref)
     assert abs(oracle.nmse(got, ref) - (0.01 / 4) / 1.0) < 1e-15
+
+
+# The decode-step form of the softmax path is the last row of the full one.
+def test_swa_last_only_matches_full():
+    B, T, H, D = 2, 11, 2, 4
+    q, k, v = (RNG.standard_normal((B, T, H, D)) for _ in range(3))
+    full = oracle.swa_sink_attention(q, k, v, 2, 3, 0.5)
+    last = oracle.swa_sink_attention(q, k, v, 2, 3, 0.5, last_only=True)
+    assert np.array_equal(last, full[:, -1])
