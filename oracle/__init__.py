@@ -56,7 +56,7 @@ def _load():
         d = ctypes.c_double
         lib.gdn_oracle_recurrence_f64.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
         lib.gdn_oracle_recurrence_f32.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
-        lib.gdn_oracle_swa_sink_f64.argtypes = [_dp] * 4 + [i] * 6 + [d]
+        lib.gdn_oracle_swa_sink_f64.argtypes = [_dp] * 4 + [i] * 6 + [d, i]
         lib.gdn_oracle_hybrid_f64.argtypes = [_dp] * 9 + [i] * 7 + [d, d]
         lib.gdn_oracle_short_conv_silu_f64.argtypes = [_dp] * 3 + [i] * 5 + [d]
         lib.gdn_oracle_num_threads.restype = i
@@ -114,18 +114,21 @@ def decode_step(q, k, v, alpha, beta, state_in, scale=1.0):
     return out[:, 0], s
 
 
-def swa_sink_attention(q, k, v, n_sink, window, softmax_scale):
+def swa_sink_attention(q, k, v, n_sink, window, softmax_scale, last_only=False):
     """Softmax over sinks {0..s-1} and window {t-w+1..t} at every t.
 
-    q, k, v [B,T,H,D] -> [B,T,H,D].  section 3.1 softmax on section 4's set I.
+    q, k, v [B,T,H,D] -> [B,T,H,D] (section 3.1 softmax on section 4's set I).
+    last_only=True computes only position T-1 (a decode step) and returns
+    [B,H,D].
     """
     q, k, v = map(_arr, (q, k, v))
     B, T, H, D = q.shape
     out = np.zeros((B, T, H, D))
+    t_begin = T - 1 if last_only else 0
     _load().gdn_oracle_swa_sink_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                     B, T, H, D, int(n_sink), int(window),
-                                    float(softmax_scale))
-    return out
+                                    float(softmax_scale), int(t_begin))
+    return out[:, -1] if last_only else out
 
 
 def hybrid(ql, kl, vl, alpha, beta, qs, ks, vs, n_sink, window,

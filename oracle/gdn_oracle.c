@@ -136,18 +136,21 @@ static int in_exact_set(long i, long t, long s, long w) {
 }
 
 /* ------------------------------------------------------------------------- */
-/* Sink + sliding-window softmax attention, every position of a sequence      */
-/* (section 3.1 softmax restricted to the set I of section 4).                */
+/* Sink + sliding-window softmax attention at positions t_begin..T-1 of a     */
+/* sequence (section 3.1 softmax restricted to the set I of section 4).       */
 /* q, k, v, out: [B, T, H, D].  logits = softmax_scale * q_t . k_i.           */
+/* Rows of out before t_begin are left untouched.                            */
 /* ------------------------------------------------------------------------- */
 void gdn_oracle_swa_sink_f64(const double* q, const double* k, const double* v,
                              double* out, int B, int T, int H, int D,
-                             int n_sink, int window, double softmax_scale) {
-  long BHT = (long)B * H * T;
+                             int n_sink, int window, double softmax_scale,
+                             int t_begin) {
+  long NT = (long)T - t_begin;
+  long BHT = (long)B * H * NT;
 #pragma omp parallel for schedule(dynamic, 16)
   for (long idx = 0; idx < BHT; ++idx) {
-    long b = idx / ((long)H * T), rem = idx % ((long)H * T);
-    long h = rem / T, t = rem % T;
+    long b = idx / ((long)H * NT), rem = idx % ((long)H * NT);
+    long h = rem / NT, t = t_begin + rem % NT;
     const double* qt = q + ((b * T + t) * H + h) * D;
     double* ot = out + ((b * T + t) * H + h) * D;
     double zmax = -INFINITY;
@@ -193,7 +196,7 @@ void gdn_oracle_hybrid_f64(const double* ql, const double* kl, const double* vl,
   long BH = (long)B * H;
   double* swa = (double*)malloc(sizeof(double) * (size_t)B * T * H * Dv);
   gdn_oracle_swa_sink_f64(qs, ks, vs, swa, B, T, H, Dv, n_sink, window,
-                          softmax_scale);
+                          softmax_scale, 0);
 #pragma omp parallel for schedule(dynamic, 1)
   for (long bh = 0; bh < BH; ++bh) {
     long b = bh / H, h = bh % H;
