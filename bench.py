@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill_long32k,decode_b256,conv_qwen32b")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times) "
+                         "and exit: the reference reading for HBM byte counters")
     return ap.parse_args()
 
 
@@ -183,14 +186,14 @@ def cpu_baseline(prefill_x, decode_x):
 
     f64 = synthetic.to_f64
     res = {}
-    # Prefill: all 32 heads of the first 8192 tokens of the 32k sequence.
-    Ts = 8192
+    # Prefill: the whole 32k-token workload (all 32 heads, every token).
+    Ts = prefill_x["q"].shape[1]
     ins = [f64(prefill_x[n][:, :Ts]) for n in ("q", "k", "v", "alpha", "beta")]
     t0 = time.perf_counter()
     oracle.gdn_recurrence(*ins)
     dt = time.perf_counter() - t0
     res["prefill"] = dict(value=Ts / dt, unit="tokens/s", seconds=dt,
-                          sample=f"all 32 heads x first {Ts} of 32768 tokens (B=1)")
+                          sample=f"the whole prefill workload: 32 heads x {Ts} tokens (B=1)")
     # Decode: the GDN step of all 256 x 32 heads.
     d_ins = [f64(decode_x[n]) for n in ("q", "k", "v", "alpha", "beta", "state")]
     t0 = time.perf_counter()
@@ -202,8 +205,24 @@ def cpu_baseline(prefill_x, decode_x):
     return res
 
 
+def copy_calibration(mib):
+    """A plain copy kernel of known size: reads and writes mib MiB per launch.
+    Profiling it with the FETCH_SIZE / WRITE_SIZE counters gives the factor
+    between those counters and real HBM bytes on this machine."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); every "
               "(batch, head) of this workload is independent, so several GPUs would run "
