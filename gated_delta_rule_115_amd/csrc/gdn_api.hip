@@ -87,7 +87,7 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv,
   if (B < 0 || T < 0 || H < 1 || !is_head_dim(Dk) || !is_head_dim(Dv)) return 0;
   if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
   if (dtype != GDN_BF16 && dtype != GDN_F32) return 0;
-  return gdn::prefill_workspace_bytes(B, T, H, chunk, dtype == GDN_BF16);
+  return gdn::prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype == GDN_BF16);
 }
 
 int gdn_prefill_chunked(const void* q, const void* k, const void* v,
@@ -116,12 +116,15 @@ int gdn_prefill_chunked(const void* q, const void* k, const void* v,
     REQUIRE_PTR(out);
     REQUIRE(alpha != nullptr && beta != nullptr, GDN_ERR_INVALID_ARG,
             "alpha/beta is NULL");
-    const size_t need = gdn::prefill_workspace_bytes(B, T, H, chunk, dtype == GDN_BF16);
-    REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
-    REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
-            "workspace is not 256-byte aligned");
-    REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG,
-            "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    const size_t need =
+        gdn::prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype == GDN_BF16);
+    if (need > 0) {
+      REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
+      REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
+              "workspace is not 256-byte aligned");
+      REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG,
+              "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    }
   }
   gdn::PrefillArgs p;
   p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;

@@ -61,7 +61,11 @@ struct SwaArgs {
 //   gam   [C]     f32: cumulative log gate within the chunk
 // Records are padded to 256 bytes.
 size_t prefill_record_bytes(int chunk, bool bf16);
-size_t prefill_workspace_bytes(int B, int T, int H, int chunk, bool bf16);
+// Workspace of the prefill for these sizes: 0 when the single-pass kernel
+// handles them (bf16 inputs, Dk = 128, chunk 64, Dv a multiple of 16, T > 0).
+size_t prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, bool bf16);
+bool prefill_fused_supported(const PrefillArgs& p);
+hipError_t launch_prefill_fused(const PrefillArgs& p);
 
 hipError_t launch_decode(const DecodeArgs& p);
 hipError_t launch_prefill(const PrefillArgs& p);

@@ -20,6 +20,10 @@
 // evolve independently, so kernel 2 splits Dv into slices of DVS columns, one
 // work-group each, to put enough work-groups on the chip.
 //
+// This two-kernel form serves the shapes the single-pass kernel
+// (gdn_prefill_fused.hip) does not: f32 inputs, head dimensions other than
+// Dk = 128, chunks of 16 or 32 tokens.
+//
 // Ragged tails: the last chunk is padded with identity tokens (alpha = 1,
 // beta = 0, q = k = v = 0), which leave S unchanged and read 0.
 //
@@ -41,7 +45,10 @@ size_t prefill_record_bytes(int C, bool bf16) {
   return (b + 255) / 256 * 256;
 }
 
-size_t prefill_workspace_bytes(int B, int T, int H, int C, bool bf16) {
+size_t prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C, bool bf16) {
+  PrefillArgs p{};
+  p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = C; p.bf16 = bf16;
+  if (prefill_fused_supported(p)) return 0;
   const size_t nc = ((size_t)T + C - 1) / C;
   return (size_t)B * H * nc * prefill_record_bytes(C, bf16);
 }
@@ -640,6 +647,7 @@ static hipError_t launch_prefill_c(const PrefillArgs& p) {
 
 hipError_t launch_prefill(const PrefillArgs& p) {
   if (p.B * p.H == 0) return hipSuccess;
+  if (prefill_fused_supported(p)) return launch_prefill_fused(p);
   return p.bf16 ? launch_prefill_c<bf16>(p) : launch_prefill_c<float>(p);
 }
 

@@ -64,10 +64,12 @@ int gdn_abi_version(void);
 const char* gdn_last_error(void);
 
 /*
- * Workspace (bytes) that gdn_prefill_chunked needs for these sizes; 0 if the
- * sizes are invalid.  The workspace holds, per chunk of `chunk` tokens, the
- * chunk's triangular-solve matrix, its decay-masked query-key products and
- * its cumulative log gates.
+ * Workspace (bytes) that gdn_prefill_chunked needs for these sizes.  0 when
+ * none is needed: bf16 inputs with Dk = 128, chunk = 64 and T > 0 run in a
+ * single pass that keeps every intermediate on chip.  Otherwise the
+ * workspace holds, per chunk of `chunk` tokens, the chunk's triangular-solve
+ * matrix, its decay-masked query-key products and its cumulative log gates.
+ * Also 0 if the sizes are invalid.
  */
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv,
                                    int chunk, int dtype);
@@ -84,6 +86,7 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv,
  *   chunk     16, 32 or 64 tokens per chunk (a tuning choice: the result is
  *             the same recurrence for any chunk, up to rounding)
  *   workspace device scratch of at least gdn_prefill_workspace_bytes(...)
+ *             bytes, 256-byte aligned; may be NULL when that size is 0
  * Limits: B >= 0, T >= 0, H >= 1, Dk and Dv in {16, 32, 64, 128}.  T = 0
  * copies state_in (or zeros) to state_out.  alpha must be > 0 (the kernels
  * work with log alpha).

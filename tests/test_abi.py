@@ -66,9 +66,11 @@ def _err():
     (dict(k=A + 2), INVALID, "aligned"),
     (dict(s_in=A + 4), INVALID, "aligned"),
     (dict(alpha=None), INVALID, "alpha"),
-    (dict(ws=None), INVALID, "workspace is NULL"),
-    (dict(ws=A + 16), INVALID, "256-byte"),
-    (dict(wsb=100), INVALID, "too small"),
+    # chunk 32 needs a workspace (chunk 64 with bf16, Dk = 128 needs none)
+    (dict(chunk=32, ws=None), INVALID, "workspace is NULL"),
+    (dict(chunk=32, ws=A + 16), INVALID, "256-byte"),
+    (dict(chunk=32, wsb=100), INVALID, "too small"),
+    (dict(dt=F32, odt=F32, ws=None), INVALID, "workspace is NULL"),
 ])
 def test_prefill_validation(kw, code, msg):
     assert _prefill(**kw) == code
@@ -82,9 +84,14 @@ def test_prefill_empty_batch_is_ok_without_gpu():
 
 def test_workspace_bytes():
     f = gdn.gdn_prefill_workspace_bytes
-    # per chunk: two C x C operand matrices + C f32 log gates, padded to 256 B
-    assert f(1, 64, 1, 128, 128, 64, BF16) == 2 * 64 * 64 * 2 + 256
-    assert f(2, 65, 3, 128, 128, 64, BF16) == 2 * 3 * 2 * (2 * 64 * 64 * 2 + 256)
+    # bf16, Dk = 128, chunk 64: single pass, no workspace at any Dv
+    for dv in (16, 32, 64, 128):
+        assert f(2, 65, 3, 128, dv, 64, BF16) == 0
+    # otherwise, per chunk: two C x C operand matrices + C f32 log gates,
+    # padded to 256 B
+    assert f(1, 64, 1, 128, 128, 32, BF16) == 2 * (2 * 32 * 32 * 2 + 256)
+    assert f(2, 65, 3, 64, 128, 64, BF16) == 2 * 3 * 2 * (2 * 64 * 64 * 2 + 256)
+    assert f(1, 64, 1, 128, 128, 64, F32) == 2 * 64 * 64 * 4 + 256
     assert f(1, 16, 1, 16, 16, 16, F32) == 2304
     assert f(1, 16, 1, 100, 16, 16, F32) == 0
 

@@ -70,6 +70,34 @@ def test_prefill_matches_oracle(dtype, B, T, H, Dk, Dv, chunk):
         assert torch.equal(sb, s)
 
 
+@pytest.mark.parametrize("B,T,H,Dv,state0", [
+    (1, 1, 2, 128, "randn"),      # a single token
+    (2, 63, 3, 16, "randn"),      # one value slice, ragged single chunk
+    (1, 64, 2, 32, "zero"),       # exactly one chunk
+    (2, 65, 2, 64, "randn"),      # one token into the second chunk
+    (1, 1000, 3, 128, "randn"),   # 16 chunks, ragged tail
+    (3, 257, 4, 16, "zero"),
+])
+def test_single_pass_prefill_matches_oracle(B, T, H, Dv, state0):
+    """bf16 inputs, Dk = 128, chunk 64: the single-pass kernel (no workspace)."""
+    say(f"single-pass prefill B={B} T={T} H={H} Dv={Dv} S0={state0}")
+    assert gdn.gdn_prefill_workspace_bytes(B, T, H, 128, Dv, 64) == 0
+    x = synthetic.gdn_inputs(B, T, H, 128, Dv, dtype="bf16", seed=T * 7 + Dv,
+                             state0=state0)
+    o, s = _run(x, 64, scale=0.9)
+    ro, rs = _oracle(x, scale=0.9)
+    eo, es = err(o, ro), err(s, rs)
+    say(f"  errs out {eo:.3e} state {es:.3e} nmse {oracle.nmse(f64(o), ro):.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    # bf16 output is the f32 result rounded once; no final state requested
+    ob, sn = gdn.gdn_prefill_chunked(dev(x["q"]), dev(x["k"]), dev(x["v"]),
+                                     dev(x["alpha"]), dev(x["beta"]), dev(x["state0"]),
+                                     chunk=64, scale=0.9, want_state=False)
+    torch.cuda.synchronize()
+    assert sn is None
+    assert_bf16_is_rounded_f32(ob, o)
+
+
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 63, 64, 65])
 def test_short_and_boundary_lengths(T):
     x = synthetic.gdn_inputs(1, T, 2, 32, 32, dtype="f32", seed=T, state0="randn")
