@@ -17,25 +17,27 @@
 // once and o is written once: nothing goes through a workspace.  The slices
 // of one head sit on one XCD and share its L2 copy of the q/k tiles.
 //
-// Wave roles (wave-uniform branches; every wave passes the same barriers):
-//   state waves 0..3  carry S in MFMA accumulators, split by key rows: wave w
-//                     owns rows 32w .. 32w+31.  Per chunk: partial K S and
-//                     Q S over its rows -> (LDS) -> token tile w reduces them,
-//                     forms Y -> (LDS) -> U = Tm Y for tile w -> (LDS) -> output
-//                     tile w and the S update of its rows.
-//   prep waves 4..7   run one chunk ahead: global loads of chunk c+2 into
-//                     registers, commit of chunk c+1's tiles and gates to LDS,
-//                     the Gram products of chunk c+1 (each wave a fixed set of
-//                     five 16x16 tiles), A and Pm, and the blocked triangular
-//                     inverse Tm: each diagonal 16x16 block as
-//                     (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8) (L is
-//                     strictly lower, so L^16 = 0) with 16x16x16 MFMAs, then
-//                     two levels of block products for the off-diagonal blocks.
-// Each chunk is four phases separated by work-group barriers:
-//   P1  state: partial K S, Q S (chunk c)      prep: commit c+1, load c+2, inverse level 1 (c)
-//   P2  state: reduce, Y                       prep: inverse level 2 (c), Gram c+1 (k 0..63)
-//   P3  state: U = Tm Y                        prep: Gram c+1 (k 64..127)
-//   P4  state: O, S update                     prep: A, Pm, diagonal Tm blocks of c+1
+// Wave roles (wave-uniform; every wave passes the same barriers, two per
+// chunk, and the loops of all roles run the same number of iterations):
+//   wave 0 (SA)   the recurrence's critical path for its slice.  It carries all
+//                 of S (128 x 16, f32) in eight MFMA accumulator tiles and per
+//                 chunk computes X = K S, Y, U = Tm Y and the S update with no
+//                 exchange inside the chunk.  The K^T operands of the update
+//                 come from LDS transpose reads (ds_read_b64_tr_b16).
+//   wave 1 (SB)   one chunk in arrears: Q S, the output tile, and the two
+//                 off-diagonal levels of Tm (its diagonal 16x16 blocks come
+//                 from the prep waves); S and U reach it through LDS.
+//   waves 2..7    prep one chunk ahead: the Gram products K K^T and Q K^T of
+//                 the next chunk (each wave a fixed set of 16x16 tiles), the
+//                 gate scaling into A and Pm, and the diagonal blocks of Tm as
+//                 (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8) (L strictly
+//                 lower, L^16 = 0) with 16x16x16 MFMAs.  Waves 3, 5, 6, 7 also
+//                 load the chunk after next from HBM (a two-deep register
+//                 ring) and commit it to LDS as f16; wave 7 scans the gates.
+// Per chunk c:
+//   P1  SA: X_c, Y_c            SB: O_{c-1}, Tm levels of c   prep: Gram of c+1
+//   P2  SA: U_c, S update       SB: Q_c S_c                   prep: A, Pm, diag Tm of c+1;
+//                                                                   commit c+2, load c+4
 //
 // Operand layouts.  A 16x16 MFMA result tile is held by lane l as rows
 // 4 (l/16) .. +3 of column l % 16 (the accumulator layout); a matrix M in
@@ -49,13 +51,13 @@
 //
 // v_mfma_f32_16x16x32_f16 sums over 32 contraction values, 8 per lane; which
 // logical index a lane's j-th value stands for is free as long as A and B
-// agree.  On the state path lane group q = lane / 16 carries the indices
-// {4q .. 4q+3} and {16 + 4q .. 16 + 4q + 3} of each 32-wide step, which is how
-// two stacked accumulator tiles hold their rows: S, Y, U and the decayed U
-// feed the next product straight from registers.  The K and Q tiles store
-// their key columns permuted to match (within each group of 32, logical
-// 16h + 4q + i sits at 8q + 4h + i), so those operands are single 16-byte
-// reads; the Gram products contract over the permuted columns unchanged.
+// agree.  Lane group q = lane / 16 carries the indices {4q .. 4q+3} and
+// {16 + 4q .. 16 + 4q + 3} of each 32-wide step, which is how two stacked
+// accumulator tiles hold their rows: S, Y, U and the decayed U feed the next
+// product straight from registers.  The K and Q tiles store their key columns
+// permuted to match (within each group of 32, logical 16h + 4q + i sits at
+// 8q + 4h + i), so those operands are single 16-byte reads; the Gram products
+// contract over the permuted columns unchanged.
 //
 // Gate ratios exp(gam_r - gam_c) are formed as exp(gam_r) * exp(-gam_c) from
 // per-token tables when the chunk's log-gate range is within 80 (no overflow
@@ -78,23 +80,22 @@ constexpr float kWideGate = -80.f;  // log-gate range beyond which exps are exac
 typedef _Float16 h16;
 typedef h16 h16x4 __attribute__((ext_vector_type(4)));
 typedef h16 h16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 struct __align__(16) FusedSmem {
-  h16 K[2][FC * FLD];      // K tiles of chunks c and c+1 (f16, [token][permuted key])
+  h16 K[2][FC * FLD];      // K tiles of chunks (f16, [token][permuted key]), by parity
   h16 Q[2][FC * FLD];      // Q tiles
-  f32x4 XP[4][4][64];      // partial K S: [state wave][token tile][lane]
-  f32x4 QP[4][4][64];      // partial Q S
-  f32x4 V[2][4][64];       // value slice, accumulator layout: [tile][lane][row]
-  h16x4 Y[4][64];          // Y tiles, accumulator layout
-  h16x4 U[4][64];          // U tiles
-  h16x4 Ud[4][64];         // diag(exp(gam_C - gam)) U tiles
-  h16x4 Af[4][4][64];      // A blocks (I, J), J < I, A-operand layout
-  h16x4 Tf[4][4][64];      // Tm blocks, A-operand layout; upper blocks stay 0
-  h16x4 TBf[4][4][64];     // Tm blocks, accumulator layout (inverse's right factors)
-  h16x4 Pmf[4][4][64];     // Pm blocks, A-operand layout; upper blocks stay 0
-  float gam[2][FC], gpos[2][FC], gneg[2][FC], bet[2][FC], dec[2][FC];
-  int wide[2];             // the chunk's log-gate range exceeds kWideGate
+  f32x4 V[2][4][64];       // value slices, accumulator layout: [tile][lane][row]
+  h16x8 Spub[2][4][64];    // S entering a chunk as B operands, per 32-key step
+  h16x4 Upub[4][64];       // U of the last chunk, accumulator layout
+  h16x4 Af[4][4][64];      // off-diagonal A blocks, A-operand layout
+  h16x4 TDa[4][64];        // diagonal Tm blocks, A-operand layout
+  h16x4 TDb[4][64];        // diagonal Tm blocks, accumulator layout
+  h16x4 Tf[4][4][64];      // Tm, A-operand layout; upper blocks stay 0
+  h16x4 Pmf[4][4][64];     // Pm, A-operand layout; upper blocks stay 0
+  float gam[3][FC], gpos[3][FC], gneg[3][FC], bet[3][FC], dec[3][FC];  // by chunk % 3
+  int wide[3];             // the chunk's log-gate range exceeds kWideGate
 };
 
 __device__ __forceinline__ f32x4 mfma32(h16x8 a, h16x8 b, f32x4 c) {
@@ -115,15 +116,24 @@ __device__ __forceinline__ h16x4 cvt4(f32x4 x) {
 __device__ __forceinline__ f32x4 ldf4(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
+__device__ __forceinline__ h16x8 ld8(const h16* p) {
+  return *reinterpret_cast<const h16x8*>(p);
+}
+// LDS transpose read: within each group of 16 lanes, lane i receives element
+// (i & 3) of the 8-byte chunks addressed by lanes (i >> 2) + 4k, k = 0..3.
+__device__ __forceinline__ h16x4 ld_tr(const h16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(h16x4, r);
+}
 // Physical column of logical key column c in the K / Q tiles.
 __device__ __forceinline__ int perm_col(int c) {
   return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
 }
 
 // (I + L)^-1 and its transpose for a nilpotent 16x16 L (L^16 = 0), from L and
-// L^T in accumulator layout (f32).  Every product is carried in both
-// orientations: with M, M^T in accumulator layout, M N = mfma(M^T, N) and
-// (M N)^T = mfma(N, M^T).
+// L^T in accumulator layout (f32).  With M, M^T in accumulator layout,
+// M N = mfma(M^T, N) and (M N)^T = mfma(N, M^T).
 __device__ __forceinline__ void inv_unit16(f32x4 Lf, f32x4 LTf, int lr, int lq, f32x4& T,
                                            f32x4& TT) {
   const h16x4 lo = cvt4(Lf), lt = cvt4(LTf);
@@ -158,38 +168,46 @@ struct PrepArgs {
   const float* ah;
   const float* bth;
   size_t qk_tok, v_tok;
-  int T, H, NC;
+  int T, H, NC, NIT;
   float scale;
 };
 
-// Prep wave W (0..3).  Gram tiles: K K^T (W = 0, 1) or Q K^T (W = 2, 3), row
-// blocks {3, 0} (W even: tiles (3,0..3) and (0,0)) or {2, 1} (W odd: tiles
-// (2,0..2) and (1,0..1)).  W = 0 also loads and scans the gates; W = 0 and 1
-// finish the triangular inverse.
-template <int W>
+// Registers holding one chunk's share of the inputs for a commit thread.
+struct ChunkRegs {
+  bf16x8 k[4], q[4];
+  bf16x4_t v;
+  float a, b;
+};
+
+// Prep wave PW (0..5).  Gram tiles: row block RA (tiles (RA, 0..RA)) and, if
+// RB >= 0, row block RB, of K K^T (GQ false) or Q K^T (GQ true):
+//   PW 0: KK row 3        PW 1: QK row 3
+//   PW 2: KK row 2        PW 3: QK rows 2, 0
+//   PW 4: KK rows 1, 0    PW 5: QK row 1
+// Commit threads CT (0..3): PW 1, 3, 4, 5; CT 3 also scans the gates.
+template <int PW>
 __device__ __forceinline__ void prep_loop(FusedSmem& sm, const PrepArgs& a, int l) {
-  constexpr bool GQ = W >= 2;
-  constexpr int RA = (W & 1) ? 2 : 3;
-  constexpr int RB = (W & 1) ? 1 : 0;
+  constexpr bool GQ = (PW & 1) != 0;
+  constexpr int RA = (PW <= 1) ? 3 : (PW <= 3) ? 2 : 1;
+  constexpr int RB = (PW == 3 || PW == 4) ? 0 : -1;
+  constexpr int CT = (PW == 1) ? 0 : (PW == 3) ? 1 : (PW == 4) ? 2 : (PW == 5) ? 3 : -1;
   const int lr = l & 15, lq = l >> 4;
-  const int pt = W * 64 + l;  // prep thread 0..255
   const int T = a.T, NC = a.NC;
+  const int pt = CT * 64 + l;  // commit thread 0..255 (meaningless if CT < 0)
 
-  // Per-thread element offsets of its share of a chunk (token row in the
-  // chunk times the token stride, plus the column): 4 q/k vectors, 1 v quad.
-  int off_qk[4];
+  int off_qk[4] = {0, 0, 0, 0};
+  int off_v = 0;
+  if (CT >= 0) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int vi = pt + 256 * u;
-    off_qk[u] = (vi >> 4) * (int)a.qk_tok + (vi & 15) * 8;
+    for (int u = 0; u < 4; ++u) {
+      const int vi = pt + 256 * u;
+      off_qk[u] = (vi >> 4) * (int)a.qk_tok + (vi & 15) * 8;
+    }
+    off_v = (pt >> 2) * (int)a.v_tok + (pt & 3) * 4;
   }
-  const int off_v = (pt >> 2) * (int)a.v_tok + (pt & 3) * 4;
+  ChunkRegs regs[2];
 
-  bf16x8 kreg[4], qreg[4];
-  bf16x4_t vreg;
-  float areg = 1.f, breg = 0.f;
-
-  auto prefetch = [&](int c) {
+  auto prefetch = [&](int c, ChunkRegs& r) {
     const int t0 = c * FC;
     const bf16* kc = a.kh + (size_t)t0 * a.qk_tok;
     const bf16* qc = a.qh + (size_t)t0 * a.qk_tok;
@@ -197,41 +215,42 @@ __device__ __forceinline__ void prep_loop(FusedSmem& sm, const PrepArgs& a, int 
     if (t0 + FC <= T) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        kreg[u] = *reinterpret_cast<const bf16x8*>(kc + off_qk[u]);
-        qreg[u] = *reinterpret_cast<const bf16x8*>(qc + off_qk[u]);
+        r.k[u] = *reinterpret_cast<const bf16x8*>(kc + off_qk[u]);
+        r.q[u] = *reinterpret_cast<const bf16x8*>(qc + off_qk[u]);
       }
-      vreg = *reinterpret_cast<const bf16x4_t*>(vc + off_v);
+      r.v = *reinterpret_cast<const bf16x4_t*>(vc + off_v);
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (t0 + ((pt + 256 * u) >> 4) < T) {
-          kreg[u] = *reinterpret_cast<const bf16x8*>(kc + off_qk[u]);
-          qreg[u] = *reinterpret_cast<const bf16x8*>(qc + off_qk[u]);
+          r.k[u] = *reinterpret_cast<const bf16x8*>(kc + off_qk[u]);
+          r.q[u] = *reinterpret_cast<const bf16x8*>(qc + off_qk[u]);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            kreg[u][e] = (bf16)0.f;
-            qreg[u][e] = (bf16)0.f;
+            r.k[u][e] = (bf16)0.f;
+            r.q[u][e] = (bf16)0.f;
           }
         }
       }
       if (t0 + (pt >> 2) < T) {
-        vreg = *reinterpret_cast<const bf16x4_t*>(vc + off_v);
+        r.v = *reinterpret_cast<const bf16x4_t*>(vc + off_v);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vreg[e] = (bf16)0.f;
+        for (int e = 0; e < 4; ++e) r.v[e] = (bf16)0.f;
       }
     }
-    if (W == 0) {
+    if (CT == 3) {
       const int t = t0 + l;
-      areg = (t < T) ? a.ah[(size_t)t * a.H] : 1.f;
-      breg = (t < T) ? a.bth[(size_t)t * a.H] : 0.f;
+      r.a = (t < T) ? a.ah[(size_t)t * a.H] : 1.f;
+      r.b = (t < T) ? a.bth[(size_t)t * a.H] : 0.f;
     }
   };
 
-  // Registers -> LDS for a chunk: K, Q tiles as f16 (key columns permuted),
-  // the value slice in accumulator layout, and (W = 0) the gate tables.
-  auto commit = [&](int nb) {
+  // Registers -> LDS for chunk c: K, Q tiles as f16 (key columns permuted),
+  // the value slice in accumulator layout, and (CT = 3) the gate tables.
+  auto commit = [&](int c, const ChunkRegs& r) {
+    const int nb = c & 1, g3 = c % 3;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int vi = pt + 256 * u;
@@ -240,10 +259,10 @@ __device__ __forceinline__ void prep_loop(FusedSmem& sm, const PrepArgs& a, int 
       h16x4 k0, k1, q0, q1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        k0[e] = (h16)(float)kreg[u][e];
-        k1[e] = (h16)(float)kreg[u][4 + e];
-        q0[e] = (h16)(float)qreg[u][e];
-        q1[e] = (h16)(float)qreg[u][4 + e];
+        k0[e] = (h16)(float)r.k[u][e];
+        k1[e] = (h16)(float)r.k[u][4 + e];
+        q0[e] = (h16)(float)r.q[u][e];
+        q1[e] = (h16)(float)r.q[u][4 + e];
       }
       *reinterpret_cast<h16x4*>(sm.K[nb] + p0) = k0;
       *reinterpret_cast<h16x4*>(sm.K[nb] + p1) = k1;
@@ -255,10 +274,10 @@ __device__ __forceinline__ void prep_loop(FusedSmem& sm, const PrepArgs& a, int 
       const int rt = row >> 4, qq = (row & 15) >> 2, ii = row & 3;
       float* vb = reinterpret_cast<float*>(&sm.V[nb][rt][0]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vb[(16 * qq + c4 + e) * 4 + ii] = (float)vreg[e];
+      for (int e = 0; e < 4; ++e) vb[(16 * qq + c4 + e) * 4 + ii] = (float)r.v[e];
     }
-    if (W == 0) {
-      float la = logf(areg);
+    if (CT == 3) {
+      float la = logf(r.a);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(la, off);
@@ -266,54 +285,60 @@ __device__ __forceinline__ void prep_loop(FusedSmem& sm, const PrepArgs& a, int 
       }
       const float gl = __shfl(la, 63);
       const bool wide = gl < kWideGate;
-      sm.gam[nb][l] = la;
-      sm.gpos[nb][l] = __expf(la);
-      sm.gneg[nb][l] = wide ? 0.f : __expf(-la);
-      sm.bet[nb][l] = breg;
-      sm.dec[nb][l] = __expf(gl - la);
-      if (l == 0) sm.wide[nb] = wide ? 1 : 0;
+      sm.gam[g3][l] = la;
+      sm.gpos[g3][l] = __expf(la);
+      sm.gneg[g3][l] = wide ? 0.f : __expf(-la);
+      sm.bet[g3][l] = r.b;
+      sm.dec[g3][l] = __expf(gl - la);
+      if (l == 0) sm.wide[g3] = wide ? 1 : 0;
     }
   };
 
-  // Gram accumulators.  Tile (R, C) is computed as mfma(K_C, X_R) with X = K
-  // (W = 0, 1) or Q (W = 2, 3): the result is (X K^T) restricted to the tile,
-  // in A-operand layout (lane holds element (16R + lr, 16C + 4 lq + i)); for
-  // K K^T this uses its symmetry.
-  f32x4 GA[RA + 1], GB[RB + 1];
+  // Gram accumulators.  Tile (R, Cb) is computed as mfma(K_Cb, X_R) with X = K
+  // or Q: the result is (X K^T) restricted to the tile, in A-operand layout
+  // (lane holds element (16R + lr, 16Cb + 4 lq + i)); for K K^T this uses its
+  // symmetry.
+  constexpr int NBB = (RB >= 0) ? RB + 1 : 1;
+  f32x4 GA[RA + 1], GB[NBB];
 
-  auto gram_steps = [&](int nb, int k_begin, int k_end) {
+  auto gram = [&](int c) {
+    const int nb = c & 1;
     const h16* Kb = sm.K[nb];
     const h16* Qb = sm.Q[nb];
-    for (int ks = k_begin; ks < k_end; ++ks) {
+#pragma unroll
+    for (int j = 0; j <= RA; ++j) GA[j] = zero4();
+#pragma unroll
+    for (int j = 0; j < NBB; ++j) GB[j] = zero4();
+    for (int ks = 0; ks < 4; ++ks) {
       const int kc = ks * 32 + lq * 8;
       h16x8 kf[RA + 1];
 #pragma unroll
-      for (int c = 0; c <= RA; ++c)
-        kf[c] = *reinterpret_cast<const h16x8*>(Kb + (16 * c + lr) * FLD + kc);
-      const h16x8 fa = GQ ? *reinterpret_cast<const h16x8*>(Qb + (16 * RA + lr) * FLD + kc)
-                          : kf[RA];
-      const h16x8 fb = GQ ? *reinterpret_cast<const h16x8*>(Qb + (16 * RB + lr) * FLD + kc)
-                          : kf[RB];
+      for (int cc = 0; cc <= RA; ++cc) kf[cc] = ld8(Kb + (16 * cc + lr) * FLD + kc);
+      const h16x8 fa = GQ ? ld8(Qb + (16 * RA + lr) * FLD + kc) : kf[RA];
 #pragma unroll
-      for (int c = 0; c <= RA; ++c) GA[c] = mfma32(kf[c], fa, GA[c]);
+      for (int cc = 0; cc <= RA; ++cc) GA[cc] = mfma32(kf[cc], fa, GA[cc]);
+      if (RB >= 0) {
+        const h16x8 fb = GQ ? ld8(Qb + (16 * (RB < 0 ? 0 : RB) + lr) * FLD + kc)
+                            : kf[RB < 0 ? 0 : RB];
 #pragma unroll
-      for (int c = 0; c <= RB; ++c) GB[c] = mfma32(kf[c], fb, GB[c]);
+        for (int cc = 0; cc < NBB; ++cc) GB[cc] = mfma32(kf[cc], fb, GB[cc]);
+      }
     }
   };
 
-  // Tile (R, C) -> Pm (W = 2, 3), an off-diagonal block of A (C < R), or the
-  // diagonal block of A, whose inverse is written to Tm in both layouts.
-  auto finish_tile = [&](int nb, bool wide, int R, int C, f32x4 G) {
-    const float* gm = sm.gam[nb];
-    const float* bt = sm.bet[nb];
-    const int r = 16 * R + lr;         // this lane's row
-    const int cb = 16 * C + 4 * lq;    // first of this lane's 4 columns
+  // Tile (R, Cb) -> Pm (QK waves), an off-diagonal block of A, or a diagonal
+  // block of A whose inverse is written in both layouts.
+  auto finish_tile = [&](int g3, bool wide, int R, int Cb, f32x4 G) {
+    const float* gm = sm.gam[g3];
+    const float* bt = sm.bet[g3];
+    const int r = 16 * R + lr;        // this lane's row
+    const int cb = 16 * Cb + 4 * lq;  // first of this lane's 4 columns
     const float rowf = GQ ? a.scale : bt[r];
-    if (GQ || C < R) {
+    if (GQ || Cb < R) {
       f32x4 f;
       if (!wide) {
-        const float rs = rowf * sm.gpos[nb][r];
-        const f32x4 gn = ldf4(&sm.gneg[nb][cb]);
+        const float rs = rowf * sm.gpos[g3][r];
+        const f32x4 gn = ldf4(&sm.gneg[g3][cb]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) f[i] = rs * gn[i];
       } else {
@@ -324,11 +349,11 @@ __device__ __forceinline__ void prep_loop(FusedSmem& sm, const PrepArgs& a, int 
       }
       f32x4 x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = (C < R || cb + i <= r) ? f[i] * G[i] : 0.f;
+      for (int i = 0; i < 4; ++i) x[i] = (Cb < R || cb + i <= r) ? f[i] * G[i] : 0.f;
       if (GQ) {
-        sm.Pmf[R][C][l] = cvt4(x);
+        sm.Pmf[R][Cb][l] = cvt4(x);
       } else {
-        sm.Af[R][C][l] = cvt4(x);
+        sm.Af[R][Cb][l] = cvt4(x);
       }
     } else {
       // Diagonal block: G is symmetric, so lane (lq, lr) holds G at both
@@ -338,9 +363,9 @@ __device__ __forceinline__ void prep_loop(FusedSmem& sm, const PrepArgs& a, int 
       const f32x4 bv = ldf4(&bt[rb + 4 * lq]);
       f32x4 fL, fT;
       if (!wide) {
-        const f32x4 gpv = ldf4(&sm.gpos[nb][rb + 4 * lq]);
-        const f32x4 gnv = ldf4(&sm.gneg[nb][rb + 4 * lq]);
-        const float gpl = sm.gpos[nb][rb + lr], gnl = sm.gneg[nb][rb + lr];
+        const f32x4 gpv = ldf4(&sm.gpos[g3][rb + 4 * lq]);
+        const f32x4 gnv = ldf4(&sm.gneg[g3][rb + 4 * lq]);
+        const float gpl = sm.gpos[g3][rb + lr], gnl = sm.gneg[g3][rb + lr];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           fL[i] = bv[i] * gpv[i] * gnl;
@@ -363,73 +388,43 @@ __device__ __forceinline__ void prep_loop(FusedSmem& sm, const PrepArgs& a, int 
       }
       f32x4 Tb, TTb;
       inv_unit16(Lf, LTf, lr, lq, Tb, TTb);
-      sm.Tf[R][R][l] = cvt4(TTb);
-      sm.TBf[R][R][l] = cvt4(Tb);
+      sm.TDa[R][l] = cvt4(TTb);
+      sm.TDb[R][l] = cvt4(Tb);
     }
   };
 
-  auto finish = [&](int nb) {
-    const bool wide = __builtin_amdgcn_readfirstlane(sm.wide[nb]) != 0;
+  auto finish = [&](int c) {
+    const int g3 = c % 3;
+    const bool wide = __builtin_amdgcn_readfirstlane(sm.wide[g3]) != 0;
 #pragma unroll
-    for (int c = 0; c <= RA; ++c) finish_tile(nb, wide, RA, c, GA[c]);
+    for (int cc = 0; cc <= RA; ++cc) finish_tile(g3, wide, RA, cc, GA[cc]);
+    if (RB >= 0) {
 #pragma unroll
-    for (int c = 0; c <= RB; ++c) finish_tile(nb, wide, RB, c, GB[c]);
-  };
-
-  // Level 1: T_10 = -T_11 A_10 T_00 (W = 0), T_32 = -T_33 A_32 T_22 (W = 1).
-  auto inverse_level1 = [&]() {
-    constexpr int I = (W == 0) ? 1 : 3, J = I - 1;
-    const h16x4 x = cvt4(mfma16(sm.Af[I][J][l], sm.TBf[J][J][l], zero4()));  // A_IJ T_JJ
-    const h16x4 tii = sm.Tf[I][I][l];
-    sm.TBf[I][J][l] = cvt4(-mfma16(tii, x, zero4()));  // -T_II X
-    sm.Tf[I][J][l] = cvt4(-mfma16(x, tii, zero4()));   // -(X^T T_II^T)
-  };
-
-  // Level 2: lower-left 32x32 block -T22 (A21 T11), column block j = W, in
-  // A-operand layout (the Tm consumers' layout).
-  auto inverse_level2 = [&]() {
-    constexpr int j = W;
-    f32x4 Z2 = zero4(), Z3 = zero4();
-#pragma unroll
-    for (int K = j; K < 2; ++K) {
-      const h16x4 tb = sm.TBf[K][j][l];
-      Z2 = mfma16(sm.Af[2][K][l], tb, Z2);
-      Z3 = mfma16(sm.Af[3][K][l], tb, Z3);
+      for (int cc = 0; cc < NBB; ++cc) finish_tile(g3, wide, RB < 0 ? 0 : RB, cc, GB[cc]);
     }
-    const h16x4 z2 = cvt4(Z2), z3 = cvt4(Z3);
-    sm.Tf[2][j][l] = cvt4(-mfma16(z2, sm.Tf[2][2][l], zero4()));
-    sm.Tf[3][j][l] =
-        cvt4(-(mfma16(z2, sm.Tf[3][2][l], zero4()) + mfma16(z3, sm.Tf[3][3][l], zero4())));
   };
 
-  prefetch(0);
-  for (int c = 0; c <= NC; ++c) {
-    // Iteration c prepares chunk c (tiles, gates, Gram, A, Pm, diagonal Tm
-    // blocks) and finishes the inverse of chunk c - 1.
-    const int nb = c & 1;
-    const bool prev = c >= 1;
-    const bool cur = c < NC;
-    // P1: commit chunk c, load chunk c + 1, inverse level 1 of chunk c - 1.
-    if (cur) commit(nb);
-    if (c + 1 < NC) prefetch(c + 1);
-    if (W < 2 && prev) inverse_level1();
+  // One iteration of the common loop; R0 is the register set of chunk c + 2.
+  auto iteration = [&](int c, ChunkRegs& r) {
+    // P1: Gram of chunk c + 1.
+    if (c + 1 >= 0 && c + 1 < NC) gram(c + 1);
     __syncthreads();
-    // P2: inverse level 2 of chunk c - 1; first half of chunk c's Gram.
-    if (W < 2 && prev) inverse_level2();
-    if (cur) {
-#pragma unroll
-      for (int j = 0; j <= RA; ++j) GA[j] = zero4();
-#pragma unroll
-      for (int j = 0; j <= RB; ++j) GB[j] = zero4();
-      gram_steps(nb, 0, 2);
+    // P2: A, Pm, diagonal Tm of chunk c + 1; commit chunk c + 2; load c + 4.
+    if (c + 1 >= 0 && c + 1 < NC) finish(c + 1);
+    if (CT >= 0) {
+      if (c + 2 >= 0 && c + 2 < NC) commit(c + 2, r);
+      if (c + 4 < NC) prefetch(c + 4, r);
     }
     __syncthreads();
-    // P3: second half of the Gram.
-    if (cur) gram_steps(nb, 2, 4);
-    __syncthreads();
-    // P4: A, Pm and the diagonal Tm blocks of chunk c.
-    if (cur) finish(nb);
-    __syncthreads();
+  };
+
+  if (CT >= 0) {
+    if (0 < NC) prefetch(0, regs[0]);
+    if (1 < NC) prefetch(1, regs[1]);
+  }
+  for (int it = 0; it < a.NIT; it += 2) {
+    iteration(it - 2, regs[0]);
+    iteration(it - 1, regs[1]);
   }
 }
 
@@ -445,7 +440,8 @@ __global__ __launch_bounds__(NTHR) void prefill_fused_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int lr = l & 15, lq = l >> 4;
-  const int w4 = wave & 3;  // index within the role group
+  // Iterations c = -2 .. NC of the common loop, rounded up to an even count.
+  const int NIT = (NC + 3 + 1) & ~1;
 
   int bh, slice;
   xcd_group_map(blockIdx.x, gridDim.x / NS, NS, &bh, &slice);
@@ -466,7 +462,7 @@ __global__ __launch_bounds__(NTHR) void prefill_fused_kernel(
   }
   __syncthreads();
 
-  if (wave >= 4) {
+  if (wave >= 2) {
     PrepArgs pa;
     pa.qh = q + (size_t)b * T * qk_tok + (size_t)h * FDK;
     pa.kh = k + (size_t)b * T * qk_tok + (size_t)h * FDK;
@@ -478,150 +474,223 @@ __global__ __launch_bounds__(NTHR) void prefill_fused_kernel(
     pa.T = T;
     pa.H = H;
     pa.NC = NC;
+    pa.NIT = NIT;
     pa.scale = scale;
-    switch (w4) {
-      case 0: prep_loop<0>(sm, pa, l); break;
-      case 1: prep_loop<1>(sm, pa, l); break;
-      case 2: prep_loop<2>(sm, pa, l); break;
-      default: prep_loop<3>(sm, pa, l); break;
+    switch (wave) {
+      case 2: prep_loop<0>(sm, pa, l); break;
+      case 3: prep_loop<1>(sm, pa, l); break;
+      case 4: prep_loop<2>(sm, pa, l); break;
+      case 5: prep_loop<3>(sm, pa, l); break;
+      case 6: prep_loop<4>(sm, pa, l); break;
+      default: prep_loop<5>(sm, pa, l); break;
     }
     return;
   }
 
-  // ===================== state waves =====================
-  // S rows 32 w4 + 16 hh + 4 lq + i, column col0 + lr.
-  TOut* oh = out + (size_t)b * T * v_tok + (size_t)h * DV + col0;
-  f32x4 S[2];
+  if (wave == 0) {
+    // ============================ SA ============================
+    // S tile m holds key rows 16m + 4 lq + i, value column col0 + lr.
+    f32x4 S[8];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
+    for (int m = 0; m < 8; ++m) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 32 * w4 + 16 * hh + 4 * lq + i;
-      S[hh][i] = state_in ? state_in[((size_t)bh * FDK + row) * DV + col0 + lr] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * m + 4 * lq + i;
+        S[m][i] = state_in ? state_in[((size_t)bh * FDK + row) * DV + col0 + lr] : 0.f;
+      }
     }
-  }
-  // K^T gather columns: logical key rows 32 w4 + 16 hh + lr of the S update.
-  int kcol[2];
+    // Transpose-read source chunk of this lane: key columns 16m + 4 (lr & 3)
+    // .. +3 (contiguous after the permutation), token row offset lr >> 2.
+    int kcolT[8];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) kcol[hh] = perm_col(32 * w4 + 16 * hh + lr);
-  const int r0 = 16 * w4 + 4 * lq;  // this lane's 4 token rows: r0 .. r0 + 3
+    for (int m = 0; m < 8; ++m) kcolT[m] = perm_col(16 * m + 4 * (lr & 3));
+    const int trow = 4 * lq + (lr >> 2);
 
-  f32x4 QSr = zero4();
-  h16x8 pmf[2];
-  h16x8 ktf[2][2];
-  for (int c = 0; c <= NC; ++c) {
-    // Iteration c works on chunk c - 1 (the prep waves run one chunk ahead,
-    // so the first iteration only waits for them).
-    const int cc = c - 1;
-    const int cb = cc & 1;
-    const bool run = cc >= 0;
-    // P1: partial K S and Q S over this wave's 32 key rows.
-    if (run) {
-      const h16x8 sb = cat8(cvt4(S[0]), cvt4(S[1]));
-      const h16* Kb = sm.K[cb];
-      const h16* Qb = sm.Q[cb];
-      const int kc = 32 * w4 + 8 * lq;  // permuted columns of this wave's keys
+    h16x4 y16[4];
+    h16x8 ktr[8][2];
+    for (int it = 0; it < NIT; ++it) {
+      const int c = it - 2;
+      const bool run = c >= 0 && c < NC;
+      const int b2 = c & 1, g3 = run ? c % 3 : 0;
+      // P1: X = K S, Y = diag(beta) (V - diag(g) X); K^T operands of the update.
+      if (run) {
+        h16x8 sb[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int row = 16 * rt + lr;
-        const h16x8 ka = *reinterpret_cast<const h16x8*>(Kb + row * FLD + kc);
-        const h16x8 qa = *reinterpret_cast<const h16x8*>(Qb + row * FLD + kc);
-        sm.XP[w4][rt][l] = mfma32(ka, sb, zero4());
-        sm.QP[w4][rt][l] = mfma32(qa, sb, zero4());
-      }
-    }
-    __syncthreads();
-    // P2: reduce token tile w4; Y = diag(beta) (V - diag(g) K S).
-    if (run) {
-      f32x4 X = sm.XP[0][w4][l];
-      QSr = sm.QP[0][w4][l];
+        for (int j = 0; j < 4; ++j) sb[j] = cat8(cvt4(S[2 * j]), cvt4(S[2 * j + 1]));
+        const h16* Kb = sm.K[b2];
+        const f32x4* Vb = &sm.V[b2][0][0];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        X += sm.XP[w][w4][l];
-        QSr += sm.QP[w][w4][l];
-      }
-      const f32x4 Vv = sm.V[cb][w4][l];
-      const f32x4 bv = ldf4(&sm.bet[cb][r0]);
-      const f32x4 gv = ldf4(&sm.gpos[cb][r0]);
-      h16x4 y;
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 X = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = (h16)(bv[i] * (Vv[i] - gv[i] * X[i]));
-      sm.Y[w4][l] = y;
-      // K^T operands of this chunk's S update (key rows of this wave).
-      const h16* Kb = sm.K[cb];
+          for (int j = 0; j < 4; ++j)
+            X = mfma32(ld8(Kb + (16 * rt + lr) * FLD + 32 * j + 8 * lq), sb[j], X);
+          const int r0 = 16 * rt + 4 * lq;
+          const f32x4 bv = ldf4(&sm.bet[g3][r0]);
+          const f32x4 gv = ldf4(&sm.gpos[g3][r0]);
+          const f32x4 Vv = Vb[rt * 64 + l];
+          h16x4 y;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+          for (int i = 0; i < 4; ++i) y[i] = (h16)(bv[i] * (Vv[i] - gv[i] * X[i]));
+          y16[rt] = y;
+        }
 #pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
+        for (int m = 0; m < 8; ++m) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ktf[hh][jp][i] = Kb[(32 * jp + 4 * lq + i) * FLD + kcol[hh]];
-            ktf[hh][jp][4 + i] = Kb[(32 * jp + 16 + 4 * lq + i) * FLD + kcol[hh]];
+          for (int jp = 0; jp < 2; ++jp) {
+            ktr[m][jp] = cat8(ld_tr(Kb + (32 * jp + trow) * FLD + kcolT[m]),
+                              ld_tr(Kb + (32 * jp + 16 + trow) * FLD + kcolT[m]));
           }
         }
       }
-    }
-    __syncthreads();
-    // P3: U = Tm Y for token tile w4 (Tm lower triangular).
-    if (run) {
-      f32x4 U = zero4();
+      __syncthreads();
+      // P2: U = Tm Y; S <- g_C S + K^T diag(dec) U; publish U and the new S.
+      if (run) {
+        h16x8 udb[2];
+        h16x4 ud[4];
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        pmf[jp] = cat8(sm.Pmf[w4][2 * jp][l], sm.Pmf[w4][2 * jp + 1][l]);
-        if (jp == 0 || w4 >= 2) {
-          const h16x8 ta = cat8(sm.Tf[w4][2 * jp][l], sm.Tf[w4][2 * jp + 1][l]);
-          U = mfma32(ta, cat8(sm.Y[2 * jp][l], sm.Y[2 * jp + 1][l]), U);
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 U = zero4();
+#pragma unroll
+          for (int jp = 0; jp < 2; ++jp) {
+            if (jp == 0 || rt >= 2) {
+              const h16x8 ta = cat8(sm.Tf[rt][2 * jp][l], sm.Tf[rt][2 * jp + 1][l]);
+              U = mfma32(ta, cat8(y16[2 * jp], y16[2 * jp + 1]), U);
+            }
+          }
+          const f32x4 dv = ldf4(&sm.dec[g3][16 * rt + 4 * lq]);
+          h16x4 u16, d16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u16[i] = (h16)U[i];
+            d16[i] = (h16)(dv[i] * U[i]);
+          }
+          sm.Upub[rt][l] = u16;
+          ud[rt] = d16;
+        }
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) udb[jp] = cat8(ud[2 * jp], ud[2 * jp + 1]);
+        const float gC = sm.gpos[g3][FC - 1];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          f32x4 acc = gC * S[m];
+#pragma unroll
+          for (int jp = 0; jp < 2; ++jp) acc = mfma32(ktr[m][jp], udb[jp], acc);
+          S[m] = acc;
         }
       }
-      const f32x4 dv = ldf4(&sm.dec[cb][r0]);
-      h16x4 u16, ud16;
+      if (run || c == -1) {
+        // S entering chunk c + 1, as the B operands of Q S.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u16[i] = (h16)U[i];
-        ud16[i] = (h16)(dv[i] * U[i]);
+        for (int j = 0; j < 4; ++j)
+          sm.Spub[(c + 1) & 1][j][l] = cat8(cvt4(S[2 * j]), cvt4(S[2 * j + 1]));
       }
-      sm.U[w4][l] = u16;
-      sm.Ud[w4][l] = ud16;
+      __syncthreads();
     }
-    __syncthreads();
-    // P4: O = diag(scale g) Q S + Pm U;  S <- g_C S + K^T diag(dec) U.
-    if (run) {
-      const f32x4 gv = ldf4(&sm.gpos[cb][r0]);
-      f32x4 O;
+    if (state_out) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[i] = scale * gv[i] * QSr[i];
+      for (int m = 0; m < 8; ++m) {
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp)
-        if (jp == 0 || w4 >= 2)
-          O = mfma32(pmf[jp], cat8(sm.U[2 * jp][l], sm.U[2 * jp + 1][l]), O);
-      const float gC = sm.gpos[cb][FC - 1];
-      h16x8 udb[2];
-#pragma unroll
-      for (int jp = 0; jp < 2; ++jp) udb[jp] = cat8(sm.Ud[2 * jp][l], sm.Ud[2 * jp + 1][l]);
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f32x4 acc = gC * S[hh];
-#pragma unroll
-        for (int jp = 0; jp < 2; ++jp) acc = mfma32(ktf[hh][jp], udb[jp], acc);
-        S[hh] = acc;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = cc * FC + r0 + i;
-        if (t < T) oh[(size_t)t * v_tok + lr] = from_f32<TOut>(O[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * m + 4 * lq + i;
+          state_out[((size_t)bh * FDK + row) * DV + col0 + lr] = S[m][i];
+        }
       }
     }
-    __syncthreads();
+    return;
   }
-  if (state_out) {
+
+  // ============================== SB ==============================
+  TOut* oh = out + (size_t)b * T * v_tok + (size_t)h * DV + col0;
+  f32x4 QS[4];
+  f32x4 gp[4];
+  h16x8 pma[4][2];
+  h16x8 qa[4][4];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+  for (int rt = 0; rt < 4; ++rt) {
+    QS[rt] = zero4();
+    gp[rt] = zero4();
+  }
+  for (int it = 0; it < NIT; ++it) {
+    const int c = it - 2;
+    // P1: output of chunk c - 1; Tm of chunk c; operands of chunk c.
+    if (c >= 1 && c <= NC) {
+      const int cp = c - 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 32 * w4 + 16 * hh + 4 * lq + i;
-        state_out[((size_t)bh * FDK + row) * DV + col0 + lr] = S[hh][i];
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 O;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[i] = scale * gp[rt][i] * QS[rt][i];
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp)
+          if (jp == 0 || rt >= 2)
+            O = mfma32(pma[rt][jp], cat8(sm.Upub[2 * jp][l], sm.Upub[2 * jp + 1][l]), O);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = cp * FC + 16 * rt + 4 * lq + i;
+          if (t < T) oh[(size_t)t * v_tok + lr] = from_f32<TOut>(O[i]);
+        }
       }
     }
+    if (c >= 0 && c < NC) {
+      // Tm levels (blocks in A-operand layout for SA; T_10 also in
+      // accumulator layout as a right factor of level 2):
+      //   T_10 = -T_11 A_10 T_00,   T_32 = -T_33 A_32 T_22,
+      //   T_2j = -T_22 Z_2j,   T_3j = -(T_32 Z_2j + T_33 Z_3j),
+      //   Z_mj = A_m0 T_0j + A_m1 T_1j.
+      const h16x4 x10 = cvt4(mfma16(sm.Af[1][0][l], sm.TDb[0][l], zero4()));
+      const h16x4 ta11 = sm.TDa[1][l];
+      const h16x4 tb10 = cvt4(-mfma16(ta11, x10, zero4()));
+      sm.Tf[1][0][l] = cvt4(-mfma16(x10, ta11, zero4()));
+      const h16x4 x32 = cvt4(mfma16(sm.Af[3][2][l], sm.TDb[2][l], zero4()));
+      const h16x4 ta32 = cvt4(-mfma16(x32, sm.TDa[3][l], zero4()));
+      sm.Tf[3][2][l] = ta32;
+      const h16x4 ta22 = sm.TDa[2][l], ta33 = sm.TDa[3][l];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x4 Z2, Z3;
+        if (j == 0) {
+          const h16x4 t00 = sm.TDb[0][l];
+          Z2 = mfma16(sm.Af[2][1][l], tb10, mfma16(sm.Af[2][0][l], t00, zero4()));
+          Z3 = mfma16(sm.Af[3][1][l], tb10, mfma16(sm.Af[3][0][l], t00, zero4()));
+        } else {
+          const h16x4 t11 = sm.TDb[1][l];
+          Z2 = mfma16(sm.Af[2][1][l], t11, zero4());
+          Z3 = mfma16(sm.Af[3][1][l], t11, zero4());
+        }
+        const h16x4 z2 = cvt4(Z2), z3 = cvt4(Z3);
+        sm.Tf[2][j][l] = cvt4(-mfma16(z2, ta22, zero4()));
+        sm.Tf[3][j][l] = cvt4(-(mfma16(z2, ta32, zero4()) + mfma16(z3, ta33, zero4())));
+      }
+#pragma unroll
+      for (int I = 0; I < 4; ++I) sm.Tf[I][I][l] = sm.TDa[I][l];
+      // Operands of chunk c kept for the next iterations.
+      const int b2 = c & 1, g3 = c % 3;
+      const h16* Qb = sm.Q[b2];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qa[rt][j] = ld8(Qb + (16 * rt + lr) * FLD + 32 * j + 8 * lq);
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp)
+          pma[rt][jp] = (jp == 0 || rt >= 2)
+                            ? cat8(sm.Pmf[rt][2 * jp][l], sm.Pmf[rt][2 * jp + 1][l])
+                            : h16x8{};
+        gp[rt] = ldf4(&sm.gpos[g3][16 * rt + 4 * lq]);
+      }
+    }
+    __syncthreads();
+    // P2: Q S of chunk c.
+    if (c >= 0 && c < NC) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma32(qa[rt][j], sm.Spub[c & 1][j][l], acc);
+        QS[rt] = acc;
+      }
+    }
+    __syncthreads();
   }
 }
 
