@@ -27,20 +27,24 @@
 // nothing goes through a workspace.  The slices of one head sit on one XCD and
 // share its L2 copy of the q/k tiles.
 //
+// Waves w and w + 4 share a SIMD; the roles are paired so that each SIMD
+// carries a similar mix of MFMA and VALU work.
+//
 // Pipeline.  Every wave runs the same loop of iterations, one barrier each;
 // each role works on a different chunk and hands results on through LDS ring
 // slots (no role waits for another inside an iteration).  At iteration i:
-//   CM  (waves 4, 6)  chunk i: K tile -> LDS as f16 (key columns permuted);
+//   CM  (waves 4, 7)  chunk i: K tile -> LDS as f16 (key columns permuted);
 //                     global loads for chunk i + 2
 //   KK  (waves 1, 2)  chunk i - 1: Gram blocks of K K^T for two block rows,
-//                     scaled into A, and the diagonal blocks of Tm inverted as
+//                     scaled into A; diagonal blocks 0, 1 of Tm inverted as
 //                     (I + L)^-1 = (I + L^8)(I + L^4)(I + L^2)(I - L)
-//   LV  (wave 5)      chunk i - 2: off-diagonal blocks of Tm (block forward
-//                     substitution); chunk i: gate tables and the scaled V slice
+//   LV  (wave 3)      chunk i - 2: diagonal blocks 2, 3 of Tm, then the
+//                     off-diagonal blocks (block forward substitution);
+//                     chunk i: gate tables and the scaled V slice
 //   CH  (wave 0)      chunk i - 3: the recurrence for this slice: X = K S,
 //                     Y~, U^ = T Y~, S update.  S (128 x 16, f32) lives in
 //                     eight MFMA accumulator tiles for the whole sequence.
-//   OUT (waves 3, 7)  chunk i - 3: Q rows of two block rows (own global loads,
+//   OUT (waves 5, 6)  chunk i - 3: Q rows of two block rows (own global loads,
 //                     f16), their Q K^T blocks -> P; chunk i - 4: Q S, P U^ and
 //                     the output rows.
 //
@@ -98,7 +102,8 @@ struct __align__(16) Smem {
   h16 K[4][FC * FLD];     // K tiles (f16, permuted key columns), slot = chunk & 3
   f32x4 Vt[4][4][64];     // a * V, accumulator layout [row tile][lane], slot = chunk & 3
   h16x4 Ga[2][6][64];     // A blocks 10, 20, 21, 30, 31, 32 as A operands, slot = chunk & 1
-  h16x4 Td[2][7][64];     // D(T00), D(T00^T), D(T11), D(T11^T), D(T22), D(T22^T), D(T33^T)
+  h16x4 Td[2][4][64];     // D(T00), D(T00^T), D(T11), D(T11^T)
+  f32x4 Ld[2][4][64];     // D(L2), D(L2^T), D(L3), D(L3^T): diagonal blocks 2, 3 of A
   h16x8 Tc[2][6][64];     // Tm operands of the recurrence (row tile, 32-step pairs)
   h16x8 Sp[2][4][64];     // S entering a chunk as B operands, per 32-key step
   h16x4 Up[2][4][64];     // U^ of a chunk, accumulator layout
@@ -145,6 +150,32 @@ __device__ __forceinline__ h16x4 ld_tr(const h16* p) {
 // Physical column of logical key column c in the K tile.
 __device__ __forceinline__ int perm_col(int c) {
   return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+// Work-group barrier ordering LDS only.  Waves exchange data through LDS
+// alone, so global loads issued for later chunks stay in flight across it
+// (a full __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (lanes read as zero where the shifted source is absent).
+__device__ __forceinline__ float wave_incl_sum(float x) {
+  const int z = 0;
+  auto sh = [&](float v, auto ctrl) -> float {
+    constexpr int C = decltype(ctrl)::value;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, v), C, 0xf, 0xf, false));
+  };
+  x += sh(x, ic<0x111>());  // row_shr:1
+  x += sh(x, ic<0x112>());  // row_shr:2
+  x += sh(x, ic<0x114>());  // row_shr:4
+  x += sh(x, ic<0x118>());  // row_shr:8
+  // row_bcast:15 adds lane 15 of each row to the next row; row_bcast:31 adds
+  // lane 31 to rows 2 and 3.
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return x;
 }
 __device__ __forceinline__ f32x4 ident4(int lr, int lq) {
   f32x4 r;
@@ -219,22 +250,25 @@ __device__ void role_commit(Smem& sm, const Args& a, int l) {
     constexpr int p = decltype(P)::value;  // it & 1
     if (it < a.NC) {
       h16* Kb = sm.K[it & 3];
+      h16x4 kh[8][2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kh[u][0][e] = (h16)(float)raw[p][u][e];
+          kh[u][1][e] = (h16)(float)raw[p][u][4 + e];
+        }
+      }
+      if (it + 2 < a.NC) load(it + 2, raw[p]);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int vi = l + 64 * u;
         const int row = 32 * W + (vi >> 4), c0 = (vi & 15) * 8;
-        h16x4 k0, k1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k0[e] = (h16)(float)raw[p][u][e];
-          k1[e] = (h16)(float)raw[p][u][4 + e];
-        }
-        *reinterpret_cast<h16x4*>(Kb + row * FLD + perm_col(c0)) = k0;
-        *reinterpret_cast<h16x4*>(Kb + row * FLD + perm_col(c0 + 4)) = k1;
+        *reinterpret_cast<h16x4*>(Kb + row * FLD + perm_col(c0)) = kh[u][0];
+        *reinterpret_cast<h16x4*>(Kb + row * FLD + perm_col(c0 + 4)) = kh[u][1];
       }
-      if (it + 2 < a.NC) load(it + 2, raw[p]);
     }
-    __syncthreads();
+    lds_barrier();
   };
   if (0 < a.NC) load(0, raw[0]);
   if (1 < a.NC) load(1, raw[1]);
@@ -322,31 +356,30 @@ __device__ void role_kk(Smem& sm, const Args& a, int l) {
         // Rows 0 and 3: A30, A31, A32; T00 in both layouts, T33^T.
 #pragma unroll
         for (int C = 0; C < 3; ++C) sm.Ga[s][3 + C][l] = offdiag(gs, wide, 3, C, GB[C]);
-        f32x4 L0, LT0, L3, LT3, T00, TT00, T33, TT33;
-        diag(gs, wide, 0, GA[0], L0, LT0);
+        f32x4 L0, LT0, L3, LT3, T00, TT00;
         diag(gs, wide, 3, GB[3], L3, LT3);
+        sm.Ld[s][2][l] = L3;
+        sm.Ld[s][3][l] = LT3;
+        diag(gs, wide, 0, GA[0], L0, LT0);
         inv16<true, true>(L0, LT0, lr, lq, T00, TT00);
-        inv16<false, true>(L3, LT3, lr, lq, T33, TT33);
         sm.Td[s][0][l] = cvt4(T00);
         sm.Td[s][1][l] = cvt4(TT00);
-        sm.Td[s][6][l] = cvt4(TT33);
       } else {
         // Rows 1 and 2: A10, A20, A21; T11 and T22 in both layouts.
         sm.Ga[s][0][l] = offdiag(gs, wide, 1, 0, GA[0]);
         sm.Ga[s][1][l] = offdiag(gs, wide, 2, 0, GB[0]);
         sm.Ga[s][2][l] = offdiag(gs, wide, 2, 1, GB[1]);
-        f32x4 L1, LT1, L2, LT2, T11, TT11, T22, TT22;
-        diag(gs, wide, 1, GA[1], L1, LT1);
+        f32x4 L1, LT1, L2, LT2, T11, TT11;
         diag(gs, wide, 2, GB[2], L2, LT2);
+        sm.Ld[s][0][l] = L2;
+        sm.Ld[s][1][l] = LT2;
+        diag(gs, wide, 1, GA[1], L1, LT1);
         inv16<true, true>(L1, LT1, lr, lq, T11, TT11);
-        inv16<true, true>(L2, LT2, lr, lq, T22, TT22);
         sm.Td[s][2][l] = cvt4(T11);
         sm.Td[s][3][l] = cvt4(TT11);
-        sm.Td[s][4][l] = cvt4(T22);
-        sm.Td[s][5][l] = cvt4(TT22);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -356,6 +389,7 @@ __device__ void role_kk(Smem& sm, const Args& a, int l) {
 //   T2j = -T22 Z2j,  T3j = -(T32 Z2j + T33 Z3j),  Zmj = Am0 T0j + Am1 T1j;
 // gate tables and the scaled value slice of chunk i (lane = token).
 __device__ void role_lv(Smem& sm, const Args& a, int l) {
+  const int lr = l & 15, lq = l >> 4;
   float ra[2], rb[2];
   bf16x8 rv[2][2];
   auto load = [&](int c, int p) {
@@ -385,8 +419,11 @@ __device__ void role_lv(Smem& sm, const Args& a, int l) {
       const h16x4 ga30 = sm.Ga[s][3][l], ga31 = sm.Ga[s][4][l], ga32 = sm.Ga[s][5][l];
       const h16x4 d00 = sm.Td[s][0][l], d00t = sm.Td[s][1][l];
       const h16x4 d11 = sm.Td[s][2][l], d11t = sm.Td[s][3][l];
-      const h16x4 d22 = sm.Td[s][4][l], d22t = sm.Td[s][5][l];
-      const h16x4 d33t = sm.Td[s][6][l];
+      f32x4 T22, TT22, T33, TT33;
+      inv16<true, true>(sm.Ld[s][0][l], sm.Ld[s][1][l], lr, lq, T22, TT22);
+      inv16<false, true>(sm.Ld[s][2][l], sm.Ld[s][3][l], lr, lq, T33, TT33);
+      const h16x4 d22 = cvt4(T22), d22t = cvt4(TT22);
+      const h16x4 d33t = cvt4(TT33);
       const h16x4 x10 = cvt4(mfma16(ga10, d00, zero4()));    // D(A10 T00)
       const h16x4 t10t = cvt4(-mfma16(x10, d11t, zero4()));  // D(T10^T)
       const h16x4 t10 = cvt4(-mfma16(d11t, x10, zero4()));   // D(T10)
@@ -412,16 +449,19 @@ __device__ void role_lv(Smem& sm, const Args& a, int l) {
     }
     if (it < a.NC) {
       GateSlot& gs = sm.g[it % 5];
-      float la = __logf(ra[p]);
+      float vf[16];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(la, off);
-        if (l >= off) la += y;
+      for (int n = 0; n < 8; ++n) {
+        vf[n] = (float)rv[p][0][n];
+        vf[8 + n] = (float)rv[p][1][n];
       }
-      const float g0 = __shfl(la, 0), gl = __shfl(la, 63);
+      const float lalpha = __logf(ra[p]), bt = rb[p];
+      if (it + 2 < a.NC) load(it + 2, p);
+      const float la = wave_incl_sum(lalpha);
+      const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 0));
+      const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 63));
       const bool wide = (g0 - gl) > kWideRange;
       const float gm = 0.5f * (g0 + gl);
-      const float bt = rb[p];
       const float g = __expf(la);
       const float av = wide ? bt : bt * __expf(gm - la);
       gs.a[l] = av;
@@ -441,13 +481,9 @@ __device__ void role_lv(Smem& sm, const Args& a, int l) {
       float* vb = reinterpret_cast<float*>(&sm.Vt[it & 3][l >> 4][0]);
       const int lb = ((l & 15) >> 2) * 16, e = l & 3;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        vb[(lb + n) * 4 + e] = av * (float)rv[p][0][n];
-        vb[(lb + 8 + n) * 4 + e] = av * (float)rv[p][1][n];
-      }
-      if (it + 2 < a.NC) load(it + 2, p);
+      for (int n = 0; n < 16; ++n) vb[(lb + n) * 4 + e] = av * vf[n];
     }
-    __syncthreads();
+    lds_barrier();
   };
   if (0 < a.NC) load(0, 0);
   if (1 < a.NC) load(1, 1);
@@ -542,7 +578,7 @@ __device__ void role_chain(Smem& sm, const Args& a, int l) {
         S[m] = gC * S[m] + cS * dS;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (a.state_out) {
 #pragma unroll
@@ -604,6 +640,7 @@ __device__ void role_out(Smem& sm, const Args& a, int l) {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 4; ++j) qh[p][b][j] = cvt8(raw[p][b][j][0], raw[p][b][j][1]);
+      if (it - 1 < a.NC) load(it - 1, p);
       const h16* Kb = sm.K[c & 3];
       f32x4 GA[RA + 1], GB[RB + 1];
 #pragma unroll
@@ -644,7 +681,7 @@ __device__ void role_out(Smem& sm, const Args& a, int l) {
         pf[p][1][C] = C <= RB ? mk(RB, C, GB[C <= RB ? C : 0]) : zz;
       }
     }
-    if (it >= 1 && it - 1 < a.NC) load(it - 1, p);
+    if (c < 0 && it >= 1 && it - 1 < a.NC) load(it - 1, p);
     const int cp = it - 4;
     if (cp >= 0 && cp < a.NC) {
       const int s = cp & 1;
@@ -668,7 +705,7 @@ __device__ void role_out(Smem& sm, const Args& a, int l) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   };
   // Iteration it works on chunk it - 3, of parity (it + 1) & 1; the loop starts
   // at it = 0 and is unrolled by two.
@@ -717,11 +754,11 @@ __global__ __launch_bounds__(NTHR) void prefill_fused_kernel(
     case 0: role_chain(sm, a, l); break;
     case 1: role_kk<0>(sm, a, l); break;
     case 2: role_kk<1>(sm, a, l); break;
-    case 3: role_out<0, TOut>(sm, a, l); break;
+    case 3: role_lv(sm, a, l); break;
     case 4: role_commit<0>(sm, a, l); break;
-    case 5: role_lv(sm, a, l); break;
-    case 6: role_commit<1>(sm, a, l); break;
-    default: role_out<1, TOut>(sm, a, l); break;
+    case 5: role_out<0, TOut>(sm, a, l); break;
+    case 6: role_out<1, TOut>(sm, a, l); break;
+    default: role_commit<1>(sm, a, l); break;
   }
 }
 
