@@ -27,8 +27,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -70,6 +70,28 @@ def decode_swa_bytes(d, n_slots, esize=2):
     return esize * (2 * d * (n_slots - 1) + 2 * d + 2 * d + d + 2 * d)
 
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
+# scaled by the copy calibration (read x2.00, write x1.00), recorded with the
+# SHA-1 of the kernel source they were taken on: a kernel whose source has
+# changed since reports traffic null.  Each figure is copied from the profile
+# summary named in "profile".
+COUNTERS = {
+    # kernel: dict(src=..., sha1=..., fetch_kib=..., write_kib=..., profile=...)
+}
+READ_FACTOR, WRITE_FACTOR = 2.00, 1.00
+
+
+def traffic_bytes(kernel):
+    rec = COUNTERS.get(kernel)
+    if rec is None:
+        return None
+    path = os.path.join(HERE, rec["src"])
+    with open(path, "rb") as f:
+        if hashlib.sha1(f.read()).hexdigest() != rec["sha1"]:
+            return None
+    return (rec["fetch_kib"] * READ_FACTOR + rec["write_kib"] * WRITE_FACTOR) * 1024
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,9 +128,10 @@ def make_prefill_leg():
     ws = torch.empty(gdn.gdn_prefill_workspace_bytes(B, T, H, d, d, 64), dtype=torch.uint8,
                      device="cuda")
 
-    def run():
+    def run(mark):
         gdn.gdn_prefill_chunked(x["q"], x["k"], x["v"], x["alpha"], x["beta"], None,
                                 chunk=64, out=out, state_out=st, workspace=ws)
+        mark("prefill")
 
     info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
                 flops=prefill_flops_per_token_head(d) * B * T * H,
@@ -139,10 +162,12 @@ def make_decode_leg():
     nt = torch.full((B,), ctx + 1, dtype=torch.int32, device="cuda")
     out = torch.empty(B, H, d, dtype=torch.bfloat16, device="cuda")
 
-    def run():
+    def run(mark):
         gdn.gdn_decode_step(q, k, v, a, b, st, state_out=st, out=out)
+        mark("decode_step")
         gdn.gdn_swa_sink_decode(qs, kc, vc, nt, n_sink=s, window=w, k_new=kn, v_new=vn,
                                 accumulate=True, out=out)
+        mark("swa_sink_decode")
 
     info = dict(B=B, H=H, d=d, tokens=B, n_slots=s + w,
                 bytes=B * H * (decode_gdn_bytes(d) + decode_swa_bytes(d, s + w)),
@@ -165,12 +190,14 @@ def make_conv_leg():
     ws = torch.empty(gdn.gdn_prefill_workspace_bytes(B, T, H, d, d, 64), dtype=torch.uint8,
                      device="cuda")
 
-    def run():
+    def run(mark):
         for n, grp in (("q", d), ("k", d), ("v", 0)):
             gdn.gdn_short_conv_silu(raw[n], taps[n], l2norm_group=grp, out=conv[n])
+        mark("conv")
         gdn.gdn_prefill_chunked(conv["q"].view(B, T, H, d), conv["k"].view(B, T, H, d),
                                 conv["v"].view(B, T, H, d), g["alpha"], g["beta"], None,
                                 chunk=64, out=out, state_out=st, workspace=ws)
+        mark("prefill")
 
     info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
                 conv_bytes=3 * B * T * H * d * 2 * 2,
@@ -250,17 +277,24 @@ def main():
     torch.cuda.synchronize()
 
     def step(record):
+        """One pass of every leg.  With record, HIP events on the kernels'
+        stream bracket each leg and each kernel segment inside it."""
         evs = {}
         for name, fn in legs.items():
-            if record:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                fn()
-                b.record(stream)
-                evs[name] = (a, b)
-            else:
-                fn()
+            if not record:
+                fn(lambda seg: None)
+                continue
+            a = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            marks = [("", a)]
+
+            def mark(seg, marks=marks):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append((seg, e))
+
+            fn(mark)
+            evs[name] = marks
         return evs
 
     for _ in range(args.warmup):
@@ -270,7 +304,14 @@ def main():
     all_evs = [step(True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    leg_ms = {n: [e[n][0].elapsed_time(e[n][1]) for e in all_evs] for n in legs}
+    leg_ms = {n: [e[n][0][1].elapsed_time(e[n][-1][1]) for e in all_evs] for n in legs}
+    # per-kernel segment times (ms), averaged over the timed steps
+    seg_ms = {}
+    for n in legs:
+        for i in range(1, len(all_evs[0][n])):
+            seg = all_evs[0][n][i][0]
+            vals = [e[n][i - 1][1].elapsed_time(e[n][i][1]) for e in all_evs]
+            seg_ms[(n, seg)] = sum(vals) / len(vals)
 
     out_legs = {}
     for n, ms in leg_ms.items():
@@ -288,25 +329,43 @@ def main():
             rec["hbm_frac"] = inf["bytes"] / sec / PEAK_HBM_BPS
         out_legs[n] = rec
 
+    for (n, seg), ms in seg_ms.items():
+        out_legs[n].setdefault("kernel_ms", {})[seg] = ms
+
+    def hbm_roof(kernel, nbytes, ms):
+        sec = ms / 1e3
+        t = traffic_bytes(kernel)
+        return dict(bound="hbm", kernel=kernel, achieved=nbytes / sec / 1e9,
+                    peak=PEAK_HBM_BPS / 1e9, unit="GB/s", frac=nbytes / sec / PEAK_HBM_BPS,
+                    traffic=t, bytes_per_launch=nbytes, ms_per_launch=ms)
+
     head = out_legs.get("prefill_long32k")
     value = head["tokens_per_s"] if head else None
     roofline = None
     if head:
         inf = infos["prefill_long32k"]
-        sec = head["ms_avg"] / 1e3
-        roofline = dict(bound="mfma", kernel="gdn_prefill_chunked (chunk_prep + chunk_recur)",
-                        achieved=inf["flops"] / sec / 1e12, peak=PEAK_BF16_FLOPS / 1e12,
-                        unit="TFLOP/s", frac=inf["flops"] / sec / PEAK_BF16_FLOPS,
-                        traffic=None, flops_per_launch=inf["flops"],
-                        flops_per_token_head=prefill_flops_per_token_head(inf["d"]))
+        ms = seg_ms[("prefill_long32k", "prefill")]
+        sec = ms / 1e3
+        kern = "prefill_fused_kernel<bf16>"
+        roofline = dict(bound="mfma", kernel=kern, achieved=inf["flops"] / sec / 1e12,
+                        peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                        frac=inf["flops"] / sec / PEAK_BF16_FLOPS, traffic=traffic_bytes(kern),
+                        ms_per_launch=ms, flops_per_launch=inf["flops"],
+                        flops_per_token_head=prefill_flops_per_token_head(inf["d"]),
+                        hbm_bytes_algorithmic=inf["bytes"],
+                        hbm_frac_algorithmic=inf["bytes"] / sec / PEAK_HBM_BPS)
     roof_dec = None
     if "decode_b256" in out_legs:
         inf = infos["decode_b256"]
-        sec = out_legs["decode_b256"]["ms_avg"] / 1e3
-        roof_dec = dict(bound="hbm", kernel="gdn_decode_step + gdn_swa_sink_decode",
-                        achieved=inf["bytes"] / sec / 1e9, peak=PEAK_HBM_BPS / 1e9,
-                        unit="GB/s", frac=inf["bytes"] / sec / PEAK_HBM_BPS, traffic=None,
-                        bytes_per_launch=inf["bytes"])
+        roof_dec = [hbm_roof("decode_step_kernel<bf16,bf16,128,128>", inf["bytes_gdn"],
+                             seg_ms[("decode_b256", "decode_step")]),
+                    hbm_roof("swa_sink_decode_kernel<bf16,bf16,128>", inf["bytes_swa"],
+                             seg_ms[("decode_b256", "swa_sink_decode")])]
+    roof_conv = None
+    if "conv_qwen32b" in out_legs:
+        inf = infos["conv_qwen32b"]
+        roof_conv = hbm_roof("short_conv_silu_kernel<bf16,bf16,4> (x3)", inf["conv_bytes"],
+                             seg_ms[("conv_qwen32b", "conv")])
 
     cpu = None
     if not args.no_cpu_baseline and "prefill" in keep and "decode" in keep:
@@ -342,6 +401,7 @@ def main():
         "legs": out_legs,
         "roofline": roofline,
         "roofline_decode": roof_dec,
+        "roofline_conv": roof_conv,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
     }

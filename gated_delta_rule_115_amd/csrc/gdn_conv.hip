@@ -7,32 +7,16 @@
 //   y_t[c] = SiLU( sum_{j<K} taps[c][j] * x_{t-K+1+j}[c] ),   x_{<0} = 0
 //
 // Elementwise stencil, HBM-bound.  One thread owns 8 consecutive channels and
-// walks TT consecutive tokens, keeping the last K-1 input rows in registers,
-// so every input element is read from memory once per token run (plus a
-// K-1 row halo) and every output is written once with 16-byte accesses.
-// L2 groups (a head's channels) are consecutive lanes of one wave, reduced
-// with cross-lane shuffles.
+// walks a run of consecutive tokens, keeping the last K-1 input rows in
+// registers, so every input element is read from memory once per run (plus a
+// K-1 row halo) and every output is written once with 16-byte accesses.  The
+// run is taken in blocks of rows whose loads are all issued before any is
+// used, and the next block is loaded while the current one is computed.  L2 groups (a head's channels) are
+// consecutive lanes of one wave, reduced with cross-lane shuffles.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
-
-template <class TIn>
-__device__ __forceinline__ void load8(const TIn* p, float* f) {
-  if constexpr (sizeof(TIn) == 2) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (float)x[e];
-  } else {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[e] = a[e];
-      f[4 + e] = b[e];
-    }
-  }
-}
 
 template <class TIn>
 __device__ __forceinline__ void store8(TIn* p, const float* f) {
@@ -47,17 +31,62 @@ __device__ __forceinline__ void store8(TIn* p, const float* f) {
   }
 }
 
+// Raw 8-channel piece as loaded (bf16: one 16-byte load; f32: two).
+template <class TIn>
+struct Raw8 {
+  bf16x8 v;
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+};
+template <class TIn>
+__device__ __forceinline__ Raw8<TIn> load_raw8(const TIn* p) {
+  Raw8<TIn> r;
+  if constexpr (sizeof(TIn) == 2) {
+    r.v = *reinterpret_cast<const bf16x8*>(p);
+  } else {
+    r.a = *reinterpret_cast<const f32x4*>(p);
+    r.b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  return r;
+}
+template <class TIn>
+__device__ __forceinline__ void zero_raw8(Raw8<TIn>& r) {
+  if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.v[e] = (bf16)0.f;
+  } else {
+    r.a = zero4();
+    r.b = zero4();
+  }
+}
+template <class TIn>
+__device__ __forceinline__ float raw8_at(const Raw8<TIn>& r, int e) {
+  if constexpr (sizeof(TIn) == 2) {
+    return (float)r.v[e];
+  } else {
+    return e < 4 ? r.a[e] : r.b[e - 4];
+  }
+}
+
+constexpr int kConvThreads = 128;
+constexpr int kConvRun = 128;  // tokens per thread
+constexpr int kConvBlk = 8;    // tokens whose loads are in flight together
+
 template <class TIn, class TOut, int K>
-__global__ __launch_bounds__(256) void short_conv_silu_kernel(
+__global__ __launch_bounds__(kConvThreads) void short_conv_silu_kernel(
     const TIn* __restrict__ x, const float* __restrict__ taps,
-    TOut* __restrict__ y, int T, int Ch, int group, float eps, int TT) {
+    TOut* __restrict__ y, int T, int Ch, int group, float eps) {
   const int nvec = Ch / 8;
-  const int vi = blockIdx.x * 256 + threadIdx.x;  // channel vector index
+  const int vi = blockIdx.x * kConvThreads + threadIdx.x;  // channel vector index
   const bool active = vi < nvec;
   const int b = blockIdx.z;
-  const int tb = blockIdx.y * TT;
-  const int te = min(T, tb + TT);
+  const int tb = blockIdx.y * kConvRun;
+  const int te = min(T, tb + kConvRun);
   const int c0 = (active ? vi : 0) * 8;
+  const TIn* xb = x + (size_t)b * T * Ch + c0;
+  TOut* yb = y + (size_t)b * T * Ch + c0;
 
   float w[8][K];
 #pragma unroll
@@ -70,55 +99,80 @@ __global__ __launch_bounds__(256) void short_conv_silu_kernel(
 #pragma unroll
   for (int j = 0; j < K - 1; ++j) {
     const int ts = tb - (K - 1) + j;
-    if (active && ts >= 0)
-      load8(x + ((size_t)b * T + ts) * Ch + c0, hist[j]);
-    else
+    if (active && ts >= 0) {
+      const Raw8<TIn> r = load_raw8(xb + (size_t)ts * Ch);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hist[j][e] = raw8_at(r, e);
+    } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) hist[j][e] = 0.f;
+    }
   }
 
   const int gl = group / 8;  // lanes per L2 group (0 = no normalisation)
-  for (int t = tb; t < te; ++t) {
-    float cur[8], o[8];
-    if (active)
-      load8(x + ((size_t)b * T + t) * Ch + c0, cur);
-    else
+  // Rows of block t0 .. t0 + kConvBlk - 1 (zero past the run or when inactive).
+  auto fetch = [&](int t0, Raw8<TIn>* rows) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cur[e] = 0.f;
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float a = w[e][K - 1] * cur[e];
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) a += w[e][j] * hist[j][e];
-      o[e] = a / (1.f + __expf(-a));
-      ss += o[e] * o[e];
+    for (int u = 0; u < kConvBlk; ++u) {
+      if (active && t0 + u < te)
+        rows[u] = load_raw8(xb + (size_t)(t0 + u) * Ch);
+      else
+        zero_raw8(rows[u]);
     }
-    if (gl > 0) {
-      for (int m = 1; m < gl; m <<= 1) ss += __shfl_xor(ss, m);
-      const float inv = 1.f / (sqrtf(ss) + eps);
+  };
+  auto consume = [&](int t0, const Raw8<TIn>* rows) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] *= inv;
+    for (int u = 0; u < kConvBlk; ++u) {
+      const int t = t0 + u;
+      float cur[8], o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cur[e] = raw8_at(rows[u], e);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = w[e][K - 1] * cur[e];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) a += w[e][j] * hist[j][e];
+        o[e] = a * __builtin_amdgcn_rcpf(1.f + __expf(-a));  // hardware reciprocal
+        ss += o[e] * o[e];
+      }
+      if (gl > 0) {
+        for (int m = 1; m < gl; m <<= 1) ss += __shfl_xor(ss, m);
+        const float inv = __builtin_amdgcn_rcpf(sqrtf(ss) + eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= inv;
+      }
+      if (active && t < te) store8(yb + (size_t)t * Ch, o);
+#pragma unroll
+      for (int j = 0; j + 1 < K - 1; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hist[j][e] = hist[j + 1][e];
+      if (K > 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hist[K > 1 ? K - 2 : 0][e] = cur[e];
     }
-    if (active) store8(y + ((size_t)b * T + t) * Ch + c0, o);
-#pragma unroll
-    for (int j = 0; j + 1 < K - 1; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hist[j][e] = hist[j + 1][e];
-    if (K > 1)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hist[K > 1 ? K - 2 : 0][e] = cur[e];
+  };
+  // Two blocks in flight: block b + 1 is loaded before block b is consumed.
+  Raw8<TIn> ra[kConvBlk], rb[kConvBlk];
+  fetch(tb, ra);
+  for (int t0 = tb; t0 < te; t0 += 2 * kConvBlk) {
+    const int t1 = t0 + kConvBlk;
+    if (t1 < te) fetch(t1, rb);
+    consume(t0, ra);
+    if (t1 < te) {
+      if (t1 + kConvBlk < te) fetch(t1 + kConvBlk, ra);
+      consume(t1, rb);
+    }
   }
 }
 
 template <class TIn, class TOut, int K>
 static hipError_t launch_conv_t(const ConvArgs& p) {
-  const int TT = 64;
   const int nvec = p.Ch / 8;
-  dim3 grid((nvec + 255) / 256, (p.T + TT - 1) / TT, p.B);
-  hipLaunchKernelGGL((short_conv_silu_kernel<TIn, TOut, K>), grid, dim3(256), 0,
+  dim3 grid((nvec + kConvThreads - 1) / kConvThreads, (p.T + kConvRun - 1) / kConvRun, p.B);
+  hipLaunchKernelGGL((short_conv_silu_kernel<TIn, TOut, K>), grid, dim3(kConvThreads), 0,
                      (hipStream_t)p.stream, (const TIn*)p.x, p.taps, (TOut*)p.y, p.T,
-                     p.Ch, p.group, p.eps, TT);
+                     p.Ch, p.group, p.eps);
   return hipGetLastError();
 }
 

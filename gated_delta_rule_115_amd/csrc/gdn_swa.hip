@@ -7,28 +7,54 @@
 //
 // HBM-bound: every cached key and value of the (b, h) is streamed once.  One
 // work-group per (b, h); a group of D/8 lanes owns one key at a time (8
-// elements per lane, one 16-byte load for bf16), so a wave covers 64/(D/8)
-// keys per step and each lane group keeps its own running max / sum /
-// accumulator (online softmax, f32).  Groups are merged through LDS at the end.
+// elements per lane, one 16-byte load for bf16).  Each lane group takes 8 keys
+// per step, the groups of a wave reading consecutive keys, and the next step's
+// keys and values are loaded before the current step is consumed.  Each group
+// keeps its own running max / sum / accumulator (online softmax, f32, one
+// rescale per step); groups are merged through LDS at the end.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
+// Raw 8-element piece as loaded (bf16: one 16-byte load; f32: two).
 template <class TIn>
-__device__ __forceinline__ void ld8(const TIn* p, float* f) {
+struct Piece {
+  bf16x8 v;
+};
+template <>
+struct Piece<float> {
+  f32x4 a, b;
+};
+template <class TIn>
+__device__ __forceinline__ Piece<TIn> load_piece(const TIn* p) {
+  Piece<TIn> r;
   if constexpr (sizeof(TIn) == 2) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (float)x[e];
+    r.v = *reinterpret_cast<const bf16x8*>(p);
   } else {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    r.a = *reinterpret_cast<const f32x4*>(p);
+    r.b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  return r;
+}
+template <class TIn>
+__device__ __forceinline__ Piece<TIn> zero_piece() {
+  Piece<TIn> r;
+  if constexpr (sizeof(TIn) == 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[e] = a[e];
-      f[4 + e] = b[e];
-    }
+    for (int e = 0; e < 8; ++e) r.v[e] = (bf16)0.f;
+  } else {
+    r.a = zero4();
+    r.b = zero4();
+  }
+  return r;
+}
+template <class TIn>
+__device__ __forceinline__ float piece_at(const Piece<TIn>& r, int e) {
+  if constexpr (sizeof(TIn) == 2) {
+    return (float)r.v[e];
+  } else {
+    return e < 4 ? r.a[e] : r.b[e - 4];
   }
 }
 
@@ -49,9 +75,10 @@ __global__ __launch_bounds__(256) void swa_sink_decode_kernel(
     TIn* __restrict__ v_cache, const int* __restrict__ n_tokens, int H,
     int n_sink, int window, float sm_scale, int accumulate, TOut* __restrict__ out) {
   constexpr int LPK = D / 8;             // lanes per key
-  constexpr int KPW = kWave / LPK;       // keys per wave per step
+  constexpr int KPW = kWave / LPK;       // keys per wave per load
   constexpr int NG = 4 * KPW;            // lane groups per work-group
-  constexpr int UNR = 4;                 // keys per lane group per step
+  constexpr int UNR = 8;                 // keys per lane group per step
+  constexpr int STEP = NG * UNR;         // keys per step
 
   __shared__ float gm[NG], gs[NG];
   __shared__ float gacc[NG][D + 4];
@@ -81,57 +108,82 @@ __global__ __launch_bounds__(256) void swa_sink_decode_kernel(
   }
 
   float qf[8];
-  ld8(q + (size_t)bh * D + sub * 8, qf);
+  {
+    const Piece<TIn> qp = load_piece(q + (size_t)bh * D + sub * 8);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qf[e] *= sm_scale;
+    for (int e = 0; e < 8; ++e) qf[e] = piece_at(qp, e) * sm_scale;
+  }
+
+  // Valid slots are [0, n_s) and [n_sink, n_sink + n_w): position j in
+  // [0, n_valid) -> slot(j).  Step s, piece u of group g: j = s STEP + u NG + g,
+  // so the groups of a wave read consecutive keys.
+  Piece<TIn> kr[2][UNR], vr[2][UNR];
+  auto fetch = [&](int st, Piece<TIn>* kk, Piece<TIn>* vv) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int j = st * STEP + u * NG + grp;
+      if (j < n_valid) {
+        const int slot = (j < n_s) ? j : n_sink + (j - n_s);
+        const TIn* kp;
+        const TIn* vp;
+        if (have_new && slot == cur) {
+          kp = k_new + (size_t)bh * D;
+          vp = v_new + (size_t)bh * D;
+        } else {
+          kp = k_cache + cbase + (size_t)slot * D;
+          vp = v_cache + cbase + (size_t)slot * D;
+        }
+        kk[u] = load_piece(kp + sub * 8);
+        vv[u] = load_piece(vp + sub * 8);
+      } else {
+        kk[u] = zero_piece<TIn>();  // weight 0 below; must not hold NaN
+        vv[u] = zero_piece<TIn>();
+      }
+    }
+  };
 
   float m = -INFINITY, s = 0.f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-
-  // Valid slots are [0, n_s) and [n_sink, n_sink + n_w): enumerate as j in
-  // [0, n_valid) -> slot(j).
-  for (int j0 = grp * UNR; j0 < n_valid; j0 += NG * UNR) {
-    float kf[UNR][8], vf[UNR][8];
-    bool ok[UNR];
+  auto consume = [&](int st, const Piece<TIn>* kk, const Piece<TIn>* vv) {
+    float z[UNR];
+    float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int j = j0 + u;
-      ok[u] = j < n_valid;
-      const int slot = (j < n_s) ? j : n_sink + (j - n_s);
-      const TIn* kp;
-      const TIn* vp;
-      if (have_new && slot == cur) {
-        kp = k_new + (size_t)bh * D;
-        vp = v_new + (size_t)bh * D;
-      } else {
-        kp = k_cache + cbase + (size_t)slot * D;
-        vp = v_cache + cbase + (size_t)slot * D;
-      }
-      if (ok[u]) {
-        ld8(kp + sub * 8, kf[u]);
-        ld8(vp + sub * 8, vf[u]);
-      } else {
+      float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kf[u][e] = vf[u][e] = 0.f;
-      }
+      for (int e = 0; e < 8; ++e) d += qf[e] * piece_at(kk[u], e);
+#pragma unroll
+      for (int off = 1; off < LPK; off <<= 1) d += __shfl_xor(d, off);
+      const bool ok = st * STEP + u * NG + grp < n_valid;
+      z[u] = ok ? d : -INFINITY;
+      mx = fmaxf(mx, z[u]);
     }
+    if (mx == -INFINITY) return;  // no valid key for this group in this step
+    const float mn = fmaxf(m, mx);
+    const float corr = __expf(m - mn);
+    s *= corr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= corr;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      float z = 0.f;
+      const float pr = __expf(z[u] - mn);  // 0 for the invalid pieces
+      s += pr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z += qf[e] * kf[u][e];
-#pragma unroll
-      for (int off = 1; off < LPK; off <<= 1) z += __shfl_xor(z, off);
-      if (ok[u]) {
-        const float mn = fmaxf(m, z);
-        const float corr = __expf(m - mn);
-        const float p = __expf(z - mn);
-        s = s * corr + p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = acc[e] * corr + p * vf[u][e];
-        m = mn;
-      }
+      for (int e = 0; e < 8; ++e) acc[e] += pr * piece_at(vv[u], e);
+    }
+    m = mn;
+  };
+
+  // Two steps in flight: step s + 1 is loaded before step s is consumed.
+  const int nsteps = (n_valid + STEP - 1) / STEP;
+  if (nsteps > 0) fetch(0, kr[0], vr[0]);
+  for (int st = 0; st < nsteps; st += 2) {
+    if (st + 1 < nsteps) fetch(st + 1, kr[1], vr[1]);
+    consume(st, kr[0], vr[0]);
+    if (st + 1 < nsteps) {
+      if (st + 2 < nsteps) fetch(st + 2, kr[0], vr[0]);
+      consume(st + 1, kr[1], vr[1]);
     }
   }
 
