@@ -46,7 +46,10 @@
 //                     eight MFMA accumulator tiles for the whole sequence.
 //   OUT (waves 5, 6)  chunk i - 3: Q rows of two block rows (own global loads,
 //                     f16), their Q K^T blocks -> P; chunk i - 4: Q S, P U^ and
-//                     the output rows.
+//                     the output rows, staged in LDS; wave 2 (KK) stores them
+//                     at iteration i + 1.  (Vector-memory counters count stores
+//                     too, so a wave that waits for its loads would otherwise
+//                     also wait for its earlier stores.)
 //
 // Operand layouts.  A 16x16 MFMA result is held by lane l as rows 4 (l/16) ..
 // +3 of column l % 16 (accumulator layout, written D(M)).  The A-operand
@@ -75,6 +78,15 @@ constexpr int FDK = 128;        // key dimension
 constexpr int FLD = FDK + 8;    // f16 row stride of the K tile (272 B)
 constexpr int NTHR = 512;
 constexpr float kWideRange = 10.f;  // log-gate range above which gates are per element
+// Scaled value slice in LDS: element (token t, column n) of row tile rt sits at
+// rt * VRT + n * VCS + (t % 16).  The padding makes both the per-token writes
+// (64 lanes, one column) and the 16-byte reads of 4 consecutive tokens of one
+// column (accumulator layout) free of bank conflicts.
+constexpr int VCS = 20;            // column stride (floats)
+constexpr int VRT = 16 * VCS + 16; // row-tile stride (floats)
+// Output staging [column][token] with column stride OCS: the 16-byte writes of
+// 4 tokens of one column and the per-token reads are free of bank conflicts.
+constexpr int OCS = FC + 4;
 
 typedef _Float16 h16;
 typedef h16 h16x4 __attribute__((ext_vector_type(4)));
@@ -100,7 +112,8 @@ struct GateSlot {
 
 struct __align__(16) Smem {
   h16 K[4][FC * FLD];     // K tiles (f16, permuted key columns), slot = chunk & 3
-  f32x4 Vt[4][4][64];     // a * V, accumulator layout [row tile][lane], slot = chunk & 3
+  float Vt[4][4 * VRT];   // a * V: [row tile][column][token] (see VRT), slot = chunk & 3
+  float Ost[2][16 * OCS]; // output rows of a chunk, f32 [column][token], slot = chunk & 1
   h16x4 Ga[2][6][64];     // A blocks 10, 20, 21, 30, 31, 32 as A operands, slot = chunk & 1
   h16x4 Td[2][4][64];     // D(T00), D(T00^T), D(T11), D(T11^T)
   f32x4 Ld[2][4][64];     // D(L2), D(L2^T), D(L3), D(L3^T): diagonal blocks 2, 3 of A
@@ -125,14 +138,17 @@ __device__ __forceinline__ h16x4 cvt4(f32x4 x) {
   for (int i = 0; i < 4; ++i) r[i] = (h16)x[i];
   return r;
 }
+// bf16 -> f16 of four values.  Every bf16 value in the f16 normal range is
+// exactly representable, so the packed round-toward-zero conversion is exact
+// there (and only flushes magnitudes below 2^-14 towards zero).
+__device__ __forceinline__ h16x4 bf16_to_h4(bf16x4 x) {
+  typedef h16 h16x2 __attribute__((ext_vector_type(2)));
+  const h16x2 a = __builtin_bit_cast(h16x2, __builtin_amdgcn_cvt_pkrtz((float)x[0], (float)x[1]));
+  const h16x2 b = __builtin_bit_cast(h16x2, __builtin_amdgcn_cvt_pkrtz((float)x[2], (float)x[3]));
+  return h16x4{a[0], a[1], b[0], b[1]};
+}
 __device__ __forceinline__ h16x8 cvt8(bf16x4 lo, bf16x4 hi) {
-  h16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (h16)(float)lo[i];
-    r[4 + i] = (h16)(float)hi[i];
-  }
-  return r;
+  return cat8(bf16_to_h4(lo), bf16_to_h4(hi));
 }
 __device__ __forceinline__ f32x4 ldf4(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
@@ -253,11 +269,8 @@ __device__ void role_commit(Smem& sm, const Args& a, int l) {
       h16x4 kh[8][2];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kh[u][0][e] = (h16)(float)raw[p][u][e];
-          kh[u][1][e] = (h16)(float)raw[p][u][4 + e];
-        }
+        kh[u][0] = bf16_to_h4(__builtin_shufflevector(raw[p][u], raw[p][u], 0, 1, 2, 3));
+        kh[u][1] = bf16_to_h4(__builtin_shufflevector(raw[p][u], raw[p][u], 4, 5, 6, 7));
       }
       if (it + 2 < a.NC) load(it + 2, raw[p]);
 #pragma unroll
@@ -281,7 +294,7 @@ __device__ void role_commit(Smem& sm, const Args& a, int l) {
 // ---------------------------------------------------------------- KK --------
 // Block rows RA < RB of chunk i - 1: W 0 -> rows 0, 3; W 1 -> rows 1, 2.
 // Gram tile (R, C) = mfma(K_C, K_R) is the A-operand fragment of (K K^T)_RC.
-template <int W>
+template <int W, class TOut>
 __device__ void role_kk(Smem& sm, const Args& a, int l) {
   constexpr int RA = W == 0 ? 0 : 1;
   constexpr int RB = W == 0 ? 3 : 2;
@@ -377,6 +390,31 @@ __device__ void role_kk(Smem& sm, const Args& a, int l) {
         inv16<true, true>(L1, LT1, lr, lq, T11, TT11);
         sm.Td[s][2][l] = cvt4(T11);
         sm.Td[s][3][l] = cvt4(TT11);
+      }
+    }
+    // W 1 also writes the output rows of chunk i - 5 (staged by the output
+    // waves): this wave issues no global loads, so nothing ever waits for the
+    // stores to complete.  Lane = token.
+    const int cs = it - 5;
+    if (W == 1 && cs >= 0 && cs < a.NC && cs * FC + l < a.T) {
+      const float* ob = &sm.Ost[cs & 1][l];
+      float o[16];
+#pragma unroll
+      for (int n = 0; n < 16; ++n) o[n] = ob[n * OCS];
+      TOut* dst = reinterpret_cast<TOut*>(a.out) + (size_t)(cs * FC + l) * a.v_tok;
+      if constexpr (sizeof(TOut) == 2) {
+        bf16x8 v0, v1;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          v0[n] = (bf16)o[n];
+          v1[n] = (bf16)o[8 + n];
+        }
+        *reinterpret_cast<bf16x8*>(dst) = v0;
+        *reinterpret_cast<bf16x8*>(dst + 8) = v1;
+      } else {
+#pragma unroll
+        for (int n = 0; n < 16; n += 4)
+          *reinterpret_cast<f32x4*>(dst + n) = f32x4{o[n], o[n + 1], o[n + 2], o[n + 3]};
       }
     }
     lds_barrier();
@@ -476,12 +514,10 @@ __device__ void role_lv(Smem& sm, const Args& a, int l) {
         gs.cS = wide ? 1.f : __expf(gl - gm);
         gs.wide = wide ? 1 : 0;
       }
-      // a * V in accumulator layout: token l, column n -> tile l / 16,
-      // lane 16 ((l % 16) / 4) + n, element l % 4.
-      float* vb = reinterpret_cast<float*>(&sm.Vt[it & 3][l >> 4][0]);
-      const int lb = ((l & 15) >> 2) * 16, e = l & 3;
+      // a * V: token l, column n -> (l / 16) * VRT + n * VCS + l % 16.
+      float* vb = &sm.Vt[it & 3][(l >> 4) * VRT + (l & 15)];
 #pragma unroll
-      for (int n = 0; n < 16; ++n) vb[(lb + n) * 4 + e] = av * vf[n];
+      for (int n = 0; n < 16; ++n) vb[n * VCS] = av * vf[n];
     }
     lds_barrier();
   };
@@ -535,7 +571,7 @@ __device__ void role_chain(Smem& sm, const Args& a, int l) {
         for (int j = 0; j < 4; ++j)
           X = mfma32(ld8(Kb + (16 * rt + lr) * FLD + 32 * j + 8 * lq), sb[j], X);
         const f32x4 bv = ldf4(&gs.b[16 * rt + 4 * lq]);
-        const f32x4 Vv = sm.Vt[c & 3][rt][l];
+        const f32x4 Vv = ldf4(&sm.Vt[c & 3][rt * VRT + lr * VCS + 4 * lq]);
         y16[rt] = cvt4(Vv - bv * X);
       }
       h16x8 ktr[8][2];
@@ -602,7 +638,6 @@ __device__ void role_out(Smem& sm, const Args& a, int l) {
   constexpr int RA = W == 0 ? 0 : 1;
   constexpr int RB = W == 0 ? 3 : 2;
   const int lr = l & 15, lq = l >> 4;
-  TOut* oh = reinterpret_cast<TOut*>(a.out);
 
   bf16x4 raw[2][2][4][2];  // [chunk parity][block][k step][half]
   h16x8 qh[2][2][4];       // [chunk parity][block][k step]
@@ -698,11 +733,10 @@ __device__ void role_out(Smem& sm, const Args& a, int l) {
         if (R >= 2) PU = mfma32(cat8(pf[pp][b][2], pf[pp][b][3]), uhi, PU);
         const f32x4 og = ldf4(&gs.og[16 * R + 4 * lq]);
         const f32x4 of = ldf4(&gs.of[16 * R + 4 * lq]);
+        f32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = cp * FC + 16 * R + 4 * lq + i;
-          if (t < a.T) oh[(size_t)t * a.v_tok + lr] = from_f32<TOut>(og[i] * QS[i] + of[i] * PU[i]);
-        }
+        for (int i = 0; i < 4; ++i) o[i] = og[i] * QS[i] + of[i] * PU[i];
+        *reinterpret_cast<f32x4*>(&sm.Ost[cp & 1][lr * OCS + 16 * R + 4 * lq]) = o;
       }
     }
     lds_barrier();
@@ -744,20 +778,20 @@ __global__ __launch_bounds__(NTHR) void prefill_fused_kernel(
   a.T = T;
   a.H = H;
   a.NC = NC;
-  // Chunk c's last step (its output rows) runs at iteration c + 4; the count is
-  // rounded up to even for the two-way unrolled loops.
-  a.NIT = (NC + 4 + 1) & ~1;
+  // Chunk c's last step (the store of its output rows) runs at iteration c + 5;
+  // the count is rounded up to even for the two-way unrolled loops.
+  a.NIT = (NC + 5 + 1) & ~1;
   a.DV = DV;
   a.scale = scale;
 
   switch (wave) {
     case 0: role_chain(sm, a, l); break;
-    case 1: role_kk<0>(sm, a, l); break;
-    case 2: role_kk<1>(sm, a, l); break;
-    case 3: role_lv(sm, a, l); break;
-    case 4: role_commit<0>(sm, a, l); break;
-    case 5: role_out<0, TOut>(sm, a, l); break;
-    case 6: role_out<1, TOut>(sm, a, l); break;
+    case 1: role_kk<0, TOut>(sm, a, l); break;
+    case 2: role_out<0, TOut>(sm, a, l); break;
+    case 3: role_out<1, TOut>(sm, a, l); break;
+    case 4: role_lv(sm, a, l); break;
+    case 5: role_kk<1, TOut>(sm, a, l); break;
+    case 6: role_commit<0>(sm, a, l); break;
     default: role_commit<1>(sm, a, l); break;
   }
 }
