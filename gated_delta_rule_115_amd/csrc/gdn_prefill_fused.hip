@@ -245,8 +245,7 @@ struct Args {
 // K rows 32 W .. 32 W + 31 of chunk i -> LDS (f16, permuted columns).  Each
 // lane moves 8 pieces of 8 consecutive keys; chunk i + 2 is loaded into the
 // registers just freed.
-template <int W>
-__device__ void role_commit(Smem& sm, const Args& a, int l) {
+__device__ void role_commit(Smem& sm, const Args& a, int l, int W) {
   bf16x8 raw[2][8];
   auto load = [&](int c, bf16x8* r) {
     const int t0 = c * FC;
@@ -791,8 +790,7 @@ __global__ __launch_bounds__(NTHR) void prefill_fused_kernel(
     case 3: role_out<1, TOut>(sm, a, l); break;
     case 4: role_lv(sm, a, l); break;
     case 5: role_kk<1, TOut>(sm, a, l); break;
-    case 6: role_commit<0>(sm, a, l); break;
-    default: role_commit<1>(sm, a, l); break;
+    default: role_commit(sm, a, l, wave - 6); break;
   }
 }
 
