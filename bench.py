@@ -75,8 +75,25 @@ def decode_swa_bytes(d, n_slots, esize=2):
 # SHA-1 of the kernel source they were taken on: a kernel whose source has
 # changed since reports traffic null.  Each figure is copied from the profile
 # summary named in "profile".
+PROFILE = "profiles/gdn_kernels_bench_workloads.md"
 COUNTERS = {
-    # kernel: dict(src=..., sha1=..., fetch_kib=..., write_kib=..., profile=...)
+    "prefill_fused_kernel<bf16>": dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_prefill_fused.hip",
+        sha1="cfa47af2d72fd6cb289304951f12df8723369cc6",
+        fetch_kib=426312, write_kib=264192, profile=PROFILE),
+    "decode_step_kernel<bf16,bf16,128,128>": dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
+        sha1="b476cc39e7e5f69ceb396d81745208125716902b",
+        fetch_kib=265794, write_kib=526336, profile=PROFILE),
+    "swa_sink_decode_kernel<bf16,bf16,128>": dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_swa.hip",
+        sha1="f2d0a8fbd56e119c1501157da94f01005e2a3f95",
+        fetch_kib=1061017, write_kib=6144, profile=PROFILE),
+    # the three projections of the leg together
+    "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
+        sha1="dc58eef25b3e6bd35e4799338aa19dcd478fa1df",
+        fetch_kib=168117 + 168135 + 168149, write_kib=3 * 327680, profile=PROFILE),
 }
 READ_FACTOR, WRITE_FACTOR = 2.00, 1.00
 

@@ -33,20 +33,20 @@
 // Pipeline.  Every wave runs the same loop of iterations, one barrier each;
 // each role works on a different chunk and hands results on through LDS ring
 // slots (no role waits for another inside an iteration).  At iteration i:
-//   CM  (waves 4, 7)  chunk i: K tile -> LDS as f16 (key columns permuted);
+//   CM  (waves 6, 7)  chunk i: K tile -> LDS as f16 (key columns permuted);
 //                     global loads for chunk i + 2
-//   KK  (waves 1, 2)  chunk i - 1: Gram blocks of K K^T for two block rows,
+//   KK  (waves 1, 5)  chunk i - 1: Gram blocks of K K^T for two block rows,
 //                     scaled into A; diagonal blocks 0, 1 of Tm inverted as
 //                     (I + L)^-1 = (I + L^8)(I + L^4)(I + L^2)(I - L)
-//   LV  (wave 3)      chunk i - 2: diagonal blocks 2, 3 of Tm, then the
+//   LV  (wave 4)      chunk i - 2: diagonal blocks 2, 3 of Tm, then the
 //                     off-diagonal blocks (block forward substitution);
 //                     chunk i: gate tables and the scaled V slice
 //   CH  (wave 0)      chunk i - 3: the recurrence for this slice: X = K S,
 //                     Y~, U^ = T Y~, S update.  S (128 x 16, f32) lives in
 //                     eight MFMA accumulator tiles for the whole sequence.
-//   OUT (waves 5, 6)  chunk i - 3: Q rows of two block rows (own global loads,
+//   OUT (waves 2, 3)  chunk i - 3: Q rows of two block rows (own global loads,
 //                     f16), their Q K^T blocks -> P; chunk i - 4: Q S, P U^ and
-//                     the output rows, staged in LDS; wave 2 (KK) stores them
+//                     the output rows, staged in LDS; wave 5 (KK) stores them
 //                     at iteration i + 1.  (Vector-memory counters count stores
 //                     too, so a wave that waits for its loads would otherwise
 //                     also wait for its earlier stores.)
