@@ -1,0 +1,168 @@
+// f16 MFMA building blocks of the chunked prefill kernels (gfx950).
+//
+// Operand layouts.  A 16x16 MFMA result is held by lane l = 16 q + r as rows
+// 4 q .. 4 q + 3 of column r (accumulator layout, written D(M)).  The
+// A-operand fragment of M is D(M^T), the B-operand fragment is D(M), so
+// D(M N) = mfma(D(M^T), D(N)) and D((M N)^T) = mfma(D(N), D(M^T)).  A 32-deep
+// product (v_mfma_f32_16x16x32_f16) takes 8 contraction values per lane; which
+// logical index sits in which lane slot is free as long as both operands
+// agree, so two stacked accumulator tiles can serve as one operand.
+#pragma once
+
+#include <type_traits>
+
+#include "gdn_device.h"
+
+namespace gdn {
+namespace f16ops {
+
+typedef _Float16 h16;
+typedef h16 h16x4 __attribute__((ext_vector_type(4)));
+typedef h16 h16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+__device__ __forceinline__ f32x4 mfma32(h16x8 a, h16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(h16x4 a, h16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ h16x8 cat8(h16x4 lo, h16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ h16x4 cvt4(f32x4 x) {
+  h16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (h16)x[i];
+  return r;
+}
+// bf16 -> f16 of four values.  Every bf16 value in the f16 normal range is
+// exactly representable, so the packed round-toward-zero conversion is exact
+// there (and only flushes magnitudes below 2^-14 towards zero).
+__device__ __forceinline__ h16x4 bf16_to_h4(bf16x4 x) {
+  typedef h16 h16x2 __attribute__((ext_vector_type(2)));
+  const h16x2 a = __builtin_bit_cast(h16x2, __builtin_amdgcn_cvt_pkrtz((float)x[0], (float)x[1]));
+  const h16x2 b = __builtin_bit_cast(h16x2, __builtin_amdgcn_cvt_pkrtz((float)x[2], (float)x[3]));
+  return h16x4{a[0], a[1], b[0], b[1]};
+}
+__device__ __forceinline__ h16x8 cvt8(bf16x4 lo, bf16x4 hi) {
+  return cat8(bf16_to_h4(lo), bf16_to_h4(hi));
+}
+__device__ __forceinline__ h16x8 bf16x8_to_h8(bf16x8 x) {
+  return cvt8(__builtin_shufflevector(x, x, 0, 1, 2, 3), __builtin_shufflevector(x, x, 4, 5, 6, 7));
+}
+__device__ __forceinline__ f32x4 ldf4(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ h16x8 ld8(const h16* p) {
+  return *reinterpret_cast<const h16x8*>(p);
+}
+// LDS transpose read: within each group of 16 lanes, lane i receives element
+// (i & 3) of the 8-byte chunks addressed by lanes (i >> 2) + 4k, k = 0..3.
+__device__ __forceinline__ h16x4 ld_tr(const h16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(h16x4, r);
+}
+// Work-group barrier ordering LDS only.  Waves exchange data through LDS
+// alone, so global loads issued for later chunks stay in flight across it
+// (a full __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (lanes read as zero where the shifted source is absent).
+__device__ __forceinline__ float wave_incl_sum(float x) {
+  const int z = 0;
+  auto sh = [&](float v, auto ctrl) -> float {
+    constexpr int C = decltype(ctrl)::value;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, v), C, 0xf, 0xf, false));
+  };
+  x += sh(x, ic<0x111>());  // row_shr:1
+  x += sh(x, ic<0x112>());  // row_shr:2
+  x += sh(x, ic<0x114>());  // row_shr:4
+  x += sh(x, ic<0x118>());  // row_shr:8
+  // row_bcast:15 adds lane 15 of each row to the next row; row_bcast:31 adds
+  // lane 31 to rows 2 and 3.
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+__device__ __forceinline__ f32x4 ident4(int lr, int lq) {
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (4 * lq + i == lr) ? 1.f : 0.f;
+  return r;
+}
+
+// (I + L)^-1 for a strictly lower 16x16 L (L^16 = 0), from D(L) and D(L^T):
+// T = D(Tm), TT = D(Tm^T), each as (I + L^8)(I + L^4)(I + L^2)(I - L) applied
+// from the left to the running product.
+template <bool NT, bool NTT>
+__device__ __forceinline__ void inv16(f32x4 Lf, f32x4 LTf, int lr, int lq, f32x4& T, f32x4& TT) {
+  const h16x4 lo = cvt4(Lf), lt = cvt4(LTf);
+  const h16x4 l2 = cvt4(mfma16(lt, lo, zero4()));    // D(L^2)
+  const h16x4 l2t = cvt4(mfma16(lo, lt, zero4()));   // D((L^2)^T)
+  const h16x4 l4 = cvt4(mfma16(l2t, l2, zero4()));   // D(L^4)
+  const h16x4 l4t = cvt4(mfma16(l2, l2t, zero4()));  // D((L^4)^T)
+  const f32x4 id = ident4(lr, lq);
+  if (NT) {
+    const h16x4 l8t = cvt4(mfma16(l4, l4t, zero4()));  // D((L^8)^T)
+    f32x4 X = id - Lf;
+    X = mfma16(l2t, cvt4(X), X);
+    X = mfma16(l4t, cvt4(X), X);
+    T = mfma16(l8t, cvt4(X), X);
+  }
+  if (NTT) {
+    const h16x4 l8 = cvt4(mfma16(l4t, l4, zero4()));  // D(L^8)
+    f32x4 X = id - LTf;
+    X = mfma16(l2, cvt4(X), X);
+    X = mfma16(l4, cvt4(X), X);
+    TT = mfma16(l8, cvt4(X), X);
+  }
+}
+
+// Off-diagonal blocks of the unit lower triangular Tm = (I + A)^-1 of a
+// 64-token chunk by block forward substitution, from the A-operand fragments
+// of the strictly lower blocks of A and the diagonal inverses:
+//   T10 = -T11 A10 T00,  T32 = -T33 A32 T22,
+//   T2j = -T22 Z2j,  T3j = -(T32 Z2j + T33 Z3j),  Zmj = Am0 T0j + Am1 T1j.
+// ga = {A10, A20, A21, A30, A31, A32}; d = {D(T00), D(T00^T), D(T11),
+// D(T11^T), D(T22), D(T22^T), D(T33^T)}.  Out: the six A operands of Tm for
+// the 64 x 16 product Tm Y with Y as two 32-row operands (row tile, step):
+//   tc[0] = (0,0) [T00 | 0]    tc[1] = (1,0) [T10 | T11]
+//   tc[2] = (2,0) [T20 | T21]  tc[3] = (2,1) [T22 | 0]
+//   tc[4] = (3,0) [T30 | T31]  tc[5] = (3,1) [T32 | T33]
+__device__ __forceinline__ void tm_offdiag(const h16x4 ga[6], const h16x4 d[7], h16x8 tc[6]) {
+  const h16x4 d00 = d[0], d00t = d[1], d11 = d[2], d11t = d[3];
+  const h16x4 d22 = d[4], d22t = d[5], d33t = d[6];
+  const h16x4 x10 = cvt4(mfma16(ga[0], d00, zero4()));   // D(A10 T00)
+  const h16x4 t10t = cvt4(-mfma16(x10, d11t, zero4()));  // D(T10^T)
+  const h16x4 t10 = cvt4(-mfma16(d11t, x10, zero4()));   // D(T10)
+  const h16x4 x32 = cvt4(mfma16(ga[5], d22, zero4()));   // D(A32 T22)
+  const h16x4 t32t = cvt4(-mfma16(x32, d33t, zero4()));  // D(T32^T)
+  const h16x8 d0010 = cat8(d00, t10);
+  const h16x4 z20 = cvt4(mfma32(cat8(ga[1], ga[2]), d0010, zero4()));
+  const h16x4 z30 = cvt4(mfma32(cat8(ga[3], ga[4]), d0010, zero4()));
+  const h16x4 z21 = cvt4(mfma16(ga[2], d11, zero4()));
+  const h16x4 z31 = cvt4(mfma16(ga[4], d11, zero4()));
+  const h16x4 t20t = cvt4(-mfma16(z20, d22t, zero4()));
+  const h16x4 t21t = cvt4(-mfma16(z21, d22t, zero4()));
+  const h16x8 t3233 = cat8(t32t, d33t);
+  const h16x4 t30t = cvt4(-mfma32(cat8(z20, z30), t3233, zero4()));
+  const h16x4 t31t = cvt4(-mfma32(cat8(z21, z31), t3233, zero4()));
+  const h16x4 zz = {0, 0, 0, 0};
+  tc[0] = cat8(d00t, zz);
+  tc[1] = cat8(t10t, d11t);
+  tc[2] = cat8(t20t, t21t);
+  tc[3] = cat8(d22t, zz);
+  tc[4] = cat8(t30t, t31t);
+  tc[5] = t3233;
+}
+
+}  // namespace f16ops
+}  // namespace gdn

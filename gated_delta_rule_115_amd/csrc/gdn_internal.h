@@ -66,6 +66,13 @@ size_t prefill_record_bytes(int chunk, bool bf16);
 size_t prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, bool bf16);
 bool prefill_fused_supported(const PrefillArgs& p);
 hipError_t launch_prefill_fused(const PrefillArgs& p);
+// Per-head kernels: bf16 inputs, Dk = Dv = 128, chunk 64, T > 0.  Long
+// sequences of few heads are split into P segments of L chunks (P = 1: one
+// pass, no workspace).
+bool prefill_head_supported(const PrefillArgs& p);
+void prefill_head_segments(int B, int T, int H, int* P, int* L);
+size_t prefill_head_workspace_bytes(int B, int T, int H);
+hipError_t launch_prefill_head(const PrefillArgs& p);
 
 hipError_t launch_decode(const DecodeArgs& p);
 hipError_t launch_prefill(const PrefillArgs& p);

@@ -48,6 +48,7 @@ size_t prefill_record_bytes(int C, bool bf16) {
 size_t prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C, bool bf16) {
   PrefillArgs p{};
   p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = C; p.bf16 = bf16;
+  if (prefill_head_supported(p)) return prefill_head_workspace_bytes(B, T, H);
   if (prefill_fused_supported(p)) return 0;
   const size_t nc = ((size_t)T + C - 1) / C;
   return (size_t)B * H * nc * prefill_record_bytes(C, bf16);
@@ -647,6 +648,7 @@ static hipError_t launch_prefill_c(const PrefillArgs& p) {
 
 hipError_t launch_prefill(const PrefillArgs& p) {
   if (p.B * p.H == 0) return hipSuccess;
+  if (prefill_head_supported(p)) return launch_prefill_head(p);
   if (prefill_fused_supported(p)) return launch_prefill_fused(p);
   return p.bf16 ? launch_prefill_c<bf16>(p) : launch_prefill_c<float>(p);
 }

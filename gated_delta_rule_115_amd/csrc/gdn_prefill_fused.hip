@@ -65,13 +65,13 @@
 //
 // Precision: bf16 inputs convert to f16 exactly (unit-scale values); products
 // take f16 operands with f32 accumulation; S is f32.
-#include <type_traits>
-
-#include "gdn_device.h"
+#include "gdn_f16ops.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
+
+using namespace f16ops;
 
 constexpr int FC = 64;          // tokens per chunk
 constexpr int FDK = 128;        // key dimension
@@ -87,13 +87,6 @@ constexpr int VRT = 16 * VCS + 16; // row-tile stride (floats)
 // Output staging [column][token] with column stride OCS: the 16-byte writes of
 // 4 tokens of one column and the per-token reads are free of bank conflicts.
 constexpr int OCS = FC + 4;
-
-typedef _Float16 h16;
-typedef h16 h16x4 __attribute__((ext_vector_type(4)));
-typedef h16 h16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-template <int V>
-using ic = std::integral_constant<int, V>;
 
 // Per-chunk gate tables (one slot per chunk in flight).
 struct GateSlot {
@@ -123,108 +116,9 @@ struct __align__(16) Smem {
   GateSlot g[5];          // slot = chunk % 5
 };
 
-__device__ __forceinline__ f32x4 mfma32(h16x8 a, h16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(h16x4 a, h16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ h16x8 cat8(h16x4 lo, h16x4 hi) {
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ h16x4 cvt4(f32x4 x) {
-  h16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (h16)x[i];
-  return r;
-}
-// bf16 -> f16 of four values.  Every bf16 value in the f16 normal range is
-// exactly representable, so the packed round-toward-zero conversion is exact
-// there (and only flushes magnitudes below 2^-14 towards zero).
-__device__ __forceinline__ h16x4 bf16_to_h4(bf16x4 x) {
-  typedef h16 h16x2 __attribute__((ext_vector_type(2)));
-  const h16x2 a = __builtin_bit_cast(h16x2, __builtin_amdgcn_cvt_pkrtz((float)x[0], (float)x[1]));
-  const h16x2 b = __builtin_bit_cast(h16x2, __builtin_amdgcn_cvt_pkrtz((float)x[2], (float)x[3]));
-  return h16x4{a[0], a[1], b[0], b[1]};
-}
-__device__ __forceinline__ h16x8 cvt8(bf16x4 lo, bf16x4 hi) {
-  return cat8(bf16_to_h4(lo), bf16_to_h4(hi));
-}
-__device__ __forceinline__ f32x4 ldf4(const float* p) {
-  return *reinterpret_cast<const f32x4*>(p);
-}
-__device__ __forceinline__ h16x8 ld8(const h16* p) {
-  return *reinterpret_cast<const h16x8*>(p);
-}
-// LDS transpose read: within each group of 16 lanes, lane i receives element
-// (i & 3) of the 8-byte chunks addressed by lanes (i >> 2) + 4k, k = 0..3.
-__device__ __forceinline__ h16x4 ld_tr(const h16* p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(h16x4, r);
-}
 // Physical column of logical key column c in the K tile.
 __device__ __forceinline__ int perm_col(int c) {
   return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
-}
-// Work-group barrier ordering LDS only.  Waves exchange data through LDS
-// alone, so global loads issued for later chunks stay in flight across it
-// (a full __syncthreads would wait for them).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
-// row broadcasts (lanes read as zero where the shifted source is absent).
-__device__ __forceinline__ float wave_incl_sum(float x) {
-  const int z = 0;
-  auto sh = [&](float v, auto ctrl) -> float {
-    constexpr int C = decltype(ctrl)::value;
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, v), C, 0xf, 0xf, false));
-  };
-  x += sh(x, ic<0x111>());  // row_shr:1
-  x += sh(x, ic<0x112>());  // row_shr:2
-  x += sh(x, ic<0x114>());  // row_shr:4
-  x += sh(x, ic<0x118>());  // row_shr:8
-  // row_bcast:15 adds lane 15 of each row to the next row; row_bcast:31 adds
-  // lane 31 to rows 2 and 3.
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
-  return x;
-}
-__device__ __forceinline__ f32x4 ident4(int lr, int lq) {
-  f32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (4 * lq + i == lr) ? 1.f : 0.f;
-  return r;
-}
-
-// (I + L)^-1 for a strictly lower 16x16 L (L^16 = 0), from D(L) and D(L^T):
-// T = D(Tm), TT = D(Tm^T), each as (I + L^8)(I + L^4)(I + L^2)(I - L) applied
-// from the left to the running product.
-template <bool NT, bool NTT>
-__device__ __forceinline__ void inv16(f32x4 Lf, f32x4 LTf, int lr, int lq, f32x4& T, f32x4& TT) {
-  const h16x4 lo = cvt4(Lf), lt = cvt4(LTf);
-  const h16x4 l2 = cvt4(mfma16(lt, lo, zero4()));    // D(L^2)
-  const h16x4 l2t = cvt4(mfma16(lo, lt, zero4()));   // D((L^2)^T)
-  const h16x4 l4 = cvt4(mfma16(l2t, l2, zero4()));   // D(L^4)
-  const h16x4 l4t = cvt4(mfma16(l2, l2t, zero4()));  // D((L^4)^T)
-  const f32x4 id = ident4(lr, lq);
-  if (NT) {
-    const h16x4 l8t = cvt4(mfma16(l4, l4t, zero4()));  // D((L^8)^T)
-    f32x4 X = id - Lf;
-    X = mfma16(l2t, cvt4(X), X);
-    X = mfma16(l4t, cvt4(X), X);
-    T = mfma16(l8t, cvt4(X), X);
-  }
-  if (NTT) {
-    const h16x4 l8 = cvt4(mfma16(l4t, l4, zero4()));  // D(L^8)
-    f32x4 X = id - LTf;
-    X = mfma16(l2, cvt4(X), X);
-    X = mfma16(l4, cvt4(X), X);
-    TT = mfma16(l8, cvt4(X), X);
-  }
 }
 
 struct Args {

@@ -1,0 +1,811 @@
+// Per-head chunked GDN prefill for gfx950: bf16 inputs, d_k = d_v = 128,
+// chunks of 64 tokens, one work-group per (batch, head).
+//
+// Method: "The Key to Going Linear: Analysis-Driven Transformer
+// Linearization", section 3.1.2 (S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1}
+// + beta_t k_t v_t^T, o_t = scale * S_t^T q_t), computed chunk by chunk with the
+// exact WY/UT rewrite.  Within a chunk (gam_r = cumulative log gate from the
+// chunk start, g_r = exp(gam_r), S entering the chunk):
+//   A_ri = beta_r exp(gam_r - gam_i) k_r.k_i  (i < r),   Tm = (I + A)^-1
+//   Y = diag(beta) (V - diag(g) K S),   U = Tm Y
+//   O = scale diag(g) Q S + Pm U,   Pm_ri = scale exp(gam_r - gam_i) q_r.k_i (i <= r)
+//   S <- g_C S + K^T diag(exp(gam_C - gam)) U
+// With the midpoint gam_m of the chunk's log-gate range and D = diag(exp(gam_m
+// - gam)), Tm = D^-1 T0 D with T0 = (I + A0)^-1, A0_ri = beta_r k_r.k_i, so the
+// gates reach only vectors:
+//   Y~ = av V - bx X,  av = beta exp(gam_m - gam),  bx = beta exp(gam_m)
+//   U^ = T0 Y~,  S <- g_C S + c_S K^T U^,  c_S = exp(gam_C - gam_m)
+//   O = og (Q S) + of (P0 U^),  og = scale g,  of = scale exp(gam - gam_m)
+// (P0 = lower(Q K^T)).  A chunk whose log-gate range exceeds kWide uses the
+// unfactored form (gate ratios per element, D = I, c_S = 1, U weighted by
+// exp(gam_C - gam) in the state update).
+//
+// The state is carried as S = sigma S~ with a per-chunk scalar sigma: the
+// update S~ <- (g_C sigma / c_S) S~ + K^T U^ then accumulates straight into
+// the MFMA tiles that hold S~ (no element-wise pass after the products), with
+// sigma <- c_S; X = K S = sigma K S~ and Q S = sigma Q S~ fold sigma into
+// bx and og.
+//
+// Work split.  The work-group has 8 waves; wave w keeps columns 16 w .. 16 w
+// + 15 of S~ (128 x 16, f32) in eight MFMA accumulator tiles for the whole
+// sequence and runs that slice's recurrence.  Everything that does not depend
+// on S -- gates, Gram products, the triangular inverse, Q K^T -- is computed
+// once per chunk and shared through LDS.  Iteration i has two phases, each
+// ended by a work-group barrier:
+//   phase 1  all:      X~ = K S~ and (Q S~)^T of chunk i - 2
+//            waves 0-3: diagonal block w of A for chunk i - 1, inverted as
+//                      (I + L)^-1 = (I + L^8)(I + L^4)(I + L^2)(I - L)
+//            waves 4-7: off-diagonal blocks of A (chunk i - 1) and the blocks
+//                      of P (chunk i - 2)
+//            all:      av V of chunk i - 2 -> LDS
+//   phase 2  all:      Y~, U^ = T0 Y~, S~ update, (P U^)^T and the output rows
+//                      of chunk i - 2
+//            wave 3:   off-diagonal blocks of Tm for chunk i - 1 (block
+//                      forward substitution)
+//            wave 6:   gate tables of chunk i
+//            all:      K of chunk i and Q of chunk i - 1 -> LDS as f16
+// Global loads run one to two iterations ahead of their use (K of chunk
+// i + 1, Q of chunk i, V of chunk i - 1 are issued in phase 1 of iteration i).
+//
+// Operand layouts: see gdn_f16ops.h.  Contractions over the key index use, in
+// each 32-key step j, lane group q = l / 16 for keys 32 j + 8 q .. + 7, so K
+// and Q fragments are single 16-byte LDS reads; S~ tile m therefore holds
+// key 32 (m / 2) + 8 (r / 4) + 4 (m % 2) + r % 4 in accumulator row r, so two
+// stacked tiles form the B operand directly.  K^T and (av V) fragments come
+// from LDS transpose reads.  Outputs are formed transposed, D((Q S)^T) =
+// mfma(S operand, Q operand), so each lane holds 4 consecutive columns of one
+// token and writes them with one store.
+//
+// LDS tiles (K, Q, av V: 64 x 128 f16) have 288-byte rows.  Measured on
+// gfx950 with 8 waves per CU, this padding runs the 16-byte fragment reads at
+// ~195 bytes per clock and the transpose reads at 128 (a 256-byte row runs
+// the transpose reads at 41); every read offset is a lane base plus a
+// constant.
+//
+// Ragged tails: rows past T load a copy of the last token and get alpha = 1,
+// beta = 0, which makes them exact no-ops (their A rows, Y~ rows and U^ rows
+// vanish); their output rows are not stored.
+//
+// Sequence segments.  One work-group per head leaves most of the chip idle
+// when B * H is small, so the chunks of a head are split into P segments of
+// L chunks.  A chunk maps the state entering it affinely, S -> M_c S + B_c,
+// with M_c = g_C I - c_S K^T T0 diag(bx) K (the same recurrence with V = 0)
+// and B_c the image of S = 0; a segment composes these maps.  Three passes:
+//   transition pass  (MODE 1, work-group per head and segment s < P - 1): the
+//                    recurrence run on M (from the identity, V = 0) and B
+//                    (from 0) side by side -- wave w holds columns
+//                    16 w .. 16 w + 15 of both -- giving the segment's map
+//                    M_s, B_s (f32, workspace);
+//   combine pass     (work-group per head and 16-column slice): S_0 = state
+//                    in, S_{s+1} = M_s S_s + B_s (f32 products), the initial
+//                    state of every segment (workspace);
+//   output pass      (MODE 0, work-group per head and segment): the recurrence
+//                    and the outputs of the segment from its initial state;
+//                    the last segment writes the final state.
+// This is an exact rewrite of the same recurrence (composition of the affine
+// chunk maps); each pass rounds like the single pass does.
+//
+// Precision: bf16 inputs convert to f16 exactly (unit-scale values); products
+// take f16 operands with f32 accumulation; S~ is f32.
+#include <algorithm>
+
+#include "gdn_f16ops.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+using namespace f16ops;
+
+constexpr int HC = 64;     // tokens per chunk
+constexpr int HD = 128;    // key and value dimension
+constexpr int HNT = 512;   // threads per work-group
+constexpr int HRS = 144;   // f16 row stride of the LDS tiles (288 bytes)
+constexpr int OFFDIAG_WAVE = 3;
+constexpr int GATE_WAVE = 6;
+constexpr float kWide = 10.f;  // log-gate range above which gates are per element
+
+struct HGate {
+  float bet[HC];  // beta
+  float gam[HC];  // cumulative log gate from the chunk start
+  float av[HC];   // Y~ = av V - bx X
+  float bx[HC];
+  float og[HC];   // O = og (Q S) + of (P U^)
+  float of[HC];
+  float dec[HC];  // exp(gam_C - gam), wide chunks
+  float gC;       // exp(gam_C)
+  float cS;       // exp(gam_C - gam_m), 1 for a wide chunk
+  float gCc;      // gC / cS
+  int wide;
+};
+
+struct __align__(16) HSmem {
+  h16 K[3][HC * HRS];    // K tiles, slot = chunk % 3
+  h16 Q[HC * HRS];       // Q tile of the chunk whose outputs are formed next
+  h16 V[HC * HRS];       // av V of the chunk in the recurrence
+  h16x8 Tc[2][6][64];    // Tm operands (see tm_offdiag), slot = chunk & 1
+  h16x4 Ab[6][64];       // A10, A20, A21, A30, A31, A32 as A operands
+  h16x4 Dg[7][64];       // D(T00), D(T00^T), D(T11), D(T11^T), D(T22), D(T22^T), D(T33^T)
+  h16x4 Pb[6][64][2];    // P operands per (row tile, 32-token step); halves = block columns
+  HGate g[3];            // slot = chunk % 3
+};
+
+// Slot of P block (R, C) in Pb: row tile R, 32-token step C / 2.
+__device__ __forceinline__ int pslot(int R, int C) {
+  return R == 0 ? 0 : R == 1 ? 1 : 2 * (R - 1) + (C >> 1);
+}
+
+// Global loads of the streamed tiles and gates.  The compiler does not track
+// these: the kernel waits for them itself with vm_wait, so the loads stay in
+// flight across the loop back-edge (the compiler's own accounting falls back
+// to waiting for every load there).
+__device__ __forceinline__ void gld16(bf16x8& r, const bf16* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+}
+__device__ __forceinline__ void gld4(float& r, const float* p) {
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+}
+// Wait until at most N vector-memory operations are outstanding.  The
+// registers a load wrote are tied to the wait, so no read of them is placed
+// before it and they stay reserved until the data has arrived.
+template <int N>
+__device__ __forceinline__ void vm_wait(bf16x8 (&r)[2]) {
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait(float& a, float& b) {
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+}
+
+// Four consecutive output columns of one token (byte offset `off`).
+template <class TOut>
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t rs, int off, f32x4 o) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (sizeof(TOut) == 2) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)o[i];
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, off, 0, 0);
+  }
+}
+
+// Per-head workspace of the segment split: M_s, B_s (segments 0 .. P - 2) and
+// the initial states of segments 1 .. P - 1, each 128 x 128 f32 [key][column].
+struct SegWs {
+  float* M;
+  float* B;
+  float* S;
+  __device__ __host__ size_t at(int bh, int s, int P) const { return ((size_t)bh * (P - 1) + s) * HD * HD; }
+};
+
+// MODE 0: outputs of one segment (work-group = head * P + segment).
+// MODE 1: transition map of one segment (work-group = head * (P - 1) + segment).
+template <int MODE, class TOut>
+__global__ __launch_bounds__(HNT) void prefill_head_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
+    float* state_out, TOut* __restrict__ out, SegWs ws, int T, int H, int NCT, int P, int L,
+    float scale) {
+  __shared__ HSmem sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lq = l >> 4;
+  const int nseg = MODE == 0 ? P : P - 1;
+  const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const int b = bh / H, h = bh % H;
+  const int c0 = seg * L;                // first chunk of the segment
+  const int NC = min(L, NCT - c0);       // chunks of the segment
+  const int tok = H * HD;  // elements between consecutive tokens
+  const size_t head0 = ((size_t)b * T + (size_t)c0 * HC) * tok + (size_t)h * HD;
+  const int Ts = T - c0 * HC;            // tokens from the segment start to the sequence end
+  const bf16* qh = q + head0;
+  const bf16* kh = k + head0;
+  const bf16* vh = v + head0;
+  const float* ah = alpha + ((size_t)b * T + (size_t)c0 * HC) * H + h;
+  const float* bhp = beta + ((size_t)b * T + (size_t)c0 * HC) * H + h;
+
+  // Tile pieces of this thread: rows pr and pr + 32, 8 columns from pc.
+  const int pr = tid >> 4, pc = (tid & 15) * 8;
+  // Every iteration issues the same vector-memory operations in the same
+  // order (output pass: K 2 loads, V 2, output stores 4, gates 2, Q 2;
+  // transition pass: K 2, V 2, gates 2; the chunk index is clamped into
+  // range, surplus loads are never used).  Each stream is consumed one
+  // iteration after its loads were issued, when exactly 10 (output pass) or
+  // 4 (transition pass) later operations have been issued.
+  constexpr int kInFlight = MODE == 0 ? 10 : 4;
+  auto ld_tile = [&](const bf16* base, int c, bf16x8* r) {
+    c = min(max(c, 0), NC - 1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = min(c * HC + pr + 32 * u, Ts - 1);
+      gld16(r[u], base + (size_t)t * tok + pc);
+    }
+  };
+  // Tile store offset of this thread's first piece (the second is 32 rows on).
+  const int st_off = pr * HRS + pc;
+  auto st_tile = [&](h16* tile, const bf16x8* r) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<h16x8*>(tile + st_off + 32 * u * HRS) = bf16x8_to_h8(r[u]);
+  };
+  float ra, rb;  // alpha, beta of one token per lane (used by the gate wave)
+  auto ld_gate = [&](int c) {
+    c = min(c, NC - 1);
+    const int t = min(c * HC + l, Ts - 1);
+    gld4(ra, ah + (size_t)t * H);
+    gld4(rb, bhp + (size_t)t * H);
+  };
+
+  // S~ tile m: keys kap(m, 4 lq + i), column 16 w + lr.  The transition pass
+  // keeps B~ in S and M~ in SM.
+  auto kap = [](int m, int r) { return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3); };
+  f32x4 S[8], SM[8];
+  {
+    const float* s0 = nullptr;
+    if (MODE == 0) s0 = seg == 0 ? (state_in ? state_in + (size_t)bh * HD * HD : nullptr)
+                                 : ws.S + ws.at(bh, seg - 1, P);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kap(m, 4 * lq + i), col = 16 * w + lr;
+        S[m][i] = s0 ? s0[key * HD + col] : 0.f;
+        SM[m][i] = (MODE == 1 && key == col) ? 1.f : 0.f;
+      }
+  }
+  float sig = 1.f;
+  // The state loads complete before the loop, so no wait inside it refers to them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  // Zero halves of the P operands (block columns above the diagonal).
+  if (tid < 64) {
+    sm.Pb[0][tid][1] = h16x4{0, 0, 0, 0};
+    sm.Pb[3][tid][1] = h16x4{0, 0, 0, 0};
+  }
+
+  // Gram-tile scalings (lane row 16 R + lr, columns 16 C + 4 lq + i).
+  auto offdiag = [&](const HGate& gs, bool wide, int R, int C, f32x4 G) -> h16x4 {
+    const int r = 16 * R + lr;
+    f32x4 x;
+    if (!wide) {
+      const float rf = gs.bet[r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = rf * G[i];
+    } else {
+      const float rf = gs.bet[r], gr = gs.gam[r];
+      const f32x4 gc = ldf4(&gs.gam[16 * C + 4 * lq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = rf * __expf(gr - gc[i]) * G[i];
+    }
+    return cvt4(x);
+  };
+  auto pblock = [&](const HGate& gs, bool wide, int R, int C, f32x4 G) -> h16x4 {
+    f32x4 x;
+    if (!wide) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (C < R || 4 * lq + i <= lr) ? G[i] : 0.f;
+    } else {
+      const float gr = gs.gam[16 * R + lr];
+      const f32x4 gc = ldf4(&gs.gam[16 * C + 4 * lq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[i] = (C < R || 4 * lq + i <= lr) ? scale * __expf(gr - gc[i]) * G[i] : 0.f;
+    }
+    return cvt4(x);
+  };
+  // Diagonal block R: D(L) and D(L^T) from the symmetric Gram tile.
+  auto diag = [&](const HGate& gs, bool wide, int R, f32x4 G, f32x4& Lf, f32x4& LTf) {
+    const int rb0 = 16 * R;
+    const f32x4 bv = ldf4(&gs.bet[rb0 + 4 * lq]);
+    const float bl = gs.bet[rb0 + lr];
+    f32x4 fL, fT;
+    if (!wide) {
+      fL = bv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fT[i] = bl;
+    } else {
+      const f32x4 gv = ldf4(&gs.gam[rb0 + 4 * lq]);
+      const float gl = gs.gam[rb0 + lr];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fL[i] = bv[i] * __expf(gv[i] - gl);
+        fT[i] = bl * __expf(gl - gv[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      Lf[i] = (4 * lq + i > lr) ? fL[i] * G[i] : 0.f;
+      LTf[i] = (lr > 4 * lq + i) ? fT[i] * G[i] : 0.f;
+    }
+  };
+  // LDS read offsets.  Fragment (A or B operand) of rows 16 R .. 16 R + 15,
+  // 32-key step j: lane row lr, keys 32 j + 8 lq .. + 7.
+  const int fb = lr * HRS + 8 * lq;
+  auto frag = [&](const h16* tile, int R, int j) { return ld8(tile + fb + 16 * R * HRS + 32 * j); };
+  // Transpose reads of K: token row 4 lq + lr / 4 (+ 16 per row step), keys
+  // 32 M + 8 (lr % 4) + 4 h .. + 3.
+  const int tb = (4 * lq + (lr >> 2)) * HRS + 8 * (lr & 3);
+  // Transpose reads of av V: token rows 16 rt + 4 lq + lr / 4, columns 16 w +
+  // 4 (lr % 4) .. + 3.
+  const int vb = (4 * lq + (lr >> 2)) * HRS + 16 * w + 4 * (lr & 3);
+
+  // One register slot per stream: each tile goes to LDS one iteration after
+  // its load was issued, and the next load reuses the registers at once.
+  bf16x8 kr[2], qr[2], vr[2];
+  ld_tile(kh, 0, kr);
+  ld_gate(0);
+  vm_wait<0>(kr);
+
+  auto body = [&](int it) {
+    const int c1 = it - 1, c2 = it - 2;
+    const bool h1 = c1 >= 0 && c1 < NC;
+    const bool h2 = c2 >= 0 && c2 < NC;
+
+    // ------------------------------------------------------------ phase 1
+    // K of chunk it -> LDS (slot it % 3 was last read in phase 2 of it - 1).
+    vm_wait<kInFlight>(kr);
+    if (it < NC) st_tile(sm.K[it % 3], kr);
+    ld_tile(kh, it + 1, kr);
+
+    f32x4 X[4], QS[4], XM[4];
+    if (h2) {
+      const h16* Kb = sm.K[c2 % 3];
+      const HGate& gs = sm.g[c2 % 3];
+      // All 16 K fragments are requested first; the products then run
+      // breadth-first over the row tiles (consecutive MFMAs independent)
+      // while the Q fragments are requested one per product.
+      h16x8 kf[4][4], sb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) kf[rt][j] = frag(Kb, rt, j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sb[j] = cat8(cvt4(S[2 * j]), cvt4(S[2 * j + 1]));
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) X[rt] = zero4(), QS[rt] = zero4(), XM[rt] = zero4();
+      if constexpr (MODE == 0) {
+        h16x8 qf[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            X[rt] = mfma32(kf[rt][j], sb[j], X[rt]);
+            qf[rt][j] = frag(sm.Q, rt, j);
+          }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int R = 0; R < 4; ++R) QS[R] = mfma32(sb[j], qf[R][j], QS[R]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // K fragment reads
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // X product
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // Q fragment read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // Q S products
+      } else {
+        // X~ of B~ and of M~ share the K fragments.
+        h16x8 sm8[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm8[j] = cat8(cvt4(SM[2 * j]), cvt4(SM[2 * j + 1]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            X[rt] = mfma32(kf[rt][j], sb[j], X[rt]);
+            XM[rt] = mfma32(kf[rt][j], sm8[j], XM[rt]);
+          }
+        // Fragments of steps j + 2 are requested while step j is multiplied.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
+      const float rho = gs.gCc * sig;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        S[m] *= rho;
+        if constexpr (MODE == 1) SM[m] *= rho;
+      }
+    }
+
+    if (w < 4) {
+      if (h1) {
+        // Diagonal block R = w of A for chunk c1, inverted.
+        const h16* Kb = sm.K[c1 % 3];
+        const HGate& gs = sm.g[c1 % 3];
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        f32x4 G = zero4();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h16x8 kf = frag(Kb, w, j);
+          G = mfma32(kf, kf, G);
+        }
+        f32x4 L, LT, Tt, TT;
+        diag(gs, wide, w, G, L, LT);
+        if (w < 3) {
+          inv16<true, true>(L, LT, lr, lq, Tt, TT);
+          sm.Dg[2 * w][l] = cvt4(Tt);
+          sm.Dg[2 * w + 1][l] = cvt4(TT);
+        } else {
+          inv16<false, true>(L, LT, lr, lq, Tt, TT);
+          sm.Dg[6][l] = cvt4(TT);
+        }
+      }
+    } else if (w < 6) {
+      // Off-diagonal blocks of A (chunk c1): rows 1, 2 (wave 4) or 3 (wave 5);
+      // P block (0, 0) (wave 4) or (1, 0) (wave 5) of chunk c2.
+      if (h1) {
+        const h16* Kb = sm.K[c1 % 3];
+        const HGate& gs = sm.g[c1 % 3];
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        f32x4 G0 = zero4(), G1 = zero4(), G2 = zero4();
+        if (w == 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 k0 = frag(Kb, 0, j), k1 = frag(Kb, 1, j), k2 = frag(Kb, 2, j);
+            G0 = mfma32(k0, k1, G0);  // (1, 0)
+            G1 = mfma32(k0, k2, G1);  // (2, 0)
+            G2 = mfma32(k1, k2, G2);  // (2, 1)
+          }
+          sm.Ab[0][l] = offdiag(gs, wide, 1, 0, G0);
+          sm.Ab[1][l] = offdiag(gs, wide, 2, 0, G1);
+          sm.Ab[2][l] = offdiag(gs, wide, 2, 1, G2);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 k3 = frag(Kb, 3, j);
+            G0 = mfma32(frag(Kb, 0, j), k3, G0);  // (3, 0)
+            G1 = mfma32(frag(Kb, 1, j), k3, G1);  // (3, 1)
+            G2 = mfma32(frag(Kb, 2, j), k3, G2);  // (3, 2)
+          }
+          sm.Ab[3][l] = offdiag(gs, wide, 3, 0, G0);
+          sm.Ab[4][l] = offdiag(gs, wide, 3, 1, G1);
+          sm.Ab[5][l] = offdiag(gs, wide, 3, 2, G2);
+        }
+      }
+      if (MODE == 0 && h2) {
+        const h16* Kb = sm.K[c2 % 3];
+        const HGate& gs = sm.g[c2 % 3];
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        const int R = w - 4;
+        f32x4 G = zero4();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) G = mfma32(frag(Kb, 0, j), frag(sm.Q, R, j), G);
+        sm.Pb[pslot(R, 0)][l][0] = pblock(gs, wide, R, 0, G);
+      }
+    } else {
+      // P blocks of chunk c2: (1, 1), (2, 0..2) (wave 6) or (3, 0..3) (wave 7).
+      if (MODE == 0 && h2) {
+        const h16* Kb = sm.K[c2 % 3];
+        const HGate& gs = sm.g[c2 % 3];
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        f32x4 G[4] = {zero4(), zero4(), zero4(), zero4()};
+        if (w == 6) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 k1 = frag(Kb, 1, j), q2 = frag(sm.Q, 2, j);
+            G[0] = mfma32(k1, frag(sm.Q, 1, j), G[0]);  // (1, 1)
+            G[1] = mfma32(frag(Kb, 0, j), q2, G[1]);    // (2, 0)
+            G[2] = mfma32(k1, q2, G[2]);                // (2, 1)
+            G[3] = mfma32(frag(Kb, 2, j), q2, G[3]);    // (2, 2)
+          }
+          sm.Pb[pslot(1, 1)][l][1] = pblock(gs, wide, 1, 1, G[0]);
+#pragma unroll
+          for (int C = 0; C < 3; ++C) sm.Pb[pslot(2, C)][l][C & 1] = pblock(gs, wide, 2, C, G[1 + C]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 q3 = frag(sm.Q, 3, j);
+#pragma unroll
+            for (int C = 0; C < 4; ++C) G[C] = mfma32(frag(Kb, C, j), q3, G[C]);
+          }
+#pragma unroll
+          for (int C = 0; C < 4; ++C) sm.Pb[pslot(3, C)][l][C & 1] = pblock(gs, wide, 3, C, G[C]);
+        }
+      }
+    }
+
+    vm_wait<kInFlight>(vr);
+    if (h2) {
+      // av V of chunk c2 -> LDS.
+      const HGate& gs = sm.g[c2 % 3];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float a = gs.av[pr + 32 * u];
+        h16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (h16)(a * (float)vr[u][e]);
+        *reinterpret_cast<h16x8*>(sm.V + st_off + 32 * u * HRS) = x;
+      }
+    }
+    ld_tile(vh, it - 1, vr);
+    lds_barrier();
+
+    // ------------------------------------------------------------ phase 2
+    f32x4 o[4] = {zero4(), zero4(), zero4(), zero4()};
+    if (h2) {
+      const h16* Kb = sm.K[c2 % 3];
+      const HGate& gs = sm.g[c2 % 3];
+      const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+      // LDS operands are requested ahead of the dependent chain: av V, bx and
+      // Tm for Y~ and U^ and the first half of the K^T fragments of the state
+      // update (keys 32 (m / 2) + 8 (lr % 4) + 4 (m % 2) .. + 3 of token rows
+      // 4 lq + lr / 4 + 16 r) up front, the second half and the P operands
+      // once U^ is formed.
+      const int s = c2 & 1;
+      h16x4 va[4], kt[8][4];
+      f32x4 bv[4];
+      h16x8 tc[6];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        va[rt] = ld_tr(sm.V + vb + 16 * rt * HRS);
+        bv[rt] = ldf4(&gs.bx[16 * rt + 4 * lq]);
+      }
+#pragma unroll
+      for (int i = 0; i < 6; ++i) tc[i] = sm.Tc[s][i][l];
+      auto ktr = [&](int m, int r) { return ld_tr(Kb + tb + 16 * r * HRS + 32 * (m >> 1) + 4 * (m & 1)); };
+#pragma unroll
+      for (int m = 0; m < 8; ++m) kt[m][0] = ktr(m, 0), kt[m][1] = ktr(m, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // U^ = T0 Y~ with Y~ = av V - (bx sigma) X~ (accumulator layout: tokens
+      // 16 rt + 4 lq + i, column lr); the transition pass also forms it for M~
+      // (V = 0).  Returns U^ (f16) and the state-update operand (U^, or
+      // exp(gam_C - gam) U^ for a wide chunk).
+      auto solve = [&](const f32x4* Xs, bool withv, h16x4* u16, h16x8* udb) {
+        h16x4 y16[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            y[i] = (withv ? (float)va[rt][i] : 0.f) - (bv[rt][i] * sig) * Xs[rt][i];
+          y16[rt] = cvt4(y);
+        }
+        const h16x8 ylo = cat8(y16[0], y16[1]), yhi = cat8(y16[2], y16[3]);
+        f32x4 U[4];
+        U[0] = mfma32(tc[0], ylo, zero4());
+        U[1] = mfma32(tc[1], ylo, zero4());
+        U[2] = mfma32(tc[2], ylo, zero4());
+        U[3] = mfma32(tc[4], ylo, zero4());
+        U[2] = mfma32(tc[3], yhi, U[2]);
+        U[3] = mfma32(tc[5], yhi, U[3]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) u16[rt] = cvt4(U[rt]);
+        if (!wide) {
+          udb[0] = cat8(u16[0], u16[1]);
+          udb[1] = cat8(u16[2], u16[3]);
+        } else {
+          h16x4 d16[4];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) d16[rt] = cvt4(ldf4(&gs.dec[16 * rt + 4 * lq]) * U[rt]);
+          udb[0] = cat8(d16[0], d16[1]);
+          udb[1] = cat8(d16[2], d16[3]);
+        }
+      };
+      h16x4 u16[4], u16m[4];
+      h16x8 udb[2], udbm[2];
+      solve(X, true, u16, udb);
+      if constexpr (MODE == 1) solve(XM, false, u16m, udbm);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) kt[m][2] = ktr(m, 2), kt[m][3] = ktr(m, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      // S~ += K^T U^, breadth-first over the eight state tiles.
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        S[m] = mfma32(cat8(kt[m][0], kt[m][1]), udb[0], S[m]);
+        if constexpr (MODE == 1) SM[m] = mfma32(cat8(kt[m][0], kt[m][1]), udbm[0], SM[m]);
+      }
+      h16x8 pb[6];
+      if constexpr (MODE == 0) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) pb[i] = *reinterpret_cast<const h16x8*>(&sm.Pb[i][l][0]);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        S[m] = mfma32(cat8(kt[m][2], kt[m][3]), udb[1], S[m]);
+        if constexpr (MODE == 1) SM[m] = mfma32(cat8(kt[m][2], kt[m][3]), udbm[1], SM[m]);
+      }
+      if constexpr (MODE == 0) {
+        // Outputs: (P U^)^T and (Q S~)^T hold token 16 R + lr, columns 4 lq + i.
+        const h16x8 ulo = cat8(u16[0], u16[1]), uhi = cat8(u16[2], u16[3]);
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          f32x4 PU = mfma32(ulo, pb[pslot(R, 0)], zero4());
+          if (R >= 2) PU = mfma32(uhi, pb[pslot(R, 2)], PU);
+          const int t = 16 * R + lr;
+          const float og = gs.og[t] * sig, of = gs.of[t];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[R][i] = og * QS[R][i] + of * PU[i];
+        }
+      }
+      sig = gs.cS;
+    }
+    if constexpr (MODE == 0) {
+      // Output rows of chunk c2 through a buffer resource covering its valid
+      // rows only: stores past T (or of a chunk out of range) are dropped by
+      // the range check, so every iteration issues the same stores.
+      const int nrows = h2 ? min(HC, Ts - c2 * HC) : 0;
+      const TOut* cb = out + head0 + (size_t)max(c2, 0) * HC * tok;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<TOut*>(cb), (short)0, nrows * tok * (int)sizeof(TOut), 0x00020000);
+#pragma unroll
+      for (int R = 0; R < 4; ++R)
+        store4<TOut>(rs, ((16 * R + lr) * tok + 16 * w + 4 * lq) * (int)sizeof(TOut), o[R]);
+    }
+
+    if (w == OFFDIAG_WAVE && h1) {
+      h16x4 ga[6], d[7];
+      h16x8 tc[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) ga[i] = sm.Ab[i][l];
+#pragma unroll
+      for (int i = 0; i < 7; ++i) d[i] = sm.Dg[i][l];
+      tm_offdiag(ga, d, tc);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) sm.Tc[c1 & 1][i][l] = tc[i];
+    }
+
+    vm_wait<kInFlight>(ra, rb);
+    if (w == GATE_WAVE && it < NC) {
+      // Gate tables of chunk it (lane = token).
+      HGate& gs = sm.g[it % 3];
+      const bool valid = it * HC + l < Ts;
+      const float lal = valid ? __logf(ra) : 0.f;
+      const float bt = valid ? rb : 0.f;
+      const float la = wave_incl_sum(lal);
+      const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 0));
+      const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 63));
+      const bool wide = (g0 - gl) > kWide;
+      const float gm = 0.5f * (g0 + gl);
+      const float g = __expf(la);
+      const float av = wide ? bt : bt * __expf(gm - la);
+      gs.bet[l] = bt;
+      gs.gam[l] = la;
+      gs.av[l] = av;
+      gs.bx[l] = av * g;
+      gs.og[l] = scale * g;
+      gs.of[l] = wide ? 1.f : scale * __expf(la - gm);
+      gs.dec[l] = __expf(gl - la);
+      if (l == 0) {
+        gs.gC = __expf(gl);
+        gs.cS = wide ? 1.f : __expf(gl - gm);
+        gs.gCc = wide ? gs.gC : __expf(gm);
+        gs.wide = wide ? 1 : 0;
+      }
+    }
+    ld_gate(it + 1);
+    if constexpr (MODE == 0) {
+      vm_wait<kInFlight>(qr);
+      if (h1) st_tile(sm.Q, qr);
+      ld_tile(qh, it, qr);
+    }
+    lds_barrier();
+  };
+
+  // Chunk c's outputs are formed at iteration c + 2.
+  const int NIT = NC + 2;
+  for (int it = 0; it < NIT; ++it) body(it);
+
+  float* dst = nullptr;
+  float* dstm = nullptr;
+  if (MODE == 0) {
+    if (seg == P - 1 && state_out) dst = state_out + (size_t)bh * HD * HD;
+  } else {
+    dst = ws.B + ws.at(bh, seg, P);
+    dstm = ws.M + ws.at(bh, seg, P);
+  }
+  if (dst) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = kap(m, 4 * lq + i) * HD + 16 * w + lr;
+        dst[o] = sig * S[m][i];
+        if (MODE == 1) dstm[o] = sig * SM[m][i];
+      }
+  }
+}
+
+// Initial states of segments 1 .. P - 1: S_0 = state in (or 0), S_{s+1} =
+// M_s S_s + B_s.  One work-group of 256 threads per (head, 16-column slice);
+// thread t computes rows t / 2 and columns 8 (t % 2) .. + 7 of the slice.
+__global__ __launch_bounds__(256) void segment_combine_kernel(const float* state_in, SegWs ws,
+                                                              int P) {
+  __shared__ float Ssl[HD][16];
+  const int bh = blockIdx.x >> 3, col0 = 16 * (blockIdx.x & 7);
+  const int t = threadIdx.x, row = t >> 1, cg = 8 * (t & 1);
+  for (int i = t; i < HD * 16; i += 256) {
+    const int r = i >> 4, c = i & 15;
+    Ssl[r][c] = state_in ? state_in[(size_t)bh * HD * HD + r * HD + col0 + c] : 0.f;
+  }
+  __syncthreads();
+  for (int sg = 0; sg + 1 < P; ++sg) {
+    const float* M = ws.M + ws.at(bh, sg, P) + (size_t)row * HD;
+    const float* Bs = ws.B + ws.at(bh, sg, P) + (size_t)row * HD + col0 + cg;
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = Bs[c];
+    for (int kk = 0; kk < HD; kk += 4) {
+      const f32x4 mv = *reinterpret_cast<const f32x4*>(M + kk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += mv[e] * Ssl[kk + e][cg + c];
+    }
+    __syncthreads();
+    float* dst = ws.S + ws.at(bh, sg, P) + (size_t)row * HD + col0 + cg;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      Ssl[row][cg + c] = acc[c];
+      dst[c] = acc[c];
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool prefill_head_supported(const PrefillArgs& p) {
+  return p.bf16 && p.Dk == HD && p.Dv == HD && p.chunk == HC && p.T > 0;
+}
+
+// Segments per head: enough work-groups for one per CU (the kernels hold
+// ~120 KB of LDS, so one work-group per CU runs at a time), each segment at
+// least kMinSegChunks chunks.  The transition pass costs about as much per
+// chunk as the output pass, so a split into P segments shortens the serial
+// chain about P / 2 times: fewer than 3 segments do not pay.
+constexpr int kCUs = 256;
+constexpr int kMinSegChunks = 8;
+void prefill_head_segments(int B, int T, int H, int* P, int* L) {
+  const int NC = (T + HC - 1) / HC;
+  const long long BH = std::max(1LL, (long long)B * H);
+  int p = (int)std::min<long long>(kCUs / BH, NC / kMinSegChunks);
+  if (p < 3) p = 1;
+  const int l = (NC + p - 1) / p;
+  *L = l;
+  *P = (NC + l - 1) / l;
+}
+
+size_t prefill_head_workspace_bytes(int B, int T, int H) {
+  int P, L;
+  prefill_head_segments(B, T, H, &P, &L);
+  if (P <= 1) return 0;
+  return 3 * (size_t)B * H * (P - 1) * HD * HD * sizeof(float);
+}
+
+template <class TOut>
+static hipError_t launch_head_t(const PrefillArgs& p) {
+  const int NC = (p.T + HC - 1) / HC;
+  int P, L;
+  prefill_head_segments(p.B, p.T, p.H, &P, &L);
+  const int BH = p.B * p.H;
+  SegWs ws{nullptr, nullptr, nullptr};
+  const hipStream_t st = (hipStream_t)p.stream;
+  if (P > 1) {
+    const size_t n = (size_t)BH * (P - 1) * HD * HD;
+    ws.M = (float*)p.workspace;
+    ws.B = ws.M + n;
+    ws.S = ws.B + n;
+    hipLaunchKernelGGL((prefill_head_kernel<1, float>), dim3(BH * (P - 1)), dim3(HNT), 0, st,
+                       (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.alpha, p.beta,
+                       nullptr, nullptr, (float*)nullptr, ws, p.T, p.H, NC, P, L, p.scale);
+    hipLaunchKernelGGL(segment_combine_kernel, dim3(BH * 8), dim3(256), 0, st, p.state_in, ws, P);
+  }
+  hipLaunchKernelGGL((prefill_head_kernel<0, TOut>), dim3(BH * P), dim3(HNT), 0, st,
+                     (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.alpha, p.beta,
+                     p.state_in, p.state_out, (TOut*)p.out, ws, p.T, p.H, NC, P, L, p.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_head(const PrefillArgs& p) {
+  return p.out_bf16 ? launch_head_t<bf16>(p) : launch_head_t<float>(p);
+}
+
+}  // namespace gdn

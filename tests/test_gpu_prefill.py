@@ -98,6 +98,41 @@ def test_single_pass_prefill_matches_oracle(B, T, H, Dv, state0):
     assert_bf16_is_rounded_f32(ob, o)
 
 
+@pytest.mark.parametrize("B,T,H,state0,gate_pow", [
+    (1, 1536, 2, "randn", 1),       # 3 segments of 8 chunks
+    (1, 1536 - 17, 2, "randn", 1),  # ragged tail in the last segment
+    (1, 4096, 1, "zero", 1),        # 8 segments
+    (2, 2048 + 5, 1, "randn", 1),   # 4 segments, short ragged last one
+    (1, 1536, 2, "randn", 3),       # steeper gates: some chunks take the wide path
+    (1, 1536, 2, "randn", 8),       # most chunks wide
+])
+def test_segmented_prefill_matches_oracle(B, T, H, state0, gate_pow):
+    """bf16, Dk = Dv = 128, chunk 64 and few heads: the sequence is split into
+    segments (transition pass, combine pass, output pass)."""
+    assert gdn.gdn_prefill_workspace_bytes(B, T, H, 128, 128, 64) > 0
+    say(f"segmented prefill B={B} T={T} H={H} S0={state0} alpha^{gate_pow}")
+    x = synthetic.gdn_inputs(B, T, H, 128, 128, dtype="bf16", seed=T + 31 * H + gate_pow,
+                             state0=state0)
+    x["alpha"] = (x["alpha"] ** gate_pow).contiguous()
+    o, s = _run(x, 64, scale=0.9)
+    ro, rs = _oracle(x, scale=0.9)
+    eo, es = err(o, ro), err(s, rs)
+    say(f"  errs out {eo:.3e} state {es:.3e} nmse {oracle.nmse(f64(o), ro):.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    ob, _ = _run(x, 64, scale=0.9, out_dtype=torch.bfloat16)
+    assert_bf16_is_rounded_f32(ob, o)
+
+
+def test_segmented_prefill_rejects_small_workspace():
+    B, T, H = 1, 1536, 2
+    need = gdn.gdn_prefill_workspace_bytes(B, T, H, 128, 128, 64)
+    x = synthetic.gdn_inputs(B, T, H, 128, 128, dtype="bf16", seed=3, state0="zero")
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(RuntimeError, match="workspace too small"):
+        gdn.gdn_prefill_chunked(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["alpha"]),
+                                dev(x["beta"]), None, chunk=64, workspace=ws)
+
+
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 63, 64, 65])
 def test_short_and_boundary_lengths(T):
     x = synthetic.gdn_inputs(1, T, 2, 32, 32, dtype="f32", seed=T, state0="randn")
