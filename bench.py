@@ -76,11 +76,11 @@ def decode_swa_bytes(d, n_slots, esize=2):
 # changed since reports traffic null.  Each figure is copied from the profile
 # summary named in "profile".
 PROFILE = "profiles/gdn_kernels_bench_workloads.md"
+# The long32k prefill call launches three kernels (segment transition pass,
+# combine pass, output pass); its entry sums them.
+PREFILL_KERNELS = ("prefill_head_kernel<1,float> + segment_combine_kernel + "
+                   "prefill_head_kernel<0,bf16>")
 COUNTERS = {
-    "prefill_fused_kernel<bf16>": dict(
-        src="gated_delta_rule_115_amd/csrc/gdn_prefill_fused.hip",
-        sha1="cfa47af2d72fd6cb289304951f12df8723369cc6",
-        fetch_kib=426312, write_kib=264192, profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
         sha1="b476cc39e7e5f69ceb396d81745208125716902b",
@@ -363,7 +363,7 @@ def main():
         inf = infos["prefill_long32k"]
         ms = seg_ms[("prefill_long32k", "prefill")]
         sec = ms / 1e3
-        kern = "prefill_fused_kernel<bf16>"
+        kern = PREFILL_KERNELS
         roofline = dict(bound="mfma", kernel=kern, achieved=inf["flops"] / sec / 1e12,
                         peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
                         frac=inf["flops"] / sec / PEAK_BF16_FLOPS, traffic=traffic_bytes(kern),
