@@ -714,39 +714,68 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
 }
 
 // Initial states of segments 1 .. P - 1: S_0 = state in (or 0), S_{s+1} =
-// M_s S_s + B_s.  One work-group of 256 threads per (head, 16-column slice);
-// thread t computes rows t / 2 and columns 8 (t % 2) .. + 7 of the slice.
+// M_s S_s + B_s, in f32.  One work-group of 4 waves per (head, 16-column
+// slice); wave w forms row tiles 2 w, 2 w + 1 (16 rows each) of every step
+// with v_mfma_f32_16x16x4_f32: in the 16-key block jj, product i takes key
+// 16 jj + 4 q + i in lane group q, so each lane reads its 4 keys of M with
+// one 16-byte load and S (kept transposed in LDS) with one 16-byte read.  The
+// next segment's M and B are loaded while the current product runs.
 __global__ __launch_bounds__(256) void segment_combine_kernel(const float* state_in, SegWs ws,
                                                               int P) {
-  __shared__ float Ssl[HD][16];
+  __shared__ __align__(16) float St[16][HD + 4];  // S slice transposed: [column][key]
   const int bh = blockIdx.x >> 3, col0 = 16 * (blockIdx.x & 7);
-  const int t = threadIdx.x, row = t >> 1, cg = 8 * (t & 1);
-  for (int i = t; i < HD * 16; i += 256) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
+  for (int i = tid; i < HD * 16; i += 256) {
     const int r = i >> 4, c = i & 15;
-    Ssl[r][c] = state_in ? state_in[(size_t)bh * HD * HD + r * HD + col0 + c] : 0.f;
+    St[c][r] = state_in ? state_in[(size_t)bh * HD * HD + r * HD + col0 + c] : 0.f;
   }
+  // Lane (lq, lr) of row tile R: M row 16 R + lr, keys 16 jj + 4 lq .. + 3.
+  f32x4 mA[2][8], bA[2], mN[2][8], bN[2];
+  auto load = [&](int sg, f32x4 (&m)[2][8], f32x4 (&bb)[2]) {
+    const float* M = ws.M + ws.at(bh, sg, P);
+    const float* Bs = ws.B + ws.at(bh, sg, P);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = 16 * (2 * w + t) + lr;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) m[t][jj] = ldf4(M + (size_t)row * HD + 16 * jj + 4 * lq);
+      // B in accumulator layout: rows 16 R + 4 lq + i, column lr.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bb[t][i] = Bs[(size_t)(16 * (2 * w + t) + 4 * lq + i) * HD + col0 + lr];
+    }
+  };
+  load(0, mA, bA);
   __syncthreads();
   for (int sg = 0; sg + 1 < P; ++sg) {
-    const float* M = ws.M + ws.at(bh, sg, P) + (size_t)row * HD;
-    const float* Bs = ws.B + ws.at(bh, sg, P) + (size_t)row * HD + col0 + cg;
-    float acc[8];
+    if (sg + 2 < P) load(sg + 1, mN, bN);
+    f32x4 acc[2];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = Bs[c];
-    for (int kk = 0; kk < HD; kk += 4) {
-      const f32x4 mv = *reinterpret_cast<const f32x4*>(M + kk);
+    for (int t = 0; t < 2; ++t) {
+      acc[t] = bA[t];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int jj = 0; jj < 8; ++jj) {
+        const f32x4 sv = ldf4(&St[lr][16 * jj + 4 * lq]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] += mv[e] * Ssl[kk + e][cg + c];
+        for (int i = 0; i < 4; ++i)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mA[t][jj][i], sv[i], acc[t], 0, 0, 0);
+      }
     }
     __syncthreads();
-    float* dst = ws.S + ws.at(bh, sg, P) + (size_t)row * HD + col0 + cg;
+    float* dst = ws.S + ws.at(bh, sg, P);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      Ssl[row][cg + c] = acc[c];
-      dst[c] = acc[c];
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 16 * (2 * w + t) + 4 * lq;
+      *reinterpret_cast<f32x4*>(&St[lr][r0]) = acc[t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(size_t)(r0 + i) * HD + col0 + lr] = acc[t][i];
     }
     __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bA[t] = bN[t];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) mA[t][jj] = mN[t][jj];
+    }
   }
 }
 
