@@ -193,6 +193,9 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
+  // Waves w and w + 4 share a SIMD and the older wave wins instruction issue;
+  // waves 4-7 carry the longer phase-1 work, so they get the higher priority.
+  if (w >= 4) __builtin_amdgcn_s_setprio(1);
   const int nseg = MODE == 0 ? P : P - 1;
   const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   const int b = bh / H, h = bh % H;
