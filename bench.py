@@ -81,6 +81,11 @@ PROFILE = "profiles/gdn_kernels_bench_workloads.md"
 PREFILL_KERNELS = ("prefill_head_kernel<1,float> + segment_combine_kernel + "
                    "prefill_head_kernel<0,bf16>")
 COUNTERS = {
+    PREFILL_KERNELS: dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
+        sha1="a683234c27feda93344398fb14b2405c2519dcd6",
+        fetch_kib=262220 + 71711 + 404599, write_kib=36737 + 14336 + 264192,
+        profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
         sha1="b476cc39e7e5f69ceb396d81745208125716902b",
