@@ -64,11 +64,16 @@ int gdn_abi_version(void);
 const char* gdn_last_error(void);
 
 /*
- * Workspace (bytes) that gdn_prefill_chunked needs for these sizes.  0 when
- * none is needed: bf16 inputs with Dk = 128, chunk = 64 and T > 0 run in a
- * single pass that keeps every intermediate on chip.  Otherwise the
- * workspace holds, per chunk of `chunk` tokens, the chunk's triangular-solve
- * matrix, its decay-masked query-key products and its cumulative log gates.
+ * Workspace (bytes) that gdn_prefill_chunked needs for these sizes.
+ *   - bf16 inputs, Dk = Dv = 128, chunk = 64: 0 when one pass per head fills
+ *     the GPU; with few (batch, head) pairs and long sequences the sequence
+ *     is split into P segments, and the workspace holds, per head, the f32
+ *     128 x 128 state maps of the first P - 1 segments and their initial
+ *     states (3 (P - 1) x 64 KiB).
+ *   - bf16 inputs, Dk = 128, Dv < 128, chunk = 64: 0 (single pass).
+ *   - otherwise: per chunk of `chunk` tokens, the chunk's triangular-solve
+ *     matrix, its decay-masked query-key products and its cumulative log
+ *     gates.
  * Also 0 if the sizes are invalid.
  */
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv,
