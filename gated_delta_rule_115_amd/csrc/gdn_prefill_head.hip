@@ -181,6 +181,98 @@ struct SegWs {
   __device__ __host__ size_t at(int bh, int s, int P) const { return ((size_t)bh * (P - 1) + s) * HD * HD; }
 };
 
+// Gram-tile scalings (lane row 16 R + lr, columns 16 C + 4 lq + i).
+// Off-diagonal block (R, C) of A as an A operand.
+__device__ __forceinline__ h16x4 a_offdiag(const HGate& gs, bool wide, int R, int C, f32x4 G,
+                                           int lr, int lq) {
+  const int r = 16 * R + lr;
+  f32x4 x;
+  if (!wide) {
+    const float rf = gs.bet[r];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = rf * G[i];
+  } else {
+    const float rf = gs.bet[r], gr = gs.gam[r];
+    const f32x4 gc = ldf4(&gs.gam[16 * C + 4 * lq]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = rf * __expf(gr - gc[i]) * G[i];
+  }
+  return cvt4(x);
+}
+// Block (R, C) of P (lower triangle of Q K^T; gate ratios and scale for a
+// wide chunk) as an A operand.
+__device__ __forceinline__ h16x4 p_block(const HGate& gs, bool wide, int R, int C, f32x4 G, int lr,
+                                         int lq, float scale) {
+  f32x4 x;
+  if (!wide) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (C < R || 4 * lq + i <= lr) ? G[i] : 0.f;
+  } else {
+    const float gr = gs.gam[16 * R + lr];
+    const f32x4 gc = ldf4(&gs.gam[16 * C + 4 * lq]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = (C < R || 4 * lq + i <= lr) ? scale * __expf(gr - gc[i]) * G[i] : 0.f;
+  }
+  return cvt4(x);
+}
+// Diagonal block R: D(L) and D(L^T) from the symmetric Gram tile.
+__device__ __forceinline__ void a_diag(const HGate& gs, bool wide, int R, f32x4 G, int lr, int lq,
+                                       f32x4& Lf, f32x4& LTf) {
+  const int rb0 = 16 * R;
+  const f32x4 bv = ldf4(&gs.bet[rb0 + 4 * lq]);
+  const float bl = gs.bet[rb0 + lr];
+  f32x4 fL, fT;
+  if (!wide) {
+    fL = bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fT[i] = bl;
+  } else {
+    const f32x4 gv = ldf4(&gs.gam[rb0 + 4 * lq]);
+    const float gl = gs.gam[rb0 + lr];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fL[i] = bv[i] * __expf(gv[i] - gl);
+      fT[i] = bl * __expf(gl - gv[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Lf[i] = (4 * lq + i > lr) ? fL[i] * G[i] : 0.f;
+    LTf[i] = (lr > 4 * lq + i) ? fT[i] * G[i] : 0.f;
+  }
+}
+// Gate tables of one chunk from alpha, beta of token l (one wave, lane = token).
+__device__ __forceinline__ void gate_tables(HGate& gs, float alpha_l, float beta_l, bool valid,
+                                            float scale, int l) {
+  const float lal = valid ? __logf(alpha_l) : 0.f;
+  const float bt = valid ? beta_l : 0.f;
+  const float la = wave_incl_sum(lal);
+  const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 0));
+  const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 63));
+  const bool wide = (g0 - gl) > kWide;
+  const float gm = 0.5f * (g0 + gl);
+  const float g = __expf(la);
+  const float av = wide ? bt : bt * __expf(gm - la);
+  gs.bet[l] = bt;
+  gs.gam[l] = la;
+  gs.av[l] = av;
+  gs.bx[l] = av * g;
+  gs.og[l] = scale * g;
+  gs.of[l] = wide ? 1.f : scale * __expf(la - gm);
+  gs.dec[l] = __expf(gl - la);
+  if (l == 0) {
+    gs.gC = __expf(gl);
+    gs.cS = wide ? 1.f : __expf(gl - gm);
+    gs.gCc = wide ? gs.gC : __expf(gm);
+    gs.wide = wide ? 1 : 0;
+  }
+}
+// S~ tile m, accumulator row r: key kap(m, r).
+__device__ __forceinline__ int kap(int m, int r) {
+  return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
+}
+
 // MODE 0: outputs of one segment (work-group = head * P + segment).
 // MODE 1: transition map of one segment (work-group = head * (P - 1) + segment).
 template <int MODE, class TOut>
@@ -244,7 +336,6 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
 
   // S~ tile m: keys kap(m, 4 lq + i), column 16 w + lr.  The transition pass
   // keeps B~ in S and M~ in SM.
-  auto kap = [](int m, int r) { return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3); };
   f32x4 S[8], SM[8];
   {
     const float* s0 = nullptr;
@@ -269,60 +360,14 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
     sm.Pb[3][tid][1] = h16x4{0, 0, 0, 0};
   }
 
-  // Gram-tile scalings (lane row 16 R + lr, columns 16 C + 4 lq + i).
-  auto offdiag = [&](const HGate& gs, bool wide, int R, int C, f32x4 G) -> h16x4 {
-    const int r = 16 * R + lr;
-    f32x4 x;
-    if (!wide) {
-      const float rf = gs.bet[r];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = rf * G[i];
-    } else {
-      const float rf = gs.bet[r], gr = gs.gam[r];
-      const f32x4 gc = ldf4(&gs.gam[16 * C + 4 * lq]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = rf * __expf(gr - gc[i]) * G[i];
-    }
-    return cvt4(x);
+  auto offdiag = [&](const HGate& gs, bool wide, int R, int C, f32x4 G) {
+    return a_offdiag(gs, wide, R, C, G, lr, lq);
   };
-  auto pblock = [&](const HGate& gs, bool wide, int R, int C, f32x4 G) -> h16x4 {
-    f32x4 x;
-    if (!wide) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = (C < R || 4 * lq + i <= lr) ? G[i] : 0.f;
-    } else {
-      const float gr = gs.gam[16 * R + lr];
-      const f32x4 gc = ldf4(&gs.gam[16 * C + 4 * lq]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        x[i] = (C < R || 4 * lq + i <= lr) ? scale * __expf(gr - gc[i]) * G[i] : 0.f;
-    }
-    return cvt4(x);
+  auto pblock = [&](const HGate& gs, bool wide, int R, int C, f32x4 G) {
+    return p_block(gs, wide, R, C, G, lr, lq, scale);
   };
-  // Diagonal block R: D(L) and D(L^T) from the symmetric Gram tile.
   auto diag = [&](const HGate& gs, bool wide, int R, f32x4 G, f32x4& Lf, f32x4& LTf) {
-    const int rb0 = 16 * R;
-    const f32x4 bv = ldf4(&gs.bet[rb0 + 4 * lq]);
-    const float bl = gs.bet[rb0 + lr];
-    f32x4 fL, fT;
-    if (!wide) {
-      fL = bv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fT[i] = bl;
-    } else {
-      const f32x4 gv = ldf4(&gs.gam[rb0 + 4 * lq]);
-      const float gl = gs.gam[rb0 + lr];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fL[i] = bv[i] * __expf(gv[i] - gl);
-        fT[i] = bl * __expf(gl - gv[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      Lf[i] = (4 * lq + i > lr) ? fL[i] * G[i] : 0.f;
-      LTf[i] = (lr > 4 * lq + i) ? fT[i] * G[i] : 0.f;
-    }
+    a_diag(gs, wide, R, G, lr, lq, Lf, LTf);
   };
   // LDS read offsets.  Fragment (A or B operand) of rows 16 R .. 16 R + 15,
   // 32-key step j: lane row lr, keys 32 j + 8 lq .. + 7.
@@ -658,30 +703,7 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
     vm_wait<kInFlight>(ra, rb);
     if (w == GATE_WAVE && it < NC) {
       // Gate tables of chunk it (lane = token).
-      HGate& gs = sm.g[it % 3];
-      const bool valid = it * HC + l < Ts;
-      const float lal = valid ? __logf(ra) : 0.f;
-      const float bt = valid ? rb : 0.f;
-      const float la = wave_incl_sum(lal);
-      const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 0));
-      const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), 63));
-      const bool wide = (g0 - gl) > kWide;
-      const float gm = 0.5f * (g0 + gl);
-      const float g = __expf(la);
-      const float av = wide ? bt : bt * __expf(gm - la);
-      gs.bet[l] = bt;
-      gs.gam[l] = la;
-      gs.av[l] = av;
-      gs.bx[l] = av * g;
-      gs.og[l] = scale * g;
-      gs.of[l] = wide ? 1.f : scale * __expf(la - gm);
-      gs.dec[l] = __expf(gl - la);
-      if (l == 0) {
-        gs.gC = __expf(gl);
-        gs.cS = wide ? 1.f : __expf(gl - gm);
-        gs.gCc = wide ? gs.gC : __expf(gm);
-        gs.wide = wide ? 1 : 0;
-      }
+      gate_tables(sm.g[it % 3], ra, rb, it * HC + l < Ts, scale, l);
     }
     ld_gate(it + 1);
     if constexpr (MODE == 0) {
@@ -713,6 +735,450 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
         dst[o] = sig * S[m][i];
         if (MODE == 1) dstm[o] = sig * SM[m][i];
       }
+  }
+}
+
+// Output pass with wave roles (work-group = head * P + segment).  Waves 0-3
+// each run the recurrence of two 16-column slices (columns 32 c .. 32 c + 31),
+// so every K, Q and K^T fragment read from LDS serves two products; waves
+// 4-7 (one per SIMD, next to a recurrence wave) do all global loads, the
+// f16 conversions, the Gram blocks, the inverse and the gate tables.
+// Iteration i, phase 1: recurrence waves X~, (Q S~)^T, Y~ and U^ of chunk
+// i - 2; helpers: K of chunk i -> LDS, diagonal blocks and inverses (chunk
+// i - 1), off-diagonal blocks of A (i - 1) and of P (i - 2).  Phase 2:
+// recurrence waves S~ update, (P U^)^T and the outputs of chunk i - 2;
+// helpers: off-diagonal blocks of Tm (i - 1), gate tables (i), Q of chunk
+// i - 1 and av V of chunk i - 1 -> LDS.
+template <class TOut>
+__global__ __launch_bounds__(HNT) void prefill_out_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
+    float* state_out, TOut* __restrict__ out, SegWs ws, int T, int H, int NCT, int P, int L,
+    float scale) {
+  __shared__ HSmem sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lq = l >> 4;
+  const int bh = blockIdx.x / P, seg = blockIdx.x % P;
+  const int b = bh / H, h = bh % H;
+  const int c0 = seg * L;                // first chunk of the segment
+  const int NC = min(L, NCT - c0);       // chunks of the segment
+  const int tok = H * HD;                // elements between consecutive tokens
+  const size_t head0 = ((size_t)b * T + (size_t)c0 * HC) * tok + (size_t)h * HD;
+  const int Ts = T - c0 * HC;            // tokens from the segment start to the sequence end
+  const int NIT = NC + 2;                // chunk c's outputs are formed at iteration c + 2
+
+  if (tid < 64) {  // zero halves of the P operands (block columns above the diagonal)
+    sm.Pb[0][tid][1] = h16x4{0, 0, 0, 0};
+    sm.Pb[3][tid][1] = h16x4{0, 0, 0, 0};
+  }
+  // Fragment rows 16 R .. 16 R + 15, 32-key step j: lane row lr, keys 32 j + 8 lq .. + 7.
+  // The lane offsets are passed through an empty asm once per iteration
+  // (lane_offset): otherwise the compiler hoists base + offset + constant out
+  // of the loop as one register per read instead of folding the constants
+  // into the instructions' offset fields.
+  int fb = lr * HRS + 8 * lq;
+  auto frag = [&](const h16* tile, int R, int j) { return ld8(tile + fb + 16 * R * HRS + 32 * j); };
+  auto lane_offset = [](int& x) { asm volatile("" : "+v"(x)); };
+
+  if (w < 4) {
+    // ------------------------------------------------------- recurrence waves
+    const int cw = w;
+    // Transpose reads of K (token row 4 lq + lr / 4 + 16 r, keys 32 M + 8 (lr % 4) + 4 h)
+    // and of av V (token rows 16 rt + 4 lq + lr / 4, columns of slice s).
+    int tb = (4 * lq + (lr >> 2)) * HRS + 8 * (lr & 3);
+    int vb = (4 * lq + (lr >> 2)) * HRS + 32 * cw + 4 * (lr & 3);
+    f32x4 S[2][8];
+    {
+      const float* s0 = seg == 0 ? (state_in ? state_in + (size_t)bh * HD * HD : nullptr)
+                                 : ws.S + ws.at(bh, seg - 1, P);
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[sl][m][i] = s0 ? s0[kap(m, 4 * lq + i) * HD + 32 * cw + 16 * sl + lr] : 0.f;
+    }
+    float sig = 1.f;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): state loads done before the loop
+    for (int it = 0; it < NIT; ++it) {
+      const int c2 = it - 2;
+      const bool h2 = c2 >= 0 && c2 < NC;
+      lane_offset(fb);
+      lane_offset(tb);
+      lane_offset(vb);
+      // ---- phase 1: X~ = K S~, (Q S~)^T, Y~, U^ for both slices of chunk c2
+      f32x4 X[2][4], QS[2][4];
+      h16x4 u16[2][4];
+      h16x8 udb[2][2];
+      if (h2) {
+        const h16* Kb = sm.K[c2 % 3];
+        const HGate& gs = sm.g[c2 % 3];
+        h16x8 sb[2][4];
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sb[sl][j] = cat8(cvt4(S[sl][2 * j]), cvt4(S[sl][2 * j + 1]));
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) X[sl][rt] = zero4(), QS[sl][rt] = zero4();
+        // Per 32-key step: 4 K fragments (8 X products), 4 Q fragments (8
+        // Q S products); the K fragments of step j + 1 are requested during
+        // the X products of step j, the Q fragments during its Q S products.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h16x8 kf[4], qf[4];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) kf[rt] = frag(Kb, rt, j);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) qf[rt] = frag(sm.Q, rt, j);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) X[sl][rt] = mfma32(kf[rt], sb[sl][j], X[sl][rt]);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) QS[sl][rt] = mfma32(sb[sl][j], qf[rt], QS[sl][rt]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        // Y~ = av V - (bx sigma) X~, U^ = T0 Y~ (av V and Tm of chunk c2 were
+        // written in phase 2 of the previous iteration).
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        const int s = c2 & 1;
+        h16x4 va[2][4];
+        f32x4 bv[4];
+        h16x8 tc[6];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) va[sl][rt] = ld_tr(sm.V + vb + 16 * sl + 16 * rt * HRS);
+          bv[rt] = ldf4(&gs.bx[16 * rt + 4 * lq]);
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i) tc[i] = sm.Tc[s][i][l];
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          h16x4 y16[4];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            f32x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = (float)va[sl][rt][i] - (bv[rt][i] * sig) * X[sl][rt][i];
+            y16[rt] = cvt4(y);
+          }
+          const h16x8 ylo = cat8(y16[0], y16[1]), yhi = cat8(y16[2], y16[3]);
+          f32x4 U[4];
+          U[0] = mfma32(tc[0], ylo, zero4());
+          U[1] = mfma32(tc[1], ylo, zero4());
+          U[2] = mfma32(tc[2], ylo, zero4());
+          U[3] = mfma32(tc[4], ylo, zero4());
+          U[2] = mfma32(tc[3], yhi, U[2]);
+          U[3] = mfma32(tc[5], yhi, U[3]);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) u16[sl][rt] = cvt4(U[rt]);
+          if (!wide) {
+            udb[sl][0] = cat8(u16[sl][0], u16[sl][1]);
+            udb[sl][1] = cat8(u16[sl][2], u16[sl][3]);
+          } else {
+            h16x4 d16[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) d16[rt] = cvt4(ldf4(&gs.dec[16 * rt + 4 * lq]) * U[rt]);
+            udb[sl][0] = cat8(d16[0], d16[1]);
+            udb[sl][1] = cat8(d16[2], d16[3]);
+          }
+        }
+      }
+      lds_barrier();
+      // ---- phase 2: Y~, U^, S~ update, outputs of chunk c2
+      f32x4 o[2][4];
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int R = 0; R < 4; ++R) o[sl][R] = zero4();
+      if (h2) {
+        const h16* Kb = sm.K[c2 % 3];
+        const HGate& gs = sm.g[c2 % 3];
+        const float rho = gs.gCc * sig;
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) S[sl][m] *= rho;
+        // K^T fragments (keys 32 (m / 2) + 8 (lr % 4) + 4 (m % 2) .. + 3 of
+        // token rows 4 lq + lr / 4 + 16 r) for the state update.
+        h16x4 kt[8][4];
+        auto ktr = [&](int m, int r) { return ld_tr(Kb + tb + 16 * r * HRS + 32 * (m >> 1) + 4 * (m & 1)); };
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) kt[m][r] = ktr(m, r);
+        __builtin_amdgcn_sched_barrier(0);
+        // S~ += K^T U^, breadth-first over the 16 state tiles.
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const h16x8 k0 = cat8(kt[m][0], kt[m][1]);
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) S[sl][m] = mfma32(k0, udb[sl][0], S[sl][m]);
+        }
+        h16x8 pb[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) pb[i] = *reinterpret_cast<const h16x8*>(&sm.Pb[i][l][0]);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const h16x8 k1 = cat8(kt[m][2], kt[m][3]);
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) S[sl][m] = mfma32(k1, udb[sl][1], S[sl][m]);
+        }
+        // Outputs: (P U^)^T and (Q S~)^T hold token 16 R + lr, columns 4 lq + i.
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          const int t = 16 * R + lr;
+          const float og = gs.og[t] * sig, of = gs.of[t];
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) {
+            f32x4 PU = mfma32(cat8(u16[sl][0], u16[sl][1]), pb[pslot(R, 0)], zero4());
+            if (R >= 2) PU = mfma32(cat8(u16[sl][2], u16[sl][3]), pb[pslot(R, 2)], PU);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[sl][R][i] = og * QS[sl][R][i] + of * PU[i];
+          }
+        }
+        sig = gs.cS;
+      }
+      {
+        // Output rows of chunk c2 through a buffer resource covering its valid
+        // rows only (stores past T or of a chunk out of range are dropped).
+        const int nrows = h2 ? min(HC, Ts - c2 * HC) : 0;
+        const TOut* cb = out + head0 + (size_t)max(c2, 0) * HC * tok;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<TOut*>(cb), (short)0, nrows * tok * (int)sizeof(TOut), 0x00020000);
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+          for (int R = 0; R < 4; ++R)
+            store4<TOut>(rs, ((16 * R + lr) * tok + 32 * cw + 16 * sl + 4 * lq) * (int)sizeof(TOut),
+                         o[sl][R]);
+      }
+      lds_barrier();
+    }
+    if (seg == P - 1 && state_out) {
+      float* dst = state_out + (size_t)bh * HD * HD;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dst[kap(m, 4 * lq + i) * HD + 32 * cw + 16 * sl + lr] = sig * S[sl][m][i];
+    }
+  } else {
+    // ------------------------------------------------------------ helpers
+    // The helpers carry the longer chain of dependent steps per phase; they
+    // win instruction issue over the recurrence wave on their SIMD.
+    __builtin_amdgcn_s_setprio(1);
+    const int hw = w - 4, ht = tid - 256;
+    const bf16* qh = q + head0;
+    const bf16* kh = k + head0;
+    const bf16* vh = v + head0;
+    const float* ah = alpha + ((size_t)b * T + (size_t)c0 * HC) * H + h;
+    const float* bhp = beta + ((size_t)b * T + (size_t)c0 * HC) * H + h;
+    // Tile pieces of this thread: rows pr + 16 u (u = 0..3), 8 columns from pc.
+    const int pr = ht >> 4, pc = (ht & 15) * 8;
+    // Each iteration issues K 4 loads (phase 1), gates 2, Q 4, V 4 (phase
+    // 2), in this order; a stream is consumed one iteration after its loads,
+    // when 10 later operations (12 for the gates) have been issued.
+    auto ld_tile = [&](const bf16* base, int c, bf16x8* r) {
+      c = min(max(c, 0), NC - 1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = min(c * HC + pr + 16 * u, Ts - 1);
+        gld16(r[u], base + (size_t)t * tok + pc);
+      }
+    };
+    const int st_off = pr * HRS + pc;
+    auto st_tile = [&](h16* tile, const bf16x8* r) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<h16x8*>(tile + st_off + 16 * u * HRS) = bf16x8_to_h8(r[u]);
+    };
+
+    // Two register slots per stream (slot = iteration parity): a tile is
+    // loaded two iterations before it goes to LDS.
+    bf16x8 kr[2][4], qr[2][4], vr[2][4];
+    float ra[2], rb[2];
+    auto ld_gate = [&](int c, int p) {
+      c = min(c, NC - 1);
+      const int t = min(c * HC + l, Ts - 1);
+      gld4(ra[p], ah + (size_t)t * H);
+      gld4(rb[p], bhp + (size_t)t * H);
+    };
+    ld_tile(kh, 0, kr[0]);
+    ld_tile(kh, 1, kr[1]);
+    ld_gate(0, 0);
+    ld_gate(1, 1);
+    ld_tile(qh, 0, qr[1]);
+    ld_tile(vh, 0, vr[1]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Each iteration issues K 4 loads (phase 1), gates 2, Q 4, V 4 (phase 2),
+    // in this order; a stream is consumed two iterations after its loads,
+    // when 24 later operations (26 for the gates) have been issued.
+    auto wait24 = [&](bf16x8* r) {
+      asm volatile("s_waitcnt vmcnt(24)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) :: "memory");
+    };
+    auto hbody = [&](int it, auto P) {
+      constexpr int p = decltype(P)::value;  // it & 1
+      const int c1 = it - 1, c2 = it - 2;
+      const bool h1 = c1 >= 0 && c1 < NC;
+      const bool h2 = c2 >= 0 && c2 < NC;
+      lane_offset(fb);
+      // ---- phase 1
+      wait24(kr[p]);
+      if (it < NC) st_tile(sm.K[it % 3], kr[p]);  // slot it % 3 was last read in phase 2 of it - 1
+      ld_tile(kh, it + 2, kr[p]);
+      if (h1) {
+        // Diagonal block hw of A for chunk c1, inverted.
+        const h16* Kb = sm.K[c1 % 3];
+        const HGate& gs = sm.g[c1 % 3];
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        f32x4 G = zero4();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h16x8 kf = frag(Kb, hw, j);
+          G = mfma32(kf, kf, G);
+        }
+        f32x4 Lb, LT, Tt, TT;
+        a_diag(gs, wide, hw, G, lr, lq, Lb, LT);
+        if (hw < 3) {
+          inv16<true, true>(Lb, LT, lr, lq, Tt, TT);
+          sm.Dg[2 * hw][l] = cvt4(Tt);
+          sm.Dg[2 * hw + 1][l] = cvt4(TT);
+        } else {
+          inv16<false, true>(Lb, LT, lr, lq, Tt, TT);
+          sm.Dg[6][l] = cvt4(TT);
+        }
+      }
+      if (hw < 2) {
+        // Off-diagonal blocks of A (chunk c1): rows 1, 2 (helper 0) or 3
+        // (helper 1); P block (0, 0) or (1, 0) of chunk c2.
+        if (h1) {
+          const h16* Kb = sm.K[c1 % 3];
+          const HGate& gs = sm.g[c1 % 3];
+          const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+          f32x4 G0 = zero4(), G1 = zero4(), G2 = zero4();
+          if (hw == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const h16x8 k0 = frag(Kb, 0, j), k1 = frag(Kb, 1, j), k2 = frag(Kb, 2, j);
+              G0 = mfma32(k0, k1, G0);  // (1, 0)
+              G1 = mfma32(k0, k2, G1);  // (2, 0)
+              G2 = mfma32(k1, k2, G2);  // (2, 1)
+            }
+            sm.Ab[0][l] = a_offdiag(gs, wide, 1, 0, G0, lr, lq);
+            sm.Ab[1][l] = a_offdiag(gs, wide, 2, 0, G1, lr, lq);
+            sm.Ab[2][l] = a_offdiag(gs, wide, 2, 1, G2, lr, lq);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const h16x8 k3 = frag(Kb, 3, j);
+              G0 = mfma32(frag(Kb, 0, j), k3, G0);  // (3, 0)
+              G1 = mfma32(frag(Kb, 1, j), k3, G1);  // (3, 1)
+              G2 = mfma32(frag(Kb, 2, j), k3, G2);  // (3, 2)
+            }
+            sm.Ab[3][l] = a_offdiag(gs, wide, 3, 0, G0, lr, lq);
+            sm.Ab[4][l] = a_offdiag(gs, wide, 3, 1, G1, lr, lq);
+            sm.Ab[5][l] = a_offdiag(gs, wide, 3, 2, G2, lr, lq);
+          }
+        }
+        if (h2) {
+          const h16* Kb = sm.K[c2 % 3];
+          const HGate& gs = sm.g[c2 % 3];
+          const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+          const int R = hw;
+          f32x4 G = zero4();
+#pragma unroll
+          for (int j = 0; j < 4; ++j) G = mfma32(frag(Kb, 0, j), frag(sm.Q, R, j), G);
+          sm.Pb[pslot(R, 0)][l][0] = p_block(gs, wide, R, 0, G, lr, lq, scale);
+        }
+      } else if (h2) {
+        // P blocks of chunk c2: (1, 1), (2, 0..2) (helper 2) or (3, 0..3) (helper 3).
+        const h16* Kb = sm.K[c2 % 3];
+        const HGate& gs = sm.g[c2 % 3];
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        f32x4 G[4] = {zero4(), zero4(), zero4(), zero4()};
+        if (hw == 2) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 k1 = frag(Kb, 1, j), q2 = frag(sm.Q, 2, j);
+            G[0] = mfma32(k1, frag(sm.Q, 1, j), G[0]);  // (1, 1)
+            G[1] = mfma32(frag(Kb, 0, j), q2, G[1]);    // (2, 0)
+            G[2] = mfma32(k1, q2, G[2]);                // (2, 1)
+            G[3] = mfma32(frag(Kb, 2, j), q2, G[3]);    // (2, 2)
+          }
+          sm.Pb[pslot(1, 1)][l][1] = p_block(gs, wide, 1, 1, G[0], lr, lq, scale);
+#pragma unroll
+          for (int C = 0; C < 3; ++C)
+            sm.Pb[pslot(2, C)][l][C & 1] = p_block(gs, wide, 2, C, G[1 + C], lr, lq, scale);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 q3 = frag(sm.Q, 3, j);
+#pragma unroll
+            for (int C = 0; C < 4; ++C) G[C] = mfma32(frag(Kb, C, j), q3, G[C]);
+          }
+#pragma unroll
+          for (int C = 0; C < 4; ++C)
+            sm.Pb[pslot(3, C)][l][C & 1] = p_block(gs, wide, 3, C, G[C], lr, lq, scale);
+        }
+      }
+      lds_barrier();
+      // ---- phase 2
+      if (hw == 3 && h1) {
+        h16x4 ga[6], d[7];
+        h16x8 tc[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) ga[i] = sm.Ab[i][l];
+#pragma unroll
+        for (int i = 0; i < 7; ++i) d[i] = sm.Dg[i][l];
+        tm_offdiag(ga, d, tc);
+#pragma unroll
+        for (int i = 0; i < 6; ++i) sm.Tc[c1 & 1][i][l] = tc[i];
+      }
+      asm volatile("s_waitcnt vmcnt(26)" : "+v"(ra[p]), "+v"(rb[p]) :: "memory");
+      if (hw == 2 && it < NC) gate_tables(sm.g[it % 3], ra[p], rb[p], it * HC + l < Ts, scale, l);
+      ld_gate(it + 2, p);
+      wait24(qr[p]);
+      if (h1) st_tile(sm.Q, qr[p]);
+      ld_tile(qh, it + 1, qr[p]);
+      wait24(vr[p]);
+      if (h1) {
+        // av V of chunk c1 -> LDS (read by the recurrence waves in phase 1 of
+        // the next iteration).
+        const HGate& gs = sm.g[c1 % 3];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float a = gs.av[pr + 16 * u];
+          h16x8 x;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (h16)(a * (float)vr[p][u][e]);
+          *reinterpret_cast<h16x8*>(sm.V + st_off + 16 * u * HRS) = x;
+        }
+      }
+      ld_tile(vh, it + 1, vr[p]);
+      lds_barrier();
+    };
+    for (int it = 0; it < NIT; it += 2) {
+      hbody(it, ic<0>());
+      if (it + 1 < NIT) hbody(it + 1, ic<1>());
+    }
   }
 }
 
@@ -830,7 +1296,7 @@ static hipError_t launch_head_t(const PrefillArgs& p) {
                        nullptr, nullptr, (float*)nullptr, ws, p.T, p.H, NC, P, L, p.scale);
     hipLaunchKernelGGL(segment_combine_kernel, dim3(BH * 8), dim3(256), 0, st, p.state_in, ws, P);
   }
-  hipLaunchKernelGGL((prefill_head_kernel<0, TOut>), dim3(BH * P), dim3(HNT), 0, st,
+  hipLaunchKernelGGL((prefill_out_kernel<TOut>), dim3(BH * P), dim3(HNT), 0, st,
                      (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.alpha, p.beta,
                      p.state_in, p.state_out, (TOut*)p.out, ws, p.T, p.H, NC, P, L, p.scale);
   return hipGetLastError();
