@@ -101,8 +101,6 @@ constexpr int HC = 64;     // tokens per chunk
 constexpr int HD = 128;    // key and value dimension
 constexpr int HNT = 512;   // threads per work-group
 constexpr int HRS = 144;   // f16 row stride of the LDS tiles (288 bytes)
-constexpr int OFFDIAG_WAVE = 3;
-constexpr int GATE_WAVE = 6;
 constexpr float kWide = 10.f;  // log-gate range above which gates are per element
 
 struct HGate {
@@ -273,30 +271,45 @@ __device__ __forceinline__ int kap(int m, int r) {
   return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
 }
 
-// MODE 0: outputs of one segment (work-group = head * P + segment).
-// MODE 1: transition map of one segment (work-group = head * (P - 1) + segment).
-template <int MODE, class TOut>
-__global__ __launch_bounds__(HNT) void prefill_head_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
-    float* state_out, TOut* __restrict__ out, SegWs ws, int T, int H, int NCT, int P, int L,
-    float scale) {
-  __shared__ HSmem sm;
+// LDS of the transition pass.  Each stage of a chunk runs one iteration after
+// the stage it reads (one work-group barrier per iteration), so the K tiles
+// and gate tables are read up to three iterations after they were written.
+struct __align__(16) TSmem {
+  h16 K[4][HC * HRS];    // K tiles, slot = chunk % 4
+  h16 V[2][HC * HRS];    // av V, slot = chunk % 2
+  h16x8 Tc[2][6][64];    // Tm operands (see tm_offdiag), slot = chunk % 2
+  h16x4 Ab[2][6][64];    // A10, A20, A21, A30, A31, A32 as A operands, slot = chunk % 2
+  h16x4 Dg[2][7][64];    // D(T00), D(T00^T), D(T11), D(T11^T), D(T22), D(T22^T), D(T33^T)
+  HGate g[4];            // slot = chunk % 4
+};
+
+// Transition pass (work-group = head * (P - 1) + segment): the map S -> M_s S
+// + B_s of one segment, from the recurrence run on M~ (from the identity,
+// V = 0) and B~ (from 0) side by side; wave w holds columns 16 w .. 16 w + 15
+// of both.  Iteration i (one work-group barrier at its end):
+//   all waves  K of chunk i -> LDS; recurrence step of chunk i - 3 (X~ of both
+//              states with shared K fragments, Y~, U^, state update); av V of
+//              chunk i - 2 -> LDS
+//   waves 0-3  diagonal block w of A for chunk i - 1, inverted
+//   waves 4-5  off-diagonal blocks of A for chunk i - 1
+//   wave 6     off-diagonal blocks of Tm for chunk i - 2
+//   wave 7     gate tables of chunk i
+// Every chunk of a transition segment lies inside the sequence (only the last
+// segment can be ragged, and it has no transition).
+__global__ __launch_bounds__(HNT) void prefill_transition_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, SegWs ws, int T, int H, int NCT, int P, int L) {
+  __shared__ TSmem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
-  // Waves w and w + 4 share a SIMD and the older wave wins instruction issue;
-  // waves 4-7 carry the longer phase-1 work, so they get the higher priority.
-  if (w >= 4) __builtin_amdgcn_s_setprio(1);
-  const int nseg = MODE == 0 ? P : P - 1;
-  const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const int bh = blockIdx.x / (P - 1), seg = blockIdx.x % (P - 1);
   const int b = bh / H, h = bh % H;
   const int c0 = seg * L;                // first chunk of the segment
   const int NC = min(L, NCT - c0);       // chunks of the segment
-  const int tok = H * HD;  // elements between consecutive tokens
+  const int tok = H * HD;                // elements between consecutive tokens
   const size_t head0 = ((size_t)b * T + (size_t)c0 * HC) * tok + (size_t)h * HD;
   const int Ts = T - c0 * HC;            // tokens from the segment start to the sequence end
-  const bf16* qh = q + head0;
   const bf16* kh = k + head0;
   const bf16* vh = v + head0;
   const float* ah = alpha + ((size_t)b * T + (size_t)c0 * HC) * H + h;
@@ -304,13 +317,6 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
 
   // Tile pieces of this thread: rows pr and pr + 32, 8 columns from pc.
   const int pr = tid >> 4, pc = (tid & 15) * 8;
-  // Every iteration issues the same vector-memory operations in the same
-  // order (output pass: K 2 loads, V 2, output stores 4, gates 2, Q 2;
-  // transition pass: K 2, V 2, gates 2; the chunk index is clamped into
-  // range, surplus loads are never used).  Each stream is consumed one
-  // iteration after its loads were issued, when exactly 10 (output pass) or
-  // 4 (transition pass) later operations have been issued.
-  constexpr int kInFlight = MODE == 0 ? 10 : 4;
   auto ld_tile = [&](const bf16* base, int c, bf16x8* r) {
     c = min(max(c, 0), NC - 1);
 #pragma unroll
@@ -319,294 +325,127 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
       gld16(r[u], base + (size_t)t * tok + pc);
     }
   };
-  // Tile store offset of this thread's first piece (the second is 32 rows on).
-  const int st_off = pr * HRS + pc;
-  auto st_tile = [&](h16* tile, const bf16x8* r) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      *reinterpret_cast<h16x8*>(tile + st_off + 32 * u * HRS) = bf16x8_to_h8(r[u]);
-  };
-  float ra, rb;  // alpha, beta of one token per lane (used by the gate wave)
-  auto ld_gate = [&](int c) {
+  float ra[2], rb[2];  // alpha, beta of token l (used by the gate wave)
+  auto ld_gate = [&](int c, int p) {
     c = min(c, NC - 1);
     const int t = min(c * HC + l, Ts - 1);
-    gld4(ra, ah + (size_t)t * H);
-    gld4(rb, bhp + (size_t)t * H);
+    gld4(ra[p], ah + (size_t)t * H);
+    gld4(rb[p], bhp + (size_t)t * H);
   };
-
-  // S~ tile m: keys kap(m, 4 lq + i), column 16 w + lr.  The transition pass
-  // keeps B~ in S and M~ in SM.
-  f32x4 S[8], SM[8];
-  {
-    const float* s0 = nullptr;
-    if (MODE == 0) s0 = seg == 0 ? (state_in ? state_in + (size_t)bh * HD * HD : nullptr)
-                                 : ws.S + ws.at(bh, seg - 1, P);
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kap(m, 4 * lq + i), col = 16 * w + lr;
-        S[m][i] = s0 ? s0[key * HD + col] : 0.f;
-        SM[m][i] = (MODE == 1 && key == col) ? 1.f : 0.f;
-      }
-  }
-  float sig = 1.f;
-  // The state loads complete before the loop, so no wait inside it refers to them.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-
-  // Zero halves of the P operands (block columns above the diagonal).
-  if (tid < 64) {
-    sm.Pb[0][tid][1] = h16x4{0, 0, 0, 0};
-    sm.Pb[3][tid][1] = h16x4{0, 0, 0, 0};
-  }
-
-  auto offdiag = [&](const HGate& gs, bool wide, int R, int C, f32x4 G) {
-    return a_offdiag(gs, wide, R, C, G, lr, lq);
-  };
-  auto pblock = [&](const HGate& gs, bool wide, int R, int C, f32x4 G) {
-    return p_block(gs, wide, R, C, G, lr, lq, scale);
-  };
-  auto diag = [&](const HGate& gs, bool wide, int R, f32x4 G, f32x4& Lf, f32x4& LTf) {
-    a_diag(gs, wide, R, G, lr, lq, Lf, LTf);
-  };
-  // LDS read offsets.  Fragment (A or B operand) of rows 16 R .. 16 R + 15,
-  // 32-key step j: lane row lr, keys 32 j + 8 lq .. + 7.
-  const int fb = lr * HRS + 8 * lq;
+  // The lane offsets pass through an empty asm once per iteration, so the
+  // compiler folds the constant parts of every LDS address into the
+  // instructions' offset fields instead of hoisting one register per address.
+  auto lane_offset = [](int& x) { asm volatile("" : "+v"(x)); };
+  int st_off = pr * HRS + pc;               // tile store offset (second piece 32 rows on)
+  int fb = lr * HRS + 8 * lq;               // fragment: row lr, keys 32 j + 8 lq .. + 7
+  int tb = (4 * lq + (lr >> 2)) * HRS + 8 * (lr & 3);       // K^T transpose reads
+  int vb = (4 * lq + (lr >> 2)) * HRS + 16 * w + 4 * (lr & 3);  // av V transpose reads
   auto frag = [&](const h16* tile, int R, int j) { return ld8(tile + fb + 16 * R * HRS + 32 * j); };
-  // Transpose reads of K: token row 4 lq + lr / 4 (+ 16 per row step), keys
-  // 32 M + 8 (lr % 4) + 4 h .. + 3.
-  const int tb = (4 * lq + (lr >> 2)) * HRS + 8 * (lr & 3);
-  // Transpose reads of av V: token rows 16 rt + 4 lq + lr / 4, columns 16 w +
-  // 4 (lr % 4) .. + 3.
-  const int vb = (4 * lq + (lr >> 2)) * HRS + 16 * w + 4 * (lr & 3);
 
-  // One register slot per stream: each tile goes to LDS one iteration after
-  // its load was issued, and the next load reuses the registers at once.
-  bf16x8 kr[2], qr[2], vr[2];
-  ld_tile(kh, 0, kr);
-  ld_gate(0);
-  vm_wait<0>(kr);
+  // B~ in S, M~ in SM; tile m holds keys kap(m, 4 lq + i) of column 16 w + lr.
+  f32x4 S[8], SM[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      S[m][i] = 0.f;
+      SM[m][i] = kap(m, 4 * lq + i) == 16 * w + lr ? 1.f : 0.f;
+    }
+  float sig = 1.f;
 
-  auto body = [&](int it) {
-    const int c1 = it - 1, c2 = it - 2;
+  // Two register slots per stream (slot = iteration parity).  Iteration i
+  // issues K of chunk i + 2 (2 loads), gates of chunk i + 2 (2), V of chunk i
+  // (2), in this order, and consumes each two iterations later, when 10
+  // later operations have been issued.
+  bf16x8 kr[2][2], vr[2][2];
+  ld_tile(kh, 0, kr[0]);
+  ld_tile(kh, 1, kr[1]);
+  ld_gate(0, 0);
+  ld_gate(1, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  auto wait10 = [](bf16x8* r) {
+    asm volatile("s_waitcnt vmcnt(10)" : "+v"(r[0]), "+v"(r[1])::"memory");
+  };
+
+  auto body = [&](int it, auto Par) {
+    constexpr int p = decltype(Par)::value;  // it & 1
+    const int c1 = it - 1, c2 = it - 2, c3 = it - 3;
     const bool h1 = c1 >= 0 && c1 < NC;
     const bool h2 = c2 >= 0 && c2 < NC;
+    const bool h3 = c3 >= 0 && c3 < NC;
+    lane_offset(st_off);
+    lane_offset(fb);
+    lane_offset(tb);
+    lane_offset(vb);
+    // Lane index, re-derived each iteration (keeps per-lane LDS addresses and
+    // masks from being hoisted out of the loop as one register each).
+    int ll = l;
+    lane_offset(ll);
+    const int llr = ll & 15, llq = ll >> 4;
 
-    // ------------------------------------------------------------ phase 1
-    // K of chunk it -> LDS (slot it % 3 was last read in phase 2 of it - 1).
-    vm_wait<kInFlight>(kr);
-    if (it < NC) st_tile(sm.K[it % 3], kr);
-    ld_tile(kh, it + 1, kr);
+    wait10(kr[p]);
+    if (it < NC) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<h16x8*>(sm.K[it & 3] + st_off + 32 * u * HRS) = bf16x8_to_h8(kr[p][u]);
+    }
+    ld_tile(kh, it + 2, kr[p]);
 
-    f32x4 X[4], QS[4], XM[4];
-    if (h2) {
-      const h16* Kb = sm.K[c2 % 3];
-      const HGate& gs = sm.g[c2 % 3];
-      // All 16 K fragments are requested first; the products then run
-      // breadth-first over the row tiles (consecutive MFMAs independent)
-      // while the Q fragments are requested one per product.
-      h16x8 kf[4][4], sb[4];
+    if (h3) {
+      // ---- recurrence step of chunk c3
+      const h16* Kb = sm.K[c3 & 3];
+      const HGate& gs = sm.g[c3 & 3];
+      const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+      // X~ of B~ and of M~ share the K fragments.  Per 32-key step j: four K
+      // fragments, the f16 state rows of that step, eight products; the
+      // fragments of step j + 1 are requested during the products of step j.
+      f32x4 X[4], XM[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int rt = 0; rt < 4; ++rt) X[rt] = zero4(), XM[rt] = zero4();
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) kf[rt][j] = frag(Kb, rt, j);
+      for (int j = 0; j < 4; ++j) {
+        h16x8 kf[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sb[j] = cat8(cvt4(S[2 * j]), cvt4(S[2 * j + 1]));
+        for (int rt = 0; rt < 4; ++rt) kf[rt] = frag(Kb, rt, j);
+        const h16x8 sb = cat8(cvt4(S[2 * j]), cvt4(S[2 * j + 1]));
+        const h16x8 sm8 = cat8(cvt4(SM[2 * j]), cvt4(SM[2 * j + 1]));
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) X[rt] = zero4(), QS[rt] = zero4(), XM[rt] = zero4();
-      if constexpr (MODE == 0) {
-        h16x8 qf[4][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            X[rt] = mfma32(kf[rt][j], sb[j], X[rt]);
-            qf[rt][j] = frag(sm.Q, rt, j);
-          }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int R = 0; R < 4; ++R) QS[R] = mfma32(sb[j], qf[R][j], QS[R]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // K fragment reads
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // X product
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // Q fragment read
+        for (int rt = 0; rt < 4; ++rt) {
+          X[rt] = mfma32(kf[rt], sb, X[rt]);
+          XM[rt] = mfma32(kf[rt], sm8, XM[rt]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // Q S products
-      } else {
-        // X~ of B~ and of M~ share the K fragments.
-        h16x8 sm8[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sm8[j] = cat8(cvt4(SM[2 * j]), cvt4(SM[2 * j + 1]));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            X[rt] = mfma32(kf[rt][j], sb[j], X[rt]);
-            XM[rt] = mfma32(kf[rt][j], sm8[j], XM[rt]);
-          }
-        // Fragments of steps j + 2 are requested while step j is multiplied.
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       const float rho = gs.gCc * sig;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        S[m] *= rho;
-        if constexpr (MODE == 1) SM[m] *= rho;
-      }
-    }
-
-    if (w < 4) {
-      if (h1) {
-        // Diagonal block R = w of A for chunk c1, inverted.
-        const h16* Kb = sm.K[c1 % 3];
-        const HGate& gs = sm.g[c1 % 3];
-        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-        f32x4 G = zero4();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const h16x8 kf = frag(Kb, w, j);
-          G = mfma32(kf, kf, G);
-        }
-        f32x4 L, LT, Tt, TT;
-        diag(gs, wide, w, G, L, LT);
-        if (w < 3) {
-          inv16<true, true>(L, LT, lr, lq, Tt, TT);
-          sm.Dg[2 * w][l] = cvt4(Tt);
-          sm.Dg[2 * w + 1][l] = cvt4(TT);
-        } else {
-          inv16<false, true>(L, LT, lr, lq, Tt, TT);
-          sm.Dg[6][l] = cvt4(TT);
-        }
-      }
-    } else if (w < 6) {
-      // Off-diagonal blocks of A (chunk c1): rows 1, 2 (wave 4) or 3 (wave 5);
-      // P block (0, 0) (wave 4) or (1, 0) (wave 5) of chunk c2.
-      if (h1) {
-        const h16* Kb = sm.K[c1 % 3];
-        const HGate& gs = sm.g[c1 % 3];
-        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-        f32x4 G0 = zero4(), G1 = zero4(), G2 = zero4();
-        if (w == 4) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h16x8 k0 = frag(Kb, 0, j), k1 = frag(Kb, 1, j), k2 = frag(Kb, 2, j);
-            G0 = mfma32(k0, k1, G0);  // (1, 0)
-            G1 = mfma32(k0, k2, G1);  // (2, 0)
-            G2 = mfma32(k1, k2, G2);  // (2, 1)
-          }
-          sm.Ab[0][l] = offdiag(gs, wide, 1, 0, G0);
-          sm.Ab[1][l] = offdiag(gs, wide, 2, 0, G1);
-          sm.Ab[2][l] = offdiag(gs, wide, 2, 1, G2);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h16x8 k3 = frag(Kb, 3, j);
-            G0 = mfma32(frag(Kb, 0, j), k3, G0);  // (3, 0)
-            G1 = mfma32(frag(Kb, 1, j), k3, G1);  // (3, 1)
-            G2 = mfma32(frag(Kb, 2, j), k3, G2);  // (3, 2)
-          }
-          sm.Ab[3][l] = offdiag(gs, wide, 3, 0, G0);
-          sm.Ab[4][l] = offdiag(gs, wide, 3, 1, G1);
-          sm.Ab[5][l] = offdiag(gs, wide, 3, 2, G2);
-        }
-      }
-      if (MODE == 0 && h2) {
-        const h16* Kb = sm.K[c2 % 3];
-        const HGate& gs = sm.g[c2 % 3];
-        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-        const int R = w - 4;
-        f32x4 G = zero4();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) G = mfma32(frag(Kb, 0, j), frag(sm.Q, R, j), G);
-        sm.Pb[pslot(R, 0)][l][0] = pblock(gs, wide, R, 0, G);
-      }
-    } else {
-      // P blocks of chunk c2: (1, 1), (2, 0..2) (wave 6) or (3, 0..3) (wave 7).
-      if (MODE == 0 && h2) {
-        const h16* Kb = sm.K[c2 % 3];
-        const HGate& gs = sm.g[c2 % 3];
-        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-        f32x4 G[4] = {zero4(), zero4(), zero4(), zero4()};
-        if (w == 6) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h16x8 k1 = frag(Kb, 1, j), q2 = frag(sm.Q, 2, j);
-            G[0] = mfma32(k1, frag(sm.Q, 1, j), G[0]);  // (1, 1)
-            G[1] = mfma32(frag(Kb, 0, j), q2, G[1]);    // (2, 0)
-            G[2] = mfma32(k1, q2, G[2]);                // (2, 1)
-            G[3] = mfma32(frag(Kb, 2, j), q2, G[3]);    // (2, 2)
-          }
-          sm.Pb[pslot(1, 1)][l][1] = pblock(gs, wide, 1, 1, G[0]);
-#pragma unroll
-          for (int C = 0; C < 3; ++C) sm.Pb[pslot(2, C)][l][C & 1] = pblock(gs, wide, 2, C, G[1 + C]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h16x8 q3 = frag(sm.Q, 3, j);
-#pragma unroll
-            for (int C = 0; C < 4; ++C) G[C] = mfma32(frag(Kb, C, j), q3, G[C]);
-          }
-#pragma unroll
-          for (int C = 0; C < 4; ++C) sm.Pb[pslot(3, C)][l][C & 1] = pblock(gs, wide, 3, C, G[C]);
-        }
-      }
-    }
-
-    vm_wait<kInFlight>(vr);
-    if (h2) {
-      // av V of chunk c2 -> LDS.
-      const HGate& gs = sm.g[c2 % 3];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float a = gs.av[pr + 32 * u];
-        h16x8 x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (h16)(a * (float)vr[u][e]);
-        *reinterpret_cast<h16x8*>(sm.V + st_off + 32 * u * HRS) = x;
-      }
-    }
-    ld_tile(vh, it - 1, vr);
-    lds_barrier();
-
-    // ------------------------------------------------------------ phase 2
-    f32x4 o[4] = {zero4(), zero4(), zero4(), zero4()};
-    if (h2) {
-      const h16* Kb = sm.K[c2 % 3];
-      const HGate& gs = sm.g[c2 % 3];
-      const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-      // LDS operands are requested ahead of the dependent chain: av V, bx and
-      // Tm for Y~ and U^ and the first half of the K^T fragments of the state
-      // update (keys 32 (m / 2) + 8 (lr % 4) + 4 (m % 2) .. + 3 of token rows
-      // 4 lq + lr / 4 + 16 r) up front, the second half and the P operands
-      // once U^ is formed.
-      const int s = c2 & 1;
+      for (int m = 0; m < 8; ++m) S[m] *= rho, SM[m] *= rho;
+      // av V, bx and Tm for Y~ and U^ and the first half of the K^T fragments
+      // (keys 32 (m / 2) + 8 (lr % 4) + 4 (m % 2) .. + 3 of token rows
+      // 4 lq + lr / 4 + 16 r) are requested ahead of the dependent chain.
       h16x4 va[4], kt[8][4];
       f32x4 bv[4];
       h16x8 tc[6];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        va[rt] = ld_tr(sm.V + vb + 16 * rt * HRS);
-        bv[rt] = ldf4(&gs.bx[16 * rt + 4 * lq]);
+        va[rt] = ld_tr(sm.V[c3 & 1] + vb + 16 * rt * HRS);
+        bv[rt] = ldf4(&gs.bx[16 * rt + 4 * llq]);
       }
 #pragma unroll
-      for (int i = 0; i < 6; ++i) tc[i] = sm.Tc[s][i][l];
+      for (int i = 0; i < 6; ++i) tc[i] = sm.Tc[c3 & 1][i][ll];
       auto ktr = [&](int m, int r) { return ld_tr(Kb + tb + 16 * r * HRS + 32 * (m >> 1) + 4 * (m & 1)); };
 #pragma unroll
       for (int m = 0; m < 8; ++m) kt[m][0] = ktr(m, 0), kt[m][1] = ktr(m, 1);
       __builtin_amdgcn_sched_barrier(0);
       // U^ = T0 Y~ with Y~ = av V - (bx sigma) X~ (accumulator layout: tokens
-      // 16 rt + 4 lq + i, column lr); the transition pass also forms it for M~
-      // (V = 0).  Returns U^ (f16) and the state-update operand (U^, or
-      // exp(gam_C - gam) U^ for a wide chunk).
-      auto solve = [&](const f32x4* Xs, bool withv, h16x4* u16, h16x8* udb) {
+      // 16 rt + 4 lq + i, column lr), for B~ (with V) and M~ (V = 0).  Returns
+      // U^ weighted for the state update (by exp(gam_C - gam) for a wide chunk).
+      auto solve = [&](const f32x4* Xs, bool withv, h16x8* udb) {
         h16x4 y16[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -624,118 +463,152 @@ __global__ __launch_bounds__(HNT) void prefill_head_kernel(
         U[3] = mfma32(tc[4], ylo, zero4());
         U[2] = mfma32(tc[3], yhi, U[2]);
         U[3] = mfma32(tc[5], yhi, U[3]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) u16[rt] = cvt4(U[rt]);
+        h16x4 u16[4];
         if (!wide) {
-          udb[0] = cat8(u16[0], u16[1]);
-          udb[1] = cat8(u16[2], u16[3]);
-        } else {
-          h16x4 d16[4];
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) d16[rt] = cvt4(ldf4(&gs.dec[16 * rt + 4 * lq]) * U[rt]);
-          udb[0] = cat8(d16[0], d16[1]);
-          udb[1] = cat8(d16[2], d16[3]);
+          for (int rt = 0; rt < 4; ++rt) u16[rt] = cvt4(U[rt]);
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) u16[rt] = cvt4(ldf4(&gs.dec[16 * rt + 4 * llq]) * U[rt]);
         }
+        udb[0] = cat8(u16[0], u16[1]);
+        udb[1] = cat8(u16[2], u16[3]);
       };
-      h16x4 u16[4], u16m[4];
       h16x8 udb[2], udbm[2];
-      solve(X, true, u16, udb);
-      if constexpr (MODE == 1) solve(XM, false, u16m, udbm);
+      solve(X, true, udb);
+      solve(XM, false, udbm);
 #pragma unroll
       for (int m = 0; m < 8; ++m) kt[m][2] = ktr(m, 2), kt[m][3] = ktr(m, 3);
       __builtin_amdgcn_sched_barrier(0);
-      // S~ += K^T U^, breadth-first over the eight state tiles.
+      // S~ += K^T U^, breadth-first over the sixteen state tiles.
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        S[m] = mfma32(cat8(kt[m][0], kt[m][1]), udb[0], S[m]);
-        if constexpr (MODE == 1) SM[m] = mfma32(cat8(kt[m][0], kt[m][1]), udbm[0], SM[m]);
-      }
-      h16x8 pb[6];
-      if constexpr (MODE == 0) {
-#pragma unroll
-        for (int i = 0; i < 6; ++i) pb[i] = *reinterpret_cast<const h16x8*>(&sm.Pb[i][l][0]);
+        const h16x8 k0 = cat8(kt[m][0], kt[m][1]);
+        S[m] = mfma32(k0, udb[0], S[m]);
+        SM[m] = mfma32(k0, udbm[0], SM[m]);
       }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        S[m] = mfma32(cat8(kt[m][2], kt[m][3]), udb[1], S[m]);
-        if constexpr (MODE == 1) SM[m] = mfma32(cat8(kt[m][2], kt[m][3]), udbm[1], SM[m]);
-      }
-      if constexpr (MODE == 0) {
-        // Outputs: (P U^)^T and (Q S~)^T hold token 16 R + lr, columns 4 lq + i.
-        const h16x8 ulo = cat8(u16[0], u16[1]), uhi = cat8(u16[2], u16[3]);
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-          f32x4 PU = mfma32(ulo, pb[pslot(R, 0)], zero4());
-          if (R >= 2) PU = mfma32(uhi, pb[pslot(R, 2)], PU);
-          const int t = 16 * R + lr;
-          const float og = gs.og[t] * sig, of = gs.of[t];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[R][i] = og * QS[R][i] + of * PU[i];
-        }
+        const h16x8 k1 = cat8(kt[m][2], kt[m][3]);
+        S[m] = mfma32(k1, udb[1], S[m]);
+        SM[m] = mfma32(k1, udbm[1], SM[m]);
       }
       sig = gs.cS;
     }
-    if constexpr (MODE == 0) {
-      // Output rows of chunk c2 through a buffer resource covering its valid
-      // rows only: stores past T (or of a chunk out of range) are dropped by
-      // the range check, so every iteration issues the same stores.
-      const int nrows = h2 ? min(HC, Ts - c2 * HC) : 0;
-      const TOut* cb = out + head0 + (size_t)max(c2, 0) * HC * tok;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<TOut*>(cb), (short)0, nrows * tok * (int)sizeof(TOut), 0x00020000);
+
+    if (w < 4) {
+      if (h1) {
+        // Diagonal block R = w of A for chunk c1, inverted.
+        const h16* Kb = sm.K[c1 & 3];
+        const HGate& gs = sm.g[c1 & 3];
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        f32x4 G = zero4();
 #pragma unroll
-      for (int R = 0; R < 4; ++R)
-        store4<TOut>(rs, ((16 * R + lr) * tok + 16 * w + 4 * lq) * (int)sizeof(TOut), o[R]);
+        for (int j = 0; j < 4; ++j) {
+          const h16x8 kf = frag(Kb, w, j);
+          G = mfma32(kf, kf, G);
+        }
+        f32x4 Lb, LT, Tt, TT;
+        a_diag(gs, wide, w, G, llr, llq, Lb, LT);
+        if (w < 3) {
+          inv16<true, true>(Lb, LT, llr, llq, Tt, TT);
+          sm.Dg[c1 & 1][2 * w][ll] = cvt4(Tt);
+          sm.Dg[c1 & 1][2 * w + 1][ll] = cvt4(TT);
+        } else {
+          inv16<false, true>(Lb, LT, llr, llq, Tt, TT);
+          sm.Dg[c1 & 1][6][ll] = cvt4(TT);
+        }
+      }
+    } else if (w < 6) {
+      if (h1) {
+        // Off-diagonal blocks of A for chunk c1: rows 1, 2 (wave 4) or 3 (wave 5).
+        const h16* Kb = sm.K[c1 & 3];
+        const HGate& gs = sm.g[c1 & 3];
+        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+        h16x4* ab = sm.Ab[c1 & 1][0];
+        f32x4 G0 = zero4(), G1 = zero4(), G2 = zero4();
+        if (w == 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 k0 = frag(Kb, 0, j), k1 = frag(Kb, 1, j), k2 = frag(Kb, 2, j);
+            G0 = mfma32(k0, k1, G0);  // (1, 0)
+            G1 = mfma32(k0, k2, G1);  // (2, 0)
+            G2 = mfma32(k1, k2, G2);  // (2, 1)
+          }
+          ab[0 * 64 + ll] = a_offdiag(gs, wide, 1, 0, G0, llr, llq);
+          ab[1 * 64 + ll] = a_offdiag(gs, wide, 2, 0, G1, llr, llq);
+          ab[2 * 64 + ll] = a_offdiag(gs, wide, 2, 1, G2, llr, llq);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 k3 = frag(Kb, 3, j);
+            G0 = mfma32(frag(Kb, 0, j), k3, G0);  // (3, 0)
+            G1 = mfma32(frag(Kb, 1, j), k3, G1);  // (3, 1)
+            G2 = mfma32(frag(Kb, 2, j), k3, G2);  // (3, 2)
+          }
+          ab[3 * 64 + ll] = a_offdiag(gs, wide, 3, 0, G0, llr, llq);
+          ab[4 * 64 + ll] = a_offdiag(gs, wide, 3, 1, G1, llr, llq);
+          ab[5 * 64 + ll] = a_offdiag(gs, wide, 3, 2, G2, llr, llq);
+        }
+      }
+    } else if (w == 6) {
+      if (h2) {
+        // Off-diagonal blocks of Tm for chunk c2 (block forward substitution).
+        h16x4 ga[6], d[7];
+        h16x8 tc[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) ga[i] = sm.Ab[c2 & 1][i][ll];
+#pragma unroll
+        for (int i = 0; i < 7; ++i) d[i] = sm.Dg[c2 & 1][i][ll];
+        tm_offdiag(ga, d, tc);
+#pragma unroll
+        for (int i = 0; i < 6; ++i) sm.Tc[c2 & 1][i][ll] = tc[i];
+      }
     }
 
-    if (w == OFFDIAG_WAVE && h1) {
-      h16x4 ga[6], d[7];
-      h16x8 tc[6];
-#pragma unroll
-      for (int i = 0; i < 6; ++i) ga[i] = sm.Ab[i][l];
-#pragma unroll
-      for (int i = 0; i < 7; ++i) d[i] = sm.Dg[i][l];
-      tm_offdiag(ga, d, tc);
-#pragma unroll
-      for (int i = 0; i < 6; ++i) sm.Tc[c1 & 1][i][l] = tc[i];
-    }
+    asm volatile("s_waitcnt vmcnt(10)" : "+v"(ra[p]), "+v"(rb[p])::"memory");
+    if (w == 7 && it < NC) gate_tables(sm.g[it & 3], ra[p], rb[p], it * HC + ll < Ts, 1.f, ll);
+    ld_gate(it + 2, p);
 
-    vm_wait<kInFlight>(ra, rb);
-    if (w == GATE_WAVE && it < NC) {
-      // Gate tables of chunk it (lane = token).
-      gate_tables(sm.g[it % 3], ra, rb, it * HC + l < Ts, scale, l);
+    wait10(vr[p]);
+    if (h2) {
+      // av V of chunk c2 -> LDS (its V tile was loaded at iteration c2).
+      const HGate& gs = sm.g[c2 & 3];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float a = gs.av[pr + 32 * u];
+        h16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (h16)(a * (float)vr[p][u][e]);
+        *reinterpret_cast<h16x8*>(sm.V[c2 & 1] + st_off + 32 * u * HRS) = x;
+      }
     }
-    ld_gate(it + 1);
-    if constexpr (MODE == 0) {
-      vm_wait<kInFlight>(qr);
-      if (h1) st_tile(sm.Q, qr);
-      ld_tile(qh, it, qr);
-    }
+    ld_tile(vh, it, vr[p]);
     lds_barrier();
   };
 
-  // Chunk c's outputs are formed at iteration c + 2.
-  const int NIT = NC + 2;
-  for (int it = 0; it < NIT; ++it) body(it);
+  // Chunk c completes its recurrence step at iteration c + 3.
+  const int NIT = NC + 3;
+  for (int it = 0; it < NIT; it += 2) {
+    body(it, ic<0>());
+    if (it + 1 < NIT) body(it + 1, ic<1>());
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  float* dst = nullptr;
-  float* dstm = nullptr;
-  if (MODE == 0) {
-    if (seg == P - 1 && state_out) dst = state_out + (size_t)bh * HD * HD;
-  } else {
-    dst = ws.B + ws.at(bh, seg, P);
-    dstm = ws.M + ws.at(bh, seg, P);
-  }
-  if (dst) {
+  float* dst = ws.B + ws.at(bh, seg, P);
+  float* dstm = ws.M + ws.at(bh, seg, P);
+  // Recomputed here rather than kept live from the state set-up.
+  int lq4 = 4 * lq, col = 16 * w + lr;
+  lane_offset(lq4);
+  lane_offset(col);
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = kap(m, 4 * lq + i) * HD + 16 * w + lr;
-        dst[o] = sig * S[m][i];
-        if (MODE == 1) dstm[o] = sig * SM[m][i];
-      }
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int o = kap(m, lq4 + i) * HD + col;
+      dst[o] = sig * S[m][i];
+      dstm[o] = sig * SM[m][i];
+    }
 }
 
 // Output pass with wave roles (work-group = head * P + segment).  Waves 0-3
@@ -1291,9 +1164,8 @@ static hipError_t launch_head_t(const PrefillArgs& p) {
     ws.M = (float*)p.workspace;
     ws.B = ws.M + n;
     ws.S = ws.B + n;
-    hipLaunchKernelGGL((prefill_head_kernel<1, float>), dim3(BH * (P - 1)), dim3(HNT), 0, st,
-                       (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.alpha, p.beta,
-                       nullptr, nullptr, (float*)nullptr, ws, p.T, p.H, NC, P, L, p.scale);
+    hipLaunchKernelGGL(prefill_transition_kernel, dim3(BH * (P - 1)), dim3(HNT), 0, st,
+                       (const bf16*)p.k, (const bf16*)p.v, p.alpha, p.beta, ws, p.T, p.H, NC, P, L);
     hipLaunchKernelGGL(segment_combine_kernel, dim3(BH * 8), dim3(256), 0, st, p.state_in, ws, P);
   }
   hipLaunchKernelGGL((prefill_out_kernel<TOut>), dim3(BH * P), dim3(HNT), 0, st,
