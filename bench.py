@@ -78,13 +78,12 @@ def decode_swa_bytes(d, n_slots, esize=2):
 PROFILE = "profiles/gdn_kernels_bench_workloads.md"
 # The long32k prefill call launches three kernels (segment transition pass,
 # combine pass, output pass); its entry sums them.
-PREFILL_KERNELS = ("prefill_head_kernel<1,float> + segment_combine_kernel + "
-                   "prefill_head_kernel<0,bf16>")
+PREFILL_KERNELS = "prefill_transition_kernel + segment_combine_kernel + prefill_out_kernel<bf16>"
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="a683234c27feda93344398fb14b2405c2519dcd6",
-        fetch_kib=262220 + 71711 + 404599, write_kib=36737 + 14336 + 264192,
+        sha1="25cc6d6ec9848d990a8b5a34bb15c4213211b026",
+        fetch_kib=258220 + 71711 + 404975, write_kib=28672 + 14336 + 264195,
         profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",

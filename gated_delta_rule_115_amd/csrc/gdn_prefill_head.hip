@@ -26,26 +26,19 @@
 // sigma <- c_S; X = K S = sigma K S~ and Q S = sigma Q S~ fold sigma into
 // bx and og.
 //
-// Work split.  The work-group has 8 waves; wave w keeps columns 16 w .. 16 w
-// + 15 of S~ (128 x 16, f32) in eight MFMA accumulator tiles for the whole
-// sequence and runs that slice's recurrence.  Everything that does not depend
-// on S -- gates, Gram products, the triangular inverse, Q K^T -- is computed
-// once per chunk and shared through LDS.  Iteration i has two phases, each
-// ended by a work-group barrier:
-//   phase 1  all:      X~ = K S~ and (Q S~)^T of chunk i - 2
-//            waves 0-3: diagonal block w of A for chunk i - 1, inverted as
-//                      (I + L)^-1 = (I + L^8)(I + L^4)(I + L^2)(I - L)
-//            waves 4-7: off-diagonal blocks of A (chunk i - 1) and the blocks
-//                      of P (chunk i - 2)
-//            all:      av V of chunk i - 2 -> LDS
-//   phase 2  all:      Y~, U^ = T0 Y~, S~ update, (P U^)^T and the output rows
-//                      of chunk i - 2
-//            wave 3:   off-diagonal blocks of Tm for chunk i - 1 (block
-//                      forward substitution)
-//            wave 6:   gate tables of chunk i
-//            all:      K of chunk i and Q of chunk i - 1 -> LDS as f16
-// Global loads run one to two iterations ahead of their use (K of chunk
-// i + 1, Q of chunk i, V of chunk i - 1 are issued in phase 1 of iteration i).
+// Work split.  One work-group of 8 waves per head and sequence segment (see
+// below).  The state S~ (128 x 128, f32) lives in MFMA accumulator tiles,
+// 16-column slices per wave, for the whole segment.  Everything that does not
+// depend on S -- gates, Gram products, the triangular inverse, Q K^T -- is
+// computed once per chunk and shared through LDS; a chunk moves through
+// stages (tile to LDS, Gram blocks and diagonal inverses, Tm off-diagonal
+// blocks, recurrence step) in successive iterations, so the stages of
+// different chunks run side by side between two work-group barriers.  The
+// diagonal blocks are inverted as (I + L)^-1 = (I + L^8)(I + L^4)(I + L^2)
+// (I - L); the off-diagonal blocks of Tm follow by block forward
+// substitution.  Global loads are inline asm issued one or two iterations
+// ahead of their use in a fixed order per iteration, so every wait is a
+// fixed vmcnt and loads stay in flight across the loop back-edge.
 //
 // Operand layouts: see gdn_f16ops.h.  Contractions over the key index use, in
 // each 32-key step j, lane group q = l / 16 for keys 32 j + 8 q .. + 7, so K
@@ -71,17 +64,20 @@
 // L chunks.  A chunk maps the state entering it affinely, S -> M_c S + B_c,
 // with M_c = g_C I - c_S K^T T0 diag(bx) K (the same recurrence with V = 0)
 // and B_c the image of S = 0; a segment composes these maps.  Three passes:
-//   transition pass  (MODE 1, work-group per head and segment s < P - 1): the
+//   transition pass  (work-group per head and segment s < P - 1): the
 //                    recurrence run on M (from the identity, V = 0) and B
 //                    (from 0) side by side -- wave w holds columns
-//                    16 w .. 16 w + 15 of both -- giving the segment's map
-//                    M_s, B_s (f32, workspace);
+//                    16 w .. 16 w + 15 of both, so each K fragment serves two
+//                    products -- giving the segment's map M_s, B_s (f32,
+//                    workspace); all waves share the per-chunk stages;
 //   combine pass     (work-group per head and 16-column slice): S_0 = state
 //                    in, S_{s+1} = M_s S_s + B_s (f32 products), the initial
 //                    state of every segment (workspace);
-//   output pass      (MODE 0, work-group per head and segment): the recurrence
-//                    and the outputs of the segment from its initial state;
-//                    the last segment writes the final state.
+//   output pass      (work-group per head and segment): the recurrence and
+//                    the outputs of the segment from its initial state, the
+//                    last segment writing the final state; waves 0-3 run the
+//                    recurrence (two 16-column slices each), waves 4-7 do the
+//                    loads, conversions and shared per-chunk stages.
 // This is an exact rewrite of the same recurrence (composition of the affine
 // chunk maps); each pass rounds like the single pass does.
 //
@@ -391,180 +387,185 @@ __global__ __launch_bounds__(HNT) void prefill_transition_kernel(
     }
     ld_tile(kh, it + 2, kr[p]);
 
-    if (h3) {
-      // ---- recurrence step of chunk c3
-      const h16* Kb = sm.K[c3 & 3];
-      const HGate& gs = sm.g[c3 & 3];
-      const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-      // X~ of B~ and of M~ share the K fragments.  Per 32-key step j: four K
-      // fragments, the f16 state rows of that step, eight products; the
-      // fragments of step j + 1 are requested during the products of step j.
-      f32x4 X[4], XM[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) X[rt] = zero4(), XM[rt] = zero4();
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h16x8 kf[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) kf[rt] = frag(Kb, rt, j);
-        const h16x8 sb = cat8(cvt4(S[2 * j]), cvt4(S[2 * j + 1]));
-        const h16x8 sm8 = cat8(cvt4(SM[2 * j]), cvt4(SM[2 * j + 1]));
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          X[rt] = mfma32(kf[rt], sb, X[rt]);
-          XM[rt] = mfma32(kf[rt], sm8, XM[rt]);
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      const float rho = gs.gCc * sig;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) S[m] *= rho, SM[m] *= rho;
-      // av V, bx and Tm for Y~ and U^ and the first half of the K^T fragments
-      // (keys 32 (m / 2) + 8 (lr % 4) + 4 (m % 2) .. + 3 of token rows
-      // 4 lq + lr / 4 + 16 r) are requested ahead of the dependent chain.
-      h16x4 va[4], kt[8][4];
-      f32x4 bv[4];
-      h16x8 tc[6];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        va[rt] = ld_tr(sm.V[c3 & 1] + vb + 16 * rt * HRS);
-        bv[rt] = ldf4(&gs.bx[16 * rt + 4 * llq]);
-      }
-#pragma unroll
-      for (int i = 0; i < 6; ++i) tc[i] = sm.Tc[c3 & 1][i][ll];
-      auto ktr = [&](int m, int r) { return ld_tr(Kb + tb + 16 * r * HRS + 32 * (m >> 1) + 4 * (m & 1)); };
-#pragma unroll
-      for (int m = 0; m < 8; ++m) kt[m][0] = ktr(m, 0), kt[m][1] = ktr(m, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      // U^ = T0 Y~ with Y~ = av V - (bx sigma) X~ (accumulator layout: tokens
-      // 16 rt + 4 lq + i, column lr), for B~ (with V) and M~ (V = 0).  Returns
-      // U^ weighted for the state update (by exp(gam_C - gam) for a wide chunk).
-      auto solve = [&](const f32x4* Xs, bool withv, h16x8* udb) {
-        h16x4 y16[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          f32x4 y;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            y[i] = (withv ? (float)va[rt][i] : 0.f) - (bv[rt][i] * sig) * Xs[rt][i];
-          y16[rt] = cvt4(y);
-        }
-        const h16x8 ylo = cat8(y16[0], y16[1]), yhi = cat8(y16[2], y16[3]);
-        f32x4 U[4];
-        U[0] = mfma32(tc[0], ylo, zero4());
-        U[1] = mfma32(tc[1], ylo, zero4());
-        U[2] = mfma32(tc[2], ylo, zero4());
-        U[3] = mfma32(tc[4], ylo, zero4());
-        U[2] = mfma32(tc[3], yhi, U[2]);
-        U[3] = mfma32(tc[5], yhi, U[3]);
-        h16x4 u16[4];
-        if (!wide) {
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) u16[rt] = cvt4(U[rt]);
-        } else {
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) u16[rt] = cvt4(ldf4(&gs.dec[16 * rt + 4 * llq]) * U[rt]);
-        }
-        udb[0] = cat8(u16[0], u16[1]);
-        udb[1] = cat8(u16[2], u16[3]);
-      };
-      h16x8 udb[2], udbm[2];
-      solve(X, true, udb);
-      solve(XM, false, udbm);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) kt[m][2] = ktr(m, 2), kt[m][3] = ktr(m, 3);
-      __builtin_amdgcn_sched_barrier(0);
-      // S~ += K^T U^, breadth-first over the sixteen state tiles.
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const h16x8 k0 = cat8(kt[m][0], kt[m][1]);
-        S[m] = mfma32(k0, udb[0], S[m]);
-        SM[m] = mfma32(k0, udbm[0], SM[m]);
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const h16x8 k1 = cat8(kt[m][2], kt[m][3]);
-        S[m] = mfma32(k1, udb[1], S[m]);
-        SM[m] = mfma32(k1, udbm[1], SM[m]);
-      }
-      sig = gs.cS;
-    }
-
-    if (w < 4) {
-      if (h1) {
-        // Diagonal block R = w of A for chunk c1, inverted.
-        const h16* Kb = sm.K[c1 & 3];
-        const HGate& gs = sm.g[c1 & 3];
+    auto recurrence = [&]() {
+      if (h3) {
+        // ---- recurrence step of chunk c3
+        const h16* Kb = sm.K[c3 & 3];
+        const HGate& gs = sm.g[c3 & 3];
         const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-        f32x4 G = zero4();
-#pragma unroll
+        // X~ of B~ and of M~ share the K fragments.  Per 32-key step j: four K
+        // fragments, the f16 state rows of that step, eight products; the
+        // fragments of step j + 1 are requested during the products of step j.
+        f32x4 X[4], XM[4];
+  #pragma unroll
+        for (int rt = 0; rt < 4; ++rt) X[rt] = zero4(), XM[rt] = zero4();
+  #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const h16x8 kf = frag(Kb, w, j);
-          G = mfma32(kf, kf, G);
-        }
-        f32x4 Lb, LT, Tt, TT;
-        a_diag(gs, wide, w, G, llr, llq, Lb, LT);
-        if (w < 3) {
-          inv16<true, true>(Lb, LT, llr, llq, Tt, TT);
-          sm.Dg[c1 & 1][2 * w][ll] = cvt4(Tt);
-          sm.Dg[c1 & 1][2 * w + 1][ll] = cvt4(TT);
-        } else {
-          inv16<false, true>(Lb, LT, llr, llq, Tt, TT);
-          sm.Dg[c1 & 1][6][ll] = cvt4(TT);
-        }
-      }
-    } else if (w < 6) {
-      if (h1) {
-        // Off-diagonal blocks of A for chunk c1: rows 1, 2 (wave 4) or 3 (wave 5).
-        const h16* Kb = sm.K[c1 & 3];
-        const HGate& gs = sm.g[c1 & 3];
-        const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-        h16x4* ab = sm.Ab[c1 & 1][0];
-        f32x4 G0 = zero4(), G1 = zero4(), G2 = zero4();
-        if (w == 4) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h16x8 k0 = frag(Kb, 0, j), k1 = frag(Kb, 1, j), k2 = frag(Kb, 2, j);
-            G0 = mfma32(k0, k1, G0);  // (1, 0)
-            G1 = mfma32(k0, k2, G1);  // (2, 0)
-            G2 = mfma32(k1, k2, G2);  // (2, 1)
+          h16x8 kf[4];
+  #pragma unroll
+          for (int rt = 0; rt < 4; ++rt) kf[rt] = frag(Kb, rt, j);
+          const h16x8 sb = cat8(cvt4(S[2 * j]), cvt4(S[2 * j + 1]));
+          const h16x8 sm8 = cat8(cvt4(SM[2 * j]), cvt4(SM[2 * j + 1]));
+  #pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            X[rt] = mfma32(kf[rt], sb, X[rt]);
+            XM[rt] = mfma32(kf[rt], sm8, XM[rt]);
           }
-          ab[0 * 64 + ll] = a_offdiag(gs, wide, 1, 0, G0, llr, llq);
-          ab[1 * 64 + ll] = a_offdiag(gs, wide, 2, 0, G1, llr, llq);
-          ab[2 * 64 + ll] = a_offdiag(gs, wide, 2, 1, G2, llr, llq);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h16x8 k3 = frag(Kb, 3, j);
-            G0 = mfma32(frag(Kb, 0, j), k3, G0);  // (3, 0)
-            G1 = mfma32(frag(Kb, 1, j), k3, G1);  // (3, 1)
-            G2 = mfma32(frag(Kb, 2, j), k3, G2);  // (3, 2)
-          }
-          ab[3 * 64 + ll] = a_offdiag(gs, wide, 3, 0, G0, llr, llq);
-          ab[4 * 64 + ll] = a_offdiag(gs, wide, 3, 1, G1, llr, llq);
-          ab[5 * 64 + ll] = a_offdiag(gs, wide, 3, 2, G2, llr, llq);
         }
-      }
-    } else if (w == 6) {
-      if (h2) {
-        // Off-diagonal blocks of Tm for chunk c2 (block forward substitution).
-        h16x4 ga[6], d[7];
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  #pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        const float rho = gs.gCc * sig;
+  #pragma unroll
+        for (int m = 0; m < 8; ++m) S[m] *= rho, SM[m] *= rho;
+        // av V, bx and Tm for Y~ and U^ and the first half of the K^T fragments
+        // (keys 32 (m / 2) + 8 (lr % 4) + 4 (m % 2) .. + 3 of token rows
+        // 4 lq + lr / 4 + 16 r) are requested ahead of the dependent chain.
+        h16x4 va[4], kt[8][4];
+        f32x4 bv[4];
         h16x8 tc[6];
-#pragma unroll
-        for (int i = 0; i < 6; ++i) ga[i] = sm.Ab[c2 & 1][i][ll];
-#pragma unroll
-        for (int i = 0; i < 7; ++i) d[i] = sm.Dg[c2 & 1][i][ll];
-        tm_offdiag(ga, d, tc);
-#pragma unroll
-        for (int i = 0; i < 6; ++i) sm.Tc[c2 & 1][i][ll] = tc[i];
+  #pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          va[rt] = ld_tr(sm.V[c3 & 1] + vb + 16 * rt * HRS);
+          bv[rt] = ldf4(&gs.bx[16 * rt + 4 * llq]);
+        }
+  #pragma unroll
+        for (int i = 0; i < 6; ++i) tc[i] = sm.Tc[c3 & 1][i][ll];
+        auto ktr = [&](int m, int r) { return ld_tr(Kb + tb + 16 * r * HRS + 32 * (m >> 1) + 4 * (m & 1)); };
+  #pragma unroll
+        for (int m = 0; m < 8; ++m) kt[m][0] = ktr(m, 0), kt[m][1] = ktr(m, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // U^ = T0 Y~ with Y~ = av V - (bx sigma) X~ (accumulator layout: tokens
+        // 16 rt + 4 lq + i, column lr), for B~ (with V) and M~ (V = 0).  Returns
+        // U^ weighted for the state update (by exp(gam_C - gam) for a wide chunk).
+        auto solve = [&](const f32x4* Xs, bool withv, h16x8* udb) {
+          h16x4 y16[4];
+  #pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            f32x4 y;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i)
+              y[i] = (withv ? (float)va[rt][i] : 0.f) - (bv[rt][i] * sig) * Xs[rt][i];
+            y16[rt] = cvt4(y);
+          }
+          const h16x8 ylo = cat8(y16[0], y16[1]), yhi = cat8(y16[2], y16[3]);
+          f32x4 U[4];
+          U[0] = mfma32(tc[0], ylo, zero4());
+          U[1] = mfma32(tc[1], ylo, zero4());
+          U[2] = mfma32(tc[2], ylo, zero4());
+          U[3] = mfma32(tc[4], ylo, zero4());
+          U[2] = mfma32(tc[3], yhi, U[2]);
+          U[3] = mfma32(tc[5], yhi, U[3]);
+          h16x4 u16[4];
+          if (!wide) {
+  #pragma unroll
+            for (int rt = 0; rt < 4; ++rt) u16[rt] = cvt4(U[rt]);
+          } else {
+  #pragma unroll
+            for (int rt = 0; rt < 4; ++rt) u16[rt] = cvt4(ldf4(&gs.dec[16 * rt + 4 * llq]) * U[rt]);
+          }
+          udb[0] = cat8(u16[0], u16[1]);
+          udb[1] = cat8(u16[2], u16[3]);
+        };
+        h16x8 udb[2], udbm[2];
+        solve(X, true, udb);
+        solve(XM, false, udbm);
+  #pragma unroll
+        for (int m = 0; m < 8; ++m) kt[m][2] = ktr(m, 2), kt[m][3] = ktr(m, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        // S~ += K^T U^, breadth-first over the sixteen state tiles.
+  #pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const h16x8 k0 = cat8(kt[m][0], kt[m][1]);
+          S[m] = mfma32(k0, udb[0], S[m]);
+          SM[m] = mfma32(k0, udbm[0], SM[m]);
+        }
+  #pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const h16x8 k1 = cat8(kt[m][2], kt[m][3]);
+          S[m] = mfma32(k1, udb[1], S[m]);
+          SM[m] = mfma32(k1, udbm[1], SM[m]);
+        }
+        sig = gs.cS;
       }
-    }
+    };
+    auto shared_stage = [&]() {
+      if (w < 4) {
+        if (h1) {
+          // Diagonal block R = w of A for chunk c1, inverted.
+          const h16* Kb = sm.K[c1 & 3];
+          const HGate& gs = sm.g[c1 & 3];
+          const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+          f32x4 G = zero4();
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h16x8 kf = frag(Kb, w, j);
+            G = mfma32(kf, kf, G);
+          }
+          f32x4 Lb, LT, Tt, TT;
+          a_diag(gs, wide, w, G, llr, llq, Lb, LT);
+          if (w < 3) {
+            inv16<true, true>(Lb, LT, llr, llq, Tt, TT);
+            sm.Dg[c1 & 1][2 * w][ll] = cvt4(Tt);
+            sm.Dg[c1 & 1][2 * w + 1][ll] = cvt4(TT);
+          } else {
+            inv16<false, true>(Lb, LT, llr, llq, Tt, TT);
+            sm.Dg[c1 & 1][6][ll] = cvt4(TT);
+          }
+        }
+      } else if (w < 6) {
+        if (h1) {
+          // Off-diagonal blocks of A for chunk c1: rows 1, 2 (wave 4) or 3 (wave 5).
+          const h16* Kb = sm.K[c1 & 3];
+          const HGate& gs = sm.g[c1 & 3];
+          const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+          h16x4* ab = sm.Ab[c1 & 1][0];
+          f32x4 G0 = zero4(), G1 = zero4(), G2 = zero4();
+          if (w == 4) {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const h16x8 k0 = frag(Kb, 0, j), k1 = frag(Kb, 1, j), k2 = frag(Kb, 2, j);
+              G0 = mfma32(k0, k1, G0);  // (1, 0)
+              G1 = mfma32(k0, k2, G1);  // (2, 0)
+              G2 = mfma32(k1, k2, G2);  // (2, 1)
+            }
+            ab[0 * 64 + ll] = a_offdiag(gs, wide, 1, 0, G0, llr, llq);
+            ab[1 * 64 + ll] = a_offdiag(gs, wide, 2, 0, G1, llr, llq);
+            ab[2 * 64 + ll] = a_offdiag(gs, wide, 2, 1, G2, llr, llq);
+          } else {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const h16x8 k3 = frag(Kb, 3, j);
+              G0 = mfma32(frag(Kb, 0, j), k3, G0);  // (3, 0)
+              G1 = mfma32(frag(Kb, 1, j), k3, G1);  // (3, 1)
+              G2 = mfma32(frag(Kb, 2, j), k3, G2);  // (3, 2)
+            }
+            ab[3 * 64 + ll] = a_offdiag(gs, wide, 3, 0, G0, llr, llq);
+            ab[4 * 64 + ll] = a_offdiag(gs, wide, 3, 1, G1, llr, llq);
+            ab[5 * 64 + ll] = a_offdiag(gs, wide, 3, 2, G2, llr, llq);
+          }
+        }
+      } else if (w == 6) {
+        if (h2) {
+          // Off-diagonal blocks of Tm for chunk c2 (block forward substitution).
+          h16x4 ga[6], d[7];
+          h16x8 tc[6];
+  #pragma unroll
+          for (int i = 0; i < 6; ++i) ga[i] = sm.Ab[c2 & 1][i][ll];
+  #pragma unroll
+          for (int i = 0; i < 7; ++i) d[i] = sm.Dg[c2 & 1][i][ll];
+          tm_offdiag(ga, d, tc);
+  #pragma unroll
+          for (int i = 0; i < 6; ++i) sm.Tc[c2 & 1][i][ll] = tc[i];
+        }
+      }
+    };
+    recurrence();
+    shared_stage();
 
     asm volatile("s_waitcnt vmcnt(10)" : "+v"(ra[p]), "+v"(rb[p])::"memory");
     if (w == 7 && it < NC) gate_tables(sm.g[it & 3], ra[p], rb[p], it * HC + ll < Ts, 1.f, ll);
