@@ -78,7 +78,7 @@ def decode_swa_bytes(d, n_slots, esize=2):
 PROFILE = "profiles/gdn_kernels_bench_workloads.md"
 # The long32k prefill call launches three kernels (segment transition pass,
 # combine pass, output pass); its entry sums them.
-PREFILL_KERNELS = "prefill_transition_kernel + segment_combine_kernel + prefill_out_kernel<bf16>"
+PREFILL_KERNELS = "prefill_lead_kernel<bf16> + segment_combine_kernel + prefill_out_kernel<bf16>"
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",

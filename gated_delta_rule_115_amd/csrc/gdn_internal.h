@@ -67,10 +67,10 @@ size_t prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, b
 bool prefill_fused_supported(const PrefillArgs& p);
 hipError_t launch_prefill_fused(const PrefillArgs& p);
 // Per-head kernels: bf16 inputs, Dk = Dv = 128, chunk 64, T > 0.  Long
-// sequences of few heads are split into P segments of L chunks (P = 1: one
-// pass, no workspace).
+// sequences of few heads are split into P segments: segment 0 of L0 chunks,
+// the others of L (the last may be shorter); P = 1: one pass, no workspace.
 bool prefill_head_supported(const PrefillArgs& p);
-void prefill_head_segments(int B, int T, int H, int* P, int* L);
+void prefill_head_segments(int B, int T, int H, int* P, int* L0, int* L);
 size_t prefill_head_workspace_bytes(int B, int T, int H);
 hipError_t launch_prefill_head(const PrefillArgs& p);
 

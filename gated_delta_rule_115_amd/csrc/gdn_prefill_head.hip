@@ -84,6 +84,7 @@
 // Precision: bf16 inputs convert to f16 exactly (unit-scale values); products
 // take f16 operands with f32 accumulation; S~ is f32.
 #include <algorithm>
+#include <cmath>
 
 #include "gdn_f16ops.h"
 #include "gdn_internal.h"
@@ -173,6 +174,19 @@ struct SegWs {
   float* B;
   float* S;
   __device__ __host__ size_t at(int bh, int s, int P) const { return ((size_t)bh * (P - 1) + s) * HD * HD; }
+};
+
+// Chunk ranges of a head's segments.  Segment 0 has L0 chunks: its output
+// pass runs beside the transition passes of segments 1 .. P - 2, which cost
+// less per chunk, so it is made shorter to finish with them.  Segments 1 ..
+// P - 1 have L chunks (the last one may have fewer).
+struct SegGeom {
+  int P, L0, L, NCT;
+  __device__ __host__ int first(int s) const { return s == 0 ? 0 : L0 + (s - 1) * L; }
+  __device__ __host__ int count(int s) const {
+    const int left = NCT - first(s);
+    return s == 0 ? L0 : (left < L ? left : L);
+  }
 };
 
 // Gram-tile scalings (lane row 16 R + lr, columns 16 C + 4 lq + i).
@@ -279,8 +293,8 @@ struct __align__(16) TSmem {
   HGate g[4];            // slot = chunk % 4
 };
 
-// Transition pass (work-group = head * (P - 1) + segment): the map S -> M_s S
-// + B_s of one segment, from the recurrence run on M~ (from the identity,
+// Transition pass of one segment (chunks c0 .. c0 + NC - 1 of head (b, h)):
+// its map S -> M_s S + B_s, from the recurrence run on M~ (from the identity,
 // V = 0) and B~ (from 0) side by side; wave w holds columns 16 w .. 16 w + 15
 // of both.  Iteration i (one work-group barrier at its end):
 //   all waves  K of chunk i -> LDS; recurrence step of chunk i - 3 (X~ of both
@@ -291,18 +305,17 @@ struct __align__(16) TSmem {
 //   wave 6     off-diagonal blocks of Tm for chunk i - 2
 //   wave 7     gate tables of chunk i
 // Every chunk of a transition segment lies inside the sequence (only the last
-// segment can be ragged, and it has no transition).
-__global__ __launch_bounds__(HNT) void prefill_transition_kernel(
-    const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ alpha,
-    const float* __restrict__ beta, SegWs ws, int T, int H, int NCT, int P, int L) {
-  __shared__ TSmem sm;
+// segment can be ragged, and it has no transition).  B_s and M_s go to dstB
+// and dstM (128 x 128 f32, [key][column]).
+__device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __restrict__ k,
+                                                   const bf16* __restrict__ v,
+                                                   const float* __restrict__ alpha,
+                                                   const float* __restrict__ beta, float* dstB,
+                                                   float* dstM, int b, int h, int T, int H,
+                                                   int c0, int NC) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
-  const int bh = blockIdx.x / (P - 1), seg = blockIdx.x % (P - 1);
-  const int b = bh / H, h = bh % H;
-  const int c0 = seg * L;                // first chunk of the segment
-  const int NC = min(L, NCT - c0);       // chunks of the segment
   const int tok = H * HD;                // elements between consecutive tokens
   const size_t head0 = ((size_t)b * T + (size_t)c0 * HC) * tok + (size_t)h * HD;
   const int Ts = T - c0 * HC;            // tokens from the segment start to the sequence end
@@ -596,8 +609,8 @@ __global__ __launch_bounds__(HNT) void prefill_transition_kernel(
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  float* dst = ws.B + ws.at(bh, seg, P);
-  float* dstm = ws.M + ws.at(bh, seg, P);
+  float* dst = dstB;
+  float* dstm = dstM;
   // Recomputed here rather than kept live from the state set-up.
   int lq4 = 4 * lq, col = 16 * w + lr;
   lane_offset(lq4);
@@ -612,7 +625,9 @@ __global__ __launch_bounds__(HNT) void prefill_transition_kernel(
     }
 }
 
-// Output pass with wave roles (work-group = head * P + segment).  Waves 0-3
+// Output pass of one segment (chunks c0 .. c0 + NC - 1 of head (b, h)) from
+// the initial state s0 (null: zero), writing the final state to s_final
+// unless null.  Wave roles: waves 0-3
 // each run the recurrence of two 16-column slices (columns 32 c .. 32 c + 31),
 // so every K, Q and K^T fragment read from LDS serves two products; waves
 // 4-7 (one per SIMD, next to a recurrence wave) do all global loads, the
@@ -624,19 +639,16 @@ __global__ __launch_bounds__(HNT) void prefill_transition_kernel(
 // helpers: off-diagonal blocks of Tm (i - 1), gate tables (i), Q of chunk
 // i - 1 and av V of chunk i - 1 -> LDS.
 template <class TOut>
-__global__ __launch_bounds__(HNT) void prefill_out_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
-    float* state_out, TOut* __restrict__ out, SegWs ws, int T, int H, int NCT, int P, int L,
-    float scale) {
-  __shared__ HSmem sm;
+__device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ q,
+                                            const bf16* __restrict__ k,
+                                            const bf16* __restrict__ v,
+                                            const float* __restrict__ alpha,
+                                            const float* __restrict__ beta, const float* s0,
+                                            float* s_final, TOut* __restrict__ out, int b, int h,
+                                            int T, int H, int c0, int NC, float scale) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
-  const int bh = blockIdx.x / P, seg = blockIdx.x % P;
-  const int b = bh / H, h = bh % H;
-  const int c0 = seg * L;                // first chunk of the segment
-  const int NC = min(L, NCT - c0);       // chunks of the segment
   const int tok = H * HD;                // elements between consecutive tokens
   const size_t head0 = ((size_t)b * T + (size_t)c0 * HC) * tok + (size_t)h * HD;
   const int Ts = T - c0 * HC;            // tokens from the segment start to the sequence end
@@ -664,8 +676,6 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
     int vb = (4 * lq + (lr >> 2)) * HRS + 32 * cw + 4 * (lr & 3);
     f32x4 S[2][8];
     {
-      const float* s0 = seg == 0 ? (state_in ? state_in + (size_t)bh * HD * HD : nullptr)
-                                 : ws.S + ws.at(bh, seg - 1, P);
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
@@ -844,8 +854,8 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
       }
       lds_barrier();
     }
-    if (seg == P - 1 && state_out) {
-      float* dst = state_out + (size_t)bh * HD * HD;
+    if (s_final) {
+      float* dst = s_final;
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
@@ -1056,21 +1066,68 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
   }
 }
 
-// Initial states of segments 1 .. P - 1: S_0 = state in (or 0), S_{s+1} =
-// M_s S_s + B_s, in f32.  One work-group of 4 waves per (head, 16-column
+union __align__(16) PrefillSmem {
+  TSmem t;
+  HSmem h;
+};
+
+// Segments 0 .. P - 2 of a segmented prefill (work-group = head * (P - 1) +
+// s): s = 0 runs the output pass of segment 0 from the state in and leaves
+// its final state, the initial state of segment 1, in the workspace; s >= 1
+// runs the transition pass of segment s.
+template <class TOut>
+__global__ __launch_bounds__(HNT) void prefill_lead_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
+    TOut* __restrict__ out, SegWs ws, SegGeom g, int T, int H, float scale) {
+  __shared__ PrefillSmem sm;
+  const int bh = blockIdx.x / (g.P - 1), s = blockIdx.x % (g.P - 1);
+  const int b = bh / H, h = bh % H;
+  if (s == 0) {
+    out_segment<TOut>(sm.h, q, k, v, alpha, beta,
+                      state_in ? state_in + (size_t)bh * HD * HD : nullptr,
+                      ws.S + ws.at(bh, 0, g.P), out, b, h, T, H, 0, g.count(0), scale);
+  } else {
+    transition_segment(sm.t, k, v, alpha, beta, ws.B + ws.at(bh, s, g.P),
+                       ws.M + ws.at(bh, s, g.P), b, h, T, H, g.first(s), g.count(s));
+  }
+}
+
+// Output pass of segments s_first .. P - 1 (work-group = head * (P - s_first)
+// + s - s_first) from their initial states (segment 0: the state in; others:
+// the workspace); segment P - 1 writes the final state.
+template <class TOut>
+__global__ __launch_bounds__(HNT) void prefill_out_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
+    float* state_out, TOut* __restrict__ out, SegWs ws, SegGeom g, int s_first, int T, int H,
+    float scale) {
+  __shared__ HSmem sm;
+  const int n = g.P - s_first;
+  const int bh = blockIdx.x / n, s = s_first + blockIdx.x % n;
+  const int b = bh / H, h = bh % H;
+  const float* s0 = s == 0 ? (state_in ? state_in + (size_t)bh * HD * HD : nullptr)
+                           : ws.S + ws.at(bh, s - 1, g.P);
+  float* sf = (s == g.P - 1 && state_out) ? state_out + (size_t)bh * HD * HD : nullptr;
+  out_segment<TOut>(sm, q, k, v, alpha, beta, s0, sf, out, b, h, T, H, g.first(s), g.count(s),
+                    scale);
+}
+
+// Initial states of segments 2 .. P - 1: from S_1 (left in the workspace by
+// the output pass of segment 0), S_{s+1} = M_s S_s + B_s, in f32.  One work-group of 4 waves per (head, 16-column
 // slice); wave w forms row tiles 2 w, 2 w + 1 (16 rows each) of every step
 // with v_mfma_f32_16x16x4_f32: in the 16-key block jj, product i takes key
 // 16 jj + 4 q + i in lane group q, so each lane reads its 4 keys of M with
 // one 16-byte load and S (kept transposed in LDS) with one 16-byte read.  The
 // next segment's M and B are loaded while the current product runs.
-__global__ __launch_bounds__(256) void segment_combine_kernel(const float* state_in, SegWs ws,
-                                                              int P) {
+__global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
   __shared__ __align__(16) float St[16][HD + 4];  // S slice transposed: [column][key]
   const int bh = blockIdx.x >> 3, col0 = 16 * (blockIdx.x & 7);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
+  const float* s1 = ws.S + ws.at(bh, 0, P);
   for (int i = tid; i < HD * 16; i += 256) {
     const int r = i >> 4, c = i & 15;
-    St[c][r] = state_in ? state_in[(size_t)bh * HD * HD + r * HD + col0 + c] : 0.f;
+    St[c][r] = s1[r * HD + col0 + c];
   }
   // Lane (lq, lr) of row tile R: M row 16 R + lr, keys 16 jj + 4 lq .. + 3.
   f32x4 mA[2][8], bA[2], mN[2][8], bN[2];
@@ -1087,9 +1144,9 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float* state
       for (int i = 0; i < 4; ++i) bb[t][i] = Bs[(size_t)(16 * (2 * w + t) + 4 * lq + i) * HD + col0 + lr];
     }
   };
-  load(0, mA, bA);
+  load(1, mA, bA);
   __syncthreads();
-  for (int sg = 0; sg + 1 < P; ++sg) {
+  for (int sg = 1; sg + 1 < P; ++sg) {
     if (sg + 2 < P) load(sg + 1, mN, bN);
     f32x4 acc[2];
 #pragma unroll
@@ -1128,50 +1185,68 @@ bool prefill_head_supported(const PrefillArgs& p) {
   return p.bf16 && p.Dk == HD && p.Dv == HD && p.chunk == HC && p.T > 0;
 }
 
-// Segments per head: enough work-groups for one per CU (the kernels hold
-// ~120 KB of LDS, so one work-group per CU runs at a time), each segment at
-// least kMinSegChunks chunks.  The transition pass costs about as much per
-// chunk as the output pass, so a split into P segments shortens the serial
-// chain about P / 2 times: fewer than 3 segments do not pay.
+// Segments per head.  Both segmented launches (the output pass of segment 0
+// beside the transition passes of segments 1 .. P - 2, then the output passes
+// of segments 1 .. P - 1) have B H (P - 1) work-groups, at most one per CU
+// (the kernels hold 120-143 KB of LDS).  Segment 0 gets kLeadRatio times the
+// chunks of the others -- about the transition pass's cost per chunk
+// relative to the output pass's -- so both kinds of work-group in the first
+// launch finish together.  Segments average at least kMinSegChunks chunks;
+// fewer than 3 segments do not shorten the serial chain.
 constexpr int kCUs = 256;
 constexpr int kMinSegChunks = 8;
-void prefill_head_segments(int B, int T, int H, int* P, int* L) {
+constexpr double kLeadRatio = 0.8;
+void prefill_head_segments(int B, int T, int H, int* P, int* L0, int* L) {
   const int NC = (T + HC - 1) / HC;
   const long long BH = std::max(1LL, (long long)B * H);
-  int p = (int)std::min<long long>(kCUs / BH, NC / kMinSegChunks);
-  if (p < 3) p = 1;
-  const int l = (NC + p - 1) / p;
+  int p = (int)std::min<long long>(1 + kCUs / BH, NC / kMinSegChunks);
+  if (p < 3) {
+    *P = 1;
+    *L0 = *L = NC;
+    return;
+  }
+  const int l = (int)std::ceil(NC / (p - 1 + kLeadRatio));
+  int l0 = NC - (p - 1) * l;
+  if (l0 < 1) {  // rounding left segment 0 empty: give it its share, drop the surplus
+    l0 = std::max(1, (int)(kLeadRatio * l));
+    p = 1 + (NC - l0 + l - 1) / l;
+  }
+  *P = p;
+  *L0 = l0;
   *L = l;
-  *P = (NC + l - 1) / l;
 }
 
 size_t prefill_head_workspace_bytes(int B, int T, int H) {
-  int P, L;
-  prefill_head_segments(B, T, H, &P, &L);
+  int P, L0, L;
+  prefill_head_segments(B, T, H, &P, &L0, &L);
   if (P <= 1) return 0;
   return 3 * (size_t)B * H * (P - 1) * HD * HD * sizeof(float);
 }
 
 template <class TOut>
 static hipError_t launch_head_t(const PrefillArgs& p) {
-  const int NC = (p.T + HC - 1) / HC;
-  int P, L;
-  prefill_head_segments(p.B, p.T, p.H, &P, &L);
+  SegGeom g;
+  g.NCT = (p.T + HC - 1) / HC;
+  prefill_head_segments(p.B, p.T, p.H, &g.P, &g.L0, &g.L);
   const int BH = p.B * p.H;
   SegWs ws{nullptr, nullptr, nullptr};
   const hipStream_t st = (hipStream_t)p.stream;
-  if (P > 1) {
-    const size_t n = (size_t)BH * (P - 1) * HD * HD;
+  const bf16 *q = (const bf16*)p.q, *k = (const bf16*)p.k, *v = (const bf16*)p.v;
+  int s_first = 0;
+  if (g.P > 1) {
+    const size_t n = (size_t)BH * (g.P - 1) * HD * HD;
     ws.M = (float*)p.workspace;
     ws.B = ws.M + n;
     ws.S = ws.B + n;
-    hipLaunchKernelGGL(prefill_transition_kernel, dim3(BH * (P - 1)), dim3(HNT), 0, st,
-                       (const bf16*)p.k, (const bf16*)p.v, p.alpha, p.beta, ws, p.T, p.H, NC, P, L);
-    hipLaunchKernelGGL(segment_combine_kernel, dim3(BH * 8), dim3(256), 0, st, p.state_in, ws, P);
+    hipLaunchKernelGGL((prefill_lead_kernel<TOut>), dim3(BH * (g.P - 1)), dim3(HNT), 0, st, q, k,
+                       v, p.alpha, p.beta, p.state_in, (TOut*)p.out, ws, g, p.T, p.H, p.scale);
+    if (g.P > 2)
+      hipLaunchKernelGGL(segment_combine_kernel, dim3(BH * 8), dim3(256), 0, st, ws, g.P);
+    s_first = 1;
   }
-  hipLaunchKernelGGL((prefill_out_kernel<TOut>), dim3(BH * P), dim3(HNT), 0, st,
-                     (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.alpha, p.beta,
-                     p.state_in, p.state_out, (TOut*)p.out, ws, p.T, p.H, NC, P, L, p.scale);
+  hipLaunchKernelGGL((prefill_out_kernel<TOut>), dim3(BH * (g.P - s_first)), dim3(HNT), 0, st, q,
+                     k, v, p.alpha, p.beta, p.state_in, p.state_out, (TOut*)p.out, ws, g, s_first,
+                     p.T, p.H, p.scale);
   return hipGetLastError();
 }
 
