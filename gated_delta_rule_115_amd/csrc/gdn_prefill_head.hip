@@ -1195,7 +1195,7 @@ bool prefill_head_supported(const PrefillArgs& p) {
 // fewer than 3 segments do not shorten the serial chain.
 constexpr int kCUs = 256;
 constexpr int kMinSegChunks = 8;
-constexpr double kLeadRatio = 0.8;
+constexpr double kLeadRatio = 0.9;
 void prefill_head_segments(int B, int T, int H, int* P, int* L0, int* L) {
   const int NC = (T + HC - 1) / HC;
   const long long BH = std::max(1LL, (long long)B * H);
