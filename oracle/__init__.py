@@ -59,6 +59,7 @@ def _load():
         lib.gdn_oracle_swa_sink_f64.argtypes = [_dp] * 4 + [i] * 6 + [d, i]
         lib.gdn_oracle_hybrid_f64.argtypes = [_dp] * 9 + [i] * 7 + [d, d]
         lib.gdn_oracle_short_conv_silu_f64.argtypes = [_dp] * 3 + [i] * 5 + [d]
+        lib.gdn_oracle_short_conv_step_f64.argtypes = [_dp] * 5 + [i] * 4 + [d]
         lib.gdn_oracle_num_threads.restype = i
         _lib = lib
     return _lib
@@ -167,6 +168,24 @@ def short_conv_silu(x, taps, l2norm_group=0, eps=1e-6):
     _load().gdn_oracle_short_conv_silu_f64(_ptr(x), _ptr(taps), _ptr(y), B, T,
                                            Ch, K, int(l2norm_group), float(eps))
     return y
+
+
+def short_conv_step(x, taps, state, l2norm_group=0, eps=1e-6):
+    """One decode step of short_conv_silu from the previous K-1 inputs.
+
+    x [B,Ch], taps [Ch,K], state [B,K-1,Ch] (oldest row first) ->
+    (y [B,Ch], new state [B,K-1,Ch] = previous rows 1.. followed by x).
+    """
+    x, taps, state = _arr(x), _arr(taps), _arr(state)
+    B, Ch = x.shape
+    K = taps.shape[1]
+    assert taps.shape == (Ch, K) and state.shape == (B, K - 1, Ch)
+    y = np.zeros_like(x)
+    new_state = np.zeros_like(state)
+    _load().gdn_oracle_short_conv_step_f64(_ptr(x), _ptr(taps), _ptr(state),
+                                           _ptr(new_state), _ptr(y), B, Ch, K,
+                                           int(l2norm_group), float(eps))
+    return y, new_state
 
 
 def rms_normalised_max_error(got, ref) -> float:

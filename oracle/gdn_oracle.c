@@ -271,6 +271,48 @@ void gdn_oracle_short_conv_silu_f64(const double* x, const double* taps,
   }
 }
 
+/* ------------------------------------------------------------------------- */
+/* One decode step of the same convolution (section 4 "Adapting Q/K/V": the   */
+/* causal convolution evaluated at one new token), from the K - 1 previous    */
+/* inputs of each channel.                                                    */
+/* x, y: [B, Ch]; state_in, state_out: [B, K-1, Ch], oldest row first.        */
+/*   window = (state_in[0], ..., state_in[K-2], x)                            */
+/*   a = sum_{j=0}^{K-1} taps[c][j] * window[j][c];  y = a * sigmoid(a)       */
+/*   state_out = (state_in[1], ..., state_in[K-2], x)                         */
+/* Optional group L2 normalisation as above.                                  */
+/* ------------------------------------------------------------------------- */
+void gdn_oracle_short_conv_step_f64(const double* x, const double* taps,
+                                    const double* state_in, double* state_out,
+                                    double* y, int B, int Ch, int K, int group,
+                                    double eps) {
+  const long H1 = K - 1;
+  for (long b = 0; b < B; ++b) {
+    const double* xb = x + b * Ch;
+    const double* sb = state_in + b * H1 * Ch;
+    double* ob = state_out + b * H1 * Ch;
+    double* yb = y + b * Ch;
+    for (long c = 0; c < Ch; ++c) {
+      double a = 0;
+      for (long j = 0; j < K; ++j) {
+        double w = (j < H1) ? sb[j * Ch + c] : xb[c];
+        a += taps[c * K + j] * w;
+      }
+      yb[c] = a / (1.0 + exp(-a));
+    }
+    if (group > 0) {
+      for (long g0 = 0; g0 < Ch; g0 += group) {
+        double ss = 0;
+        for (long c = g0; c < g0 + group; ++c) ss += yb[c] * yb[c];
+        double inv = 1.0 / (sqrt(ss) + eps);
+        for (long c = g0; c < g0 + group; ++c) yb[c] *= inv;
+      }
+    }
+    for (long j = 0; j < H1; ++j)
+      for (long c = 0; c < Ch; ++c)
+        ob[j * Ch + c] = (j + 1 < H1) ? sb[(j + 1) * Ch + c] : xb[c];
+  }
+}
+
 int gdn_oracle_num_threads(void) {
   int n = 1;
 #ifdef _OPENMP

@@ -283,6 +283,48 @@ def test_short_conv_equals_torch_conv1d():
 
 
 # --------------------------------------------------------------------------
+# P-vii': one decode step of the short convolution.  Stepping a zero history
+# through a sequence reproduces torch conv1d token by token and leaves the
+# last K-1 inputs as the state; a one-hot tap j reads the input K-1-j tokens
+# back; a prefix in sequence form followed by steps from the prefix's last
+# K-1 inputs equals the whole sequence (with the L2 option too); K = 1 has
+# an empty history.
+# --------------------------------------------------------------------------
+def test_short_conv_step_chains_to_conv1d():
+    B, T, Ch, K = 3, 11, 16, 4
+    x = RNG.standard_normal((B, T, Ch))
+    taps = 0.5 * RNG.standard_normal((Ch, K))
+    xt = torch.from_numpy(x).permute(0, 2, 1)
+    ref = torch.nn.functional.conv1d(xt, torch.from_numpy(taps)[:, None, :],
+                                     padding=K - 1, groups=Ch)[..., :T]
+    ref = torch.nn.functional.silu(ref).permute(0, 2, 1).numpy()
+    st = np.zeros((B, K - 1, Ch))
+    for t in range(T):
+        y, st = oracle.short_conv_step(x[:, t], taps, st)
+        np.testing.assert_allclose(y, ref[:, t], atol=1e-12, rtol=0)
+    np.testing.assert_array_equal(st, x[:, T - K + 1:])
+    for j in range(K):
+        oh = np.zeros((Ch, K))
+        oh[:, j] = 1.0
+        s0 = RNG.standard_normal((B, K - 1, Ch))
+        x0 = RNG.standard_normal((B, Ch))
+        y, _ = oracle.short_conv_step(x0, oh, s0)
+        src = s0[:, j] if j < K - 1 else x0
+        np.testing.assert_allclose(y, src / (1.0 + np.exp(-src)), atol=1e-15, rtol=0)
+    T1 = 6
+    full = oracle.short_conv_silu(x, taps, l2norm_group=8, eps=1e-3)
+    st = x[:, T1 - K + 1:T1].copy()
+    for t in range(T1, T):
+        y, st = oracle.short_conv_step(x[:, t], taps, st, l2norm_group=8, eps=1e-3)
+        np.testing.assert_allclose(y, full[:, t], atol=1e-12, rtol=0)
+    t1 = RNG.standard_normal((Ch, 1))
+    y, s1 = oracle.short_conv_step(x[:, 0], t1, np.zeros((B, 0, Ch)))
+    a = t1[:, 0] * x[:, 0]
+    np.testing.assert_allclose(y, a / (1.0 + np.exp(-a)), atol=1e-15, rtol=0)
+    assert s1.shape == (B, 0, Ch)
+
+
+# --------------------------------------------------------------------------
 # P-viii: the oracle's own rounding: float32 vs float64 on the tiny workload.
 # --------------------------------------------------------------------------
 def test_oracle_f32_vs_f64_on_tiny():
