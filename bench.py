@@ -119,7 +119,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill_long32k,decode_b256,conv_qwen32b")
+    ap.add_argument("--legs", default="prefill_long32k,decode_b256,conv_qwen32b,convstep_b256")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) "
                          "and exit: the reference reading for HBM byte counters")
@@ -227,6 +227,30 @@ def make_conv_leg():
     return run, info
 
 
+def make_convstep_leg():
+    """Decode-time short conv of the Qwen-32B-shaped layer: one new token for
+    each of 256 sequences through the q, k, v convolutions (K = 4, per-head L2
+    norm on q and k), each with its K - 1 = 3 previous inputs as state."""
+    c = synthetic.CONFIGS["qwen32b_conv"]
+    H, d, K, B = c["H"], c["Dk"], 4, 256
+    Ch = H * d
+    xs = {n: synthetic.conv_inputs(B, K, Ch, K, seed=c["seed"] * 100 + i, device="cuda")
+          for i, n in enumerate(("q", "k", "v"))}
+    x = {n: xs[n][0][:, K - 1].contiguous() for n in xs}
+    state = {n: xs[n][0][:, :K - 1].contiguous() for n in xs}
+    taps = {n: xs[n][1] for n in xs}
+    y = {n: torch.empty_like(x[n]) for n in xs}
+
+    def run(mark):
+        for n, grp in (("q", d), ("k", d), ("v", 0)):
+            gdn.gdn_short_conv_step(x[n], taps[n], state[n], l2norm_group=grp, out=y[n])
+        mark("conv_step")
+
+    # per projection: x read, y written, the K - 1 history rows read and written (bf16)
+    info = dict(B=B, Ch=Ch, K=K, tokens=B, bytes=3 * B * Ch * 2 * (2 + 2 * (K - 1)))
+    return run, info
+
+
 def cpu_baseline(prefill_x, decode_x):
     """The oracle as it stands, on a bounded sample of each workload."""
     import numpy as np
@@ -295,6 +319,9 @@ def main():
     if "conv_qwen32b" in legs_wanted:
         run, info = make_conv_leg()
         legs["conv_qwen32b"], infos["conv_qwen32b"] = run, info
+    if "convstep_b256" in legs_wanted:
+        run, info = make_convstep_leg()
+        legs["convstep_b256"], infos["convstep_b256"] = run, info
     torch.cuda.synchronize()
 
     def step(record):
@@ -388,6 +415,12 @@ def main():
         roof_conv = hbm_roof("short_conv_silu_kernel<bf16,bf16,4> (x3)", inf["conv_bytes"],
                              seg_ms[("conv_qwen32b", "conv")])
 
+    roof_convstep = None
+    if "convstep_b256" in out_legs:
+        inf = infos["convstep_b256"]
+        roof_convstep = hbm_roof("short_conv_step_kernel<bf16,bf16,4> (x3)", inf["bytes"],
+                                 seg_ms[("convstep_b256", "conv_step")])
+
     cpu = None
     if not args.no_cpu_baseline and "prefill" in keep and "decode" in keep:
         cb = cpu_baseline(keep["prefill"], keep["decode"])
@@ -415,7 +448,8 @@ def main():
         "config": {
             "workload": "long32k prefill (B1 H32 T32768 d128, chunk 64) + hybrid decode "
                         "(B256 H32 d128, 4 sinks + 512 window) + qwen32b conv+prefill "
-                        "(B2 H40 T16384 d128)",
+                        "(B2 H40 T16384 d128) + decode-time conv step (B256, 3 x 5120 "
+                        "channels, K 4)",
             "global_batch": 1, "seq_len": 32768, "parallelism": "single-gpu",
         },
         "decode_tokens_per_s": out_legs.get("decode_b256", {}).get("tokens_per_s"),
@@ -423,6 +457,7 @@ def main():
         "roofline": roofline,
         "roofline_decode": roof_dec,
         "roofline_conv": roof_conv,
+        "roofline_conv_step": roof_convstep,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
     }

@@ -24,8 +24,8 @@ import torch
 __all__ = [
     "GDN_BF16", "GDN_F32", "GdnError", "lib", "library_path",
     "gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
-    "gdn_decode_step", "gdn_short_conv_silu", "gdn_swa_sink_decode",
-    "EXPORTED_SYMBOLS",
+    "gdn_decode_step", "gdn_short_conv_silu", "gdn_short_conv_step",
+    "gdn_swa_sink_decode", "EXPORTED_SYMBOLS",
 ]
 
 GDN_BF16 = 0
@@ -37,7 +37,7 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 EXPORTED_SYMBOLS = (
     "gdn_abi_version", "gdn_last_error", "gdn_prefill_workspace_bytes",
     "gdn_prefill_chunked", "gdn_decode_step", "gdn_short_conv_silu",
-    "gdn_swa_sink_decode",
+    "gdn_short_conv_step", "gdn_swa_sink_decode",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_decode_step.argtypes = [vp] * 8 + [i] * 6 + [f, vp]
     L.gdn_short_conv_silu.restype = i
     L.gdn_short_conv_silu.argtypes = [vp] * 3 + [i] * 5 + [f, i, i, vp]
+    L.gdn_short_conv_step.restype = i
+    L.gdn_short_conv_step.argtypes = [vp] * 4 + [i] * 4 + [f, i, i, vp]
     L.gdn_swa_sink_decode.restype = i
     L.gdn_swa_sink_decode.argtypes = [vp] * 6 + [i] * 5 + [f, i, vp, i, i, vp]
     _lib = L
@@ -208,6 +210,28 @@ def gdn_short_conv_silu(x, taps, *, l2norm_group=0, eps=1e-6, out=None,
                                    int(l2norm_group), float(eps), dt,
                                    _dtype_code(out), _stream(stream))
     _check("gdn_short_conv_silu", st)
+    return out
+
+
+def gdn_short_conv_step(x, taps, conv_state, *, l2norm_group=0, eps=1e-6, out=None,
+                        out_dtype=None, stream=None):
+    """One decode step of the short conv.  x [B,Ch], taps [Ch,K] f32,
+    conv_state [B,K-1,Ch] (x's dtype; the previous K-1 inputs, oldest first),
+    updated in place.  Returns y [B,Ch]."""
+    B, Ch = x.shape
+    K = taps.shape[1]
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    _dev(taps, "taps", torch.float32, (Ch, K))
+    _dev(conv_state, "conv_state", x.dtype, (B, K - 1, Ch))
+    odt = _out_dtype(x.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        out = torch.empty((B, Ch), dtype=odt, device=x.device)
+    _dev(out, "out", odt, (B, Ch))
+    st = lib().gdn_short_conv_step(_ptr(x), _ptr(taps), _ptr(conv_state), _ptr(out), B, Ch,
+                                   K, int(l2norm_group), float(eps), dt, _dtype_code(out),
+                                   _stream(stream))
+    _check("gdn_short_conv_step", st)
     return out
 
 

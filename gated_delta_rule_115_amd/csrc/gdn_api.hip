@@ -194,6 +194,41 @@ int gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
   return hip_status(gdn::launch_conv(p), "gdn_short_conv_silu launch");
 }
 
+int gdn_short_conv_step(const void* x, const float* taps, void* conv_state, void* y,
+                        int B, int Ch, int K, int l2norm_group, float eps, int dtype,
+                        int out_dtype, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && Ch >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d Ch=%d", B, Ch);
+  REQUIRE(K >= 1 && K <= 8, GDN_ERR_UNSUPPORTED, "kernel size %d not in 1..8", K);
+  REQUIRE(Ch % 8 == 0, GDN_ERR_UNSUPPORTED, "Ch=%d is not a multiple of 8", Ch);
+  const int g = l2norm_group;
+  REQUIRE(g == 0 || (g >= 8 && g <= 512 && (g & (g - 1)) == 0 && Ch % g == 0),
+          GDN_ERR_UNSUPPORTED,
+          "l2norm_group %d must be 0 or a power of two in 8..512 dividing Ch", g);
+  REQUIRE((long long)B * (Ch / 8) <= (long long)INT32_MAX, GDN_ERR_UNSUPPORTED, "grid too large");
+  if (B == 0) return ok();
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(y);
+  REQUIRE(taps != nullptr, GDN_ERR_INVALID_ARG, "taps is NULL");
+  if (K > 1) REQUIRE_PTR(conv_state);
+  const size_t xbytes = (size_t)B * Ch * esize(dtype);
+  const size_t ybytes = (size_t)B * Ch * esize(out_dtype);
+  const size_t sbytes = (size_t)B * (K - 1) * Ch * esize(dtype);
+  const char* xa = (const char*)x;
+  const char* ya = (const char*)y;
+  const char* sa = (const char*)conv_state;
+  REQUIRE(ya + ybytes <= xa || xa + xbytes <= ya, GDN_ERR_INVALID_ARG, "y overlaps x");
+  REQUIRE(K == 1 || ya + ybytes <= sa || sa + sbytes <= ya, GDN_ERR_INVALID_ARG,
+          "y overlaps conv_state");
+  REQUIRE(K == 1 || xa + xbytes <= sa || sa + sbytes <= xa, GDN_ERR_INVALID_ARG,
+          "x overlaps conv_state");
+  gdn::ConvArgs p;
+  p.x = x; p.taps = taps; p.y = y;
+  p.B = B; p.T = 1; p.Ch = Ch; p.K = K; p.group = g; p.eps = eps;
+  p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16; p.stream = stream;
+  return hip_status(gdn::launch_conv_step(p, conv_state), "gdn_short_conv_step launch");
+}
+
 int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
                         void* k_cache, void* v_cache, const int* n_tokens,
                         int B, int H, int D, int n_sink, int window,

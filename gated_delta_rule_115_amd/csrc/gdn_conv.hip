@@ -191,6 +191,98 @@ static hipError_t launch_conv_k(const ConvArgs& p) {
   return hipErrorInvalidValue;
 }
 
+// One decode step: the same convolution at one new token per sequence, from
+// the K - 1 previous inputs of each channel kept in `state` [B][K-1][Ch]
+// (oldest row first), which is then shifted by one row with the new token
+// appended.  A thread owns 8 channels of one sequence: it reads the token and
+// its history rows, writes y and the shifted history (every thread reads its
+// own channels before writing them, so the update is in place).  L2 groups
+// are consecutive lanes of one wave (a group's channels are consecutive and
+// groups do not straddle sequences).
+template <class TIn, class TOut, int K>
+__global__ __launch_bounds__(kConvThreads) void short_conv_step_kernel(
+    const TIn* __restrict__ x, const float* __restrict__ taps, TIn* __restrict__ state,
+    TOut* __restrict__ y, int B, int Ch, int group, float eps) {
+  const int nvec = Ch / 8;
+  const long long gi = (long long)blockIdx.x * kConvThreads + threadIdx.x;
+  const bool active = gi < (long long)B * nvec;
+  const int b = active ? (int)(gi / nvec) : 0;
+  const int c0 = (active ? (int)(gi % nvec) : 0) * 8;
+  float w[8][K];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int j = 0; j < K; ++j) w[e][j] = active ? taps[(size_t)(c0 + e) * K + j] : 0.f;
+  Raw8<TIn> rows[K];  // history rows 0 .. K - 2, then the new token
+  TIn* sb = state + (size_t)b * (K - 1) * Ch + c0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (!active)
+      zero_raw8(rows[j]);
+    else if (j < K - 1)
+      rows[j] = load_raw8(sb + (size_t)j * Ch);
+    else
+      rows[j] = load_raw8(x + (size_t)b * Ch + c0);
+  }
+  float o[8], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) a += w[e][j] * raw8_at(rows[j], e);
+    o[e] = a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
+    ss += o[e] * o[e];
+  }
+  const int gl = group / 8;
+  if (gl > 0) {
+    for (int m = 1; m < gl; m <<= 1) ss += __shfl_xor(ss, m);
+    const float inv = __builtin_amdgcn_rcpf(sqrtf(ss) + eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv;
+  }
+  if (!active) return;
+  store8(y + (size_t)b * Ch + c0, o);
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = raw8_at(rows[j + 1], e);
+    store8(sb + (size_t)j * Ch, f);
+  }
+}
+
+template <class TIn, class TOut, int K>
+static hipError_t launch_conv_step_t(const ConvArgs& p, void* state) {
+  const long long n = (long long)p.B * (p.Ch / 8);
+  hipLaunchKernelGGL((short_conv_step_kernel<TIn, TOut, K>),
+                     dim3((unsigned)((n + kConvThreads - 1) / kConvThreads)), dim3(kConvThreads), 0,
+                     (hipStream_t)p.stream, (const TIn*)p.x, p.taps, (TIn*)state, (TOut*)p.y, p.B,
+                     p.Ch, p.group, p.eps);
+  return hipGetLastError();
+}
+
+template <class TIn, class TOut>
+static hipError_t launch_conv_step_k(const ConvArgs& p, void* state) {
+  switch (p.K) {
+    case 1: return launch_conv_step_t<TIn, TOut, 1>(p, state);
+    case 2: return launch_conv_step_t<TIn, TOut, 2>(p, state);
+    case 3: return launch_conv_step_t<TIn, TOut, 3>(p, state);
+    case 4: return launch_conv_step_t<TIn, TOut, 4>(p, state);
+    case 5: return launch_conv_step_t<TIn, TOut, 5>(p, state);
+    case 6: return launch_conv_step_t<TIn, TOut, 6>(p, state);
+    case 7: return launch_conv_step_t<TIn, TOut, 7>(p, state);
+    case 8: return launch_conv_step_t<TIn, TOut, 8>(p, state);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv_step(const ConvArgs& p, void* state) {
+  if (p.B == 0) return hipSuccess;
+  if (!p.bf16) return launch_conv_step_k<float, float>(p, state);
+  return p.out_bf16 ? launch_conv_step_k<bf16, bf16>(p, state)
+                    : launch_conv_step_k<bf16, float>(p, state);
+}
+
 hipError_t launch_conv(const ConvArgs& p) {
   if ((long)p.B * p.T == 0) return hipSuccess;
   if (!p.bf16) return launch_conv_k<float, float>(p);

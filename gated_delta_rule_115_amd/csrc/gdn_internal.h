@@ -77,6 +77,8 @@ hipError_t launch_prefill_head(const PrefillArgs& p);
 hipError_t launch_decode(const DecodeArgs& p);
 hipError_t launch_prefill(const PrefillArgs& p);
 hipError_t launch_conv(const ConvArgs& p);
+// One decode step (T unused): state [B][K-1][Ch] of the input dtype, in place.
+hipError_t launch_conv_step(const ConvArgs& p, void* state);
 hipError_t launch_swa(const SwaArgs& p);
 
 }  // namespace gdn

@@ -133,6 +133,27 @@ int gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
                         int dtype, int out_dtype, void* stream);
 
 /*
+ * One decode step of the same short convolution (section 4, "Adapting
+ * Q/K/V": the causal convolution evaluated at one new token), for callers
+ * that generate token by token.  For every sequence b and channel c:
+ *   a = sum_{j<K-1} taps[c][j] * conv_state[b][j][c] + taps[c][K-1] * x[b][c]
+ *   y[b][c] = SiLU(a)  (then the optional group L2 normalisation)
+ * and conv_state[b] becomes rows 1 .. K-2 of itself followed by x[b].
+ *   x          [B, Ch] dtype: the new token's projection output
+ *   taps       [Ch, K] f32, as in gdn_short_conv_silu
+ *   conv_state [B, K-1, Ch] dtype, caller-owned, updated in place: the
+ *              previous K-1 inputs, oldest first (zeros before the first
+ *              token).  After gdn_short_conv_silu over tokens 0 .. T-1 the
+ *              matching state is x_{T-K+1} .. x_{T-1} (rows before token 0
+ *              are zero).  May be NULL when K = 1.
+ *   y          [B, Ch] out_dtype
+ * Limits as gdn_short_conv_silu.  x, y and conv_state must not overlap.
+ */
+int gdn_short_conv_step(const void* x, const float* taps, void* conv_state,
+                        void* y, int B, int Ch, int K, int l2norm_group,
+                        float eps, int dtype, int out_dtype, void* stream);
+
+/*
  * Softmax decode step over sink tokens and a sliding window (section 4,
  * "Adding Sliding Window Attention": I = sinks + window, logits scaled by
  * softmax_scale, normally 1/sqrt(D)).

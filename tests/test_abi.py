@@ -122,6 +122,25 @@ def test_conv_validation():
     assert call(T=0, x=None) == OK
 
 
+def test_conv_step_validation():
+    L = gdn.lib()
+    call = lambda **kw: L.gdn_short_conv_step(
+        kw.get("x", A), A, kw.get("s", A + (2 << 30)), kw.get("y", A + (1 << 30)),
+        kw.get("B", 4), kw.get("Ch", 256), kw.get("K", 4), kw.get("g", 0), 1e-6, BF16,
+        BF16, None)
+    assert call(K=9) == UNSUPPORTED
+    assert call(K=0) == UNSUPPORTED
+    assert call(Ch=12) == UNSUPPORTED
+    assert call(g=24) == UNSUPPORTED
+    assert call(y=A + 16) == INVALID and "overlaps x" in _err()
+    assert call(s=A + 16) == INVALID and "x overlaps conv_state" in _err()
+    assert call(y=A + (2 << 30) + 64) == INVALID and "conv_state" in _err()
+    assert call(s=None) == INVALID
+    assert call(x=None) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(B=0, x=None, s=None) == OK
+
+
 def test_swa_validation():
     L = gdn.lib()
     call = lambda **kw: L.gdn_swa_sink_decode(

@@ -1,4 +1,4 @@
-"""GPU parity: gdn_short_conv_silu against the oracle's direct loop
+"""GPU parity: gdn_short_conv_silu and gdn_short_conv_step against the oracle's direct loops
 ("The Key to Going Linear: Analysis-Driven Transformer Linearization",
 section 4 "Adapting Q/K/V"; key normalisation of appendix B.1), and the
 conv -> prefill chain of the Qwen-32B-shaped layer against oracle conv ->
@@ -34,6 +34,65 @@ def test_conv_matches_oracle(dtype, B, T, Ch, K, group):
         yb = gdn.gdn_short_conv_silu(dev(x), dev(taps), l2norm_group=group, eps=1e-6)
         torch.cuda.synchronize()
         assert_bf16_is_rounded_f32(yb, y)
+
+
+@pytest.mark.parametrize("dtype,B,Ch,K,group", [
+    ("f32", 3, 256, 4, 0), ("f32", 3, 256, 4, 64), ("f32", 2, 64, 1, 32),
+    ("bf16", 5, 512, 4, 128), ("bf16", 2, 1024, 3, 0), ("bf16", 4, 96, 8, 32),
+])
+def test_conv_step_matches_oracle(dtype, B, Ch, K, group):
+    """One decode step (section 4 "Adapting Q/K/V" at one new token): y against
+    the oracle's step, and the shifted history bit-exact (it is a copy)."""
+    say(f"conv step {dtype} B={B} Ch={Ch} K={K} group={group}")
+    xs, taps = synthetic.conv_inputs(B, K, Ch, K, dtype=dtype, seed=Ch + 10 * K)
+    state, x = xs[:, :K - 1].contiguous(), xs[:, K - 1].contiguous()
+    st = dev(state)
+    y = gdn.gdn_short_conv_step(dev(x), dev(taps), st, l2norm_group=group, eps=1e-6,
+                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ry, rs = oracle.short_conv_step(f64(x), f64(taps), f64(state), l2norm_group=group,
+                                    eps=1e-6)
+    assert err(y, ry) <= TOL[dtype]
+    assert np.array_equal(f64(st), rs)
+    if dtype == "bf16":
+        st2 = dev(state)
+        yb = gdn.gdn_short_conv_step(dev(x), dev(taps), st2, l2norm_group=group, eps=1e-6)
+        torch.cuda.synchronize()
+        assert_bf16_is_rounded_f32(yb, y)
+
+
+def test_conv_prefill_then_steps_equals_sequence():
+    """The sequence kernel over a prefix, then steps from the prefix's last K-1
+    inputs, reproduce the whole sequence (oracle and sequence kernel)."""
+    B, T, Ch, K, group, T1 = 2, 40, 256, 4, 128, 25
+    x, taps = synthetic.conv_inputs(B, T, Ch, K, dtype="bf16", seed=7)
+    xd, td = dev(x), dev(taps)
+    full = gdn.gdn_short_conv_silu(xd, td, l2norm_group=group, out_dtype=torch.float32)
+    state = xd[:, T1 - K + 1:T1].contiguous()
+    ys = [gdn.gdn_short_conv_step(xd[:, t].contiguous(), td, state, l2norm_group=group,
+                                  out_dtype=torch.float32) for t in range(T1, T)]
+    torch.cuda.synchronize()
+    got = torch.stack(ys, 1)
+    ref = oracle.short_conv_silu(f64(x), f64(taps), l2norm_group=group, eps=1e-6)[:, T1:]
+    assert err(got, ref) <= TOL["bf16"]
+    assert torch.allclose(got, full[:, T1:], atol=1e-5, rtol=1e-5)
+    assert torch.equal(state, xd[:, T - K + 1:])
+
+
+def test_conv_step_qwen32b_projection_b256():
+    """Decode-time conv of one projection of the Qwen-32B-shaped layer for 256
+    sequences (40 heads x 128 channels, K = 4, per-head L2 norm)."""
+    B, Ch, K = 256, 40 * 128, 4
+    xs, taps = synthetic.conv_inputs(B, K, Ch, K, dtype="bf16", seed=11, device="cuda")
+    state, x = xs[:, :K - 1].contiguous(), xs[:, K - 1].contiguous()
+    ry, rs = oracle.short_conv_step(f64(x), f64(taps), f64(state), l2norm_group=128,
+                                    eps=1e-6)
+    y = gdn.gdn_short_conv_step(x, taps, state, l2norm_group=128, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    e = err(y, ry)
+    say(f"  conv step B256 err {e:.3e}")
+    assert e <= TOL["bf16"]
+    assert np.array_equal(f64(state), rs)
 
 
 def test_conv_full_qwen32b_projection():
