@@ -7,11 +7,11 @@
 //
 // HBM-bound: every cached key and value of the (b, h) is streamed once.  One
 // work-group per (b, h); a group of D/8 lanes owns one key at a time (8
-// elements per lane, one 16-byte load for bf16).  Each lane group takes 8 keys
-// per step, the groups of a wave reading consecutive keys, and the next step's
-// keys and values are loaded before the current step is consumed.  Each group
-// keeps its own running max / sum / accumulator (online softmax, f32, one
-// rescale per step); groups are merged through LDS at the end.
+// elements per lane, one 16-byte load for bf16).  Each lane group takes UNR
+// keys per step, the groups of a wave reading consecutive keys, and NBUF steps
+// of loads are in flight (a software pipeline whose buffers are registers).
+// Each group keeps its own running max / sum / accumulator (online softmax,
+// f32, one rescale per step); groups are merged through LDS at the end.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -26,26 +26,17 @@ template <>
 struct Piece<float> {
   f32x4 a, b;
 };
+// Cache rows are streamed with non-temporal loads: each is read once per
+// step, and the scan is several times larger than the caches.
 template <class TIn>
 __device__ __forceinline__ Piece<TIn> load_piece(const TIn* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   Piece<TIn> r;
   if constexpr (sizeof(TIn) == 2) {
-    r.v = *reinterpret_cast<const bf16x8*>(p);
+    r.v = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
   } else {
-    r.a = *reinterpret_cast<const f32x4*>(p);
-    r.b = *reinterpret_cast<const f32x4*>(p + 4);
-  }
-  return r;
-}
-template <class TIn>
-__device__ __forceinline__ Piece<TIn> zero_piece() {
-  Piece<TIn> r;
-  if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.v[e] = (bf16)0.f;
-  } else {
-    r.a = zero4();
-    r.b = zero4();
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
   }
   return r;
 }
@@ -68,16 +59,39 @@ __device__ __forceinline__ void copy8(TIn* dst, const TIn* src) {
   }
 }
 
-template <class TIn, class TOut, int D>
-__global__ __launch_bounds__(256) void swa_sink_decode_kernel(
+// Sum over the LPK lanes of a row group (LPK = 8 or 16, groups aligned to
+// 8 or 16 lanes) with DPP row permutations: swap neighbours, swap pairs,
+// mirror within 8 lanes, mirror within 16 lanes.  Every lane of the group
+// ends with the total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int LPK>
+__device__ __forceinline__ float group_sum(float d) {
+  static_assert(LPK == 8 || LPK == 16, "lane groups of 8 or 16");
+  d += dpp_f<0xB1>(d);   // quad_perm [1, 0, 3, 2]
+  d += dpp_f<0x4E>(d);   // quad_perm [2, 3, 0, 1]
+  d += dpp_f<0x141>(d);  // row_half_mirror
+  if constexpr (LPK == 16) d += dpp_f<0x140>(d);  // row_mirror
+  return d;
+}
+
+// NT threads per work-group; each lane group takes UNR keys per step and
+// NBUF steps are in flight (the loads of step s + NBUF - 1 are issued before
+// step s is consumed).  Past the last valid key the loads repeat that key
+// (same cache lines, no extra HBM traffic) and its weight is zero, so every
+// step issues the same loads without branches and the waits are fixed counts.
+template <class TIn, class TOut, int D, int NT, int UNR, int NBUF>
+__global__ __launch_bounds__(NT) void swa_sink_decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k_new,
     const TIn* __restrict__ v_new, TIn* __restrict__ k_cache,
     TIn* __restrict__ v_cache, const int* __restrict__ n_tokens, int H,
     int n_sink, int window, float sm_scale, int accumulate, TOut* __restrict__ out) {
   constexpr int LPK = D / 8;             // lanes per key
   constexpr int KPW = kWave / LPK;       // keys per wave per load
-  constexpr int NG = 4 * KPW;            // lane groups per work-group
-  constexpr int UNR = 8;                 // keys per lane group per step
+  constexpr int NG = (NT / kWave) * KPW; // lane groups per work-group
   constexpr int STEP = NG * UNR;         // keys per step
 
   __shared__ float gm[NG], gs[NG];
@@ -117,28 +131,17 @@ __global__ __launch_bounds__(256) void swa_sink_decode_kernel(
   // Valid slots are [0, n_s) and [n_sink, n_sink + n_w): position j in
   // [0, n_valid) -> slot(j).  Step s, piece u of group g: j = s STEP + u NG + g,
   // so the groups of a wave read consecutive keys.
-  Piece<TIn> kr[2][UNR], vr[2][UNR];
+  Piece<TIn> kr[NBUF][UNR], vr[NBUF][UNR];
   auto fetch = [&](int st, Piece<TIn>* kk, Piece<TIn>* vv) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int j = st * STEP + u * NG + grp;
-      if (j < n_valid) {
-        const int slot = (j < n_s) ? j : n_sink + (j - n_s);
-        const TIn* kp;
-        const TIn* vp;
-        if (have_new && slot == cur) {
-          kp = k_new + (size_t)bh * D;
-          vp = v_new + (size_t)bh * D;
-        } else {
-          kp = k_cache + cbase + (size_t)slot * D;
-          vp = v_cache + cbase + (size_t)slot * D;
-        }
-        kk[u] = load_piece(kp + sub * 8);
-        vv[u] = load_piece(vp + sub * 8);
-      } else {
-        kk[u] = zero_piece<TIn>();  // weight 0 below; must not hold NaN
-        vv[u] = zero_piece<TIn>();
-      }
+      const int j = min(st * STEP + u * NG + grp, n_valid - 1);
+      const int slot = (j < n_s) ? j : n_sink + (j - n_s);
+      const bool fresh = have_new && slot == cur;
+      const TIn* kp = fresh ? k_new + (size_t)bh * D : k_cache + cbase + (size_t)slot * D;
+      const TIn* vp = fresh ? v_new + (size_t)bh * D : v_cache + cbase + (size_t)slot * D;
+      kk[u] = load_piece(kp + sub * 8);
+      vv[u] = load_piece(vp + sub * 8);
     }
   };
 
@@ -153,8 +156,7 @@ __global__ __launch_bounds__(256) void swa_sink_decode_kernel(
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d += qf[e] * piece_at(kk[u], e);
-#pragma unroll
-      for (int off = 1; off < LPK; off <<= 1) d += __shfl_xor(d, off);
+      d = group_sum<LPK>(d);
       const bool ok = st * STEP + u * NG + grp < n_valid;
       z[u] = ok ? d : -INFINITY;
       mx = fmaxf(mx, z[u]);
@@ -175,15 +177,20 @@ __global__ __launch_bounds__(256) void swa_sink_decode_kernel(
     m = mn;
   };
 
-  // Two steps in flight: step s + 1 is loaded before step s is consumed.
+  // Software pipeline over steps, NBUF deep; buffer indices are compile-time.
   const int nsteps = (n_valid + STEP - 1) / STEP;
-  if (nsteps > 0) fetch(0, kr[0], vr[0]);
-  for (int st = 0; st < nsteps; st += 2) {
-    if (st + 1 < nsteps) fetch(st + 1, kr[1], vr[1]);
-    consume(st, kr[0], vr[0]);
-    if (st + 1 < nsteps) {
-      if (st + 2 < nsteps) fetch(st + 2, kr[0], vr[0]);
-      consume(st + 1, kr[1], vr[1]);
+#pragma unroll
+  for (int bb = 0; bb + 1 < NBUF; ++bb)
+    if (bb < nsteps) fetch(bb, kr[bb], vr[bb]);
+  for (int st = 0; st < nsteps; st += NBUF) {
+#pragma unroll
+    for (int bb = 0; bb < NBUF; ++bb) {
+      const int sc = st + bb;
+      if (sc < nsteps) {
+        if (sc + NBUF - 1 < nsteps)
+          fetch(sc + NBUF - 1, kr[(bb + NBUF - 1) % NBUF], vr[(bb + NBUF - 1) % NBUF]);
+        consume(sc, kr[bb], vr[bb]);
+      }
     }
   }
 
@@ -212,9 +219,21 @@ __global__ __launch_bounds__(256) void swa_sink_decode_kernel(
   }
 }
 
+// Work-group shape per element type: bf16 keys are one 16-byte load per lane.
+template <class TIn>
+struct SwaShape {
+  static constexpr int NT = 512, UNR = 4, NBUF = 2;
+};
+template <>
+struct SwaShape<float> {
+  static constexpr int NT = 256, UNR = 4, NBUF = 2;
+};
+
 template <class TIn, class TOut, int D>
 static hipError_t launch_swa_t(const SwaArgs& p) {
-  hipLaunchKernelGGL((swa_sink_decode_kernel<TIn, TOut, D>), dim3(p.B * p.H), dim3(256), 0,
+  typedef SwaShape<TIn> Sh;
+  hipLaunchKernelGGL((swa_sink_decode_kernel<TIn, TOut, D, Sh::NT, Sh::UNR, Sh::NBUF>),
+                     dim3(p.B * p.H), dim3(Sh::NT), 0,
                      (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k_new,
                      (const TIn*)p.v_new, (TIn*)p.k_cache, (TIn*)p.v_cache, p.n_tokens,
                      p.H, p.n_sink, p.window, p.softmax_scale, p.accumulate,
