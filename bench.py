@@ -11,6 +11,12 @@ One step = one pass of the whole hot path over one batch of synthetic input:
                          512 window slots, bf16 KV, writes the new token,
                          adds into the same output); the f32 state comes from
                          a GPU prefill of the 4096-token context (set-up)
+  leg "hybrid_prefill":  the hybrid layer over whole sequences, B=4, H=32,
+                         T=4096, d=128, 4 sinks + 512 window, bf16:
+                         gdn_hybrid_prefill (linear state over the tokens
+                         outside sinks and window, read with q shifted by the
+                         window; sink/window softmax added; decode caches and
+                         final state written)
   leg "conv_qwen32b":    Qwen-32B-shaped layer with projection adaptation:
                          gdn_short_conv_silu on q, k (with per-head L2 norm)
                          and v, then gdn_prefill_chunked; B=2, H=40, T=16384
@@ -66,6 +72,24 @@ def decode_gdn_bytes(d, esize=2):
     return 8 * d * d + esize * 3 * d + 8 + esize * d
 
 
+def swa_set_sizes(T, n_sink, window):
+    """|I_t| for t = 0..T-1: sinks {0..s-1} and window {t-w+1..t}, each once."""
+    t = torch.arange(T, dtype=torch.int64)
+    sinks = torch.clamp(t + 1, max=n_sink)
+    lo = torch.clamp(t - window + 1, min=n_sink)
+    return sinks + torch.clamp(t - lo + 1, min=0)
+
+
+# Softmax path over a sequence: q.k and p.v per attended pair, 2 d flops each.
+def swa_prefill_flops(B, T, H, d, n_sink, window):
+    return int(4 * d * swa_set_sizes(T, n_sink, window).sum().item()) * B * H
+
+
+# bf16 q, k, v read once; out written, and read back on the rows it adds to.
+def swa_prefill_bytes(B, T, H, d, acc_rows, esize=2):
+    return B * H * (T * (3 * d * esize + d * esize) + acc_rows * d * esize)
+
+
 def decode_swa_bytes(d, n_slots, esize=2):
     return esize * (2 * d * (n_slots - 1) + 2 * d + 2 * d + d + 2 * d)
 
@@ -119,7 +143,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill_long32k,decode_b256,conv_qwen32b,convstep_b256")
+    ap.add_argument("--legs", default="prefill_long32k,decode_b256,hybrid_prefill,"
+                                      "conv_qwen32b,convstep_b256")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) "
                          "and exit: the reference reading for HBM byte counters")
@@ -195,6 +220,39 @@ def make_decode_leg():
                 bytes_gdn=B * H * decode_gdn_bytes(d),
                 bytes_swa=B * H * decode_swa_bytes(d, s + w))
     return run, info, dict(q=q, k=k, v=v, alpha=a, beta=b, state=st)
+
+
+def make_hybrid_prefill_leg():
+    c = synthetic.CONFIGS["hybrid_prefill"]
+    B, T, H, d, s, w = c["B"], c["T"], c["H"], c["Dk"], c["n_sink"], c["window"]
+    x = synthetic.gdn_inputs(B, T, H, d, d, dtype="bf16", seed=c["seed"], device="cuda")
+    qs, ks, vs = synthetic.swa_seq_inputs(B, T, H, d, seed=c["seed"] + 1000, device="cuda")
+    out = torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda")
+    st = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    kc = torch.empty(B, H, s + w, d, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    ws = torch.empty(max(1, gdn.gdn_hybrid_prefill_workspace_bytes(B, T, H, d, s, w)),
+                     dtype=torch.uint8, device="cuda")
+
+    def run(mark):
+        gdn.gdn_hybrid_prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], qs, ks, vs,
+                               n_sink=s, window=w, state_out=st, out=out, k_cache=kc,
+                               v_cache=vc, workspace=ws)
+        mark("hybrid_prefill")
+
+    def swa_only():
+        gdn.gdn_swa_sink_prefill(qs, ks, vs, n_sink=s, window=w, accumulate_from=s + w,
+                                 out=out)
+
+    t_lin = T - w - s
+    swa_f = swa_prefill_flops(B, T, H, d, s, w)
+    swa_b = swa_prefill_bytes(B, T, H, d, T - s - w)
+    lin_f = prefill_flops_per_token_head(d) * B * t_lin * H
+    lin_b = prefill_bytes(B, t_lin, H, d)
+    info = dict(B=B, T=T, H=H, d=d, tokens=B * T, flops=lin_f + swa_f,
+                bytes=lin_b + swa_b + 2 * 2 * B * H * (s + w) * d * 2,
+                swa_flops=swa_f, swa_bytes=swa_b, swa_only=swa_only)
+    return run, info
 
 
 def make_conv_leg():
@@ -316,6 +374,9 @@ def main():
     if "decode_b256" in legs_wanted:
         run, info, x = make_decode_leg()
         legs["decode_b256"], infos["decode_b256"], keep["decode"] = run, info, x
+    if "hybrid_prefill" in legs_wanted:
+        run, info = make_hybrid_prefill_leg()
+        legs["hybrid_prefill"], infos["hybrid_prefill"] = run, info
     if "conv_qwen32b" in legs_wanted:
         run, info = make_conv_leg()
         legs["conv_qwen32b"], infos["conv_qwen32b"] = run, info
@@ -352,6 +413,20 @@ def main():
     all_evs = [step(True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # The softmax-path kernel of the hybrid prefill on its own (same inputs and
+    # launch shape as inside gdn_hybrid_prefill), for its roofline line.
+    swa_pref_ms = None
+    if "hybrid_prefill" in legs:
+        fn = infos["hybrid_prefill"]["swa_only"]
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        swa_pref_ms = a.elapsed_time(b) / args.steps
     leg_ms = {n: [e[n][0][1].elapsed_time(e[n][-1][1]) for e in all_evs] for n in legs}
     # per-kernel segment times (ms), averaged over the timed steps
     seg_ms = {}
@@ -409,6 +484,20 @@ def main():
                              seg_ms[("decode_b256", "decode_step")]),
                     hbm_roof("swa_sink_decode_kernel<bf16,bf16,128>", inf["bytes_swa"],
                              seg_ms[("decode_b256", "swa_sink_decode")])]
+    roof_swa_pref = None
+    if swa_pref_ms is not None:
+        inf = infos["hybrid_prefill"]
+        sec = swa_pref_ms / 1e3
+        kern = "swa_sink_prefill_kernel<bf16>"
+        # q, k, v and the output move 1,280 B per token-head against 264 kflop
+        # (516 attended keys): below the ridge, so HBM bounds it.
+        roof_swa_pref = dict(bound="hbm", kernel=kern, achieved=inf["swa_bytes"] / sec / 1e9,
+                             peak=PEAK_HBM_BPS / 1e9, unit="GB/s",
+                             frac=inf["swa_bytes"] / sec / PEAK_HBM_BPS,
+                             traffic=traffic_bytes(kern), bytes_per_launch=inf["swa_bytes"],
+                             ms_per_launch=swa_pref_ms, flops_per_launch=inf["swa_flops"],
+                             tflops=inf["swa_flops"] / sec / 1e12,
+                             mfma_frac=inf["swa_flops"] / sec / PEAK_BF16_FLOPS)
     roof_conv = None
     if "conv_qwen32b" in out_legs:
         inf = infos["conv_qwen32b"]
@@ -447,7 +536,8 @@ def main():
         "data": "synthetic (seeded torch.Generator; Llama/Qwen-shaped layers, random init)",
         "config": {
             "workload": "long32k prefill (B1 H32 T32768 d128, chunk 64) + hybrid decode "
-                        "(B256 H32 d128, 4 sinks + 512 window) + qwen32b conv+prefill "
+                        "(B256 H32 d128, 4 sinks + 512 window) + hybrid prefill (B4 H32 "
+                        "T4096 d128, 4 sinks + 512 window) + qwen32b conv+prefill "
                         "(B2 H40 T16384 d128) + decode-time conv step (B256, 3 x 5120 "
                         "channels, K 4)",
             "global_batch": 1, "seq_len": 32768, "parallelism": "single-gpu",
@@ -456,6 +546,7 @@ def main():
         "legs": out_legs,
         "roofline": roofline,
         "roofline_decode": roof_dec,
+        "roofline_swa_prefill": roof_swa_pref,
         "roofline_conv": roof_conv,
         "roofline_conv_step": roof_convstep,
         "cpu_baseline": cpu,

@@ -25,7 +25,8 @@ __all__ = [
     "GDN_BF16", "GDN_F32", "GdnError", "lib", "library_path",
     "gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
     "gdn_decode_step", "gdn_short_conv_silu", "gdn_short_conv_step",
-    "gdn_swa_sink_decode", "EXPORTED_SYMBOLS",
+    "gdn_swa_sink_decode", "gdn_swa_sink_prefill", "gdn_swa_cache_fill",
+    "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill", "EXPORTED_SYMBOLS",
 ]
 
 GDN_BF16 = 0
@@ -37,7 +38,8 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 EXPORTED_SYMBOLS = (
     "gdn_abi_version", "gdn_last_error", "gdn_prefill_workspace_bytes",
     "gdn_prefill_chunked", "gdn_decode_step", "gdn_short_conv_silu",
-    "gdn_short_conv_step", "gdn_swa_sink_decode",
+    "gdn_short_conv_step", "gdn_swa_sink_decode", "gdn_swa_sink_prefill",
+    "gdn_swa_cache_fill", "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +80,14 @@ def lib() -> ctypes.CDLL:
     L.gdn_short_conv_step.argtypes = [vp] * 4 + [i] * 4 + [f, i, i, vp]
     L.gdn_swa_sink_decode.restype = i
     L.gdn_swa_sink_decode.argtypes = [vp] * 6 + [i] * 5 + [f, i, vp, i, i, vp]
+    L.gdn_swa_sink_prefill.restype = i
+    L.gdn_swa_sink_prefill.argtypes = [vp] * 4 + [i] * 6 + [f, i, i, i, vp]
+    L.gdn_swa_cache_fill.restype = i
+    L.gdn_swa_cache_fill.argtypes = [vp] * 4 + [i] * 7 + [vp]
+    L.gdn_hybrid_prefill_workspace_bytes.restype = sz
+    L.gdn_hybrid_prefill_workspace_bytes.argtypes = [i] * 6
+    L.gdn_hybrid_prefill.restype = i
+    L.gdn_hybrid_prefill.argtypes = [vp] * 12 + [i] * 6 + [f, f, i, i, vp, sz, vp]
     _lib = L
     return L
 
@@ -265,3 +275,85 @@ def gdn_swa_sink_decode(q, k_cache, v_cache, n_tokens, *, n_sink, window,
         int(bool(accumulate)), _ptr(out), dt, _dtype_code(out), _stream(stream))
     _check("gdn_swa_sink_decode", st)
     return out
+
+
+def gdn_swa_sink_prefill(q, k, v, *, n_sink, window, softmax_scale=None,
+                         accumulate_from=None, out=None, out_dtype=None, stream=None):
+    """Softmax over sinks + sliding window at every position of a sequence.
+    q, k, v [B,T,H,D] bf16 (D = 128).  Rows t >= accumulate_from add into out
+    (None: write every row)."""
+    B, T, H, D = q.shape
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, q.shape)
+    _dev(v, "v", q.dtype, q.shape)
+    odt = _out_dtype(q.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        if accumulate_from is not None and accumulate_from < T:
+            raise ValueError("accumulate_from < T needs out")
+        out = torch.empty((B, T, H, D), dtype=odt, device=q.device)
+    _dev(out, "out", odt, (B, T, H, D))
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    acc = T if accumulate_from is None else int(accumulate_from)
+    st = lib().gdn_swa_sink_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H, D, int(n_sink), int(window),
+        float(softmax_scale), acc, _dtype_code(q), _dtype_code(out), _stream(stream))
+    _check("gdn_swa_sink_prefill", st)
+    return out
+
+
+def gdn_swa_cache_fill(k, v, k_cache, v_cache, *, n_sink, window, stream=None):
+    """Fill the [B,H,n_sink+window,D] decode caches from k, v [B,T,H,D]."""
+    B, T, H, D = k.shape
+    _dev(k, "k")
+    _dev(v, "v", k.dtype, k.shape)
+    _dev(k_cache, "k_cache", k.dtype, (B, H, n_sink + window, D))
+    _dev(v_cache, "v_cache", k.dtype, (B, H, n_sink + window, D))
+    st = lib().gdn_swa_cache_fill(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), B, T, H, D,
+                                  int(n_sink), int(window), _dtype_code(k), _stream(stream))
+    _check("gdn_swa_cache_fill", st)
+    return k_cache, v_cache
+
+
+def gdn_hybrid_prefill_workspace_bytes(B, T, H, D, n_sink, window) -> int:
+    return lib().gdn_hybrid_prefill_workspace_bytes(B, T, H, D, int(n_sink), int(window))
+
+
+def gdn_hybrid_prefill(q_lin, k_lin, v_lin, alpha, beta, q_swa, k_swa, v_swa, *, n_sink,
+                       window, lin_scale=1.0, softmax_scale=None, state_out=None, out=None,
+                       out_dtype=None, k_cache=None, v_cache=None, workspace=None,
+                       stream=None):
+    """Hybrid layer over a sequence: linear state over the tokens outside the
+    sinks and the window, read with q_lin, plus the sink/window softmax of
+    (q_swa, k_swa, v_swa).  All token tensors [B,T,H,D] bf16 (D = 128);
+    alpha, beta [B,T,H] f32.  Returns (out, state_out)."""
+    B, T, H, D = q_lin.shape
+    shp = (B, T, H, D)
+    for t, n in ((q_lin, "q_lin"), (k_lin, "k_lin"), (v_lin, "v_lin"), (q_swa, "q_swa"),
+                 (k_swa, "k_swa"), (v_swa, "v_swa")):
+        _dev(t, n, q_lin.dtype, shp)
+    _dev(alpha, "alpha", torch.float32, (B, T, H))
+    _dev(beta, "beta", torch.float32, (B, T, H))
+    odt = _out_dtype(q_lin.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        out = torch.empty(shp, dtype=odt, device=q_lin.device)
+    _dev(out, "out", odt, shp)
+    if state_out is None:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q_lin.device)
+    _dev(state_out, "state_out", torch.float32, (B, H, D, D))
+    nslot = n_sink + window
+    _dev(k_cache, "k_cache", q_lin.dtype, (B, H, nslot, D))
+    _dev(v_cache, "v_cache", q_lin.dtype, (B, H, nslot, D))
+    need = gdn_hybrid_prefill_workspace_bytes(B, T, H, D, n_sink, window)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lin.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    st = lib().gdn_hybrid_prefill(
+        _ptr(q_lin), _ptr(k_lin), _ptr(v_lin), _ptr(alpha), _ptr(beta), _ptr(q_swa),
+        _ptr(k_swa), _ptr(v_swa), _ptr(state_out), _ptr(out), _ptr(k_cache), _ptr(v_cache),
+        B, T, H, D, int(n_sink), int(window), float(lin_scale), float(softmax_scale),
+        _dtype_code(q_lin), _dtype_code(out), _ptr(workspace), wbytes, _stream(stream))
+    _check("gdn_hybrid_prefill", st)
+    return out, state_out

@@ -263,4 +263,142 @@ int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
   return hip_status(gdn::launch_swa(p), "gdn_swa_sink_decode launch");
 }
 
+int gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out, int B,
+                         int T, int H, int D, int n_sink, int window, float softmax_scale,
+                         int accumulate_from, int dtype, int out_dtype, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
+          H);
+  REQUIRE(n_sink >= 0 && window >= 1, GDN_ERR_INVALID_ARG, "bad n_sink=%d window=%d", n_sink,
+          window);
+  REQUIRE(dtype == GDN_BF16 && D == 128, GDN_ERR_UNSUPPORTED,
+          "the sequence softmax path takes bf16 inputs with D = 128 (got dtype %d, D %d)",
+          dtype, D);
+  REQUIRE((long long)B * H * ((T + 127) / 128) < (1LL << 31) && (long long)T * H * D < (1LL << 31),
+          GDN_ERR_UNSUPPORTED, "grid too large");
+  if ((long long)B * T == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  gdn::SwaPrefillArgs p;
+  p.q = q; p.k = k; p.v = v; p.out = out;
+  p.B = B; p.T = T; p.H = H; p.n_sink = n_sink; p.window = window;
+  p.acc_from = accumulate_from; p.softmax_scale = softmax_scale;
+  p.out_bf16 = out_dtype == GDN_BF16; p.stream = stream;
+  return hip_status(gdn::launch_swa_prefill(p), "gdn_swa_sink_prefill launch");
+}
+
+int gdn_swa_cache_fill(const void* k, const void* v, void* k_cache, void* v_cache, int B,
+                       int T, int H, int D, int n_sink, int window, int dtype, void* stream) {
+  REQUIRE(dtype == GDN_BF16 || dtype == GDN_F32, GDN_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
+          H);
+  REQUIRE(D == 64 || D == 128, GDN_ERR_UNSUPPORTED, "head dim %d not in {64,128}", D);
+  REQUIRE(n_sink >= 0 && window >= 1, GDN_ERR_INVALID_ARG, "bad n_sink=%d window=%d", n_sink,
+          window);
+  REQUIRE((long long)B * H < (1LL << 31), GDN_ERR_UNSUPPORTED, "grid too large");
+  if ((long long)B * T == 0) return ok();
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  gdn::SwaCacheFillArgs p;
+  p.k = k; p.v = v; p.k_cache = k_cache; p.v_cache = v_cache;
+  p.B = B; p.T = T; p.H = H; p.D = D; p.n_sink = n_sink; p.window = window;
+  p.bf16 = dtype == GDN_BF16; p.stream = stream;
+  return hip_status(gdn::launch_swa_cache_fill(p), "gdn_swa_cache_fill launch");
+}
+
+size_t gdn_hybrid_prefill_workspace_bytes(int B, int T, int H, int D, int n_sink, int window) {
+  if (B < 0 || T < 0 || H < 1 || D != 128 || n_sink < 0 || window < 1) return 0;
+  const long long t_lin = (long long)T - window - n_sink;
+  if (t_lin <= 0) return 0;
+  return gdn::prefill_workspace_bytes(B, (int)t_lin, H, D, D, 64, true);
+}
+
+int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
+                       const float* alpha, const float* beta, const void* q_swa,
+                       const void* k_swa, const void* v_swa, float* state_out, void* out,
+                       void* k_cache, void* v_cache, int B, int T, int H, int D, int n_sink,
+                       int window, float lin_scale, float softmax_scale, int dtype,
+                       int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
+          H);
+  REQUIRE(n_sink >= 0 && window >= 1, GDN_ERR_INVALID_ARG, "bad n_sink=%d window=%d", n_sink,
+          window);
+  REQUIRE(dtype == GDN_BF16 && D == 128, GDN_ERR_UNSUPPORTED,
+          "the hybrid prefill takes bf16 inputs with D = 128 (got dtype %d, D %d)", dtype, D);
+  REQUIRE((long long)B * H * ((T + 127) / 128) < (1LL << 31) && (long long)T * H * D < (1LL << 31),
+          GDN_ERR_UNSUPPORTED, "grid too large");
+  REQUIRE((k_cache == nullptr) == (v_cache == nullptr), GDN_ERR_INVALID_ARG,
+          "k_cache and v_cache must both be given or both be NULL");
+  REQUIRE_ALIGNED_OR_NULL(state_out);
+  REQUIRE_ALIGNED_OR_NULL(k_cache);
+  REQUIRE_ALIGNED_OR_NULL(v_cache);
+  if (B == 0) return ok();
+  const long long t_lin = (long long)T - window - n_sink;
+  if (T > 0) {
+    REQUIRE_PTR(q_swa);
+    REQUIRE_PTR(k_swa);
+    REQUIRE_PTR(v_swa);
+    REQUIRE_PTR(out);
+  }
+  if (t_lin > 0) {
+    REQUIRE_PTR(q_lin);
+    REQUIRE_PTR(k_lin);
+    REQUIRE_PTR(v_lin);
+    REQUIRE(alpha != nullptr && beta != nullptr, GDN_ERR_INVALID_ARG, "alpha/beta is NULL");
+    const size_t need = gdn::prefill_workspace_bytes(B, (int)t_lin, H, D, D, 64, true);
+    if (need > 0) {
+      REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
+      REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
+              "workspace is not 256-byte aligned");
+      REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG,
+              "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    }
+  }
+  // Linear path: the state at position t holds tokens n_sink .. t - window,
+  // so with q shifted by `window` it is the chunked prefill over those
+  // tokens, whose output row j is the layer's row j + window.  One launch
+  // over all sequences: their rows are views with a stride of T tokens.
+  const size_t row = (size_t)H * D;
+  const size_t os = esize(out_dtype);
+  const long long n = t_lin > 0 ? t_lin : 0;
+  if (n > 0 || state_out != nullptr) {
+    gdn::PrefillArgs p;
+    p.q = n ? (const char*)q_lin + (size_t)(n_sink + window) * row * 2 : nullptr;
+    p.k = n ? (const char*)k_lin + (size_t)n_sink * row * 2 : nullptr;
+    p.v = n ? (const char*)v_lin + (size_t)n_sink * row * 2 : nullptr;
+    p.alpha = n ? alpha + (size_t)n_sink * H : nullptr;
+    p.beta = n ? beta + (size_t)n_sink * H : nullptr;
+    p.state_in = nullptr;
+    p.state_out = state_out;
+    p.out = n ? (char*)out + (size_t)(n_sink + window) * row * os : nullptr;
+    p.B = B; p.T = (int)n; p.H = H; p.Dk = D; p.Dv = D; p.chunk = 64;
+    p.bf16 = true; p.out_bf16 = out_dtype == GDN_BF16; p.scale = lin_scale;
+    p.workspace = workspace; p.stream = stream; p.seq_stride = T;
+    const int st = hip_status(gdn::launch_prefill(p), "gdn_hybrid_prefill linear path");
+    if (st != GDN_OK) return st;
+  }
+  if (T > 0) {
+    gdn::SwaPrefillArgs p;
+    p.q = q_swa; p.k = k_swa; p.v = v_swa; p.out = out;
+    p.B = B; p.T = T; p.H = H; p.n_sink = n_sink; p.window = window;
+    p.acc_from = t_lin > 0 ? n_sink + window : T;
+    p.softmax_scale = softmax_scale; p.out_bf16 = out_dtype == GDN_BF16; p.stream = stream;
+    const int st = hip_status(gdn::launch_swa_prefill(p), "gdn_hybrid_prefill softmax path");
+    if (st != GDN_OK) return st;
+  }
+  if (k_cache != nullptr && T > 0) {
+    gdn::SwaCacheFillArgs p;
+    p.k = k_swa; p.v = v_swa; p.k_cache = k_cache; p.v_cache = v_cache;
+    p.B = B; p.T = T; p.H = H; p.D = D; p.n_sink = n_sink; p.window = window;
+    p.bf16 = true; p.stream = stream;
+    return hip_status(gdn::launch_swa_cache_fill(p), "gdn_hybrid_prefill cache fill");
+  }
+  return ok();
+}
+
 }  // extern "C"

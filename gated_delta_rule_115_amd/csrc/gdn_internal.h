@@ -30,6 +30,10 @@ struct PrefillArgs {
   float scale;
   void* workspace;
   void* stream;
+  // Tokens between the starts of consecutive sequences in q, k, v, out,
+  // alpha and beta (0 = T: dense [B, T, ...]).  Only the per-head kernels
+  // (bf16, Dk = Dv = 128, chunk 64) take another value.
+  int seq_stride = 0;
 };
 
 struct ConvArgs {
@@ -80,5 +84,27 @@ hipError_t launch_conv(const ConvArgs& p);
 // One decode step (T unused): state [B][K-1][Ch] of the input dtype, in place.
 hipError_t launch_conv_step(const ConvArgs& p, void* state);
 hipError_t launch_swa(const SwaArgs& p);
+
+// Sink + window softmax over a whole sequence: bf16 q, k, v [B, T, H, 128];
+// rows t >= acc_from add into out, rows below are written.
+struct SwaPrefillArgs {
+  const void *q, *k, *v;
+  void* out;
+  int B, T, H, n_sink, window, acc_from;
+  float softmax_scale;
+  bool out_bf16;
+  void* stream;
+};
+hipError_t launch_swa_prefill(const SwaPrefillArgs& p);
+
+// Decode-cache fill from a sequence's keys and values.
+struct SwaCacheFillArgs {
+  const void *k, *v;
+  void *k_cache, *v_cache;
+  int B, T, H, D, n_sink, window;
+  bool bf16;
+  void* stream;
+};
+hipError_t launch_swa_cache_fill(const SwaCacheFillArgs& p);
 
 }  // namespace gdn

@@ -649,6 +649,8 @@ static hipError_t launch_prefill_c(const PrefillArgs& p) {
 hipError_t launch_prefill(const PrefillArgs& p) {
   if (p.B * p.H == 0) return hipSuccess;
   if (prefill_head_supported(p)) return launch_prefill_head(p);
+  // The other kernels address dense [B, T, ...] tensors.
+  if (p.T > 0 && p.B > 1 && p.seq_stride > 0 && p.seq_stride != p.T) return hipErrorInvalidValue;
   if (prefill_fused_supported(p)) return launch_prefill_fused(p);
   return p.bf16 ? launch_prefill_c<bf16>(p) : launch_prefill_c<float>(p);
 }

@@ -311,18 +311,18 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
                                                    const bf16* __restrict__ v,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta, float* dstB,
-                                                   float* dstM, int b, int h, int T, int H,
-                                                   int c0, int NC) {
+                                                   float* dstM, int b, int h, int T, int TS,
+                                                   int H, int c0, int NC) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
   const int tok = H * HD;                // elements between consecutive tokens
-  const size_t head0 = ((size_t)b * T + (size_t)c0 * HC) * tok + (size_t)h * HD;
+  const size_t head0 = ((size_t)b * TS + (size_t)c0 * HC) * tok + (size_t)h * HD;
   const int Ts = T - c0 * HC;            // tokens from the segment start to the sequence end
   const bf16* kh = k + head0;
   const bf16* vh = v + head0;
-  const float* ah = alpha + ((size_t)b * T + (size_t)c0 * HC) * H + h;
-  const float* bhp = beta + ((size_t)b * T + (size_t)c0 * HC) * H + h;
+  const float* ah = alpha + ((size_t)b * TS + (size_t)c0 * HC) * H + h;
+  const float* bhp = beta + ((size_t)b * TS + (size_t)c0 * HC) * H + h;
 
   // Tile pieces of this thread: rows pr and pr + 32, 8 columns from pc.
   const int pr = tid >> 4, pc = (tid & 15) * 8;
@@ -645,12 +645,12 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
                                             const float* __restrict__ alpha,
                                             const float* __restrict__ beta, const float* s0,
                                             float* s_final, TOut* __restrict__ out, int b, int h,
-                                            int T, int H, int c0, int NC, float scale) {
+                                            int T, int TS, int H, int c0, int NC, float scale) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
   const int tok = H * HD;                // elements between consecutive tokens
-  const size_t head0 = ((size_t)b * T + (size_t)c0 * HC) * tok + (size_t)h * HD;
+  const size_t head0 = ((size_t)b * TS + (size_t)c0 * HC) * tok + (size_t)h * HD;
   const int Ts = T - c0 * HC;            // tokens from the segment start to the sequence end
   const int NIT = NC + 2;                // chunk c's outputs are formed at iteration c + 2
 
@@ -873,8 +873,8 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
     const bf16* qh = q + head0;
     const bf16* kh = k + head0;
     const bf16* vh = v + head0;
-    const float* ah = alpha + ((size_t)b * T + (size_t)c0 * HC) * H + h;
-    const float* bhp = beta + ((size_t)b * T + (size_t)c0 * HC) * H + h;
+    const float* ah = alpha + ((size_t)b * TS + (size_t)c0 * HC) * H + h;
+    const float* bhp = beta + ((size_t)b * TS + (size_t)c0 * HC) * H + h;
     // Tile pieces of this thread: rows pr + 16 u (u = 0..3), 8 columns from pc.
     const int pr = ht >> 4, pc = (ht & 15) * 8;
     // Each iteration issues K 4 loads (phase 1), gates 2, Q 4, V 4 (phase
@@ -1079,17 +1079,17 @@ template <class TOut>
 __global__ __launch_bounds__(HNT) void prefill_lead_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
-    TOut* __restrict__ out, SegWs ws, SegGeom g, int T, int H, float scale) {
+    TOut* __restrict__ out, SegWs ws, SegGeom g, int T, int TS, int H, float scale) {
   __shared__ PrefillSmem sm;
   const int bh = blockIdx.x / (g.P - 1), s = blockIdx.x % (g.P - 1);
   const int b = bh / H, h = bh % H;
   if (s == 0) {
     out_segment<TOut>(sm.h, q, k, v, alpha, beta,
                       state_in ? state_in + (size_t)bh * HD * HD : nullptr,
-                      ws.S + ws.at(bh, 0, g.P), out, b, h, T, H, 0, g.count(0), scale);
+                      ws.S + ws.at(bh, 0, g.P), out, b, h, T, TS, H, 0, g.count(0), scale);
   } else {
     transition_segment(sm.t, k, v, alpha, beta, ws.B + ws.at(bh, s, g.P),
-                       ws.M + ws.at(bh, s, g.P), b, h, T, H, g.first(s), g.count(s));
+                       ws.M + ws.at(bh, s, g.P), b, h, T, TS, H, g.first(s), g.count(s));
   }
 }
 
@@ -1100,8 +1100,8 @@ template <class TOut>
 __global__ __launch_bounds__(HNT) void prefill_out_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
-    float* state_out, TOut* __restrict__ out, SegWs ws, SegGeom g, int s_first, int T, int H,
-    float scale) {
+    float* state_out, TOut* __restrict__ out, SegWs ws, SegGeom g, int s_first, int T, int TS,
+    int H, float scale) {
   __shared__ HSmem sm;
   const int n = g.P - s_first;
   const int bh = blockIdx.x / n, s = s_first + blockIdx.x % n;
@@ -1109,8 +1109,8 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
   const float* s0 = s == 0 ? (state_in ? state_in + (size_t)bh * HD * HD : nullptr)
                            : ws.S + ws.at(bh, s - 1, g.P);
   float* sf = (s == g.P - 1 && state_out) ? state_out + (size_t)bh * HD * HD : nullptr;
-  out_segment<TOut>(sm, q, k, v, alpha, beta, s0, sf, out, b, h, T, H, g.first(s), g.count(s),
-                    scale);
+  out_segment<TOut>(sm, q, k, v, alpha, beta, s0, sf, out, b, h, T, TS, H, g.first(s),
+                    g.count(s), scale);
 }
 
 // Initial states of segments 2 .. P - 1: from S_1 (left in the workspace by
@@ -1229,6 +1229,7 @@ static hipError_t launch_head_t(const PrefillArgs& p) {
   g.NCT = (p.T + HC - 1) / HC;
   prefill_head_segments(p.B, p.T, p.H, &g.P, &g.L0, &g.L);
   const int BH = p.B * p.H;
+  const int TS = p.seq_stride > 0 ? p.seq_stride : p.T;  // tokens between sequence starts
   SegWs ws{nullptr, nullptr, nullptr};
   const hipStream_t st = (hipStream_t)p.stream;
   const bf16 *q = (const bf16*)p.q, *k = (const bf16*)p.k, *v = (const bf16*)p.v;
@@ -1239,14 +1240,15 @@ static hipError_t launch_head_t(const PrefillArgs& p) {
     ws.B = ws.M + n;
     ws.S = ws.B + n;
     hipLaunchKernelGGL((prefill_lead_kernel<TOut>), dim3(BH * (g.P - 1)), dim3(HNT), 0, st, q, k,
-                       v, p.alpha, p.beta, p.state_in, (TOut*)p.out, ws, g, p.T, p.H, p.scale);
+                       v, p.alpha, p.beta, p.state_in, (TOut*)p.out, ws, g, p.T, TS, p.H,
+                       p.scale);
     if (g.P > 2)
       hipLaunchKernelGGL(segment_combine_kernel, dim3(BH * 8), dim3(256), 0, st, ws, g.P);
     s_first = 1;
   }
   hipLaunchKernelGGL((prefill_out_kernel<TOut>), dim3(BH * (g.P - s_first)), dim3(HNT), 0, st, q,
                      k, v, p.alpha, p.beta, p.state_in, p.state_out, (TOut*)p.out, ws, g, s_first,
-                     p.T, p.H, p.scale);
+                     p.T, TS, p.H, p.scale);
   return hipGetLastError();
 }
 

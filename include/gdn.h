@@ -180,6 +180,78 @@ int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
                         float softmax_scale, int accumulate, void* out,
                         int dtype, int out_dtype, void* stream);
 
+/*
+ * Softmax over sink tokens and a sliding window at every position of a
+ * sequence (section 4, "Adding Sliding Window Attention", in prefill form):
+ * position t (0-based) attends to I_t = {0 .. n_sink-1} u {t-window+1 .. t},
+ * each position at most once, with logits softmax_scale * q_t . k_i.
+ *   q, k, v  [B, T, H, D] dtype: the softmax path's own projections
+ *   out      [B, T, H, D] out_dtype.  Rows t >= accumulate_from add the
+ *            result (out += y), rows below it are overwritten: pass T (or
+ *            more) for a plain write, 0 to add to every row.
+ * Limits: dtype GDN_BF16 and D = 128 (else GDN_ERR_UNSUPPORTED); n_sink >= 0;
+ * window >= 1.  out must not overlap q, k or v.
+ */
+int gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out, int B,
+                         int T, int H, int D, int n_sink, int window, float softmax_scale,
+                         int accumulate_from, int dtype, int out_dtype, void* stream);
+
+/*
+ * Fill the decode-time KV cache of gdn_swa_sink_decode from a sequence's
+ * keys and values (section 4: the cache keeps the sinks and the window):
+ *   k, v     [B, T, H, D] dtype
+ *   k_cache, v_cache [B, H, n_sink + window, D] dtype, caller-owned.  Slot
+ *            i < n_sink gets position i (i < T); position p >= n_sink, for the
+ *            last `window` such positions before T, goes to slot
+ *            n_sink + (p - n_sink) % window.  Other slots are left untouched.
+ * After it, gdn_swa_sink_decode with n_tokens = T + 1 attends the right set.
+ * Limits: D in {64, 128}; n_sink >= 0; window >= 1.
+ */
+int gdn_swa_cache_fill(const void* k, const void* v, void* k_cache, void* v_cache, int B,
+                       int T, int H, int D, int n_sink, int window, int dtype, void* stream);
+
+/*
+ * Workspace (bytes) that gdn_hybrid_prefill needs for these sizes (0 = none;
+ * reusable across calls on one stream).  0 for unsupported sizes.
+ */
+size_t gdn_hybrid_prefill_workspace_bytes(int B, int T, int H, int D, int n_sink, int window);
+
+/*
+ * The whole hybrid layer over a sequence (section 4, "Adding Sliding Window
+ * Attention": the linear state holds exactly the tokens in neither the sinks
+ * nor the window, and the two read-outs are added without weights):
+ *   out_t = lin_scale * S_lin(t)^T q_lin_t + y^swa_t,
+ * where S_lin(t) is the section 3.1.2 state over tokens n_sink .. t-window
+ * (0-based; S = 0 when that set is empty) and y^swa is gdn_swa_sink_prefill.
+ *   q_lin, k_lin, v_lin [B, T, H, D] dtype and alpha, beta [B, T, H] f32: the
+ *            linear path's inputs (token j enters the state with its own
+ *            alpha_j, beta_j, k_j, v_j when it leaves the window)
+ *   q_swa, k_swa, v_swa [B, T, H, D] dtype: the softmax path's inputs
+ *   state_out [B, H, D, D] f32 or NULL: the linear state after the sequence
+ *            (tokens n_sink .. T-1-window), the state the next decode step
+ *            starts from (that step inserts token T - window with
+ *            gdn_decode_step before reading it)
+ *   out      [B, T, H, D] out_dtype
+ *   k_cache, v_cache [B, H, n_sink + window, D] dtype, or both NULL: filled
+ *            as by gdn_swa_cache_fill for the decode steps that follow
+ *   workspace: gdn_hybrid_prefill_workspace_bytes(...) bytes, 256-byte
+ *            aligned (NULL allowed when that is 0)
+ * Enqueues the linear path (one chunked prefill over all sequences, reading
+ * them as strided views), then the softmax path adding into out, then the
+ * cache fill.  With a bf16 out, the
+ * linear read-out is stored as bf16 first and the sum is rounded once more
+ * (as in the decode pair gdn_decode_step + gdn_swa_sink_decode with
+ * accumulate = 1); an f32 out rounds neither.  Limits: dtype
+ * GDN_BF16 and D = 128 (else GDN_ERR_UNSUPPORTED).  No output may overlap
+ * an input.
+ */
+int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
+                       const float* alpha, const float* beta, const void* q_swa,
+                       const void* k_swa, const void* v_swa, float* state_out, void* out,
+                       void* k_cache, void* v_cache, int B, int T, int H, int D, int n_sink,
+                       int window, float lin_scale, float softmax_scale, int dtype,
+                       int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

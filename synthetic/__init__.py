@@ -36,6 +36,8 @@ CONFIGS = {
                          chunk=64, state0="zero", seed=4, conv_kernel=4),
     "hybrid_decode": dict(B=256, H=32, T=1, Dk=128, Dv=128, dtype="bf16",
                           n_sink=4, window=512, context=4096, seed=5),
+    "hybrid_prefill": dict(B=4, H=32, T=4096, Dk=128, Dv=128, dtype="bf16",
+                           n_sink=4, window=512, seed=6),
 }
 
 TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -92,6 +94,13 @@ def swa_inputs(B, H, D, n_slots, dtype="bf16", seed=0, device="cpu"):
     kc = _randn((B, H, n_slots, D), g, device).to(dt).contiguous()
     vc = _randn((B, H, n_slots, D), g, device).to(dt).contiguous()
     return q, kc, vc
+
+
+def swa_seq_inputs(B, T, H, D, dtype="bf16", seed=0, device="cpu"):
+    """Raw softmax-path q, k, v [B,T,H,D] ~ N(0,1) over a whole sequence."""
+    g = _gen(seed, device)
+    dt = TORCH_DTYPE[dtype]
+    return tuple(_randn((B, T, H, D), g, device).to(dt).contiguous() for _ in range(3))
 
 
 def to_f64(x):

@@ -155,6 +155,59 @@ def test_swa_validation():
     assert call(nt=None) == INVALID
 
 
+def test_swa_prefill_validation():
+    L = gdn.lib()
+    call = lambda **kw: L.gdn_swa_sink_prefill(
+        kw.get("q", A), A, A, A, kw.get("B", 2), kw.get("T", 64), 2, kw.get("D", 128),
+        kw.get("s", 4), kw.get("w", 8), 0.1, 64, kw.get("dt", BF16), kw.get("odt", BF16), None)
+    assert call(D=64) == UNSUPPORTED
+    assert call(dt=F32, odt=F32) == UNSUPPORTED
+    assert call(w=0) == INVALID
+    assert call(s=-1) == INVALID
+    assert call(q=None) == INVALID and "q" in _err()
+    assert call(q=A + 8) == INVALID and "aligned" in _err()
+    assert call(T=0, q=None) == OK
+
+
+def test_swa_cache_fill_validation():
+    L = gdn.lib()
+    call = lambda **kw: L.gdn_swa_cache_fill(
+        A, A, kw.get("kc", A), A, 2, kw.get("T", 64), 2, kw.get("D", 128), 4,
+        kw.get("w", 8), kw.get("dt", BF16), None)
+    assert call(D=96) == UNSUPPORTED
+    assert call(w=0) == INVALID
+    assert call(dt=3) == INVALID
+    assert call(kc=None) == INVALID
+    assert call(T=0, kc=None) == OK
+
+
+def test_hybrid_prefill_validation():
+    L = gdn.lib()
+    ws = L.gdn_hybrid_prefill_workspace_bytes(4, 4096, 32, 128, 4, 512)
+    assert ws > 0 and ws % 256 == 0
+    assert L.gdn_hybrid_prefill_workspace_bytes(4, 4096, 32, 64, 4, 512) == 0
+    assert L.gdn_hybrid_prefill_workspace_bytes(1, 500, 32, 128, 4, 512) == 0  # no linear set
+
+    def call(**kw):
+        a = dict(ql=A, al=A, qs=A, so=None, out=A, kc=None, vc=None, B=4, T=4096, H=32, D=128,
+                 s=4, w=512, dt=BF16, odt=BF16, ws=A, wsb=ws)
+        a.update(kw)
+        return L.gdn_hybrid_prefill(a["ql"], A, A, a["al"], A, a["qs"], A, A, a["so"], a["out"],
+                                    a["kc"], a["vc"], a["B"], a["T"], a["H"], a["D"], a["s"],
+                                    a["w"], 1.0, 0.1, a["dt"], a["odt"], a["ws"], a["wsb"], None)
+    assert call(D=64) == UNSUPPORTED
+    assert call(dt=F32, odt=F32) == UNSUPPORTED
+    assert call(w=0) == INVALID
+    assert call(kc=A) == INVALID and "both" in _err()
+    assert call(wsb=ws - 256) == INVALID and "workspace too small" in _err()
+    assert call(ws=None) == INVALID and "workspace" in _err()
+    assert call(ql=None) == INVALID and "q_lin" in _err()
+    assert call(al=None) == INVALID and "alpha" in _err()
+    assert call(qs=None) == INVALID and "q_swa" in _err()
+    assert call(so=A + 4) == INVALID and "state_out" in _err()
+    assert call(B=0, ql=None, qs=None, out=None) == OK
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "_lib", None)
     monkeypatch.setattr(gdn, "library_path", str(tmp_path / "absent.so"))

@@ -1,0 +1,172 @@
+"""GPU parity: the sink + sliding-window softmax over a whole sequence and the
+hybrid layer prefill (disjoint linear state + softmax path) of "The Key to
+Going Linear: Analysis-Driven Transformer Linearization", section 4 ("Adding
+Sliding Window Attention"), against the CPU oracle; the decode-cache fill; and
+a prefill followed by one hybrid decode step against the oracle's layer output
+at the next position.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_115_amd as gdn
+import oracle
+import synthetic
+from common import TOL, assert_bf16_is_rounded_f32, dev, err, f64, say
+
+pytestmark = pytest.mark.gpu
+D = 128
+SM = 1 / math.sqrt(D)
+
+
+def slot_of(p, s, w):
+    return p if p < s else s + (p - s) % w
+
+
+# (B, T, H, n_sink, window): several query blocks with a ragged tail; plain
+# causal softmax (no sinks, window past T); sinks spanning more than one key
+# block beside a short window; window 1 (sinks + the token itself); T = 1; a
+# window that is not a multiple of the key block.
+SWA_CASES = [(2, 300, 3, 4, 64), (1, 200, 2, 0, 1000), (1, 333, 2, 70, 40),
+             (2, 100, 2, 4, 1), (1, 1, 2, 4, 8), (1, 517, 1, 4, 100)]
+
+
+@pytest.mark.parametrize("B,T,H,s,w", SWA_CASES)
+def test_swa_prefill_matches_oracle(B, T, H, s, w):
+    say(f"swa prefill B{B} T{T} H{H} s{s} w{w}")
+    q, k, v = synthetic.swa_seq_inputs(B, T, H, D, seed=T + w)
+    y = gdn.gdn_swa_sink_prefill(dev(q), dev(k), dev(v), n_sink=s, window=w,
+                                 out_dtype=torch.float32)
+    yb = gdn.gdn_swa_sink_prefill(dev(q), dev(k), dev(v), n_sink=s, window=w)
+    torch.cuda.synchronize()
+    ref = oracle.swa_sink_attention(f64(q), f64(k), f64(v), s, w, SM)
+    e = err(y, ref)
+    say(f"  err {e:.2e}")
+    assert e <= TOL["bf16"]
+    assert_bf16_is_rounded_f32(yb.cpu(), y.cpu())
+
+
+def test_swa_prefill_accumulate_from():
+    B, T, H, s, w = 2, 260, 2, 4, 64
+    q, k, v = synthetic.swa_seq_inputs(B, T, H, D, seed=9)
+    base = torch.randn(B, T, H, D, generator=torch.Generator().manual_seed(1))
+    out = dev(base.clone())
+    gdn.gdn_swa_sink_prefill(dev(q), dev(k), dev(v), n_sink=s, window=w,
+                             accumulate_from=100, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.swa_sink_attention(f64(q), f64(k), f64(v), s, w, SM)
+    ref[:, 100:] += f64(base)[:, 100:]
+    assert err(out, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [3, 70, 600])
+def test_swa_cache_fill_follows_slot_rule(T):
+    B, H, s, w = 2, 3, 4, 64
+    q, k, v = synthetic.swa_seq_inputs(B, T, H, D, seed=T)
+    junk = torch.full((B, H, s + w, D), 7.0).to(torch.bfloat16)
+    kc, vc = dev(junk.clone()), dev(junk.clone())
+    gdn.gdn_swa_cache_fill(dev(k), dev(v), kc, vc, n_sink=s, window=w)
+    torch.cuda.synchronize()
+    ek, ev = junk.clone(), junk.clone()
+    for p in range(T):
+        if p < s or p >= max(s, T - w):
+            ek[:, :, slot_of(p, s, w)] = k[:, p]
+            ev[:, :, slot_of(p, s, w)] = v[:, p]
+    assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev)
+
+
+def _hybrid_inputs(B, T, H, seed):
+    x = synthetic.gdn_inputs(B, T, H, D, D, dtype="bf16", seed=seed)
+    qs, ks, vs = synthetic.swa_seq_inputs(B, T, H, D, seed=seed + 1000)
+    return x, (qs, ks, vs)
+
+
+def _run_hybrid(x, sw, s, w, **kw):
+    return gdn.gdn_hybrid_prefill(*(dev(x[n]) for n in ("q", "k", "v", "alpha", "beta")),
+                                  *(dev(t) for t in sw), n_sink=s, window=w, **kw)
+
+
+# (B, T, H, n_sink, window): linear part over several chunks; T <= s + w
+# (empty linear set, zero state); a linear set shorter than one chunk.
+@pytest.mark.parametrize("B,T,H,s,w", [(2, 400, 2, 4, 64), (1, 300, 2, 4, 512),
+                                       (1, 150, 2, 8, 128), (2, 1100, 1, 4, 200)])
+def test_hybrid_prefill_matches_oracle(B, T, H, s, w):
+    say(f"hybrid prefill B{B} T{T} H{H} s{s} w{w}")
+    x, sw = _hybrid_inputs(B, T, H, seed=T)
+    o, st = _run_hybrid(x, sw, s, w, out_dtype=torch.float32)
+    ob, _ = _run_hybrid(x, sw, s, w)
+    torch.cuda.synchronize()
+    args = [f64(x[n]) for n in ("q", "k", "v", "alpha", "beta")] + [f64(t) for t in sw]
+    ref = oracle.hybrid(*args, s, w, softmax_scale=SM)
+    e = err(o, ref)
+    lo, hi = s, max(s, T - w)
+    _, rs = oracle.gdn_recurrence(*(f64(x[n])[:, lo:hi] for n in ("q", "k", "v", "alpha", "beta")))
+    es = err(st, rs) if hi > lo else float(torch.count_nonzero(st))
+    say(f"  out err {e:.2e}, state err {es:.2e}")
+    assert e <= TOL["bf16"] and es <= TOL["bf16"]
+    # A bf16 output rounds the linear read-out o - y to bf16, then the sum:
+    # each rounding moves a value by at most 2^-8 of its magnitude.
+    y = gdn.gdn_swa_sink_prefill(*(dev(t) for t in sw), n_sink=s, window=w,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o, y, ob = o.cpu().double(), y.cpu().double(), ob.cpu().double()
+    bound = 2.0 ** -8 * ((o - y).abs() + o.abs()) * (1 + 2.0 ** -7) + 1e-30
+    assert bool(((ob - o).abs() <= bound).all())
+
+
+def test_hybrid_prefill_then_decode_step():
+    """Prefill T tokens (state + decode caches), then one hybrid decode step
+    for token T: equals the oracle's layer output at position T."""
+    B, T, H, s, w = 2, 300, 2, 4, 64
+    x, sw = _hybrid_inputs(B, T + 1, H, seed=77)
+    names = ("q", "k", "v", "alpha", "beta")
+    pre = {n: x[n][:, :T].contiguous() for n in names}
+    swp = tuple(t[:, :T].contiguous() for t in sw)
+    kc = dev(torch.zeros(B, H, s + w, D, dtype=torch.bfloat16))
+    vc = dev(torch.zeros(B, H, s + w, D, dtype=torch.bfloat16))
+    _, st = _run_hybrid(pre, swp, s, w, k_cache=kc, v_cache=vc)
+    # token j = T - w leaves the window and enters the state, which is then
+    # read with the current token's query
+    j = T - w
+    kj, vj, aj, bj = (dev(x[n][:, j].contiguous()) for n in ("k", "v", "alpha", "beta"))
+    out, _ = gdn.gdn_decode_step(dev(x["q"][:, T].contiguous()), kj, vj, aj, bj, st,
+                                 state_out=st, out_dtype=torch.float32)
+    nt = dev(torch.full((B,), T + 1, dtype=torch.int32))
+    gdn.gdn_swa_sink_decode(dev(sw[0][:, T].contiguous()), kc, vc, nt, n_sink=s, window=w,
+                            k_new=dev(sw[1][:, T].contiguous()),
+                            v_new=dev(sw[2][:, T].contiguous()), accumulate=True, out=out)
+    torch.cuda.synchronize()
+    args = [f64(x[n]) for n in names] + [f64(t) for t in sw]
+    ref = oracle.hybrid(*args, s, w, softmax_scale=SM)[:, T]
+    e = err(out, ref)
+    say(f"prefill + decode step err {e:.2e}")
+    assert e <= TOL["bf16"]
+
+
+def test_hybrid_prefill_full_size_sampled():
+    """The hybrid prefill workload (B4 H32 T4096, 4 sinks + 512 window) in the
+    launch configuration the bench times; three sampled heads against the
+    oracle (outputs and final state)."""
+    c = synthetic.CONFIGS["hybrid_prefill"]
+    B, T, H, s, w = c["B"], c["T"], c["H"], c["n_sink"], c["window"]
+    x, sw = _hybrid_inputs(B, T, H, seed=c["seed"])
+    o, st = _run_hybrid(x, sw, s, w, out_dtype=torch.float32)
+    ob, _ = _run_hybrid(x, sw, s, w)  # the bench's bf16 output
+    y = gdn.gdn_swa_sink_prefill(*(dev(t) for t in sw), n_sink=s, window=w,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    d = (ob.double() - o.double()).abs()
+    bound = 2.0 ** -8 * ((o.double() - y.double()).abs() + o.double().abs()) * (1 + 2.0 ** -7)
+    assert bool((d <= bound + 1e-30).all())
+    del ob, y, d, bound
+    for b, h in ((0, 0), (1, 17), (3, 31)):
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        args = [f64(x[n][sl]) for n in ("q", "k", "v", "alpha", "beta")] + [f64(t[sl]) for t in sw]
+        ref = oracle.hybrid(*args, s, w, softmax_scale=SM)
+        _, rs = oracle.gdn_recurrence(*(f64(x[n][sl])[:, s:T - w] for n in ("q", "k", "v", "alpha", "beta")))
+        e = err(o[sl].contiguous(), ref)
+        es = err(st[b:b + 1, h:h + 1].contiguous(), rs)
+        say(f"  head ({b},{h}): out err {e:.2e}, state err {es:.2e}")
+        assert e <= TOL["bf16"] and es <= TOL["bf16"]
