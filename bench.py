@@ -106,22 +106,28 @@ PREFILL_KERNELS = "prefill_lead_kernel<bf16> + segment_combine_kernel + prefill_
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="25cc6d6ec9848d990a8b5a34bb15c4213211b026",
-        fetch_kib=258220 + 71711 + 404975, write_kib=28672 + 14336 + 264195,
+        sha1="b59d12c44fab1aaa70540f5992f06ee343d3de89",
+        fetch_kib=248588 + 73758 + 373114, write_kib=55324 + 14336 + 239618,
         profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
-        sha1="b476cc39e7e5f69ceb396d81745208125716902b",
-        fetch_kib=265794, write_kib=526336, profile=PROFILE),
+        sha1="02983eefd933df1e58e3c70b84eb4b79e821b4f6",
+        fetch_kib=265774, write_kib=526431, profile=PROFILE),
     "swa_sink_decode_kernel<bf16,bf16,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa.hip",
-        sha1="f2d0a8fbd56e119c1501157da94f01005e2a3f95",
-        fetch_kib=1061017, write_kib=6144, profile=PROFILE),
+        sha1="afa1a0eccd2a4fdf0d91fdc379ee91e97784c24f",
+        fetch_kib=1062049, write_kib=6144, profile=PROFILE),
+    # mean of the three launches of the counter run (same inputs)
+    "swa_sink_prefill_kernel<bf16>": dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_swa_prefill.hip",
+        sha1="ebef4b7f4449660d27e60ada66979c84477530f1",
+        fetch_kib=(444994 + 440958 + 442816) / 3, write_kib=(133787 + 133882 + 133955) / 3,
+        profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
-        sha1="dc58eef25b3e6bd35e4799338aa19dcd478fa1df",
-        fetch_kib=168117 + 168135 + 168149, write_kib=3 * 327680, profile=PROFILE),
+        sha1="92b6d24215239cccaa8a33d420f5e803ae0fe4a5",
+        fetch_kib=168115 + 168109 + 168120, write_kib=327681 + 327680 + 327697, profile=PROFILE),
 }
 READ_FACTOR, WRITE_FACTOR = 2.00, 1.00
 

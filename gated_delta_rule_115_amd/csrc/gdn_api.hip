@@ -1,5 +1,6 @@
 // C ABI of the GDN library: host-side argument validation, then launch on the
 // caller's stream.  Nothing here allocates, frees or synchronises.
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -274,6 +275,8 @@ int gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out,
   REQUIRE(dtype == GDN_BF16 && D == 128, GDN_ERR_UNSUPPORTED,
           "the sequence softmax path takes bf16 inputs with D = 128 (got dtype %d, D %d)",
           dtype, D);
+  REQUIRE(softmax_scale > 0.f && softmax_scale < INFINITY, GDN_ERR_INVALID_ARG,
+          "softmax_scale must be positive and finite");
   REQUIRE((long long)B * H * ((T + 127) / 128) < (1LL << 31) && (long long)T * H * D < (1LL << 31),
           GDN_ERR_UNSUPPORTED, "grid too large");
   if ((long long)B * T == 0) return ok();
@@ -330,6 +333,8 @@ int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
           window);
   REQUIRE(dtype == GDN_BF16 && D == 128, GDN_ERR_UNSUPPORTED,
           "the hybrid prefill takes bf16 inputs with D = 128 (got dtype %d, D %d)", dtype, D);
+  REQUIRE(softmax_scale > 0.f && softmax_scale < INFINITY, GDN_ERR_INVALID_ARG,
+          "softmax_scale must be positive and finite");
   REQUIRE((long long)B * H * ((T + 127) / 128) < (1LL << 31) && (long long)T * H * D < (1LL << 31),
           GDN_ERR_UNSUPPORTED, "grid too large");
   REQUIRE((k_cache == nullptr) == (v_cache == nullptr), GDN_ERR_INVALID_ARG,

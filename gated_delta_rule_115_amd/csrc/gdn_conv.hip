@@ -18,16 +18,19 @@
 
 namespace gdn {
 
+// Outputs are written with non-temporal stores: each is written once and the
+// stream is larger than the caches.
 template <class TIn>
 __device__ __forceinline__ void store8(TIn* p, const float* f) {
   if constexpr (sizeof(TIn) == 2) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     bf16x8 x;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (bf16)f[e];
-    *reinterpret_cast<bf16x8*>(p) = x;
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x), reinterpret_cast<u32x4*>(p));
   } else {
-    *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+    __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{f[4], f[5], f[6], f[7]}, reinterpret_cast<f32x4*>(p + 4));
   }
 }
 
@@ -110,15 +113,12 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_silu_kernel(
   }
 
   const int gl = group / 8;  // lanes per L2 group (0 = no normalisation)
-  // Rows of block t0 .. t0 + kConvBlk - 1 (zero past the run or when inactive).
+  // Rows of block t0 .. t0 + kConvBlk - 1.  Past the run the last row is
+  // loaded again (its results are not stored), so every block issues the
+  // same loads without branches; an inactive thread reads channel 0.
   auto fetch = [&](int t0, Raw8<TIn>* rows) {
 #pragma unroll
-    for (int u = 0; u < kConvBlk; ++u) {
-      if (active && t0 + u < te)
-        rows[u] = load_raw8(xb + (size_t)(t0 + u) * Ch);
-      else
-        zero_raw8(rows[u]);
-    }
+    for (int u = 0; u < kConvBlk; ++u) rows[u] = load_raw8(xb + (size_t)min(t0 + u, te - 1) * Ch);
   };
   auto consume = [&](int t0, const Raw8<TIn>* rows) {
 #pragma unroll

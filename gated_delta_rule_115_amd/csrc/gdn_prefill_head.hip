@@ -1119,7 +1119,8 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
 // with v_mfma_f32_16x16x4_f32: in the 16-key block jj, product i takes key
 // 16 jj + 4 q + i in lane group q, so each lane reads its 4 keys of M with
 // one 16-byte load and S (kept transposed in LDS) with one 16-byte read.  The
-// next segment's M and B are loaded while the current product runs.
+// next segment's M and B are loaded while the current product runs; the
+// barriers order LDS only, so those loads stay in flight across them.
 __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
   __shared__ __align__(16) float St[16][HD + 4];  // S slice transposed: [column][key]
   const int bh = blockIdx.x >> 3, col0 = 16 * (blockIdx.x & 7);
@@ -1145,7 +1146,7 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
     }
   };
   load(1, mA, bA);
-  __syncthreads();
+  lds_barrier();
   for (int sg = 1; sg + 1 < P; ++sg) {
     if (sg + 2 < P) load(sg + 1, mN, bN);
     f32x4 acc[2];
@@ -1160,7 +1161,7 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mA[t][jj][i], sv[i], acc[t], 0, 0, 0);
       }
     }
-    __syncthreads();
+    lds_barrier();  // every wave has read St (the next segment's maps stay in flight)
     float* dst = ws.S + ws.at(bh, sg, P);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -1169,7 +1170,7 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[(size_t)(r0 + i) * HD + col0 + lr] = acc[t][i];
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       bA[t] = bN[t];

@@ -15,8 +15,10 @@
 // current one is used.  Per block and wave:
 //   S^T = K Q^T      bf16 MFMA 16x16x32; lane 16 g + r holds keys
 //                    16 tt + 4 g + i of query r, so each lane owns one query
-//   online softmax   base-2 exponent, running max / partial sum per lane,
-//                    merged over the 4 lane groups of a query by shuffles
+//   online softmax   base-2 exponent, running reference / partial sum per
+//                    lane, merged over the 4 lane groups of a query by
+//                    shuffles; the reference is raised (and O rescaled) only
+//                    when a block's max exceeds it by more than 2^8
 //   O^T += V^T P^T   f16 MFMA; P^T is the S^T accumulator pair of a 32-key
 //                    step as is (keys 4 g + i and 16 + 4 g + i in lane group
 //                    g), and the V^T operand gathers the same keys of one
@@ -37,6 +39,7 @@ constexpr int PK = 64;    // keys per block
 constexpr int PD = 128;   // head dim
 constexpr int PRS = 144;  // 16-bit row stride of the LDS tiles (288 bytes)
 constexpr int PNT = 512;  // threads per work-group
+constexpr float kLazy = 8.f;  // base-2 headroom before the softmax reference is raised
 
 struct __align__(16) SwaPSmem {
   bf16 K[2][PK * PRS];
@@ -153,26 +156,35 @@ __global__ __launch_bounds__(PNT, 2) void swa_sink_prefill_kernel(
         s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(kr + 32 * j),
                                                          qf[j], s[tt], 0, 0, 0);
     }
+    // Block max of the raw scores (the scale is positive, so it commutes
+    // with the max), then p = 2^(sm_log2 s - m) with one FMA per score.
     float mloc = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        float z = s[tt][ii] * sm_log2;
         if (!full) {
           const int key = k0 + 16 * tt + 4 * g + ii;
           const bool ok = key <= tq && (key < n_sink || key > tq - window);
-          z = ok ? z : -INFINITY;
+          s[tt][ii] = ok ? s[tt][ii] : -INFINITY;
         }
-        s[tt][ii] = z;
-        mloc = fmaxf(mloc, z);
+        mloc = fmaxf(mloc, s[tt][ii]);
       }
     mloc = fmaxf(mloc, xor_lanes<16>(mloc));
     mloc = fmaxf(mloc, xor_lanes<32>(mloc));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    const float mblk = mloc * sm_log2;
+    // Lazy reference: the running reference m_run is raised only when a
+    // block's max exceeds it by more than kLazy (so p <= 2^kLazy); numerator
+    // and denominator share the reference, so the result is unchanged.
+    if (__any(mblk > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mblk);
+      const float corr = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_part *= corr;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc_o[dt] *= corr;
+    }
+    const float m_neg = m_run == -INFINITY ? 0.f : -m_run;
     float psum = 0.f;
     h16x4 pf[4];
 #pragma unroll
@@ -180,14 +192,12 @@ __global__ __launch_bounds__(PNT, 2) void swa_sink_prefill_kernel(
       f32x4 p;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        p[ii] = __builtin_amdgcn_exp2f(s[tt][ii] - m_use);
+        p[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][ii], sm_log2, m_neg));
         psum += p[ii];
       }
       pf[tt] = cvt4(p);
     }
-    l_part = l_part * corr + psum;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc_o[dt] *= corr;
+    l_part += psum;
 
     // O^T += V^T P^T over two 32-key steps.
     const h16* vb = &sm.V[slot][(4 * g + (r >> 2)) * PRS + 4 * (r & 3)];

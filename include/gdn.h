@@ -190,7 +190,7 @@ int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
  *            result (out += y), rows below it are overwritten: pass T (or
  *            more) for a plain write, 0 to add to every row.
  * Limits: dtype GDN_BF16 and D = 128 (else GDN_ERR_UNSUPPORTED); n_sink >= 0;
- * window >= 1.  out must not overlap q, k or v.
+ * window >= 1; softmax_scale > 0 and finite.  out must not overlap q, k or v.
  */
 int gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out, int B,
                          int T, int H, int D, int n_sink, int window, float softmax_scale,
@@ -238,7 +238,7 @@ size_t gdn_hybrid_prefill_workspace_bytes(int B, int T, int H, int D, int n_sink
  *            aligned (NULL allowed when that is 0)
  * Enqueues the linear path (one chunked prefill over all sequences, reading
  * them as strided views), then the softmax path adding into out, then the
- * cache fill.  With a bf16 out, the
+ * cache fill.  softmax_scale > 0 and finite.  With a bf16 out, the
  * linear read-out is stored as bf16 first and the sum is rounded once more
  * (as in the decode pair gdn_decode_step + gdn_swa_sink_decode with
  * accumulate = 1); an f32 out rounds neither.  Limits: dtype

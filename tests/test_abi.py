@@ -167,6 +167,8 @@ def test_swa_prefill_validation():
     assert call(q=None) == INVALID and "q" in _err()
     assert call(q=A + 8) == INVALID and "aligned" in _err()
     assert call(T=0, q=None) == OK
+    assert L.gdn_swa_sink_prefill(A, A, A, A, 2, 64, 2, 128, 4, 8, -0.1, 64, BF16, BF16,
+                                  None) == INVALID and "softmax_scale" in _err()
 
 
 def test_swa_cache_fill_validation():
