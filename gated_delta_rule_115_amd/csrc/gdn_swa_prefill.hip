@@ -104,12 +104,14 @@ __global__ __launch_bounds__(PNT, 2) void swa_sink_prefill_kernel(
       qf[j] = *reinterpret_cast<const bf16x8*>(q + base + (size_t)tq * rs + 32 * j + 8 * g);
   }
 
-  // Staging: thread tid moves 16-byte pieces c = tid + 512 u of the block
+  // Staging: thread tid moves 16-byte pieces c = tid + PNT u of the block
   // (row c / 16, columns 8 (c % 16) ..), rows past T repeat row T - 1.
-  bf16x8 kst[2], vst[2];
+  constexpr int NST = PK * PD / 8 / PNT;  // pieces per thread and tensor
+  static_assert(NST * PNT * 8 == PK * PD, "the threads cover the block exactly");
+  bf16x8 kst[NST], vst[NST];
   auto fetch = [&](int kb) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NST; ++u) {
       const int c = tid + PNT * u;
       const int key = min(kb * PK + (c >> 4), T - 1);
       const size_t off = base + (size_t)key * rs + 8 * (c & 15);
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(PNT, 2) void swa_sink_prefill_kernel(
   };
   auto stage = [&](int slot) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NST; ++u) {
       const int c = tid + PNT * u;
       const int o = (c >> 4) * PRS + 8 * (c & 15);
       *reinterpret_cast<bf16x8*>(&sm.K[slot][o]) = kst[u];
