@@ -57,6 +57,7 @@ def _load():
         lib.gdn_oracle_recurrence_f64.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
         lib.gdn_oracle_recurrence_f32.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
         lib.gdn_oracle_swa_sink_f64.argtypes = [_dp] * 4 + [i] * 6 + [d, i]
+        lib.gdn_oracle_recurrence_chgate_f64.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
         lib.gdn_oracle_hybrid_f64.argtypes = [_dp] * 9 + [i] * 7 + [d, d]
         lib.gdn_oracle_short_conv_silu_f64.argtypes = [_dp] * 3 + [i] * 5 + [d]
         lib.gdn_oracle_short_conv_step_f64.argtypes = [_dp] * 5 + [i] * 4 + [d]
@@ -112,6 +113,35 @@ def decode_step(q, k, v, alpha, beta, state_in, scale=1.0):
     q, k, v = (_arr(x)[:, None] for x in (q, k, v))
     a, b = (_arr(x)[:, None] for x in (alpha, beta))
     out, s = gdn_recurrence(q, k, v, a, b, state_in, scale)
+    return out[:, 0], s
+
+
+def gdn_recurrence_chgate(q, k, v, alpha, beta, state_in=None, scale=1.0, gate_first=True):
+    """GDN with a channel-wise gate G_t = diag(alpha_t) (section 3.2's diag
+    gates in the section 3.1.2 update), alpha [B,T,H,Dk].  Returns (out, S_T).
+
+    gate_first=False applies the erase before the gate: a test hook that shows
+    the order matters once the gate is not a multiple of I.
+    """
+    q, k, v, alpha, beta = map(_arr, (q, k, v, alpha, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and alpha.shape == q.shape and beta.shape == (B, T, H)
+    s_in = None if state_in is None else _arr(state_in)
+    out = np.zeros((B, T, H, Dv))
+    s_out = np.zeros((B, H, Dk, Dv))
+    _load().gdn_oracle_recurrence_chgate_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(s_in), _ptr(s_out),
+        _ptr(out), B, T, H, Dk, Dv, float(scale), int(bool(gate_first)))
+    return out, s_out
+
+
+def decode_step_chgate(q, k, v, alpha, beta, state_in, scale=1.0):
+    """One channel-gated step per (b, h): q, k, alpha [B,H,Dk], v [B,H,Dv],
+    beta [B,H].  Returns (out [B,H,Dv], S')."""
+    q, k, v, a = (_arr(x)[:, None] for x in (q, k, v, alpha))
+    b = _arr(beta)[:, None]
+    out, s = gdn_recurrence_chgate(q, k, v, a, b, state_in, scale)
     return out[:, 0], s
 
 

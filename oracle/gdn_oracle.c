@@ -25,6 +25,8 @@
  *   - The gate G_t is a scalar alpha_t per (token, head): G_t = alpha_t I.
  *     The page applies G_t first and the erase (I - beta k k^T) second; with a
  *     scalar gate the two orders agree, and this code follows the page's order.
+ *     The channel-wise variant G_t = diag(alpha_t) (section 3.2's diag gates)
+ *     keeps that order, where it does matter.
  *   - Sliding window: the window is the w most recent tokens including the
  *     current one, the sinks are the first s tokens, and the linear state holds
  *     exactly the tokens that are in neither set.  Sets overlapping at short t
@@ -123,6 +125,66 @@ void gdn_oracle_recurrence_f32(const double* q, const double* k, const double* v
                                double* out, int B, int T, int H, int Dk, int Dv,
                                double scale, int erase)
 GDN_RECURRENCE_BODY(float)
+
+/* ------------------------------------------------------------------------- */
+/* GDN recurrence with a channel-wise gate G_t = diag(alpha_t), alpha_t in    */
+/* R^{Dk} per (token, head) (section 3.2: the gate as a product of            */
+/* diag(alpha_j); the section 3.1.2 update with a diagonal G_t).  S is        */
+/* key-major, so G_t scales the rows of S.  For every (b, h):                 */
+/*   gate_first = 1 (the page's order, G_t before the erase):                 */
+/*     S <- diag(alpha_t) S;  S <- S - beta_t k_t (k_t^T S);                  */
+/*   gate_first = 0 (test hook: the erase before the gate):                   */
+/*     S <- S - beta_t k_t (k_t^T S);  S <- diag(alpha_t) S;                  */
+/*   then S <- S + beta_t k_t v_t^T and o_t = scale * S^T q_t.                */
+/* alpha: [B, T, H, Dk]; the other layouts as above.                          */
+/* ------------------------------------------------------------------------- */
+void gdn_oracle_recurrence_chgate_f64(const double* q, const double* k, const double* v,
+                                      const double* alpha, const double* beta,
+                                      const double* state_in, double* state_out,
+                                      double* out, int B, int T, int H, int Dk, int Dv,
+                                      double scale, int gate_first) {
+  long BH = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    long b = bh / H, h = bh % H;
+    double* S = (double*)malloc(sizeof(double) * (size_t)Dk * Dv);
+    double* p = (double*)malloc(sizeof(double) * (size_t)Dv);
+    for (long e = 0; e < (long)Dk * Dv; ++e) S[e] = state_in ? state_in[bh * Dk * Dv + e] : 0.0;
+    for (long t = 0; t < T; ++t) {
+      long row = (b * T + t) * H + h;
+      const double* qt = q + row * Dk;
+      const double* kt = k + row * Dk;
+      const double* vt = v + row * Dv;
+      const double* at = alpha + row * Dk;
+      double be = beta[row];
+      for (int pass = 0; pass < 2; ++pass) {
+        if ((pass == 0) == (gate_first != 0)) {
+          for (long i = 0; i < Dk; ++i)
+            for (long j = 0; j < Dv; ++j) S[i * Dv + j] *= at[i];
+        } else {
+          for (long j = 0; j < Dv; ++j) {
+            double acc = 0;
+            for (long i = 0; i < Dk; ++i) acc += kt[i] * S[i * Dv + j];
+            p[j] = acc;
+          }
+          for (long i = 0; i < Dk; ++i)
+            for (long j = 0; j < Dv; ++j) S[i * Dv + j] -= be * kt[i] * p[j];
+        }
+      }
+      for (long i = 0; i < Dk; ++i)
+        for (long j = 0; j < Dv; ++j) S[i * Dv + j] += be * kt[i] * vt[j];
+      for (long j = 0; j < Dv; ++j) {
+        double acc = 0;
+        for (long i = 0; i < Dk; ++i) acc += S[i * Dv + j] * qt[i];
+        out[row * Dv + j] = scale * acc;
+      }
+    }
+    if (state_out)
+      for (long e = 0; e < (long)Dk * Dv; ++e) state_out[bh * Dk * Dv + e] = S[e];
+    free(S);
+    free(p);
+  }
+}
 
 /* ------------------------------------------------------------------------- */
 /* Membership of token i (0-based) in the exact-attention set of step t       */

@@ -399,3 +399,92 @@ def test_swa_last_only_matches_full():
     full = oracle.swa_sink_attention(q, k, v, 2, 3, 0.5)
     last = oracle.swa_sink_attention(q, k, v, 2, 3, 0.5, last_only=True)
     assert np.array_equal(last, full[:, -1])
+
+
+# --------------------------------------------------------------------------
+# Channel-wise gate G_t = diag(alpha_t) (section 3.2's diag gates in the
+# section 3.1.2 update; G_t applied before the erase, as the page orders it).
+# --------------------------------------------------------------------------
+def _rand_chgate(B, T, H, Dk, Dv, rng):
+    q, k, v, alpha, beta, S0 = _rand_gdn(B, T, H, Dk, Dv, rng)
+    a_ch = np.exp(-0.5 * rng.random((B, T, H, Dk)))  # per-channel gates in (0.6, 1]
+    return q, k, v, a_ch, beta, S0
+
+
+def test_chgate_equal_channels_is_the_scalar_gate():
+    """A gate that is the same on every channel is alpha_t I: the pinned
+    scalar-gate recurrence."""
+    B, T, H, Dk, Dv = 2, 9, 2, 6, 5
+    q, k, v, alpha, beta, S0 = _rand_gdn(B, T, H, Dk, Dv, RNG)
+    a_ch = np.repeat(alpha[..., None], Dk, axis=-1)
+    o1, s1 = oracle.gdn_recurrence_chgate(q, k, v, a_ch, beta, S0, scale=0.5)
+    o2, s2 = oracle.gdn_recurrence(q, k, v, alpha, beta, S0, scale=0.5)
+    np.testing.assert_allclose(o1, o2, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(s1, s2, atol=1e-13, rtol=0)
+
+
+def test_chgate_beta_zero_is_per_channel_decay():
+    """beta = 0: S_t = diag(prod_{j<=t} alpha_j) S0, so o_t = S0^T (g_t * q_t)."""
+    B, T, H, Dk, Dv = 1, 7, 2, 5, 3
+    q, k, v, a_ch, beta, S0 = _rand_chgate(B, T, H, Dk, Dv, RNG)
+    beta = np.zeros_like(beta)
+    out, ST = oracle.gdn_recurrence_chgate(q, k, v, a_ch, beta, S0)
+    g = np.cumprod(a_ch, axis=1)
+    for h in range(H):
+        for t in range(T):
+            np.testing.assert_allclose(out[0, t, h], S0[0, h].T @ (g[0, t, h] * q[0, t, h]),
+                                       atol=1e-12, rtol=0)
+        np.testing.assert_allclose(ST[0, h], g[0, T - 1, h][:, None] * S0[0, h],
+                                   atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("Dk,Dv", [(3, 2), (5, 4), (4, 4)])
+def test_chgate_brute_force_matrix_products(Dk, Dv):
+    """S_t = D_t ... D_1 S0 + sum_i D_t ... D_{i+1} beta_i k_i v_i^T with the
+    explicit D_j = (I - beta_j k_j k_j^T) diag(alpha_j), latest leftmost."""
+    B, T, H = 1, 8, 2
+    q, k, v, a_ch, beta, S0 = _rand_chgate(B, T, H, Dk, Dv, RNG)
+    out, ST = oracle.gdn_recurrence_chgate(q, k, v, a_ch, beta, S0, scale=0.75)
+    I = np.eye(Dk)
+    for h in range(H):
+        D = [(I - beta[0, j, h] * np.outer(k[0, j, h], k[0, j, h])) @ np.diag(a_ch[0, j, h])
+             for j in range(T)]
+
+        def prod(lo, hi):
+            M = np.eye(Dk)
+            for j in range(lo, hi + 1):
+                M = D[j] @ M
+            return M
+
+        for t in range(T):
+            S = prod(0, t) @ S0[0, h]
+            for i in range(t + 1):
+                S = S + prod(i + 1, t) @ (beta[0, i, h] * np.outer(k[0, i, h], v[0, i, h]))
+            np.testing.assert_allclose(out[0, t, h], 0.75 * (S.T @ q[0, t, h]),
+                                       atol=1e-12, rtol=0)
+        np.testing.assert_allclose(ST[0, h], S, atol=1e-12, rtol=0)
+
+
+def test_chgate_order_matters_and_scalar_gates_commute():
+    """With a diagonal gate, gate-then-erase and erase-then-gate differ; with
+    a scalar gate they agree (the reason the order is a reading only here)."""
+    B, T, H, Dk, Dv = 1, 6, 1, 4, 3
+    q, k, v, a_ch, beta, S0 = _rand_chgate(B, T, H, Dk, Dv, RNG)
+    o1, _ = oracle.gdn_recurrence_chgate(q, k, v, a_ch, beta, S0, gate_first=True)
+    o2, _ = oracle.gdn_recurrence_chgate(q, k, v, a_ch, beta, S0, gate_first=False)
+    assert np.max(np.abs(o1 - o2)) > 1e-3
+    a_eq = np.repeat(a_ch[..., :1], Dk, axis=-1)
+    o3, _ = oracle.gdn_recurrence_chgate(q, k, v, a_eq, beta, S0, gate_first=True)
+    o4, _ = oracle.gdn_recurrence_chgate(q, k, v, a_eq, beta, S0, gate_first=False)
+    np.testing.assert_allclose(o3, o4, atol=1e-13, rtol=0)
+
+
+def test_chgate_decode_steps_chain_to_recurrence():
+    B, T, H, Dk, Dv = 2, 5, 2, 4, 3
+    q, k, v, a_ch, beta, S0 = _rand_chgate(B, T, H, Dk, Dv, RNG)
+    out, ST = oracle.gdn_recurrence_chgate(q, k, v, a_ch, beta, S0)
+    S = S0
+    for t in range(T):
+        o, S = oracle.decode_step_chgate(q[:, t], k[:, t], v[:, t], a_ch[:, t], beta[:, t], S)
+        np.testing.assert_array_equal(o, out[:, t])
+    np.testing.assert_array_equal(S, ST)
