@@ -17,6 +17,9 @@ One step = one pass of the whole hot path over one batch of synthetic input:
                          outside sinks and window, read with q shifted by the
                          window; sink/window softmax added; decode caches and
                          final state written)
+  leg "chgate_llama8b":  GDN with a channel-wise gate diag(alpha_t), B=4, H=32,
+                         T=4096, d=128, bf16 in/out, f32 gates [B,T,H,128]:
+                         gdn_prefill_chunked_chgate (chunks of 32, f32)
   leg "conv_qwen32b":    Qwen-32B-shaped layer with projection adaptation:
                          gdn_short_conv_silu on q, k (with per-head L2 norm)
                          and v, then gdn_prefill_chunked; B=2, H=40, T=16384
@@ -50,6 +53,7 @@ import synthetic  # noqa: E402
 # MI355X published peaks (dense).
 PEAK_BF16_FLOPS = 2.5e15
 PEAK_HBM_BPS = 8.0e12
+PEAK_F32_VECTOR_FLOPS = 157.3e12  # 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
 
 # Algorithmic work per unit (fixed definitions; d = Dk = Dv, chunk C = 64):
 #   prefill flops per token-head: dense-tile count of the chunked form
@@ -70,6 +74,18 @@ def prefill_bytes(B, T, H, d, esize=2):
 # new k, v, reads q, and reads + writes the (bf16) output it adds into.
 def decode_gdn_bytes(d, esize=2):
     return 8 * d * d + esize * 3 * d + 8 + esize * d
+
+
+# Channel-gate prefill, chunks of C = 32, per token-head: gate-ratio Gram
+# blocks A and Pm (4 C dk), K S, Q S and the state update (6 dk dv), T Y and
+# Pm U (4 C dv): 131,072 flop at d = 128.
+def chgate_flops_per_token_head(dk, dv, C=32):
+    return 4 * C * dk + 6 * dk * dv + 4 * C * dv
+
+
+# bf16 q, k, v, out + f32 per-channel alpha and beta per token-head.
+def chgate_bytes(B, T, H, dk, dv, esize=2):
+    return B * T * H * (esize * (2 * dk + 2 * dv) + 4 * dk + 4) + B * H * dk * dv * 4
 
 
 def swa_set_sizes(T, n_sink, window):
@@ -150,7 +166,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill_long32k,decode_b256,hybrid_prefill,"
-                                      "conv_qwen32b,convstep_b256")
+                                      "chgate_llama8b,conv_qwen32b,convstep_b256")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) "
                          "and exit: the reference reading for HBM byte counters")
@@ -258,6 +274,26 @@ def make_hybrid_prefill_leg():
     info = dict(B=B, T=T, H=H, d=d, tokens=B * T, flops=lin_f + swa_f,
                 bytes=lin_b + swa_b + 2 * 2 * B * H * (s + w) * d * 2,
                 swa_flops=swa_f, swa_bytes=swa_b, swa_only=swa_only)
+    return run, info
+
+
+def make_chgate_leg():
+    c = synthetic.CONFIGS["chgate_llama8b"]
+    B, T, H, d = c["B"], c["T"], c["H"], c["Dk"]
+    x = synthetic.chgate_inputs(B, T, H, d, d, dtype="bf16", seed=c["seed"], device="cuda")
+    out = torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda")
+    st = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdn.gdn_prefill_chgate_workspace_bytes(B, T, H), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(mark):
+        gdn.gdn_prefill_chunked_chgate(x["q"], x["k"], x["v"], x["alpha"], x["beta"], None,
+                                       out=out, state_out=st, workspace=ws)
+        mark("chgate_prefill")
+
+    info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
+                alu_flops=chgate_flops_per_token_head(d, d) * B * T * H,
+                bytes=chgate_bytes(B, T, H, d, d))
     return run, info
 
 
@@ -383,6 +419,9 @@ def main():
     if "hybrid_prefill" in legs_wanted:
         run, info = make_hybrid_prefill_leg()
         legs["hybrid_prefill"], infos["hybrid_prefill"] = run, info
+    if "chgate_llama8b" in legs_wanted:
+        run, info = make_chgate_leg()
+        legs["chgate_llama8b"], infos["chgate_llama8b"] = run, info
     if "conv_qwen32b" in legs_wanted:
         run, info = make_conv_leg()
         legs["conv_qwen32b"], infos["conv_qwen32b"] = run, info
@@ -504,6 +543,18 @@ def main():
                              ms_per_launch=swa_pref_ms, flops_per_launch=inf["swa_flops"],
                              tflops=inf["swa_flops"] / sec / 1e12,
                              mfma_frac=inf["swa_flops"] / sec / PEAK_BF16_FLOPS)
+    roof_chgate = None
+    if "chgate_llama8b" in out_legs:
+        inf = infos["chgate_llama8b"]
+        ms = seg_ms[("chgate_llama8b", "chgate_prefill")]
+        sec = ms / 1e3
+        roof_chgate = dict(bound="alu", kernel="chgate_prep_kernel + chgate_recur_kernel (f32)",
+                           achieved=inf["alu_flops"] / sec / 1e12,
+                           peak=PEAK_F32_VECTOR_FLOPS / 1e12, unit="TFLOP/s",
+                           frac=inf["alu_flops"] / sec / PEAK_F32_VECTOR_FLOPS, traffic=None,
+                           ms_per_launch=ms, flops_per_launch=inf["alu_flops"],
+                           hbm_bytes_algorithmic=inf["bytes"],
+                           hbm_frac_algorithmic=inf["bytes"] / sec / PEAK_HBM_BPS)
     roof_conv = None
     if "conv_qwen32b" in out_legs:
         inf = infos["conv_qwen32b"]
@@ -543,7 +594,8 @@ def main():
         "config": {
             "workload": "long32k prefill (B1 H32 T32768 d128, chunk 64) + hybrid decode "
                         "(B256 H32 d128, 4 sinks + 512 window) + hybrid prefill (B4 H32 "
-                        "T4096 d128, 4 sinks + 512 window) + qwen32b conv+prefill "
+                        "T4096 d128, 4 sinks + 512 window) + channel-gate prefill (B4 H32 "
+                        "T4096 d128) + qwen32b conv+prefill "
                         "(B2 H40 T16384 d128) + decode-time conv step (B256, 3 x 5120 "
                         "channels, K 4)",
             "global_batch": 1, "seq_len": 32768, "parallelism": "single-gpu",
@@ -553,6 +605,7 @@ def main():
         "roofline": roofline,
         "roofline_decode": roof_dec,
         "roofline_swa_prefill": roof_swa_pref,
+        "roofline_chgate": roof_chgate,
         "roofline_conv": roof_conv,
         "roofline_conv_step": roof_convstep,
         "cpu_baseline": cpu,

@@ -26,7 +26,9 @@ __all__ = [
     "gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
     "gdn_decode_step", "gdn_short_conv_silu", "gdn_short_conv_step",
     "gdn_swa_sink_decode", "gdn_swa_sink_prefill", "gdn_swa_cache_fill",
-    "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill", "EXPORTED_SYMBOLS",
+    "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
+    "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
+    "EXPORTED_SYMBOLS",
 ]
 
 GDN_BF16 = 0
@@ -40,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "gdn_prefill_chunked", "gdn_decode_step", "gdn_short_conv_silu",
     "gdn_short_conv_step", "gdn_swa_sink_decode", "gdn_swa_sink_prefill",
     "gdn_swa_cache_fill", "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
+    "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +91,12 @@ def lib() -> ctypes.CDLL:
     L.gdn_hybrid_prefill_workspace_bytes.argtypes = [i] * 6
     L.gdn_hybrid_prefill.restype = i
     L.gdn_hybrid_prefill.argtypes = [vp] * 12 + [i] * 6 + [f, f, i, i, vp, sz, vp]
+    L.gdn_prefill_chgate_workspace_bytes.restype = sz
+    L.gdn_prefill_chgate_workspace_bytes.argtypes = [i] * 3
+    L.gdn_prefill_chunked_chgate.restype = i
+    L.gdn_prefill_chunked_chgate.argtypes = [vp] * 8 + [i] * 7 + [f, vp, sz, vp]
+    L.gdn_decode_step_chgate.restype = i
+    L.gdn_decode_step_chgate.argtypes = [vp] * 8 + [i] * 6 + [f, vp]
     _lib = L
     return L
 
@@ -356,4 +365,67 @@ def gdn_hybrid_prefill(q_lin, k_lin, v_lin, alpha, beta, q_swa, k_swa, v_swa, *,
         B, T, H, D, int(n_sink), int(window), float(lin_scale), float(softmax_scale),
         _dtype_code(q_lin), _dtype_code(out), _ptr(workspace), wbytes, _stream(stream))
     _check("gdn_hybrid_prefill", st)
+    return out, state_out
+
+
+def gdn_prefill_chgate_workspace_bytes(B, T, H) -> int:
+    return int(lib().gdn_prefill_chgate_workspace_bytes(B, T, H))
+
+
+def gdn_prefill_chunked_chgate(q, k, v, alpha, beta, state_in=None, *, scale=1.0, out=None,
+                               out_dtype=None, state_out=None, workspace=None, stream=None):
+    """Chunked GDN prefill with a channel-wise gate G_t = diag(alpha_t):
+    q, k, alpha [B,T,H,Dk] (alpha f32), v [B,T,H,Dv], beta [B,T,H] f32.
+    Returns (out [B,T,H,Dv], S_T [B,H,Dk,Dv])."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, q.shape)
+    _dev(v, "v", q.dtype, (B, T, H, Dv))
+    _dev(alpha, "alpha", torch.float32, (B, T, H, Dk))
+    _dev(beta, "beta", torch.float32, (B, T, H))
+    _dev(state_in, "state_in", torch.float32, (B, H, Dk, Dv))
+    odt = _out_dtype(q.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=odt, device=q.device)
+    _dev(out, "out", odt, (B, T, H, Dv))
+    if state_out is None:
+        state_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _dev(state_out, "state_out", torch.float32, (B, H, Dk, Dv))
+    need = gdn_prefill_chgate_workspace_bytes(B, T, H)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().gdn_prefill_chunked_chgate(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out),
+        _ptr(out), B, T, H, Dk, Dv, _dtype_code(q), _dtype_code(out), float(scale),
+        _ptr(workspace), wbytes, _stream(stream))
+    _check("gdn_prefill_chunked_chgate", st)
+    return out, state_out
+
+
+def gdn_decode_step_chgate(q, k, v, alpha, beta, state_in, *, state_out=None, out=None,
+                           out_dtype=None, scale=1.0, stream=None):
+    """One channel-gated step: q, k, alpha [B,H,Dk] (alpha f32), v [B,H,Dv],
+    beta [B,H]; state [B,H,Dk,Dv] (state_out may be state_in).  Returns (out, S')."""
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, q.shape)
+    _dev(v, "v", q.dtype, (B, H, Dv))
+    _dev(alpha, "alpha", torch.float32, (B, H, Dk))
+    _dev(beta, "beta", torch.float32, (B, H))
+    _dev(state_in, "state_in", torch.float32, (B, H, Dk, Dv))
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    _dev(state_out, "state_out", torch.float32, (B, H, Dk, Dv))
+    odt = _out_dtype(q.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=odt, device=q.device)
+    _dev(out, "out", odt, (B, H, Dv))
+    st = lib().gdn_decode_step_chgate(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out),
+        _ptr(out), B, H, Dk, Dv, _dtype_code(q), _dtype_code(out), float(scale),
+        _stream(stream))
+    _check("gdn_decode_step_chgate", st)
     return out, state_out

@@ -406,4 +406,73 @@ int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
   return ok();
 }
 
+size_t gdn_prefill_chgate_workspace_bytes(int B, int T, int H) {
+  if (B < 0 || T < 0 || H < 1) return 0;
+  return gdn::prefill_chgate_workspace_bytes(B, T, H);
+}
+
+int gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, const float* state_in,
+                               float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
+                               int dtype, int out_dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
+          H);
+  REQUIRE((Dk == 32 || Dk == 64 || Dk == 128) && (Dv == 32 || Dv == 64 || Dv == 128),
+          GDN_ERR_UNSUPPORTED, "channel-gate head dims Dk=%d Dv=%d not in {32,64,128}", Dk, Dv);
+  REQUIRE((long long)B * H * ((T + 31) / 32) < (1LL << 31), GDN_ERR_UNSUPPORTED,
+          "grid too large");
+  if ((long long)B * H == 0) return ok();
+  REQUIRE_ALIGNED_OR_NULL(state_in);
+  REQUIRE_ALIGNED_OR_NULL(state_out);
+  if (T > 0) {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    REQUIRE(alpha != nullptr && beta != nullptr, GDN_ERR_INVALID_ARG, "alpha/beta is NULL");
+    REQUIRE_PTR(alpha);  // read in 16-byte pieces
+    const size_t need = gdn::prefill_chgate_workspace_bytes(B, T, H);
+    REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
+    REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
+            "workspace is not 256-byte aligned");
+    REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG,
+            "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  }
+  gdn::PrefillArgs p;
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+  p.state_in = state_in; p.state_out = state_out; p.out = out;
+  p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = 32;
+  p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16;
+  p.scale = scale; p.workspace = workspace; p.stream = stream;
+  return hip_status(gdn::launch_prefill_chgate(p), "gdn_prefill_chunked_chgate launch");
+}
+
+int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* state_in, float* state_out,
+                           void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
+                           float scale, void* stream) {
+  REQUIRE_DTYPES(dtype, out_dtype);
+  REQUIRE(B >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d H=%d", B, H);
+  REQUIRE(is_head_dim(Dk) && is_head_dim(Dv), GDN_ERR_UNSUPPORTED,
+          "head dims Dk=%d Dv=%d not in {16,32,64,128}", Dk, Dv);
+  REQUIRE((long long)B * H < (1LL << 31), GDN_ERR_UNSUPPORTED, "grid too large");
+  if (B == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(state_in);
+  REQUIRE_PTR(state_out);
+  REQUIRE(alpha != nullptr && beta != nullptr, GDN_ERR_INVALID_ARG, "alpha/beta is NULL");
+  gdn::DecodeArgs p;
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+  p.state_in = state_in; p.state_out = state_out; p.out = out;
+  p.B = B; p.H = H; p.Dk = Dk; p.Dv = Dv;
+  p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16;
+  p.scale = scale; p.stream = stream; p.chgate = true;
+  return hip_status(gdn::launch_decode(p), "gdn_decode_step_chgate launch");
+}
+
 }  // extern "C"

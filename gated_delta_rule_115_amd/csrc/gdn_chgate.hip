@@ -1,0 +1,397 @@
+// GDN prefill with a channel-wise gate G_t = diag(alpha_t), gfx950.
+//
+// "The Key to Going Linear: Analysis-Driven Transformer Linearization",
+// section 3.1.2 (S_t = (I - beta_t k_t k_t^T) G_t S_{t-1} + beta_t k_t v_t^T,
+// o_t = scale * S_t^T q_t) with the diagonal gates of section 3.2
+// (prod_j diag(alpha_j)); G_t acts on the rows of the key-major state and is
+// applied before the erase, in the page's order.
+//
+// Chunked form (derived from the update; chunk of C tokens entering with S0;
+// Gam_r = sum_{j<=r} log alpha_j, a Dk-vector per token; ratios taken
+// per channel as exp(Gam_r[c] - Gam_i[c]) <= 1 for i <= r):
+//   one step is  S~ = diag(alpha_r) S_{r-1},  u_r = beta_r (v_r - S~^T k_r),
+//                S_r = S~ + k_r u_r^T;
+//   (I + A) U = diag(beta) (V - (K o e^Gam) S0),
+//     A_ri = beta_r sum_c k_r[c] k_i[c] exp(Gam_r[c] - Gam_i[c])   (i < r)
+//   O   = scale (Q o e^Gam) S0 + Pm U,
+//     Pm_ri = scale sum_c q_r[c] k_i[c] exp(Gam_r[c] - Gam_i[c])   (i <= r)
+//   S_C = diag(e^Gam_C) S0 + (K o e^(Gam_C - Gam))^T U
+// Every gate factor is at most 1, so no factor can overflow whatever the
+// gates are.  Kernel 1 (parallel over chunks) forms A, Pm and T = (I + A)^-1;
+// kernel 2 walks the chunks of one (b, h) and value slice with S in LDS.
+// All arithmetic is f32 (bf16 inputs are widened on load).  Ragged tails are
+// padded with identity tokens (alpha = 1, beta = 0, q = k = v = 0).
+#include "gdn_f16ops.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int GC = 32;    // tokens per chunk
+constexpr int GNT = 256;   // threads per work-group of the per-chunk kernel
+constexpr int GNTR = 1024; // threads per work-group of the recurrence (16 waves)
+constexpr int GDVS = 32;  // value columns per work-group of the recurrence
+
+// Per-chunk record: T (C x C), Pm (C x C), beta (C), all f32.
+constexpr size_t kRecFloats = 2 * GC * GC + GC;
+constexpr size_t kRecBytes = (kRecFloats * 4 + 255) / 256 * 256;
+
+// Eight consecutive elements as loaded (bf16: one 16-byte load; f32: two),
+// widened to f32 only when stored to LDS.
+template <class TIn>
+struct Raw8 {
+  bf16x8 v;
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+};
+template <class TIn>
+__device__ __forceinline__ Raw8<TIn> ld8(const TIn* p) {
+  Raw8<TIn> r;
+  if constexpr (sizeof(TIn) == 2) {
+    r.v = *reinterpret_cast<const bf16x8*>(p);
+  } else {
+    r.a = *reinterpret_cast<const f32x4*>(p);
+    r.b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  return r;
+}
+template <class TIn>
+__device__ __forceinline__ void st8(float* d, const Raw8<TIn>& r, bool keep) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x;
+    if constexpr (sizeof(TIn) == 2) x = (float)r.v[e];
+    else x = e < 4 ? r.a[e] : r.b[e - 4];
+    d[e] = keep ? x : 0.f;
+  }
+}
+
+// The streamed inputs of one chunk for one thread: 8-element pieces of K
+// and Q (row p / (DK / 8)), 4-float pieces of alpha, 8-element pieces of the
+// value slice and 4-float pieces of the chunk record.
+template <class TIn, int DK, int NT>
+struct ChunkRegs {
+  static constexpr int NKQ = (GC * DK / 8 + NT - 1) / NT;
+  static constexpr int NA = (GC * DK / 4 + NT - 1) / NT;
+  static constexpr int NR = (int)((kRecFloats / 4 + NT - 1) / NT);
+  Raw8<TIn> k[NKQ], q[NKQ], v;
+  f32x4 a[NA], rec[NR];
+};
+
+// Kernel 1: one work-group per (b, h, chunk).
+template <class TIn, int DK>
+__global__ __launch_bounds__(GNT) void chgate_prep_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
+    const float* __restrict__ beta, int T, int H, int NC, float scale, char* __restrict__ ws) {
+  __shared__ float Ks[GC][DK + 1], Qs[GC][DK + 1], Gs[GC][DK + 1];
+  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], bet[GC];
+  const int id = blockIdx.x;
+  const int c = id % NC, bh = id / NC, b = bh / H, h = bh % H;
+  const int tid = threadIdx.x;
+  const int t0 = c * GC;
+
+  // All loads of the chunk are issued before any is stored to LDS.
+  typedef ChunkRegs<TIn, DK, GNT> R;
+  Raw8<TIn> kr[R::NKQ], qr[R::NKQ];
+  f32x4 ar[R::NA];
+  const size_t tok = (size_t)H * DK;
+#pragma unroll
+  for (int u = 0; u < R::NKQ; ++u) {
+    const int pc = tid + GNT * u;
+    const int r = min(pc / (DK / 8), GC - 1), t = min(t0 + r, T - 1);
+    const size_t off = ((size_t)b * T + t) * tok + (size_t)h * DK + 8 * (pc % (DK / 8));
+    kr[u] = ld8(k + off);
+    qr[u] = ld8(q + off);
+  }
+#pragma unroll
+  for (int u = 0; u < R::NA; ++u) {
+    const int pc = tid + GNT * u;
+    const int r = min(pc / (DK / 4), GC - 1), t = min(t0 + r, T - 1);
+    ar[u] = *reinterpret_cast<const f32x4*>(alpha + ((size_t)b * T + t) * tok + (size_t)h * DK +
+                                            4 * (pc % (DK / 4)));
+  }
+#pragma unroll
+  for (int u = 0; u < R::NKQ; ++u) {
+    const int pc = tid + GNT * u;
+    if (pc < GC * DK / 8) {
+      const int r = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
+      st8(&Ks[r][c8], kr[u], t0 + r < T);
+      st8(&Qs[r][c8], qr[u], t0 + r < T);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < R::NA; ++u) {
+    const int pc = tid + GNT * u;
+    if (pc < GC * DK / 4) {
+      const int r = pc / (DK / 4), c4 = 4 * (pc % (DK / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = t0 + r < T ? logf(ar[u][e]) : 0.f;
+    }
+  }
+  if (tid < GC) {
+    const int t = t0 + tid;
+    bet[tid] = t < T ? beta[((size_t)b * T + t) * H + h] : 0.f;
+  }
+  __syncthreads();
+  // Cumulative log gate per channel.
+  if (tid < DK) {
+    float acc = 0.f;
+    for (int r = 0; r < GC; ++r) {
+      acc += Gs[r][tid];
+      Gs[r][tid] = acc;
+    }
+  }
+  __syncthreads();
+
+  float* rec = reinterpret_cast<float*>(ws + (size_t)id * kRecBytes);
+  float* Tg = rec;
+  float* Pg = rec + GC * GC;
+  float* Bg = rec + 2 * GC * GC;
+  // Gram blocks with exact per-channel gate ratios: pairs (r, i), i <= r.
+  for (int pr = tid; pr < GC * GC; pr += GNT) {
+    const int r = pr / GC, i = pr % GC;
+    float a = 0.f, p = 0.f;
+    if (i <= r) {
+      for (int ch = 0; ch < DK; ++ch) {
+        const float e = __expf(Gs[r][ch] - Gs[i][ch]);
+        const float ki = Ks[i][ch] * e;
+        a += Ks[r][ch] * ki;
+        p += Qs[r][ch] * ki;
+      }
+    }
+    As[r][i] = (i < r) ? bet[r] * a : 0.f;
+    Pg[r * GC + i] = (i <= r) ? scale * p : 0.f;
+  }
+  __syncthreads();
+  // T = (I + A)^-1 (unit lower triangular): lane j owns column j and runs the
+  // forward substitution T[r][j] = [r == j] - sum_{j <= m < r} A[r][m] T[m][j].
+  if (tid < GC) {
+    const int j = tid;
+    for (int r = 0; r < GC; ++r) {
+      float x = (r == j) ? 1.f : 0.f;
+      for (int m = j; m < r; ++m) x -= As[r][m] * Ts[m][j];
+      Ts[r][j] = (r < j) ? 0.f : x;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < GC * GC; e += GNT) Tg[e] = Ts[e / GC][e % GC];
+  if (tid < GC) Bg[tid] = bet[tid];
+}
+
+// Kernel 2: one work-group per (b, h, value slice of GDVS columns).
+template <class TIn, class TOut, int DK>
+__global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ alpha, const float* state_in, float* state_out,
+    TOut* __restrict__ out, int T, int H, int Dv, int NC, float scale,
+    const char* __restrict__ ws) {
+  __shared__ float Kd[GC][DK + 1];   // K o e^(Gam_C - Gam)
+  __shared__ float Kg[GC][DK + 1];   // K o e^Gam
+  __shared__ float Qg[GC][DK + 1];   // Q o e^Gam
+  __shared__ float Gs[GC][DK + 1];   // cumulative log gates
+  __shared__ float S[DK][GDVS + 1];  // state slice
+  __shared__ float Vs[GC][GDVS + 1], Us[GC][GDVS + 1];
+  __shared__ float Tm[GC][GC + 1], Pm[GC][GC + 1], bet[GC], gC[DK];
+  const int ns = Dv / GDVS;
+  const int bh = blockIdx.x / ns, sl = blockIdx.x % ns, b = bh / H, h = bh % H;
+  const int col0 = sl * GDVS;
+  const int tid = threadIdx.x;
+
+  for (int e = tid; e < DK * GDVS; e += GNTR) {
+    const int r = e / GDVS, j = e % GDVS;
+    S[r][j] = state_in ? state_in[((size_t)bh * DK + r) * Dv + col0 + j] : 0.f;
+  }
+
+  // Loads of chunk c + 1 are issued before chunk c is computed, into
+  // registers, and moved to LDS at the top of the next iteration; barriers
+  // inside the loop order LDS only, so those loads stay in flight.
+  typedef ChunkRegs<TIn, DK, GNTR> R;
+  R rg;
+  const size_t tok = (size_t)H * DK;  // elements between tokens (q, k, alpha)
+  auto fetch = [&](int c) {
+    const int t0 = c * GC;
+#pragma unroll
+    for (int u = 0; u < R::NKQ; ++u) {
+      const int pc = tid + GNTR * u;
+      const int r = min(pc / (DK / 8), GC - 1), t = min(t0 + r, T - 1);
+      const size_t off = ((size_t)b * T + t) * tok + (size_t)h * DK + 8 * (pc % (DK / 8));
+      rg.k[u] = ld8(k + off);
+      rg.q[u] = ld8(q + off);
+    }
+#pragma unroll
+    for (int u = 0; u < R::NA; ++u) {
+      const int pc = tid + GNTR * u;
+      const int r = min(pc / (DK / 4), GC - 1), t = min(t0 + r, T - 1);
+      rg.a[u] = *reinterpret_cast<const f32x4*>(alpha + ((size_t)b * T + t) * tok +
+                                                (size_t)h * DK + 4 * (pc % (DK / 4)));
+    }
+    {
+      const int r = min(tid / (GDVS / 8), GC - 1), t = min(t0 + r, T - 1);
+      rg.v = ld8(v + (((size_t)b * T + t) * H + h) * Dv + col0 + 8 * (tid % (GDVS / 8)));
+    }
+    const float* rec = reinterpret_cast<const float*>(ws + ((size_t)bh * NC + c) * kRecBytes);
+#pragma unroll
+    for (int u = 0; u < R::NR; ++u) {
+      const int pc = min(tid + GNTR * u, (int)(kRecFloats / 4) - 1);
+      rg.rec[u] = *reinterpret_cast<const f32x4*>(rec + 4 * pc);
+    }
+  };
+  auto stash = [&](int c) {
+    const int t0 = c * GC;
+#pragma unroll
+    for (int u = 0; u < R::NKQ; ++u) {
+      const int pc = tid + GNTR * u;
+      if (pc < GC * DK / 8) {
+        const int r = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
+        const bool in = t0 + r < T;
+        st8(&Kd[r][c8], rg.k[u], in);
+        st8(&Qg[r][c8], rg.q[u], in);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < R::NA; ++u) {
+      const int pc = tid + GNTR * u;
+      if (pc < GC * DK / 4) {
+        const int r = pc / (DK / 4), c4 = 4 * (pc % (DK / 4));
+        const bool in = t0 + r < T;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = in ? logf(rg.a[u][e]) : 0.f;
+      }
+    }
+    if (tid < GC * GDVS / 8) {
+      const int r = tid / (GDVS / 8), c8 = 8 * (tid % (GDVS / 8));
+      st8(&Vs[r][c8], rg.v, t0 + r < T);
+    }
+#pragma unroll
+    for (int u = 0; u < R::NR; ++u) {
+      const int pc = tid + GNTR * u;
+      if (pc < (int)(kRecFloats / 4)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * pc + e;
+          if (i < GC * GC) Tm[i / GC][i % GC] = rg.rec[u][e];
+          else if (i < 2 * GC * GC) Pm[(i - GC * GC) / GC][(i - GC * GC) % GC] = rg.rec[u][e];
+          else bet[i - 2 * GC * GC] = rg.rec[u][e];
+        }
+      }
+    }
+  };
+
+  if (NC > 0) fetch(0);
+  for (int c = 0; c < NC; ++c) {
+    const int t0 = c * GC;
+    f16ops::lds_barrier();  // the previous chunk is done with every buffer
+    stash(c);
+    if (c + 1 < NC) fetch(c + 1);
+    f16ops::lds_barrier();
+    if (tid < DK) {
+      float acc = 0.f;
+      for (int r = 0; r < GC; ++r) {
+        acc += Gs[r][tid];
+        Gs[r][tid] = acc;
+      }
+      gC[tid] = __expf(acc);
+    }
+    f16ops::lds_barrier();
+    for (int e = tid; e < GC * DK; e += GNTR) {
+      const int r = e / DK, ch = e % DK;
+      const float g = Gs[r][ch], kk = Kd[r][ch];
+      Kg[r][ch] = kk * __expf(g);
+      Qg[r][ch] *= __expf(g);
+      Kd[r][ch] = kk * __expf(Gs[GC - 1][ch] - g);
+    }
+    f16ops::lds_barrier();
+    // Y = diag(beta) (V - Kg S), then U = T Y (Y staged in Us, U in Vs).
+    for (int e = tid; e < GC * GDVS; e += GNTR) {
+      const int r = e / GDVS, j = e % GDVS;
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int ch = 0; ch < DK; ch += 4)
+#pragma unroll
+        for (int z = 0; z < 4; ++z) x[z] += Kg[r][ch + z] * S[ch + z][j];
+      Us[r][j] = bet[r] * (Vs[r][j] - ((x[0] + x[1]) + (x[2] + x[3])));
+    }
+    f16ops::lds_barrier();
+    for (int e = tid; e < GC * GDVS; e += GNTR) {
+      const int r = e / GDVS, j = e % GDVS;
+      float u = 0.f;
+      for (int m = 0; m <= r; ++m) u += Tm[r][m] * Us[m][j];
+      Vs[r][j] = u;
+    }
+    f16ops::lds_barrier();
+    // O = scale Qg S + Pm U, from the state entering the chunk.
+    for (int e = tid; e < GC * GDVS; e += GNTR) {
+      const int r = e / GDVS, j = e % GDVS, t = t0 + r;
+      float o[4] = {0.f, 0.f, 0.f, 0.f}, pu = 0.f;
+#pragma unroll 8
+      for (int ch = 0; ch < DK; ch += 4)
+#pragma unroll
+        for (int z = 0; z < 4; ++z) o[z] += Qg[r][ch + z] * S[ch + z][j];
+      for (int m = 0; m <= r; ++m) pu += Pm[r][m] * Vs[m][j];
+      if (t < T)
+        out[(((size_t)b * T + t) * H + h) * Dv + col0 + j] =
+            from_f32<TOut>(scale * ((o[0] + o[1]) + (o[2] + o[3])) + pu);
+    }
+    f16ops::lds_barrier();
+    // S = diag(e^Gam_C) S + Kd^T U.
+    for (int e = tid; e < DK * GDVS; e += GNTR) {
+      const int ch = e / GDVS, j = e % GDVS;
+      float sp[4] = {gC[ch] * S[ch][j], 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < GC; r += 4)
+#pragma unroll
+        for (int z = 0; z < 4; ++z) sp[z] += Kd[r + z][ch] * Vs[r + z][j];
+      S[ch][j] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    }
+  }
+  __syncthreads();
+  if (state_out)
+    for (int e = tid; e < DK * GDVS; e += GNTR) {
+      const int r = e / GDVS, j = e % GDVS;
+      state_out[((size_t)bh * DK + r) * Dv + col0 + j] = S[r][j];
+    }
+}
+
+template <class TIn, class TOut, int DK>
+hipError_t launch_chgate_t(const PrefillArgs& p) {
+  const int NC = (p.T + GC - 1) / GC;
+  const hipStream_t st = (hipStream_t)p.stream;
+  if (NC > 0) {
+    hipLaunchKernelGGL((chgate_prep_kernel<TIn, DK>), dim3(p.B * p.H * NC), dim3(GNT), 0, st,
+                       (const TIn*)p.q, (const TIn*)p.k, p.alpha, p.beta, p.T, p.H, NC, p.scale,
+                       (char*)p.workspace);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK>), dim3(p.B * p.H * (p.Dv / GDVS)),
+                     dim3(GNTR), 0, st, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v, p.alpha,
+                     p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC, p.scale,
+                     (const char*)p.workspace);
+  return hipGetLastError();
+}
+
+template <class TIn, class TOut>
+hipError_t launch_chgate_dk(const PrefillArgs& p) {
+  switch (p.Dk) {
+    case 32: return launch_chgate_t<TIn, TOut, 32>(p);
+    case 64: return launch_chgate_t<TIn, TOut, 64>(p);
+    case 128: return launch_chgate_t<TIn, TOut, 128>(p);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t prefill_chgate_workspace_bytes(int B, int T, int H) {
+  return (size_t)B * H * ((T + GC - 1) / GC) * kRecBytes;
+}
+
+hipError_t launch_prefill_chgate(const PrefillArgs& p) {
+  if (p.B * p.H == 0) return hipSuccess;
+  if (!p.bf16) return launch_chgate_dk<float, float>(p);
+  return p.out_bf16 ? launch_chgate_dk<bf16, bf16>(p) : launch_chgate_dk<bf16, float>(p);
+}
+
+}  // namespace gdn

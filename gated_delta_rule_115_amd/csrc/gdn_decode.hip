@@ -24,7 +24,10 @@
 
 namespace gdn {
 
-template <class TIn, class TOut, int DK, int DV>
+// CH = true: channel-wise gate, alpha is [B, H, DK] and row r of S is scaled
+// by alpha[r] before the step (G_t = diag(alpha_t) applied first, as in the
+// page's update); the step then runs with a = 1.
+template <class TIn, class TOut, int DK, int DV, bool CH>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
@@ -62,8 +65,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     qs[i] = to_f32(q[(size_t)bh * DK + i]);
   }
   for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
-  const float a = alpha[bh];
+  const float a = CH ? 1.f : alpha[bh];
   const float b = beta[bh];
+  if constexpr (CH) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + i * RG;
+      if (r < DK) s[i] *= alpha[(size_t)bh * DK + r];
+    }
+  }
   __syncthreads();
 
   // Partial S^T k and S^T q over this thread's rows; k.q from column group 0.
@@ -119,10 +129,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
 template <class TIn, class TOut, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& p) {
-  hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV>), dim3(p.B * p.H), dim3(256),
-                     0, (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k,
-                     (const TIn*)p.v, p.alpha, p.beta, p.state_in, p.state_out,
-                     (TOut*)p.out, p.scale);
+  if (p.chgate)
+    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, true>), dim3(p.B * p.H), dim3(256),
+                       0, (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k,
+                       (const TIn*)p.v, p.alpha, p.beta, p.state_in, p.state_out,
+                       (TOut*)p.out, p.scale);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, false>), dim3(p.B * p.H), dim3(256),
+                       0, (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k,
+                       (const TIn*)p.v, p.alpha, p.beta, p.state_in, p.state_out,
+                       (TOut*)p.out, p.scale);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ struct DecodeArgs {
   bool bf16, out_bf16;
   float scale;
   void* stream;
+  bool chgate = false;  // alpha is [B, H, Dk]: channel-wise gate
 };
 
 struct PrefillArgs {
@@ -84,6 +85,11 @@ hipError_t launch_conv(const ConvArgs& p);
 // One decode step (T unused): state [B][K-1][Ch] of the input dtype, in place.
 hipError_t launch_conv_step(const ConvArgs& p, void* state);
 hipError_t launch_swa(const SwaArgs& p);
+
+// Channel-wise gate prefill (alpha [B, T, H, Dk]); chunks of 32 tokens,
+// f32 arithmetic; Dk in {32, 64, 128}, Dv a multiple of 32.
+size_t prefill_chgate_workspace_bytes(int B, int T, int H);
+hipError_t launch_prefill_chgate(const PrefillArgs& p);
 
 // Sink + window softmax over a whole sequence: bf16 q, k, v [B, T, H, 128];
 // rows t >= acc_from add into out, rows below are written.

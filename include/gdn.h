@@ -252,6 +252,33 @@ int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
                        int window, float lin_scale, float softmax_scale, int dtype,
                        int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Channel-wise gate (section 3.2's diagonal gates prod_j diag(alpha_j) in
+ * the section 3.1.2 update): G_t = diag(alpha_t) with alpha_t in R^{Dk} per
+ * (token, head), applied to the rows of the key-major state BEFORE the erase,
+ * in the page's order (for a diagonal gate the order matters):
+ *   S_t = (I - beta_t k_t k_t^T) diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *   out_t = scale * S_t^T q_t.
+ * gdn_prefill_chunked_chgate: the same call as gdn_prefill_chunked with
+ *   alpha [B, T, H, Dk] f32 (every entry in (0, 1]; the prefill works with
+ *   log alpha; 16-byte aligned), chunks of 32 tokens, f32 arithmetic
+ *   throughout (bf16 inputs are widened).  workspace: gdn_prefill_chgate_workspace_bytes(B, T, H)
+ *   bytes, 256-byte aligned.  state_out may alias state_in.  Limits: Dk and
+ *   Dv in {32, 64, 128}.
+ * gdn_decode_step_chgate: the same call as gdn_decode_step with alpha
+ *   [B, H, Dk] f32.  Limits as gdn_decode_step.
+ */
+size_t gdn_prefill_chgate_workspace_bytes(int B, int T, int H);
+int gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, const float* state_in,
+                               float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
+                               int dtype, int out_dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* state_in, float* state_out,
+                           void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
+                           float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

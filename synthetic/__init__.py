@@ -38,6 +38,8 @@ CONFIGS = {
                           n_sink=4, window=512, context=4096, seed=5),
     "hybrid_prefill": dict(B=4, H=32, T=4096, Dk=128, Dv=128, dtype="bf16",
                            n_sink=4, window=512, seed=6),
+    "chgate_llama8b": dict(B=4, H=32, T=4096, Dk=128, Dv=128, dtype="bf16", chunk=32,
+                           state0="zero", seed=7),
 }
 
 TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -76,6 +78,18 @@ def gdn_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, state0="zero",
     return dict(q=q.to(dt).contiguous(), k=k.to(dt).contiguous(),
                 v=v.to(dt).contiguous(), alpha=alpha.contiguous(),
                 beta=beta.contiguous(), state0=s0)
+
+
+def chgate_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, state0="zero", gate_scale=0.1,
+                  device="cpu"):
+    """gdn_inputs with a channel-wise gate: alpha [B,T,H,Dk] f32, each entry
+    exp(-gate_scale * softplus(N(0,1))) (the scalar gate's distribution per
+    channel)."""
+    x = gdn_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=seed, state0=state0, device=device)
+    g = _gen(seed + 7919, device)
+    x["alpha"] = torch.exp(-torch.nn.functional.softplus(_randn((B, T, H, Dk), g, device))
+                           * gate_scale).contiguous()
+    return x
 
 
 def conv_inputs(B, T, Ch, K=4, dtype="bf16", seed=0, device="cpu"):

@@ -210,6 +210,38 @@ def test_hybrid_prefill_validation():
     assert call(B=0, ql=None, qs=None, out=None) == OK
 
 
+def test_chgate_validation():
+    L = gdn.lib()
+    ws = L.gdn_prefill_chgate_workspace_bytes(2, 100, 3)
+    assert ws > 0 and ws % 256 == 0
+    assert L.gdn_prefill_chgate_workspace_bytes(2, 0, 3) == 0
+
+    def pre(**kw):
+        a = dict(q=A, al=A, B=2, T=100, H=3, Dk=128, Dv=128, ws=A, wsb=ws, dt=BF16, odt=BF16)
+        a.update(kw)
+        return L.gdn_prefill_chunked_chgate(a["q"], A, A, a["al"], A, None, None, A, a["B"],
+                                            a["T"], a["H"], a["Dk"], a["Dv"], a["dt"], a["odt"],
+                                            1.0, a["ws"], a["wsb"], None)
+    assert pre(Dk=16) == UNSUPPORTED
+    assert pre(Dv=48) == UNSUPPORTED
+    assert pre(wsb=ws - 256) == INVALID and "workspace too small" in _err()
+    assert pre(ws=None) == INVALID
+    assert pre(al=None) == INVALID
+    assert pre(q=None) == INVALID
+    assert pre(dt=F32, odt=BF16) == UNSUPPORTED
+    assert pre(B=0, q=None) == OK
+
+    def dec(**kw):
+        a = dict(q=A, al=A, B=2, Dk=128)
+        a.update(kw)
+        return L.gdn_decode_step_chgate(a["q"], A, A, a["al"], A, A, A, A, a["B"], 3, a["Dk"],
+                                        128, BF16, BF16, 1.0, None)
+    assert dec(Dk=100) == UNSUPPORTED
+    assert dec(al=None) == INVALID
+    assert dec(q=None) == INVALID
+    assert dec(B=0, q=None) == OK
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "_lib", None)
     monkeypatch.setattr(gdn, "library_path", str(tmp_path / "absent.so"))
