@@ -18,8 +18,9 @@
 //   S_C = diag(e^Gam_C) S0 + (K o e^(Gam_C - Gam))^T U
 // Every gate factor is at most 1, so no factor can overflow whatever the
 // gates are.  Kernel 1 (parallel over chunks) forms A, Pm and T = (I + A)^-1;
-// kernel 2 walks the chunks of one (b, h) and value slice with S in LDS.
-// All arithmetic is f32 (bf16 inputs are widened on load).  Ragged tails are
+// kernel 2 walks the chunks of one (b, h) and value slice with S in LDS and
+// forms K S, Q S, T Y, Pm U and K^T U on f32 MFMA tiles.  All arithmetic is
+// f32 (bf16 inputs are widened on load).  Ragged tails are
 // padded with identity tokens (alpha = 1, beta = 0, q = k = v = 0).
 #include "gdn_f16ops.h"
 #include "gdn_internal.h"
@@ -303,47 +304,76 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       Kd[r][ch] = kk * __expf(Gs[GC - 1][ch] - g);
     }
     f16ops::lds_barrier();
-    // Y = diag(beta) (V - Kg S), then U = T Y (Y staged in Us, U in Vs).
-    for (int e = tid; e < GC * GDVS; e += GNTR) {
-      const int r = e / GDVS, j = e % GDVS;
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int ch = 0; ch < DK; ch += 4)
+    // The products on f32 MFMA tiles (v_mfma_f32_16x16x4_f32): lane l = 16 g
+    // + r supplies row / column r and contraction index 4 k + g of step k, and
+    // holds rows 4 g + i of column r of the 16 x 16 result.
+    const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    auto mfma = [](float a, float b, f32x4 c) {
+      return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    };
+    // Phase A: waves 0-3 form X = Kg S for one 16 x 16 tile each and keep
+    // Y = diag(beta) (V - X) in LDS; waves 4-7 form Qg S (kept for O).
+    f32x4 qs = zero4();
+    if (w < 8) {
+      const int tr = (w & 3) >> 1, tc = w & 1;
+      const float(*A)[DK + 1] = w < 4 ? Kg : Qg;
+      f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll 4
+      for (int kk = 0; kk < DK; kk += 8) {
+        acc0 = mfma(A[16 * tr + lr][kk + lg], S[kk + lg][16 * tc + lr], acc0);
+        acc1 = mfma(A[16 * tr + lr][kk + 4 + lg], S[kk + 4 + lg][16 * tc + lr], acc1);
+      }
+      const f32x4 acc = acc0 + acc1;
+      if (w < 4) {
 #pragma unroll
-        for (int z = 0; z < 4; ++z) x[z] += Kg[r][ch + z] * S[ch + z][j];
-      Us[r][j] = bet[r] * (Vs[r][j] - ((x[0] + x[1]) + (x[2] + x[3])));
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * tr + 4 * lg + i, j = 16 * tc + lr;
+          Us[r][j] = bet[r] * (Vs[r][j] - acc[i]);
+        }
+      } else {
+        qs = acc;
+      }
     }
     f16ops::lds_barrier();
-    for (int e = tid; e < GC * GDVS; e += GNTR) {
-      const int r = e / GDVS, j = e % GDVS;
-      float u = 0.f;
-      for (int m = 0; m <= r; ++m) u += Tm[r][m] * Us[m][j];
-      Vs[r][j] = u;
+    // Phase B: U = T Y (waves 0-3), into Vs (V is no longer needed).
+    if (w < 4) {
+      const int tr = w >> 1, tc = w & 1;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < GC; kk += 4)
+        acc = mfma(Tm[16 * tr + lr][kk + lg], Us[kk + lg][16 * tc + lr], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Vs[16 * tr + 4 * lg + i][16 * tc + lr] = acc[i];
     }
     f16ops::lds_barrier();
-    // O = scale Qg S + Pm U, from the state entering the chunk.
-    for (int e = tid; e < GC * GDVS; e += GNTR) {
-      const int r = e / GDVS, j = e % GDVS, t = t0 + r;
-      float o[4] = {0.f, 0.f, 0.f, 0.f}, pu = 0.f;
-#pragma unroll 8
-      for (int ch = 0; ch < DK; ch += 4)
+    // Phase C: O = scale Qg S + Pm U (waves 4-7) and the state update
+    // S = diag(e^Gam_C) S + Kd^T U, one 16 x 16 tile of S per wave.
+    if (w >= 4 && w < 8) {
+      const int tr = (w & 3) >> 1, tc = w & 1;
+      f32x4 acc = qs * scale;
 #pragma unroll
-        for (int z = 0; z < 4; ++z) o[z] += Qg[r][ch + z] * S[ch + z][j];
-      for (int m = 0; m <= r; ++m) pu += Pm[r][m] * Vs[m][j];
-      if (t < T)
-        out[(((size_t)b * T + t) * H + h) * Dv + col0 + j] =
-            from_f32<TOut>(scale * ((o[0] + o[1]) + (o[2] + o[3])) + pu);
+      for (int kk = 0; kk < GC; kk += 4)
+        acc = mfma(Pm[16 * tr + lr][kk + lg], Vs[kk + lg][16 * tc + lr], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * tr + 4 * lg + i;
+        if (t < T)
+          out[(((size_t)b * T + t) * H + h) * Dv + col0 + 16 * tc + lr] = from_f32<TOut>(acc[i]);
+      }
     }
-    f16ops::lds_barrier();
-    // S = diag(e^Gam_C) S + Kd^T U.
-    for (int e = tid; e < DK * GDVS; e += GNTR) {
-      const int ch = e / GDVS, j = e % GDVS;
-      float sp[4] = {gC[ch] * S[ch][j], 0.f, 0.f, 0.f};
+    if (w < DK / 8) {  // DK / 16 row tiles x 2 column tiles
+      const int sr = w >> 1, sc = w & 1;
+      f32x4 acc;
 #pragma unroll
-      for (int r = 0; r < GC; r += 4)
+      for (int i = 0; i < 4; ++i) {
+        const int ch = 16 * sr + 4 * lg + i;
+        acc[i] = gC[ch] * S[ch][16 * sc + lr];
+      }
 #pragma unroll
-        for (int z = 0; z < 4; ++z) sp[z] += Kd[r + z][ch] * Vs[r + z][j];
-      S[ch][j] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+      for (int kk = 0; kk < GC; kk += 4)
+        acc = mfma(Kd[kk + lg][16 * sr + lr], Vs[kk + lg][16 * sc + lr], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[16 * sr + 4 * lg + i][16 * sc + lr] = acc[i];
     }
   }
   __syncthreads();
