@@ -32,6 +32,9 @@ constexpr int GC = 32;    // tokens per chunk
 constexpr int GNT = 256;   // threads per work-group of the per-chunk kernel
 constexpr int GNTR = 1024; // threads per work-group of the recurrence (16 waves)
 constexpr int GDVS = 32;  // value columns per work-group of the recurrence
+// Largest per-channel log-gate range of a chunk for which the Gram blocks are
+// formed from midpoint-referenced factors (each at most e^(range / 2)).
+constexpr float kFactorRange = 80.f;
 
 // Per-chunk record: T (C x C), Pm (C x C), beta (C), all f32.
 constexpr size_t kRecFloats = 2 * GC * GC + GC;
@@ -86,8 +89,8 @@ template <class TIn, int DK>
 __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, int T, int H, int NC, float scale, char* __restrict__ ws) {
-  __shared__ float Ks[GC][DK + 1], Qs[GC][DK + 1], Gs[GC][DK + 1];
-  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], bet[GC];
+  __shared__ float Ks[GC][DK + 1], Qs[GC][DK + 1], Gs[GC][DK + 1], Ki[GC][DK + 1];
+  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], bet[GC], rng[DK];
   const int id = blockIdx.x;
   const int c = id % NC, bh = id / NC, b = bh / H, h = bh % H;
   const int tid = threadIdx.x;
@@ -136,34 +139,72 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     bet[tid] = t < T ? beta[((size_t)b * T + t) * H + h] : 0.f;
   }
   __syncthreads();
-  // Cumulative log gate per channel.
+  // Cumulative log gate per channel, and its range over the chunk.
   if (tid < DK) {
     float acc = 0.f;
     for (int r = 0; r < GC; ++r) {
       acc += Gs[r][tid];
       Gs[r][tid] = acc;
     }
+    rng[tid] = Gs[0][tid] - acc;
   }
   __syncthreads();
+  float wide = 0.f;
+  for (int ch = 0; ch < DK; ++ch) wide = fmaxf(wide, rng[ch]);
 
   float* rec = reinterpret_cast<float*>(ws + (size_t)id * kRecBytes);
   float* Tg = rec;
   float* Pg = rec + GC * GC;
   float* Bg = rec + 2 * GC * GC;
-  // Gram blocks with exact per-channel gate ratios: pairs (r, i), i <= r.
-  for (int pr = tid; pr < GC * GC; pr += GNT) {
-    const int r = pr / GC, i = pr % GC;
-    float a = 0.f, p = 0.f;
-    if (i <= r) {
-      for (int ch = 0; ch < DK; ++ch) {
-        const float e = __expf(Gs[r][ch] - Gs[i][ch]);
-        const float ki = Ks[i][ch] * e;
-        a += Ks[r][ch] * ki;
-        p += Qs[r][ch] * ki;
-      }
+  if (wide <= kFactorRange) {
+    // Gate factors about the chunk's per-channel midpoint Gam_m: with
+    // Kg = K o e^(Gam - Gam_m), Ki = K o e^(Gam_m - Gam), Qg = Q o e^(Gam -
+    // Gam_m) every factor is at most e^(range / 2), and A = lower(Kg Ki^T),
+    // Pm = lower(Qg Ki^T) are two f32 MFMA products (each wave one 16 x 16
+    // tile of both).  Entries above the diagonal may overflow; they are not
+    // used.
+    for (int e = tid; e < GC * DK; e += GNT) {
+      const int r = e / DK, ch = e % DK;
+      const float gm = 0.5f * (Gs[0][ch] + Gs[GC - 1][ch]);
+      const float f = __expf(Gs[r][ch] - gm);
+      Ki[r][ch] = Ks[r][ch] * __expf(gm - Gs[r][ch]);
+      Ks[r][ch] *= f;
+      Qs[r][ch] *= f;
     }
-    As[r][i] = (i < r) ? bet[r] * a : 0.f;
-    Pg[r * GC + i] = (i <= r) ? scale * p : 0.f;
+    __syncthreads();
+    const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int tr = w >> 1, tc = w & 1;
+    f32x4 a0 = zero4(), a1 = zero4(), p0 = zero4(), p1 = zero4();
+#pragma unroll 4
+    for (int kk = 0; kk < DK; kk += 8) {
+      const float ki0 = Ki[16 * tc + lr][kk + lg], ki1 = Ki[16 * tc + lr][kk + 4 + lg];
+      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[16 * tr + lr][kk + lg], ki0, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[16 * tr + lr][kk + 4 + lg], ki1, a1, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[16 * tr + lr][kk + lg], ki0, p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[16 * tr + lr][kk + 4 + lg], ki1, p1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * tr + 4 * lg + j, i = 16 * tc + lr;
+      As[r][i] = (i < r) ? bet[r] * (a0[j] + a1[j]) : 0.f;
+      Pg[r * GC + i] = (i <= r) ? scale * (p0[j] + p1[j]) : 0.f;
+    }
+  } else {
+    // Wide chunk: exact per-channel gate ratios, pairs (r, i), i <= r.
+    for (int pr = tid; pr < GC * GC; pr += GNT) {
+      const int r = pr / GC, i = pr % GC;
+      float a = 0.f, p = 0.f;
+      if (i <= r) {
+        for (int ch = 0; ch < DK; ++ch) {
+          const float e = __expf(Gs[r][ch] - Gs[i][ch]);
+          const float ki = Ks[i][ch] * e;
+          a += Ks[r][ch] * ki;
+          p += Qs[r][ch] * ki;
+        }
+      }
+      As[r][i] = (i < r) ? bet[r] * a : 0.f;
+      Pg[r * GC + i] = (i <= r) ? scale * p : 0.f;
+    }
   }
   __syncthreads();
   // T = (I + A)^-1 (unit lower triangular): lane j owns column j and runs the
