@@ -18,7 +18,8 @@
 //   S_C = diag(e^Gam_C) S0 + (K o e^(Gam_C - Gam))^T U
 // Every gate factor is at most 1, so no factor can overflow whatever the
 // gates are.  Kernel 1 (parallel over chunks) forms A, Pm and T = (I + A)^-1;
-// kernel 2 walks the chunks of one (b, h) and value slice with S in LDS and
+// kernel 2 walks the chunks of one (b, h) and value slice (64 columns, or 32
+// when Dv = 32) with S in LDS and
 // forms K S, Q S, T Y, Pm U and K^T U on f32 MFMA tiles.  All arithmetic is
 // f32 (bf16 inputs are widened on load).  Ragged tails are
 // padded with identity tokens (alpha = 1, beta = 0, q = k = v = 0).
@@ -31,7 +32,6 @@ namespace {
 constexpr int GC = 32;    // tokens per chunk
 constexpr int GNT = 256;   // threads per work-group of the per-chunk kernel
 constexpr int GNTR = 1024; // threads per work-group of the recurrence (16 waves)
-constexpr int GDVS = 32;  // value columns per work-group of the recurrence
 // Largest per-channel log-gate range of a chunk for which the Gram blocks are
 // formed from midpoint-referenced factors (each at most e^(range / 2)).
 constexpr float kFactorRange = 80.f;
@@ -222,27 +222,29 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
   if (tid < GC) Bg[tid] = bet[tid];
 }
 
-// Kernel 2: one work-group per (b, h, value slice of GDVS columns).
-template <class TIn, class TOut, int DK>
+// Kernel 2: one work-group per (b, h, value slice of DVS columns; 64 when Dv
+// allows, else 32).
+template <class TIn, class TOut, int DK, int DVS>
 __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ alpha, const float* state_in, float* state_out,
     TOut* __restrict__ out, int T, int H, int Dv, int NC, float scale,
     const char* __restrict__ ws) {
+  constexpr int GNCT = DVS / 16;     // 16-column tiles of a slice
   __shared__ float Kd[GC][DK + 1];   // K o e^(Gam_C - Gam)
   __shared__ float Kg[GC][DK + 1];   // K o e^Gam
   __shared__ float Qg[GC][DK + 1];   // Q o e^Gam
   __shared__ float Gs[GC][DK + 1];   // cumulative log gates
-  __shared__ float S[DK][GDVS + 1];  // state slice
-  __shared__ float Vs[GC][GDVS + 1], Us[GC][GDVS + 1];
+  __shared__ float S[DK][DVS + 1];  // state slice
+  __shared__ float Vs[GC][DVS + 1], Us[GC][DVS + 1];
   __shared__ float Tm[GC][GC + 1], Pm[GC][GC + 1], bet[GC], gC[DK];
-  const int ns = Dv / GDVS;
+  const int ns = Dv / DVS;
   const int bh = blockIdx.x / ns, sl = blockIdx.x % ns, b = bh / H, h = bh % H;
-  const int col0 = sl * GDVS;
+  const int col0 = sl * DVS;
   const int tid = threadIdx.x;
 
-  for (int e = tid; e < DK * GDVS; e += GNTR) {
-    const int r = e / GDVS, j = e % GDVS;
+  for (int e = tid; e < DK * DVS; e += GNTR) {
+    const int r = e / DVS, j = e % DVS;
     S[r][j] = state_in ? state_in[((size_t)bh * DK + r) * Dv + col0 + j] : 0.f;
   }
 
@@ -270,8 +272,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
                                                 (size_t)h * DK + 4 * (pc % (DK / 4)));
     }
     {
-      const int r = min(tid / (GDVS / 8), GC - 1), t = min(t0 + r, T - 1);
-      rg.v = ld8(v + (((size_t)b * T + t) * H + h) * Dv + col0 + 8 * (tid % (GDVS / 8)));
+      const int r = min(tid / (DVS / 8), GC - 1), t = min(t0 + r, T - 1);
+      rg.v = ld8(v + (((size_t)b * T + t) * H + h) * Dv + col0 + 8 * (tid % (DVS / 8)));
     }
     const float* rec = reinterpret_cast<const float*>(ws + ((size_t)bh * NC + c) * kRecBytes);
 #pragma unroll
@@ -302,8 +304,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
         for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = in ? logf(rg.a[u][e]) : 0.f;
       }
     }
-    if (tid < GC * GDVS / 8) {
-      const int r = tid / (GDVS / 8), c8 = 8 * (tid % (GDVS / 8));
+    if (tid < GC * DVS / 8) {
+      const int r = tid / (DVS / 8), c8 = 8 * (tid % (DVS / 8));
       st8(&Vs[r][c8], rg.v, t0 + r < T);
     }
 #pragma unroll
@@ -352,12 +354,14 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     auto mfma = [](float a, float b, f32x4 c) {
       return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     };
-    // Phase A: waves 0-3 form X = Kg S for one 16 x 16 tile each and keep
-    // Y = diag(beta) (V - X) in LDS; waves 4-7 form Qg S (kept for O).
+    // Phase A: waves 0 .. XT-1 form X = Kg S for one 16 x 16 tile each and
+    // keep Y = diag(beta) (V - X) in LDS; waves XT .. 2 XT-1 form Qg S (kept
+    // for O).  XT = 2 row tiles x GNCT column tiles.
+    constexpr int XT = 2 * GNCT;
     f32x4 qs = zero4();
-    if (w < 8) {
-      const int tr = (w & 3) >> 1, tc = w & 1;
-      const float(*A)[DK + 1] = w < 4 ? Kg : Qg;
+    if (w < 2 * XT) {
+      const int x = w % XT, tr = x / GNCT, tc = x % GNCT;
+      const float(*A)[DK + 1] = w < XT ? Kg : Qg;
       f32x4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll 4
       for (int kk = 0; kk < DK; kk += 8) {
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
         acc1 = mfma(A[16 * tr + lr][kk + 4 + lg], S[kk + 4 + lg][16 * tc + lr], acc1);
       }
       const f32x4 acc = acc0 + acc1;
-      if (w < 4) {
+      if (w < XT) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * tr + 4 * lg + i, j = 16 * tc + lr;
@@ -376,9 +380,9 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       }
     }
     f16ops::lds_barrier();
-    // Phase B: U = T Y (waves 0-3), into Vs (V is no longer needed).
-    if (w < 4) {
-      const int tr = w >> 1, tc = w & 1;
+    // Phase B: U = T Y (waves 0 .. XT-1), into Vs (V is no longer needed).
+    if (w < XT) {
+      const int tr = w / GNCT, tc = w % GNCT;
       f32x4 acc = zero4();
 #pragma unroll
       for (int kk = 0; kk < GC; kk += 4)
@@ -387,10 +391,11 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       for (int i = 0; i < 4; ++i) Vs[16 * tr + 4 * lg + i][16 * tc + lr] = acc[i];
     }
     f16ops::lds_barrier();
-    // Phase C: O = scale Qg S + Pm U (waves 4-7) and the state update
-    // S = diag(e^Gam_C) S + Kd^T U, one 16 x 16 tile of S per wave.
-    if (w >= 4 && w < 8) {
-      const int tr = (w & 3) >> 1, tc = w & 1;
+    // Phase C: O = scale Qg S + Pm U (waves XT .. 2 XT-1) and the state
+    // update S = diag(e^Gam_C) S + Kd^T U, 16 x 16 tiles of S spread over the
+    // waves.
+    if (w >= XT && w < 2 * XT) {
+      const int x = w - XT, tr = x / GNCT, tc = x % GNCT;
       f32x4 acc = qs * scale;
 #pragma unroll
       for (int kk = 0; kk < GC; kk += 4)
@@ -402,8 +407,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
           out[(((size_t)b * T + t) * H + h) * Dv + col0 + 16 * tc + lr] = from_f32<TOut>(acc[i]);
       }
     }
-    if (w < DK / 8) {  // DK / 16 row tiles x 2 column tiles
-      const int sr = w >> 1, sc = w & 1;
+    for (int st = w; st < (DK / 16) * GNCT; st += GNTR / 64) {
+      const int sr = st / GNCT, sc = st % GNCT;
       f32x4 acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -419,8 +424,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
   }
   __syncthreads();
   if (state_out)
-    for (int e = tid; e < DK * GDVS; e += GNTR) {
-      const int r = e / GDVS, j = e % GDVS;
+    for (int e = tid; e < DK * DVS; e += GNTR) {
+      const int r = e / DVS, j = e % DVS;
       state_out[((size_t)bh * DK + r) * Dv + col0 + j] = S[r][j];
     }
 }
@@ -436,10 +441,16 @@ hipError_t launch_chgate_t(const PrefillArgs& p) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK>), dim3(p.B * p.H * (p.Dv / GDVS)),
-                     dim3(GNTR), 0, st, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v, p.alpha,
-                     p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC, p.scale,
-                     (const char*)p.workspace);
+  if (p.Dv % 64 == 0)
+    hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 64>), dim3(p.B * p.H * (p.Dv / 64)),
+                       dim3(GNTR), 0, st, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v,
+                       p.alpha, p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC,
+                       p.scale, (const char*)p.workspace);
+  else
+    hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 32>), dim3(p.B * p.H * (p.Dv / 32)),
+                       dim3(GNTR), 0, st, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v,
+                       p.alpha, p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC,
+                       p.scale, (const char*)p.workspace);
   return hipGetLastError();
 }
 
