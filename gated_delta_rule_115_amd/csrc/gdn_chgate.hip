@@ -36,9 +36,11 @@ constexpr int GNTR = 1024; // threads per work-group of the recurrence (16 waves
 // formed from midpoint-referenced factors (each at most e^(range / 2)).
 constexpr float kFactorRange = 80.f;
 
-// Per-chunk record: T (C x C), Pm (C x C), beta (C), all f32.
+// Per-chunk record: T (C x C), Pm (C x C), beta (C), then from kGamOff the
+// cumulative log gates Gam (C x Dk, room for Dk = 128), all f32.
 constexpr size_t kRecFloats = 2 * GC * GC + GC;
-constexpr size_t kRecBytes = (kRecFloats * 4 + 255) / 256 * 256;
+constexpr size_t kGamOff = (kRecFloats * 4 + 255) / 256 * 256;  // bytes
+constexpr size_t kRecBytes = kGamOff + (size_t)GC * 128 * 4;
 
 // Eight consecutive elements as loaded (bf16: one 16-byte load; f32: two),
 // widened to f32 only when stored to LDS.
@@ -73,8 +75,9 @@ __device__ __forceinline__ void st8(float* d, const Raw8<TIn>& r, bool keep) {
 }
 
 // The streamed inputs of one chunk for one thread: 8-element pieces of K
-// and Q (row p / (DK / 8)), 4-float pieces of alpha, 8-element pieces of the
-// value slice and 4-float pieces of the chunk record.
+// and Q (row p / (DK / 8)), 4-float pieces of alpha (per-chunk kernel) or of
+// the cumulative log gates (recurrence), 8-element pieces of the value slice
+// and 4-float pieces of the chunk record.
 template <class TIn, int DK, int NT>
 struct ChunkRegs {
   static constexpr int NKQ = (GC * DK / 8 + NT - 1) / NT;
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, int T, int H, int NC, float scale, char* __restrict__ ws) {
   __shared__ float Ks[GC][DK + 1], Qs[GC][DK + 1], Gs[GC][DK + 1], Ki[GC][DK + 1];
-  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], bet[GC], rng[DK];
+  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], Rb[GC][GC + 1], bet[GC], rng[DK];
   const int id = blockIdx.x;
   const int c = id % NC, bh = id / NC, b = bh / H, h = bh % H;
   const int tid = threadIdx.x;
@@ -149,6 +152,14 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     rng[tid] = Gs[0][tid] - acc;
   }
   __syncthreads();
+  {
+    float* gam = reinterpret_cast<float*>(ws + (size_t)id * kRecBytes + kGamOff);
+    for (int e = tid; e < GC * DK / 4; e += GNT) {
+      const int r = e / (DK / 4), c4 = 4 * (e % (DK / 4));
+      *reinterpret_cast<f32x4*>(gam + r * DK + c4) =
+          f32x4{Gs[r][c4], Gs[r][c4 + 1], Gs[r][c4 + 2], Gs[r][c4 + 3]};
+    }
+  }
   float wide = 0.f;
   for (int ch = 0; ch < DK; ++ch) wide = fmaxf(wide, rng[ch]);
 
@@ -207,17 +218,67 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     }
   }
   __syncthreads();
-  // T = (I + A)^-1 (unit lower triangular): lane j owns column j and runs the
-  // forward substitution T[r][j] = [r == j] - sum_{j <= m < r} A[r][m] T[m][j].
-  if (tid < GC) {
-    const int j = tid;
-    for (int r = 0; r < GC; ++r) {
-      float x = (r == j) ? 1.f : 0.f;
-      for (int m = j; m < r; ++m) x -= As[r][m] * Ts[m][j];
-      Ts[r][j] = (r < j) ? 0.f : x;
+  // T = (I + A)^-1 for the strictly lower A (A^32 = 0) in product form,
+  //   T = (I - A)(I + A^2)(I + A^4)(I + A^8)(I + A^16),
+  // from four squarings and four products on f32 MFMA tiles (wave w: output
+  // tile (w / 2, w % 2)).  The powers use LDS the Gram blocks are done with.
+  {
+    const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int tr = w >> 1, tc = w & 1;
+    constexpr int LD = GC + 1;
+    float* P2 = &Ks[0][0];
+    float* P4 = &Qs[0][0];
+    float* P8 = &Ki[0][0];
+    float* P16 = &Gs[0][0];
+    // Z = X Y (32 x 32), tile of this wave in accumulator layout, plus C.
+    auto prod = [&](const float* X, const float* Y, f32x4 acc) {
+#pragma unroll
+      for (int kk = 0; kk < GC; kk += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[(16 * tr + lr) * LD + kk + lg],
+                                                   Y[(kk + lg) * LD + 16 * tc + lr], acc, 0, 0, 0);
+      return acc;
+    };
+    auto put = [&](float* Z, f32x4 acc) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Z[(16 * tr + 4 * lg + i) * LD + 16 * tc + lr] = acc[i];
+    };
+    auto get = [&](const float* Z) {
+      f32x4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = Z[(16 * tr + 4 * lg + i) * LD + 16 * tc + lr];
+      return acc;
+    };
+    const float* N = &As[0][0];
+    put(P2, prod(N, N, zero4()));
+    __syncthreads();
+    put(P4, prod(P2, P2, zero4()));
+    __syncthreads();
+    put(P8, prod(P4, P4, zero4()));
+    __syncthreads();
+    put(P16, prod(P8, P8, zero4()));
+    // R = I - A
+    f32x4 id;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * tr + 4 * lg + i, c = 16 * tc + lr;
+      id[i] = (r == c ? 1.f : 0.f) - As[r][c];
     }
+    put(&Ts[0][0], id);
+    __syncthreads();
+    // R <- R + R P for P = A^2, A^4, A^8, A^16 (ping-pong between Ts and Rb).
+    float* R0 = &Ts[0][0];
+    float* R1 = &Rb[0][0];
+    const float* pw[4] = {P2, P4, P8, P16};
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      put(R1, prod(R0, pw[s2], get(R0)));
+      __syncthreads();
+      float* tmp = R0;
+      R0 = R1;
+      R1 = tmp;
+    }
+    // The result is in R0 (Ts after an even number of swaps).
   }
-  __syncthreads();
   for (int e = tid; e < GC * GC; e += GNT) Tg[e] = Ts[e / GC][e % GC];
   if (tid < GC) Bg[tid] = bet[tid];
 }
@@ -227,7 +288,7 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
 template <class TIn, class TOut, int DK, int DVS>
 __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ alpha, const float* state_in, float* state_out,
+    const float* state_in, float* state_out,
     TOut* __restrict__ out, int T, int H, int Dv, int NC, float scale,
     const char* __restrict__ ws) {
   constexpr int GNCT = DVS / 16;     // 16-column tiles of a slice
@@ -253,7 +314,7 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
   // inside the loop order LDS only, so those loads stay in flight.
   typedef ChunkRegs<TIn, DK, GNTR> R;
   R rg;
-  const size_t tok = (size_t)H * DK;  // elements between tokens (q, k, alpha)
+  const size_t tok = (size_t)H * DK;  // elements between tokens (q, k)
   auto fetch = [&](int c) {
     const int t0 = c * GC;
 #pragma unroll
@@ -264,12 +325,12 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       rg.k[u] = ld8(k + off);
       rg.q[u] = ld8(q + off);
     }
+    const float* gam =
+        reinterpret_cast<const float*>(ws + ((size_t)bh * NC + c) * kRecBytes + kGamOff);
 #pragma unroll
     for (int u = 0; u < R::NA; ++u) {
-      const int pc = tid + GNTR * u;
-      const int r = min(pc / (DK / 4), GC - 1), t = min(t0 + r, T - 1);
-      rg.a[u] = *reinterpret_cast<const f32x4*>(alpha + ((size_t)b * T + t) * tok +
-                                                (size_t)h * DK + 4 * (pc % (DK / 4)));
+      const int pc = min(tid + GNTR * u, GC * DK / 4 - 1);
+      rg.a[u] = *reinterpret_cast<const f32x4*>(gam + 4 * pc);
     }
     {
       const int r = min(tid / (DVS / 8), GC - 1), t = min(t0 + r, T - 1);
@@ -299,9 +360,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       const int pc = tid + GNTR * u;
       if (pc < GC * DK / 4) {
         const int r = pc / (DK / 4), c4 = 4 * (pc % (DK / 4));
-        const bool in = t0 + r < T;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = in ? logf(rg.a[u][e]) : 0.f;
+        for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = rg.a[u][e];
       }
     }
     if (tid < GC * DVS / 8) {
@@ -330,14 +390,7 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     stash(c);
     if (c + 1 < NC) fetch(c + 1);
     f16ops::lds_barrier();
-    if (tid < DK) {
-      float acc = 0.f;
-      for (int r = 0; r < GC; ++r) {
-        acc += Gs[r][tid];
-        Gs[r][tid] = acc;
-      }
-      gC[tid] = __expf(acc);
-    }
+    if (tid < DK) gC[tid] = __expf(Gs[GC - 1][tid]);
     f16ops::lds_barrier();
     for (int e = tid; e < GC * DK; e += GNTR) {
       const int r = e / DK, ch = e % DK;
@@ -444,12 +497,12 @@ hipError_t launch_chgate_t(const PrefillArgs& p) {
   if (p.Dv % 64 == 0)
     hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 64>), dim3(p.B * p.H * (p.Dv / 64)),
                        dim3(GNTR), 0, st, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v,
-                       p.alpha, p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC,
+                       p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC,
                        p.scale, (const char*)p.workspace);
   else
     hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 32>), dim3(p.B * p.H * (p.Dv / 32)),
                        dim3(GNTR), 0, st, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v,
-                       p.alpha, p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC,
+                       p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC,
                        p.scale, (const char*)p.workspace);
   return hipGetLastError();
 }
