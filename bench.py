@@ -119,26 +119,31 @@ PROFILE = "profiles/gdn_kernels_bench_workloads.md"
 # The long32k prefill call launches three kernels (segment transition pass,
 # combine pass, output pass); its entry sums them.
 PREFILL_KERNELS = "prefill_lead_kernel<bf16> + segment_combine_kernel + prefill_out_kernel<bf16>"
+CHGATE_KERNELS = "chgate_prep_kernel + chgate_recur_kernel (f32)"
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
         sha1="b59d12c44fab1aaa70540f5992f06ee343d3de89",
-        fetch_kib=248588 + 73758 + 373114, write_kib=55324 + 14336 + 239618,
+        fetch_kib=248592 + 73758 + 373030, write_kib=55419 + 14336 + 239616,
         profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
-        sha1="02983eefd933df1e58e3c70b84eb4b79e821b4f6",
-        fetch_kib=265774, write_kib=526431, profile=PROFILE),
+        sha1="556df9b0674b65c32a725eb4e02f64b0b1605c12",
+        fetch_kib=265776, write_kib=526490, profile=PROFILE),
     "swa_sink_decode_kernel<bf16,bf16,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa.hip",
         sha1="afa1a0eccd2a4fdf0d91fdc379ee91e97784c24f",
-        fetch_kib=1062049, write_kib=6144, profile=PROFILE),
+        fetch_kib=1062142, write_kib=6144, profile=PROFILE),
     # mean of the three launches of the counter run (same inputs)
     "swa_sink_prefill_kernel<bf16>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa_prefill.hip",
-        sha1="ebef4b7f4449660d27e60ada66979c84477530f1",
-        fetch_kib=(444994 + 440958 + 442816) / 3, write_kib=(133787 + 133882 + 133955) / 3,
+        sha1="22b363dac7d447a545132a0e123c8b66d2eff229",
+        fetch_kib=(444559 + 440543 + 444151) / 3, write_kib=(133710 + 134342 + 133952) / 3,
         profile=PROFILE),
+    CHGATE_KERNELS: dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
+        sha1="e6f24fb2117a24e606ce9cb50b818561ee82a6d7",
+        fetch_kib=266587 + 723003, write_kib=395306 + 139264, profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
@@ -548,10 +553,12 @@ def main():
         inf = infos["chgate_llama8b"]
         ms = seg_ms[("chgate_llama8b", "chgate_prefill")]
         sec = ms / 1e3
-        roof_chgate = dict(bound="alu", kernel="chgate_prep_kernel + chgate_recur_kernel (f32)",
+        kern = CHGATE_KERNELS
+        roof_chgate = dict(bound="alu", kernel=kern,
                            achieved=inf["alu_flops"] / sec / 1e12,
                            peak=PEAK_F32_VECTOR_FLOPS / 1e12, unit="TFLOP/s",
-                           frac=inf["alu_flops"] / sec / PEAK_F32_VECTOR_FLOPS, traffic=None,
+                           frac=inf["alu_flops"] / sec / PEAK_F32_VECTOR_FLOPS,
+                           traffic=traffic_bytes(kern),
                            ms_per_launch=ms, flops_per_launch=inf["alu_flops"],
                            hbm_bytes_algorithmic=inf["bytes"],
                            hbm_frac_algorithmic=inf["bytes"] / sec / PEAK_HBM_BPS)
