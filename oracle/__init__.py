@@ -58,6 +58,7 @@ def _load():
         lib.gdn_oracle_recurrence_f32.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
         lib.gdn_oracle_swa_sink_f64.argtypes = [_dp] * 4 + [i] * 6 + [d, i]
         lib.gdn_oracle_recurrence_chgate_f64.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
+        lib.gdn_oracle_recurrence_bwd_f64.argtypes = [_dp] * 14 + [i] * 5 + [d]
         lib.gdn_oracle_hybrid_f64.argtypes = [_dp] * 9 + [i] * 7 + [d, d]
         lib.gdn_oracle_short_conv_silu_f64.argtypes = [_dp] * 3 + [i] * 5 + [d]
         lib.gdn_oracle_short_conv_step_f64.argtypes = [_dp] * 5 + [i] * 4 + [d]
@@ -114,6 +115,26 @@ def decode_step(q, k, v, alpha, beta, state_in, scale=1.0):
     a, b = (_arr(x)[:, None] for x in (alpha, beta))
     out, s = gdn_recurrence(q, k, v, a, b, state_in, scale)
     return out[:, 0], s
+
+
+def gdn_recurrence_backward(q, k, v, alpha, beta, dout, state_in=None, dstate_out=None,
+                            scale=1.0):
+    """Gradients of gdn_recurrence (section 3.1.2, scalar gate) by the adjoint
+    of the token loop.  dout [B,T,H,Dv], dstate_out [B,H,Dk,Dv] or None.
+    Returns dict dq, dk, dv, dalpha, dbeta, dstate_in."""
+    q, k, v, alpha, beta, dout = map(_arr, (q, k, v, alpha, beta, dout))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    s_in = None if state_in is None else _arr(state_in)
+    ds = None if dstate_out is None else _arr(dstate_out)
+    r = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+             dalpha=np.zeros_like(alpha), dbeta=np.zeros_like(beta),
+             dstate_in=np.zeros((B, H, Dk, Dv)))
+    _load().gdn_oracle_recurrence_bwd_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(s_in), _ptr(dout), _ptr(ds),
+        _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dalpha"]), _ptr(r["dbeta"]),
+        _ptr(r["dstate_in"]), B, T, H, Dk, Dv, float(scale))
+    return r
 
 
 def gdn_recurrence_chgate(q, k, v, alpha, beta, state_in=None, scale=1.0, gate_first=True):

@@ -187,6 +187,111 @@ void gdn_oracle_recurrence_chgate_f64(const double* q, const double* k, const do
 }
 
 /* ------------------------------------------------------------------------- */
+/* Gradient of the GDN recurrence (section 3.1.2, scalar gate) by the adjoint */
+/* of the token loop: with A_t = alpha_t (I - beta_t k_t k_t^T) (symmetric),  */
+/* S_t = A_t S_{t-1} + beta_t k_t v_t^T and o_t = scale S_t^T q_t, the total  */
+/* gradient G_t = dL/dS_t obeys                                               */
+/*   G_t = scale q_t do_t^T + A_{t+1} G_{t+1},   G_T-1 includes dS_T,         */
+/* and with P = S_{t-1}, p = P^T k_t, g = G_t^T k_t:                           */
+/*   dq_t = scale S_t do_t                                                    */
+/*   dv_t = beta_t g                                                          */
+/*   dalpha_t = <G_t, P> - beta_t g.p                                         */
+/*   dbeta_t  = g.(v_t - alpha_t p)                                           */
+/*   dk_t = -alpha_t beta_t (G_t p + P g) + beta_t G_t v_t                    */
+/*   dS0 = A_0 G_0.                                                           */
+/* dstate_out may be NULL (no gradient into the final state).  The forward    */
+/* states are recomputed and kept for the whole sequence (small cases only).  */
+/* ------------------------------------------------------------------------- */
+void gdn_oracle_recurrence_bwd_f64(const double* q, const double* k, const double* v,
+                                   const double* alpha, const double* beta,
+                                   const double* state_in, const double* dout,
+                                   const double* dstate_out, double* dq, double* dk,
+                                   double* dv, double* dalpha, double* dbeta,
+                                   double* dstate_in, int B, int T, int H, int Dk, int Dv,
+                                   double scale) {
+  long BH = (long)B * H;
+  long SZ = (long)Dk * Dv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    long b = bh / H, h = bh % H;
+    double* Ss = (double*)malloc(sizeof(double) * (size_t)(T + 1) * SZ);  /* S_{-1} .. S_{T-1} */
+    double* G = (double*)malloc(sizeof(double) * (size_t)SZ);
+    double* p = (double*)malloc(sizeof(double) * (size_t)Dv);
+    double* g = (double*)malloc(sizeof(double) * (size_t)Dv);
+    for (long e = 0; e < SZ; ++e) Ss[e] = state_in ? state_in[bh * SZ + e] : 0.0;
+    for (long t = 0; t < T; ++t) {
+      long row = (b * T + t) * H + h;
+      const double* kt = k + row * Dk;
+      const double* vt = v + row * Dv;
+      const double* P = Ss + t * SZ;
+      double* S = Ss + (t + 1) * SZ;
+      double a = alpha[row], be = beta[row];
+      for (long j = 0; j < Dv; ++j) {
+        double acc = 0;
+        for (long i = 0; i < Dk; ++i) acc += kt[i] * P[i * Dv + j];
+        p[j] = acc;
+      }
+      for (long i = 0; i < Dk; ++i)
+        for (long j = 0; j < Dv; ++j)
+          S[i * Dv + j] = a * (P[i * Dv + j] - be * kt[i] * p[j]) + be * kt[i] * vt[j];
+    }
+    for (long e = 0; e < SZ; ++e) G[e] = dstate_out ? dstate_out[bh * SZ + e] : 0.0;
+    for (long t = T - 1; t >= 0; --t) {
+      long row = (b * T + t) * H + h;
+      const double* qt = q + row * Dk;
+      const double* kt = k + row * Dk;
+      const double* vt = v + row * Dv;
+      const double* dot = dout + row * Dv;
+      const double* P = Ss + t * SZ;
+      const double* S = Ss + (t + 1) * SZ;
+      double a = alpha[row], be = beta[row];
+      for (long i = 0; i < Dk; ++i)
+        for (long j = 0; j < Dv; ++j) G[i * Dv + j] += scale * qt[i] * dot[j];
+      for (long i = 0; i < Dk; ++i) {
+        double acc = 0;
+        for (long j = 0; j < Dv; ++j) acc += S[i * Dv + j] * dot[j];
+        dq[row * Dk + i] = scale * acc;
+      }
+      for (long j = 0; j < Dv; ++j) {
+        double ap = 0, ag = 0;
+        for (long i = 0; i < Dk; ++i) {
+          ap += kt[i] * P[i * Dv + j];
+          ag += kt[i] * G[i * Dv + j];
+        }
+        p[j] = ap;
+        g[j] = ag;
+      }
+      double gp = 0, gvp = 0, gP = 0;
+      for (long j = 0; j < Dv; ++j) {
+        gp += g[j] * p[j];
+        gvp += g[j] * (vt[j] - a * p[j]);
+        dv[row * Dv + j] = be * g[j];
+      }
+      for (long e = 0; e < SZ; ++e) gP += G[e] * P[e];
+      dalpha[row] = gP - be * gp;
+      dbeta[row] = gvp;
+      for (long i = 0; i < Dk; ++i) {
+        double Gp = 0, Pg = 0, Gv = 0;
+        for (long j = 0; j < Dv; ++j) {
+          Gp += G[i * Dv + j] * p[j];
+          Pg += P[i * Dv + j] * g[j];
+          Gv += G[i * Dv + j] * vt[j];
+        }
+        dk[row * Dk + i] = -a * be * (Gp + Pg) + be * Gv;
+      }
+      /* G_{t-1} part carried back: A_t G_t = a (G - be k g^T) */
+      for (long i = 0; i < Dk; ++i)
+        for (long j = 0; j < Dv; ++j) G[i * Dv + j] = a * (G[i * Dv + j] - be * kt[i] * g[j]);
+    }
+    for (long e = 0; e < SZ; ++e) dstate_in[bh * SZ + e] = G[e];
+    free(Ss);
+    free(G);
+    free(p);
+    free(g);
+  }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Membership of token i (0-based) in the exact-attention set of step t       */
 /* (0-based) with s sinks and a window of w tokens (section 4, sliding        */
 /* window display): sinks are tokens 0..s-1, the window is t-w+1..t.          */

@@ -488,3 +488,59 @@ def test_chgate_decode_steps_chain_to_recurrence():
         o, S = oracle.decode_step_chgate(q[:, t], k[:, t], v[:, t], a_ch[:, t], beta[:, t], S)
         np.testing.assert_array_equal(o, out[:, t])
     np.testing.assert_array_equal(S, ST)
+
+
+# --------------------------------------------------------------------------
+# Backward of the recurrence (the gradients a layer trained through the mixer
+# needs).  Pinned by torch autograd over a plain token loop (fp64, CPU) and by
+# central finite differences of the oracle's own forward.
+# --------------------------------------------------------------------------
+def _torch_forward(q, k, v, a, b, S0, scale):
+    B, T, H, Dk = q.shape
+    outs, S = [], S0
+    for t in range(T):
+        kt, vt, qt = k[:, t], v[:, t], q[:, t]                    # [B,H,D]
+        at, bt = a[:, t][..., None, None], b[:, t][..., None, None]
+        p = torch.einsum("bhi,bhij->bhj", kt, S)
+        S = at * (S - bt * kt[..., :, None] * p[..., None, :]) + bt * kt[..., :, None] * vt[..., None, :]
+        outs.append(scale * torch.einsum("bhij,bhi->bhj", S, qt))
+    return torch.stack(outs, 1), S
+
+
+@pytest.mark.parametrize("Dk,Dv", [(4, 3), (3, 5)])
+def test_backward_matches_torch_autograd(Dk, Dv):
+    B, T, H = 2, 7, 2
+    q, k, v, alpha, beta, S0 = _rand_gdn(B, T, H, Dk, Dv, RNG)
+    dout = RNG.standard_normal((B, T, H, Dv))
+    dST = RNG.standard_normal((B, H, Dk, Dv))
+    ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True)
+          for x in (q, k, v, alpha, beta, S0)]
+    o, ST = _torch_forward(*ts, 0.7)
+    ((o * torch.from_numpy(dout)).sum() + (ST * torch.from_numpy(dST)).sum()).backward()
+    r = oracle.gdn_recurrence_backward(q, k, v, alpha, beta, dout, S0, dST, scale=0.7)
+    for name, t in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dstate_in"), ts):
+        np.testing.assert_allclose(r[name], t.grad.numpy(), atol=1e-11, rtol=1e-9, err_msg=name)
+
+
+def test_backward_matches_finite_differences():
+    B, T, H, Dk, Dv = 1, 6, 1, 3, 2
+    q, k, v, alpha, beta, S0 = _rand_gdn(B, T, H, Dk, Dv, RNG)
+    dout = RNG.standard_normal((B, T, H, Dv))
+    r = oracle.gdn_recurrence_backward(q, k, v, alpha, beta, dout, S0)
+
+    def loss(xs):
+        o, _ = oracle.gdn_recurrence(*xs)
+        return float((o * dout).sum())
+
+    xs = [q, k, v, alpha, beta, S0]
+    names = ("dq", "dk", "dv", "dalpha", "dbeta", "dstate_in")
+    eps = 1e-6
+    for i, name in enumerate(names):
+        d = RNG.standard_normal(xs[i].shape)
+        plus = [x.copy() for x in xs]
+        minus = [x.copy() for x in xs]
+        plus[i] = plus[i] + eps * d
+        minus[i] = minus[i] - eps * d
+        fd = (loss(plus) - loss(minus)) / (2 * eps)
+        np.testing.assert_allclose(float((r[name] * d).sum()), fd, rtol=1e-6, atol=1e-8,
+                                   err_msg=name)
