@@ -20,6 +20,9 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   leg "chgate_llama8b":  GDN with a channel-wise gate diag(alpha_t), B=4, H=32,
                          T=4096, d=128, bf16 in/out, f32 gates [B,T,H,128]:
                          gdn_prefill_chunked_chgate (chunks of 32, f32)
+  leg "backward_t1024":  gradients of the scalar-gate prefill (dq, dk, dv,
+                         dalpha, dbeta, dS0) for B=4, H=32, T=1024, d=128,
+                         bf16 inputs, f32 gradients: gdn_prefill_backward
   leg "conv_qwen32b":    Qwen-32B-shaped layer with projection adaptation:
                          gdn_short_conv_silu on q, k (with per-head L2 norm)
                          and v, then gdn_prefill_chunked; B=2, H=40, T=16384
@@ -86,6 +89,14 @@ def chgate_flops_per_token_head(dk, dv, C=32):
 # bf16 q, k, v, out + f32 per-channel alpha and beta per token-head.
 def chgate_bytes(B, T, H, dk, dv, esize=2):
     return B * T * H * (esize * (2 * dk + 2 * dv) + 4 * dk + 4) + B * H * dk * dv * 4
+
+
+# Backward (direct adjoint with recompute) per token-head: the forward state
+# update twice (checkpoint sweep and per-chunk recompute, ~5 dk dv each) and
+# the adjoint step (~19 dk dv: G += q do^T, S do, G v, G^T k, P^T k, P g,
+# <G, P>, G p, the carry of G).
+def backward_flops_per_token_head(dk, dv):
+    return 29 * dk * dv
 
 
 def swa_set_sizes(T, n_sink, window):
@@ -171,7 +182,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill_long32k,decode_b256,hybrid_prefill,"
-                                      "chgate_llama8b,conv_qwen32b,convstep_b256")
+                                      "chgate_llama8b,backward_t1024,conv_qwen32b,"
+                                      "convstep_b256")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) "
                          "and exit: the reference reading for HBM byte counters")
@@ -302,6 +314,25 @@ def make_chgate_leg():
     return run, info
 
 
+def make_backward_leg():
+    B, T, H, d = 4, 1024, 32, 128
+    x = synthetic.gdn_inputs(B, T, H, d, d, dtype="bf16", seed=8, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    dout = torch.randn(B, T, H, d, generator=gen, device="cuda")
+    ws = torch.empty(gdn.gdn_prefill_backward_workspace_bytes(B, T, H, d, d), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(mark):
+        gdn.gdn_prefill_backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dout,
+                                 workspace=ws)
+        mark("backward")
+
+    info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
+                alu_flops=backward_flops_per_token_head(d, d) * B * T * H,
+                bytes=B * T * H * (2 * 3 * d + 8 + 4 * d + 4 * (3 * d + 2)))
+    return run, info
+
+
 def make_conv_leg():
     c = synthetic.CONFIGS["qwen32b_conv"]
     B, T, H, d = c["B"], c["T"], c["H"], c["Dk"]
@@ -427,6 +458,9 @@ def main():
     if "chgate_llama8b" in legs_wanted:
         run, info = make_chgate_leg()
         legs["chgate_llama8b"], infos["chgate_llama8b"] = run, info
+    if "backward_t1024" in legs_wanted:
+        run, info = make_backward_leg()
+        legs["backward_t1024"], infos["backward_t1024"] = run, info
     if "conv_qwen32b" in legs_wanted:
         run, info = make_conv_leg()
         legs["conv_qwen32b"], infos["conv_qwen32b"] = run, info
@@ -562,6 +596,16 @@ def main():
                            ms_per_launch=ms, flops_per_launch=inf["alu_flops"],
                            hbm_bytes_algorithmic=inf["bytes"],
                            hbm_frac_algorithmic=inf["bytes"] / sec / PEAK_HBM_BPS)
+    roof_bwd = None
+    if "backward_t1024" in out_legs:
+        inf = infos["backward_t1024"]
+        ms = seg_ms[("backward_t1024", "backward")]
+        sec = ms / 1e3
+        roof_bwd = dict(bound="alu", kernel="gdn_bwd_kernel (f32)",
+                        achieved=inf["alu_flops"] / sec / 1e12,
+                        peak=PEAK_F32_VECTOR_FLOPS / 1e12, unit="TFLOP/s",
+                        frac=inf["alu_flops"] / sec / PEAK_F32_VECTOR_FLOPS, traffic=None,
+                        ms_per_launch=ms, flops_per_launch=inf["alu_flops"])
     roof_conv = None
     if "conv_qwen32b" in out_legs:
         inf = infos["conv_qwen32b"]
@@ -602,7 +646,7 @@ def main():
             "workload": "long32k prefill (B1 H32 T32768 d128, chunk 64) + hybrid decode "
                         "(B256 H32 d128, 4 sinks + 512 window) + hybrid prefill (B4 H32 "
                         "T4096 d128, 4 sinks + 512 window) + channel-gate prefill (B4 H32 "
-                        "T4096 d128) + qwen32b conv+prefill "
+                        "T4096 d128) + backward (B4 H32 T1024 d128) + qwen32b conv+prefill "
                         "(B2 H40 T16384 d128) + decode-time conv step (B256, 3 x 5120 "
                         "channels, K 4)",
             "global_batch": 1, "seq_len": 32768, "parallelism": "single-gpu",
@@ -613,6 +657,7 @@ def main():
         "roofline_decode": roof_dec,
         "roofline_swa_prefill": roof_swa_pref,
         "roofline_chgate": roof_chgate,
+        "roofline_backward": roof_bwd,
         "roofline_conv": roof_conv,
         "roofline_conv_step": roof_convstep,
         "cpu_baseline": cpu,

@@ -28,7 +28,7 @@ __all__ = [
     "gdn_swa_sink_decode", "gdn_swa_sink_prefill", "gdn_swa_cache_fill",
     "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
     "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
-    "EXPORTED_SYMBOLS",
+    "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward", "EXPORTED_SYMBOLS",
 ]
 
 GDN_BF16 = 0
@@ -43,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "gdn_short_conv_step", "gdn_swa_sink_decode", "gdn_swa_sink_prefill",
     "gdn_swa_cache_fill", "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
     "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
+    "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +98,10 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_chunked_chgate.argtypes = [vp] * 8 + [i] * 7 + [f, vp, sz, vp]
     L.gdn_decode_step_chgate.restype = i
     L.gdn_decode_step_chgate.argtypes = [vp] * 8 + [i] * 6 + [f, vp]
+    L.gdn_prefill_backward_workspace_bytes.restype = sz
+    L.gdn_prefill_backward_workspace_bytes.argtypes = [i] * 5
+    L.gdn_prefill_backward.restype = i
+    L.gdn_prefill_backward.argtypes = [vp] * 14 + [i] * 6 + [f, vp, sz, vp]
     _lib = L
     return L
 
@@ -429,3 +434,39 @@ def gdn_decode_step_chgate(q, k, v, alpha, beta, state_in, *, state_out=None, ou
         _stream(stream))
     _check("gdn_decode_step_chgate", st)
     return out, state_out
+
+
+def gdn_prefill_backward_workspace_bytes(B, T, H, Dk, Dv) -> int:
+    return int(lib().gdn_prefill_backward_workspace_bytes(B, T, H, Dk, Dv))
+
+
+def gdn_prefill_backward(q, k, v, alpha, beta, dout, state_in=None, dstate_out=None, *,
+                         scale=1.0, workspace=None, stream=None):
+    """Gradients of gdn_prefill_chunked (scalar gate): returns dict dq, dk, dv,
+    dalpha, dbeta, dstate_in (f32).  dout [B,T,H,Dv] f32; dstate_out
+    [B,H,Dk,Dv] f32 or None."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, q.shape)
+    _dev(v, "v", q.dtype, (B, T, H, Dv))
+    _dev(alpha, "alpha", torch.float32, (B, T, H))
+    _dev(beta, "beta", torch.float32, (B, T, H))
+    _dev(state_in, "state_in", torch.float32, (B, H, Dk, Dv))
+    _dev(dout, "dout", torch.float32, (B, T, H, Dv))
+    _dev(dstate_out, "dstate_out", torch.float32, (B, H, Dk, Dv))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    r = dict(dq=torch.empty((B, T, H, Dk), **f32), dk=torch.empty((B, T, H, Dk), **f32),
+             dv=torch.empty((B, T, H, Dv), **f32), dalpha=torch.empty((B, T, H), **f32),
+             dbeta=torch.empty((B, T, H), **f32), dstate_in=torch.empty((B, H, Dk, Dv), **f32))
+    need = gdn_prefill_backward_workspace_bytes(B, T, H, Dk, Dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib().gdn_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(dout),
+        _ptr(dstate_out), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dalpha"]),
+        _ptr(r["dbeta"]), _ptr(r["dstate_in"]), B, T, H, Dk, Dv, _dtype_code(q),
+        float(scale), _ptr(workspace), wbytes, _stream(stream))
+    _check("gdn_prefill_backward", st)
+    return r

@@ -475,4 +475,46 @@ int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const fl
   return hip_status(gdn::launch_decode(p), "gdn_decode_step_chgate launch");
 }
 
+size_t gdn_prefill_backward_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
+  if (B < 0 || T < 0 || H < 1 || !is_head_dim(Dk) || !is_head_dim(Dv)) return 0;
+  return gdn::backward_workspace_bytes(B, T, H, Dk, Dv);
+}
+
+int gdn_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* state_in, const float* dout,
+                         const float* dstate_out, float* dq, float* dk, float* dv,
+                         float* dalpha, float* dbeta, float* dstate_in, int B, int T, int H,
+                         int Dk, int Dv, int dtype, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  REQUIRE(dtype == GDN_BF16 || dtype == GDN_F32, GDN_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
+          H);
+  REQUIRE(is_head_dim(Dk) && is_head_dim(Dv), GDN_ERR_UNSUPPORTED,
+          "head dims Dk=%d Dv=%d not in {16,32,64,128}", Dk, Dv);
+  REQUIRE((long long)B * H < (1LL << 31), GDN_ERR_UNSUPPORTED, "grid too large");
+  if ((long long)B * H == 0) return ok();
+  REQUIRE_ALIGNED_OR_NULL(state_in);
+  REQUIRE_ALIGNED_OR_NULL(dstate_out);
+  REQUIRE(dstate_in != nullptr, GDN_ERR_INVALID_ARG, "dstate_in is NULL");
+  if (T > 0) {
+    REQUIRE(q && k && v && alpha && beta && dout, GDN_ERR_INVALID_ARG,
+            "q, k, v, alpha, beta and dout are required");
+    REQUIRE(dq && dk && dv && dalpha && dbeta, GDN_ERR_INVALID_ARG,
+            "dq, dk, dv, dalpha and dbeta are required");
+  }
+  const size_t need = gdn::backward_workspace_bytes(B, T, H, Dk, Dv);
+  REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
+  REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
+          "workspace is not 256-byte aligned");
+  REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes",
+          workspace_bytes, need);
+  gdn::BwdArgs p;
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta; p.state_in = state_in;
+  p.dout = dout; p.dstate_out = dstate_out; p.dq = dq; p.dk = dk; p.dv = dv;
+  p.dalpha = dalpha; p.dbeta = dbeta; p.dstate_in = dstate_in;
+  p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.bf16 = dtype == GDN_BF16;
+  p.scale = scale; p.workspace = workspace; p.stream = stream;
+  return hip_status(gdn::launch_backward(p), "gdn_prefill_backward launch");
+}
+
 }  // extern "C"

@@ -86,6 +86,22 @@ hipError_t launch_conv(const ConvArgs& p);
 hipError_t launch_conv_step(const ConvArgs& p, void* state);
 hipError_t launch_swa(const SwaArgs& p);
 
+// Backward of the scalar-gate recurrence: gradients of q, k, v, alpha, beta
+// and the initial state for an output gradient (and optional final-state
+// gradient); f32 gradients; Dk, Dv in {16, 32, 64, 128}.
+struct BwdArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta, *state_in, *dout, *dstate_out;
+  float *dq, *dk, *dv, *dalpha, *dbeta, *dstate_in;
+  int B, T, H, Dk, Dv;
+  bool bf16;
+  float scale;
+  void* workspace;
+  void* stream;
+};
+size_t backward_workspace_bytes(int B, int T, int H, int Dk, int Dv);
+hipError_t launch_backward(const BwdArgs& p);
+
 // Channel-wise gate prefill (alpha [B, T, H, Dk]); chunks of 32 tokens,
 // f32 arithmetic; Dk in {32, 64, 128}, Dv a multiple of 32.
 size_t prefill_chgate_workspace_bytes(int B, int T, int H);

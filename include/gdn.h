@@ -279,6 +279,36 @@ int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const fl
                            void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
                            float scale, void* stream);
 
+/*
+ * Backward pass of gdn_prefill_chunked (scalar gate; section 3.1.2 update,
+ * trained through as in section 3.3): for an output gradient dout and an
+ * optional gradient dstate_out of the final state, the gradients of the
+ * inputs by the adjoint of the token loop,
+ *   G_t = scale q_t dout_t^T + A_{t+1} G_{t+1},  A_t = alpha_t (I - beta_t k_t k_t^T),
+ *   dq_t = scale S_t dout_t, dv_t = beta_t G_t^T k_t,
+ *   dk_t = -alpha_t beta_t (G_t p_t + S_{t-1} G_t^T k_t) + beta_t G_t v_t,
+ *   dalpha_t = <G_t, S_{t-1}> - beta_t (G_t^T k_t).p_t,
+ *   dbeta_t = (G_t^T k_t).(v_t - alpha_t p_t),  p_t = S_{t-1}^T k_t,
+ *   dstate_in = A_0 G_0.
+ *   q, k [B,T,H,Dk], v [B,T,H,Dv] dtype; alpha, beta [B,T,H] f32;
+ *   state_in [B,H,Dk,Dv] f32 or NULL (zeros); dout [B,T,H,Dv] f32;
+ *   dstate_out [B,H,Dk,Dv] f32 or NULL (zeros).
+ *   Outputs (f32, caller-owned): dq, dk [B,T,H,Dk], dv [B,T,H,Dv],
+ *   dalpha, dbeta [B,T,H], dstate_in [B,H,Dk,Dv].
+ *   workspace: gdn_prefill_backward_workspace_bytes(B, T, H, Dk, Dv) bytes,
+ *   256-byte aligned (forward-state checkpoints every 32 tokens and one
+ *   chunk of recomputed states per head).
+ * One work-group per (b, h), sequential over tokens, f32 arithmetic.
+ * Limits: Dk and Dv in {16, 32, 64, 128}.
+ */
+size_t gdn_prefill_backward_workspace_bytes(int B, int T, int H, int Dk, int Dv);
+int gdn_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* state_in, const float* dout,
+                         const float* dstate_out, float* dq, float* dk, float* dv,
+                         float* dalpha, float* dbeta, float* dstate_in, int B, int T, int H,
+                         int Dk, int Dv, int dtype, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

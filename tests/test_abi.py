@@ -242,6 +242,27 @@ def test_chgate_validation():
     assert dec(B=0, q=None) == OK
 
 
+def test_backward_validation():
+    L = gdn.lib()
+    ws = L.gdn_prefill_backward_workspace_bytes(2, 100, 3, 64, 64)
+    assert ws == 2 * 3 * (4 + 32) * 64 * 64 * 4
+    assert L.gdn_prefill_backward_workspace_bytes(2, 100, 3, 100, 64) == 0
+
+    def call(**kw):
+        a = dict(q=A, ds=A, Dk=64, Dv=64, ws=A, wsb=ws, dt=F32, B=2)
+        a.update(kw)
+        return L.gdn_prefill_backward(a["q"], A, A, A, A, None, A, None, A, A, A, A, A, a["ds"],
+                                      a["B"], 100, 3, a["Dk"], a["Dv"], a["dt"], 1.0, a["ws"],
+                                      a["wsb"], None)
+    assert call(Dk=96) == UNSUPPORTED
+    assert call(dt=5) == INVALID
+    assert call(wsb=ws - 1) == INVALID and "workspace too small" in _err()
+    assert call(ws=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(ds=None) == INVALID
+    assert call(B=0, q=None) == OK
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "_lib", None)
     monkeypatch.setattr(gdn, "library_path", str(tmp_path / "absent.so"))
