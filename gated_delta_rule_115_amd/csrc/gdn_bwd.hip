@@ -13,14 +13,20 @@
 //   dk_t = -alpha_t beta_t (G_t p + P g) + beta_t G_t v_t,
 //   and the initial-state gradient is A_0 G_0.
 //
-// One work-group of 512 threads per (b, h) holds S and G (f32) in LDS.  A
-// forward sweep stores the state entering every chunk of BCK = 32 tokens
-// (the checkpoints); the backward sweep takes the chunks in reverse, recomputes
-// the chunk's states from its checkpoint into a per-head buffer, and runs
-// the adjoint over the chunk's tokens in reverse, reading S_{t-1} back from
-// that buffer.  The buffer is written and read by the same work-group across
-// full barriers.  All arithmetic is f32; this is the direct form of the
-// adjoint (no chunked rewrite), sequential over tokens.
+// The columns of S and G evolve independently, so one work-group of 512
+// threads takes one (b, h) and a slice of 32 state columns and holds that
+// DK x 32 part of S and G (f32) in LDS.  A forward sweep stores the state
+// entering every chunk of BCK = 32 tokens (the checkpoints); the backward
+// sweep takes the chunks in reverse, recomputes the chunk's states from its
+// checkpoint into a per-work-group buffer, and runs the adjoint over the
+// chunk's tokens in reverse, reading S_{t-1} back from that buffer.  The
+// buffer and the checkpoints are written and read by the same thread.
+// Gradients that sum over all columns (dq, dk, dalpha, dbeta) are written as
+// per-slice partials and summed in slice order by a second kernel.  All
+// arithmetic is f32; this is the direct form of the adjoint (no chunked
+// rewrite), sequential over tokens.
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -35,58 +41,96 @@ __device__ __forceinline__ float ldin(const TIn* p) {
   return to_f32(*p);
 }
 
-template <class TIn, int DK, int DV>
+// Work-group per (b, h, slice of DVS state columns): the columns of S and of
+// its adjoint G evolve independently, so each work-group carries DK x DVS of
+// both.  Per-token quantities that sum over all columns (dq, dk, dalpha,
+// dbeta) are written per slice to `part` and summed by bwd_reduce_kernel
+// (written directly when there is one slice).  Every matrix-vector product
+// uses the whole work-group: NPC threads per column (reduction index
+// interleaved, lanes of one group summed by shuffles) or NPR threads per row.
+template <class TIn, int DK, int DV, int DVS>
 __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ state_in, const float* __restrict__ dout,
     const float* __restrict__ dstate_out, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta,
-    float* __restrict__ dstate_in, int T, int H, float scale, float* __restrict__ ws) {
-  constexpr int LD = DV + 1;
-  constexpr int SZ = DK * DV;
+    float* __restrict__ dstate_in, int T, int H, float scale, float* __restrict__ ws,
+    float* __restrict__ part) {
+  constexpr int NS = DV / DVS;
+  constexpr int LD = DVS + 1;
+  constexpr int SZ = DK * DVS;
+  constexpr int NPC = (BNT / DVS < DK) ? BNT / DVS : DK;  // threads per column
+  constexpr int NPR = (BNT / DK < DVS) ? BNT / DK : DVS;  // threads per row
   __shared__ float S[DK * LD], G[DK * LD];
-  __shared__ float kv[DK], qv[DK], vv[DV], dov[DV];
-  __shared__ float pv[DV], gv[DV], Gv[DK], Pg[DK], red[BNT / 64][3], sc[3];
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  __shared__ float kv[DK], qv[DK], vv[DVS], dov[DVS];
+  __shared__ float pv[DVS], gv[DVS], Gv[DK], Pg[DK], red[BNT / 64][3], sc[3];
+  const int bh = blockIdx.x / NS, sl = blockIdx.x % NS, b = bh / H, h = bh % H;
+  const int col0 = sl * DVS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int NC = (T + BCK - 1) / BCK;
-  float* ckpt = ws + (size_t)bh * (NC + BCK) * SZ;  // NC checkpoints, then BCK chunk states
+  float* ckpt = ws + (size_t)blockIdx.x * (NC + BCK) * SZ;  // NC checkpoints, BCK chunk states
   float* cbuf = ckpt + (size_t)NC * SZ;
+  const size_t BTH = (size_t)gridDim.x / NS * T;  // token-heads
+  float* pdq = part + ((size_t)sl * BTH) * DK;
+  float* pdk = part + ((size_t)NS * BTH) * DK + ((size_t)sl * BTH) * DK;
+  float* pda = part + ((size_t)2 * NS * BTH) * DK + (size_t)sl * BTH;
+  float* pdb = pda + (size_t)NS * BTH;
 
-  auto load_tok = [&](int t) {  // k, q, v, do of token t into LDS
+  // y_j = sum_i M[i][j] x_i for the slice's columns (x in LDS, length DK).
+  auto colsum = [&](const float* M, const float* x, float* y) {
+    const int j = tid / NPC, pp = tid % NPC;
+    if (j < DVS) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = pp; i < DK; i += NPC) acc += M[i * LD + j] * x[i];
+#pragma unroll
+      for (int off = 1; off < NPC; off <<= 1) acc += __shfl_xor(acc, off);
+      if (pp == 0) y[j] = acc;
+    }
+  };
+  // y_i = sum_j M[i][j] x_j over the slice's columns; returns the sum in the
+  // lane with pp == 0 of row i (other lanes: partial), row index via *row.
+  auto rowsum = [&](const float* M, const float* x, int* row) {
+    const int i = tid / NPR, pp = tid % NPR;
+    *row = (i < DK && pp == 0) ? i : -1;
+    float acc = 0.f;
+    if (i < DK) {
+#pragma unroll
+      for (int j = pp; j < DVS; j += NPR) acc += M[i * LD + j] * x[j];
+    }
+#pragma unroll
+    for (int off = 1; off < NPR; off <<= 1) acc += __shfl_xor(acc, off);
+    return acc;
+  };
+  auto load_tok = [&](int t) {
     const size_t row = ((size_t)b * T + t) * H + h;
     for (int i = tid; i < DK; i += BNT) {
       kv[i] = ldin(k + row * DK + i);
       qv[i] = ldin(q + row * DK + i);
     }
-    for (int j = tid; j < DV; j += BNT) {
-      vv[j] = ldin(v + row * DV + j);
-      dov[j] = dout[row * DV + j];
+    for (int j = tid; j < DVS; j += BNT) {
+      vv[j] = ldin(v + row * DV + col0 + j);
+      dov[j] = dout[row * DV + col0 + j];
     }
   };
   auto step = [&](int t) {  // S <- A_t S + beta_t k v^T
     const size_t row = ((size_t)b * T + t) * H + h;
     const float a = alpha[row], be = beta[row];
-    __syncthreads();  // kv, vv of token t visible
-    if (tid < DV) {
-      float acc = 0.f;
-      for (int i = 0; i < DK; ++i) acc += S[i * LD + tid] * kv[i];
-      pv[tid] = acc;
-    }
+    __syncthreads();
+    colsum(S, kv, pv);
     __syncthreads();
     for (int e = tid; e < SZ; e += BNT) {
-      const int i = e / DV, j = e % DV;
+      const int i = e / DVS, j = e % DVS;
       S[i * LD + j] = a * (S[i * LD + j] - be * kv[i] * pv[j]) + be * kv[i] * vv[j];
     }
   };
-  auto save = [&](float* dst) {  // S -> dst (dense DK x DV)
-    for (int e = tid; e < SZ; e += BNT) dst[e] = S[(e / DV) * LD + e % DV];
+  auto save = [&](float* dst) {
+    for (int e = tid; e < SZ; e += BNT) dst[e] = S[(e / DVS) * LD + e % DVS];
   };
   auto restore = [&](const float* src) {
-    for (int e = tid; e < SZ; e += BNT) S[(e / DV) * LD + e % DV] = src[e];
+    for (int e = tid; e < SZ; e += BNT) S[(e / DVS) * LD + e % DVS] = src[e];
   };
-  // Sums over the work-group of three values per thread (into sc).
   auto block_sum3 = [&](float x0, float x1, float x2) {
     for (int off = 32; off > 0; off >>= 1) {
       x0 += __shfl_xor(x0, off);
@@ -100,16 +144,17 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
     }
     __syncthreads();
     if (tid < 3) {
-      float s = 0.f;
-      for (int w = 0; w < BNT / 64; ++w) s += red[w][tid];
-      sc[tid] = s;
+      float s2 = 0.f;
+      for (int w = 0; w < BNT / 64; ++w) s2 += red[w][tid];
+      sc[tid] = s2;
     }
     __syncthreads();
   };
 
   // Forward sweep: checkpoints.
   for (int e = tid; e < SZ; e += BNT)
-    S[(e / DV) * LD + e % DV] = state_in ? state_in[(size_t)bh * SZ + e] : 0.f;
+    S[(e / DVS) * LD + e % DVS] =
+        state_in ? state_in[((size_t)bh * DK + e / DVS) * DV + col0 + e % DVS] : 0.f;
   __syncthreads();
   for (int c = 0; c < NC; ++c) {
     save(ckpt + (size_t)c * SZ);
@@ -123,7 +168,8 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
 
   // Backward sweep.
   for (int e = tid; e < SZ; e += BNT)
-    G[(e / DV) * LD + e % DV] = dstate_out ? dstate_out[(size_t)bh * SZ + e] : 0.f;
+    G[(e / DVS) * LD + e % DVS] =
+        dstate_out ? dstate_out[((size_t)bh * DK + e / DVS) * DV + col0 + e % DVS] : 0.f;
   for (int c = NC - 1; c >= 0; --c) {
     const int t0 = c * BCK, t1 = min(T, t0 + BCK);
     __syncthreads();
@@ -134,92 +180,114 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
       load_tok(t);
       step(t);
     }
-    // S holds S_{t1-1}.
     for (int t = t1 - 1; t >= t0; --t) {
       const size_t row = ((size_t)b * T + t) * H + h;
+      const size_t th = (size_t)b * T * H + (size_t)t * H + h;  // token-head index
       const float a = alpha[row], be = beta[row];
       __syncthreads();
       load_tok(t);
       __syncthreads();
-      // G_t = scale q do^T + (carried part)
       for (int e = tid; e < SZ; e += BNT) {
-        const int i = e / DV, j = e % DV;
+        const int i = e / DVS, j = e % DVS;
         G[i * LD + j] += scale * qv[i] * dov[j];
       }
       __syncthreads();
-      // dq = scale S_t do (threads 0..DK-1), G v (threads 128..128+DK-1) and
-      // g = G^T k (threads 256..256+DV-1) side by side.
-      if (tid < DK) {
-        float acc = 0.f;
-        for (int j = 0; j < DV; ++j) acc += S[tid * LD + j] * dov[j];
-        dq[row * DK + tid] = scale * acc;
-      } else if (tid >= 128 && tid < 128 + DK) {
-        const int i = tid - 128;
-        float acc = 0.f;
-        for (int j = 0; j < DV; ++j) acc += G[i * LD + j] * vv[j];
-        Gv[i] = acc;
-      } else if (tid >= 256 && tid < 256 + DV) {
-        const int j = tid - 256;
-        float acc = 0.f;
-        for (int i = 0; i < DK; ++i) acc += G[i * LD + j] * kv[i];
-        gv[j] = acc;
-      }
+      int ri;
+      const float dqp = rowsum(S, dov, &ri);  // S_t do (this slice's columns)
+      if (ri >= 0) (NS == 1 ? dq + row * DK : pdq + th * DK)[ri] = scale * dqp;
+      const float gvp = rowsum(G, vv, &ri);
+      if (ri >= 0) Gv[ri] = gvp;
+      colsum(G, kv, gv);
       __syncthreads();
-      // S <- S_{t-1} (P).
-      restore(cbuf + (size_t)(t - t0) * SZ);
+      restore(cbuf + (size_t)(t - t0) * SZ);  // S <- S_{t-1}
       __syncthreads();
-      // p = P^T k (threads 0..DV-1), P g (threads 256..256+DK-1).
-      if (tid < DV) {
-        float acc = 0.f;
-        for (int i = 0; i < DK; ++i) acc += S[i * LD + tid] * kv[i];
-        pv[tid] = acc;
-      } else if (tid >= 256 && tid < 256 + DK) {
-        const int i = tid - 256;
-        float acc = 0.f;
-        for (int j = 0; j < DV; ++j) acc += S[i * LD + j] * gv[j];
-        Pg[i] = acc;
-      }
-      float part = 0.f;  // <G, P>
+      colsum(S, kv, pv);
+      const float pg = rowsum(S, gv, &ri);
+      if (ri >= 0) Pg[ri] = pg;
+      float gP = 0.f;
       for (int e = tid; e < SZ; e += BNT) {
-        const int i = e / DV, j = e % DV;
-        part += G[i * LD + j] * S[i * LD + j];
+        const int i = e / DVS, j = e % DVS;
+        gP += G[i * LD + j] * S[i * LD + j];
       }
       __syncthreads();  // pv, Pg ready
-      float gpp = 0.f, gvp = 0.f;
-      if (tid < DV) {
+      float gpp = 0.f, gvv = 0.f;
+      if (tid < DVS) {
         gpp = gv[tid] * pv[tid];
-        gvp = gv[tid] * (vv[tid] - a * pv[tid]);
-        dv[row * DV + tid] = be * gv[tid];
+        gvv = gv[tid] * (vv[tid] - a * pv[tid]);
+        dv[row * DV + col0 + tid] = be * gv[tid];
       }
-      block_sum3(part, gpp, gvp);
+      const float gp = rowsum(G, pv, &ri);
+      if (ri >= 0)
+        (NS == 1 ? dk + row * DK : pdk + th * DK)[ri] = -a * be * (gp + Pg[ri]) + be * Gv[ri];
+      block_sum3(gP, gpp, gvv);
       if (tid == 0) {
-        dalpha[row] = sc[0] - be * sc[1];
-        dbeta[row] = sc[2];
+        (NS == 1 ? dalpha + row : pda + th)[0] = sc[0] - be * sc[1];
+        (NS == 1 ? dbeta + row : pdb + th)[0] = sc[2];
       }
-      // dk = -a be (G p + P g) + be G v (threads 0..DK-1; G p here).
-      if (tid < DK) {
-        float acc = 0.f;
-        for (int j = 0; j < DV; ++j) acc += G[tid * LD + j] * pv[j];
-        dk[row * DK + tid] = -a * be * (acc + Pg[tid]) + be * Gv[tid];
-      }
-      __syncthreads();
-      // Carry: G <- A_t G = a (G - be k g^T).
+      // Carry: G <- A_t G (block_sum3 ended with a barrier).
       for (int e = tid; e < SZ; e += BNT) {
-        const int i = e / DV, j = e % DV;
+        const int i = e / DVS, j = e % DVS;
         G[i * LD + j] = a * (G[i * LD + j] - be * kv[i] * gv[j]);
       }
     }
   }
   __syncthreads();
-  for (int e = tid; e < SZ; e += BNT) dstate_in[(size_t)bh * SZ + e] = G[(e / DV) * LD + e % DV];
+  for (int e = tid; e < SZ; e += BNT)
+    dstate_in[((size_t)bh * DK + e / DVS) * DV + col0 + e % DVS] = G[(e / DVS) * LD + e % DVS];
 }
+
+// Sums the per-slice partials of dq, dk, dalpha, dbeta (NS slices).
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ dq,
+                                                         float* __restrict__ dk,
+                                                         float* __restrict__ dalpha,
+                                                         float* __restrict__ dbeta, size_t BTH,
+                                                         int DK, int NS) {
+  const size_t n = BTH * DK;
+  const float* pdq = part;
+  const float* pdk = part + (size_t)NS * n;
+  const float* pda = part + (size_t)2 * NS * n;
+  const float* pdb = pda + (size_t)NS * BTH;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    float a = 0.f, c = 0.f;
+    for (int s2 = 0; s2 < NS; ++s2) {
+      a += pdq[(size_t)s2 * n + e];
+      c += pdk[(size_t)s2 * n + e];
+    }
+    dq[e] = a;
+    dk[e] = c;
+  }
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < BTH; e += (size_t)gridDim.x * 256) {
+    float a = 0.f, c = 0.f;
+    for (int s2 = 0; s2 < NS; ++s2) {
+      a += pda[(size_t)s2 * BTH + e];
+      c += pdb[(size_t)s2 * BTH + e];
+    }
+    dalpha[e] = a;
+    dbeta[e] = c;
+  }
+}
+
+constexpr int kBwdSlice = 32;  // state columns per work-group
 
 template <class TIn, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& p) {
-  hipLaunchKernelGGL((gdn_bwd_kernel<TIn, DK, DV>), dim3(p.B * p.H), dim3(BNT), 0,
-                     (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v,
-                     p.alpha, p.beta, p.state_in, p.dout, p.dstate_out, p.dq, p.dk, p.dv,
-                     p.dalpha, p.dbeta, p.dstate_in, p.T, p.H, p.scale, (float*)p.workspace);
+  constexpr int DVS = DV < kBwdSlice ? DV : kBwdSlice;
+  constexpr int NS = DV / DVS;
+  const int NC = (p.T + BCK - 1) / BCK;
+  float* ws = (float*)p.workspace;
+  float* part = ws + (size_t)p.B * p.H * NS * (NC + BCK) * DK * DVS;
+  const hipStream_t st = (hipStream_t)p.stream;
+  hipLaunchKernelGGL((gdn_bwd_kernel<TIn, DK, DV, DVS>), dim3(p.B * p.H * NS), dim3(BNT), 0, st,
+                     (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v, p.alpha, p.beta,
+                     p.state_in, p.dout, p.dstate_out, p.dq, p.dk, p.dv, p.dalpha, p.dbeta,
+                     p.dstate_in, p.T, p.H, p.scale, ws, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || NS == 1 || p.T == 0) return e;
+  const size_t BTH = (size_t)p.B * p.T * p.H;
+  const unsigned blocks = (unsigned)std::min<size_t>((BTH * DK + 255) / 256, 4096);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(blocks), dim3(256), 0, st, part, p.dq, p.dk,
+                     p.dalpha, p.dbeta, BTH, DK, NS);
   return hipGetLastError();
 }
 
@@ -244,12 +312,14 @@ hipError_t launch_bwd_dk(const BwdArgs& p) {
   }
   return hipErrorInvalidValue;
 }
-
 }  // namespace
 
 size_t backward_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
   const size_t nc = ((size_t)T + BCK - 1) / BCK;
-  return (size_t)B * H * (nc + BCK) * Dk * Dv * sizeof(float);
+  const size_t dvs = Dv < kBwdSlice ? Dv : kBwdSlice, ns = Dv / dvs;
+  const size_t ckpt = (size_t)B * H * ns * (nc + BCK) * Dk * dvs;
+  const size_t part = ns > 1 ? ns * (size_t)B * T * H * (2 * (size_t)Dk + 2) : 0;
+  return (ckpt + part) * sizeof(float);
 }
 
 hipError_t launch_backward(const BwdArgs& p) {

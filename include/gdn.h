@@ -297,8 +297,11 @@ int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const fl
  *   dalpha, dbeta [B,T,H], dstate_in [B,H,Dk,Dv].
  *   workspace: gdn_prefill_backward_workspace_bytes(B, T, H, Dk, Dv) bytes,
  *   256-byte aligned (forward-state checkpoints every 32 tokens and one
- *   chunk of recomputed states per head).
- * One work-group per (b, h), sequential over tokens, f32 arithmetic.
+ *   chunk of recomputed states per head and column slice, plus per-slice
+ *   partial sums of dq, dk, dalpha, dbeta when Dv > 32).
+ * One work-group per (b, h, slice of 32 state columns), sequential over
+ * tokens, f32 arithmetic; a second kernel sums the slices' partials in a
+ * fixed order, so results are deterministic.
  * Limits: Dk and Dv in {16, 32, 64, 128}.
  */
 size_t gdn_prefill_backward_workspace_bytes(int B, int T, int H, int Dk, int Dv);
