@@ -41,6 +41,27 @@ __device__ __forceinline__ float ldin(const TIn* p) {
   return to_f32(*p);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N a power of two up to 64); every lane
+// of the group ends with the total.  Within a row of 16 lanes by DPP moves
+// (quad swaps, then half-row and row mirrors), across rows by swizzles.
+template <int N>
+__device__ __forceinline__ float lane_sum(float x) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power-of-two lane group");
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
 // Work-group per (b, h, slice of DVS state columns): the columns of S and of
 // its adjoint G evolve independently, so each work-group carries DK x DVS of
 // both.  Per-token quantities that sum over all columns (dq, dk, dalpha,
@@ -60,11 +81,13 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
   constexpr int NS = DV / DVS;
   constexpr int LD = DVS + 1;
   constexpr int SZ = DK * DVS;
+  constexpr int NPT = (SZ + BNT - 1) / BNT;               // state elements per thread
   constexpr int NPC = (BNT / DVS < DK) ? BNT / DVS : DK;  // threads per column
   constexpr int NPR = (BNT / DK < DVS) ? BNT / DK : DVS;  // threads per row
   __shared__ float S[DK * LD], G[DK * LD];
-  __shared__ float kv[DK], qv[DK], vv[DVS], dov[DVS];
-  __shared__ float pv[DVS], gv[DVS], Gv[DK], Pg[DK], red[BNT / 64][3], sc[3];
+  // The current chunk's token inputs (k, q rows; the slice's v, dout columns).
+  __shared__ float ck[BCK * DK], cq[BCK * DK], cv[BCK * DVS], cdo[BCK * DVS], ca[BCK], cb[BCK];
+  __shared__ float pv[DVS], gv[DVS], Gv[DK], Pg[DK], red[2][BNT / 64][3];
   const int bh = blockIdx.x / NS, sl = blockIdx.x % NS, b = bh / H, h = bh % H;
   const int col0 = sl * DVS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -84,8 +107,7 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
       float acc = 0.f;
 #pragma unroll
       for (int i = pp; i < DK; i += NPC) acc += M[i * LD + j] * x[i];
-#pragma unroll
-      for (int off = 1; off < NPC; off <<= 1) acc += __shfl_xor(acc, off);
+      acc = lane_sum<NPC>(acc);
       if (pp == 0) y[j] = acc;
     }
   };
@@ -99,25 +121,32 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
 #pragma unroll
       for (int j = pp; j < DVS; j += NPR) acc += M[i * LD + j] * x[j];
     }
-#pragma unroll
-    for (int off = 1; off < NPR; off <<= 1) acc += __shfl_xor(acc, off);
-    return acc;
+    return lane_sum<NPR>(acc);
   };
-  auto load_tok = [&](int t) {
-    const size_t row = ((size_t)b * T + t) * H + h;
-    for (int i = tid; i < DK; i += BNT) {
-      kv[i] = ldin(k + row * DK + i);
-      qv[i] = ldin(q + row * DK + i);
+  // Tokens [t0, t1) of the chunk into LDS (q and dout only when wanted).
+  auto load_chunk = [&](int t0, int t1, bool with_q) {
+    const int n = t1 - t0;
+    const size_t row0 = ((size_t)b * T + t0) * H + h;
+    for (int e = tid; e < n * DK; e += BNT) {
+      const size_t off = (row0 + (size_t)(e / DK) * H) * DK + e % DK;
+      ck[e] = ldin(k + off);
+      if (with_q) cq[e] = ldin(q + off);
     }
-    for (int j = tid; j < DVS; j += BNT) {
-      vv[j] = ldin(v + row * DV + col0 + j);
-      dov[j] = dout[row * DV + col0 + j];
+    for (int e = tid; e < n * DVS; e += BNT) {
+      const size_t off = (row0 + (size_t)(e / DVS) * H) * DV + col0 + e % DVS;
+      cv[e] = ldin(v + off);
+      if (with_q) cdo[e] = dout[off];
+    }
+    if (tid < n) {
+      ca[tid] = alpha[row0 + (size_t)tid * H];
+      cb[tid] = beta[row0 + (size_t)tid * H];
     }
   };
-  auto step = [&](int t) {  // S <- A_t S + beta_t k v^T
-    const size_t row = ((size_t)b * T + t) * H + h;
-    const float a = alpha[row], be = beta[row];
-    __syncthreads();
+  auto step = [&](int tl) {  // S <- A_t S + beta_t k v^T, token tl of the chunk
+    const float* kv = ck + tl * DK;
+    const float* vv = cv + tl * DVS;
+    __syncthreads();  // chunk inputs loaded, previous update done
+    const float a = ca[tl], be = cb[tl];
     colsum(S, kv, pv);
     __syncthreads();
     for (int e = tid; e < SZ; e += BNT) {
@@ -131,39 +160,29 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
   auto restore = [&](const float* src) {
     for (int e = tid; e < SZ; e += BNT) S[(e / DVS) * LD + e % DVS] = src[e];
   };
-  auto block_sum3 = [&](float x0, float x1, float x2) {
-    for (int off = 32; off > 0; off >>= 1) {
-      x0 += __shfl_xor(x0, off);
-      x1 += __shfl_xor(x1, off);
-      x2 += __shfl_xor(x2, off);
-    }
+  // Per-wave partial sums of three values into red[par]; read after the
+  // next barrier (red is double-buffered by token parity).
+  auto wave_sum3 = [&](float x0, float x1, float x2, int par) {
+    x0 = lane_sum<64>(x0);
+    x1 = lane_sum<64>(x1);
+    x2 = lane_sum<64>(x2);
     if (lane == 0) {
-      red[wv][0] = x0;
-      red[wv][1] = x1;
-      red[wv][2] = x2;
+      red[par][wv][0] = x0;
+      red[par][wv][1] = x1;
+      red[par][wv][2] = x2;
     }
-    __syncthreads();
-    if (tid < 3) {
-      float s2 = 0.f;
-      for (int w = 0; w < BNT / 64; ++w) s2 += red[w][tid];
-      sc[tid] = s2;
-    }
-    __syncthreads();
   };
 
   // Forward sweep: checkpoints.
   for (int e = tid; e < SZ; e += BNT)
     S[(e / DVS) * LD + e % DVS] =
         state_in ? state_in[((size_t)bh * DK + e / DVS) * DV + col0 + e % DVS] : 0.f;
-  __syncthreads();
   for (int c = 0; c < NC; ++c) {
+    const int t0 = c * BCK, t1 = min(T, t0 + BCK);
+    __syncthreads();  // previous chunk's last update done
     save(ckpt + (size_t)c * SZ);
-    for (int t = c * BCK; t < min(T, (c + 1) * BCK); ++t) {
-      __syncthreads();
-      load_tok(t);
-      step(t);
-    }
-    __syncthreads();
+    load_chunk(t0, t1, false);
+    for (int t = t0; t < t1; ++t) step(t - t0);
   }
 
   // Backward sweep.
@@ -172,21 +191,30 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
         dstate_out ? dstate_out[((size_t)bh * DK + e / DVS) * DV + col0 + e % DVS] : 0.f;
   for (int c = NC - 1; c >= 0; --c) {
     const int t0 = c * BCK, t1 = min(T, t0 + BCK);
-    __syncthreads();
+    __syncthreads();  // previous chunk's last carry done, chunk buffers free
     restore(ckpt + (size_t)c * SZ);
+    load_chunk(t0, t1, true);
     for (int t = t0; t < t1; ++t) {
       __syncthreads();
       save(cbuf + (size_t)(t - t0) * SZ);  // S_{t-1}
-      load_tok(t);
-      step(t);
+      step(t - t0);
     }
     for (int t = t1 - 1; t >= t0; --t) {
+      const int tl = t - t0;
       const size_t row = ((size_t)b * T + t) * H + h;
-      const size_t th = (size_t)b * T * H + (size_t)t * H + h;  // token-head index
-      const float a = alpha[row], be = beta[row];
-      __syncthreads();
-      load_tok(t);
-      __syncthreads();
+      const float a = ca[tl], be = cb[tl];
+      const float* kv = ck + tl * DK;
+      const float* qv = cq + tl * DK;
+      const float* vv = cv + tl * DVS;
+      const float* dov = cdo + tl * DVS;
+      // S_{t-1}, written by this thread in the recompute loop, fetched early.
+      float prev[NPT];
+#pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        const int e = tid + u * BNT;
+        prev[u] = (e < SZ) ? cbuf[(size_t)tl * SZ + e] : 0.f;
+      }
+      __syncthreads();  // previous carry done
       for (int e = tid; e < SZ; e += BNT) {
         const int i = e / DVS, j = e % DVS;
         G[i * LD + j] += scale * qv[i] * dov[j];
@@ -194,12 +222,16 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
       __syncthreads();
       int ri;
       const float dqp = rowsum(S, dov, &ri);  // S_t do (this slice's columns)
-      if (ri >= 0) (NS == 1 ? dq + row * DK : pdq + th * DK)[ri] = scale * dqp;
+      if (ri >= 0) (NS == 1 ? dq + row * DK : pdq + row * DK)[ri] = scale * dqp;
       const float gvp = rowsum(G, vv, &ri);
       if (ri >= 0) Gv[ri] = gvp;
       colsum(G, kv, gv);
       __syncthreads();
-      restore(cbuf + (size_t)(t - t0) * SZ);  // S <- S_{t-1}
+#pragma unroll
+      for (int u = 0; u < NPT; ++u) {  // S <- S_{t-1}
+        const int e = tid + u * BNT;
+        if (e < SZ) S[(e / DVS) * LD + e % DVS] = prev[u];
+      }
       __syncthreads();
       colsum(S, kv, pv);
       const float pg = rowsum(S, gv, &ri);
@@ -218,13 +250,20 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
       }
       const float gp = rowsum(G, pv, &ri);
       if (ri >= 0)
-        (NS == 1 ? dk + row * DK : pdk + th * DK)[ri] = -a * be * (gp + Pg[ri]) + be * Gv[ri];
-      block_sum3(gP, gpp, gvv);
+        (NS == 1 ? dk + row * DK : pdk + row * DK)[ri] = -a * be * (gp + Pg[ri]) + be * Gv[ri];
+      wave_sum3(gP, gpp, gvv, t & 1);
+      __syncthreads();  // G reads and wave partials done
       if (tid == 0) {
-        (NS == 1 ? dalpha + row : pda + th)[0] = sc[0] - be * sc[1];
-        (NS == 1 ? dbeta + row : pdb + th)[0] = sc[2];
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+        for (int w = 0; w < BNT / 64; ++w) {
+          s0 += red[t & 1][w][0];
+          s1 += red[t & 1][w][1];
+          s2 += red[t & 1][w][2];
+        }
+        (NS == 1 ? dalpha + row : pda + row)[0] = s0 - be * s1;
+        (NS == 1 ? dbeta + row : pdb + row)[0] = s2;
       }
-      // Carry: G <- A_t G (block_sum3 ended with a barrier).
+      // Carry: G <- A_t G.
       for (int e = tid; e < SZ; e += BNT) {
         const int i = e / DVS, j = e % DVS;
         G[i * LD + j] = a * (G[i * LD + j] - be * kv[i] * gv[j]);
