@@ -13,18 +13,19 @@
 //   dk_t = -alpha_t beta_t (G_t p + P g) + beta_t G_t v_t,
 //   and the initial-state gradient is A_0 G_0.
 //
-// The columns of S and G evolve independently, so one work-group of 512
-// threads takes one (b, h) and a slice of 32 state columns and holds that
-// DK x 32 part of S and G (f32) in LDS.  A forward sweep stores the state
-// entering every chunk of BCK = 32 tokens (the checkpoints); the backward
-// sweep takes the chunks in reverse, recomputes the chunk's states from its
-// checkpoint into a per-work-group buffer, and runs the adjoint over the
-// chunk's tokens in reverse, reading S_{t-1} back from that buffer.  The
-// buffer and the checkpoints are written and read by the same thread.
-// Gradients that sum over all columns (dq, dk, dalpha, dbeta) are written as
-// per-slice partials and summed in slice order by a second kernel.  All
-// arithmetic is f32; this is the direct form of the adjoint (no chunked
-// rewrite), sequential over tokens.
+// The columns of S and G evolve independently, so one work-group takes one
+// (b, h) and a slice of 32 state columns (16 when Dv = 16) and holds that
+// Dk x 32 part of S and G (f32) in registers, 16 lanes per column.  A forward
+// sweep stores the state entering every chunk of BCK = 32 tokens (the
+// checkpoints); the backward sweep takes the chunks in reverse, recomputes
+// the chunk's states from its checkpoint into a per-work-group buffer, and
+// runs the adjoint over the chunk's tokens in reverse, reading S_{t-1} back
+// from that buffer.  Each thread reads back only what it wrote itself.  The
+// chunk's token inputs are staged in LDS once per chunk.  Gradients that sum
+// over all columns (dq, dk, dalpha, dbeta) are written as per-slice partials
+// and summed in slice order by a second kernel.  All arithmetic is f32; this
+// is the direct form of the adjoint (no chunked rewrite), sequential over
+// tokens.
 #include <algorithm>
 
 #include "gdn_device.h"
@@ -34,7 +35,6 @@ namespace gdn {
 namespace {
 
 constexpr int BCK = 32;   // tokens per checkpointed chunk
-constexpr int BNT = 512;  // threads per work-group
 
 template <class TIn>
 __device__ __forceinline__ float ldin(const TIn* p) {
@@ -69,8 +69,48 @@ __device__ __forceinline__ float lane_sum(float x) {
 // (written directly when there is one slice).  Every matrix-vector product
 // uses the whole work-group: NPC threads per column (reduction index
 // interleaved, lanes of one group summed by shuffles) or NPR threads per row.
+// Sum over the four 16-lane column groups of a wave of R per-lane row
+// values x[u] (rows pp*R + u), written as the wave's partial to dst[row].
+// For R >= 4 it is a reduce-scatter (halving over lane bit 5, then bit 4);
+// each row is written by exactly one lane.
+template <int R>
+__device__ __forceinline__ void wave_rows_to_lds(const float (&x)[R], int lane, int pp,
+                                                 float* dst) {
+  const bool b5 = lane & 32, b4 = lane & 16;
+  if constexpr (R >= 4) {
+    float y[R / 2], z[R / 4];
+#pragma unroll
+    for (int m = 0; m < R / 2; ++m) {
+      const float send = b5 ? x[m] : x[m + R / 2];
+      y[m] = (b5 ? x[m + R / 2] : x[m]) + __shfl_xor(send, 32);
+    }
+#pragma unroll
+    for (int m = 0; m < R / 4; ++m) {
+      const float send = b4 ? y[m] : y[m + R / 4];
+      z[m] = (b4 ? y[m + R / 4] : y[m]) + __shfl_xor(send, 16);
+    }
+    const int u0 = (b5 ? R / 2 : 0) + (b4 ? R / 4 : 0);
+#pragma unroll
+    for (int m = 0; m < R / 4; ++m) dst[pp * R + u0 + m] = z[m];
+  } else if constexpr (R == 2) {
+    float y = (b5 ? x[1] : x[0]) + __shfl_xor(b5 ? x[0] : x[1], 32);
+    y += __shfl_xor(y, 16);
+    if (!b4) dst[pp * 2 + (b5 ? 1 : 0)] = y;
+  } else {
+    float y = x[0] + __shfl_xor(x[0], 32);
+    y += __shfl_xor(y, 16);
+    if (lane < 16) dst[pp] = y;
+  }
+}
+
+// Thread layout: 16 lanes per state column (a DPP row), DVS columns, so
+// NT = 16 * DVS threads; lane pp of column j holds rows pp*RPT .. pp*RPT+RPT-1
+// of that column of S and of G in registers.  Column sums (S^T k, G^T k) are
+// 16-lane DPP sums; row sums (dq, dk) go through a per-wave reduce-scatter and
+// an LDS array double-buffered by token parity, so the backward token loop
+// has one barrier per token and the forward steps none.
 template <class TIn, int DK, int DV, int DVS>
-__global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
+__global__ __launch_bounds__(512) void gdn_bwd_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ state_in, const float* __restrict__ dout,
@@ -79,18 +119,18 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
     float* __restrict__ dstate_in, int T, int H, float scale, float* __restrict__ ws,
     float* __restrict__ part) {
   constexpr int NS = DV / DVS;
-  constexpr int LD = DVS + 1;
+  constexpr int NT = 16 * DVS;
+  constexpr int NW = NT / 64;
+  constexpr int RPT = DK / 16;
   constexpr int SZ = DK * DVS;
-  constexpr int NPT = (SZ + BNT - 1) / BNT;               // state elements per thread
-  constexpr int NPC = (BNT / DVS < DK) ? BNT / DVS : DK;  // threads per column
-  constexpr int NPR = (BNT / DK < DVS) ? BNT / DK : DVS;  // threads per row
-  __shared__ float S[DK * LD], G[DK * LD];
+  static_assert(NT * RPT == SZ && NT <= 512, "thread layout");
   // The current chunk's token inputs (k, q rows; the slice's v, dout columns).
   __shared__ float ck[BCK * DK], cq[BCK * DK], cv[BCK * DVS], cdo[BCK * DVS], ca[BCK], cb[BCK];
-  __shared__ float pv[DVS], gv[DVS], Gv[DK], Pg[DK], red[2][BNT / 64][3];
+  __shared__ float rowp[2][2][NW][DK], scal[2][NW][2];
   const int bh = blockIdx.x / NS, sl = blockIdx.x % NS, b = bh / H, h = bh % H;
   const int col0 = sl * DVS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int j = tid >> 4, pp = tid & 15, r0 = pp * RPT;
   const int NC = (T + BCK - 1) / BCK;
   float* ckpt = ws + (size_t)blockIdx.x * (NC + BCK) * SZ;  // NC checkpoints, BCK chunk states
   float* cbuf = ckpt + (size_t)NC * SZ;
@@ -99,40 +139,19 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
   float* pdk = part + ((size_t)NS * BTH) * DK + ((size_t)sl * BTH) * DK;
   float* pda = part + ((size_t)2 * NS * BTH) * DK + (size_t)sl * BTH;
   float* pdb = pda + (size_t)NS * BTH;
+  const size_t sbase = (size_t)bh * DK * DV + col0 + j;  // element (r0, j) of a [DK, DV] state
 
-  // y_j = sum_i M[i][j] x_i for the slice's columns (x in LDS, length DK).
-  auto colsum = [&](const float* M, const float* x, float* y) {
-    const int j = tid / NPC, pp = tid % NPC;
-    if (j < DVS) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = pp; i < DK; i += NPC) acc += M[i * LD + j] * x[i];
-      acc = lane_sum<NPC>(acc);
-      if (pp == 0) y[j] = acc;
-    }
-  };
-  // y_i = sum_j M[i][j] x_j over the slice's columns; returns the sum in the
-  // lane with pp == 0 of row i (other lanes: partial), row index via *row.
-  auto rowsum = [&](const float* M, const float* x, int* row) {
-    const int i = tid / NPR, pp = tid % NPR;
-    *row = (i < DK && pp == 0) ? i : -1;
-    float acc = 0.f;
-    if (i < DK) {
-#pragma unroll
-      for (int j = pp; j < DVS; j += NPR) acc += M[i * LD + j] * x[j];
-    }
-    return lane_sum<NPR>(acc);
-  };
+  float S[RPT], G[RPT];
   // Tokens [t0, t1) of the chunk into LDS (q and dout only when wanted).
   auto load_chunk = [&](int t0, int t1, bool with_q) {
     const int n = t1 - t0;
     const size_t row0 = ((size_t)b * T + t0) * H + h;
-    for (int e = tid; e < n * DK; e += BNT) {
+    for (int e = tid; e < n * DK; e += NT) {
       const size_t off = (row0 + (size_t)(e / DK) * H) * DK + e % DK;
       ck[e] = ldin(k + off);
       if (with_q) cq[e] = ldin(q + off);
     }
-    for (int e = tid; e < n * DVS; e += BNT) {
+    for (int e = tid; e < n * DVS; e += NT) {
       const size_t off = (row0 + (size_t)(e / DVS) * H) * DV + col0 + e % DVS;
       cv[e] = ldin(v + off);
       if (with_q) cdo[e] = dout[off];
@@ -143,136 +162,122 @@ __global__ __launch_bounds__(BNT) void gdn_bwd_kernel(
     }
   };
   auto step = [&](int tl) {  // S <- A_t S + beta_t k v^T, token tl of the chunk
-    const float* kv = ck + tl * DK;
-    const float* vv = cv + tl * DVS;
-    __syncthreads();  // chunk inputs loaded, previous update done
-    const float a = ca[tl], be = cb[tl];
-    colsum(S, kv, pv);
-    __syncthreads();
-    for (int e = tid; e < SZ; e += BNT) {
-      const int i = e / DVS, j = e % DVS;
-      S[i * LD + j] = a * (S[i * LD + j] - be * kv[i] * pv[j]) + be * kv[i] * vv[j];
+    const float a = ca[tl], be = cb[tl], vj = cv[tl * DVS + j];
+    float kk[RPT], acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      kk[u] = ck[tl * DK + r0 + u];
+      acc += S[u] * kk[u];
     }
+    const float pj = lane_sum<16>(acc);
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) S[u] = a * (S[u] - be * kk[u] * pj) + be * kk[u] * vj;
   };
   auto save = [&](float* dst) {
-    for (int e = tid; e < SZ; e += BNT) dst[e] = S[(e / DVS) * LD + e % DVS];
-  };
-  auto restore = [&](const float* src) {
-    for (int e = tid; e < SZ; e += BNT) S[(e / DVS) * LD + e % DVS] = src[e];
-  };
-  // Per-wave partial sums of three values into red[par]; read after the
-  // next barrier (red is double-buffered by token parity).
-  auto wave_sum3 = [&](float x0, float x1, float x2, int par) {
-    x0 = lane_sum<64>(x0);
-    x1 = lane_sum<64>(x1);
-    x2 = lane_sum<64>(x2);
-    if (lane == 0) {
-      red[par][wv][0] = x0;
-      red[par][wv][1] = x1;
-      red[par][wv][2] = x2;
-    }
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) dst[u * NT + tid] = S[u];
   };
 
   // Forward sweep: checkpoints.
-  for (int e = tid; e < SZ; e += BNT)
-    S[(e / DVS) * LD + e % DVS] =
-        state_in ? state_in[((size_t)bh * DK + e / DVS) * DV + col0 + e % DVS] : 0.f;
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) S[u] = state_in ? state_in[sbase + (size_t)(r0 + u) * DV] : 0.f;
   for (int c = 0; c < NC; ++c) {
     const int t0 = c * BCK, t1 = min(T, t0 + BCK);
-    __syncthreads();  // previous chunk's last update done
     save(ckpt + (size_t)c * SZ);
+    __syncthreads();  // previous chunk's reads of the chunk buffers done
     load_chunk(t0, t1, false);
+    __syncthreads();
     for (int t = t0; t < t1; ++t) step(t - t0);
   }
 
   // Backward sweep.
-  for (int e = tid; e < SZ; e += BNT)
-    G[(e / DVS) * LD + e % DVS] =
-        dstate_out ? dstate_out[((size_t)bh * DK + e / DVS) * DV + col0 + e % DVS] : 0.f;
+#pragma unroll
+  for (int u = 0; u < RPT; ++u)
+    G[u] = dstate_out ? dstate_out[sbase + (size_t)(r0 + u) * DV] : 0.f;
   for (int c = NC - 1; c >= 0; --c) {
     const int t0 = c * BCK, t1 = min(T, t0 + BCK);
-    __syncthreads();  // previous chunk's last carry done, chunk buffers free
-    restore(ckpt + (size_t)c * SZ);
+    const float* src = ckpt + (size_t)c * SZ;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) S[u] = src[u * NT + tid];
+    __syncthreads();  // previous chunk's reads of the chunk buffers done
     load_chunk(t0, t1, true);
+    __syncthreads();
     for (int t = t0; t < t1; ++t) {
-      __syncthreads();
       save(cbuf + (size_t)(t - t0) * SZ);  // S_{t-1}
       step(t - t0);
     }
     for (int t = t1 - 1; t >= t0; --t) {
-      const int tl = t - t0;
+      const int tl = t - t0, par = t & 1;
       const size_t row = ((size_t)b * T + t) * H + h;
+      float P[RPT];  // S_{t-1}, written by this thread in the recompute loop
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) P[u] = cbuf[(size_t)tl * SZ + u * NT + tid];
       const float a = ca[tl], be = cb[tl];
-      const float* kv = ck + tl * DK;
-      const float* qv = cq + tl * DK;
-      const float* vv = cv + tl * DVS;
-      const float* dov = cdo + tl * DVS;
-      // S_{t-1}, written by this thread in the recompute loop, fetched early.
-      float prev[NPT];
+      const float vj = cv[tl * DVS + j], doj = cdo[tl * DVS + j];
+      float kk[RPT], qq[RPT], rq[RPT], rk[RPT];
+      float gacc = 0.f;
 #pragma unroll
-      for (int u = 0; u < NPT; ++u) {
-        const int e = tid + u * BNT;
-        prev[u] = (e < SZ) ? cbuf[(size_t)tl * SZ + e] : 0.f;
+      for (int u = 0; u < RPT; ++u) {
+        kk[u] = ck[tl * DK + r0 + u];
+        qq[u] = cq[tl * DK + r0 + u];
+        G[u] += scale * qq[u] * doj;  // G_t
+        rq[u] = S[u] * doj;           // S_t do (row sums give dq / scale)
+        gacc += G[u] * kk[u];
       }
-      __syncthreads();  // previous carry done
-      for (int e = tid; e < SZ; e += BNT) {
-        const int i = e / DVS, j = e % DVS;
-        G[i * LD + j] += scale * qv[i] * dov[j];
-      }
-      __syncthreads();
-      int ri;
-      const float dqp = rowsum(S, dov, &ri);  // S_t do (this slice's columns)
-      if (ri >= 0) (NS == 1 ? dq + row * DK : pdq + row * DK)[ri] = scale * dqp;
-      const float gvp = rowsum(G, vv, &ri);
-      if (ri >= 0) Gv[ri] = gvp;
-      colsum(G, kv, gv);
-      __syncthreads();
+      const float gj = lane_sum<16>(gacc);  // (G_t^T k)_j
+      float pacc = 0.f;
 #pragma unroll
-      for (int u = 0; u < NPT; ++u) {  // S <- S_{t-1}
-        const int e = tid + u * BNT;
-        if (e < SZ) S[(e / DVS) * LD + e % DVS] = prev[u];
+      for (int u = 0; u < RPT; ++u) pacc += P[u] * kk[u];
+      const float pj = lane_sum<16>(pacc);  // (S_{t-1}^T k)_j
+      float sA = 0.f;
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) {
+        rk[u] = -a * be * (G[u] * pj + P[u] * gj) + be * G[u] * vj;
+        sA += G[u] * P[u];
       }
-      __syncthreads();
-      colsum(S, kv, pv);
-      const float pg = rowsum(S, gv, &ri);
-      if (ri >= 0) Pg[ri] = pg;
-      float gP = 0.f;
-      for (int e = tid; e < SZ; e += BNT) {
-        const int i = e / DVS, j = e % DVS;
-        gP += G[i * LD + j] * S[i * LD + j];
+      float sB = 0.f;
+      if (pp == 0) {
+        sA -= be * gj * pj;
+        sB = gj * (vj - a * pj);
+        dv[row * DV + col0 + j] = be * gj;
       }
-      __syncthreads();  // pv, Pg ready
-      float gpp = 0.f, gvv = 0.f;
-      if (tid < DVS) {
-        gpp = gv[tid] * pv[tid];
-        gvv = gv[tid] * (vv[tid] - a * pv[tid]);
-        dv[row * DV + col0 + tid] = be * gv[tid];
+      wave_rows_to_lds<RPT>(rq, lane, pp, rowp[par][0][wv]);
+      wave_rows_to_lds<RPT>(rk, lane, pp, rowp[par][1][wv]);
+      sA = lane_sum<64>(sA);
+      sB = lane_sum<64>(sB);
+      if (lane == 0) {
+        scal[par][wv][0] = sA;
+        scal[par][wv][1] = sB;
       }
-      const float gp = rowsum(G, pv, &ri);
-      if (ri >= 0)
-        (NS == 1 ? dk + row * DK : pdk + row * DK)[ri] = -a * be * (gp + Pg[ri]) + be * Gv[ri];
-      wave_sum3(gP, gpp, gvv, t & 1);
-      __syncthreads();  // G reads and wave partials done
-      if (tid == 0) {
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
-        for (int w = 0; w < BNT / 64; ++w) {
-          s0 += red[t & 1][w][0];
-          s1 += red[t & 1][w][1];
-          s2 += red[t & 1][w][2];
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) {
+        G[u] = a * (G[u] - be * kk[u] * gj);  // carry: A_t G_t
+        S[u] = P[u];
+      }
+      __syncthreads();  // wave partials of token t complete
+      if (tid < DK) {
+        float x = 0.f, y = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          x += rowp[par][0][w][tid];
+          y += rowp[par][1][w][tid];
         }
-        (NS == 1 ? dalpha + row : pda + row)[0] = s0 - be * s1;
-        (NS == 1 ? dbeta + row : pdb + row)[0] = s2;
-      }
-      // Carry: G <- A_t G.
-      for (int e = tid; e < SZ; e += BNT) {
-        const int i = e / DVS, j = e % DVS;
-        G[i * LD + j] = a * (G[i * LD + j] - be * kv[i] * gv[j]);
+        (NS == 1 ? dq : pdq)[row * DK + tid] = scale * x;
+        (NS == 1 ? dk : pdk)[row * DK + tid] = y;
+      } else if (tid == DK) {
+        float x = 0.f, y = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          x += scal[par][w][0];
+          y += scal[par][w][1];
+        }
+        (NS == 1 ? dalpha : pda)[row] = x;
+        (NS == 1 ? dbeta : pdb)[row] = y;
       }
     }
   }
-  __syncthreads();
-  for (int e = tid; e < SZ; e += BNT)
-    dstate_in[((size_t)bh * DK + e / DVS) * DV + col0 + e % DVS] = G[(e / DVS) * LD + e % DVS];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) dstate_in[sbase + (size_t)(r0 + u) * DV] = G[u];
 }
 
 // Sums the per-slice partials of dq, dk, dalpha, dbeta (NS slices).
@@ -317,7 +322,7 @@ hipError_t launch_bwd_t(const BwdArgs& p) {
   float* ws = (float*)p.workspace;
   float* part = ws + (size_t)p.B * p.H * NS * (NC + BCK) * DK * DVS;
   const hipStream_t st = (hipStream_t)p.stream;
-  hipLaunchKernelGGL((gdn_bwd_kernel<TIn, DK, DV, DVS>), dim3(p.B * p.H * NS), dim3(BNT), 0, st,
+  hipLaunchKernelGGL((gdn_bwd_kernel<TIn, DK, DV, DVS>), dim3(p.B * p.H * NS), dim3(16 * DVS), 0, st,
                      (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v, p.alpha, p.beta,
                      p.state_in, p.dout, p.dstate_out, p.dq, p.dk, p.dv, p.dalpha, p.dbeta,
                      p.dstate_in, p.T, p.H, p.scale, ws, part);
