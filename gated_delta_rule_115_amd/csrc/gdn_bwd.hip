@@ -29,6 +29,7 @@
 #include <algorithm>
 
 #include "gdn_device.h"
+#include "gdn_f16ops.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -143,22 +144,46 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
 
   float S[RPT], G[RPT];
   // Tokens [t0, t1) of the chunk into LDS (q and dout only when wanted).
+  // Every thread issues a fixed number of loads, all before the first LDS
+  // store; slots past the chunk's last token repeat that token.
+  constexpr int KE = BCK * DK / NT, VE = BCK * DVS / NT;
+  static_assert(KE * NT == BCK * DK && VE * NT == BCK * DVS && BCK <= NT, "chunk staging");
   auto load_chunk = [&](int t0, int t1, bool with_q) {
-    const int n = t1 - t0;
+    const int last = t1 - t0 - 1;
     const size_t row0 = ((size_t)b * T + t0) * H + h;
-    for (int e = tid; e < n * DK; e += NT) {
-      const size_t off = (row0 + (size_t)(e / DK) * H) * DK + e % DK;
-      ck[e] = ldin(k + off);
-      if (with_q) cq[e] = ldin(q + off);
+    float kr[KE], qr[KE], vr[VE], dr[VE];
+#pragma unroll
+    for (int u = 0; u < KE; ++u) {
+      const int e = tid + u * NT;
+      const size_t off = (row0 + (size_t)min(e / DK, last) * H) * DK + e % DK;
+      kr[u] = ldin(k + off);
+      if (with_q) qr[u] = ldin(q + off);
     }
-    for (int e = tid; e < n * DVS; e += NT) {
-      const size_t off = (row0 + (size_t)(e / DVS) * H) * DV + col0 + e % DVS;
-      cv[e] = ldin(v + off);
-      if (with_q) cdo[e] = dout[off];
+#pragma unroll
+    for (int u = 0; u < VE; ++u) {
+      const int e = tid + u * NT;
+      const size_t off = (row0 + (size_t)min(e / DVS, last) * H) * DV + col0 + e % DVS;
+      vr[u] = ldin(v + off);
+      if (with_q) dr[u] = dout[off];
     }
-    if (tid < n) {
-      ca[tid] = alpha[row0 + (size_t)tid * H];
-      cb[tid] = beta[row0 + (size_t)tid * H];
+    float ar = 0.f, br = 0.f;
+    if (tid < BCK) {
+      ar = alpha[row0 + (size_t)min(tid, last) * H];
+      br = beta[row0 + (size_t)min(tid, last) * H];
+    }
+#pragma unroll
+    for (int u = 0; u < KE; ++u) {
+      ck[tid + u * NT] = kr[u];
+      if (with_q) cq[tid + u * NT] = qr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VE; ++u) {
+      cv[tid + u * NT] = vr[u];
+      if (with_q) cdo[tid + u * NT] = dr[u];
+    }
+    if (tid < BCK) {
+      ca[tid] = ar;
+      cb[tid] = br;
     }
   };
   auto step = [&](int tl) {  // S <- A_t S + beta_t k v^T, token tl of the chunk
@@ -169,9 +194,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
       kk[u] = ck[tl * DK + r0 + u];
       acc += S[u] * kk[u];
     }
-    const float pj = lane_sum<16>(acc);
+    // a (S - be k p^T) + be k v^T = a S + k (be (v - a p))^T
+    const float cj = be * (vj - a * lane_sum<16>(acc));
 #pragma unroll
-    for (int u = 0; u < RPT; ++u) S[u] = a * (S[u] - be * kk[u] * pj) + be * kk[u] * vj;
+    for (int u = 0; u < RPT; ++u) S[u] = fmaf(kk[u], cj, a * S[u]);
   };
   auto save = [&](float* dst) {
 #pragma unroll
@@ -184,9 +210,9 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
   for (int c = 0; c < NC; ++c) {
     const int t0 = c * BCK, t1 = min(T, t0 + BCK);
     save(ckpt + (size_t)c * SZ);
-    __syncthreads();  // previous chunk's reads of the chunk buffers done
+    f16ops::lds_barrier();  // previous chunk's reads of the chunk buffers done
     load_chunk(t0, t1, false);
-    __syncthreads();
+    f16ops::lds_barrier();
     for (int t = t0; t < t1; ++t) step(t - t0);
   }
 
@@ -199,41 +225,52 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
     const float* src = ckpt + (size_t)c * SZ;
 #pragma unroll
     for (int u = 0; u < RPT; ++u) S[u] = src[u * NT + tid];
-    __syncthreads();  // previous chunk's reads of the chunk buffers done
+    f16ops::lds_barrier();  // previous chunk's reads of the chunk buffers done
     load_chunk(t0, t1, true);
-    __syncthreads();
+    f16ops::lds_barrier();
     for (int t = t0; t < t1; ++t) {
       save(cbuf + (size_t)(t - t0) * SZ);  // S_{t-1}
       step(t - t0);
     }
+    // S_{t-1} of each token, written by this thread in the recompute loop,
+    // is fetched one token ahead (the barriers below wait on LDS only).
+    float Pn[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) Pn[u] = cbuf[(size_t)(t1 - 1 - t0) * SZ + u * NT + tid];
     for (int t = t1 - 1; t >= t0; --t) {
       const int tl = t - t0, par = t & 1;
       const size_t row = ((size_t)b * T + t) * H + h;
-      float P[RPT];  // S_{t-1}, written by this thread in the recompute loop
+      float P[RPT];
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) P[u] = cbuf[(size_t)tl * SZ + u * NT + tid];
+      for (int u = 0; u < RPT; ++u) {
+        P[u] = Pn[u];  // at the chunk's first token this re-reads that token's slot
+        Pn[u] = cbuf[(size_t)max(tl - 1, 0) * SZ + u * NT + tid];
+      }
       const float a = ca[tl], be = cb[tl];
       const float vj = cv[tl * DVS + j], doj = cdo[tl * DVS + j];
       float kk[RPT], qq[RPT], rq[RPT], rk[RPT];
       float gacc = 0.f;
+      const float sdo = scale * doj;
 #pragma unroll
       for (int u = 0; u < RPT; ++u) {
         kk[u] = ck[tl * DK + r0 + u];
         qq[u] = cq[tl * DK + r0 + u];
-        G[u] += scale * qq[u] * doj;  // G_t
-        rq[u] = S[u] * doj;           // S_t do (row sums give dq / scale)
-        gacc += G[u] * kk[u];
+        G[u] = fmaf(qq[u], sdo, G[u]);  // G_t
+        rq[u] = S[u] * doj;             // S_t do (row sums give dq / scale)
+        gacc = fmaf(G[u], kk[u], gacc);
       }
       const float gj = lane_sum<16>(gacc);  // (G_t^T k)_j
       float pacc = 0.f;
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) pacc += P[u] * kk[u];
+      for (int u = 0; u < RPT; ++u) pacc = fmaf(P[u], kk[u], pacc);
       const float pj = lane_sum<16>(pacc);  // (S_{t-1}^T k)_j
+      // dk row terms: -a be (G p + P g) + be G v = G (be (v - a p)) + P (-a be g)
+      const float c1 = be * (vj - a * pj), c2 = -a * be * gj;
       float sA = 0.f;
 #pragma unroll
       for (int u = 0; u < RPT; ++u) {
-        rk[u] = -a * be * (G[u] * pj + P[u] * gj) + be * G[u] * vj;
-        sA += G[u] * P[u];
+        rk[u] = fmaf(G[u], c1, P[u] * c2);
+        sA = fmaf(G[u], P[u], sA);
       }
       float sB = 0.f;
       if (pp == 0) {
@@ -251,10 +288,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
       }
 #pragma unroll
       for (int u = 0; u < RPT; ++u) {
-        G[u] = a * (G[u] - be * kk[u] * gj);  // carry: A_t G_t
+        G[u] = fmaf(kk[u], c2, a * G[u]);  // carry: A_t G_t = a G - a be k g^T
         S[u] = P[u];
       }
-      __syncthreads();  // wave partials of token t complete
+      f16ops::lds_barrier();  // wave partials of token t complete
       if (tid < DK) {
         float x = 0.f, y = 0.f;
 #pragma unroll
