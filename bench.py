@@ -131,6 +131,8 @@ PROFILE = "profiles/gdn_kernels_bench_workloads.md"
 # combine pass, output pass); its entry sums them.
 PREFILL_KERNELS = "prefill_lead_kernel<bf16> + segment_combine_kernel + prefill_out_kernel<bf16>"
 CHGATE_KERNELS = "chgate_prep_kernel + chgate_recur_kernel (f32)"
+# The backward call launches the adjoint kernel and the slice-partial sum.
+BWD_KERNELS = "gdn_bwd_kernel<bf16,128,128,32> + bwd_reduce_kernel (f32)"
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
@@ -601,10 +603,11 @@ def main():
         inf = infos["backward_t1024"]
         ms = seg_ms[("backward_t1024", "backward")]
         sec = ms / 1e3
-        roof_bwd = dict(bound="alu", kernel="gdn_bwd_kernel (f32)",
+        roof_bwd = dict(bound="alu", kernel=BWD_KERNELS,
                         achieved=inf["alu_flops"] / sec / 1e12,
                         peak=PEAK_F32_VECTOR_FLOPS / 1e12, unit="TFLOP/s",
-                        frac=inf["alu_flops"] / sec / PEAK_F32_VECTOR_FLOPS, traffic=None,
+                        frac=inf["alu_flops"] / sec / PEAK_F32_VECTOR_FLOPS,
+                        traffic=traffic_bytes(BWD_KERNELS),
                         ms_per_launch=ms, flops_per_launch=inf["alu_flops"])
     roof_conv = None
     if "conv_qwen32b" in out_legs:

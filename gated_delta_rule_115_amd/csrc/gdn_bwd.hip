@@ -16,16 +16,14 @@
 // The columns of S and G evolve independently, so one work-group takes one
 // (b, h) and a slice of 32 state columns (16 when Dv = 16) and holds that
 // Dk x 32 part of S and G (f32) in registers, 16 lanes per column.  A forward
-// sweep stores the state entering every chunk of BCK = 32 tokens (the
-// checkpoints); the backward sweep takes the chunks in reverse, recomputes
-// the chunk's states from its checkpoint into a per-work-group buffer, and
-// runs the adjoint over the chunk's tokens in reverse, reading S_{t-1} back
-// from that buffer.  Each thread reads back only what it wrote itself.  The
-// chunk's token inputs are staged in LDS once per chunk.  Gradients that sum
-// over all columns (dq, dk, dalpha, dbeta) are written as per-slice partials
-// and summed in slice order by a second kernel.  All arithmetic is f32; this
-// is the direct form of the adjoint (no chunked rewrite), sequential over
-// tokens.
+// sweep stores the state entering every SUB = 4th token (the checkpoints);
+// the backward sweep takes the tokens in reverse, SUB at a time: it
+// recomputes the states entering those tokens from their checkpoint into
+// registers and runs the adjoint over them.  Token inputs are staged in LDS
+// BCK = 32 tokens at a time.  Gradients that sum over all columns (dq, dk,
+// dalpha, dbeta) are written as per-slice partials and summed in slice order
+// by a second kernel.  All arithmetic is f32; this is the direct form of the
+// adjoint (no chunked rewrite), sequential over tokens.
 #include <algorithm>
 
 #include "gdn_device.h"
@@ -35,7 +33,9 @@
 namespace gdn {
 namespace {
 
-constexpr int BCK = 32;   // tokens per checkpointed chunk
+constexpr int BCK = 32;  // tokens staged in LDS at a time
+constexpr int SUB = 4;  // tokens per checkpoint (states recomputed into registers)
+static_assert(BCK % SUB == 0, "checkpoints fall on sub-chunk starts within a staged chunk");
 
 template <class TIn>
 __device__ __forceinline__ float ldin(const TIn* p) {
@@ -133,8 +133,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int j = tid >> 4, pp = tid & 15, r0 = pp * RPT;
   const int NC = (T + BCK - 1) / BCK;
-  float* ckpt = ws + (size_t)blockIdx.x * (NC + BCK) * SZ;  // NC checkpoints, BCK chunk states
-  float* cbuf = ckpt + (size_t)NC * SZ;
+  float* ckpt = ws + (size_t)blockIdx.x * ((T + SUB - 1) / SUB) * SZ;  // one per SUB tokens
   const size_t BTH = (size_t)gridDim.x / NS * T;  // token-heads
   float* pdq = part + ((size_t)sl * BTH) * DK;
   float* pdk = part + ((size_t)NS * BTH) * DK + ((size_t)sl * BTH) * DK;
@@ -204,112 +203,128 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
     for (int u = 0; u < RPT; ++u) dst[u * NT + tid] = S[u];
   };
 
-  // Forward sweep: checkpoints.
+  // One token of the adjoint, token tl of the staged chunk, with S = S_t and
+  // P = S_{t-1}; leaves G = A_t G_t.
+  auto adjoint = [&](int t, int tl, const float (&P)[RPT]) {
+    const int par = t & 1;
+    const size_t row = ((size_t)b * T + t) * H + h;
+    const float a = ca[tl], be = cb[tl];
+    const float vj = cv[tl * DVS + j], doj = cdo[tl * DVS + j];
+    float kk[RPT], rq[RPT], rk[RPT];
+    float gacc = 0.f;
+    const float sdo = scale * doj;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      kk[u] = ck[tl * DK + r0 + u];
+      G[u] = fmaf(cq[tl * DK + r0 + u], sdo, G[u]);  // G_t
+      rq[u] = S[u] * doj;                            // S_t do (row sums give dq / scale)
+      gacc = fmaf(G[u], kk[u], gacc);
+    }
+    const float gj = lane_sum<16>(gacc);  // (G_t^T k)_j
+    float pacc = 0.f;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) pacc = fmaf(P[u], kk[u], pacc);
+    const float pj = lane_sum<16>(pacc);  // (S_{t-1}^T k)_j
+    // dk row terms: -a be (G p + P g) + be G v = G (be (v - a p)) + P (-a be g)
+    const float c1 = be * (vj - a * pj), c2 = -a * be * gj;
+    float sA = 0.f;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      rk[u] = fmaf(G[u], c1, P[u] * c2);
+      sA = fmaf(G[u], P[u], sA);
+    }
+    float sB = 0.f;
+    if (pp == 0) {
+      sA -= be * gj * pj;
+      sB = gj * (vj - a * pj);
+      dv[row * DV + col0 + j] = be * gj;
+    }
+    wave_rows_to_lds<RPT>(rq, lane, pp, rowp[par][0][wv]);
+    wave_rows_to_lds<RPT>(rk, lane, pp, rowp[par][1][wv]);
+    sA = lane_sum<64>(sA);
+    sB = lane_sum<64>(sB);
+    if (lane == 0) {
+      scal[par][wv][0] = sA;
+      scal[par][wv][1] = sB;
+    }
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) G[u] = fmaf(kk[u], c2, a * G[u]);  // A_t G_t
+    f16ops::lds_barrier();  // wave partials of token t complete
+    if (tid < DK) {
+      float x = 0.f, y = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        x += rowp[par][0][w][tid];
+        y += rowp[par][1][w][tid];
+      }
+      (NS == 1 ? dq : pdq)[row * DK + tid] = scale * x;
+      (NS == 1 ? dk : pdk)[row * DK + tid] = y;
+    } else if (tid == DK) {
+      float x = 0.f, y = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        x += scal[par][w][0];
+        y += scal[par][w][1];
+      }
+      (NS == 1 ? dalpha : pda)[row] = x;
+      (NS == 1 ? dbeta : pdb)[row] = y;
+    }
+  };
+
+  // Forward sweep: the state entering every SUB-th token is checkpointed.
 #pragma unroll
   for (int u = 0; u < RPT; ++u) S[u] = state_in ? state_in[sbase + (size_t)(r0 + u) * DV] : 0.f;
   for (int c = 0; c < NC; ++c) {
     const int t0 = c * BCK, t1 = min(T, t0 + BCK);
-    save(ckpt + (size_t)c * SZ);
     f16ops::lds_barrier();  // previous chunk's reads of the chunk buffers done
     load_chunk(t0, t1, false);
     f16ops::lds_barrier();
-    for (int t = t0; t < t1; ++t) step(t - t0);
+    for (int t = t0; t < t1; ++t) {
+      if (t % SUB == 0) save(ckpt + (size_t)(t / SUB) * SZ);
+      step(t - t0);
+    }
   }
 
-  // Backward sweep.
+  // Backward sweep: chunks of BCK tokens staged in LDS, in reverse; within
+  // a chunk, sub-chunks of SUB tokens in reverse: the states entering the
+  // sub-chunk's tokens are recomputed from its checkpoint into registers
+  // (hist), then the adjoint runs over them.  The checkpoint of the next
+  // sub-chunk is fetched while the current one is processed.
 #pragma unroll
   for (int u = 0; u < RPT; ++u)
     G[u] = dstate_out ? dstate_out[sbase + (size_t)(r0 + u) * DV] : 0.f;
+  const int NCK = (T + SUB - 1) / SUB;
+  float nxt[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) nxt[u] = ckpt[(size_t)max(NCK - 1, 0) * SZ + u * NT + tid];
   for (int c = NC - 1; c >= 0; --c) {
     const int t0 = c * BCK, t1 = min(T, t0 + BCK);
-    const float* src = ckpt + (size_t)c * SZ;
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) S[u] = src[u * NT + tid];
     f16ops::lds_barrier();  // previous chunk's reads of the chunk buffers done
     load_chunk(t0, t1, true);
     f16ops::lds_barrier();
-    for (int t = t0; t < t1; ++t) {
-      save(cbuf + (size_t)(t - t0) * SZ);  // S_{t-1}
-      step(t - t0);
-    }
-    // S_{t-1} of each token, written by this thread in the recompute loop,
-    // is fetched one token ahead (the barriers below wait on LDS only).
-    float Pn[RPT];
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) Pn[u] = cbuf[(size_t)(t1 - 1 - t0) * SZ + u * NT + tid];
-    for (int t = t1 - 1; t >= t0; --t) {
-      const int tl = t - t0, par = t & 1;
-      const size_t row = ((size_t)b * T + t) * H + h;
-      float P[RPT];
+    for (int s0 = t0 + ((t1 - 1 - t0) / SUB) * SUB; s0 >= t0; s0 -= SUB) {
+      const int n = min(SUB, t1 - s0), ci = s0 / SUB;
 #pragma unroll
       for (int u = 0; u < RPT; ++u) {
-        P[u] = Pn[u];  // at the chunk's first token this re-reads that token's slot
-        Pn[u] = cbuf[(size_t)max(tl - 1, 0) * SZ + u * NT + tid];
+        S[u] = nxt[u];
+        nxt[u] = ckpt[(size_t)max(ci - 1, 0) * SZ + u * NT + tid];
       }
-      const float a = ca[tl], be = cb[tl];
-      const float vj = cv[tl * DVS + j], doj = cdo[tl * DVS + j];
-      float kk[RPT], qq[RPT], rq[RPT], rk[RPT];
-      float gacc = 0.f;
-      const float sdo = scale * doj;
+      float hist[SUB][RPT];
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) {
-        kk[u] = ck[tl * DK + r0 + u];
-        qq[u] = cq[tl * DK + r0 + u];
-        G[u] = fmaf(qq[u], sdo, G[u]);  // G_t
-        rq[u] = S[u] * doj;             // S_t do (row sums give dq / scale)
-        gacc = fmaf(G[u], kk[u], gacc);
-      }
-      const float gj = lane_sum<16>(gacc);  // (G_t^T k)_j
-      float pacc = 0.f;
+      for (int i = 0; i < SUB; ++i) {
+        if (i < n) {
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) pacc = fmaf(P[u], kk[u], pacc);
-      const float pj = lane_sum<16>(pacc);  // (S_{t-1}^T k)_j
-      // dk row terms: -a be (G p + P g) + be G v = G (be (v - a p)) + P (-a be g)
-      const float c1 = be * (vj - a * pj), c2 = -a * be * gj;
-      float sA = 0.f;
-#pragma unroll
-      for (int u = 0; u < RPT; ++u) {
-        rk[u] = fmaf(G[u], c1, P[u] * c2);
-        sA = fmaf(G[u], P[u], sA);
-      }
-      float sB = 0.f;
-      if (pp == 0) {
-        sA -= be * gj * pj;
-        sB = gj * (vj - a * pj);
-        dv[row * DV + col0 + j] = be * gj;
-      }
-      wave_rows_to_lds<RPT>(rq, lane, pp, rowp[par][0][wv]);
-      wave_rows_to_lds<RPT>(rk, lane, pp, rowp[par][1][wv]);
-      sA = lane_sum<64>(sA);
-      sB = lane_sum<64>(sB);
-      if (lane == 0) {
-        scal[par][wv][0] = sA;
-        scal[par][wv][1] = sB;
-      }
-#pragma unroll
-      for (int u = 0; u < RPT; ++u) {
-        G[u] = fmaf(kk[u], c2, a * G[u]);  // carry: A_t G_t = a G - a be k g^T
-        S[u] = P[u];
-      }
-      f16ops::lds_barrier();  // wave partials of token t complete
-      if (tid < DK) {
-        float x = 0.f, y = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          x += rowp[par][0][w][tid];
-          y += rowp[par][1][w][tid];
+          for (int u = 0; u < RPT; ++u) hist[i][u] = S[u];
+          step(s0 + i - t0);
         }
-        (NS == 1 ? dq : pdq)[row * DK + tid] = scale * x;
-        (NS == 1 ? dk : pdk)[row * DK + tid] = y;
-      } else if (tid == DK) {
-        float x = 0.f, y = 0.f;
+      }
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          x += scal[par][w][0];
-          y += scal[par][w][1];
+      for (int i = SUB - 1; i >= 0; --i) {
+        if (i < n) {
+          adjoint(s0 + i, s0 + i - t0, hist[i]);
+#pragma unroll
+          for (int u = 0; u < RPT; ++u) S[u] = hist[i][u];
         }
-        (NS == 1 ? dalpha : pda)[row] = x;
-        (NS == 1 ? dbeta : pdb)[row] = y;
       }
     }
   }
@@ -355,9 +370,9 @@ template <class TIn, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& p) {
   constexpr int DVS = DV < kBwdSlice ? DV : kBwdSlice;
   constexpr int NS = DV / DVS;
-  const int NC = (p.T + BCK - 1) / BCK;
+  const int NCK = (p.T + SUB - 1) / SUB;
   float* ws = (float*)p.workspace;
-  float* part = ws + (size_t)p.B * p.H * NS * (NC + BCK) * DK * DVS;
+  float* part = ws + (size_t)p.B * p.H * NS * NCK * DK * DVS;
   const hipStream_t st = (hipStream_t)p.stream;
   hipLaunchKernelGGL((gdn_bwd_kernel<TIn, DK, DV, DVS>), dim3(p.B * p.H * NS), dim3(16 * DVS), 0, st,
                      (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v, p.alpha, p.beta,
@@ -396,9 +411,9 @@ hipError_t launch_bwd_dk(const BwdArgs& p) {
 }  // namespace
 
 size_t backward_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
-  const size_t nc = ((size_t)T + BCK - 1) / BCK;
+  const size_t nck = ((size_t)T + SUB - 1) / SUB;
   const size_t dvs = Dv < kBwdSlice ? Dv : kBwdSlice, ns = Dv / dvs;
-  const size_t ckpt = (size_t)B * H * ns * (nc + BCK) * Dk * dvs;
+  const size_t ckpt = (size_t)B * H * ns * nck * Dk * dvs;
   const size_t part = ns > 1 ? ns * (size_t)B * T * H * (2 * (size_t)Dk + 2) : 0;
   return (ckpt + part) * sizeof(float);
 }

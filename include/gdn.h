@@ -296,9 +296,9 @@ int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const fl
  *   Outputs (f32, caller-owned): dq, dk [B,T,H,Dk], dv [B,T,H,Dv],
  *   dalpha, dbeta [B,T,H], dstate_in [B,H,Dk,Dv].
  *   workspace: gdn_prefill_backward_workspace_bytes(B, T, H, Dk, Dv) bytes,
- *   256-byte aligned (forward-state checkpoints every 32 tokens and one
- *   chunk of recomputed states per head and column slice, plus per-slice
- *   partial sums of dq, dk, dalpha, dbeta when Dv > 32).
+ *   256-byte aligned (the forward state every 4 tokens per head and column
+ *   slice, plus per-slice partial sums of dq, dk, dalpha, dbeta when
+ *   Dv > 32).
  * One work-group per (b, h, slice of 32 state columns), sequential over
  * tokens, f32 arithmetic; a second kernel sums the slices' partials in a
  * fixed order, so results are deterministic.

@@ -245,11 +245,11 @@ def test_chgate_validation():
 def test_backward_validation():
     L = gdn.lib()
     ws = L.gdn_prefill_backward_workspace_bytes(2, 100, 3, 64, 64)
-    # checkpoints and chunk states per (b, h, 32-column slice), then per-slice
+    # the state every 4 tokens per (b, h, 32-column slice), then per-slice
     # partials of dq, dk [B,T,H,Dk] and dalpha, dbeta [B,T,H]
     ns = 64 // 32
-    assert ws == (2 * 3 * ns * (4 + 32) * 64 * 32 + ns * 2 * 100 * 3 * (2 * 64 + 2)) * 4
-    assert L.gdn_prefill_backward_workspace_bytes(1, 10, 1, 16, 16) == (1 + 32) * 16 * 16 * 4
+    assert ws == (2 * 3 * ns * 25 * 64 * 32 + ns * 2 * 100 * 3 * (2 * 64 + 2)) * 4
+    assert L.gdn_prefill_backward_workspace_bytes(1, 10, 1, 16, 16) == 3 * 16 * 16 * 4
     assert L.gdn_prefill_backward_workspace_bytes(2, 100, 3, 100, 64) == 0
 
     def call(**kw):
