@@ -92,7 +92,8 @@ def chgate_bytes(B, T, H, dk, dv, esize=2):
 
 
 # Backward (direct adjoint with recompute) per token-head: the forward state
-# update twice (checkpoint sweep and per-chunk recompute, ~5 dk dv each) and
+# update twice (checkpoint sweep and recompute from the checkpoints, ~5 dk dv
+# each) and
 # the adjoint step (~19 dk dv: G += q do^T, S do, G v, G^T k, P^T k, P g,
 # <G, P>, G p, the carry of G).
 def backward_flops_per_token_head(dk, dv):
@@ -157,6 +158,10 @@ COUNTERS = {
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
         sha1="e6f24fb2117a24e606ce9cb50b818561ee82a6d7",
         fetch_kib=266587 + 723003, write_kib=395306 + 139264, profile=PROFILE),
+    BWD_KERNELS: dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_bwd.hip",
+        sha1="0d97e13eb430339a9cb0feafecd2f4145b0ceb99",
+        fetch_kib=1348886 + 264211, write_kib=2703880 + 132096, profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
