@@ -48,18 +48,31 @@ __device__ __forceinline__ float dpp_mov(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// Value of lane (lane ^ 16): ds_swizzle in bit-mask mode within 32-lane
+// halves (and mask 0x1F, or mask 0, xor mask 0x10).
+__device__ __forceinline__ float xor16(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+// Value of lane (lane ^ 32); a32 = ((lane ^ 32) << 2), computed once.
+__device__ __forceinline__ float xor32(float x, int a32) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_bpermute(a32, __builtin_bit_cast(int, x)));
+}
+
 // Sum over aligned groups of N lanes (N a power of two up to 64); every lane
 // of the group ends with the total.  Within a row of 16 lanes by DPP moves
-// (quad swaps, then half-row and row mirrors), across rows by swizzles.
+// (quad swaps, then half-row and row mirrors), across rows by a swizzle and
+// a permute.
 template <int N>
-__device__ __forceinline__ float lane_sum(float x) {
+__device__ __forceinline__ float lane_sum(float x, int a32 = 0) {
   static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power-of-two lane group");
   if constexpr (N >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]
   if constexpr (N >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]
   if constexpr (N >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
   if constexpr (N >= 16) x += dpp_mov<0x140>(x); // row_mirror
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  if constexpr (N >= 32) x += xor16(x);
+  if constexpr (N >= 64) x += xor32(x, a32);
   return x;
 }
 
@@ -75,7 +88,7 @@ __device__ __forceinline__ float lane_sum(float x) {
 // For R >= 4 it is a reduce-scatter (halving over lane bit 5, then bit 4);
 // each row is written by exactly one lane.
 template <int R>
-__device__ __forceinline__ void wave_rows_to_lds(const float (&x)[R], int lane, int pp,
+__device__ __forceinline__ void wave_rows_to_lds(const float (&x)[R], int lane, int pp, int a32,
                                                  float* dst) {
   const bool b5 = lane & 32, b4 = lane & 16;
   if constexpr (R >= 4) {
@@ -83,23 +96,23 @@ __device__ __forceinline__ void wave_rows_to_lds(const float (&x)[R], int lane, 
 #pragma unroll
     for (int m = 0; m < R / 2; ++m) {
       const float send = b5 ? x[m] : x[m + R / 2];
-      y[m] = (b5 ? x[m + R / 2] : x[m]) + __shfl_xor(send, 32);
+      y[m] = (b5 ? x[m + R / 2] : x[m]) + xor32(send, a32);
     }
 #pragma unroll
     for (int m = 0; m < R / 4; ++m) {
       const float send = b4 ? y[m] : y[m + R / 4];
-      z[m] = (b4 ? y[m + R / 4] : y[m]) + __shfl_xor(send, 16);
+      z[m] = (b4 ? y[m + R / 4] : y[m]) + xor16(send);
     }
     const int u0 = (b5 ? R / 2 : 0) + (b4 ? R / 4 : 0);
 #pragma unroll
     for (int m = 0; m < R / 4; ++m) dst[pp * R + u0 + m] = z[m];
   } else if constexpr (R == 2) {
-    float y = (b5 ? x[1] : x[0]) + __shfl_xor(b5 ? x[0] : x[1], 32);
-    y += __shfl_xor(y, 16);
+    float y = (b5 ? x[1] : x[0]) + xor32(b5 ? x[0] : x[1], a32);
+    y += xor16(y);
     if (!b4) dst[pp * 2 + (b5 ? 1 : 0)] = y;
   } else {
-    float y = x[0] + __shfl_xor(x[0], 32);
-    y += __shfl_xor(y, 16);
+    float y = x[0] + xor32(x[0], a32);
+    y += xor16(y);
     if (lane < 16) dst[pp] = y;
   }
 }
@@ -132,6 +145,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
   const int col0 = sl * DVS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int j = tid >> 4, pp = tid & 15, r0 = pp * RPT;
+  const int a32 = (lane ^ 32) << 2;  // byte address of lane ^ 32 for ds_bpermute
   const int NC = (T + BCK - 1) / BCK;
   float* ckpt = ws + (size_t)blockIdx.x * ((T + SUB - 1) / SUB) * SZ;  // one per SUB tokens
   const size_t BTH = (size_t)gridDim.x / NS * T;  // token-heads
@@ -239,10 +253,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
       sB = gj * (vj - a * pj);
       dv[row * DV + col0 + j] = be * gj;
     }
-    wave_rows_to_lds<RPT>(rq, lane, pp, rowp[par][0][wv]);
-    wave_rows_to_lds<RPT>(rk, lane, pp, rowp[par][1][wv]);
-    sA = lane_sum<64>(sA);
-    sB = lane_sum<64>(sB);
+    wave_rows_to_lds<RPT>(rq, lane, pp, a32, rowp[par][0][wv]);
+    wave_rows_to_lds<RPT>(rk, lane, pp, a32, rowp[par][1][wv]);
+    sA = lane_sum<64>(sA, a32);
+    sB = lane_sum<64>(sB, a32);
     if (lane == 0) {
       scal[par][wv][0] = sA;
       scal[par][wv][1] = sB;
