@@ -199,27 +199,28 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
       cb[tid] = br;
     }
   };
-  auto step = [&](int tl) {  // S <- A_t S + beta_t k v^T, token tl of the chunk
+  // dst <- A_t src + beta_t k v^T for token tl of the chunk (dst may be src).
+  auto step = [&](int tl, const float (&src)[RPT], float (&dst)[RPT]) {
     const float a = ca[tl], be = cb[tl], vj = cv[tl * DVS + j];
     float kk[RPT], acc = 0.f;
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
       kk[u] = ck[tl * DK + r0 + u];
-      acc += S[u] * kk[u];
+      acc += src[u] * kk[u];
     }
     // a (S - be k p^T) + be k v^T = a S + k (be (v - a p))^T
     const float cj = be * (vj - a * lane_sum<16>(acc));
 #pragma unroll
-    for (int u = 0; u < RPT; ++u) S[u] = fmaf(kk[u], cj, a * S[u]);
+    for (int u = 0; u < RPT; ++u) dst[u] = fmaf(kk[u], cj, a * src[u]);
   };
   auto save = [&](float* dst) {
 #pragma unroll
     for (int u = 0; u < RPT; ++u) dst[u * NT + tid] = S[u];
   };
 
-  // One token of the adjoint, token tl of the staged chunk, with S = S_t and
+  // One token of the adjoint, token tl of the staged chunk, with St = S_t and
   // P = S_{t-1}; leaves G = A_t G_t.
-  auto adjoint = [&](int t, int tl, const float (&P)[RPT]) {
+  auto adjoint = [&](int t, int tl, const float (&St)[RPT], const float (&P)[RPT]) {
     const int par = t & 1;
     const size_t row = ((size_t)b * T + t) * H + h;
     const float a = ca[tl], be = cb[tl];
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
     for (int u = 0; u < RPT; ++u) {
       kk[u] = ck[tl * DK + r0 + u];
       G[u] = fmaf(cq[tl * DK + r0 + u], sdo, G[u]);  // G_t
-      rq[u] = S[u] * doj;                            // S_t do (row sums give dq / scale)
+      rq[u] = St[u] * doj;                           // S_t do (row sums give dq / scale)
       gacc = fmaf(G[u], kk[u], gacc);
     }
     const float gj = lane_sum<16>(gacc);  // (G_t^T k)_j
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
     f16ops::lds_barrier();
     for (int t = t0; t < t1; ++t) {
       if (t % SUB == 0) save(ckpt + (size_t)(t / SUB) * SZ);
-      step(t - t0);
+      step(t - t0, S, S);
     }
   }
 
@@ -318,28 +319,18 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
     f16ops::lds_barrier();
     for (int s0 = t0 + ((t1 - 1 - t0) / SUB) * SUB; s0 >= t0; s0 -= SUB) {
       const int n = min(SUB, t1 - s0), ci = s0 / SUB;
+      float hist[SUB + 1][RPT];  // hist[i]: the state entering token s0 + i
 #pragma unroll
       for (int u = 0; u < RPT; ++u) {
-        S[u] = nxt[u];
+        hist[0][u] = nxt[u];
         nxt[u] = ckpt[(size_t)max(ci - 1, 0) * SZ + u * NT + tid];
       }
-      float hist[SUB][RPT];
 #pragma unroll
-      for (int i = 0; i < SUB; ++i) {
-        if (i < n) {
+      for (int i = 0; i < SUB; ++i)
+        if (i < n) step(s0 + i - t0, hist[i], hist[i + 1]);
 #pragma unroll
-          for (int u = 0; u < RPT; ++u) hist[i][u] = S[u];
-          step(s0 + i - t0);
-        }
-      }
-#pragma unroll
-      for (int i = SUB - 1; i >= 0; --i) {
-        if (i < n) {
-          adjoint(s0 + i, s0 + i - t0, hist[i]);
-#pragma unroll
-          for (int u = 0; u < RPT; ++u) S[u] = hist[i][u];
-        }
-      }
+      for (int i = SUB - 1; i >= 0; --i)
+        if (i < n) adjoint(s0 + i, s0 + i - t0, hist[i + 1], hist[i]);
     }
   }
 #pragma unroll
