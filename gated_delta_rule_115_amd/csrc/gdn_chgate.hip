@@ -292,13 +292,17 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     TOut* __restrict__ out, int T, int H, int Dv, int NC, float scale,
     const char* __restrict__ ws) {
   constexpr int GNCT = DVS / 16;     // 16-column tiles of a slice
-  __shared__ float Kd[GC][DK + 1];   // K o e^(Gam_C - Gam)
-  __shared__ float Kg[GC][DK + 1];   // K o e^Gam
-  __shared__ float Qg[GC][DK + 1];   // Q o e^Gam
+  // Row strides: an MFMA operand read as [16 rows by lane][4 columns by
+  // lane group] has a stride of 4 mod 64 words, one read as [4 rows by lane
+  // group][16 columns by lane] a stride of 16 mod 64, so the 64 lanes of a
+  // read fall in 64 distinct banks.
+  __shared__ float Kd[GC][DK + 16];  // K o e^(Gam_C - Gam), read transposed
+  __shared__ float Kg[GC][DK + 4];   // K o e^Gam
+  __shared__ float Qg[GC][DK + 4];   // Q o e^Gam
   __shared__ float Gs[GC][DK + 1];   // cumulative log gates
-  __shared__ float S[DK][DVS + 1];  // state slice
-  __shared__ float Vs[GC][DVS + 1], Us[GC][DVS + 1];
-  __shared__ float Tm[GC][GC + 1], Pm[GC][GC + 1], bet[GC], gC[DK];
+  __shared__ float S[DK][DVS + 16];  // state slice
+  __shared__ float Vs[GC][DVS + 16], Us[GC][DVS + 16];
+  __shared__ float Tm[GC][GC + 4], Pm[GC][GC + 4], bet[GC], gC[DK];
   const int ns = Dv / DVS;
   const int bh = blockIdx.x / ns, sl = blockIdx.x % ns, b = bh / H, h = bh % H;
   const int col0 = sl * DVS;
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     f32x4 qs = zero4();
     if (w < 2 * XT) {
       const int x = w % XT, tr = x / GNCT, tc = x % GNCT;
-      const float(*A)[DK + 1] = w < XT ? Kg : Qg;
+      const float(*A)[DK + 4] = w < XT ? Kg : Qg;
       f32x4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll 4
       for (int kk = 0; kk < DK; kk += 8) {
