@@ -156,8 +156,8 @@ COUNTERS = {
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
-        sha1="e6f24fb2117a24e606ce9cb50b818561ee82a6d7",
-        fetch_kib=266587 + 723003, write_kib=395306 + 139264, profile=PROFILE),
+        sha1="3d36ea53a1014f69370520e7dc7655a81b6e49cb",
+        fetch_kib=266654 + 723003, write_kib=395306 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd.hip",
         sha1="529eac588317f55a2e5ef9fd786f967420c300c7",
