@@ -308,10 +308,12 @@ __global__ __launch_bounds__(512) void gdn_bwd_kernel(
 #pragma unroll
   for (int u = 0; u < RPT; ++u)
     G[u] = dstate_out ? dstate_out[sbase + (size_t)(r0 + u) * DV] : 0.f;
-  const int NCK = (T + SUB - 1) / SUB;
-  float nxt[RPT];
+  const int NCK = (T + SUB - 1) / SUB;  // 0 when T = 0: no checkpoint to read
+  float nxt[RPT] = {};
+  if (NCK > 0) {
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) nxt[u] = ckpt[(size_t)max(NCK - 1, 0) * SZ + u * NT + tid];
+    for (int u = 0; u < RPT; ++u) nxt[u] = ckpt[(size_t)(NCK - 1) * SZ + u * NT + tid];
+  }
   for (int c = NC - 1; c >= 0; --c) {
     const int t0 = c * BCK, t1 = min(T, t0 + BCK);
     f16ops::lds_barrier();  // previous chunk's reads of the chunk buffers done
