@@ -160,8 +160,8 @@ COUNTERS = {
         fetch_kib=266654 + 723003, write_kib=395306 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd.hip",
-        sha1="529eac588317f55a2e5ef9fd786f967420c300c7",
-        fetch_kib=1348693 + 264212, write_kib=2704048 + 132096, profile=PROFILE),
+        sha1="c17595e858a5302d13a5199bfbb3355398e23a48",
+        fetch_kib=1348593 + 264211, write_kib=2703770 + 132096, profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
