@@ -25,11 +25,14 @@ def _grads(x, dout, dst, scale, dtype):
     return g, r
 
 
-# (dtype, B, T, H, Dk, Dv): ragged chunk tails (70 = 2 x 32 + 6), Dk != Dv both
-# ways, one chunk exactly, T = 1, bf16 inputs at d = 128.
+# (dtype, B, T, H, Dk, Dv): ragged tails of the 32-token staging chunks and of
+# the 4-token checkpoint intervals (70 = 2 x 32 + 4 + 2, 99 = 3 x 32 + 3,
+# 131 = 4 x 32 + 3, 33 = 32 + 1, T = 2, T = 1), Dk != Dv both ways, one chunk
+# exactly, one to four 32-column state slices, bf16 inputs at d = 128.
 @pytest.mark.parametrize("dtype,B,T,H,Dk,Dv", [
     ("f32", 2, 70, 2, 32, 32), ("f32", 1, 64, 2, 64, 16), ("f32", 2, 33, 1, 16, 128),
-    ("f32", 1, 32, 2, 128, 128), ("f32", 2, 1, 2, 32, 64), ("bf16", 1, 100, 2, 128, 128)])
+    ("f32", 1, 32, 2, 128, 128), ("f32", 2, 1, 2, 32, 64), ("bf16", 1, 100, 2, 128, 128),
+    ("f32", 1, 99, 2, 64, 64), ("bf16", 2, 131, 2, 128, 64), ("f32", 1, 2, 1, 128, 32)])
 def test_backward_matches_oracle(dtype, B, T, H, Dk, Dv):
     say(f"backward {dtype} B{B} T{T} H{H} Dk{Dk} Dv{Dv}")
     x = synthetic.gdn_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=T + Dk + Dv, state0="randn")
