@@ -64,27 +64,28 @@ __device__ __forceinline__ Raw8<TIn> ld8(const TIn* p) {
   return r;
 }
 template <class TIn>
+__device__ __forceinline__ float at8(const Raw8<TIn>& r, int e) {
+  if constexpr (sizeof(TIn) == 2) return (float)r.v[e];
+  else return e < 4 ? r.a[e] : r.b[e - 4];
+}
+template <class TIn>
 __device__ __forceinline__ void st8(float* d, const Raw8<TIn>& r, bool keep) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float x;
-    if constexpr (sizeof(TIn) == 2) x = (float)r.v[e];
-    else x = e < 4 ? r.a[e] : r.b[e - 4];
-    d[e] = keep ? x : 0.f;
-  }
+  for (int e = 0; e < 8; ++e) d[e] = keep ? at8(r, e) : 0.f;
 }
 
 // The streamed inputs of one chunk for one thread: 8-element pieces of K
-// and Q (row p / (DK / 8)), 4-float pieces of alpha (per-chunk kernel) or of
-// the cumulative log gates (recurrence), 8-element pieces of the value slice
-// and 4-float pieces of the chunk record.
+// and Q (row p / (DK / 8)); in the recurrence also the cumulative log gates
+// of the same 8 channels at that row and at the chunk's last row, an
+// 8-element piece of the value slice and 4-float pieces of the chunk record.
+// (The per-chunk kernel uses the counts only, and 4-float pieces of alpha.)
 template <class TIn, int DK, int NT>
 struct ChunkRegs {
   static constexpr int NKQ = (GC * DK / 8 + NT - 1) / NT;
   static constexpr int NA = (GC * DK / 4 + NT - 1) / NT;
   static constexpr int NR = (int)((kRecFloats / 4 + NT - 1) / NT);
   Raw8<TIn> k[NKQ], q[NKQ], v;
-  f32x4 a[NA], rec[NR];
+  f32x4 g[NKQ][2], gl[NKQ][2], rec[NR];
 };
 
 // Kernel 1: one work-group per (b, h, chunk).
@@ -299,7 +300,6 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
   __shared__ float Kd[GC][DK + 16];  // K o e^(Gam_C - Gam), read transposed
   __shared__ float Kg[GC][DK + 4];   // K o e^Gam
   __shared__ float Qg[GC][DK + 4];   // Q o e^Gam
-  __shared__ float Gs[GC][DK + 1];   // cumulative log gates
   __shared__ float S[DK][DVS + 16];  // state slice
   __shared__ float Vs[GC][DVS + 16], Us[GC][DVS + 16];
   __shared__ float Tm[GC][GC + 4], Pm[GC][GC + 4], bet[GC], gC[DK];
@@ -321,20 +321,20 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
   const size_t tok = (size_t)H * DK;  // elements between tokens (q, k)
   auto fetch = [&](int c) {
     const int t0 = c * GC;
+    const float* gam =
+        reinterpret_cast<const float*>(ws + ((size_t)bh * NC + c) * kRecBytes + kGamOff);
 #pragma unroll
     for (int u = 0; u < R::NKQ; ++u) {
       const int pc = tid + GNTR * u;
       const int r = min(pc / (DK / 8), GC - 1), t = min(t0 + r, T - 1);
-      const size_t off = ((size_t)b * T + t) * tok + (size_t)h * DK + 8 * (pc % (DK / 8));
+      const int c8 = 8 * (pc % (DK / 8));
+      const size_t off = ((size_t)b * T + t) * tok + (size_t)h * DK + c8;
       rg.k[u] = ld8(k + off);
       rg.q[u] = ld8(q + off);
-    }
-    const float* gam =
-        reinterpret_cast<const float*>(ws + ((size_t)bh * NC + c) * kRecBytes + kGamOff);
-#pragma unroll
-    for (int u = 0; u < R::NA; ++u) {
-      const int pc = min(tid + GNTR * u, GC * DK / 4 - 1);
-      rg.a[u] = *reinterpret_cast<const f32x4*>(gam + 4 * pc);
+      rg.g[u][0] = *reinterpret_cast<const f32x4*>(gam + r * DK + c8);
+      rg.g[u][1] = *reinterpret_cast<const f32x4*>(gam + r * DK + c8 + 4);
+      rg.gl[u][0] = *reinterpret_cast<const f32x4*>(gam + (GC - 1) * DK + c8);
+      rg.gl[u][1] = *reinterpret_cast<const f32x4*>(gam + (GC - 1) * DK + c8 + 4);
     }
     {
       const int r = min(tid / (DVS / 8), GC - 1), t = min(t0 + r, T - 1);
@@ -347,6 +347,9 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       rg.rec[u] = *reinterpret_cast<const f32x4*>(rec + 4 * pc);
     }
   };
+  // The gated K and Q of the chunk go to LDS directly: Kg = K o e^Gam,
+  // Qg = Q o e^Gam, Kd = K o e^(Gam_C - Gam), and gC = e^(Gam_C) from the
+  // threads of row 0 (rows past T have K = Q = 0).
   auto stash = [&](int c) {
     const int t0 = c * GC;
 #pragma unroll
@@ -355,17 +358,15 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       if (pc < GC * DK / 8) {
         const int r = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
         const bool in = t0 + r < T;
-        st8(&Kd[r][c8], rg.k[u], in);
-        st8(&Qg[r][c8], rg.q[u], in);
-      }
-    }
 #pragma unroll
-    for (int u = 0; u < R::NA; ++u) {
-      const int pc = tid + GNTR * u;
-      if (pc < GC * DK / 4) {
-        const int r = pc / (DK / 4), c4 = 4 * (pc % (DK / 4));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = rg.a[u][e];
+        for (int e = 0; e < 8; ++e) {
+          const float g = rg.g[u][e / 4][e % 4], gl = rg.gl[u][e / 4][e % 4];
+          const float kk = in ? at8(rg.k[u], e) : 0.f, qq = in ? at8(rg.q[u], e) : 0.f;
+          Kg[r][c8 + e] = kk * __expf(g);
+          Qg[r][c8 + e] = qq * __expf(g);
+          Kd[r][c8 + e] = kk * __expf(gl - g);
+          if (r == 0) gC[c8 + e] = __expf(gl);
+        }
       }
     }
     if (tid < GC * DVS / 8) {
@@ -393,16 +394,6 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     f16ops::lds_barrier();  // the previous chunk is done with every buffer
     stash(c);
     if (c + 1 < NC) fetch(c + 1);
-    f16ops::lds_barrier();
-    if (tid < DK) gC[tid] = __expf(Gs[GC - 1][tid]);
-    f16ops::lds_barrier();
-    for (int e = tid; e < GC * DK; e += GNTR) {
-      const int r = e / DK, ch = e % DK;
-      const float g = Gs[r][ch], kk = Kd[r][ch];
-      Kg[r][ch] = kk * __expf(g);
-      Qg[r][ch] *= __expf(g);
-      Kd[r][ch] = kk * __expf(Gs[GC - 1][ch] - g);
-    }
     f16ops::lds_barrier();
     // The products on f32 MFMA tiles (v_mfma_f32_16x16x4_f32): lane l = 16 g
     // + r supplies row / column r and contraction index 4 k + g of step k, and
