@@ -156,8 +156,8 @@ COUNTERS = {
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
-        sha1="3d36ea53a1014f69370520e7dc7655a81b6e49cb",
-        fetch_kib=266654 + 723003, write_kib=395306 + 139264, profile=PROFILE),
+        sha1="8ab99f4af934583d2fde4d656ae6d716ea539583",
+        fetch_kib=266566 + 723008, write_kib=395293 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd.hip",
         sha1="c17595e858a5302d13a5199bfbb3355398e23a48",
