@@ -131,7 +131,8 @@ PROFILE = "profiles/gdn_kernels_bench_workloads.md"
 # The long32k prefill call launches three kernels (segment transition pass,
 # combine pass, output pass); its entry sums them.
 PREFILL_KERNELS = "prefill_lead_kernel<bf16> + segment_combine_kernel + prefill_out_kernel<bf16>"
-CHGATE_KERNELS = "chgate_prep_kernel + chgate_recur_kernel (f32)"
+CHGATE_KERNELS = ("chgate_prep_kernel (f32) + chgate_recur_kernel (bf16 inputs: f16 MFMA operands, "
+                  "f32 accumulation and state)")
 # The backward call launches the adjoint kernel and the slice-partial sum.
 BWD_KERNELS = "gdn_bwd_kernel<bf16,128,128,32> + bwd_reduce_kernel (f32)"
 COUNTERS = {

@@ -20,8 +20,10 @@
 // gates are.  Kernel 1 (parallel over chunks) forms A, Pm and T = (I + A)^-1;
 // kernel 2 walks the chunks of one (b, h) and value slice (64 columns, or 32
 // when Dv = 32) with S in LDS and
-// forms K S, Q S, T Y, Pm U and K^T U on f32 MFMA tiles.  All arithmetic is
-// f32 (bf16 inputs are widened on load).  Ragged tails are
+// forms K S, Q S, T Y, Pm U and K^T U on MFMA tiles: f32 MFMA for f32
+// inputs; for bf16 inputs f16 operands (converted from the f32 values in LDS)
+// on the 32-deep f16 MFMA with f32 accumulation, S kept in f32.  Kernel 1 is
+// f32 throughout (bf16 inputs are widened on load).  Ragged tails are
 // padded with identity tokens (alpha = 1, beta = 0, q = k = v = 0).
 #include "gdn_f16ops.h"
 #include "gdn_internal.h"
@@ -411,10 +413,27 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       const int x = w % XT, tr = x / GNCT, tc = x % GNCT;
       const float(*A)[DK + 4] = w < XT ? Kg : Qg;
       f32x4 acc0 = zero4(), acc1 = zero4();
+      if constexpr (sizeof(TIn) == 2) {
+        // bf16 inputs: f16 operands on the 32-deep MFMA, f32 accumulation (S
+        // stays f32 in LDS).  Lane slot (lg, jj) of a step takes key
+        // kk + lg + 4 jj in both operands, so both reads are conflict free.
+#pragma unroll
+        for (int kk = 0; kk < DK; kk += 32) {
+          f16ops::h16x8 fa, fb;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            fa[jj] = (f16ops::h16)A[16 * tr + lr][kk + lg + 4 * jj];
+            fb[jj] = (f16ops::h16)S[kk + lg + 4 * jj][16 * tc + lr];
+          }
+          if ((kk / 32) % 2 == 0) acc0 = f16ops::mfma32(fa, fb, acc0);
+          else acc1 = f16ops::mfma32(fa, fb, acc1);
+        }
+      } else {
 #pragma unroll 4
-      for (int kk = 0; kk < DK; kk += 8) {
-        acc0 = mfma(A[16 * tr + lr][kk + lg], S[kk + lg][16 * tc + lr], acc0);
-        acc1 = mfma(A[16 * tr + lr][kk + 4 + lg], S[kk + 4 + lg][16 * tc + lr], acc1);
+        for (int kk = 0; kk < DK; kk += 8) {
+          acc0 = mfma(A[16 * tr + lr][kk + lg], S[kk + lg][16 * tc + lr], acc0);
+          acc1 = mfma(A[16 * tr + lr][kk + 4 + lg], S[kk + 4 + lg][16 * tc + lr], acc1);
+        }
       }
       const f32x4 acc = acc0 + acc1;
       if (w < XT) {
@@ -428,13 +447,31 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       }
     }
     f16ops::lds_barrier();
+    // acc + sum over the chunk's GC = 32 tokens k of fa(k) fb(k), fa / fb this
+    // lane's row / column entries.  bf16 inputs: one 32-deep f16 MFMA, lane
+    // slot (lg, jj) taking token lg + 4 jj in both operands (conflict-free
+    // reads with the strides above); f32 inputs: eight f32 MFMA steps.
+    static_assert(GC == 32, "one 32-deep step per chunk");
+    auto prod_c = [&](auto fa, auto fb, f32x4 acc) {
+      if constexpr (sizeof(TIn) == 2) {
+        f16ops::h16x8 ha, hb;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          ha[jj] = (f16ops::h16)fa(lg + 4 * jj);
+          hb[jj] = (f16ops::h16)fb(lg + 4 * jj);
+        }
+        return f16ops::mfma32(ha, hb, acc);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < GC; kk += 4) acc = mfma(fa(kk + lg), fb(kk + lg), acc);
+        return acc;
+      }
+    };
     // Phase B: U = T Y (waves 0 .. XT-1), into Vs (V is no longer needed).
     if (w < XT) {
       const int tr = w / GNCT, tc = w % GNCT;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kk = 0; kk < GC; kk += 4)
-        acc = mfma(Tm[16 * tr + lr][kk + lg], Us[kk + lg][16 * tc + lr], acc);
+      const f32x4 acc = prod_c([&](int k) { return Tm[16 * tr + lr][k]; },
+                               [&](int k) { return Us[k][16 * tc + lr]; }, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) Vs[16 * tr + 4 * lg + i][16 * tc + lr] = acc[i];
     }
@@ -444,10 +481,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     // waves.
     if (w >= XT && w < 2 * XT) {
       const int x = w - XT, tr = x / GNCT, tc = x % GNCT;
-      f32x4 acc = qs * scale;
-#pragma unroll
-      for (int kk = 0; kk < GC; kk += 4)
-        acc = mfma(Pm[16 * tr + lr][kk + lg], Vs[kk + lg][16 * tc + lr], acc);
+      const f32x4 acc = prod_c([&](int k) { return Pm[16 * tr + lr][k]; },
+                               [&](int k) { return Vs[k][16 * tc + lr]; }, qs * scale);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * tr + 4 * lg + i;
@@ -463,9 +498,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
         const int ch = 16 * sr + 4 * lg + i;
         acc[i] = gC[ch] * S[ch][16 * sc + lr];
       }
-#pragma unroll
-      for (int kk = 0; kk < GC; kk += 4)
-        acc = mfma(Kd[kk + lg][16 * sr + lr], Vs[kk + lg][16 * sc + lr], acc);
+      acc = prod_c([&](int k) { return Kd[k][16 * sr + lr]; },
+                   [&](int k) { return Vs[k][16 * sc + lr]; }, acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[16 * sr + 4 * lg + i][16 * sc + lr] = acc[i];
     }

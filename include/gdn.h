@@ -25,7 +25,9 @@
  *     inputs (f32 results of bf16 inputs; a bf16 output is exactly that f32
  *     result rounded once to nearest-even).  Gates, states and taps are
  *     always f32.  In bf16 mode all arithmetic accumulates in f32 and the
- *     matrix products take bf16 operands; in f32 mode every product is f32.
+ *     matrix products take 16-bit operands (bf16, or f16: bf16 inputs convert
+ *     to f16 exactly, intermediates are rounded to f16); in f32 mode every
+ *     product is f32.
  *   - Token/state pointers must be 16-byte aligned.
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     failed check returns GDN_ERR_INVALID_ARG or GDN_ERR_UNSUPPORTED and
@@ -261,9 +263,11 @@ int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
  *   out_t = scale * S_t^T q_t.
  * gdn_prefill_chunked_chgate: the same call as gdn_prefill_chunked with
  *   alpha [B, T, H, Dk] f32 (every entry in (0, 1]; the prefill works with
- *   log alpha; 16-byte aligned), chunks of 32 tokens, f32 arithmetic
- *   throughout (bf16 inputs are widened).  workspace: gdn_prefill_chgate_workspace_bytes(B, T, H)
- *   bytes, 256-byte aligned.  state_out may alias state_in.  Limits: Dk and
+ *   log alpha; 16-byte aligned), chunks of 32 tokens.  f32 inputs: f32
+ *   arithmetic throughout.  bf16 inputs: the per-chunk pass in f32, the
+ *   recurrence's products with f16 operands and f32 accumulation (state f32).
+ *   workspace: gdn_prefill_chgate_workspace_bytes(B, T, H) bytes, 256-byte
+ *   aligned.  state_out may alias state_in.  Limits: Dk and
  *   Dv in {32, 64, 128}.
  * gdn_decode_step_chgate: the same call as gdn_decode_step with alpha
  *   [B, H, Dk] f32.  Limits as gdn_decode_step.
