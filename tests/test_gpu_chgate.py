@@ -26,12 +26,15 @@ def _ref(x, state_in=None, scale=1.0):
 # (dtype, B, T, H, Dk, Dv, gate_scale): a ragged tail (100 = 3 x 32 + 4), Dk != Dv both
 # ways, T = 1, strong gates (per-channel log-gate ranges up to ~70 within a
 # chunk: midpoint-factored Gram blocks) and very strong ones (ranges past 80:
-# the exact per-element path).
+# the exact per-element path); bf16 inputs (f16 MFMA operands in the
+# recurrence) at every Dk and with 32- and 64-column value slices.
 @pytest.mark.parametrize("dtype,B,T,H,Dk,Dv,gs", [
     ("f32", 2, 100, 2, 32, 32, 0.1), ("f32", 1, 64, 2, 64, 128, 0.1),
     ("f32", 1, 96, 2, 128, 32, 0.1), ("bf16", 2, 130, 3, 128, 128, 0.1),
     ("bf16", 1, 1, 2, 128, 64, 0.1), ("f32", 2, 70, 2, 64, 64, 2.0),
-    ("bf16", 1, 200, 2, 128, 128, 2.0), ("f32", 1, 96, 2, 64, 64, 5.0)])
+    ("bf16", 1, 200, 2, 128, 128, 2.0), ("f32", 1, 96, 2, 64, 64, 5.0),
+    ("bf16", 2, 70, 2, 32, 32, 0.1), ("bf16", 1, 99, 2, 64, 128, 0.1),
+    ("bf16", 1, 64, 2, 128, 32, 2.0)])
 def test_chgate_prefill_matches_oracle(dtype, B, T, H, Dk, Dv, gs):
     say(f"chgate prefill {dtype} B{B} T{T} H{H} Dk{Dk} Dv{Dv} gate {gs}")
     x = synthetic.chgate_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=T + Dk, state0="randn",
