@@ -168,6 +168,11 @@ COUNTERS = {
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
         sha1="92b6d24215239cccaa8a33d420f5e803ae0fe4a5",
         fetch_kib=168115 + 168109 + 168120, write_kib=327681 + 327680 + 327697, profile=PROFILE),
+    # the three projections' decode-time steps together
+    "short_conv_step_kernel<bf16,bf16,4> (x3)": dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
+        sha1="92b6d24215239cccaa8a33d420f5e803ae0fe4a5",
+        fetch_kib=5480 + 5478 + 5476, write_kib=10240 + 10240 + 10240, profile=PROFILE),
 }
 READ_FACTOR, WRITE_FACTOR = 2.00, 1.00
 
