@@ -157,8 +157,8 @@ COUNTERS = {
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
-        sha1="121e4f228a5d971501523d15a779a40d4f342fc7",
-        fetch_kib=266456 + 723012, write_kib=395305 + 139264, profile=PROFILE),
+        sha1="594fa98533bc44fd3a33a244b72a8ae641e225c5",
+        fetch_kib=264713 + 723012, write_kib=395282 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd.hip",
         sha1="c17595e858a5302d13a5199bfbb3355398e23a48",
