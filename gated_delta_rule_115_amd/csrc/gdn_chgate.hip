@@ -101,7 +101,8 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     const float* __restrict__ beta, int T, int H, int NC, float scale, char* __restrict__ ws,
     int total) {
   __shared__ float Ks[GC][DK + 1], Qs[GC][DK + 1], Gs[GC][DK + 1], Ki[GC][DK + 1];
-  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], Rb[GC][GC + 1], bet[GC], rng[DK];
+  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], bet[GC], rng[DK];
+  __shared__ __align__(16) float Iv[2][f16ops::kInvScratch];
   const int tid = threadIdx.x;
   typedef ChunkRegs<TIn, DK, GNT> R;
   Raw8<TIn> kr[R::NKQ], qr[R::NKQ];
@@ -231,66 +232,43 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
       }
     }
     f16ops::lds_barrier();
-    // T = (I + A)^-1 for the strictly lower A (A^32 = 0) in product form,
-    //   T = (I - A)(I + A^2)(I + A^4)(I + A^8)(I + A^16),
-    // from four squarings and four products on f32 MFMA tiles (wave w: output
-    // tile (w / 2, w % 2)).  The powers use LDS the Gram blocks are done with.
+    // T = (I + A)^-1 by 16-row blocks, all in f32: the diagonal blocks by
+    // forward substitution (inv16; waves 0 and 1), then T10 = -T11 A10 T00 on
+    // f32 MFMA tiles (wave 2).  The product form (I - A)(I + A^2)...(I + A^16)
+    // is not used: with keys clustered around one direction the powers of A
+    // reach 1e2..1e7 and cancel.
     {
       const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-      const int tr = w >> 1, tc = w & 1;
-      constexpr int LD = GC + 1;
-      float* P2 = &Ks[0][0];
-      float* P4 = &Qs[0][0];
-      float* P8 = &Ki[0][0];
-      float* P16 = &Gs[0][0];
-      // Z = X Y (32 x 32), tile of this wave in accumulator layout, plus C.
-      auto prod = [&](const float* X, const float* Y, f32x4 acc) {
+      if (w < 2) {
+        const int o = 16 * w;
+        f32x4 LT, Td, TTd;
 #pragma unroll
-        for (int kk = 0; kk < GC; kk += 4)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
-              X[(16 * tr + lr) * LD + kk + lg], Y[(kk + lg) * LD + 16 * tc + lr], acc, 0, 0, 0);
-        return acc;
-      };
-      auto put = [&](float* Z, f32x4 acc) {
+        for (int j = 0; j < 4; ++j) LT[j] = As[o + lr][o + 4 * lg + j];  // L[lr][4 lg + j]
+        f16ops::inv16(LT, lr, lg, Iv[w], Td, TTd);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Z[(16 * tr + 4 * lg + i) * LD + 16 * tc + lr] = acc[i];
-      };
-      auto get = [&](const float* Z) {
-        f32x4 acc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = Z[(16 * tr + 4 * lg + i) * LD + 16 * tc + lr];
-        return acc;
-      };
-      const float* N = &As[0][0];
-      put(P2, prod(N, N, zero4()));
-      f16ops::lds_barrier();
-      put(P4, prod(P2, P2, zero4()));
-      f16ops::lds_barrier();
-      put(P8, prod(P4, P4, zero4()));
-      f16ops::lds_barrier();
-      put(P16, prod(P8, P8, zero4()));
-      // R = I - A
-      f32x4 id;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * tr + 4 * lg + i, c = 16 * tc + lr;
-        id[i] = (r == c ? 1.f : 0.f) - As[r][c];
+        for (int j = 0; j < 4; ++j) {
+          Ts[o + 4 * lg + j][o + lr] = Td[j];
+          if (w == 0) Ts[4 * lg + j][16 + lr] = 0.f;
+        }
       }
-      put(&Ts[0][0], id);
       f16ops::lds_barrier();
-      // R <- R + R P for P = A^2, A^4, A^8, A^16 (ping-pong between Ts and Rb).
-      float* R0 = &Ts[0][0];
-      float* R1 = &Rb[0][0];
-      const float* pw[4] = {P2, P4, P8, P16};
+      if (w == 2) {
+        float* Xs = &Qs[0][0];  // X = A10 T00, [row][column], row stride GC + 1
+        f32x4 X = zero4();
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        put(R1, prod(R0, pw[s2], get(R0)));
-        f16ops::lds_barrier();
-        float* tmp = R0;
-        R0 = R1;
-        R1 = tmp;
+        for (int kk = 0; kk < 16; kk += 4)
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(As[16 + lr][kk + lg], Ts[kk + lg][lr], X, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Xs[(4 * lg + j) * (GC + 1) + lr] = X[j];
+        f32x4 Y = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 4)
+          Y = __builtin_amdgcn_mfma_f32_16x16x4f32(Ts[16 + lr][16 + kk + lg],
+                                                   Xs[(kk + lg) * (GC + 1) + lr], Y, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Ts[16 + 4 * lg + j][lr] = -Y[j];
       }
-      // The result is in R0 (Ts after an even number of swaps).
+      f16ops::lds_barrier();
     }
     for (int e = tid; e < GC * GC; e += GNT) Tg[e] = Ts[e / GC][e % GC];
     if (tid < GC) Bg[tid] = bet[tid];

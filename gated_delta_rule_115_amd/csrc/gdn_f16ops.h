@@ -92,38 +92,85 @@ __device__ __forceinline__ float wave_incl_sum(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(z, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
   return x;
 }
-__device__ __forceinline__ f32x4 ident4(int lr, int lq) {
-  f32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (4 * lq + i == lr) ? 1.f : 0.f;
-  return r;
+// Lane group p's value (16 lanes) broadcast to every lane group, same lane
+// within the group.  v_permlane16_swap exchanges odd rows of its first
+// operand with even rows of its second (with both = x: {x0, x0, x2, x2} and
+// {x1, x1, x3, x3}); v_permlane32_swap exchanges the upper half of the first
+// with the lower half of the second (with both = s: {s0, s1, s0, s1} and
+// {s2, s3, s2, s3}).
+template <int P>
+__device__ __forceinline__ float bcast_group(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned s = (P & 1) ? a[1] : a[0];
+  const auto b = __builtin_amdgcn_permlane32_swap(s, s, false, false);
+  return __builtin_bit_cast(float, (P & 2) ? b[1] : b[0]);
 }
 
-// (I + L)^-1 for a strictly lower 16x16 L (L^16 = 0), from D(L) and D(L^T):
-// T = D(Tm), TT = D(Tm^T), each as (I + L^8)(I + L^4)(I + L^2)(I - L) applied
-// from the left to the running product.
-template <bool NT, bool NTT>
-__device__ __forceinline__ void inv16(f32x4 Lf, f32x4 LTf, int lr, int lq, f32x4& T, f32x4& TT) {
-  const h16x4 lo = cvt4(Lf), lt = cvt4(LTf);
-  const h16x4 l2 = cvt4(mfma16(lt, lo, zero4()));    // D(L^2)
-  const h16x4 l2t = cvt4(mfma16(lo, lt, zero4()));   // D((L^2)^T)
-  const h16x4 l4 = cvt4(mfma16(l2t, l2, zero4()));   // D(L^4)
-  const h16x4 l4t = cvt4(mfma16(l2, l2t, zero4()));  // D((L^4)^T)
-  const f32x4 id = ident4(lr, lq);
-  if (NT) {
-    const h16x4 l8t = cvt4(mfma16(l4, l4t, zero4()));  // D((L^8)^T)
-    f32x4 X = id - Lf;
-    X = mfma16(l2t, cvt4(X), X);
-    X = mfma16(l4t, cvt4(X), X);
-    T = mfma16(l8t, cvt4(X), X);
-  }
-  if (NTT) {
-    const h16x4 l8 = cvt4(mfma16(l4t, l4, zero4()));  // D(L^8)
-    f32x4 X = id - LTf;
-    X = mfma16(l2, cvt4(X), X);
-    X = mfma16(l4, cvt4(X), X);
-    TT = mfma16(l8, cvt4(X), X);
-  }
+// LDS scratch of inv16 per wave (floats): L row-major and the solution
+// column-major, 16 x 16 f32 each with a row stride of 20 floats (the reads
+// then touch distinct banks).
+constexpr int kInvLd = 20;
+constexpr int kInvScratch = 2 * 16 * kInvLd;
+
+// T = (I + L)^-1 for a strictly lower 16x16 L, by forward substitution in
+// f32.  The product form (I + L^8)(I + L^4)(I + L^2)(I - L) is not used: when
+// keys cluster around one direction the powers of L grow to hundreds or
+// thousands and cancel, and their rounding swamps T.  In: D(L^T) (the
+// accumulator layout of L^T).  Out: D(T), D(T^T) (f32).  scr: this wave's LDS
+// scratch, kInvScratch floats, 16-byte aligned, used by no other wave.
+// Lane (lq, lr) solves rows 4 lq .. 4 lq + 3 of column lr of (I + L) T = I,
+// in four steps over row blocks p = 0..3: block p is final once it has
+// taken its 4 x 4 diagonal solve; it is broadcast across the lane groups
+// (cross-lane swaps), and every later block subtracts L[its rows][4 p ..
+// 4 p + 3] times it.  T then goes through the scratch column-major, from
+// which D(T^T) is read.
+__device__ __forceinline__ void inv16(f32x4 LTf, int lr, int lq, float* scr, f32x4& T, f32x4& TT) {
+  float* Lm = scr;                // Lm[r][i] = L[r][i]
+  float* Xc = scr + 16 * kInvLd;  // Xc[c][r] = T[r][c]
+  // Lane (lq, lr) holds L^T[4 lq + j][lr] = L[lr][4 lq + j], j = 0..3.
+  *reinterpret_cast<f32x4*>(Lm + kInvLd * lr + 4 * lq) = LTf;
+  f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = (4 * lq + j == lr) ? 1.f : 0.f;
+  // L[4 lq + j][4 p .. 4 p + 3] for j = 0..3.
+  auto lblk = [&](int p, f32x4* m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = *reinterpret_cast<const f32x4*>(Lm + kInvLd * (4 * lq + j) + 4 * p);
+  };
+  f32x4 m[4][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) lblk(p, m[p]);
+  auto step = [&](auto P) {
+    constexpr int p = decltype(P)::value;
+    if (lq == p) {
+      // 4 x 4 diagonal block: x_j -= sum_{i < j} L[4 p + j][4 p + i] x_i.
+#pragma unroll
+      for (int j = 1; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < j; ++i) x[j] = __builtin_fmaf(-m[p][j][i], x[i], x[j]);
+    }
+    if constexpr (p < 3) {
+      // Rows of later blocks: x_j -= sum_i L[4 lq + j][4 p + i] T[4 p + i][lr].
+      f32x4 xp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xp[i] = bcast_group<p>(x[i]);
+      if (lq > p) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[j] = __builtin_fmaf(-m[p][j][i], xp[i], x[j]);
+      }
+    }
+  };
+  step(ic<0>());
+  step(ic<1>());
+  step(ic<2>());
+  step(ic<3>());
+  T = x;  // T[4 lq + j][lr]
+  *reinterpret_cast<f32x4*>(Xc + kInvLd * lr + 4 * lq) = x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) TT[j] = Xc[kInvLd * (4 * lq + j) + lr];  // T[lr][4 lq + j]
 }
 
 // Off-diagonal blocks of the unit lower triangular Tm = (I + A)^-1 of a

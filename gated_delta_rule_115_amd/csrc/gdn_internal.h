@@ -66,11 +66,10 @@ struct SwaArgs {
 //   gam   [C]     f32: cumulative log gate within the chunk
 // Records are padded to 256 bytes.
 size_t prefill_record_bytes(int chunk, bool bf16);
-// Workspace of the prefill for these sizes: 0 when the single-pass kernel
-// handles them (bf16 inputs, Dk = 128, chunk 64, Dv a multiple of 16, T > 0).
+// Workspace of the prefill for these sizes: per-chunk records of the
+// two-kernel form, or the segment maps of the per-head kernels (0 when they
+// run in one pass).
 size_t prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, bool bf16);
-bool prefill_fused_supported(const PrefillArgs& p);
-hipError_t launch_prefill_fused(const PrefillArgs& p);
 // Per-head kernels: bf16 inputs, Dk = Dv = 128, chunk 64, T > 0.  Long
 // sequences of few heads are split into P segments: segment 0 of L0 chunks,
 // the others of L (the last may be shorter); P = 1: one pass, no workspace.

@@ -20,9 +20,9 @@
 // evolve independently, so kernel 2 splits Dv into slices of DVS columns, one
 // work-group each, to put enough work-groups on the chip.
 //
-// This two-kernel form serves the shapes the single-pass kernel
-// (gdn_prefill_fused.hip) does not: f32 inputs, head dimensions other than
-// Dk = 128, chunks of 16 or 32 tokens.
+// This two-kernel form serves the shapes the per-head kernels
+// (gdn_prefill_head.hip) do not: f32 inputs, head dimensions other than
+// Dk = Dv = 128, chunks of 16 or 32 tokens.
 //
 // Ragged tails: the last chunk is padded with identity tokens (alpha = 1,
 // beta = 0, q = k = v = 0), which leave S unchanged and read 0.
@@ -49,7 +49,6 @@ size_t prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C, bool 
   PrefillArgs p{};
   p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = C; p.bf16 = bf16;
   if (prefill_head_supported(p)) return prefill_head_workspace_bytes(B, T, H);
-  if (prefill_fused_supported(p)) return 0;
   const size_t nc = ((size_t)T + C - 1) / C;
   return (size_t)B * H * nc * prefill_record_bytes(C, bf16);
 }
@@ -651,7 +650,6 @@ hipError_t launch_prefill(const PrefillArgs& p) {
   if (prefill_head_supported(p)) return launch_prefill_head(p);
   // The other kernels address dense [B, T, ...] tensors.
   if (p.T > 0 && p.B > 1 && p.seq_stride > 0 && p.seq_stride != p.T) return hipErrorInvalidValue;
-  if (prefill_fused_supported(p)) return launch_prefill_fused(p);
   return p.bf16 ? launch_prefill_c<bf16>(p) : launch_prefill_c<float>(p);
 }
 

@@ -34,9 +34,9 @@
 // stages (tile to LDS, Gram blocks and diagonal inverses, Tm off-diagonal
 // blocks, recurrence step) in successive iterations, so the stages of
 // different chunks run side by side between two work-group barriers.  The
-// diagonal blocks are inverted as (I + L)^-1 = (I + L^8)(I + L^4)(I + L^2)
-// (I - L); the off-diagonal blocks of Tm follow by block forward
-// substitution.  Global loads are inline asm issued one or two iterations
+// diagonal 16 x 16 blocks of Tm are inverted by forward substitution in f32
+// (rounded to f16 once formed); the off-diagonal blocks follow by block
+// forward substitution.  Global loads are inline asm issued one or two iterations
 // ahead of their use in a fixed order per iteration, so every wait is a
 // fixed vmcnt and loads stay in flight across the loop back-edge.
 //
@@ -123,6 +123,7 @@ struct __align__(16) HSmem {
   h16x4 Dg[7][64];       // D(T00), D(T00^T), D(T11), D(T11^T), D(T22), D(T22^T), D(T33^T)
   h16x4 Pb[6][64][2];    // P operands per (row tile, 32-token step); halves = block columns
   HGate g[3];            // slot = chunk % 3
+  float Iv[4][kInvScratch];  // inverse scratch of helper waves 4-7
 };
 
 // Slot of P block (R, C) in Pb: row tile R, 32-token step C / 2.
@@ -291,6 +292,7 @@ struct __align__(16) TSmem {
   h16x4 Ab[2][6][64];    // A10, A20, A21, A30, A31, A32 as A operands, slot = chunk % 2
   h16x4 Dg[2][7][64];    // D(T00), D(T00^T), D(T11), D(T11^T), D(T22), D(T22^T), D(T33^T)
   HGate g[4];            // slot = chunk % 4
+  float Iv[4][kInvScratch];  // inverse scratch of waves 0-3
 };
 
 // Transition pass of one segment (chunks c0 .. c0 + NC - 1 of head (b, h)):
@@ -521,12 +523,11 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
           }
           f32x4 Lb, LT, Tt, TT;
           a_diag(gs, wide, w, G, llr, llq, Lb, LT);
+          inv16(LT, llr, llq, sm.Iv[w], Tt, TT);
           if (w < 3) {
-            inv16<true, true>(Lb, LT, llr, llq, Tt, TT);
             sm.Dg[c1 & 1][2 * w][ll] = cvt4(Tt);
             sm.Dg[c1 & 1][2 * w + 1][ll] = cvt4(TT);
           } else {
-            inv16<false, true>(Lb, LT, llr, llq, Tt, TT);
             sm.Dg[c1 & 1][6][ll] = cvt4(TT);
           }
         }
@@ -941,12 +942,11 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
         }
         f32x4 Lb, LT, Tt, TT;
         a_diag(gs, wide, hw, G, lr, lq, Lb, LT);
+        inv16(LT, lr, lq, sm.Iv[hw], Tt, TT);
         if (hw < 3) {
-          inv16<true, true>(Lb, LT, lr, lq, Tt, TT);
           sm.Dg[2 * hw][l] = cvt4(Tt);
           sm.Dg[2 * hw + 1][l] = cvt4(TT);
         } else {
-          inv16<false, true>(Lb, LT, lr, lq, Tt, TT);
           sm.Dg[6][l] = cvt4(TT);
         }
       }

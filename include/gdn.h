@@ -25,8 +25,9 @@
  *     inputs (f32 results of bf16 inputs; a bf16 output is exactly that f32
  *     result rounded once to nearest-even).  Gates, states and taps are
  *     always f32.  In bf16 mode all arithmetic accumulates in f32 and the
- *     matrix products take 16-bit operands (bf16, or f16: bf16 inputs convert
- *     to f16 exactly, intermediates are rounded to f16); in f32 mode every
+ *     matrix products take 16-bit operands (bf16, or f16: bf16 values convert
+ *     to f16 exactly when their magnitude lies in f16's normal range,
+ *     2^-14 .. 65504, intermediates are rounded to f16); in f32 mode every
  *     product is f32.
  *   - Token/state pointers must be 16-byte aligned.
  *   - Arguments are validated on the host before anything is enqueued.  A
@@ -36,7 +37,14 @@
  *     inside a kernel surface at the caller's next synchronisation.
  *   - Data-dependent preconditions are documented, not checked: alpha in
  *     (0, 1], beta in [0, 1], q and k of moderate norm (the workloads
- *     L2-normalise them per token).
+ *     L2-normalise them per token).  In bf16 mode the prefills' products
+ *     take f16 operands, so v, the state and the chunk intermediates must
+ *     stay below 65504 in magnitude: a value beyond it becomes +-inf in its
+ *     operand and the outputs are not finite (q and k convert rounding
+ *     toward zero and clip at +-65504 instead); magnitudes below 2^-14 keep
+ *     fewer bits.  With unit-norm keys and beta in [0, 1] the erase keeps
+ *     every state entry within the sum of the |beta v| written into it.  The
+ *     decode steps and the f32 mode have no such limit.
  *   - Calls are thread-safe; there is no mutable global state besides the
  *     per-thread error message.
  */
@@ -72,7 +80,6 @@ const char* gdn_last_error(void);
  *     is split into P segments, and the workspace holds, per head, the f32
  *     128 x 128 state maps of the first P - 1 segments and their initial
  *     states (3 (P - 1) x 64 KiB).
- *   - bf16 inputs, Dk = 128, Dv < 128, chunk = 64: 0 (single pass).
  *   - otherwise: per chunk of `chunk` tokens, the chunk's triangular-solve
  *     matrix, its decay-masked query-key products and its cumulative log
  *     gates.

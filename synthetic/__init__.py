@@ -14,6 +14,11 @@ Recipe (per (token, head) unless stated):
   beta  = sigmoid(N(0, 1))                      float32, in (0, 1)
   alpha = exp(-softplus(N(0, 1)) * 0.1)         float32, in (~0.6, 1)
   S0    = 0, or N(0, 1) / sqrt(Dk) per element  float32 [B, H, Dk, Dv]
+Concentrated keys (key_cos = c): each head draws one unit direction mu, and
+every key is c mu + sqrt(1 - c^2) z with z a random unit vector orthogonal to
+mu, so cos(k_t, mu) = c and the running mean key points along mu (the key
+concentration of appendix B.1, Metric 1); beta_shift b draws beta =
+sigmoid(N(0, 1) + b) (b > 0 pushes the step sizes towards 1).
 Short-convolution inputs: raw q, k, v ~ N(0, 1) and taps ~ N(0, 0.5^2).
 Sliding-window inputs: raw q and k/v cache ~ N(0, 1) (logits ~ N(0, 1)).
 """
@@ -59,10 +64,21 @@ def _unit(x):
     return x / (torch.linalg.vector_norm(x, dim=-1, keepdim=True) + 1e-6)
 
 
+def concentrated_unit(x, cos, g, device):
+    """Unit vectors along the last axis of x's shape [B, T, H, D] at cosine
+    `cos` to one random unit direction per (batch, head)."""
+    B, T, H, D = x.shape
+    mu = _unit(_randn((B, 1, H, D), g, device))
+    z = x - (x * mu).sum(-1, keepdim=True) * mu
+    z = z / torch.linalg.vector_norm(z, dim=-1, keepdim=True)
+    return cos * mu + math.sqrt(max(0.0, 1.0 - cos * cos)) * z
+
+
 def gdn_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, state0="zero",
-               normalise_qk=True, device="cpu"):
+               normalise_qk=True, key_cos=None, beta_shift=0.0, device="cpu"):
     """q, k [B,T,H,Dk], v [B,T,H,Dv] in `dtype`; alpha, beta [B,T,H] f32;
-    state0 [B,H,Dk,Dv] f32 or None."""
+    state0 [B,H,Dk,Dv] f32 or None.  key_cos: keys concentrated around a
+    per-head direction at that cosine (see the module docstring)."""
     g = _gen(seed, device)
     dt = TORCH_DTYPE[dtype]
     q = _randn((B, T, H, Dk), g, device)
@@ -70,22 +86,25 @@ def gdn_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, state0="zero",
     if normalise_qk:
         q, k = _unit(q), _unit(k)
     v = _randn((B, T, H, Dv), g, device)
-    beta = torch.sigmoid(_randn((B, T, H), g, device))
+    beta = torch.sigmoid(_randn((B, T, H), g, device) + beta_shift)
     alpha = torch.exp(-torch.nn.functional.softplus(_randn((B, T, H), g, device)) * 0.1)
     s0 = None
     if state0 == "randn":
         s0 = _randn((B, H, Dk, Dv), g, device) / math.sqrt(Dk)
+    if key_cos is not None:
+        k = _unit(concentrated_unit(k, float(key_cos), _gen(seed + 104729, device), device))
     return dict(q=q.to(dt).contiguous(), k=k.to(dt).contiguous(),
                 v=v.to(dt).contiguous(), alpha=alpha.contiguous(),
                 beta=beta.contiguous(), state0=s0)
 
 
 def chgate_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, state0="zero", gate_scale=0.1,
-                  device="cpu"):
+                  key_cos=None, beta_shift=0.0, device="cpu"):
     """gdn_inputs with a channel-wise gate: alpha [B,T,H,Dk] f32, each entry
     exp(-gate_scale * softplus(N(0,1))) (the scalar gate's distribution per
     channel)."""
-    x = gdn_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=seed, state0=state0, device=device)
+    x = gdn_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=seed, state0=state0, key_cos=key_cos,
+                   beta_shift=beta_shift, device=device)
     g = _gen(seed + 7919, device)
     x["alpha"] = torch.exp(-torch.nn.functional.softplus(_randn((B, T, H, Dk), g, device))
                            * gate_scale).contiguous()

@@ -84,9 +84,11 @@ def test_prefill_empty_batch_is_ok_without_gpu():
 
 def test_workspace_bytes():
     f = gdn.gdn_prefill_workspace_bytes
-    # bf16, Dk = 128, chunk 64: single pass, no workspace at any Dv
-    for dv in (16, 32, 64, 128):
-        assert f(2, 65, 3, 128, dv, 64, BF16) == 0
+    # bf16, Dk = Dv = 128, chunk 64: the per-head kernels in one pass, no workspace
+    assert f(2, 65, 3, 128, 128, 64, BF16) == 0
+    # bf16, Dk = 128, Dv < 128: the two-kernel form's per-chunk records
+    for dv in (16, 32, 64):
+        assert f(2, 65, 3, 128, dv, 64, BF16) == 2 * 3 * 2 * (2 * 64 * 64 * 2 + 256)
     # otherwise, per chunk: two C x C operand matrices + C f32 log gates,
     # padded to 256 B
     assert f(1, 64, 1, 128, 128, 32, BF16) == 2 * (2 * 32 * 32 * 2 + 256)

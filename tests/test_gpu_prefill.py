@@ -78,10 +78,11 @@ def test_prefill_matches_oracle(dtype, B, T, H, Dk, Dv, chunk):
     (1, 1000, 3, 128, "randn"),   # 16 chunks, ragged tail
     (3, 257, 4, 16, "zero"),
 ])
-def test_single_pass_prefill_matches_oracle(B, T, H, Dv, state0):
-    """bf16 inputs, Dk = 128, chunk 64: the single-pass kernel (no workspace)."""
-    say(f"single-pass prefill B={B} T={T} H={H} Dv={Dv} S0={state0}")
-    assert gdn.gdn_prefill_workspace_bytes(B, T, H, 128, Dv, 64) == 0
+def test_bf16_dk128_prefill_matches_oracle(B, T, H, Dv, state0):
+    """bf16 inputs, Dk = 128, chunk 64: the per-head kernel in one pass (no
+    workspace) for Dv = 128, the two-kernel form for narrower values."""
+    say(f"bf16 Dk128 prefill B={B} T={T} H={H} Dv={Dv} S0={state0}")
+    assert (gdn.gdn_prefill_workspace_bytes(B, T, H, 128, Dv, 64) == 0) == (Dv == 128)
     x = synthetic.gdn_inputs(B, T, H, 128, Dv, dtype="bf16", seed=T * 7 + Dv,
                              state0=state0)
     o, s = _run(x, 64, scale=0.9)
