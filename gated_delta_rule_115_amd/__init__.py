@@ -28,7 +28,8 @@ __all__ = [
     "gdn_swa_sink_decode", "gdn_swa_sink_prefill", "gdn_swa_cache_fill",
     "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
     "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
-    "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward", "EXPORTED_SYMBOLS",
+    "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward",
+    "gdn_prefill_chunked_noalloc", "GDN_NOALLOC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
 ]
 
 GDN_BF16 = 0
@@ -44,7 +45,11 @@ EXPORTED_SYMBOLS = (
     "gdn_swa_cache_fill", "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
     "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
     "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward",
+    "gdn_prefill_chunked_noalloc",
 )
+
+# Size of the static scratch of gdn_prefill_chunked_noalloc (gdn.h).
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libgdn.so")
@@ -77,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_chunked.restype = i
     L.gdn_prefill_chunked.argtypes = [vp] * 8 + [i] * 8 + [f, vp, sz, vp]
     L.gdn_decode_step.restype = i
+    L.gdn_prefill_chunked_noalloc.restype = i
+    L.gdn_prefill_chunked_noalloc.argtypes = [vp] * 8 + [i] * 8 + [f, vp]
     L.gdn_decode_step.argtypes = [vp] * 8 + [i] * 6 + [f, vp]
     L.gdn_short_conv_silu.restype = i
     L.gdn_short_conv_silu.argtypes = [vp] * 3 + [i] * 5 + [f, i, i, vp]
@@ -185,6 +192,31 @@ def gdn_prefill_chunked(q, k, v, alpha, beta, state_in=None, *, chunk=64,
         _ptr(state_out), _ptr(out), B, T, H, Dk, Dv, chunk, dt, _dtype_code(out),
         float(scale), _ptr(workspace), workspace.numel(), _stream(stream))
     _check("gdn_prefill_chunked", st)
+    return out, state_out
+
+
+def gdn_prefill_chunked_noalloc(q, k, v, alpha, beta, state_in, out, state_out=None, *,
+                                chunk=64, scale=1.0, stream=None):
+    """gdn_prefill_chunked with the library's static scratch instead of a
+    workspace: allocates nothing (the caller passes out, and state_out or
+    None).  Calls on one GPU share the scratch: order them on one stream."""
+    if out is None:
+        raise ValueError("gdn_prefill_chunked_noalloc allocates nothing: pass out")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, (B, T, H, Dk))
+    _dev(v, "v", q.dtype, (B, T, H, Dv))
+    _dev(alpha, "alpha", torch.float32, (B, T, H))
+    _dev(beta, "beta", torch.float32, (B, T, H))
+    _dev(state_in, "state_in", torch.float32, (B, H, Dk, Dv))
+    _dev(out, "out", out.dtype, (B, T, H, Dv))
+    _dev(state_out, "state_out", torch.float32, (B, H, Dk, Dv))
+    st = lib().gdn_prefill_chunked_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
+        _ptr(state_out), _ptr(out), B, T, H, Dk, Dv, chunk, _dtype_code(q), _dtype_code(out),
+        float(scale), _stream(stream))
+    _check("gdn_prefill_chunked_noalloc", st)
     return out, state_out
 
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/gdn.h"
@@ -91,12 +92,18 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv,
   return gdn::prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype == GDN_BF16);
 }
 
-int gdn_prefill_chunked(const void* q, const void* k, const void* v,
-                        const float* alpha, const float* beta,
-                        const float* state_in, float* state_out, void* out,
-                        int B, int T, int H, int Dk, int Dv, int chunk,
-                        int dtype, int out_dtype, float scale, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a gdn_prefill_chunked call, common to the entry point
+// with a caller workspace and the one with the static scratch.  On success
+// returns GDN_OK, fills p (without workspace and stream) and sets *need to
+// the scratch bytes the launch uses.
+int check_prefill(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta, const float* state_in, float* state_out, void* out,
+                  int B, int T, int H, int Dk, int Dv, int chunk, int dtype, int out_dtype,
+                  float scale, gdn::PrefillArgs* p, size_t* need) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG,
           "bad sizes B=%d T=%d H=%d", B, T, H);
@@ -107,33 +114,114 @@ int gdn_prefill_chunked(const void* q, const void* k, const void* v,
   const long long nc = ((long long)T + chunk - 1) / chunk;
   REQUIRE((long long)B * H * nc < (1LL << 31) && (long long)B * H * 8 < (1LL << 31),
           GDN_ERR_UNSUPPORTED, "grid too large");
-  if ((long long)B * H == 0) return ok();
-  REQUIRE_ALIGNED_OR_NULL(state_in);
-  REQUIRE_ALIGNED_OR_NULL(state_out);
-  if (T > 0) {
-    REQUIRE_PTR(q);
-    REQUIRE_PTR(k);
-    REQUIRE_PTR(v);
-    REQUIRE_PTR(out);
-    REQUIRE(alpha != nullptr && beta != nullptr, GDN_ERR_INVALID_ARG,
-            "alpha/beta is NULL");
-    const size_t need =
-        gdn::prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype == GDN_BF16);
-    if (need > 0) {
-      REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
-      REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
-              "workspace is not 256-byte aligned");
-      REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG,
-              "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  *need = 0;
+  if ((long long)B * H > 0) {
+    REQUIRE_ALIGNED_OR_NULL(state_in);
+    REQUIRE_ALIGNED_OR_NULL(state_out);
+    if (T > 0) {
+      REQUIRE_PTR(q);
+      REQUIRE_PTR(k);
+      REQUIRE_PTR(v);
+      REQUIRE_PTR(out);
+      REQUIRE(alpha != nullptr && beta != nullptr, GDN_ERR_INVALID_ARG,
+              "alpha/beta is NULL");
+      *need = gdn::prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype == GDN_BF16);
     }
   }
+  p->q = q; p->k = k; p->v = v; p->alpha = alpha; p->beta = beta;
+  p->state_in = state_in; p->state_out = state_out; p->out = out;
+  p->B = B; p->T = T; p->H = H; p->Dk = Dk; p->Dv = Dv; p->chunk = chunk;
+  p->bf16 = dtype == GDN_BF16; p->out_bf16 = out_dtype == GDN_BF16;
+  p->scale = scale; p->workspace = nullptr; p->stream = nullptr;
+  return GDN_OK;
+}
+
+// Scratch of gdn_prefill_chunked_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in); it uses the device
+// address hipGetSymbolAddress returns, looked up once per device with that
+// device current and kept in scratch_addr.
+constexpr size_t kNoAllocScratchBytes = (size_t)GDN_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr and an error
+// message on failure).
+void* scratch_on_current_device(int* status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = hip_status(e, "gdn_prefill_chunked_noalloc: hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_chunked_noalloc: device %d out of range", dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *status = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                           "gdn_prefill_chunked_noalloc: hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    scratch_addr[dev] = ptr;
+  }
+  *status = GDN_OK;
+  return scratch_addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_chunked(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        const float* state_in, float* state_out, void* out,
+                        int B, int T, int H, int Dk, int Dv, int chunk,
+                        int dtype, int out_dtype, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   gdn::PrefillArgs p;
-  p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
-  p.state_in = state_in; p.state_out = state_out; p.out = out;
-  p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = chunk;
-  p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16;
-  p.scale = scale; p.workspace = workspace; p.stream = stream;
+  size_t need = 0;
+  const int st = check_prefill(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk,
+                               Dv, chunk, dtype, out_dtype, scale, &p, &need);
+  if (st != GDN_OK) return st;
+  if ((long long)B * H == 0) return ok();
+  if (need > 0) {
+    REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
+    REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
+            "workspace is not 256-byte aligned");
+    REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG,
+            "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  }
+  p.workspace = workspace; p.stream = stream;
   return hip_status(gdn::launch_prefill(p), "gdn_prefill_chunked launch");
+}
+
+int gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const float* state_in, float* state_out, void* out,
+                                int B, int T, int H, int Dk, int Dv, int chunk,
+                                int dtype, int out_dtype, float scale, void* stream) {
+  gdn::PrefillArgs p;
+  size_t need = 0;
+  int st = check_prefill(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk, Dv,
+                         chunk, dtype, out_dtype, scale, &p, &need);
+  if (st != GDN_OK) return st;
+  if ((long long)B * H == 0) return ok();
+  REQUIRE(need <= kNoAllocScratchBytes, GDN_ERR_UNSUPPORTED,
+          "gdn_prefill_chunked_noalloc: these sizes need %zu bytes of scratch, more than "
+          "the %zu-byte static scratch; call gdn_prefill_chunked with a workspace",
+          need, kNoAllocScratchBytes);
+  void* ws = scratch_on_current_device(&st);
+  if (st != GDN_OK) return st;
+  p.workspace = need > 0 ? ws : nullptr; p.stream = stream;
+  return hip_status(gdn::launch_prefill(p), "gdn_prefill_chunked_noalloc launch");
 }
 
 int gdn_decode_step(const void* q, const void* k, const void* v,

@@ -46,7 +46,8 @@
  *     every state entry within the sum of the |beta v| written into it.  The
  *     decode steps and the f32 mode have no such limit.
  *   - Calls are thread-safe; there is no mutable global state besides the
- *     per-thread error message.
+ *     per-thread error message, and the static scratch of
+ *     gdn_prefill_chunked_noalloc (with its per-device address, set once).
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -111,6 +112,32 @@ int gdn_prefill_chunked(const void* q, const void* k, const void* v,
                         int B, int T, int H, int Dk, int Dv, int chunk,
                         int dtype, int out_dtype, float scale, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus workspace and
+ * workspace_bytes), same results (the same kernels run): the scratch they
+ * need comes from a static device array of GDN_NOALLOC_SCRATCH_BYTES in the
+ * library, one copy per GPU, held until the process ends.  The call itself
+ * allocates nothing; its first call on a device, with that device current,
+ * looks up the array's device address (hipGetSymbolAddress) and keeps it.
+ *   - Sizes whose gdn_prefill_workspace_bytes(...) exceeds
+ *     GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_UNSUPPORTED and enqueue
+ *     nothing (use gdn_prefill_chunked with a workspace).
+ *   - `stream` must belong to the current device.
+ *   - Every call on one GPU shares that GPU's scratch and leaves its contents
+ *     behind (nothing in it needs to start at zero): calls that can run at
+ *     the same time on one GPU (other streams, other threads) race and give
+ *     wrong results; order them on one stream.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const float* state_in, float* state_out,
+                                void* out, int B, int T, int H, int Dk, int Dv,
+                                int chunk, int dtype, int out_dtype, float scale,
+                                void* stream);
 
 /*
  * One recurrence step for a batch of sequences (section 3.1.2 at a single
