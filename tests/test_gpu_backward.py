@@ -56,20 +56,17 @@ def test_backward_zero_length_passes_state_gradient():
     assert torch.equal(g["dstate_in"].cpu(), dst)
 
 
-def test_backward_sampled_heads_b4_h32_t1024():
+def test_backward_all_heads_b4_h32_t1024():
     """The backward workload the bench times (B4 H32 T1024 d128, bf16 inputs):
-    three sampled heads against the oracle."""
+    every head's gradients against the oracle."""
     B, T, H, D = 4, 1024, 32, 128
     x = synthetic.gdn_inputs(B, T, H, D, D, dtype="bf16", seed=8, device="cuda")
     gen = torch.Generator(device="cuda").manual_seed(9)
     dout = torch.randn(B, T, H, D, generator=gen, device="cuda")
     g = gdn.gdn_prefill_backward(*(x[n] for n in NAMES), dout)
     torch.cuda.synchronize()
-    for b, h in ((0, 0), (1, 20), (3, 31)):
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
-        r = oracle.gdn_recurrence_backward(*(f64(x[n][sl]) for n in NAMES), f64(dout[sl]))
-        for n in GRADS:
-            got = g[n][b:b + 1, h:h + 1] if n == "dstate_in" else g[n][sl]
-            e = err(got.contiguous(), r[n])
-            assert e <= TOL["f32"], (n, b, h, e)
-        say(f"  head ({b},{h}) ok")
+    r = oracle.gdn_recurrence_backward(*(f64(x[n]) for n in NAMES), f64(dout))
+    for n in GRADS:
+        e = err(g[n], r[n])
+        say(f"  all {B * H} heads {n}: {e:.2e}")
+        assert e <= TOL["f32"], n

@@ -107,16 +107,18 @@ def test_conv_full_qwen32b_projection():
     assert e <= TOL["bf16"]
 
 
-def test_conv_then_prefill_qwen32b_sampled():
-    """Qwen-32B-shaped layer with projection adaptation: conv -> SiLU -> L2 on
-    q, k (conv -> SiLU on v) then the GDN prefill; sampled heads checked
-    against oracle conv -> oracle recurrence on the same raw inputs.
-
-    The prefill consumes bf16 q, k, v, so the layer stores the conv outputs
-    in bf16 between the two calls.  The oracle chain applies that same
-    storage rounding (its own f64 conv output rounded to bf16) at the same
-    boundary: without it, the bf16 storage alone moves the f64 recurrence's
-    output by ~3e-2 of its RMS, more than the kernels' own error budget."""
+def test_conv_then_prefill_qwen32b_all_heads():
+    """Qwen-32B-shaped layer with projection adaptation, as two calls: conv ->
+    SiLU -> L2 on q, k (conv -> SiLU on v), stored in bf16, then the GDN
+    prefill.  Each call is checked on every element against the oracle on
+    the bits it received: the three convolutions against the oracle's
+    convolution of the raw inputs, the prefill against the oracle's
+    recurrence over the GPU's bf16 conv outputs.  (The oracle's own f64 conv
+    output rounds to bf16 differently in the last place for some elements;
+    at outputs ~20x the RMS those one-ulp input differences alone move the
+    layer output by ~1e-2 of its RMS.  The fused form, which never rounds
+    the conv outputs to bf16, is checked against the unrounded oracle chain
+    separately.)"""
     c = synthetic.CONFIGS["qwen32b_conv"]
     B, T, H, D = c["B"], c["T"], c["H"], c["Dk"]
     say(f"qwen32b conv+prefill B={B} T={T} H={H}")
@@ -126,31 +128,22 @@ def test_conv_then_prefill_qwen32b_sampled():
     taps = {n: synthetic.conv_inputs(1, 1, H * D, 4, seed=c["seed"] * 10 + i,
                                      device="cuda")[1]
             for i, n in enumerate(("q", "k", "v"))}
-    qc = gdn.gdn_short_conv_silu(raw["q"], taps["q"], l2norm_group=D)
-    kc = gdn.gdn_short_conv_silu(raw["k"], taps["k"], l2norm_group=D)
-    vc = gdn.gdn_short_conv_silu(raw["v"], taps["v"], l2norm_group=0)
-    o, s = gdn.gdn_prefill_chunked(qc.view(B, T, H, D), kc.view(B, T, H, D),
-                                   vc.view(B, T, H, D), g["alpha"], g["beta"], None,
+    conv = {}
+    for n, grp in (("q", D), ("k", D), ("v", 0)):
+        y = gdn.gdn_short_conv_silu(raw[n], taps[n], l2norm_group=grp)
+        yf = gdn.gdn_short_conv_silu(raw[n], taps[n], l2norm_group=grp, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert_bf16_is_rounded_f32(y, yf)
+        e = err(yf, oracle.short_conv_silu(f64(raw[n]), f64(taps[n]), l2norm_group=grp))
+        say(f"  conv {n}: err {e:.2e}")
+        assert e <= TOL["bf16"]
+        conv[n] = y.view(B, T, H, D)
+        del yf
+    o, s = gdn.gdn_prefill_chunked(conv["q"], conv["k"], conv["v"], g["alpha"], g["beta"], None,
                                    chunk=c["chunk"], out_dtype=torch.float32)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    picks = rng.choice(B * H, size=6, replace=False)
-    refs_o, refs_s, got_o, got_s = [], [], [], []
-    for p in picks:
-        b, h = int(p // H), int(p % H)
-        sl = slice(h * D, (h + 1) * D)
-        conv = {}
-        for n, grp in (("q", D), ("k", D), ("v", 0)):
-            c64 = oracle.short_conv_silu(f64(raw[n][b:b + 1, :, sl]),
-                                         f64(taps[n][sl]), l2norm_group=grp)
-            conv[n] = torch.from_numpy(c64).to(torch.bfloat16).double().numpy()
-        ro, rs = oracle.gdn_recurrence(conv["q"][:, :, None], conv["k"][:, :, None],
-                                       conv["v"][:, :, None],
-                                       f64(g["alpha"][b:b + 1, :, h:h + 1]),
-                                       f64(g["beta"][b:b + 1, :, h:h + 1]))
-        refs_o.append(ro[0, :, 0]); refs_s.append(rs[0, 0])
-        got_o.append(f64(o[b, :, h])); got_s.append(f64(s[b, h]))
-    eo = oracle.rms_normalised_max_error(np.stack(got_o), np.stack(refs_o))
-    es = oracle.rms_normalised_max_error(np.stack(got_s), np.stack(refs_s))
-    say(f"  sampled heads: out err {eo:.3e} state err {es:.3e}")
+    ro, rs = oracle.gdn_recurrence(f64(conv["q"]), f64(conv["k"]), f64(conv["v"]),
+                                   f64(g["alpha"]), f64(g["beta"]))
+    eo, es = err(o, ro), err(s, rs)
+    say(f"  prefill, all {B * H} heads: out err {eo:.3e} state err {es:.3e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
