@@ -13,7 +13,8 @@ layouts documented in the C file:
     state [B, H, Dk, Dv]
 
 Sources followed ("The Key to Going Linear: Analysis-Driven Transformer
-Linearization"): section 3.1.2 (GDN update and read-out), section 3.1
+Linearization"): section 3.1.2 (GDN update and read-out), section 3.2.2
+(gated linear attention with a key-dependent gate), section 3.1
 (softmax), section 4 (disjoint sliding window + sinks; short convolutions),
 appendix B.1 (key normalisation), appendix B.1 "Approximation error" (nMSE).
 
@@ -59,6 +60,7 @@ def _load():
         lib.gdn_oracle_swa_sink_f64.argtypes = [_dp] * 4 + [i] * 6 + [d, i]
         lib.gdn_oracle_recurrence_chgate_f64.argtypes = [_dp] * 8 + [i] * 5 + [d, i]
         lib.gdn_oracle_recurrence_bwd_f64.argtypes = [_dp] * 14 + [i] * 5 + [d]
+        lib.gdn_oracle_kgla_f64.argtypes = [_dp] * 8 + [i] * 5 + [d]
         lib.gdn_oracle_hybrid_f64.argtypes = [_dp] * 9 + [i] * 7 + [d, d]
         lib.gdn_oracle_short_conv_silu_f64.argtypes = [_dp] * 3 + [i] * 5 + [d]
         lib.gdn_oracle_short_conv_step_f64.argtypes = [_dp] * 5 + [i] * 4 + [d]
@@ -163,6 +165,32 @@ def decode_step_chgate(q, k, v, alpha, beta, state_in, scale=1.0):
     q, k, v, a = (_arr(x)[:, None] for x in (q, k, v, alpha))
     b = _arr(beta)[:, None]
     out, s = gdn_recurrence_chgate(q, k, v, a, b, state_in, scale)
+    return out[:, 0], s
+
+
+def kgla(q, k, v, alpha, beta, state_in=None, scale=1.0):
+    """Gated linear attention with a key-dependent gate (section 3.2.2):
+    per-channel gate alpha_t o (1 - beta_t k_t o k_t), write k_t v_t^T, read
+    after the write.  q, k, alpha [B,T,H,Dk], v [B,T,H,Dv], beta [B,T,H].
+    Returns (out [B,T,H,Dv], S_T [B,H,Dk,Dv])."""
+    q, k, v, alpha, beta = map(_arr, (q, k, v, alpha, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and alpha.shape == q.shape and beta.shape == (B, T, H)
+    s_in = None if state_in is None else _arr(state_in)
+    out = np.zeros((B, T, H, Dv))
+    s_out = np.zeros((B, H, Dk, Dv))
+    _load().gdn_oracle_kgla_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(s_in), _ptr(s_out), _ptr(out), B, T, H, Dk, Dv,
+                                float(scale))
+    return out, s_out
+
+
+def kgla_step(q, k, v, alpha, beta, state_in, scale=1.0):
+    """One kGLA step per (b, h): q, k, alpha [B,H,Dk], v [B,H,Dv], beta [B,H]."""
+    q, k, v, a = (_arr(x)[:, None] for x in (q, k, v, alpha))
+    b = _arr(beta)[:, None]
+    out, s = kgla(q, k, v, a, b, state_in, scale)
     return out[:, 0], s
 
 

@@ -187,6 +187,53 @@ void gdn_oracle_recurrence_chgate_f64(const double* q, const double* k, const do
 }
 
 /* ------------------------------------------------------------------------- */
+/* Gated linear attention with a key-dependent gate (kGLA, section 3.2.2):    */
+/*   y_t = sum_{i<=t} ( q_t^T [prod_{j=i+1}^{t} diag(alpha_j)                  */
+/*                              (I - beta_j Diag(k_j o k_j))] k_i ) v_i,       */
+/* taken as the state recurrence it unrolls from (every factor is diagonal,   */
+/* so the product's order does not matter):                                    */
+/*   S_t = diag(alpha_t o (1 - beta_t k_t o k_t)) S_{t-1} + k_t v_t^T,         */
+/*   o_t = scale * S_t^T q_t   (read after the write, i = t included).         */
+/* Readings: the printed sum has no step size on the write, so the write is   */
+/* k_i v_i^T; the sum runs over i <= t (causal); alpha_j is a d_k-vector per  */
+/* token (diag(alpha_j)); a state S_0 (state_in, or zero) enters as the first  */
+/* term, decayed by every gate from token 1 on.                                */
+/* alpha [B,T,H,Dk]; beta [B,T,H].                                            */
+/* ------------------------------------------------------------------------- */
+void gdn_oracle_kgla_f64(const double* q, const double* k, const double* v,
+                         const double* alpha, const double* beta,
+                         const double* state_in, double* state_out, double* out,
+                         int B, int T, int H, int Dk, int Dv, double scale) {
+  long BH = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    long b = bh / H, h = bh % H;
+    double* S = (double*)malloc(sizeof(double) * (size_t)Dk * Dv);
+    for (long e = 0; e < (long)Dk * Dv; ++e) S[e] = state_in ? state_in[bh * Dk * Dv + e] : 0.0;
+    for (long t = 0; t < T; ++t) {
+      long row = (b * T + t) * H + h;
+      const double* qt = q + row * Dk;
+      const double* kt = k + row * Dk;
+      const double* vt = v + row * Dv;
+      const double* at = alpha + row * Dk;
+      double be = beta[row];
+      for (long i = 0; i < Dk; ++i) {
+        double g = at[i] * (1.0 - be * kt[i] * kt[i]);
+        for (long j = 0; j < Dv; ++j) S[i * Dv + j] = g * S[i * Dv + j] + kt[i] * vt[j];
+      }
+      for (long j = 0; j < Dv; ++j) {
+        double acc = 0;
+        for (long i = 0; i < Dk; ++i) acc += S[i * Dv + j] * qt[i];
+        out[row * Dv + j] = scale * acc;
+      }
+    }
+    if (state_out)
+      for (long e = 0; e < (long)Dk * Dv; ++e) state_out[bh * Dk * Dv + e] = S[e];
+    free(S);
+  }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Gradient of the GDN recurrence (section 3.1.2, scalar gate) by the adjoint */
 /* of the token loop: with A_t = alpha_t (I - beta_t k_t k_t^T) (symmetric),  */
 /* S_t = A_t S_{t-1} + beta_t k_t v_t^T and o_t = scale S_t^T q_t, the total  */

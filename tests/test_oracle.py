@@ -491,6 +491,88 @@ def test_chgate_decode_steps_chain_to_recurrence():
 
 
 # --------------------------------------------------------------------------
+# Gated linear attention with a key-dependent gate (kGLA, section 3.2.2):
+# y_t = sum_{i<=t} (q_t^T [prod_{j=i+1}^{t} diag(alpha_j)(I - beta_j
+# Diag(k_j o k_j))] k_i) v_i.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("Dk,Dv", [(3, 2), (5, 4)])
+def test_kgla_equals_the_printed_sum(Dk, Dv):
+    """The printed sum, with the explicit diagonal factors multiplied as full
+    matrices (no state), against the oracle from a zero state; and with a
+    state S0 the extra term q_t^T (prod_{j<=t} D_j) S0."""
+    B, T, H = 1, 7, 2
+    q, k, v, a_ch, beta, S0 = _rand_chgate(B, T, H, Dk, Dv, RNG)
+    out0, _ = oracle.kgla(q, k, v, a_ch, beta, None, scale=0.5)
+    out1, S1 = oracle.kgla(q, k, v, a_ch, beta, S0)
+    I = np.eye(Dk)
+    for h in range(H):
+        D = [np.diag(a_ch[0, j, h]) @ (I - beta[0, j, h] * np.diag(k[0, j, h] * k[0, j, h]))
+             for j in range(T)]
+
+        def prod(lo, hi):
+            M = np.eye(Dk)
+            for j in range(lo, hi + 1):
+                M = D[j] @ M
+            return M
+
+        for t in range(T):
+            y = sum((q[0, t, h] @ prod(i + 1, t) @ k[0, i, h]) * v[0, i, h] for i in range(t + 1))
+            np.testing.assert_allclose(out0[0, t, h], 0.5 * y, atol=1e-12, rtol=0)
+            y1 = y + q[0, t, h] @ prod(0, t) @ S0[0, h]
+            np.testing.assert_allclose(out1[0, t, h], y1, atol=1e-12, rtol=0)
+        S = prod(0, T - 1) @ S0[0, h] + sum(
+            prod(i + 1, T - 1) @ np.outer(k[0, i, h], v[0, i, h]) for i in range(T))
+        np.testing.assert_allclose(S1[0, h], S, atol=1e-12, rtol=0)
+
+
+def test_kgla_beta_zero_scalar_gate_is_gla():
+    """beta = 0 and one gate value on every channel: scalar-gated linear
+    attention, i.e. the GDN oracle's no-erase hook with a unit write (pinned
+    above), and for a constant gate a the closed form sum a^(t-i) (q.k_i) v_i."""
+    B, T, H, Dk, Dv = 2, 9, 2, 6, 5
+    q, k, v, alpha, beta, S0 = _rand_gdn(B, T, H, Dk, Dv, RNG)
+    a_ch = np.repeat(alpha[..., None], Dk, axis=-1)
+    o1, s1 = oracle.kgla(q, k, v, a_ch, np.zeros_like(beta), S0)
+    o2, s2 = oracle.gdn_recurrence(q, k, v, alpha, np.ones_like(beta), S0, erase=False)
+    np.testing.assert_allclose(o1, o2, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(s1, s2, atol=1e-13, rtol=0)
+    a = 0.9
+    o3, _ = oracle.kgla(q, k, v, np.full_like(a_ch, a), np.zeros_like(beta))
+    for t in range(T):
+        y = sum(a ** (t - i) * np.einsum("bhd,bhd->bh", q[:, t], k[:, i])[..., None] * v[:, i]
+                for i in range(t + 1))
+        np.testing.assert_allclose(o3[:, t], y, atol=1e-12, rtol=0)
+
+
+def test_kgla_one_hot_keys_with_unit_step_equal_gdn():
+    """For a one-hot key e_c, Diag(k o k) = k k^T, so with beta = 1 (the GDN
+    write beta k v^T is then k v^T) kGLA is the channel-gated GDN update."""
+    B, T, H, Dk, Dv = 1, 12, 2, 5, 3
+    q, _, v, a_ch, beta, S0 = _rand_chgate(B, T, H, Dk, Dv, RNG)
+    k = np.eye(Dk)[RNG.integers(0, Dk, (B, T, H))]
+    ones = np.ones_like(beta)
+    o1, s1 = oracle.kgla(q, k, v, a_ch, ones, S0)
+    o2, s2 = oracle.gdn_recurrence_chgate(q, k, v, a_ch, ones, S0)
+    np.testing.assert_allclose(o1, o2, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(s1, s2, atol=1e-13, rtol=0)
+    # and with beta < 1 the two differ (the write is not scaled by beta in kGLA)
+    o3, _ = oracle.kgla(q, k, v, a_ch, beta, S0)
+    o4, _ = oracle.gdn_recurrence_chgate(q, k, v, a_ch, beta, S0)
+    assert np.max(np.abs(o3 - o4)) > 1e-2
+
+
+def test_kgla_steps_chain_to_recurrence():
+    B, T, H, Dk, Dv = 2, 5, 2, 4, 3
+    q, k, v, a_ch, beta, S0 = _rand_chgate(B, T, H, Dk, Dv, RNG)
+    out, ST = oracle.kgla(q, k, v, a_ch, beta, S0, scale=0.7)
+    S = S0
+    for t in range(T):
+        o, S = oracle.kgla_step(q[:, t], k[:, t], v[:, t], a_ch[:, t], beta[:, t], S, scale=0.7)
+        np.testing.assert_array_equal(o, out[:, t])
+    np.testing.assert_array_equal(S, ST)
+
+
+# --------------------------------------------------------------------------
 # Backward of the recurrence (the gradients a layer trained through the mixer
 # needs).  Pinned by torch autograd over a plain token loop (fp64, CPU) and by
 # central finite differences of the oracle's own forward.
