@@ -29,7 +29,8 @@ __all__ = [
     "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
     "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
     "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward",
-    "gdn_prefill_chunked_noalloc", "GDN_NOALLOC_SCRATCH_BYTES", "EXPORTED_SYMBOLS",
+    "gdn_prefill_chunked_noalloc", "GDN_NOALLOC_SCRATCH_BYTES",
+    "gdn_prefill_chunked_kgla", "gdn_decode_step_kgla", "EXPORTED_SYMBOLS",
 ]
 
 GDN_BF16 = 0
@@ -45,7 +46,7 @@ EXPORTED_SYMBOLS = (
     "gdn_swa_cache_fill", "gdn_hybrid_prefill_workspace_bytes", "gdn_hybrid_prefill",
     "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
     "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward",
-    "gdn_prefill_chunked_noalloc",
+    "gdn_prefill_chunked_noalloc", "gdn_prefill_chunked_kgla", "gdn_decode_step_kgla",
 )
 
 # Size of the static scratch of gdn_prefill_chunked_noalloc (gdn.h).
@@ -105,6 +106,10 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_chunked_chgate.argtypes = [vp] * 8 + [i] * 7 + [f, vp, sz, vp]
     L.gdn_decode_step_chgate.restype = i
     L.gdn_decode_step_chgate.argtypes = [vp] * 8 + [i] * 6 + [f, vp]
+    L.gdn_prefill_chunked_kgla.restype = i
+    L.gdn_prefill_chunked_kgla.argtypes = [vp] * 8 + [i] * 7 + [f, vp, sz, vp]
+    L.gdn_decode_step_kgla.restype = i
+    L.gdn_decode_step_kgla.argtypes = [vp] * 8 + [i] * 6 + [f, vp]
     L.gdn_prefill_backward_workspace_bytes.restype = sz
     L.gdn_prefill_backward_workspace_bytes.argtypes = [i] * 5
     L.gdn_prefill_backward.restype = i
@@ -409,11 +414,8 @@ def gdn_prefill_chgate_workspace_bytes(B, T, H) -> int:
     return int(lib().gdn_prefill_chgate_workspace_bytes(B, T, H))
 
 
-def gdn_prefill_chunked_chgate(q, k, v, alpha, beta, state_in=None, *, scale=1.0, out=None,
-                               out_dtype=None, state_out=None, workspace=None, stream=None):
-    """Chunked GDN prefill with a channel-wise gate G_t = diag(alpha_t):
-    q, k, alpha [B,T,H,Dk] (alpha f32), v [B,T,H,Dv], beta [B,T,H] f32.
-    Returns (out [B,T,H,Dv], S_T [B,H,Dk,Dv])."""
+def _prefill_chgate(fn, q, k, v, alpha, beta, state_in, scale, out, out_dtype, state_out,
+                    workspace, stream):
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     _dev(q, "q")
@@ -433,18 +435,16 @@ def gdn_prefill_chunked_chgate(q, k, v, alpha, beta, state_in=None, *, scale=1.0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().gdn_prefill_chunked_chgate(
+    st = getattr(lib(), fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out),
         _ptr(out), B, T, H, Dk, Dv, _dtype_code(q), _dtype_code(out), float(scale),
         _ptr(workspace), wbytes, _stream(stream))
-    _check("gdn_prefill_chunked_chgate", st)
+    _check(fn, st)
     return out, state_out
 
 
-def gdn_decode_step_chgate(q, k, v, alpha, beta, state_in, *, state_out=None, out=None,
-                           out_dtype=None, scale=1.0, stream=None):
-    """One channel-gated step: q, k, alpha [B,H,Dk] (alpha f32), v [B,H,Dv],
-    beta [B,H]; state [B,H,Dk,Dv] (state_out may be state_in).  Returns (out, S')."""
+def _decode_chgate(fn, q, k, v, alpha, beta, state_in, state_out, out, out_dtype, scale,
+                   stream):
     B, H, Dk = q.shape
     Dv = v.shape[-1]
     _dev(q, "q")
@@ -460,12 +460,45 @@ def gdn_decode_step_chgate(q, k, v, alpha, beta, state_in, *, state_out=None, ou
     if out is None:
         out = torch.empty((B, H, Dv), dtype=odt, device=q.device)
     _dev(out, "out", odt, (B, H, Dv))
-    st = lib().gdn_decode_step_chgate(
+    st = getattr(lib(), fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out),
         _ptr(out), B, H, Dk, Dv, _dtype_code(q), _dtype_code(out), float(scale),
         _stream(stream))
-    _check("gdn_decode_step_chgate", st)
+    _check(fn, st)
     return out, state_out
+
+
+def gdn_prefill_chunked_chgate(q, k, v, alpha, beta, state_in=None, *, scale=1.0, out=None,
+                               out_dtype=None, state_out=None, workspace=None, stream=None):
+    """Chunked GDN prefill with a channel-wise gate G_t = diag(alpha_t):
+    q, k, alpha [B,T,H,Dk] (alpha f32), v [B,T,H,Dv], beta [B,T,H] f32.
+    Returns (out [B,T,H,Dv], S_T [B,H,Dk,Dv])."""
+    return _prefill_chgate("gdn_prefill_chunked_chgate", q, k, v, alpha, beta, state_in, scale,
+                           out, out_dtype, state_out, workspace, stream)
+
+
+def gdn_decode_step_chgate(q, k, v, alpha, beta, state_in, *, state_out=None, out=None,
+                           out_dtype=None, scale=1.0, stream=None):
+    """One channel-gated step: q, k, alpha [B,H,Dk] (alpha f32), v [B,H,Dv],
+    beta [B,H]; state [B,H,Dk,Dv] (state_out may be state_in).  Returns (out, S')."""
+    return _decode_chgate("gdn_decode_step_chgate", q, k, v, alpha, beta, state_in, state_out,
+                          out, out_dtype, scale, stream)
+
+
+def gdn_prefill_chunked_kgla(q, k, v, alpha, beta, state_in=None, *, scale=1.0, out=None,
+                             out_dtype=None, state_out=None, workspace=None, stream=None):
+    """Gated linear attention with a key-dependent gate (kGLA): per-channel
+    gate alpha o (1 - beta k o k), write k v^T.  Shapes as for
+    gdn_prefill_chunked_chgate.  Returns (out [B,T,H,Dv], S_T [B,H,Dk,Dv])."""
+    return _prefill_chgate("gdn_prefill_chunked_kgla", q, k, v, alpha, beta, state_in, scale,
+                           out, out_dtype, state_out, workspace, stream)
+
+
+def gdn_decode_step_kgla(q, k, v, alpha, beta, state_in, *, state_out=None, out=None,
+                         out_dtype=None, scale=1.0, stream=None):
+    """One kGLA step; shapes as for gdn_decode_step_chgate.  Returns (out, S')."""
+    return _decode_chgate("gdn_decode_step_kgla", q, k, v, alpha, beta, state_in, state_out,
+                          out, out_dtype, scale, stream)
 
 
 def gdn_prefill_backward_workspace_bytes(B, T, H, Dk, Dv) -> int:

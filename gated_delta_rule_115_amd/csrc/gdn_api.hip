@@ -499,16 +499,21 @@ size_t gdn_prefill_chgate_workspace_bytes(int B, int T, int H) {
   return gdn::prefill_chgate_workspace_bytes(B, T, H);
 }
 
-int gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
-                               const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
-                               int dtype, int out_dtype, float scale, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The channel-gate prefill and decode step, and kGLA on the same kernels.
+int prefill_chgate_call(const void* q, const void* k, const void* v, const float* alpha,
+                        const float* beta, const float* state_in, float* state_out, void* out,
+                        int B, int T, int H, int Dk, int Dv, int dtype, int out_dtype,
+                        float scale, void* workspace, size_t workspace_bytes, void* stream,
+                        bool kgla, const char* name) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
           H);
   REQUIRE((Dk == 32 || Dk == 64 || Dk == 128) && (Dv == 32 || Dv == 64 || Dv == 128),
-          GDN_ERR_UNSUPPORTED, "channel-gate head dims Dk=%d Dv=%d not in {32,64,128}", Dk, Dv);
+          GDN_ERR_UNSUPPORTED, "%s: head dims Dk=%d Dv=%d not in {32,64,128}", name, Dk, Dv);
   REQUIRE((long long)B * H * ((T + 31) / 32) < (1LL << 31), GDN_ERR_UNSUPPORTED,
           "grid too large");
   if ((long long)B * H == 0) return ok();
@@ -533,14 +538,14 @@ int gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
   p.state_in = state_in; p.state_out = state_out; p.out = out;
   p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.chunk = 32;
   p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16;
-  p.scale = scale; p.workspace = workspace; p.stream = stream;
-  return hip_status(gdn::launch_prefill_chgate(p), "gdn_prefill_chunked_chgate launch");
+  p.scale = scale; p.workspace = workspace; p.stream = stream; p.kgla = kgla;
+  return hip_status(gdn::launch_prefill_chgate(p), name);
 }
 
-int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* state_in, float* state_out,
-                           void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
-                           float scale, void* stream) {
+int decode_chgate_call(const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, const float* state_in, float* state_out, void* out,
+                       int B, int H, int Dk, int Dv, int dtype, int out_dtype, float scale,
+                       void* stream, bool kgla, const char* name) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d H=%d", B, H);
   REQUIRE(is_head_dim(Dk) && is_head_dim(Dv), GDN_ERR_UNSUPPORTED,
@@ -559,8 +564,48 @@ int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const fl
   p.state_in = state_in; p.state_out = state_out; p.out = out;
   p.B = B; p.H = H; p.Dk = Dk; p.Dv = Dv;
   p.bf16 = dtype == GDN_BF16; p.out_bf16 = out_dtype == GDN_BF16;
-  p.scale = scale; p.stream = stream; p.chgate = true;
-  return hip_status(gdn::launch_decode(p), "gdn_decode_step_chgate launch");
+  p.scale = scale; p.stream = stream; p.chgate = true; p.kgla = kgla;
+  return hip_status(gdn::launch_decode(p), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, const float* state_in,
+                               float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
+                               int dtype, int out_dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return prefill_chgate_call(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk, Dv,
+                             dtype, out_dtype, scale, workspace, workspace_bytes, stream, false,
+                             "gdn_prefill_chunked_chgate launch");
+}
+
+int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* state_in, float* state_out,
+                           void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
+                           float scale, void* stream) {
+  return decode_chgate_call(q, k, v, alpha, beta, state_in, state_out, out, B, H, Dk, Dv, dtype,
+                            out_dtype, scale, stream, false, "gdn_decode_step_chgate launch");
+}
+
+int gdn_prefill_chunked_kgla(const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* state_in,
+                             float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
+                             int dtype, int out_dtype, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return prefill_chgate_call(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk, Dv,
+                             dtype, out_dtype, scale, workspace, workspace_bytes, stream, true,
+                             "gdn_prefill_chunked_kgla launch");
+}
+
+int gdn_decode_step_kgla(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* state_in, float* state_out, void* out,
+                         int B, int H, int Dk, int Dv, int dtype, int out_dtype, float scale,
+                         void* stream) {
+  return decode_chgate_call(q, k, v, alpha, beta, state_in, state_out, out, B, H, Dk, Dv, dtype,
+                            out_dtype, scale, stream, true, "gdn_decode_step_kgla launch");
 }
 
 size_t gdn_prefill_backward_workspace_bytes(int B, int T, int H, int Dk, int Dv) {

@@ -25,6 +25,14 @@
 // on the 32-deep f16 MFMA with f32 accumulation, S kept in f32.  Kernel 1 is
 // f32 throughout (bf16 inputs are widened on load).  Ragged tails are
 // padded with identity tokens (alpha = 1, beta = 0, q = k = v = 0).
+//
+// Gated linear attention with a key-dependent gate (kGLA, section 3.2.2)
+// runs on the same two kernels (KG = true): its update
+//   S_t = diag(alpha_t o (1 - beta_t k_t o k_t)) S_{t-1} + k_t v_t^T
+// has the per-channel gate alpha_t o (1 - beta_t k_t o k_t), whose log the
+// per-chunk pass accumulates into Gam, and no erase, so A = 0, T = I and
+// U = V: kernel 1 forms only Pm and Gam, kernel 2 only Q S, Pm V and the
+// state update.
 #include "gdn_f16ops.h"
 #include "gdn_internal.h"
 
@@ -95,7 +103,7 @@ struct ChunkRegs {
 // index w, w + gridDim.x, ... and loads the next one's q, k, alpha, beta into
 // registers while the current one is computed (barriers order LDS only, so
 // those loads stay in flight).
-template <class TIn, int DK>
+template <class TIn, int DK, bool KG>
 __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, int T, int H, int NC, float scale, char* __restrict__ ws,
@@ -156,11 +164,13 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     if (tid < GC) bet[tid] = t0 + tid < T ? br : 0.f;
     if (id + (int)gridDim.x < total) fetch(id + gridDim.x);
     f16ops::lds_barrier();
-    // Cumulative log gate per channel, and its range over the chunk.
+    // Cumulative log gate per channel, and its range over the chunk (kGLA:
+    // the gate is alpha o (1 - beta k o k); rows past T have k = beta = 0).
     if (tid < DK) {
       float acc = 0.f;
       for (int r = 0; r < GC; ++r) {
         acc += Gs[r][tid];
+        if constexpr (KG) acc += log1pf(-bet[r] * Ks[r][tid] * Ks[r][tid]);
         Gs[r][tid] = acc;
       }
       rng[tid] = Gs[0][tid] - acc;
@@ -203,15 +213,17 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
 #pragma unroll 4
       for (int kk = 0; kk < DK; kk += 8) {
         const float ki0 = Ki[16 * tc + lr][kk + lg], ki1 = Ki[16 * tc + lr][kk + 4 + lg];
-        a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[16 * tr + lr][kk + lg], ki0, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[16 * tr + lr][kk + 4 + lg], ki1, a1, 0, 0, 0);
+        if constexpr (!KG) {
+          a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[16 * tr + lr][kk + lg], ki0, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[16 * tr + lr][kk + 4 + lg], ki1, a1, 0, 0, 0);
+        }
         p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[16 * tr + lr][kk + lg], ki0, p0, 0, 0, 0);
         p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[16 * tr + lr][kk + 4 + lg], ki1, p1, 0, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * tr + 4 * lg + j, i = 16 * tc + lr;
-        As[r][i] = (i < r) ? bet[r] * (a0[j] + a1[j]) : 0.f;
+        if constexpr (!KG) As[r][i] = (i < r) ? bet[r] * (a0[j] + a1[j]) : 0.f;
         Pg[r * GC + i] = (i <= r) ? scale * (p0[j] + p1[j]) : 0.f;
       }
     } else {
@@ -227,11 +239,15 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
             p += Qs[r][ch] * ki;
           }
         }
-        As[r][i] = (i < r) ? bet[r] * a : 0.f;
+        if constexpr (!KG) As[r][i] = (i < r) ? bet[r] * a : 0.f;
         Pg[r * GC + i] = (i <= r) ? scale * p : 0.f;
       }
     }
     f16ops::lds_barrier();
+    if constexpr (KG) {  // no erase: T = I is implied, the recurrence uses U = V
+      if (tid < GC) Bg[tid] = bet[tid];
+      continue;
+    }
     // T = (I + A)^-1 by 16-row blocks, all in f32: the diagonal blocks by
     // forward substitution (inv16; waves 0 and 1), then T10 = -T11 A10 T00 on
     // f32 MFMA tiles (wave 2).  The product form (I - A)(I + A^2)...(I + A^16)
@@ -277,7 +293,7 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
 
 // Kernel 2: one work-group per (b, h, value slice of DVS columns; 64 when Dv
 // allows, else 32).
-template <class TIn, class TOut, int DK, int DVS>
+template <class TIn, class TOut, int DK, int DVS, bool KG>
 __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* state_in, float* state_out,
@@ -294,6 +310,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
   __shared__ float S[DK][DVS + 16];  // state slice
   __shared__ float Vs[GC][DVS + 16], Us[GC][DVS + 16];
   __shared__ float Tm[GC][GC + 4], Pm[GC][GC + 4], bet[GC], gC[DK];
+  // kGLA records hold no T: their fetch starts at Pm.
+  constexpr int kRecPc0 = KG ? GC * GC / 4 : 0;
   const int ns = Dv / DVS;
   const int bh = blockIdx.x / ns, sl = blockIdx.x % ns, b = bh / H, h = bh % H;
   const int col0 = sl * DVS;
@@ -334,7 +352,7 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     const float* rec = reinterpret_cast<const float*>(ws + ((size_t)bh * NC + c) * kRecBytes);
 #pragma unroll
     for (int u = 0; u < R::NR; ++u) {
-      const int pc = min(tid + GNTR * u, (int)(kRecFloats / 4) - 1);
+      const int pc = min(kRecPc0 + tid + GNTR * u, (int)(kRecFloats / 4) - 1);
       rg.rec[u] = *reinterpret_cast<const f32x4*>(rec + 4 * pc);
     }
   };
@@ -366,7 +384,7 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     }
 #pragma unroll
     for (int u = 0; u < R::NR; ++u) {
-      const int pc = tid + GNTR * u;
+      const int pc = kRecPc0 + tid + GNTR * u;
       if (pc < (int)(kRecFloats / 4)) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -398,7 +416,7 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     // for O).  XT = 2 row tiles x GNCT column tiles.
     constexpr int XT = 2 * GNCT;
     f32x4 qs = zero4();
-    if (w < 2 * XT) {
+    if (w < 2 * XT && (!KG || w >= XT)) {
       const int x = w % XT, tr = x / GNCT, tc = x % GNCT;
       const float(*A)[DK + 4] = w < XT ? Kg : Qg;
       f32x4 acc0 = zero4(), acc1 = zero4();
@@ -457,7 +475,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
       }
     };
     // Phase B: U = T Y (waves 0 .. XT-1), into Vs (V is no longer needed).
-    if (w < XT) {
+    // kGLA: U = V, already in Vs.
+    if (!KG && w < XT) {
       const int tr = w / GNCT, tc = w % GNCT;
       const f32x4 acc = prod_c([&](int k) { return Tm[16 * tr + lr][k]; },
                                [&](int k) { return Us[k][16 * tc + lr]; }, zero4());
@@ -501,37 +520,42 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     }
 }
 
-template <class TIn, class TOut, int DK>
+template <class TIn, class TOut, int DK, bool KG>
 hipError_t launch_chgate_t(const PrefillArgs& p) {
   const int NC = (p.T + GC - 1) / GC;
   const hipStream_t st = (hipStream_t)p.stream;
   if (NC > 0) {
     const int total = p.B * p.H * NC;
-    hipLaunchKernelGGL((chgate_prep_kernel<TIn, DK>), dim3(std::min(total, kPrepGrid)), dim3(GNT),
-                       0, st, (const TIn*)p.q, (const TIn*)p.k, p.alpha, p.beta, p.T, p.H, NC,
-                       p.scale, (char*)p.workspace, total);
+    hipLaunchKernelGGL((chgate_prep_kernel<TIn, DK, KG>), dim3(std::min(total, kPrepGrid)),
+                       dim3(GNT), 0, st, (const TIn*)p.q, (const TIn*)p.k, p.alpha, p.beta, p.T,
+                       p.H, NC, p.scale, (char*)p.workspace, total);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.Dv % 64 == 0)
-    hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 64>), dim3(p.B * p.H * (p.Dv / 64)),
-                       dim3(GNTR), 0, st, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v,
-                       p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC,
-                       p.scale, (const char*)p.workspace);
+    hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 64, KG>),
+                       dim3(p.B * p.H * (p.Dv / 64)), dim3(GNTR), 0, st, (const TIn*)p.q,
+                       (const TIn*)p.k, (const TIn*)p.v, p.state_in, p.state_out, (TOut*)p.out,
+                       p.T, p.H, p.Dv, NC, p.scale, (const char*)p.workspace);
   else
-    hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 32>), dim3(p.B * p.H * (p.Dv / 32)),
-                       dim3(GNTR), 0, st, (const TIn*)p.q, (const TIn*)p.k, (const TIn*)p.v,
-                       p.state_in, p.state_out, (TOut*)p.out, p.T, p.H, p.Dv, NC,
-                       p.scale, (const char*)p.workspace);
+    hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 32, KG>),
+                       dim3(p.B * p.H * (p.Dv / 32)), dim3(GNTR), 0, st, (const TIn*)p.q,
+                       (const TIn*)p.k, (const TIn*)p.v, p.state_in, p.state_out, (TOut*)p.out,
+                       p.T, p.H, p.Dv, NC, p.scale, (const char*)p.workspace);
   return hipGetLastError();
+}
+
+template <class TIn, class TOut, int DK>
+hipError_t launch_chgate_kg(const PrefillArgs& p) {
+  return p.kgla ? launch_chgate_t<TIn, TOut, DK, true>(p) : launch_chgate_t<TIn, TOut, DK, false>(p);
 }
 
 template <class TIn, class TOut>
 hipError_t launch_chgate_dk(const PrefillArgs& p) {
   switch (p.Dk) {
-    case 32: return launch_chgate_t<TIn, TOut, 32>(p);
-    case 64: return launch_chgate_t<TIn, TOut, 64>(p);
-    case 128: return launch_chgate_t<TIn, TOut, 128>(p);
+    case 32: return launch_chgate_kg<TIn, TOut, 32>(p);
+    case 64: return launch_chgate_kg<TIn, TOut, 64>(p);
+    case 128: return launch_chgate_kg<TIn, TOut, 128>(p);
   }
   return hipErrorInvalidValue;
 }

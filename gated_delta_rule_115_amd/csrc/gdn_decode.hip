@@ -24,10 +24,14 @@
 
 namespace gdn {
 
-// CH = true: channel-wise gate, alpha is [B, H, DK] and row r of S is scaled
-// by alpha[r] before the step (G_t = diag(alpha_t) applied first, as in the
+// MODE 0: scalar gate alpha [B, H].
+// MODE 1: channel-wise gate, alpha is [B, H, DK] and row r of S is scaled by
+// alpha[r] before the step (G_t = diag(alpha_t) applied first, as in the
 // page's update); the step then runs with a = 1.
-template <class TIn, class TOut, int DK, int DV, bool CH>
+// MODE 2: gated linear attention with a key-dependent gate (section 3.2.2):
+// row r of S is scaled by alpha[r] (1 - beta k[r]^2), there is no erase and
+// the write is k v^T, so u = v.
+template <class TIn, class TOut, int DK, int DV, int MODE>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
@@ -65,9 +69,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     qs[i] = to_f32(q[(size_t)bh * DK + i]);
   }
   for (int i = tid; i < DV; i += NT) vs[i] = to_f32(v[(size_t)bh * DV + i]);
-  const float a = CH ? 1.f : alpha[bh];
+  const float a = MODE == 0 ? alpha[bh] : 1.f;
   const float b = beta[bh];
-  if constexpr (CH) {
+  if constexpr (MODE == 1) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = rg + i * RG;
@@ -75,6 +79,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
   }
   __syncthreads();
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + i * RG;
+      if (r < DK) s[i] *= alpha[(size_t)bh * DK + r] * (1.f - b * ks[r] * ks[r]);
+    }
+  }
 
   // Partial S^T k and S^T q over this thread's rows; k.q from column group 0.
   float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
@@ -107,7 +118,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
       sq += red_q[g][tid];
       kq += red_kq[g];
     }
-    const float u = b * (vs[tid] - a * sk);
+    const float u = MODE == 2 ? vs[tid] : b * (vs[tid] - a * sk);
     us[tid] = u;
     out[(size_t)bh * DV + tid] = from_f32<TOut>(scale * (a * sq + kq * u));
   }
@@ -129,13 +140,18 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
 template <class TIn, class TOut, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& p) {
-  if (p.chgate)
-    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, true>), dim3(p.B * p.H), dim3(256),
+  if (p.chgate && p.kgla)
+    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, 2>), dim3(p.B * p.H), dim3(256),
+                       0, (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k,
+                       (const TIn*)p.v, p.alpha, p.beta, p.state_in, p.state_out,
+                       (TOut*)p.out, p.scale);
+  else if (p.chgate)
+    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, 1>), dim3(p.B * p.H), dim3(256),
                        0, (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k,
                        (const TIn*)p.v, p.alpha, p.beta, p.state_in, p.state_out,
                        (TOut*)p.out, p.scale);
   else
-    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, false>), dim3(p.B * p.H), dim3(256),
+    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, 0>), dim3(p.B * p.H), dim3(256),
                        0, (hipStream_t)p.stream, (const TIn*)p.q, (const TIn*)p.k,
                        (const TIn*)p.v, p.alpha, p.beta, p.state_in, p.state_out,
                        (TOut*)p.out, p.scale);

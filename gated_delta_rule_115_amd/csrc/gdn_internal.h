@@ -18,6 +18,7 @@ struct DecodeArgs {
   float scale;
   void* stream;
   bool chgate = false;  // alpha is [B, H, Dk]: channel-wise gate
+  bool kgla = false;    // with chgate: key-dependent gate, no erase, write k v^T
 };
 
 struct PrefillArgs {
@@ -35,6 +36,9 @@ struct PrefillArgs {
   // alpha and beta (0 = T: dense [B, T, ...]).  Only the per-head kernels
   // (bf16, Dk = Dv = 128, chunk 64) take another value.
   int seq_stride = 0;
+  // Channel-gate kernels only: gated linear attention with a key-dependent
+  // gate (no erase, gate alpha o (1 - beta k o k), write k v^T).
+  bool kgla = false;
 };
 
 struct ConvArgs {
@@ -102,7 +106,8 @@ size_t backward_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 hipError_t launch_backward(const BwdArgs& p);
 
 // Channel-wise gate prefill (alpha [B, T, H, Dk]); chunks of 32 tokens,
-// f32 arithmetic; Dk in {32, 64, 128}, Dv a multiple of 32.
+// f32 arithmetic; Dk in {32, 64, 128}, Dv a multiple of 32.  With p.kgla:
+// gated linear attention with a key-dependent gate, same workspace.
 size_t prefill_chgate_workspace_bytes(int B, int T, int H);
 hipError_t launch_prefill_chgate(const PrefillArgs& p);
 

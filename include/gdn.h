@@ -318,6 +318,40 @@ int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const fl
                            float scale, void* stream);
 
 /*
+ * Gated linear attention with a key-dependent gate (kGLA, section 3.2.2,
+ * "Gated Linear Attention with Key-Dependent Gate"):
+ *   y_t = sum_{i<=t} ( q_t^T [prod_{j=i+1}^{t} diag(alpha_j)
+ *                               (I - beta_j Diag(k_j o k_j))] k_i ) v_i,
+ * i.e. the state update S_t = diag(alpha_t o (1 - beta_t k_t o k_t)) S_{t-1}
+ * + k_t v_t^T with out_t = scale * S_t^T q_t read after the write.  The
+ * diagonal erase Diag(k o k) stands in for the delta rule's rank-1 k k^T; the
+ * write carries no step size (the printed sum has none).  Arguments, layouts,
+ * limits and workspace (gdn_prefill_chgate_workspace_bytes) as for
+ * gdn_prefill_chunked_chgate: alpha [B, T, H, Dk] f32, beta [B, T, H] f32.
+ * Precondition (documented, not checked): alpha in (0, 1], beta in [0, 1]
+ * and beta k[c]^2 < 1 for every channel (the kernels work with the log of
+ * the gate, which must be positive).
+ */
+int gdn_prefill_chunked_kgla(const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta,
+                             const float* state_in, float* state_out, void* out,
+                             int B, int T, int H, int Dk, int Dv, int dtype,
+                             int out_dtype, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * One kGLA step per (b, h) (section 3.2.2 at a single token):
+ *   S' = diag(alpha o (1 - beta k o k)) S + k v^T,   out = scale * S'^T q;
+ * q, k, alpha [B, H, Dk]; v [B, H, Dv]; beta [B, H]; states as for
+ * gdn_decode_step_chgate (may alias).  No precondition on the gate's sign:
+ * the step multiplies by it directly.
+ */
+int gdn_decode_step_kgla(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* state_in, float* state_out,
+                         void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
+                         float scale, void* stream);
+
+/*
  * Backward pass of gdn_prefill_chunked (scalar gate; section 3.1.2 update,
  * trained through as in section 3.3): for an output gradient dout and an
  * optional gradient dstate_out of the final state, the gradients of the
