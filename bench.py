@@ -54,9 +54,12 @@ import gated_delta_rule_115_amd as gdn  # noqa: E402
 import synthetic  # noqa: E402
 
 # MI355X published peaks (dense).
-PEAK_BF16_FLOPS = 2.5e15
+PEAK_BF16_FLOPS = 2.5e15   # bf16 and f16 MFMA
+PEAK_F32_MFMA_FLOPS = 157.3e12
 PEAK_HBM_BPS = 8.0e12
-PEAK_F32_VECTOR_FLOPS = 157.3e12  # 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
+# f32 VALU without packed-f32 instructions (the library is built with them
+# off): 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz.
+PEAK_F32_VALU_FLOPS = 78.6e12
 
 # Algorithmic work per unit (fixed definitions; d = Dk = Dv, chunk C = 64):
 #   prefill flops per token-head: dense-tile count of the chunked form
@@ -79,11 +82,16 @@ def decode_gdn_bytes(d, esize=2):
     return 8 * d * d + esize * 3 * d + 8 + esize * d
 
 
-# Channel-gate prefill, chunks of C = 32, per token-head: gate-ratio Gram
-# blocks A and Pm (4 C dk), K S, Q S and the state update (6 dk dv), T Y and
-# Pm U (4 C dv): 131,072 flop at d = 128.
-def chgate_flops_per_token_head(dk, dv, C=32):
-    return 4 * C * dk + 6 * dk * dv + 4 * C * dv
+# Channel-gate prefill, chunks of C = 32, per token-head: the per-chunk pass
+# forms the gate-ratio Gram blocks A and Pm (4 C dk) on f32 MFMA; the
+# recurrence forms K S, Q S and the state update (6 dk dv), T Y and Pm U
+# (4 C dv), on f16 MFMA for bf16 inputs: 16,384 + 114,688 flop at d = 128.
+def chgate_prep_flops_per_token_head(dk, C=32):
+    return 4 * C * dk
+
+
+def chgate_recur_flops_per_token_head(dk, dv, C=32):
+    return 6 * dk * dv + 4 * C * dv
 
 
 # bf16 q, k, v, out + f32 per-channel alpha and beta per token-head.
@@ -321,8 +329,10 @@ def make_chgate_leg():
                                        out=out, state_out=st, workspace=ws)
         mark("chgate_prefill")
 
+    n = B * T * H
     info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
-                alu_flops=chgate_flops_per_token_head(d, d) * B * T * H,
+                prep_flops=chgate_prep_flops_per_token_head(d) * n,
+                recur_flops=chgate_recur_flops_per_token_head(d, d) * n,
                 bytes=chgate_bytes(B, T, H, d, d))
     return run, info
 
@@ -601,12 +611,21 @@ def main():
         ms = seg_ms[("chgate_llama8b", "chgate_prefill")]
         sec = ms / 1e3
         kern = CHGATE_KERNELS
-        roof_chgate = dict(bound="alu", kernel=kern,
-                           achieved=inf["alu_flops"] / sec / 1e12,
-                           peak=PEAK_F32_VECTOR_FLOPS / 1e12, unit="TFLOP/s",
-                           frac=inf["alu_flops"] / sec / PEAK_F32_VECTOR_FLOPS,
-                           traffic=traffic_bytes(kern),
-                           ms_per_launch=ms, flops_per_launch=inf["alu_flops"],
+        # Each kernel against the pipe its products use: the per-chunk pass's
+        # Gram blocks on f32 MFMA, the recurrence on f16 MFMA.  The call's peak
+        # is the flop-weighted one: total flops over the time both would take
+        # at their peaks.
+        flops = inf["prep_flops"] + inf["recur_flops"]
+        t_min = inf["prep_flops"] / PEAK_F32_MFMA_FLOPS + inf["recur_flops"] / PEAK_BF16_FLOPS
+        peak = flops / t_min
+        roof_chgate = dict(bound="mfma", kernel=kern,
+                           achieved=flops / sec / 1e12, peak=peak / 1e12, unit="TFLOP/s",
+                           frac=t_min / sec, traffic=traffic_bytes(kern),
+                           peak_note="flop-weighted: per-chunk pass on f32 MFMA (157.3 TFLOP/s), "
+                                     "recurrence on f16 MFMA (2.5 PFLOP/s)",
+                           ms_per_launch=ms, flops_per_launch=flops,
+                           prep_flops_per_launch=inf["prep_flops"],
+                           recur_flops_per_launch=inf["recur_flops"],
                            hbm_bytes_algorithmic=inf["bytes"],
                            hbm_frac_algorithmic=inf["bytes"] / sec / PEAK_HBM_BPS)
     roof_bwd = None
@@ -616,8 +635,8 @@ def main():
         sec = ms / 1e3
         roof_bwd = dict(bound="alu", kernel=BWD_KERNELS,
                         achieved=inf["alu_flops"] / sec / 1e12,
-                        peak=PEAK_F32_VECTOR_FLOPS / 1e12, unit="TFLOP/s",
-                        frac=inf["alu_flops"] / sec / PEAK_F32_VECTOR_FLOPS,
+                        peak=PEAK_F32_VALU_FLOPS / 1e12, unit="TFLOP/s",
+                        frac=inf["alu_flops"] / sec / PEAK_F32_VALU_FLOPS,
                         traffic=traffic_bytes(BWD_KERNELS),
                         ms_per_launch=ms, flops_per_launch=inf["alu_flops"])
     roof_conv = None
@@ -654,7 +673,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 I/O, f16 MFMA operands, f32 accumulation and state",
         "data": "synthetic (seeded torch.Generator; Llama/Qwen-shaped layers, random init)",
         "config": {
             "workload": "long32k prefill (B1 H32 T32768 d128, chunk 64) + hybrid decode "

@@ -251,3 +251,51 @@ def test_full_llama8b_layer_all_heads():
 
 def test_full_long32k_all_heads_with_final_state():
     _full_check("long32k")
+
+
+# ---------------------------------------------------------------------------
+# Magnitude range of the f16 operands (bf16 mode).  gdn.h documents that v,
+# the state and the chunk intermediates must stay below 65504 in magnitude in
+# bf16 mode (beyond it an operand becomes +-inf and the outputs are not
+# finite), and that the f32 mode and the decode step have no such limit.
+# ---------------------------------------------------------------------------
+def test_value_scale_within_f16_range_keeps_the_bar():
+    """v scaled by 256 (|v| up to ~1.2e3, the state to ~1e4): the result
+    scales with it and stays within the bf16 bar."""
+    x = synthetic.gdn_inputs(1, 1000, 2, 128, 128, dtype="bf16", seed=41, state0="randn")
+    x["v"] = (x["v"].float() * 256).to(torch.bfloat16)
+    x["state0"] = x["state0"] * 256
+    o, s = _run(x, 64)
+    ro, rs = _oracle(x)
+    eo, es = err(o, ro), err(s, rs)
+    say(f"v x256: out {eo:.2e} state {es:.2e}, max|S| {float(s.abs().max()):.3g}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_values_beyond_f16_range():
+    """|v| up to ~1e5: the bf16-mode prefill gives non-finite outputs (the
+    documented behaviour), while the f32 mode and the decode step, which keep
+    f32 operands, match the oracle."""
+    x = synthetic.gdn_inputs(1, 300, 2, 128, 128, dtype="bf16", seed=43)
+    x["v"] = (x["v"].float() * 3e4).to(torch.bfloat16)
+    assert float(x["v"].float().abs().max()) > 65504
+    o, s = _run(x, 64)
+    assert not bool(torch.isfinite(o).all())
+    xf = {n: (x[n].float() if n in ("q", "k", "v") else x[n]) for n in x}
+    of, sf = _run(xf, 64)
+    ro, rs = _oracle(x)
+    ef, esf = err(of, ro), err(sf, rs)
+    say(f"|v| to 1e5, f32 mode: out {ef:.2e} state {esf:.2e}")
+    assert ef <= TOL["f32"] and esf <= TOL["f32"]
+    st = torch.zeros(1, 2, 128, 128, device="cuda")
+    outs = []
+    for t in range(20):
+        ot, _ = gdn.gdn_decode_step(*(dev(x[n][:, t].contiguous())
+                                      for n in ("q", "k", "v", "alpha", "beta")),
+                                    st, state_out=st, out_dtype=torch.float32)
+        outs.append(ot)
+    torch.cuda.synchronize()
+    rd, rsd = oracle.gdn_recurrence(*(f64(x[n][:, :20]) for n in ("q", "k", "v", "alpha", "beta")))
+    ed = err(torch.stack(outs, dim=1), rd)
+    say(f"|v| to 1e5, decode steps: out {ed:.2e}")
+    assert ed <= TOL["f32"] and err(st, rsd) <= TOL["f32"]
