@@ -41,7 +41,7 @@ constexpr int decode_threads() {
 }
 
 template <class TIn, class TOut, int DK, int DV, int MODE>
-__global__ __launch_bounds__(decode_threads<DK, DV>()) void decode_step_kernel(
+__global__ __launch_bounds__((decode_threads<DK, DV>())) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* state_in, float* state_out,
