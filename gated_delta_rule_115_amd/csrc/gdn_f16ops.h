@@ -173,6 +173,53 @@ __device__ __forceinline__ void inv16(f32x4 LTf, int lr, int lq, float* scr, f32
   for (int j = 0; j < 4; ++j) TT[j] = Xc[kInvLd * (4 * lq + j) + lr];  // T[lr][4 lq + j]
 }
 
+// The four diagonal 16 x 16 blocks of a 64-token chunk's Tm = (I + A)^-1, on
+// one wave, by forward substitution in f32: lane 16 b + c solves
+// (I + L_b) x = e_c for column c of block b (column axpy form: once x_i is
+// final, x_r -= L_b[r][i] x_i for r > i).  The strictly lower blocks L_b
+// arrive column-major in the wave's LDS scratch: lcm + kInv4Block b + 20 i
+// holds L_b[0..15][i] (the caller writes D(L_b) there, one 16-byte store per
+// lane and block).  Out: the f16 operands dg = {D(T00), D(T00^T), D(T11),
+// D(T11^T), D(T22), D(T22^T), D(T33^T)} (h16x4 per lane, 64 lanes each).
+constexpr int kInv4Ld = 20;                   // floats per column
+constexpr int kInv4Block = 16 * kInv4Ld + 4;  // floats per block (bank offset 4)
+constexpr int kInv4Scratch = 4 * kInv4Block;
+__device__ __forceinline__ void inv16x4(const float* lcm, int l, h16x4* dg) {
+  const int b = l >> 4, c = l & 15;
+  const float* P = lcm + kInv4Block * b;
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+  auto col = [&](int i, f32x4* v) {
+#pragma unroll
+    for (int q = (i + 1) >> 2; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4*>(P + kInv4Ld * i + 4 * q);
+  };
+  // Columns are read two steps ahead of their use (three in flight).
+  f32x4 buf[3][4];
+  col(0, buf[0]);
+  col(1, buf[1]);
+#pragma unroll
+  for (int i = 0; i < 15; ++i) {
+    if (i + 2 < 15) col(i + 2, buf[(i + 2) % 3]);
+#pragma unroll
+    for (int r = i + 1; r < 16; ++r) x[r] = __builtin_fmaf(-buf[i % 3][r >> 2][r & 3], x[i], x[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // D(T_b): lane (q, c) of the operand holds T_b[4 q .. 4 q + 3][c], i.e.
+  // x[4 q .. 4 q + 3] of this lane.  D(T_b^T): lane (q, c') holds
+  // T_b[c'][4 q + j] = x[c'] of lane (b, 4 q + j).
+  const int nb = b < 3 ? 2 * b : -1;       // D(T_b) slot (none for b = 3)
+  const int tb = b < 3 ? 2 * b + 1 : 6;    // D(T_b^T) slot
+  if (nb >= 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dg[64 * nb + 16 * q + c] = h16x4{(h16)x[4 * q], (h16)x[4 * q + 1], (h16)x[4 * q + 2], (h16)x[4 * q + 3]};
+  }
+  h16* dt = reinterpret_cast<h16*>(dg + 64 * tb);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dt[4 * (16 * (c >> 2) + r) + (c & 3)] = (h16)x[r];
+}
+
 // Off-diagonal blocks of the unit lower triangular Tm = (I + A)^-1 of a
 // 64-token chunk by block forward substitution, from the A-operand fragments
 // of the strictly lower blocks of A and the diagonal inverses:

@@ -123,7 +123,7 @@ struct __align__(16) HSmem {
   h16x4 Dg[7][64];       // D(T00), D(T00^T), D(T11), D(T11^T), D(T22), D(T22^T), D(T33^T)
   h16x4 Pb[6][64][2];    // P operands per (row tile, 32-token step); halves = block columns
   HGate g[3];            // slot = chunk % 3
-  float Iv[4][kInvScratch];  // inverse scratch of helper waves 4-7
+  float Iv4[kInv4Scratch];  // diagonal blocks of A, column-major (helper wave 4)
 };
 
 // Slot of P block (R, C) in Pb: row tile R, 32-token step C / 2.
@@ -634,8 +634,10 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
 // 4-7 (one per SIMD, next to a recurrence wave) do all global loads, the
 // f16 conversions, the Gram blocks, the inverse and the gate tables.
 // Iteration i, phase 1: recurrence waves X~, (Q S~)^T, Y~ and U^ of chunk
-// i - 2; helpers: K of chunk i -> LDS, diagonal blocks and inverses (chunk
-// i - 1), off-diagonal blocks of A (i - 1) and of P (i - 2).  Phase 2:
+// i - 2, and from the same K fragments the blocks (c, 0), (c, 1) of P (i - 2)
+// for their wave c; helpers: K of chunk i -> LDS, the diagonal blocks of A
+// and their inverses (chunk i - 1, all on helper 0), the off-diagonal blocks
+// of A (i - 1), blocks (2, 2), (3, 2), (3, 3) of P (i - 2).  Phase 2:
 // recurrence waves S~ update, (P U^)^T and the outputs of chunk i - 2;
 // helpers: off-diagonal blocks of Tm (i - 1), gate tables (i), Q of chunk
 // i - 1 and av V of chunk i - 1 -> LDS.
@@ -712,6 +714,11 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
         // Per 32-key step: 4 K fragments (8 X products), 4 Q fragments (8
         // Q S products); the K fragments of step j + 1 are requested during
         // the X products of step j, the Q fragments during its Q S products.
+        // Blocks (cw, 0) and (cw, 1) of P0 = lower(Q K^T) for the outputs of
+        // phase 2, from the same K fragments and one more Q fragment per step
+        // (wave 0's (0, 1) lies above the diagonal and is dropped); helpers 2
+        // and 3 form (2, 2), (3, 2) and (3, 3).
+        f32x4 GP[2] = {zero4(), zero4()};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           h16x8 kf[4], qf[4];
@@ -719,6 +726,7 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
           for (int rt = 0; rt < 4; ++rt) kf[rt] = frag(Kb, rt, j);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) qf[rt] = frag(sm.Q, rt, j);
+          const h16x8 qw = frag(sm.Q, cw, j);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -727,16 +735,23 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) QS[sl][rt] = mfma32(sb[sl][j], qf[rt], QS[sl][rt]);
+#pragma unroll
+          for (int C = 0; C < 2; ++C) GP[C] = mfma32(kf[C], qw, GP[C]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 9, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 9, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 18, 0);
+        {
+          const bool widep = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
+          sm.Pb[pslot(cw, 0)][l][0] = p_block(gs, widep, cw, 0, GP[0], lr, lq, scale);
+          if (cw >= 1) sm.Pb[pslot(cw, 1)][l][1] = p_block(gs, widep, cw, 1, GP[1], lr, lq, scale);
+        }
         // Y~ = av V - (bx sigma) X~, U^ = T0 Y~ (av V and Tm of chunk c2 were
         // written in phase 2 of the previous iteration).
         const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
@@ -930,35 +945,32 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
       if (it < NC) st_tile(sm.K[it % 3], kr[p]);  // slot it % 3 was last read in phase 2 of it - 1
       ld_tile(kh, it + 2, kr[p]);
       if (h1) {
-        // Diagonal block hw of A for chunk c1, inverted.
+        // Chunk c1: helper 0 forms the four diagonal blocks of A and inverts
+        // them all (one lane per block column); helpers 1-3 form the
+        // off-diagonal blocks, (1, 0), (2, 0), (2, 1) on helper 1, (3, 0),
+        // (3, 1) on helper 2, (3, 2) on helper 3.
         const h16* Kb = sm.K[c1 % 3];
         const HGate& gs = sm.g[c1 % 3];
         const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-        f32x4 G = zero4();
+        if (hw == 0) {
+          f32x4 G[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const h16x8 kf = frag(Kb, hw, j);
-          G = mfma32(kf, kf, G);
-        }
-        f32x4 Lb, LT, Tt, TT;
-        a_diag(gs, wide, hw, G, lr, lq, Lb, LT);
-        inv16(LT, lr, lq, sm.Iv[hw], Tt, TT);
-        if (hw < 3) {
-          sm.Dg[2 * hw][l] = cvt4(Tt);
-          sm.Dg[2 * hw + 1][l] = cvt4(TT);
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+              const h16x8 kf = frag(Kb, R, j);
+              G[R] = mfma32(kf, kf, G[R]);
+            }
+#pragma unroll
+          for (int R = 0; R < 4; ++R) {
+            f32x4 Lb, LT;
+            a_diag(gs, wide, R, G[R], lr, lq, Lb, LT);
+            *reinterpret_cast<f32x4*>(sm.Iv4 + kInv4Block * R + kInv4Ld * lr + 4 * lq) = Lb;
+          }
+          inv16x4(sm.Iv4, l, &sm.Dg[0][0]);
         } else {
-          sm.Dg[6][l] = cvt4(TT);
-        }
-      }
-      if (hw < 2) {
-        // Off-diagonal blocks of A (chunk c1): rows 1, 2 (helper 0) or 3
-        // (helper 1); P block (0, 0) or (1, 0) of chunk c2.
-        if (h1) {
-          const h16* Kb = sm.K[c1 % 3];
-          const HGate& gs = sm.g[c1 % 3];
-          const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
           f32x4 G0 = zero4(), G1 = zero4(), G2 = zero4();
-          if (hw == 0) {
+          if (hw == 1) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const h16x8 k0 = frag(Kb, 0, j), k1 = frag(Kb, 1, j), k2 = frag(Kb, 2, j);
@@ -969,58 +981,42 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
             sm.Ab[0][l] = a_offdiag(gs, wide, 1, 0, G0, lr, lq);
             sm.Ab[1][l] = a_offdiag(gs, wide, 2, 0, G1, lr, lq);
             sm.Ab[2][l] = a_offdiag(gs, wide, 2, 1, G2, lr, lq);
-          } else {
+          } else if (hw == 2) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const h16x8 k3 = frag(Kb, 3, j);
               G0 = mfma32(frag(Kb, 0, j), k3, G0);  // (3, 0)
               G1 = mfma32(frag(Kb, 1, j), k3, G1);  // (3, 1)
-              G2 = mfma32(frag(Kb, 2, j), k3, G2);  // (3, 2)
             }
             sm.Ab[3][l] = a_offdiag(gs, wide, 3, 0, G0, lr, lq);
             sm.Ab[4][l] = a_offdiag(gs, wide, 3, 1, G1, lr, lq);
-            sm.Ab[5][l] = a_offdiag(gs, wide, 3, 2, G2, lr, lq);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) G0 = mfma32(frag(Kb, 2, j), frag(Kb, 3, j), G0);  // (3, 2)
+            sm.Ab[5][l] = a_offdiag(gs, wide, 3, 2, G0, lr, lq);
           }
         }
-        if (h2) {
-          const h16* Kb = sm.K[c2 % 3];
-          const HGate& gs = sm.g[c2 % 3];
-          const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-          const int R = hw;
-          f32x4 G = zero4();
-#pragma unroll
-          for (int j = 0; j < 4; ++j) G = mfma32(frag(Kb, 0, j), frag(sm.Q, R, j), G);
-          sm.Pb[pslot(R, 0)][l][0] = p_block(gs, wide, R, 0, G, lr, lq, scale);
-        }
-      } else if (h2) {
-        // P blocks of chunk c2: (1, 1), (2, 0..2) (helper 2) or (3, 0..3) (helper 3).
+      }
+      if (hw >= 2 && h2) {
+        // P blocks of chunk c2 on the block diagonal's lower right: (2, 2) on
+        // helper 2, (3, 2) and (3, 3) on helper 3.
         const h16* Kb = sm.K[c2 % 3];
         const HGate& gs = sm.g[c2 % 3];
         const bool wide = __builtin_amdgcn_readfirstlane(gs.wide) != 0;
-        f32x4 G[4] = {zero4(), zero4(), zero4(), zero4()};
+        f32x4 G0 = zero4(), G1 = zero4();
         if (hw == 2) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h16x8 k1 = frag(Kb, 1, j), q2 = frag(sm.Q, 2, j);
-            G[0] = mfma32(k1, frag(sm.Q, 1, j), G[0]);  // (1, 1)
-            G[1] = mfma32(frag(Kb, 0, j), q2, G[1]);    // (2, 0)
-            G[2] = mfma32(k1, q2, G[2]);                // (2, 1)
-            G[3] = mfma32(frag(Kb, 2, j), q2, G[3]);    // (2, 2)
-          }
-          sm.Pb[pslot(1, 1)][l][1] = p_block(gs, wide, 1, 1, G[0], lr, lq, scale);
-#pragma unroll
-          for (int C = 0; C < 3; ++C)
-            sm.Pb[pslot(2, C)][l][C & 1] = p_block(gs, wide, 2, C, G[1 + C], lr, lq, scale);
+          for (int j = 0; j < 4; ++j) G0 = mfma32(frag(Kb, 2, j), frag(sm.Q, 2, j), G0);
+          sm.Pb[pslot(2, 2)][l][0] = p_block(gs, wide, 2, 2, G0, lr, lq, scale);
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const h16x8 q3 = frag(sm.Q, 3, j);
-#pragma unroll
-            for (int C = 0; C < 4; ++C) G[C] = mfma32(frag(Kb, C, j), q3, G[C]);
+            G0 = mfma32(frag(Kb, 2, j), q3, G0);
+            G1 = mfma32(frag(Kb, 3, j), q3, G1);
           }
-#pragma unroll
-          for (int C = 0; C < 4; ++C)
-            sm.Pb[pslot(3, C)][l][C & 1] = p_block(gs, wide, 3, C, G[C], lr, lq, scale);
+          sm.Pb[pslot(3, 2)][l][0] = p_block(gs, wide, 3, 2, G0, lr, lq, scale);
+          sm.Pb[pslot(3, 3)][l][1] = p_block(gs, wide, 3, 3, G1, lr, lq, scale);
         }
       }
       lds_barrier();
