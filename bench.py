@@ -23,9 +23,13 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   leg "backward_t1024":  gradients of the scalar-gate prefill (dq, dk, dv,
                          dalpha, dbeta, dS0) for B=4, H=32, T=1024, d=128,
                          bf16 inputs, f32 gradients: gdn_prefill_backward
-  leg "conv_qwen32b":    Qwen-32B-shaped layer with projection adaptation:
-                         gdn_short_conv_silu on q, k (with per-head L2 norm)
-                         and v, then gdn_prefill_chunked; B=2, H=40, T=16384
+  leg "conv_qwen32b":    Qwen-32B-shaped layer with projection adaptation,
+                         B=2, H=40, T=16384: gdn_prefill_chunked_conv (short
+                         convolution + SiLU on the raw q, k, v and the L2 norm
+                         of q, k inside the prefill kernels' tile loads)
+  leg "conv_qwen32b_twocall": the same layer as separate calls:
+                         gdn_short_conv_silu on q, k, v (bf16 results in HBM),
+                         then gdn_prefill_chunked
 
 The headline value is the prefill leg's throughput in tokens/s (B*T per call,
 all heads), with the decode leg's tokens/s (B per step) reported beside it.
@@ -139,6 +143,10 @@ PROFILE = "profiles/gdn_kernels_bench_workloads.md"
 # The long32k prefill call launches three kernels (segment transition pass,
 # combine pass, output pass); its entry sums them.
 PREFILL_KERNELS = "prefill_lead_kernel<bf16> + segment_combine_kernel + prefill_out_kernel<bf16>"
+# The fused-convolution prefill of the Qwen-32B-shaped layer: the same three
+# kernels, instantiated with the convolution in their tile loads.
+PREFILL_CONV_KERNELS = ("prefill_lead_kernel<bf16,conv> + segment_combine_kernel + "
+                        "prefill_out_kernel<bf16,conv>")
 CHGATE_KERNELS = ("chgate_prep_kernel (f32) + chgate_recur_kernel (bf16 inputs: f16 MFMA operands, "
                   "f32 accumulation and state)")
 # The backward call launches the adjoint kernel and the slice-partial sum.
@@ -204,7 +212,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill_long32k,decode_b256,hybrid_prefill,"
                                       "chgate_llama8b,backward_t1024,conv_qwen32b,"
-                                      "convstep_b256")
+                                      "conv_qwen32b_twocall,convstep_b256")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) "
                          "and exit: the reference reading for HBM byte counters")
@@ -361,6 +369,30 @@ def make_conv_leg():
     B, T, H, d = c["B"], c["T"], c["H"], c["Dk"]
     g = synthetic.gdn_inputs(B, T, H, d, d, dtype="bf16", seed=c["seed"], normalise_qk=False,
                              device="cuda")
+    taps = {n: synthetic.conv_inputs(1, 1, H * d, 4, seed=c["seed"] * 10 + i, device="cuda")[1]
+            for i, n in enumerate(("q", "k", "v"))}
+    out = torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda")
+    st = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(B, T, H, d, d, 64), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(mark):
+        gdn.gdn_prefill_chunked_conv(g["q"], g["k"], g["v"], taps["q"], taps["k"], taps["v"],
+                                     g["alpha"], g["beta"], None, out=out, state_out=st,
+                                     workspace=ws)
+        mark("prefill_conv")
+
+    info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
+                flops=prefill_flops_per_token_head(d) * B * T * H,
+                bytes=prefill_bytes(B, T, H, d))
+    return run, info
+
+
+def make_conv_twocall_leg():
+    c = synthetic.CONFIGS["qwen32b_conv"]
+    B, T, H, d = c["B"], c["T"], c["H"], c["Dk"]
+    g = synthetic.gdn_inputs(B, T, H, d, d, dtype="bf16", seed=c["seed"], normalise_qk=False,
+                             device="cuda")
     raw = {n: g[n].reshape(B, T, H * d) for n in ("q", "k", "v")}
     taps = {n: synthetic.conv_inputs(1, 1, H * d, 4, seed=c["seed"] * 10 + i, device="cuda")[1]
             for i, n in enumerate(("q", "k", "v"))}
@@ -487,6 +519,9 @@ def main():
     if "conv_qwen32b" in legs_wanted:
         run, info = make_conv_leg()
         legs["conv_qwen32b"], infos["conv_qwen32b"] = run, info
+    if "conv_qwen32b_twocall" in legs_wanted:
+        run, info = make_conv_twocall_leg()
+        legs["conv_qwen32b_twocall"], infos["conv_qwen32b_twocall"] = run, info
     if "convstep_b256" in legs_wanted:
         run, info = make_convstep_leg()
         legs["convstep_b256"], infos["convstep_b256"] = run, info
@@ -642,8 +677,20 @@ def main():
     roof_conv = None
     if "conv_qwen32b" in out_legs:
         inf = infos["conv_qwen32b"]
-        roof_conv = hbm_roof("short_conv_silu_kernel<bf16,bf16,4> (x3)", inf["conv_bytes"],
-                             seg_ms[("conv_qwen32b", "conv")])
+        ms = seg_ms[("conv_qwen32b", "prefill_conv")]
+        sec = ms / 1e3
+        kern = PREFILL_CONV_KERNELS
+        roof_conv = dict(bound="mfma", kernel=kern, achieved=inf["flops"] / sec / 1e12,
+                         peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                         frac=inf["flops"] / sec / PEAK_BF16_FLOPS, traffic=traffic_bytes(kern),
+                         ms_per_launch=ms, flops_per_launch=inf["flops"],
+                         hbm_bytes_algorithmic=inf["bytes"],
+                         hbm_frac_algorithmic=inf["bytes"] / sec / PEAK_HBM_BPS)
+    roof_conv_kernel = None
+    if "conv_qwen32b_twocall" in out_legs:
+        inf = infos["conv_qwen32b_twocall"]
+        roof_conv_kernel = hbm_roof("short_conv_silu_kernel<bf16,bf16,4> (x3)",
+                                    inf["conv_bytes"], seg_ms[("conv_qwen32b_twocall", "conv")])
 
     roof_convstep = None
     if "convstep_b256" in out_legs:
@@ -679,9 +726,9 @@ def main():
             "workload": "long32k prefill (B1 H32 T32768 d128, chunk 64) + hybrid decode "
                         "(B256 H32 d128, 4 sinks + 512 window) + hybrid prefill (B4 H32 "
                         "T4096 d128, 4 sinks + 512 window) + channel-gate prefill (B4 H32 "
-                        "T4096 d128) + backward (B4 H32 T1024 d128) + qwen32b conv+prefill "
-                        "(B2 H40 T16384 d128) + decode-time conv step (B256, 3 x 5120 "
-                        "channels, K 4)",
+                        "T4096 d128) + backward (B4 H32 T1024 d128) + qwen32b fused "
+                        "conv+prefill (B2 H40 T16384 d128), and as separate calls + "
+                        "decode-time conv step (B256, 3 x 5120 channels, K 4)",
             "global_batch": 1, "seq_len": 32768, "parallelism": "single-gpu",
         },
         "decode_tokens_per_s": out_legs.get("decode_b256", {}).get("tokens_per_s"),
@@ -692,6 +739,7 @@ def main():
         "roofline_chgate": roof_chgate,
         "roofline_backward": roof_bwd,
         "roofline_conv": roof_conv,
+        "roofline_conv_kernel": roof_conv_kernel,
         "roofline_conv_step": roof_convstep,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),

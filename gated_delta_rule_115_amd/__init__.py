@@ -30,7 +30,8 @@ __all__ = [
     "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
     "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward",
     "gdn_prefill_chunked_noalloc", "GDN_NOALLOC_SCRATCH_BYTES",
-    "gdn_prefill_chunked_kgla", "gdn_decode_step_kgla", "EXPORTED_SYMBOLS",
+    "gdn_prefill_chunked_kgla", "gdn_decode_step_kgla", "gdn_prefill_chunked_conv",
+    "EXPORTED_SYMBOLS",
 ]
 
 GDN_BF16 = 0
@@ -47,6 +48,7 @@ EXPORTED_SYMBOLS = (
     "gdn_prefill_chgate_workspace_bytes", "gdn_prefill_chunked_chgate", "gdn_decode_step_chgate",
     "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward",
     "gdn_prefill_chunked_noalloc", "gdn_prefill_chunked_kgla", "gdn_decode_step_kgla",
+    "gdn_prefill_chunked_conv",
 )
 
 # Size of the static scratch of gdn_prefill_chunked_noalloc (gdn.h).
@@ -85,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_decode_step.restype = i
     L.gdn_prefill_chunked_noalloc.restype = i
     L.gdn_prefill_chunked_noalloc.argtypes = [vp] * 8 + [i] * 8 + [f, vp]
+    L.gdn_prefill_chunked_conv.restype = i
+    L.gdn_prefill_chunked_conv.argtypes = [vp] * 6 + [i, f] + [vp] * 5 + [i] * 8 + [f, vp, sz, vp]
     L.gdn_decode_step.argtypes = [vp] * 8 + [i] * 6 + [f, vp]
     L.gdn_short_conv_silu.restype = i
     L.gdn_short_conv_silu.argtypes = [vp] * 3 + [i] * 5 + [f, i, i, vp]
@@ -222,6 +226,47 @@ def gdn_prefill_chunked_noalloc(q, k, v, alpha, beta, state_in, out, state_out=N
         _ptr(state_out), _ptr(out), B, T, H, Dk, Dv, chunk, _dtype_code(q), _dtype_code(out),
         float(scale), _stream(stream))
     _check("gdn_prefill_chunked_noalloc", st)
+    return out, state_out
+
+
+def gdn_prefill_chunked_conv(xq, xk, xv, taps_q, taps_k, taps_v, alpha, beta, state_in=None, *,
+                             conv_eps=1e-6, chunk=64, scale=1.0, out=None, out_dtype=None,
+                             state_out=None, workspace=None, want_state=True, stream=None):
+    """gdn_prefill_chunked on the raw projections: xq, xk, xv [B,T,H,128]
+    bf16 pass through the causal short convolution (taps_* [H*128, 4] f32,
+    taps[:, 3] on the current token) and SiLU, and q, k through the per-head
+    L2 normalisation (eps conv_eps), inside the prefill kernels.  Returns
+    (out [B,T,H,128], state_out [B,H,128,128] or None)."""
+    B, T, H, Dk = xq.shape
+    Dv = xv.shape[-1]
+    dt = _dtype_code(xq)
+    _dev(xq, "xq")
+    _dev(xk, "xk", xq.dtype, (B, T, H, Dk))
+    _dev(xv, "xv", xq.dtype, (B, T, H, Dv))
+    K = taps_q.shape[-1]
+    _dev(taps_q, "taps_q", torch.float32, (H * Dk, K))
+    _dev(taps_k, "taps_k", torch.float32, (H * Dk, K))
+    _dev(taps_v, "taps_v", torch.float32, (H * Dv, K))
+    _dev(alpha, "alpha", torch.float32, (B, T, H))
+    _dev(beta, "beta", torch.float32, (B, T, H))
+    _dev(state_in, "state_in", torch.float32, (B, H, Dk, Dv))
+    odt = _out_dtype(xq.dtype, out_dtype) if out is None else out.dtype
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=odt, device=xq.device)
+    _dev(out, "out", odt, (B, T, H, Dv))
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=xq.device)
+    _dev(state_out, "state_out", torch.float32, (B, H, Dk, Dv))
+    need = gdn_prefill_workspace_bytes(B, T, H, Dk, Dv, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=xq.device)
+    _dev(workspace, "workspace", torch.uint8)
+    st = lib().gdn_prefill_chunked_conv(
+        _ptr(xq), _ptr(xk), _ptr(xv), _ptr(taps_q), _ptr(taps_k), _ptr(taps_v), K,
+        float(conv_eps), _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(out),
+        B, T, H, Dk, Dv, chunk, dt, _dtype_code(out), float(scale), _ptr(workspace),
+        workspace.numel(), _stream(stream))
+    _check("gdn_prefill_chunked_conv", st)
     return out, state_out
 
 

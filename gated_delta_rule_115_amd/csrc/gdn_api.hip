@@ -224,6 +224,41 @@ int gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
   return hip_status(gdn::launch_prefill(p), "gdn_prefill_chunked_noalloc launch");
 }
 
+int gdn_prefill_chunked_conv(const void* xq, const void* xk, const void* xv,
+                             const float* taps_q, const float* taps_k, const float* taps_v,
+                             int conv_kernel, float conv_eps, const float* alpha,
+                             const float* beta, const float* state_in, float* state_out,
+                             void* out, int B, int T, int H, int Dk, int Dv, int chunk,
+                             int dtype, int out_dtype, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  gdn::PrefillArgs p;
+  size_t need = 0;
+  const int st = check_prefill(xq, xk, xv, alpha, beta, state_in, state_out, out, B, T, H, Dk,
+                               Dv, chunk, dtype, out_dtype, scale, &p, &need);
+  if (st != GDN_OK) return st;
+  REQUIRE(conv_kernel == 4, GDN_ERR_UNSUPPORTED,
+          "gdn_prefill_chunked_conv: conv_kernel %d (the fused convolution has 4 taps)",
+          conv_kernel);
+  REQUIRE(dtype == GDN_BF16 && Dk == 128 && Dv == 128 && chunk == 64, GDN_ERR_UNSUPPORTED,
+          "gdn_prefill_chunked_conv: needs bf16 inputs, Dk = Dv = 128, chunk 64");
+  REQUIRE(conv_eps >= 0.f && conv_eps <= 1e30f, GDN_ERR_INVALID_ARG,
+          "gdn_prefill_chunked_conv: conv_eps %g not in [0, 1e30]", (double)conv_eps);
+  if ((long long)B * H == 0) return ok();
+  if (T > 0)
+    REQUIRE(taps_q != nullptr && taps_k != nullptr && taps_v != nullptr, GDN_ERR_INVALID_ARG,
+            "gdn_prefill_chunked_conv: taps_q/taps_k/taps_v is NULL");
+  if (need > 0) {
+    REQUIRE(workspace != nullptr, GDN_ERR_INVALID_ARG, "workspace is NULL");
+    REQUIRE(((uintptr_t)workspace & 255u) == 0, GDN_ERR_INVALID_ARG,
+            "workspace is not 256-byte aligned");
+    REQUIRE(workspace_bytes >= need, GDN_ERR_INVALID_ARG,
+            "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  }
+  p.taps_q = taps_q; p.taps_k = taps_k; p.taps_v = taps_v; p.conv_eps = conv_eps;
+  p.workspace = workspace; p.stream = stream;
+  return hip_status(gdn::launch_prefill(p), "gdn_prefill_chunked_conv launch");
+}
+
 int gdn_decode_step(const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta,
                     const float* state_in, float* state_out, void* out, int B,

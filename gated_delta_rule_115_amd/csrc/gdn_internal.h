@@ -39,6 +39,12 @@ struct PrefillArgs {
   // Channel-gate kernels only: gated linear attention with a key-dependent
   // gate (no erase, gate alpha o (1 - beta k o k), write k v^T).
   bool kgla = false;
+  // Per-head kernels only: q, k, v are the raw projections, and the causal
+  // short convolution (4 taps, zero history before token 0) + SiLU, with the
+  // L2 normalisation of q and k, runs in the kernels' tile loads.  taps_*
+  // [H * Dk][4] f32; all three or none.
+  const float *taps_q = nullptr, *taps_k = nullptr, *taps_v = nullptr;
+  float conv_eps = 0.f;
 };
 
 struct ConvArgs {
@@ -78,6 +84,8 @@ size_t prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, b
 // sequences of few heads are split into P segments: segment 0 of L0 chunks,
 // the others of L (the last may be shorter); P = 1: one pass, no workspace.
 bool prefill_head_supported(const PrefillArgs& p);
+// ... and with the fused short convolution (dense sequences only).
+bool prefill_head_conv_supported(const PrefillArgs& p);
 void prefill_head_segments(int B, int T, int H, int* P, int* L0, int* L);
 size_t prefill_head_workspace_bytes(int B, int T, int H);
 hipError_t launch_prefill_head(const PrefillArgs& p);

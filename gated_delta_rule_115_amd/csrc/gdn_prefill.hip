@@ -647,6 +647,11 @@ static hipError_t launch_prefill_c(const PrefillArgs& p) {
 
 hipError_t launch_prefill(const PrefillArgs& p) {
   if (p.B * p.H == 0) return hipSuccess;
+  if (p.taps_q) {
+    // The fused convolution exists in the per-head kernels only.
+    if (p.T > 0 && !prefill_head_conv_supported(p)) return hipErrorInvalidValue;
+    if (p.T > 0) return launch_prefill_head(p);
+  }
   if (prefill_head_supported(p)) return launch_prefill_head(p);
   // The other kernels address dense [B, T, ...] tensors.
   if (p.T > 0 && p.B > 1 && p.seq_stride > 0 && p.seq_stride != p.T) return hipErrorInvalidValue;

@@ -124,6 +124,7 @@ struct __align__(16) HSmem {
   h16x4 Pb[6][64][2];    // P operands per (row tile, 32-token step); halves = block columns
   HGate g[3];            // slot = chunk % 3
   float Iv4[kInv4Scratch];  // diagonal blocks of A, column-major (helper wave 4)
+  float tap[3][HD * 4];  // fused short conv: this head's taps of q, k, v
 };
 
 // Slot of P block (R, C) in Pb: row tile R, 32-token step C / 2.
@@ -166,6 +167,118 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t rs, int off, f32x4
   } else {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, off, 0, 0);
   }
+}
+
+// Short convolution fused into the tile loads (section 4, "Adapting Q/K/V"):
+// the kernels then read the raw projections and apply, per channel,
+//   y_t = SiLU(sum_{j<4} taps[c][j] x_{t-3+j}),  x_{<0} = 0,
+// then, for q and k, y / (||y||_2 + eps) over the head's 128 channels, in f32,
+// and round the result to f16 once, as the MFMA operand (never to bf16).  A
+// loader thread owns rows 4 g .. 4 g + 3 of a chunk and channels pc .. pc + 7
+// and loads those rows and the three before them (from the previous chunk or
+// segment; zero before the sequence start), so its rows' convolution needs no
+// data from other threads; the 16 lanes sharing g hold one token's 128
+// channels and sum the squares for the norm.
+struct ConvTaps {
+  const float *q, *k, *v;  // [H * 128][4] each
+  float eps;
+};
+struct ConvRows {
+  bf16x8 r[7];  // rows 4 g - 3 .. 4 g + 3
+};
+// Loads of the rows of chunk start t0 (relative to the segment start; tabs0
+// = absolute token of the segment start) for row group g: rows before the
+// sequence start read the segment's first row (zeroed when used), rows past
+// the end read the last row.
+__device__ __forceinline__ void conv_issue(ConvRows& x, const bf16* base, int t0, int g, int pc,
+                                           int Ts, int tabs0, int tok) {
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const int t = min(max(t0 + 4 * g - 3 + j, -tabs0), Ts - 1);
+    gld16(x.r[j], base + (ptrdiff_t)t * tok + pc);
+  }
+}
+// Sum over the 16 lanes of a DPP row (every lane receives it): quad swaps,
+// then the half-row and row mirrors.
+__device__ __forceinline__ float row_sum16(float x) {
+  auto dpp = [](float v, auto ctrl) -> float {
+    constexpr int C = decltype(ctrl)::value;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), C, 0xf, 0xf, false));
+  };
+  x += dpp(x, ic<0xB1>());   // quad_perm [1, 0, 3, 2]
+  x += dpp(x, ic<0x4E>());   // quad_perm [2, 3, 0, 1]
+  x += dpp(x, ic<0x141>());  // row_half_mirror
+  x += dpp(x, ic<0x140>());  // row_mirror
+  return x;
+}
+// The convolution, SiLU and (l2) norm of the thread's 4 rows, f32.  tabs_r0:
+// absolute token of row 4 g - 3; taps: this head's [128][4] in LDS.
+__device__ __forceinline__ void conv_rows(const ConvRows& x, const float* taps, int pc, int tabs_r0,
+                                          bool l2, float eps, float (&o)[4][8]) {
+  float w[8][4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const f32x4 tw = ldf4(taps + 4 * (pc + e));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[e][j] = tw[j];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float xv = (tabs_r0 + u + j >= 0) ? (float)x.r[u + j][e] : 0.f;
+        a = __builtin_fmaf(w[e][j], xv, a);
+      }
+      o[u][e] = a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
+      ss = __builtin_fmaf(o[u][e], o[u][e], ss);
+    }
+    if (l2) {
+      ss = row_sum16(ss);
+      const float inv = __builtin_amdgcn_rcpf(__builtin_sqrtf(ss) + eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[u][e] *= inv;
+    }
+  }
+}
+// The 4 conv'd rows to a tile (f16), scaled per row by av[4 g + u] when given.
+__device__ __forceinline__ void conv_store(h16* tile, const float (&o)[4][8], int g, int pc,
+                                           const float* av) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float a = av ? av[4 * g + u] : 1.f;
+    h16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (h16)(a * o[u][e]);
+    *reinterpret_cast<h16x8*>(tile + (4 * g + u) * HRS + pc) = y;
+  }
+}
+// Waits for every load still in flight at the end of a pipelined loop, with
+// the registers they write tied to the wait: the loads of the last
+// iterations are never consumed, and without the tie the compiler would
+// take those registers as free while the loads are still in flight.
+__device__ __forceinline__ void vm_drain(bf16x8 (&r)[2][2]) {
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[1][0]), "+v"(r[1][1])::"memory");
+}
+__device__ __forceinline__ void vm_drain(bf16x8 (&r)[2][4]) {
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[0][2]), "+v"(r[0][3]), "+v"(r[1][0]),
+                 "+v"(r[1][1]), "+v"(r[1][2]), "+v"(r[1][3])::"memory");
+}
+__device__ __forceinline__ void vm_drain(float (&a)[2], float (&b)[2]) {
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1])::"memory");
+}
+// Waits for the loads of a ConvRows (the registers are tied to the wait).
+template <int N>
+__device__ __forceinline__ void vm_wait_rows(ConvRows& x) {
+  asm volatile("s_waitcnt vmcnt(%7)"
+               : "+v"(x.r[0]), "+v"(x.r[1]), "+v"(x.r[2]), "+v"(x.r[3]), "+v"(x.r[4]), "+v"(x.r[5]),
+                 "+v"(x.r[6])
+               : "n"(N)
+               : "memory");
 }
 
 // Per-head workspace of the segment split: M_s, B_s (segments 0 .. P - 2) and
@@ -293,6 +406,7 @@ struct __align__(16) TSmem {
   h16x4 Dg[2][7][64];    // D(T00), D(T00^T), D(T11), D(T11^T), D(T22), D(T22^T), D(T33^T)
   HGate g[4];            // slot = chunk % 4
   float Iv[4][kInvScratch];  // inverse scratch of waves 0-3
+  float tap[2][HD * 4];  // fused short conv: this head's taps of k, v
 };
 
 // Transition pass of one segment (chunks c0 .. c0 + NC - 1 of head (b, h)):
@@ -309,12 +423,15 @@ struct __align__(16) TSmem {
 // Every chunk of a transition segment lies inside the sequence (only the last
 // segment can be ragged, and it has no transition).  B_s and M_s go to dstB
 // and dstM (128 x 128 f32, [key][column]).
+// With the fused convolution (CV), waves 0-3 load and convolve K at the top
+// of the iteration and waves 4-7 V at its end; wave 7 also loads the gates.
+template <bool CV>
 __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __restrict__ k,
                                                    const bf16* __restrict__ v,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta, float* dstB,
                                                    float* dstM, int b, int h, int T, int TS,
-                                                   int H, int c0, int NC) {
+                                                   int H, int c0, int NC, const ConvTaps& ct) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -369,11 +486,35 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
   // (2), in this order, and consumes each two iterations later, when 10
   // later operations have been issued.
   bf16x8 kr[2][2], vr[2][2];
-  ld_tile(kh, 0, kr[0]);
-  ld_tile(kh, 1, kr[1]);
-  ld_gate(0, 0);
-  ld_gate(1, 1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Fused convolution: the rows of one chunk in flight per wave, K on waves
+  // 0-3 and V on waves 4-7.  At the top of iteration i every wave waits for
+  // its rows, convolves them into LDS (K of chunk i; av V of chunk i - 2)
+  // and requests the next (K of chunk i + 1; V of chunk i - 1); the gates of
+  // chunk i + 1 are requested in the middle of iteration i.  Every wave
+  // issues the same loads at the same points (only the addresses differ), so
+  // the rows' registers have one definition per iteration.
+  ConvRows xc;
+  const int cg = (tid & 255) >> 4, cpc = (tid & 15) * 8, tabs0 = c0 * HC;
+  const bf16* xbase = w < 4 ? kh : vh;
+  const int xlag = w < 4 ? 1 : -1;  // chunk requested at iteration i: i + xlag
+  auto cissue = [&](int c) {
+    c = min(max(c, 0), NC - 1);
+    conv_issue(xc, xbase, c * HC, cg, cpc, Ts, tabs0, tok);
+  };
+  if constexpr (CV) {
+    // This head's taps of k and v -> LDS.
+    for (int i = tid; i < 2 * HD * 4; i += HNT)
+      sm.tap[i / (HD * 4)][i % (HD * 4)] = (i < HD * 4 ? ct.k : ct.v)[(size_t)h * HD * 4 + i % (HD * 4)];
+    lds_barrier();
+    cissue(w < 4 ? 0 : -2);
+    ld_gate(0, 0);
+  } else {
+    ld_tile(kh, 0, kr[0]);
+    ld_tile(kh, 1, kr[1]);
+    ld_gate(0, 0);
+    ld_gate(1, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   auto wait10 = [](bf16x8* r) {
     asm volatile("s_waitcnt vmcnt(10)" : "+v"(r[0]), "+v"(r[1])::"memory");
   };
@@ -394,13 +535,33 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
     lane_offset(ll);
     const int llr = ll & 15, llq = ll >> 4;
 
-    wait10(kr[p]);
-    if (it < NC) {
+    if constexpr (CV) {
+      vm_wait_rows<2>(xc);
+      {
+        float o[4][8];
+        if (w < 4) {
+          // K of chunk it -> LDS (slot it % 4 was last read at iteration it - 1).
+          if (it < NC) {
+            conv_rows(xc, sm.tap[0], cpc, tabs0 + it * HC + 4 * cg - 3, true, ct.eps, o);
+            conv_store(sm.K[it & 3], o, cg, cpc, nullptr);
+          }
+        } else if (h2) {
+          // av V of chunk c2 -> LDS (slot c2 % 2 was last read at iteration
+          // c2 + 1; the recurrence reads it at c2 + 3).
+          conv_rows(xc, sm.tap[1], cpc, tabs0 + c2 * HC + 4 * cg - 3, false, ct.eps, o);
+          conv_store(sm.V[c2 & 1], o, cg, cpc, sm.g[c2 & 3].av);
+        }
+      }
+      cissue(it + xlag);
+    } else {
+      wait10(kr[p]);
+      if (it < NC) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<h16x8*>(sm.K[it & 3] + st_off + 32 * u * HRS) = bf16x8_to_h8(kr[p][u]);
+        for (int u = 0; u < 2; ++u)
+          *reinterpret_cast<h16x8*>(sm.K[it & 3] + st_off + 32 * u * HRS) = bf16x8_to_h8(kr[p][u]);
+      }
+      ld_tile(kh, it + 2, kr[p]);
     }
-    ld_tile(kh, it + 2, kr[p]);
 
     auto recurrence = [&]() {
       if (h3) {
@@ -581,6 +742,13 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
     recurrence();
     shared_stage();
 
+    if constexpr (CV) {
+      asm volatile("s_waitcnt vmcnt(7)" : "+v"(ra[0]), "+v"(rb[0])::"memory");
+      if (w == 7 && it < NC) gate_tables(sm.g[it & 3], ra[0], rb[0], it * HC + ll < Ts, 1.f, ll);
+      ld_gate(it + 1, 0);
+      lds_barrier();
+      return;
+    }
     asm volatile("s_waitcnt vmcnt(10)" : "+v"(ra[p]), "+v"(rb[p])::"memory");
     if (w == 7 && it < NC) gate_tables(sm.g[it & 3], ra[p], rb[p], it * HC + ll < Ts, 1.f, ll);
     ld_gate(it + 2, p);
@@ -603,12 +771,23 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
   };
 
   // Chunk c completes its recurrence step at iteration c + 3.
+  // The odd last iteration is peeled rather than guarded inside the loop, so
+  // every path back to the loop head passes both copies of the body (the
+  // fixed vmcnt waits count the loads of both).
   const int NIT = NC + 3;
-  for (int it = 0; it < NIT; it += 2) {
+  int it = 0;
+  for (; it + 1 < NIT; it += 2) {
     body(it, ic<0>());
-    if (it + 1 < NIT) body(it + 1, ic<1>());
+    body(it + 1, ic<1>());
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (it < NIT) body(it, ic<0>());
+  if constexpr (CV) {
+    vm_wait_rows<0>(xc);
+  } else {
+    vm_drain(kr);
+    vm_drain(vr);
+  }
+  vm_drain(ra, rb);
 
   float* dst = dstB;
   float* dstm = dstM;
@@ -641,14 +820,15 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
 // recurrence waves S~ update, (P U^)^T and the outputs of chunk i - 2;
 // helpers: off-diagonal blocks of Tm (i - 1), gate tables (i), Q of chunk
 // i - 1 and av V of chunk i - 1 -> LDS.
-template <class TOut>
+template <class TOut, bool CV>
 __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ q,
                                             const bf16* __restrict__ k,
                                             const bf16* __restrict__ v,
                                             const float* __restrict__ alpha,
                                             const float* __restrict__ beta, const float* s0,
                                             float* s_final, TOut* __restrict__ out, int b, int h,
-                                            int T, int TS, int H, int c0, int NC, float scale) {
+                                            int T, int TS, int H, int c0, int NC, float scale,
+                                            const ConvTaps& ct) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -660,6 +840,15 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
   if (tid < 64) {  // zero halves of the P operands (block columns above the diagonal)
     sm.Pb[0][tid][1] = h16x4{0, 0, 0, 0};
     sm.Pb[3][tid][1] = h16x4{0, 0, 0, 0};
+  }
+  if constexpr (CV) {
+    // This head's taps of q, k, v -> LDS (read by the helpers' tile loads).
+    for (int i = tid; i < 3 * HD * 4; i += HNT) {
+      const int sq = i / (HD * 4), e = i % (HD * 4);
+      const float* src = sq == 0 ? ct.q : sq == 1 ? ct.k : ct.v;
+      sm.tap[sq][e] = src[(size_t)h * HD * 4 + e];
+    }
+    lds_barrier();
   }
   // Fragment rows 16 R .. 16 R + 15, 32-key step j: lane row lr, keys 32 j + 8 lq .. + 7.
   // The lane offsets are passed through an empty asm once per iteration
@@ -921,13 +1110,37 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
       gld4(ra[p], ah + (size_t)t * H);
       gld4(rb[p], bhp + (size_t)t * H);
     };
-    ld_tile(kh, 0, kr[0]);
-    ld_tile(kh, 1, kr[1]);
-    ld_gate(0, 0);
-    ld_gate(1, 1);
-    ld_tile(qh, 0, qr[1]);
-    ld_tile(vh, 0, vr[1]);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Fused convolution: one register slot per stream, a tile's rows are
+    // loaded one iteration before it goes to LDS.  Each iteration issues K 7
+    // loads (phase 1), gates 2, Q 7, V 7 (phase 2), in this order; a stream
+    // is consumed when 16 later operations (21 for the gates) have been
+    // issued.
+    ConvRows xk, xq, xv;
+    const int cg = ht >> 4, tabs0 = c0 * HC;
+    auto cissue = [&](ConvRows& x, const bf16* base, int c) {
+      c = min(max(c, 0), NC - 1);
+      conv_issue(x, base, c * HC, cg, pc, Ts, tabs0, tok);
+    };
+    auto cput = [&](const ConvRows& x, const float* taps, bool l2, int c, h16* tile,
+                    const float* av) {
+      float o[4][8];
+      conv_rows(x, taps, pc, tabs0 + c * HC + 4 * cg - 3, l2, ct.eps, o);
+      conv_store(tile, o, cg, pc, av);
+    };
+    if constexpr (CV) {
+      cissue(xk, kh, 0);
+      ld_gate(0, 0);
+      cissue(xq, qh, -1);
+      cissue(xv, vh, -1);
+    } else {
+      ld_tile(kh, 0, kr[0]);
+      ld_tile(kh, 1, kr[1]);
+      ld_gate(0, 0);
+      ld_gate(1, 1);
+      ld_tile(qh, 0, qr[1]);
+      ld_tile(vh, 0, vr[1]);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     // Each iteration issues K 4 loads (phase 1), gates 2, Q 4, V 4 (phase 2),
     // in this order; a stream is consumed two iterations after its loads,
     // when 24 later operations (26 for the gates) have been issued.
@@ -940,10 +1153,17 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
       const bool h1 = c1 >= 0 && c1 < NC;
       const bool h2 = c2 >= 0 && c2 < NC;
       lane_offset(fb);
-      // ---- phase 1
-      wait24(kr[p]);
-      if (it < NC) st_tile(sm.K[it % 3], kr[p]);  // slot it % 3 was last read in phase 2 of it - 1
-      ld_tile(kh, it + 2, kr[p]);
+      // ---- phase 1: K of chunk it -> LDS (slot it % 3 was last read in
+      // phase 2 of it - 1)
+      if constexpr (CV) {
+        vm_wait_rows<16>(xk);
+        if (it < NC) cput(xk, sm.tap[1], true, it, sm.K[it % 3], nullptr);
+        cissue(xk, kh, it + 1);
+      } else {
+        wait24(kr[p]);
+        if (it < NC) st_tile(sm.K[it % 3], kr[p]);
+        ld_tile(kh, it + 2, kr[p]);
+      }
       if (h1) {
         // Chunk c1: helper 0 forms the four diagonal blocks of A and inverts
         // them all (one lane per block column); helpers 1-3 form the
@@ -1032,6 +1252,21 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 6; ++i) sm.Tc[c1 & 1][i][l] = tc[i];
       }
+      if constexpr (CV) {
+        asm volatile("s_waitcnt vmcnt(21)" : "+v"(ra[0]), "+v"(rb[0]) :: "memory");
+        if (hw == 2 && it < NC) gate_tables(sm.g[it % 3], ra[0], rb[0], it * HC + l < Ts, scale, l);
+        ld_gate(it + 1, 0);
+        vm_wait_rows<16>(xq);
+        if (h1) cput(xq, sm.tap[0], true, c1, sm.Q, nullptr);
+        cissue(xq, qh, it);
+        vm_wait_rows<16>(xv);
+        // av V of chunk c1 -> LDS (read by the recurrence waves in phase 1
+        // of the next iteration).
+        if (h1) cput(xv, sm.tap[2], false, c1, sm.V, sm.g[c1 % 3].av);
+        cissue(xv, vh, it);
+        lds_barrier();
+        return;
+      }
       asm volatile("s_waitcnt vmcnt(26)" : "+v"(ra[p]), "+v"(rb[p]) :: "memory");
       if (hw == 2 && it < NC) gate_tables(sm.g[it % 3], ra[p], rb[p], it * HC + l < Ts, scale, l);
       ld_gate(it + 2, p);
@@ -1055,10 +1290,23 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
       ld_tile(vh, it + 1, vr[p]);
       lds_barrier();
     };
-    for (int it = 0; it < NIT; it += 2) {
+    // Odd last iteration peeled, as in the transition pass.
+    int it = 0;
+    for (; it + 1 < NIT; it += 2) {
       hbody(it, ic<0>());
-      if (it + 1 < NIT) hbody(it + 1, ic<1>());
+      hbody(it + 1, ic<1>());
     }
+    if (it < NIT) hbody(it, ic<0>());
+    if constexpr (CV) {
+      vm_wait_rows<0>(xk);
+      vm_wait_rows<0>(xq);
+      vm_wait_rows<0>(xv);
+    } else {
+      vm_drain(kr);
+      vm_drain(qr);
+      vm_drain(vr);
+    }
+    vm_drain(ra, rb);
   }
 }
 
@@ -1071,33 +1319,34 @@ union __align__(16) PrefillSmem {
 // s): s = 0 runs the output pass of segment 0 from the state in and leaves
 // its final state, the initial state of segment 1, in the workspace; s >= 1
 // runs the transition pass of segment s.
-template <class TOut>
+template <class TOut, bool CV>
 __global__ __launch_bounds__(HNT) void prefill_lead_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
-    TOut* __restrict__ out, SegWs ws, SegGeom g, int T, int TS, int H, float scale) {
+    TOut* __restrict__ out, SegWs ws, SegGeom g, int T, int TS, int H, float scale,
+    ConvTaps ct) {
   __shared__ PrefillSmem sm;
   const int bh = blockIdx.x / (g.P - 1), s = blockIdx.x % (g.P - 1);
   const int b = bh / H, h = bh % H;
   if (s == 0) {
-    out_segment<TOut>(sm.h, q, k, v, alpha, beta,
-                      state_in ? state_in + (size_t)bh * HD * HD : nullptr,
-                      ws.S + ws.at(bh, 0, g.P), out, b, h, T, TS, H, 0, g.count(0), scale);
+    out_segment<TOut, CV>(sm.h, q, k, v, alpha, beta,
+                          state_in ? state_in + (size_t)bh * HD * HD : nullptr,
+                          ws.S + ws.at(bh, 0, g.P), out, b, h, T, TS, H, 0, g.count(0), scale, ct);
   } else {
-    transition_segment(sm.t, k, v, alpha, beta, ws.B + ws.at(bh, s, g.P),
-                       ws.M + ws.at(bh, s, g.P), b, h, T, TS, H, g.first(s), g.count(s));
+    transition_segment<CV>(sm.t, k, v, alpha, beta, ws.B + ws.at(bh, s, g.P),
+                           ws.M + ws.at(bh, s, g.P), b, h, T, TS, H, g.first(s), g.count(s), ct);
   }
 }
 
 // Output pass of segments s_first .. P - 1 (work-group = head * (P - s_first)
 // + s - s_first) from their initial states (segment 0: the state in; others:
 // the workspace); segment P - 1 writes the final state.
-template <class TOut>
+template <class TOut, bool CV>
 __global__ __launch_bounds__(HNT) void prefill_out_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* state_in,
     float* state_out, TOut* __restrict__ out, SegWs ws, SegGeom g, int s_first, int T, int TS,
-    int H, float scale) {
+    int H, float scale, ConvTaps ct) {
   __shared__ HSmem sm;
   const int n = g.P - s_first;
   const int bh = blockIdx.x / n, s = s_first + blockIdx.x % n;
@@ -1105,8 +1354,8 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
   const float* s0 = s == 0 ? (state_in ? state_in + (size_t)bh * HD * HD : nullptr)
                            : ws.S + ws.at(bh, s - 1, g.P);
   float* sf = (s == g.P - 1 && state_out) ? state_out + (size_t)bh * HD * HD : nullptr;
-  out_segment<TOut>(sm, q, k, v, alpha, beta, s0, sf, out, b, h, T, TS, H, g.first(s),
-                    g.count(s), scale);
+  out_segment<TOut, CV>(sm, q, k, v, alpha, beta, s0, sf, out, b, h, T, TS, H, g.first(s),
+                        g.count(s), scale, ct);
 }
 
 // Initial states of segments 2 .. P - 1: from S_1 (left in the workspace by
@@ -1181,6 +1430,11 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
 bool prefill_head_supported(const PrefillArgs& p) {
   return p.bf16 && p.Dk == HD && p.Dv == HD && p.chunk == HC && p.T > 0;
 }
+// The fused convolution additionally reads each sequence's rows from its
+// start (no history before token 0), so sequences must be dense.
+bool prefill_head_conv_supported(const PrefillArgs& p) {
+  return prefill_head_supported(p) && (p.seq_stride == 0 || p.seq_stride == p.T);
+}
 
 // Segments per head.  Both segmented launches (the output pass of segment 0
 // beside the transition passes of segments 1 .. P - 2, then the output passes
@@ -1220,8 +1474,9 @@ size_t prefill_head_workspace_bytes(int B, int T, int H) {
   return 3 * (size_t)B * H * (P - 1) * HD * HD * sizeof(float);
 }
 
-template <class TOut>
+template <class TOut, bool CV>
 static hipError_t launch_head_t(const PrefillArgs& p) {
+  const ConvTaps ct{p.taps_q, p.taps_k, p.taps_v, p.conv_eps};
   SegGeom g;
   g.NCT = (p.T + HC - 1) / HC;
   prefill_head_segments(p.B, p.T, p.H, &g.P, &g.L0, &g.L);
@@ -1236,21 +1491,22 @@ static hipError_t launch_head_t(const PrefillArgs& p) {
     ws.M = (float*)p.workspace;
     ws.B = ws.M + n;
     ws.S = ws.B + n;
-    hipLaunchKernelGGL((prefill_lead_kernel<TOut>), dim3(BH * (g.P - 1)), dim3(HNT), 0, st, q, k,
-                       v, p.alpha, p.beta, p.state_in, (TOut*)p.out, ws, g, p.T, TS, p.H,
-                       p.scale);
+    hipLaunchKernelGGL((prefill_lead_kernel<TOut, CV>), dim3(BH * (g.P - 1)), dim3(HNT), 0, st, q,
+                       k, v, p.alpha, p.beta, p.state_in, (TOut*)p.out, ws, g, p.T, TS, p.H,
+                       p.scale, ct);
     if (g.P > 2)
       hipLaunchKernelGGL(segment_combine_kernel, dim3(BH * 8), dim3(256), 0, st, ws, g.P);
     s_first = 1;
   }
-  hipLaunchKernelGGL((prefill_out_kernel<TOut>), dim3(BH * (g.P - s_first)), dim3(HNT), 0, st, q,
-                     k, v, p.alpha, p.beta, p.state_in, p.state_out, (TOut*)p.out, ws, g, s_first,
-                     p.T, TS, p.H, p.scale);
+  hipLaunchKernelGGL((prefill_out_kernel<TOut, CV>), dim3(BH * (g.P - s_first)), dim3(HNT), 0, st,
+                     q, k, v, p.alpha, p.beta, p.state_in, p.state_out, (TOut*)p.out, ws, g,
+                     s_first, p.T, TS, p.H, p.scale, ct);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_head(const PrefillArgs& p) {
-  return p.out_bf16 ? launch_head_t<bf16>(p) : launch_head_t<float>(p);
+  if (p.taps_q) return p.out_bf16 ? launch_head_t<bf16, true>(p) : launch_head_t<float, true>(p);
+  return p.out_bf16 ? launch_head_t<bf16, false>(p) : launch_head_t<float, false>(p);
 }
 
 }  // namespace gdn

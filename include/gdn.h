@@ -140,6 +140,39 @@ int gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
                                 void* stream);
 
 /*
+ * gdn_prefill_chunked on the raw q, k, v projections, with the projection
+ * adaptation of section 4 ("Adapting Q/K/V") done inside the prefill's tile
+ * loads: per head and channel c, with x the raw projection and K = 4,
+ *   q_t = n(SiLU(sum_j taps_q[c][j] * xq_{t-3+j}[c])),  likewise k with taps_k
+ *   v_t =   SiLU(sum_j taps_v[c][j] * xv_{t-3+j}[c])
+ *   x_{<0} = 0 (every sequence starts with an empty convolution history),
+ *   n(y) = y / (||y||_2 + conv_eps) over the head's Dk channels (the key
+ *   normalisation of appendix B.1, "Metric 1"), then the recurrence exactly
+ *   as gdn_prefill_chunked on those q, k, v.  The convolution, SiLU and
+ *   norm run in f32 and their results go to the MFMA operands in f16 once:
+ *   they are never rounded to bf16 nor written to memory.
+ *   xq, xk, xv [B, T, H, 128] bf16 (the projections, channels of a head
+ *              consecutive: the [B, T, H * 128] layout of gdn_short_conv_silu)
+ *   taps_q, taps_k, taps_v [H * 128, conv_kernel] f32; taps[c][3] multiplies
+ *              the current token
+ *   conv_eps   >= 0 (0 gives NaN for an all-zero convolution output)
+ *   everything else as gdn_prefill_chunked (same workspace size).
+ * Limits: dtype GDN_BF16, Dk = Dv = 128, chunk = 64, conv_kernel = 4
+ * (otherwise GDN_ERR_UNSUPPORTED).  The SiLU outputs of q and k are
+ * normalised, so the f16 operand range holds for them; v's SiLU output must
+ * stay below 65504 in magnitude, as gdn_prefill_chunked's v.
+ */
+int gdn_prefill_chunked_conv(const void* xq, const void* xk, const void* xv,
+                             const float* taps_q, const float* taps_k,
+                             const float* taps_v, int conv_kernel,
+                             float conv_eps, const float* alpha,
+                             const float* beta, const float* state_in,
+                             float* state_out, void* out, int B, int T, int H,
+                             int Dk, int Dv, int chunk, int dtype,
+                             int out_dtype, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * One recurrence step for a batch of sequences (section 3.1.2 at a single
  * token; the recurrent form used for generation):
  *   q, k [B, H, Dk] dtype;  v [B, H, Dv] dtype;  alpha, beta [B, H] f32

@@ -110,6 +110,28 @@ def test_decode_validation():
     assert call(B=0, q=None) == OK
 
 
+def test_prefill_conv_validation():
+    """gdn_prefill_chunked_conv: argument checks only (nothing is launched)."""
+    L = gdn.lib()
+
+    def call(**kw):
+        a = dict(x=A, taps=A, K=4, eps=1e-6, B=1, T=64, H=2, Dk=128, Dv=128, chunk=64,
+                 dt=BF16, ws=A)
+        a.update(kw)
+        return L.gdn_prefill_chunked_conv(
+            a["x"], A, A, a["taps"], A, A, a["K"], a["eps"], A, A, None, None, A, a["B"],
+            a["T"], a["H"], a["Dk"], a["Dv"], a["chunk"], a["dt"], BF16, 1.0, a["ws"], 1 << 40,
+            None)
+    assert call(K=3) == UNSUPPORTED and "4 taps" in _err()
+    assert call(Dk=64, Dv=64) == UNSUPPORTED and "Dk = Dv = 128" in _err()
+    assert call(chunk=32) == UNSUPPORTED
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(eps=-1.0) == INVALID and "conv_eps" in _err()
+    assert call(taps=None) == INVALID and "taps" in _err()
+    assert call(x=None) == INVALID and "is NULL" in _err()
+    assert call(B=0, x=None, taps=None) == OK
+
+
 def test_conv_validation():
     L = gdn.lib()
     call = lambda **kw: L.gdn_short_conv_silu(
