@@ -211,10 +211,30 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp(x, ic<0x140>());  // row_mirror
   return x;
 }
-// The convolution, SiLU and (l2) norm of the thread's 4 rows, f32.  tabs_r0:
-// absolute token of row 4 g - 3; taps: this head's [128][4] in LDS.
+// The taps are staged in LDS multiplied by -log2(e), so the weighted sum is
+// a' = -log2(e) a and 2^a' = e^-a feeds the sigmoid directly: the kernels
+// form o' = a' / (1 + 2^a') = -log2(e) SiLU(a) and fold the constant into
+// the per-row factor that follows (the norm's, or v's gate factor).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// The convolution and SiLU of the thread's 4 rows (o' above, f32), and per
+// row the factor m that turns o' into the operand: with l2, -1 / (||o||_2 +
+// eps) over the head's 128 channels (o = SiLU(a)); without, -ln 2.  tabs_r0:
+// absolute token of row 4 g - 3; taps: this head's scaled [128][4] in LDS;
+// edge (uniform over the wave): the chunk starts within 3 tokens of the
+// sequence start, so some rows may lie before it and read as zero.
 __device__ __forceinline__ void conv_rows(const ConvRows& x, const float* taps, int pc, int tabs_r0,
-                                          bool l2, float eps, float (&o)[4][8]) {
+                                          bool edge, bool l2, float eps, float (&o)[4][8],
+                                          float (&m)[4]) {
+  bf16x8 r[7];
+#pragma unroll
+  for (int j = 0; j < 7; ++j) r[j] = x.r[j];
+  if (edge) {
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+      if (tabs_r0 + j < 0) r[j] = bf16x8{};
+  }
   float w[8][4];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -229,27 +249,25 @@ __device__ __forceinline__ void conv_rows(const ConvRows& x, const float* taps, 
     for (int e = 0; e < 8; ++e) {
       float a = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float xv = (tabs_r0 + u + j >= 0) ? (float)x.r[u + j][e] : 0.f;
-        a = __builtin_fmaf(w[e][j], xv, a);
-      }
-      o[u][e] = a * __builtin_amdgcn_rcpf(1.f + __expf(-a));
+      for (int j = 0; j < 4; ++j) a = __builtin_fmaf(w[e][j], (float)r[u + j][e], a);
+      o[u][e] = a * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a));
       ss = __builtin_fmaf(o[u][e], o[u][e], ss);
     }
     if (l2) {
+      // ||o'|| = log2(e) ||o||, so eps scales by log2(e) too.
       ss = row_sum16(ss);
-      const float inv = __builtin_amdgcn_rcpf(__builtin_sqrtf(ss) + eps);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[u][e] *= inv;
+      m[u] = -__builtin_amdgcn_rcpf(__builtin_sqrtf(ss) + eps * kLog2e);
+    } else {
+      m[u] = -kLn2;
     }
   }
 }
-// The 4 conv'd rows to a tile (f16), scaled per row by av[4 g + u] when given.
-__device__ __forceinline__ void conv_store(h16* tile, const float (&o)[4][8], int g, int pc,
-                                           const float* av) {
+// The 4 rows m o' (times av[4 g + u] when given) to a tile in f16.
+__device__ __forceinline__ void conv_store(h16* tile, const float (&o)[4][8], const float (&m)[4],
+                                           int g, int pc, const float* av) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const float a = av ? av[4 * g + u] : 1.f;
+    const float a = av ? av[4 * g + u] * m[u] : m[u];
     h16x8 y;
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = (h16)(a * o[u][e]);
@@ -487,26 +505,32 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
   // later operations have been issued.
   bf16x8 kr[2][2], vr[2][2];
   // Fused convolution: the rows of one chunk in flight per wave, K on waves
-  // 0-3 and V on waves 4-7.  At the top of iteration i every wave waits for
-  // its rows, convolves them into LDS (K of chunk i; av V of chunk i - 2)
-  // and requests the next (K of chunk i + 1; V of chunk i - 1); the gates of
-  // chunk i + 1 are requested in the middle of iteration i.  Every wave
-  // issues the same loads at the same points (only the addresses differ), so
-  // the rows' registers have one definition per iteration.
+  // 0-3 and V on waves 4-7.  Every wave requests its next rows at the top of
+  // iteration i (K of chunk i + 1; V of chunk i - 2) -- one definition of the
+  // rows' registers per iteration, outside any branch -- and the gates of
+  // chunk i + 1 in its middle.  K waves convolve K of chunk i into LDS at the
+  // top, before their recurrence step; V waves convolve av V of chunk i - 2
+  // at the end, after theirs, so on each SIMD one wave's convolution runs
+  // beside the other's matrix products.
   ConvRows xc;
   const int cg = (tid & 255) >> 4, cpc = (tid & 15) * 8, tabs0 = c0 * HC;
   const bf16* xbase = w < 4 ? kh : vh;
-  const int xlag = w < 4 ? 1 : -1;  // chunk requested at iteration i: i + xlag
   auto cissue = [&](int c) {
     c = min(max(c, 0), NC - 1);
     conv_issue(xc, xbase, c * HC, cg, cpc, Ts, tabs0, tok);
   };
+  auto cput = [&](const float* taps, bool l2, int c, h16* tile, const float* av) {
+    float o[4][8], m[4];
+    conv_rows(xc, taps, cpc, tabs0 + c * HC + 4 * cg - 3, tabs0 + c * HC < 3, l2, ct.eps, o, m);
+    conv_store(tile, o, m, cg, cpc, av);
+  };
   if constexpr (CV) {
     // This head's taps of k and v -> LDS.
     for (int i = tid; i < 2 * HD * 4; i += HNT)
-      sm.tap[i / (HD * 4)][i % (HD * 4)] = (i < HD * 4 ? ct.k : ct.v)[(size_t)h * HD * 4 + i % (HD * 4)];
+      sm.tap[i / (HD * 4)][i % (HD * 4)] =
+          -kLog2e * (i < HD * 4 ? ct.k : ct.v)[(size_t)h * HD * 4 + i % (HD * 4)];
     lds_barrier();
-    cissue(w < 4 ? 0 : -2);
+    if (w < 4) cissue(0);
     ld_gate(0, 0);
   } else {
     ld_tile(kh, 0, kr[0]);
@@ -536,23 +560,14 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
     const int llr = ll & 15, llq = ll >> 4;
 
     if constexpr (CV) {
+      // K waves wait for K of chunk it here; for V waves, whose rows arrived
+      // before the end of the previous iteration, the wait is already met.
       vm_wait_rows<2>(xc);
-      {
-        float o[4][8];
-        if (w < 4) {
-          // K of chunk it -> LDS (slot it % 4 was last read at iteration it - 1).
-          if (it < NC) {
-            conv_rows(xc, sm.tap[0], cpc, tabs0 + it * HC + 4 * cg - 3, true, ct.eps, o);
-            conv_store(sm.K[it & 3], o, cg, cpc, nullptr);
-          }
-        } else if (h2) {
-          // av V of chunk c2 -> LDS (slot c2 % 2 was last read at iteration
-          // c2 + 1; the recurrence reads it at c2 + 3).
-          conv_rows(xc, sm.tap[1], cpc, tabs0 + c2 * HC + 4 * cg - 3, false, ct.eps, o);
-          conv_store(sm.V[c2 & 1], o, cg, cpc, sm.g[c2 & 3].av);
-        }
+      if (w < 4 && it < NC) {
+        // K of chunk it -> LDS (slot it % 4 was last read at iteration it - 1).
+        cput(sm.tap[0], true, it, sm.K[it & 3], nullptr);
       }
-      cissue(it + xlag);
+      cissue(w < 4 ? it + 1 : it - 2);
     } else {
       wait10(kr[p]);
       if (it < NC) {
@@ -746,6 +761,12 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
       asm volatile("s_waitcnt vmcnt(7)" : "+v"(ra[0]), "+v"(rb[0])::"memory");
       if (w == 7 && it < NC) gate_tables(sm.g[it & 3], ra[0], rb[0], it * HC + ll < Ts, 1.f, ll);
       ld_gate(it + 1, 0);
+      if (w >= 4) {
+        // av V of chunk c2 -> LDS (slot c2 % 2 was last read at iteration
+        // c2 + 1; the recurrence reads it at c2 + 3).
+        vm_wait_rows<2>(xc);
+        if (h2) cput(sm.tap[1], false, c2, sm.V[c2 & 1], sm.g[c2 & 3].av);
+      }
       lds_barrier();
       return;
     }
@@ -846,7 +867,7 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
     for (int i = tid; i < 3 * HD * 4; i += HNT) {
       const int sq = i / (HD * 4), e = i % (HD * 4);
       const float* src = sq == 0 ? ct.q : sq == 1 ? ct.k : ct.v;
-      sm.tap[sq][e] = src[(size_t)h * HD * 4 + e];
+      sm.tap[sq][e] = -kLog2e * src[(size_t)h * HD * 4 + e];
     }
     lds_barrier();
   }
@@ -1123,9 +1144,9 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
     };
     auto cput = [&](const ConvRows& x, const float* taps, bool l2, int c, h16* tile,
                     const float* av) {
-      float o[4][8];
-      conv_rows(x, taps, pc, tabs0 + c * HC + 4 * cg - 3, l2, ct.eps, o);
-      conv_store(tile, o, cg, pc, av);
+      float o[4][8], m[4];
+      conv_rows(x, taps, pc, tabs0 + c * HC + 4 * cg - 3, tabs0 + c * HC < 3, l2, ct.eps, o, m);
+      conv_store(tile, o, m, cg, pc, av);
     };
     if constexpr (CV) {
       cissue(xk, kh, 0);
