@@ -1029,17 +1029,24 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
         h16x4 kt[8][4];
         auto ktr = [&](int m, int r) { return ld_tr(Kb + tb + 16 * r * HRS + 32 * (m >> 1) + 4 * (m & 1)); };
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) kt[m][r] = ktr(m, r);
+        for (int m = 0; m < 8; ++m) kt[m][0] = ktr(m, 0), kt[m][1] = ktr(m, 1);
         __builtin_amdgcn_sched_barrier(0);
-        // S~ += K^T U^, breadth-first over the 16 state tiles.
+        // S~ += K^T U^, breadth-first over the 16 state tiles; the second
+        // half of the K^T fragments is read during the first half's products.
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const h16x8 k0 = cat8(kt[m][0], kt[m][1]);
 #pragma unroll
           for (int sl = 0; sl < 2; ++sl) S[sl][m] = mfma32(k0, udb[sl][0], S[sl][m]);
         }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) kt[m][2] = ktr(m, 2), kt[m][3] = ktr(m, 3);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         h16x8 pb[6];
 #pragma unroll
         for (int i = 0; i < 6; ++i) pb[i] = *reinterpret_cast<const h16x8*>(&sm.Pb[i][l][0]);
