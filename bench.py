@@ -154,41 +154,46 @@ BWD_KERNELS = "gdn_bwd_kernel<bf16,128,128,32> + bwd_reduce_kernel (f32)"
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="b59d12c44fab1aaa70540f5992f06ee343d3de89",
-        fetch_kib=248592 + 73758 + 373030, write_kib=55419 + 14336 + 239616,
+        sha1="001bcaeb3d899f7975c36f8ad40593a5c0c389d3",
+        fetch_kib=248680 + 73759 + 372928, write_kib=55433 + 14336 + 239616,
+        profile=PROFILE),
+    PREFILL_CONV_KERNELS: dict(
+        src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
+        sha1="001bcaeb3d899f7975c36f8ad40593a5c0c389d3",
+        fetch_kib=313566 + 56352 + 424156, write_kib=102404 + 10240 + 258821,
         profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
-        sha1="556df9b0674b65c32a725eb4e02f64b0b1605c12",
-        fetch_kib=265776, write_kib=526490, profile=PROFILE),
+        sha1="d0e70d0a01d4633fac0a955eda54f3bd69f01b62",
+        fetch_kib=265757, write_kib=526615, profile=PROFILE),
     "swa_sink_decode_kernel<bf16,bf16,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa.hip",
         sha1="afa1a0eccd2a4fdf0d91fdc379ee91e97784c24f",
-        fetch_kib=1062142, write_kib=6144, profile=PROFILE),
+        fetch_kib=1061916, write_kib=6144, profile=PROFILE),
     # mean of the three launches of the counter run (same inputs)
     "swa_sink_prefill_kernel<bf16>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa_prefill.hip",
         sha1="22b363dac7d447a545132a0e123c8b66d2eff229",
-        fetch_kib=(444559 + 440543 + 444151) / 3, write_kib=(133710 + 134342 + 133952) / 3,
+        fetch_kib=(441745 + 443068 + 440350) / 3, write_kib=(133712 + 133862 + 133438) / 3,
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
-        sha1="594fa98533bc44fd3a33a244b72a8ae641e225c5",
-        fetch_kib=264713 + 723012, write_kib=395282 + 139264, profile=PROFILE),
+        sha1="8008f930a86046f487783f521a463bb4c0819f62",
+        fetch_kib=264781 + 723012, write_kib=395278 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd.hip",
         sha1="c17595e858a5302d13a5199bfbb3355398e23a48",
-        fetch_kib=1348593 + 264211, write_kib=2703770 + 132096, profile=PROFILE),
+        fetch_kib=1348498 + 264211, write_kib=2703754 + 132096, profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
         sha1="92b6d24215239cccaa8a33d420f5e803ae0fe4a5",
-        fetch_kib=168115 + 168109 + 168120, write_kib=327681 + 327680 + 327697, profile=PROFILE),
+        fetch_kib=168108 + 168106 + 168113, write_kib=327681 + 327682 + 327684, profile=PROFILE),
     # the three projections' decode-time steps together
     "short_conv_step_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
         sha1="92b6d24215239cccaa8a33d420f5e803ae0fe4a5",
-        fetch_kib=5480 + 5478 + 5476, write_kib=10240 + 10240 + 10240, profile=PROFILE),
+        fetch_kib=5479 + 5478 + 5476, write_kib=10240 + 10240 + 10240, profile=PROFILE),
 }
 READ_FACTOR, WRITE_FACTOR = 2.00, 1.00
 

@@ -124,7 +124,7 @@ struct __align__(16) HSmem {
   h16x4 Pb[6][64][2];    // P operands per (row tile, 32-token step); halves = block columns
   HGate g[3];            // slot = chunk % 3
   float Iv4[kInv4Scratch];  // diagonal blocks of A, column-major (helper wave 4)
-  float tap[3][HD * 4];  // fused short conv: this head's taps of q, k, v
+  float tap[3][4 * HD];  // fused short conv: this head's taps of q, k, v, [tap][channel]
 };
 
 // Slot of P block (R, C) in Pb: row tile R, 32-token step C / 2.
@@ -211,17 +211,18 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp(x, ic<0x140>());  // row_mirror
   return x;
 }
-// The taps are staged in LDS multiplied by -log2(e), so the weighted sum is
-// a' = -log2(e) a and 2^a' = e^-a feeds the sigmoid directly: the kernels
-// form o' = a' / (1 + 2^a') = -log2(e) SiLU(a) and fold the constant into
-// the per-row factor that follows (the norm's, or v's gate factor).
+// The taps are staged in LDS tap-major and multiplied by -log2(e), so the
+// weighted sum is a' = -log2(e) a and 2^a' = e^-a feeds the sigmoid
+// directly: the kernels form o' = a' / (1 + 2^a') = -log2(e) SiLU(a) and
+// fold the constant into the per-row factor that follows (the norm's, or
+// v's gate factor).
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // The convolution and SiLU of the thread's 4 rows (o' above, f32), and per
 // row the factor m that turns o' into the operand: with l2, -1 / (||o||_2 +
 // eps) over the head's 128 channels (o = SiLU(a)); without, -ln 2.  tabs_r0:
-// absolute token of row 4 g - 3; taps: this head's scaled [128][4] in LDS;
+// absolute token of row 4 g - 3; taps: this head's scaled [4][128] in LDS;
 // edge (uniform over the wave): the chunk starts within 3 tokens of the
 // sequence start, so some rows may lie before it and read as zero.
 __device__ __forceinline__ void conv_rows(const ConvRows& x, const float* taps, int pc, int tabs_r0,
@@ -235,12 +236,14 @@ __device__ __forceinline__ void conv_rows(const ConvRows& x, const float* taps, 
     for (int j = 0; j < 7; ++j)
       if (tabs_r0 + j < 0) r[j] = bf16x8{};
   }
+  // taps[j][c] (tap-major): the 16 lanes of a row group read 16 different
+  // 32-byte runs of one tap row.
   float w[8][4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const f32x4 tw = ldf4(taps + 4 * (pc + e));
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 lo = ldf4(taps + j * HD + pc), hi = ldf4(taps + j * HD + pc + 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[e][j] = tw[j];
+    for (int e = 0; e < 4; ++e) w[e][j] = lo[e], w[e + 4][j] = hi[e];
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -424,7 +427,7 @@ struct __align__(16) TSmem {
   h16x4 Dg[2][7][64];    // D(T00), D(T00^T), D(T11), D(T11^T), D(T22), D(T22^T), D(T33^T)
   HGate g[4];            // slot = chunk % 4
   float Iv[4][kInvScratch];  // inverse scratch of waves 0-3
-  float tap[2][HD * 4];  // fused short conv: this head's taps of k, v
+  float tap[2][4 * HD];  // fused short conv: this head's taps of k, v, [tap][channel]
 };
 
 // Transition pass of one segment (chunks c0 .. c0 + NC - 1 of head (b, h)):
@@ -526,9 +529,11 @@ __device__ __forceinline__ void transition_segment(TSmem& sm, const bf16* __rest
   };
   if constexpr (CV) {
     // This head's taps of k and v -> LDS.
-    for (int i = tid; i < 2 * HD * 4; i += HNT)
-      sm.tap[i / (HD * 4)][i % (HD * 4)] =
-          -kLog2e * (i < HD * 4 ? ct.k : ct.v)[(size_t)h * HD * 4 + i % (HD * 4)];
+    for (int i = tid; i < 2 * HD * 4; i += HNT) {
+      const int e = i % (HD * 4);  // [channel][tap] in memory, [tap][channel] in LDS
+      sm.tap[i / (HD * 4)][(e & 3) * HD + (e >> 2)] =
+          -kLog2e * (i < HD * 4 ? ct.k : ct.v)[(size_t)h * HD * 4 + e];
+    }
     lds_barrier();
     if (w < 4) cissue(0);
     ld_gate(0, 0);
@@ -867,7 +872,7 @@ __device__ __forceinline__ void out_segment(HSmem& sm, const bf16* __restrict__ 
     for (int i = tid; i < 3 * HD * 4; i += HNT) {
       const int sq = i / (HD * 4), e = i % (HD * 4);
       const float* src = sq == 0 ? ct.q : sq == 1 ? ct.k : ct.v;
-      sm.tap[sq][e] = -kLog2e * src[(size_t)h * HD * 4 + e];
+      sm.tap[sq][(e & 3) * HD + (e >> 2)] = -kLog2e * src[(size_t)h * HD * 4 + e];
     }
     lds_barrier();
   }
