@@ -520,6 +520,262 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
     }
 }
 
+// Kernel 2 for bf16 inputs, Dk = Dv = 128, chgate (not kGLA): one
+// work-group of 12 waves per (b, h) walks its chunks with S in MFMA
+// accumulator tiles.  Waves 0-7 each own 16 value columns of S (f32, all 128
+// keys: 8 tiles, key order kap below, so two stacked tiles form the B operand
+// of K S directly) and run the recurrence on f16 operands; waves 8-11 stream
+// the chunk's inputs and its record and write the f16 operand tiles to LDS:
+//   Kg = K o e^Gam,  Qg = Q o e^Gam,  Kd = K o e^(Gam_C - Gam)   [32 x 128]
+//   V [32 x 128], T and Pm with their columns in operand order, beta, e^Gam_C.
+// Iteration i: helpers fill slot i % 2 with chunk i; the recurrence waves
+// take chunk i - 1 from slot (i - 1) % 2:
+//   X = Kg S~, (Qg S)^T, Y = beta (V - X), U = T Y, (Pm U)^T, outputs,
+//   S <- diag(e^Gam_C) S + Kd^T U.
+// One work-group barrier per iteration.  The helpers' loads run two
+// iterations ahead (two register slots), as inline asm with fixed waits:
+// every iteration issues the same 14 loads per thread, so a slot's loads are
+// complete once vmcnt reaches 14.
+namespace tile {
+
+constexpr int RS = 144;         // f16 row stride of the 128-wide tiles (288 bytes)
+constexpr int PRS = 40;         // f16 row stride of T and Pm
+constexpr int NW = 16;          // waves: 8 recurrence, 8 helpers
+constexpr int NT = 64 * NW;     // threads
+
+struct __align__(16) Smem {
+  f16ops::h16 Kg[2][GC * RS];
+  f16ops::h16 Qg[2][GC * RS];
+  f16ops::h16 Kd[2][GC * RS];
+  f16ops::h16 V[2][GC * RS];
+  f16ops::h16 Tp[2][GC * PRS];  // Tp[r][8 g + s] = T[r][tau(g, s)]
+  f16ops::h16 Pp[2][GC * PRS];
+  float bet[2][GC];
+  float gC[2][128];             // e^Gam_C per key channel
+};
+
+// State tile m, accumulator row r (= 4 lane group + i): key kap(m, r).
+__device__ __forceinline__ int kap(int m, int r) {
+  return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
+}
+
+__device__ __forceinline__ void gld16(bf16x8& r, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+}
+__device__ __forceinline__ void gld16f(f32x4& r, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+}
+
+// One helper thread's loads of one chunk: K, Q and V at row pr and
+// channels pc .. pc + 7; Gam at that row and at the chunk's last row; 4
+// floats of T (threads 0-255) or of Pm (256-511), and 4 of beta.
+struct Loads {
+  bf16x8 k, q, v;
+  f32x4 g[2], gl[2], tp, b;
+};
+constexpr int kLoadsPerChunk = 3 + 2 + 2 + 1 + 1;  // 9
+
+template <int N>
+__device__ __forceinline__ void wait_loads(Loads& x) {
+  asm volatile("s_waitcnt vmcnt(%9)"
+               : "+v"(x.k), "+v"(x.q), "+v"(x.v), "+v"(x.g[0]), "+v"(x.g[1]), "+v"(x.gl[0]),
+                 "+v"(x.gl[1]), "+v"(x.tp), "+v"(x.b)
+               : "n"(N)
+               : "memory");
+}
+
+template <class TOut>
+__global__ __launch_bounds__(NT) void chgate_recur_tile_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* state_in, float* state_out, TOut* __restrict__ out, int T, int H, int NC,
+    float scale, const char* __restrict__ ws) {
+  using namespace f16ops;
+  constexpr int DK = 128, DV = 128;
+  __shared__ Smem sm;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lq = l >> 4;
+  const size_t tok = (size_t)H * DK;
+  const size_t head0 = (size_t)b * T * tok + (size_t)h * DK;
+  auto lane_offset = [](int& x) { asm volatile("" : "+v"(x)); };
+
+  if (w < 8) {
+    // ------------------------------------------------------ recurrence waves
+    const int col = 16 * w + lr;
+    f32x4 S[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[m][i] = state_in ? state_in[((size_t)bh * DK + kap(m, 4 * lq + i)) * DV + col] : 0.f;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state is loaded
+    int fb = lr * RS + 8 * lq;                                   // fragment reads
+    int tb = (4 * lq + (lr >> 2)) * RS + 8 * (lr & 3);           // K^T transpose reads
+    int vb = (4 * lq + (lr >> 2)) * RS + 16 * w + 4 * (lr & 3);  // V transpose reads
+    int pb = lr * PRS + 8 * lq;                                  // T, Pm rows
+    for (int it = 0; it <= NC; ++it) {
+      lane_offset(fb);
+      lane_offset(tb);
+      lane_offset(vb);
+      lane_offset(pb);
+      const int c = it - 1;
+      if (c >= 0) {
+        const int sl = c & 1;
+        const h16* Kg = sm.Kg[sl];
+        const h16* Qg = sm.Qg[sl];
+        // X = Kg S~ and (Qg S~)^T, token tiles rt = 0, 1, per 32-key step.
+        f32x4 X[2] = {zero4(), zero4()}, QS[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h16x8 sb = cat8(cvt4(S[2 * j]), cvt4(S[2 * j + 1]));
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            const h16x8 kf = f16ops::ld8(Kg + fb + 16 * rt * RS + 32 * j);
+            const h16x8 qf = f16ops::ld8(Qg + fb + 16 * rt * RS + 32 * j);
+            X[rt] = mfma32(kf, sb, X[rt]);
+            QS[rt] = mfma32(sb, qf, QS[rt]);
+          }
+        }
+        // Y = beta (V - X) (tokens 16 rt + 4 lq + i, column col), U = T Y.
+        h16x4 y16[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const h16x4 va = ld_tr(sm.V[sl] + vb + 16 * rt * RS);
+          const f32x4 bv = ldf4(&sm.bet[sl][16 * rt + 4 * lq]);
+          f32x4 y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = bv[i] * ((float)va[i] - X[rt][i]);
+          y16[rt] = cvt4(y);
+        }
+        const h16x8 yo = cat8(y16[0], y16[1]);  // B operand, tokens in tau order
+        f32x4 U[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) U[rt] = mfma32(f16ops::ld8(sm.Tp[sl] + pb + 16 * rt * PRS), yo, zero4());
+        const h16x8 ud = cat8(cvt4(U[0]), cvt4(U[1]));
+        // Outputs: (Pm U)^T + scale (Qg S)^T: token 16 R + lr, columns 4 lq + i.
+        {
+          const int nrows = min(GC, T - c * GC);
+          const TOut* cb = out + head0 + (size_t)c * GC * tok;
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<TOut*>(cb), (short)0, nrows * (int)tok * (int)sizeof(TOut), 0x00020000);
+#pragma unroll
+          for (int R = 0; R < 2; ++R) {
+            const f32x4 PU = mfma32(ud, f16ops::ld8(sm.Pp[sl] + pb + 16 * R * PRS), zero4());
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = __builtin_fmaf(scale, QS[R][i], PU[i]);
+            const int off = ((16 * R + lr) * (int)tok + 16 * w + 4 * lq) * (int)sizeof(TOut);
+            if constexpr (sizeof(TOut) == 2) {
+              typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+              bf16x4 ob;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ob[i] = (bf16)o[i];
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), rs, off, 0, 0);
+            } else {
+              typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, off, 0, 0);
+            }
+          }
+        }
+        // S <- diag(e^Gam_C) S + Kd^T U (Kd^T from transposed reads, keys
+        // in kap order, tokens in tau order).
+        const h16* Kd = sm.Kd[sl];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const f32x4 g = ldf4(&sm.gC[sl][32 * (m >> 1) + 8 * lq + 4 * (m & 1)]);
+          const int ko = tb + 32 * (m >> 1) + 4 * (m & 1);
+          const h16x8 kt = cat8(ld_tr(Kd + ko), ld_tr(Kd + ko + 16 * RS));
+          S[m] = mfma32(kt, ud, g * S[m]);
+        }
+      }
+      lds_barrier();
+    }
+    if (state_out) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          state_out[((size_t)bh * DK + kap(m, 4 * lq + i)) * DV + col] = S[m][i];
+    }
+  } else {
+    // ---------------------------------------------------------- helpers
+    const int ht = tid - 512;
+    const int pr = ht >> 4, pc = (ht & 15) * 8;           // K, Q, Gam, V pieces
+    const int tpi = ht & 255, tr = tpi >> 3, tc4 = tpi & 7;  // T or Pm piece: row tr, columns 4 tc4 ..
+    // T column tau(g, s) -> operand slot: columns 4 tc4 .. 4 tc4 + 3 land at
+    // 8 (tc4 & 3) + (tc4 < 4 ? 0 : 4) .. + 3.
+    const int tslot = 8 * (tc4 & 3) + (tc4 < 4 ? 0 : 4);
+    const bf16* kh = k + head0;
+    const bf16* qh = q + head0;
+    const bf16* vh = v + (size_t)b * T * tok + (size_t)h * DV;
+    auto issue = [&](Loads& x, int c) {
+      c = min(c, NC - 1);
+      const int t0 = c * GC;
+      const float* rec = reinterpret_cast<const float*>(ws + ((size_t)bh * NC + c) * kRecBytes);
+      const float* gam = reinterpret_cast<const float*>(ws + ((size_t)bh * NC + c) * kRecBytes + kGamOff);
+      const int t = min(t0 + pr, T - 1);
+      gld16(x.k, kh + (size_t)t * tok + pc);
+      gld16(x.q, qh + (size_t)t * tok + pc);
+      gld16(x.v, vh + (size_t)t * tok + pc);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) gld16f(x.g[e], gam + pr * DK + pc + 4 * e);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) gld16f(x.gl[e], gam + (GC - 1) * DK + pc + 4 * e);
+      gld16f(x.tp, rec + (ht < 256 ? 0 : GC * GC) + tr * GC + 4 * tc4);
+      gld16f(x.b, rec + 2 * GC * GC + 4 * (ht & 7));
+    };
+    auto put = [&](const Loads& x, int c) {
+      const int sl = c & 1;
+      const bool in = c * GC + pr < T;
+      h16x8 kg, qg, kd, vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float g = x.g[e >> 2][e & 3], gl = x.gl[e >> 2][e & 3];
+        const float eg = __expf(g), ed = __expf(gl - g);
+        const float kk = in ? (float)x.k[e] : 0.f, qq = in ? (float)x.q[e] : 0.f;
+        kg[e] = (h16)(kk * eg);
+        qg[e] = (h16)(qq * eg);
+        kd[e] = (h16)(kk * ed);
+        vv[e] = (h16)(in ? (float)x.v[e] : 0.f);
+      }
+      *reinterpret_cast<h16x8*>(sm.Kg[sl] + pr * RS + pc) = kg;
+      *reinterpret_cast<h16x8*>(sm.Qg[sl] + pr * RS + pc) = qg;
+      *reinterpret_cast<h16x8*>(sm.Kd[sl] + pr * RS + pc) = kd;
+      *reinterpret_cast<h16x8*>(sm.V[sl] + pr * RS + pc) = vv;
+      if (pr == 0) {
+        f32x4 e0, e1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) e0[e] = __expf(x.gl[0][e]), e1[e] = __expf(x.gl[1][e]);
+        *reinterpret_cast<f32x4*>(&sm.gC[sl][pc]) = e0;
+        *reinterpret_cast<f32x4*>(&sm.gC[sl][pc + 4]) = e1;
+      }
+      *reinterpret_cast<h16x4*>((ht < 256 ? sm.Tp[sl] : sm.Pp[sl]) + tr * PRS + tslot) = cvt4(x.tp);
+      if (ht < 8) *reinterpret_cast<f32x4*>(&sm.bet[sl][4 * ht]) = x.b;
+    };
+    Loads ld[2];
+    issue(ld[0], 0);
+    issue(ld[1], 1);
+    auto hbody = [&](int it, auto P) {
+      constexpr int p = decltype(P)::value;  // it & 1
+      wait_loads<kLoadsPerChunk>(ld[p]);
+      if (it < NC) put(ld[p], it);
+      issue(ld[p], it + 2);
+      lds_barrier();
+    };
+    int it = 0;
+    for (; it + 1 <= NC; it += 2) {
+      hbody(it, ic<0>());
+      hbody(it + 1, ic<1>());
+    }
+    if (it <= NC) hbody(it, ic<0>());
+    wait_loads<0>(ld[0]);
+    wait_loads<0>(ld[1]);
+  }
+}
+
+}  // namespace tile
+
 template <class TIn, class TOut, int DK, bool KG>
 hipError_t launch_chgate_t(const PrefillArgs& p) {
   const int NC = (p.T + GC - 1) / GC;
@@ -531,6 +787,15 @@ hipError_t launch_chgate_t(const PrefillArgs& p) {
                        p.H, NC, p.scale, (char*)p.workspace, total);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if constexpr (sizeof(TIn) == 2 && DK == 128 && !KG) {
+    if (p.Dv == 128 && NC > 0) {
+      hipLaunchKernelGGL((tile::chgate_recur_tile_kernel<TOut>), dim3(p.B * p.H), dim3(tile::NT), 0,
+                         st, (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.state_in,
+                         p.state_out, (TOut*)p.out, p.T, p.H, NC, p.scale,
+                         (const char*)p.workspace);
+      return hipGetLastError();
+    }
   }
   if (p.Dv % 64 == 0)
     hipLaunchKernelGGL((chgate_recur_kernel<TIn, TOut, DK, 64, KG>),

@@ -1,6 +1,7 @@
 """No register written by an in-flight inline-asm load is touched before its
-wait, in any per-head prefill kernel (see tests/asm_inflight.py), and the
-analysis itself finds a planted copy of such a register."""
+wait, in any kernel that streams its loads that way (the per-head prefill
+kernels and the tiled channel-gate recurrence; see tests/asm_inflight.py),
+and the analysis itself finds a planted copy of such a register."""
 import os
 
 import pytest
@@ -8,14 +9,28 @@ import pytest
 from asm_inflight import check_kernel, compile_asm, kernels
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "gated_delta_rule_115_amd", "csrc", "gdn_prefill_head.hip")
+CSRC = os.path.join(ROOT, "gated_delta_rule_115_amd", "csrc")
+
+
+def _compile(tmp_path_factory, name):
+    from gated_delta_rule_115_amd.build import CFLAGS
+    flags = [f for f in CFLAGS if f not in ("-Wall",)]
+    return compile_asm(os.path.join(CSRC, name), str(tmp_path_factory.mktemp("asm") / "k.s"),
+                       flags)
 
 
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
-    from gated_delta_rule_115_amd.build import CFLAGS
-    flags = [f for f in CFLAGS if f not in ("-Wall",)]
-    return compile_asm(SRC, str(tmp_path_factory.mktemp("asm") / "head.s"), flags)
+    return _compile(tmp_path_factory, "gdn_prefill_head.hip")
+
+
+def test_tiled_chgate_recurrence_has_no_inflight_hazard(tmp_path_factory):
+    text = _compile(tmp_path_factory, "gdn_chgate.hip")
+    names = [k for k in kernels(text) if "chgate_recur_tile_kernel" in k]
+    assert len(names) == 2  # bf16 and f32 output
+    for k in names:
+        rep = check_kernel(text, k)
+        assert rep == [], (k, rep[:5])
 
 
 def test_per_head_kernels_have_no_inflight_hazard(asm):

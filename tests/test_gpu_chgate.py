@@ -34,7 +34,11 @@ def _ref(x, state_in=None, scale=1.0):
     ("bf16", 1, 1, 2, 128, 64, 0.1), ("f32", 2, 70, 2, 64, 64, 2.0),
     ("bf16", 1, 200, 2, 128, 128, 2.0), ("f32", 1, 96, 2, 64, 64, 5.0),
     ("bf16", 2, 70, 2, 32, 32, 0.1), ("bf16", 1, 99, 2, 64, 128, 0.1),
-    ("bf16", 1, 64, 2, 128, 32, 2.0)])
+    ("bf16", 1, 64, 2, 128, 32, 2.0),
+    # bf16, Dk = Dv = 128: the tiled recurrence (one work-group per head) --
+    # one token, one chunk plus one token, very strong gates (exact path)
+    ("bf16", 2, 1, 2, 128, 128, 0.1), ("bf16", 1, 33, 3, 128, 128, 0.1),
+    ("bf16", 1, 96, 2, 128, 128, 5.0)])
 def test_chgate_prefill_matches_oracle(dtype, B, T, H, Dk, Dv, gs):
     say(f"chgate prefill {dtype} B{B} T{T} H{H} Dk{Dk} Dv{Dv} gate {gs}")
     x = synthetic.chgate_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=T + Dk, state0="randn",

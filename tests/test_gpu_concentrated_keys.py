@@ -72,16 +72,18 @@ def test_bf16_two_kernel_prefill_concentrated(cos, bshift):
 
 
 @pytest.mark.parametrize("cos,bshift", REGIMES)
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_chgate_prefill_concentrated(cos, bshift, dtype):
-    x = synthetic.chgate_inputs(1, 200, 2, 128, 64, dtype=dtype, seed=13, state0="randn",
+@pytest.mark.parametrize("dtype,Dv", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_chgate_prefill_concentrated(cos, bshift, dtype, Dv):
+    """Channel-wise gate: f32 and bf16 on the two-kernel recurrence (Dv = 64),
+    bf16 with Dk = Dv = 128 on the tiled one."""
+    x = synthetic.chgate_inputs(1, 200, 2, 128, Dv, dtype=dtype, seed=13, state0="randn",
                                 key_cos=cos, beta_shift=bshift)
     o, s = gdn.gdn_prefill_chunked_chgate(*(dev(x[n]) for n in NAMES), dev(x["state0"]),
                                           out_dtype=torch.float32)
     torch.cuda.synchronize()
     ro, rs = oracle.gdn_recurrence_chgate(*(f64(x[n]) for n in NAMES), f64(x["state0"]))
     eo, es = err(o, ro), err(s, rs)
-    say(f"chgate {dtype} cos {cos} shift {bshift}: out {eo:.2e} state {es:.2e}")
+    say(f"chgate {dtype} Dv{Dv} cos {cos} shift {bshift}: out {eo:.2e} state {es:.2e}")
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
