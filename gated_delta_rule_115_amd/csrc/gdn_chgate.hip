@@ -158,7 +158,7 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
       if (pc < GC * DK / 4) {
         const int r = pc / (DK / 4), c4 = 4 * (pc % (DK / 4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = t0 + r < T ? logf(ar[u][e]) : 0.f;
+        for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = t0 + r < T ? __logf(ar[u][e]) : 0.f;
       }
     }
     if (tid < GC) bet[tid] = t0 + tid < T ? br : 0.f;
@@ -166,14 +166,20 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     f16ops::lds_barrier();
     // Cumulative log gate per channel, and its range over the chunk (kGLA:
     // the gate is alpha o (1 - beta k o k); rows past T have k = beta = 0).
+    // (Each channel's 32 values are read into registers first, so the scan
+    // waits for one LDS round trip, not one per row.)
     if (tid < DK) {
-      float acc = 0.f;
+      float g[GC];
+#pragma unroll
       for (int r = 0; r < GC; ++r) {
-        acc += Gs[r][tid];
-        if constexpr (KG) acc += log1pf(-bet[r] * Ks[r][tid] * Ks[r][tid]);
-        Gs[r][tid] = acc;
+        g[r] = Gs[r][tid];
+        if constexpr (KG) g[r] += log1pf(-bet[r] * Ks[r][tid] * Ks[r][tid]);
       }
-      rng[tid] = Gs[0][tid] - acc;
+#pragma unroll
+      for (int r = 1; r < GC; ++r) g[r] += g[r - 1];
+#pragma unroll
+      for (int r = 0; r < GC; ++r) Gs[r][tid] = g[r];
+      rng[tid] = g[0] - g[GC - 1];
     }
     f16ops::lds_barrier();
     {
@@ -184,8 +190,12 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
             f32x4{Gs[r][c4], Gs[r][c4 + 1], Gs[r][c4 + 2], Gs[r][c4 + 3]};
       }
     }
+    // Largest range over the channels: lane l of every wave takes channels
+    // l, l + 64, ..., then a butterfly over the wave (ranges are >= 0).
     float wide = 0.f;
-    for (int ch = 0; ch < DK; ++ch) wide = fmaxf(wide, rng[ch]);
+    for (int ch = tid & 63; ch < DK; ch += 64) wide = fmaxf(wide, rng[ch]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) wide = fmaxf(wide, __shfl_xor(wide, m));
 
     float* rec = reinterpret_cast<float*>(ws + (size_t)id * kRecBytes);
     float* Tg = rec;
