@@ -147,48 +147,48 @@ PREFILL_KERNELS = "prefill_lead_kernel<bf16> + segment_combine_kernel + prefill_
 # kernels, instantiated with the convolution in their tile loads.
 PREFILL_CONV_KERNELS = ("prefill_lead_kernel<bf16,conv> + segment_combine_kernel + "
                         "prefill_out_kernel<bf16,conv>")
-CHGATE_KERNELS = ("chgate_prep_kernel (f32) + chgate_recur_kernel (bf16 inputs: f16 MFMA operands, "
-                  "f32 accumulation and state)")
+CHGATE_KERNELS = ("chgate_prep_kernel (f32) + chgate_recur_tile_kernel (bf16 inputs: f16 MFMA "
+                  "operands, f32 accumulation and state)")
 # The backward call launches the adjoint kernel and the slice-partial sum.
 BWD_KERNELS = "gdn_bwd_kernel<bf16,128,128,32> + bwd_reduce_kernel (f32)"
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="001bcaeb3d899f7975c36f8ad40593a5c0c389d3",
-        fetch_kib=248680 + 73759 + 372928, write_kib=55433 + 14336 + 239616,
+        sha1="d2735030a2461d9e01aa1bea23c3f5e2c211ce93",
+        fetch_kib=248635 + 73759 + 372913, write_kib=55312 + 14336 + 239617,
         profile=PROFILE),
     PREFILL_CONV_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="001bcaeb3d899f7975c36f8ad40593a5c0c389d3",
-        fetch_kib=313566 + 56352 + 424156, write_kib=102404 + 10240 + 258821,
+        sha1="d2735030a2461d9e01aa1bea23c3f5e2c211ce93",
+        fetch_kib=313718 + 56352 + 423459, write_kib=102720 + 10240 + 258846,
         profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
         sha1="d0e70d0a01d4633fac0a955eda54f3bd69f01b62",
-        fetch_kib=265757, write_kib=526615, profile=PROFILE),
+        fetch_kib=265758, write_kib=526634, profile=PROFILE),
     "swa_sink_decode_kernel<bf16,bf16,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa.hip",
         sha1="afa1a0eccd2a4fdf0d91fdc379ee91e97784c24f",
-        fetch_kib=1061916, write_kib=6144, profile=PROFILE),
+        fetch_kib=1061936, write_kib=6144, profile=PROFILE),
     # mean of the three launches of the counter run (same inputs)
     "swa_sink_prefill_kernel<bf16>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa_prefill.hip",
         sha1="22b363dac7d447a545132a0e123c8b66d2eff229",
-        fetch_kib=(441745 + 443068 + 440350) / 3, write_kib=(133712 + 133862 + 133438) / 3,
+        fetch_kib=(444899 + 441849 + 439651) / 3, write_kib=(133848 + 133726 + 133661) / 3,
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
-        sha1="8008f930a86046f487783f521a463bb4c0819f62",
-        fetch_kib=264781 + 723012, write_kib=395278 + 139264, profile=PROFILE),
+        sha1="d919a99ca61702a2b04a8647f6725c5fd6fcad7c",
+        fetch_kib=264783 + 394320, write_kib=395285 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd.hip",
         sha1="c17595e858a5302d13a5199bfbb3355398e23a48",
-        fetch_kib=1348498 + 264211, write_kib=2703754 + 132096, profile=PROFILE),
+        fetch_kib=1348643 + 264212, write_kib=2703971 + 132096, profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
         sha1="92b6d24215239cccaa8a33d420f5e803ae0fe4a5",
-        fetch_kib=168108 + 168106 + 168113, write_kib=327681 + 327682 + 327684, profile=PROFILE),
+        fetch_kib=168112 + 168107 + 168109, write_kib=327681 + 327681 + 327687, profile=PROFILE),
     # the three projections' decode-time steps together
     "short_conv_step_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
