@@ -1392,70 +1392,114 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
 }
 
 // Initial states of segments 2 .. P - 1: from S_1 (left in the workspace by
-// the output pass of segment 0), S_{s+1} = M_s S_s + B_s, in f32.  One work-group of 4 waves per (head, 16-column
-// slice); wave w forms row tiles 2 w, 2 w + 1 (16 rows each) of every step
-// with v_mfma_f32_16x16x4_f32: in the 16-key block jj, product i takes key
-// 16 jj + 4 q + i in lane group q, so each lane reads its 4 keys of M with
-// one 16-byte load and S (kept transposed in LDS) with one 16-byte read.  The
-// next segment's M and B are loaded while the current product runs; the
-// barriers order LDS only, so those loads stay in flight across them.
+// the output pass of segment 0), S_{s+1} = M_s S_s + B_s, in f32.  One
+// work-group of 4 waves per (head, 16-column slice); wave w forms row tiles
+// 2 w, 2 w + 1 (16 rows each) of every step with v_mfma_f32_16x16x4_f32: in
+// the 16-key block jj, product i takes key 16 jj + 4 q + i in lane group q,
+// so each lane reads its 4 keys of M with one 16-byte load and S (kept
+// transposed in LDS) with one 16-byte read; each row tile accumulates in two
+// chains (even and odd key blocks).  The next segment's M and B are requested
+// (inline asm, 24 loads per lane, two register slots) before the current
+// product, and each step's result is written with 8 vector stores (inline
+// asm): at the end of a step the loads are complete once at most those 8
+// stores are outstanding, so no wait covers a store.
+__device__ __forceinline__ void cb_ld4(f32x4& r, const float* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+}
+__device__ __forceinline__ void cb_ld1(float& r, const float* p) {
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+}
+__device__ __forceinline__ void cb_st1(float* p, float v) {
+  asm volatile("global_store_dword %0, %1, off" : : "v"(p), "v"(v) : "memory");
+}
+struct CombLoads {
+  f32x4 m[2][8];  // M rows 16 (2 w + t) + lr, keys 16 jj + 4 lq .. + 3
+  float b[2][4];  // B in accumulator layout: rows 16 (2 w + t) + 4 lq + i, column lr
+};
+template <int N>
+__device__ __forceinline__ void cb_wait(CombLoads& x) {
+  asm volatile("s_waitcnt vmcnt(%24)"
+               : "+v"(x.m[0][0]), "+v"(x.m[0][1]), "+v"(x.m[0][2]), "+v"(x.m[0][3]),
+                 "+v"(x.m[0][4]), "+v"(x.m[0][5]), "+v"(x.m[0][6]), "+v"(x.m[0][7]),
+                 "+v"(x.m[1][0]), "+v"(x.m[1][1]), "+v"(x.m[1][2]), "+v"(x.m[1][3]),
+                 "+v"(x.m[1][4]), "+v"(x.m[1][5]), "+v"(x.m[1][6]), "+v"(x.m[1][7]),
+                 "+v"(x.b[0][0]), "+v"(x.b[0][1]), "+v"(x.b[0][2]), "+v"(x.b[0][3]),
+                 "+v"(x.b[1][0]), "+v"(x.b[1][1]), "+v"(x.b[1][2]), "+v"(x.b[1][3])
+               : "n"(N)
+               : "memory");
+}
+
 __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
   __shared__ __align__(16) float St[16][HD + 4];  // S slice transposed: [column][key]
-  const int bh = blockIdx.x >> 3, col0 = 16 * (blockIdx.x & 7);
+  // The 8 slices of a head on one XCD (when the head count is a multiple of
+  // 8), so M_s comes from HBM into one L2 once and is read from there 8 times.
+  int bh, sl;
+  xcd_group_map(blockIdx.x, gridDim.x / 8, 8, &bh, &sl);
+  const int col0 = 16 * sl;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
   const float* s1 = ws.S + ws.at(bh, 0, P);
   for (int i = tid; i < HD * 16; i += 256) {
     const int r = i >> 4, c = i & 15;
     St[c][r] = s1[r * HD + col0 + c];
   }
-  // Lane (lq, lr) of row tile R: M row 16 R + lr, keys 16 jj + 4 lq .. + 3.
-  f32x4 mA[2][8], bA[2], mN[2][8], bN[2];
-  auto load = [&](int sg, f32x4 (&m)[2][8], f32x4 (&bb)[2]) {
+  const int last = P - 2;  // steps sg = 1 .. last
+  auto issue = [&](CombLoads& x, int sg) {
+    sg = min(sg, last);
     const float* M = ws.M + ws.at(bh, sg, P);
     const float* Bs = ws.B + ws.at(bh, sg, P);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int row = 16 * (2 * w + t) + lr;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) m[t][jj] = ldf4(M + (size_t)row * HD + 16 * jj + 4 * lq);
-      // B in accumulator layout: rows 16 R + 4 lq + i, column lr.
+      for (int jj = 0; jj < 8; ++jj) cb_ld4(x.m[t][jj], M + (size_t)row * HD + 16 * jj + 4 * lq);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bb[t][i] = Bs[(size_t)(16 * (2 * w + t) + 4 * lq + i) * HD + col0 + lr];
+      for (int i = 0; i < 4; ++i)
+        cb_ld1(x.b[t][i], Bs + (size_t)(16 * (2 * w + t) + 4 * lq + i) * HD + col0 + lr);
     }
   };
-  load(1, mA, bA);
+  CombLoads ld[2];
+  issue(ld[0], 1);
+  cb_wait<0>(ld[0]);  // also covers the compiler's loads of S_1 above
   lds_barrier();
-  for (int sg = 1; sg + 1 < P; ++sg) {
-    if (sg + 2 < P) load(sg + 1, mN, bN);
-    f32x4 acc[2];
+  auto step = [&](int sg, auto Par) {
+    constexpr int p = decltype(Par)::value;  // (sg - 1) & 1
+    issue(ld[p ^ 1], sg + 1);
+    f32x4 acc[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      acc[t] = bA[t];
+      acc[t][0] = f32x4{ld[p].b[t][0], ld[p].b[t][1], ld[p].b[t][2], ld[p].b[t][3]};
+      acc[t][1] = zero4();
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const f32x4 sv = ldf4(&St[lr][16 * jj + 4 * lq]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mA[t][jj][i], sv[i], acc[t], 0, 0, 0);
+          acc[t][jj & 1] =
+              __builtin_amdgcn_mfma_f32_16x16x4f32(ld[p].m[t][jj][i], sv[i], acc[t][jj & 1], 0, 0, 0);
       }
     }
-    lds_barrier();  // every wave has read St (the next segment's maps stay in flight)
+    lds_barrier();  // every wave has read St
     float* dst = ws.S + ws.at(bh, sg, P);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      const f32x4 a = acc[t][0] + acc[t][1];
       const int r0 = 16 * (2 * w + t) + 4 * lq;
-      *reinterpret_cast<f32x4*>(&St[lr][r0]) = acc[t];
+      *reinterpret_cast<f32x4*>(&St[lr][r0]) = a;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(size_t)(r0 + i) * HD + col0 + lr] = acc[t][i];
+      for (int i = 0; i < 4; ++i) cb_st1(dst + (size_t)(r0 + i) * HD + col0 + lr, a[i]);
     }
     lds_barrier();
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      bA[t] = bN[t];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) mA[t][jj] = mN[t][jj];
-    }
+    cb_wait<8>(ld[p ^ 1]);
+  };
+  int sg = 1;
+  for (; sg + 1 <= last; sg += 2) {
+    step(sg, ic<0>());
+    step(sg + 1, ic<1>());
   }
+  if (sg <= last) step(sg, ic<0>());
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last stores
+  cb_wait<0>(ld[0]);
+  cb_wait<0>(ld[1]);
 }
 
 }  // namespace

@@ -1,6 +1,6 @@
 """No register written by an in-flight inline-asm load is touched before its
 wait, in any kernel that streams its loads that way (the per-head prefill
-kernels and the tiled channel-gate recurrence; see tests/asm_inflight.py),
+kernels, the segment combine and the tiled channel-gate recurrence; see tests/asm_inflight.py),
 and the analysis itself finds a planted copy of such a register."""
 import os
 
@@ -36,6 +36,8 @@ def test_tiled_chgate_recurrence_has_no_inflight_hazard(tmp_path_factory):
 def test_per_head_kernels_have_no_inflight_hazard(asm):
     names = [k for k in kernels(asm) if "prefill_" in k]
     assert len(names) == 8  # lead and output kernels x {bf16, f32 out} x {fused conv, not}
+    names += [k for k in kernels(asm) if "segment_combine_kernel" in k]
+    assert len(names) == 9
     for k in names:
         rep = check_kernel(asm, k)
         assert rep == [], (k, rep[:5])
