@@ -418,6 +418,7 @@ hipError_t launch_bwd_dk(const BwdArgs& p) {
 }  // namespace
 
 size_t backward_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
+  if (backward_chunked_supported(Dk, Dv)) return backward_chunked_workspace_bytes(B, T, H);
   const size_t nck = ((size_t)T + SUB - 1) / SUB;
   const size_t dvs = Dv < kBwdSlice ? Dv : kBwdSlice, ns = Dv / dvs;
   const size_t ckpt = (size_t)B * H * ns * nck * Dk * dvs;
@@ -427,6 +428,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
 
 hipError_t launch_backward(const BwdArgs& p) {
   if ((long long)p.B * p.H == 0) return hipSuccess;
+  if (backward_chunked_supported(p.Dk, p.Dv)) return launch_backward_chunked(p);
   return p.bf16 ? launch_bwd_dk<bf16>(p) : launch_bwd_dk<float>(p);
 }
 

@@ -112,6 +112,11 @@ struct BwdArgs {
 };
 size_t backward_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 hipError_t launch_backward(const BwdArgs& p);
+// Chunked form (Dk = Dv = 128, chunks of 64 tokens, f32 MFMA): the path
+// launch_backward takes for those head sizes.
+bool backward_chunked_supported(int Dk, int Dv);
+size_t backward_chunked_workspace_bytes(int B, int T, int H);
+hipError_t launch_backward_chunked(const BwdArgs& p);
 
 // Channel-wise gate prefill (alpha [B, T, H, Dk]); chunks of 32 tokens,
 // f32 arithmetic; Dk in {32, 64, 128}, Dv a multiple of 32.  With p.kgla:

@@ -32,7 +32,10 @@ def _grads(x, dout, dst, scale, dtype):
 @pytest.mark.parametrize("dtype,B,T,H,Dk,Dv", [
     ("f32", 2, 70, 2, 32, 32), ("f32", 1, 64, 2, 64, 16), ("f32", 2, 33, 1, 16, 128),
     ("f32", 1, 32, 2, 128, 128), ("f32", 2, 1, 2, 32, 64), ("bf16", 1, 100, 2, 128, 128),
-    ("f32", 1, 99, 2, 64, 64), ("bf16", 2, 131, 2, 128, 64), ("f32", 1, 2, 1, 128, 32)])
+    ("f32", 1, 99, 2, 64, 64), ("bf16", 2, 131, 2, 128, 64), ("f32", 1, 2, 1, 128, 32),
+    # d = 128 takes the chunked form (64-token chunks): one exact chunk,
+    # several with a ragged tail, a 1-token tail, B * H not a multiple of 8.
+    ("bf16", 1, 64, 2, 128, 128), ("f32", 2, 200, 2, 128, 128), ("bf16", 1, 257, 3, 128, 128)])
 def test_backward_matches_oracle(dtype, B, T, H, Dk, Dv):
     say(f"backward {dtype} B{B} T{T} H{H} Dk{Dk} Dv{Dv}")
     x = synthetic.gdn_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=T + Dk + Dv, state0="randn")
@@ -51,6 +54,17 @@ def test_backward_zero_length_passes_state_gradient():
     e = {n: x[n][:, :0].contiguous() for n in NAMES}
     dst = torch.randn(2, 2, 32, 32)
     g = gdn.gdn_prefill_backward(*(dev(e[n]) for n in NAMES), dev(torch.zeros(2, 0, 2, 32)),
+                                 dev(x["state0"]), dev(dst))
+    torch.cuda.synchronize()
+    assert torch.equal(g["dstate_in"].cpu(), dst)
+
+
+def test_backward_chunked_zero_length_passes_state_gradient():
+    """T = 0 at d = 128 (the chunked form): no chunk, dstate_in = dstate_out."""
+    x = synthetic.gdn_inputs(1, 1, 2, 128, 128, dtype="bf16", seed=4, state0="randn")
+    e = {n: x[n][:, :0].contiguous() for n in NAMES}
+    dst = torch.randn(1, 2, 128, 128)
+    g = gdn.gdn_prefill_backward(*(dev(e[n]) for n in NAMES), dev(torch.zeros(1, 0, 2, 128)),
                                  dev(x["state0"]), dev(dst))
     torch.cuda.synchronize()
     assert torch.equal(g["dstate_in"].cpu(), dst)

@@ -106,12 +106,13 @@ def test_hybrid_prefill_concentrated(cos, bshift):
 
 @pytest.mark.parametrize("cos,bshift", [(0.9, 0.0), (0.97, 3.0), (1.0, 3.0)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_concentrated(cos, bshift, dtype):
-    x = synthetic.gdn_inputs(1, 100, 2, 128, 64, dtype=dtype, seed=31, state0="randn",
+@pytest.mark.parametrize("dv", [64, 128])  # token-loop adjoint / chunked form
+def test_backward_concentrated(cos, bshift, dtype, dv):
+    x = synthetic.gdn_inputs(1, 100, 2, 128, dv, dtype=dtype, seed=31, state0="randn",
                              key_cos=cos, beta_shift=bshift)
     gen = torch.Generator().manual_seed(7)
-    dout = torch.randn(1, 100, 2, 64, generator=gen)
-    dst = torch.randn(1, 2, 128, 64, generator=gen)
+    dout = torch.randn(1, 100, 2, dv, generator=gen)
+    dst = torch.randn(1, 2, 128, dv, generator=gen)
     g = gdn.gdn_prefill_backward(*(dev(x[n]) for n in NAMES), dev(dout), dev(x["state0"]),
                                  dev(dst))
     torch.cuda.synchronize()
@@ -119,5 +120,5 @@ def test_backward_concentrated(cos, bshift, dtype):
                                        f64(dst))
     for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dstate_in"):
         e = err(g[n], r[n])
-        say(f"backward {dtype} cos {cos} shift {bshift} {n}: {e:.2e}")
+        say(f"backward {dtype} dv {dv} cos {cos} shift {bshift} {n}: {e:.2e}")
         assert e <= TOL["f32"], n
