@@ -114,14 +114,14 @@ __device__ __forceinline__ size_t tok_off(int b, int t, int h, int T, int H) {
 }
 
 // Rows t0 .. t0 + C - 1 of a [B, T, H, D] tensor into an LDS tile [C][ld]
-// of type TL (zeros past T), 256 threads.
-template <class TIn, class TL>
+// of type TL (zeros past T), NTH threads.
+template <class TIn, class TL, int NTH = 256>
 __device__ __forceinline__ void load_tile(TL* dst, int ld, const TIn* src, int b, int t0, int h,
                                           int T, int H) {
   typedef typename Vec16<TIn>::type vec;
   constexpr int VN = Vec16<TIn>::N;
   constexpr int VPR = D / VN;
-  for (int i = threadIdx.x; i < C * VPR; i += 256) {
+  for (int i = threadIdx.x; i < C * VPR; i += NTH) {
     const int r = i / VPR, cv = i % VPR;
     const int t = t0 + r;
     vec x;
@@ -603,8 +603,61 @@ struct GradK {
 constexpr int LV = QV + 4;
 constexpr int LKF = D + 4;
 
+// Lower block-triangle tile y (0..9) of a C x C matrix: row tile, column tile.
+__device__ __forceinline__ int low_rt(int y) { return (y >= 1) + (y >= 3) + (y >= 6); }
+__device__ __forceinline__ int low_ct(int y) {
+  const int rt = low_rt(y);
+  return y - rt * (rt + 1) / 2;
+}
+
+// The value passes' inputs (32 columns of S, dSn, dO, dY, U, Vm, dU), one
+// pass ahead in registers: 9 16-byte pieces per thread (512 threads).
+struct PassRegs {
+  f32x4 x[9];
+};
+__device__ __forceinline__ void pass_issue(PassRegs& pr, const Ws& ws, size_t ch, const float* dout,
+                                           int b, int t0, int h, int T, int H, int c0) {
+  const int tid = threadIdx.x;
+  const float* S = ws.S + ch * D * D + c0;
+  const float* dS = ws.dS + ch * D * D + c0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + 512 * u, r = i >> 3, c4 = i & 7;
+    pr.x[u] = *reinterpret_cast<const f32x4*>(S + r * D + c4 * 4);
+    pr.x[2 + u] = *reinterpret_cast<const f32x4*>(dS + r * D + c4 * 4);
+  }
+  const int r = tid >> 3, c4 = tid & 7;
+  pr.x[4] = zero4();
+  if (t0 + r < T)
+    pr.x[4] = *reinterpret_cast<const f32x4*>(dout + tok_off(b, t0 + r, h, T, H) + c0 + c4 * 4);
+  const size_t o = ch * C * D + r * D + c0 + c4 * 4;
+  pr.x[5] = *reinterpret_cast<const f32x4*>(ws.dY + o);
+  pr.x[6] = *reinterpret_cast<const f32x4*>(ws.U + o);
+  pr.x[7] = *reinterpret_cast<const f32x4*>(ws.Vm + o);
+  pr.x[8] = *reinterpret_cast<const f32x4*>(ws.dU + o);
+}
+__device__ __forceinline__ void pass_store(const PassRegs& pr, GradV& sv) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + 512 * u, r = i >> 3, c4 = i & 7;
+    *reinterpret_cast<f32x4*>(sv.S + r * LV + c4 * 4) = pr.x[u];
+    *reinterpret_cast<f32x4*>(sv.dS + r * LV + c4 * 4) = pr.x[2 + u];
+  }
+  const int o = (tid >> 3) * LV + (tid & 7) * 4;
+  *reinterpret_cast<f32x4*>(sv.dO + o) = pr.x[4];
+  *reinterpret_cast<f32x4*>(sv.dY + o) = pr.x[5];
+  *reinterpret_cast<f32x4*>(sv.U + o) = pr.x[6];
+  *reinterpret_cast<f32x4*>(sv.Vm + o) = pr.x[7];
+  *reinterpret_cast<f32x4*>(sv.dU + o) = pr.x[8];
+}
+
+// Work of wave w (8 waves): token tiles 2 (w & 1) + {0, 1} x key tiles
+// 2 (w >> 1) + {0, 1} of dq_S, Z1 = dX S^T and Z2 = diag(d) U dSn^T (then dq
+// and dk); lower tiles y = w and w + 8 (w < 2) of dP and of dA; lower tiles
+// y = (w + 6) % 8 and that + 8 (< 10) of dTm.
 template <class TIn>
-__global__ __launch_bounds__(256) void bwdc_grad_kernel(
+__global__ __launch_bounds__(512) void bwdc_grad_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ dout, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H,
@@ -612,7 +665,7 @@ __global__ __launch_bounds__(256) void bwdc_grad_kernel(
   __shared__ __align__(16) char smem[sizeof(GradV) > sizeof(GradK) ? sizeof(GradV)
                                                                     : sizeof(GradK)];
   __shared__ Gates gs;
-  __shared__ float gam[C], red[4][C], redz[4][C], dbY[C], dgam[C], dbA[C], wsum[4];
+  __shared__ float gam[C], red[4][C], redz[4][C], dbY[C], dgam[C], dbA[C], colF[C], wsum[8];
   GradV& sv = *reinterpret_cast<GradV*>(smem);
   GradK& sk = *reinterpret_cast<GradK*>(smem);
 
@@ -625,174 +678,164 @@ __global__ __launch_bounds__(256) void bwdc_grad_kernel(
   load_gates(gs, rec, beta, b, t0, h, T, H);
   if (tid < C) gam[tid] = rec[3 * C * C + tid];
 
-  // Accumulators: token tiles 0..3 x key tiles 2w, 2w+1 of dq_S, Z1 = dX S^T,
-  // Z2 = diag(d) U dSn^T; dP row tile w (column tiles <= w), dTm row tile
-  // 3 - w (column tiles <= 3 - w).
-  f32x4 aQ[4][2], aZ1[4][2], aZ2[4][2], aP[4], aT[4];
+  const int tr0 = 2 * (w & 1), kt0 = 2 * (w >> 1);
+  const int nP = w < 2 ? 2 : 1;
+  const int yT0 = (w + 6) & 7, nT = yT0 + 8 < 10 ? 2 : 1;
+  f32x4 aQ[2][2], aZ1[2][2], aZ2[2][2], aP[2], aT[2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    aP[r] = aT[r] = zero4();
+  for (int t = 0; t < 2; ++t) {
+    aP[t] = aT[t] = zero4();
 #pragma unroll
-    for (int m = 0; m < 2; ++m) aQ[r][m] = aZ1[r][m] = aZ2[r][m] = zero4();
+    for (int m = 0; m < 2; ++m) aQ[t][m] = aZ1[t][m] = aZ2[t][m] = zero4();
   }
   float dbY_acc = 0.f, dgc_acc = 0.f;
-  const int wT = 3 - w;
-  const float* Sg = ws.S + ch * D * D;
-  const float* dSg = ws.dS + ch * D * D;
-  __syncthreads();
 
+  PassRegs pr;
+  pass_issue(pr, ws, ch, dout, b, t0, h, T, H, 0);
   for (int pass = 0; pass < D / QV; ++pass) {
-    const int c0 = pass * QV;
-    if (pass) __syncthreads();
-    load_f32<D, QV>(sv.S, LV, Sg + c0, D);
-    load_f32<D, QV>(sv.dS, LV, dSg + c0, D);
-    load_f32<C, QV>(sv.dY, LV, ws.dY + ch * C * D + c0, D);
-    load_f32<C, QV>(sv.U, LV, ws.U + ch * C * D + c0, D);
-    load_f32<C, QV>(sv.Vm, LV, ws.Vm + ch * C * D + c0, D);
-    load_f32<C, QV>(sv.dU, LV, ws.dU + ch * C * D + c0, D);
-    for (int i = tid; i < C * QV / 4; i += 256) {
-      const int r = i / (QV / 4), c4 = i % (QV / 4);
-      f32x4 x = zero4();
-      if (t0 + r < T)
-        x = *reinterpret_cast<const f32x4*>(dout + tok_off(b, t0 + r, h, T, H) + c0 +
-                                            c4 * 4);
-      *reinterpret_cast<f32x4*>(sv.dO + r * LV + c4 * 4) = x;
-    }
+    __syncthreads();  // the previous pass's readers are done
+    pass_store(pr, sv);
     __syncthreads();
+    if (pass + 1 < D / QV) pass_issue(pr, ws, ch, dout, b, t0, h, T, H, (pass + 1) * QV);
 
-    // dY . Vm per row (thread: row tid / 4, 8 columns) and <dSn, S>.
+    // dY . Vm per row (thread: row tid / 8, 4 columns) and <dSn, S>.
     {
-      const int r = tid >> 2, cb = (tid & 3) * 8;
-      float s = 0.f;
+      const int r = tid >> 3, cb = (tid & 7) * 4;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += sv.dY[r * LV + cb + e] * sv.Vm[r * LV + cb + e];
-      dbY_acc += s;
-      float z = 0.f;
+      for (int e = 0; e < 4; ++e) dbY_acc += sv.dY[r * LV + cb + e] * sv.Vm[r * LV + cb + e];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = tid * 16 + e, rr = i / QV, cc = i % QV;
-        z += sv.dS[rr * LV + cc] * sv.S[rr * LV + cc];
+      for (int e = 0; e < 8; ++e) {
+        const int i = tid * 8 + e, rr = i / QV, cc = i % QV;
+        dgc_acc += sv.dS[rr * LV + cc] * sv.S[rr * LV + cc];
       }
-      dgc_acc += z;
     }
 
-    // Products over this pass's 32 value columns.
 #pragma unroll 2
     for (int k0 = 0; k0 < QV; k0 += 4) {
       const int kk = k0 + (l >> 4);
       float bS[2], bD[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int key = (2 * w + m) * 16 + (l & 15);
+        const int key = (kt0 + m) * 16 + (l & 15);
         bS[m] = sv.S[key * LV + kk];
         bD[m] = sv.dS[key * LV + kk];
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = r * 16 + (l & 15);
+      for (int t = 0; t < 2; ++t) {
+        const int tok = (tr0 + t) * 16 + (l & 15);
         const float ao = scale * gs.g[tok] * sv.dO[tok * LV + kk];
         const float ay = -gs.bet[tok] * gs.g[tok] * sv.dY[tok * LV + kk];
         const float au = gs.d[tok] * sv.U[tok * LV + kk];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          aQ[r][m] = mma4(ao, bS[m], aQ[r][m]);
-          aZ1[r][m] = mma4(ay, bS[m], aZ1[r][m]);
-          aZ2[r][m] = mma4(au, bD[m], aZ2[r][m]);
+          aQ[t][m] = mma4(ao, bS[m], aQ[t][m]);
+          aZ1[t][m] = mma4(ay, bS[m], aZ1[t][m]);
+          aZ2[t][m] = mma4(au, bD[m], aZ2[t][m]);
         }
       }
-      // dP (row tile w) and dTm (row tile 3 - w).
-      const float apo = sv.dO[(16 * w + (l & 15)) * LV + kk];
-      const float atu = sv.dU[(16 * wT + (l & 15)) * LV + kk];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 16 * j + (l & 15);
-        if (j <= w) aP[j] = mma4(apo, sv.U[i * LV + kk], aP[j]);
-        if (j <= wT) aT[j] = mma4(atu, gs.bet[i] * sv.Vm[i * LV + kk], aT[j]);
+      for (int t = 0; t < 2; ++t) {
+        if (t < nP) {
+          const int y = w + 8 * t;
+          const float a = sv.dO[(16 * low_rt(y) + (l & 15)) * LV + kk];
+          aP[t] = mma4(a, sv.U[(16 * low_ct(y) + (l & 15)) * LV + kk], aP[t]);
+        }
+        if (t < nT) {
+          const int y = yT0 + 8 * t;
+          const int i = 16 * low_ct(y) + (l & 15);
+          const float a = sv.dU[(16 * low_rt(y) + (l & 15)) * LV + kk];
+          aT[t] = mma4(a, gs.bet[i] * sv.Vm[i * LV + kk], aT[t]);
+        }
       }
     }
   }
-  // Row sums of dY . Vm over the 4 threads of a row; <dSn, S> over the block.
+  // Row sums of dY . Vm over the 8 threads of a row; <dSn, S> over the block.
   dbY_acc += __shfl_xor(dbY_acc, 1);
   dbY_acc += __shfl_xor(dbY_acc, 2);
-  {
-    float z = dgc_acc;
+  dbY_acc += __shfl_xor(dbY_acc, 4);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-    if (l == 0) wsum[w] = z;
-  }
+  for (int off = 32; off >= 1; off >>= 1) dgc_acc += __shfl_xor(dgc_acc, off);
+  if (l == 0) wsum[w] = dgc_acc;
   __syncthreads();  // value passes done: the LDS becomes the key-side tiles
-  if ((tid & 3) == 0) dbY[tid >> 2] = dbY_acc;
+  if ((tid & 7) == 0) dbY[tid >> 3] = dbY_acc;
 
-  load_tile(sk.K, LKF, k, b, t0, h, T, H);
-  load_tile(sk.Q, LKF, q, b, t0, h, T, H);
-  load_f32<C, C>(sk.Tm, LC, rec, C);
-  // dTm, strictly lower part (the only part that reaches dA).
+  load_tile<TIn, float, 512>(sk.K, LKF, k, b, t0, h, T, H);
+  load_tile<TIn, float, 512>(sk.Q, LKF, q, b, t0, h, T, H);
+  for (int i = tid; i < C * C / 4; i += 512) {
+    const int r = i / (C / 4), c4 = i % (C / 4);
+    *reinterpret_cast<f32x4*>(sk.Tm + r * LC + c4 * 4) =
+        *reinterpret_cast<const f32x4*>(rec + r * C + c4 * 4);
+  }
+  // dTm, strictly lower part (the only part that reaches dA); zeros above.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (j > wT) continue;
+  for (int t = 0; t < 2; ++t) {
+    if (t >= nT) continue;
+    const int y = yT0 + 8 * t;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * wT + 4 * (l >> 4) + i, cc = 16 * j + (l & 15);
-      st_lds(&sk.dT[r * LC + cc], cc < r ? aT[j][i] : 0.f);
+      const int r = 16 * low_rt(y) + 4 * (l >> 4) + i, cc = 16 * low_ct(y) + (l & 15);
+      st_lds(&sk.dT[r * LC + cc], cc < r ? aT[t][i] : 0.f);
     }
   }
-  for (int i = tid; i < C * C; i += 256) {
+  for (int i = tid; i < C * C; i += 512) {
     const int r = i / C, cc = i % C;
     if ((cc >> 4) > (r >> 4)) sk.dT[r * LC + cc] = 0.f;
   }
   __syncthreads();
 
-  // rho: dq_S.q + Z1.k - Z2.k per row, and the sum of Z2.k (wave partials).
+  // rho: dq_S.q + Z1.k - Z2.k per row, and Z2.k (key-group partials).
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int t = 0; t < 2; ++t) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * r + 4 * (l >> 4) + i;
-      float s = 0.f, z = 0.f;
+      const int tok = 16 * (tr0 + t) + 4 * (l >> 4) + i;
+      float sq = 0.f, z = 0.f;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int key = (2 * w + m) * 16 + (l & 15);
+        const int key = (kt0 + m) * 16 + (l & 15);
         const float kv = sk.K[tok * LKF + key];
-        s += aQ[r][m][i] * sk.Q[tok * LKF + key] + aZ1[r][m][i] * kv;
-        z += aZ2[r][m][i] * kv;
+        sq += aQ[t][m][i] * sk.Q[tok * LKF + key] + aZ1[t][m][i] * kv;
+        z += aZ2[t][m][i] * kv;
       }
-      s = row16_sum(s);
+      sq = row16_sum(sq);
       z = row16_sum(z);
       if ((l & 15) == 0) {
-        red[w][tok] = s - z;
-        redz[w][tok] = z;
+        red[w >> 1][tok] = sq - z;
+        redz[w >> 1][tok] = z;
       }
     }
   }
 
-  // M1 = dTm Tm^T (tile (w, j): contraction b < 16 min(w, j) + 16).
-  f32x4 m1[4];
+  // M1 = dTm Tm^T: row tile w >> 1, column tiles 2 (w & 1) + {0, 1}
+  // (contraction b < 16 min(row tile, column tile) + 16).
+  {
+    const int at = w >> 1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    m1[j] = zero4();
-    const int kend = 16 * (min(w, j) + 1);
-    for (int k0 = 0; k0 < kend; k0 += 4) {
-      const int kk = k0 + (l >> 4);
-      m1[j] = mma4(sk.dT[(16 * w + (l & 15)) * LC + kk], sk.Tm[(16 * j + (l & 15)) * LC + kk],
-                   m1[j]);
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * (w & 1) + jj;
+      f32x4 m1 = zero4();
+      const int kend = 16 * (min(at, j) + 1);
+      for (int k0 = 0; k0 < kend; k0 += 4) {
+        const int kk = k0 + (l >> 4);
+        m1 = mma4(sk.dT[(16 * at + (l & 15)) * LC + kk], sk.Tm[(16 * j + (l & 15)) * LC + kk], m1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st_lds(&sk.M1[(16 * at + 4 * (l >> 4) + i) * LC + 16 * j + (l & 15)], m1[i]);
     }
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      st_lds(&sk.M1[(16 * w + 4 * (l >> 4) + i) * LC + 16 * j + (l & 15)], m1[j][i]);
   __syncthreads();
 
-  // dA = -Tm^T M1, row tile w (contraction a >= 16 w), strictly lower part.
-  f32x4 da[4];
+  // dA = -Tm^T M1 on lower tiles y = w, w + 8 (contraction a >= 16 row tile).
+  f32x4 da[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    da[j] = zero4();
-    if (j > w) continue;
-    for (int k0 = 16 * w; k0 < C; k0 += 4) {
+  for (int t = 0; t < 2; ++t) {
+    da[t] = zero4();
+    if (t >= nP) continue;
+    const int y = w + 8 * t, rt = low_rt(y), ct = low_ct(y);
+    for (int k0 = 16 * rt; k0 < C; k0 += 4) {
       const int kk = k0 + (l >> 4);
-      da[j] = mma4(sk.Tm[kk * LC + 16 * w + (l & 15)], sk.M1[kk * LC + 16 * j + (l & 15)], da[j]);
+      da[t] = mma4(sk.Tm[kk * LC + 16 * rt + (l & 15)], sk.M1[kk * LC + 16 * ct + (l & 15)], da[t]);
     }
   }
   __syncthreads();  // Tm, dTm, M1 no longer read
@@ -805,46 +848,57 @@ __global__ __launch_bounds__(256) void bwdc_grad_kernel(
   float* Hs = sk.M1;
   float* E1s = sk.Tm;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int t = 0; t < 2; ++t) {
+    if (t >= nP) continue;
+    const int y = w + 8 * t, rt = low_rt(y), ct = low_ct(y);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * (l >> 4) + i, cc = 16 * j + (l & 15);
-      const float gr = __expf(gam[r] - gam[cc]);
+      const int r = 16 * rt + 4 * (l >> 4) + i, cc = 16 * ct + (l & 15);
+      const float gr = cc <= r ? __expf(gam[r] - gam[cc]) : 0.f;
       float e2 = 0.f, hh = 0.f, e1 = 0.f, f = 0.f;
       if (cc < r) {
-        const float a = -da[j][i] * gr;  // dA_ri G_ri
+        const float a = -da[t][i] * gr;  // dA_ri G_ri
         hh = a * Gg[r * C + cc];
         e2 = gs.bet[r] * a;
         f = gs.bet[r] * hh;
       }
-      if (cc <= r && j <= w) {
-        e1 = scale * gr * aP[j][i];
-        f += aP[j][i] * Pg[r * C + cc];
+      if (cc <= r) {
+        e1 = scale * gr * aP[t][i];
+        f += aP[t][i] * Pg[r * C + cc];
       }
       st_lds(&E2s[r * LC + cc], e2);
       st_lds(&Hs[r * LC + cc], hh);
       st_lds(&E1s[r * LC + cc], e1);
       st_lds(&sk.Ep[r * LC + cc], f);
     }
+  }
+  for (int i = tid; i < C * C; i += 512) {
+    const int r = i / C, cc = i % C;
+    if ((cc >> 4) > (r >> 4)) {
+      E2s[r * LC + cc] = 0.f;
+      Hs[r * LC + cc] = 0.f;
+      E1s[r * LC + cc] = 0.f;
+      sk.Ep[r * LC + cc] = 0.f;
+    }
+  }
   __syncthreads();
 
-  // dgam: row sums minus column sums of F, rho, the last row's terms;
-  // dbeta: dY . Vm plus the row sums of H.
+  // Row sums of F and H (threads 0..63) and column sums of F (64..127).
   if (tid < C) {
-    float fr = 0.f, fc = 0.f, hr = 0.f;
+    float fr = 0.f, hr = 0.f;
+#pragma unroll 8
     for (int i = 0; i < C; ++i) {
       fr += sk.Ep[tid * LC + i];
-      fc += sk.Ep[i * LC + tid];
       hr += Hs[tid * LC + i];
     }
-    float g = fr - fc + red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-    if (tid == C - 1) {
-      float zs = 0.f;
-      for (int r = 0; r < C; ++r) zs += redz[0][r] + redz[1][r] + redz[2][r] + redz[3][r];
-      g += gs.gC * (wsum[0] + wsum[1] + wsum[2] + wsum[3]) + zs;
-    }
-    dgam[tid] = g;
+    dgam[tid] = fr + red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
     dbA[tid] = dbY[tid] + hr;
+  } else if (tid < 2 * C) {
+    const int c = tid - C;
+    float fc = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < C; ++r) fc += sk.Ep[r * LC + c];
+    colF[c] = fc;
   }
 
   // dq += E1 K; dk += E1^T Q + (E2 + E2^T) K.
@@ -854,34 +908,42 @@ __global__ __launch_bounds__(256) void bwdc_grad_kernel(
     float bK[2], bQ[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int key = (2 * w + m) * 16 + (l & 15);
+      const int key = (kt0 + m) * 16 + (l & 15);
       bK[m] = sk.K[kk * LKF + key];
       bQ[m] = sk.Q[kk * LKF + key];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = 16 * r + (l & 15);
+    for (int t = 0; t < 2; ++t) {
+      const int tok = 16 * (tr0 + t) + (l & 15);
       const float a1 = E1s[tok * LC + kk];
       const float a1t = E1s[kk * LC + tok];
       const float a2 = E2s[tok * LC + kk] + E2s[kk * LC + tok];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        aQ[r][m] = mma4(a1, bK[m], aQ[r][m]);
-        aZ1[r][m] = mma4(a1t, bQ[m], mma4(a2, bK[m], aZ1[r][m]));
+        aQ[t][m] = mma4(a1, bK[m], aQ[t][m]);
+        aZ1[t][m] = mma4(a1t, bQ[m], mma4(a2, bK[m], aZ1[t][m]));
       }
     }
   }
-  __syncthreads();  // dgam, dbA complete
+  __syncthreads();  // dgam, colF, dbA complete
 
-  // dlog(alpha) = reverse cumulative sum of dgam; dalpha = dlog(alpha) / alpha.
+  // dgam = row sums - column sums of F + rho (+ the last row's terms);
+  // dlog(alpha) = its reverse cumulative sum; dalpha = dlog(alpha) / alpha.
   if (w == 0) {
-    float x = dgam[C - 1 - l];
+    const int r = C - 1 - l, t = t0 + r;
+    float x = dgam[r] - colF[r];
+    if (r == C - 1) {
+      float zs = 0.f, ws8 = 0.f;
+      for (int i = 0; i < C; ++i) zs += redz[0][i] + redz[1][i] + redz[2][i] + redz[3][i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ws8 += wsum[i];
+      x += gs.gC * ws8 + zs;
+    }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off);
       if (l >= off) x += y;
     }
-    const int r = C - 1 - l, t = t0 + r;
     if (t < T) {
       const size_t gi = ((size_t)b * T + t) * H + h;
       dalpha[gi] = x / alpha[gi];
@@ -889,17 +951,17 @@ __global__ __launch_bounds__(256) void bwdc_grad_kernel(
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * r + 4 * (l >> 4) + i, t = t0 + tok;
-      if (t >= T) continue;
+      const int tok = 16 * (tr0 + t) + 4 * (l >> 4) + i, tt = t0 + tok;
+      if (tt >= T) continue;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int key = (2 * w + m) * 16 + (l & 15);
-        const size_t o = tok_off(b, t, h, T, H) + key;
-        dq[o] = aQ[r][m][i];
-        dk[o] = aZ1[r][m][i] + aZ2[r][m][i];
+        const int key = (kt0 + m) * 16 + (l & 15);
+        const size_t o = tok_off(b, tt, h, T, H) + key;
+        dq[o] = aQ[t][m][i];
+        dk[o] = aZ1[t][m][i] + aZ2[t][m][i];
       }
     }
 }
@@ -923,7 +985,7 @@ hipError_t launch_bwdc_t(const BwdArgs& p) {
                      p.beta, p.dout, p.dstate_out, p.dv, p.dstate_in, p.T, p.H, NC, NS, p.scale,
                      ws);
   if (NC > 0)
-    hipLaunchKernelGGL(bwdc_grad_kernel<TIn>, dim3(BH * NC), dim3(256), 0, st, q, k, p.alpha,
+    hipLaunchKernelGGL(bwdc_grad_kernel<TIn>, dim3(BH * NC), dim3(512), 0, st, q, k, p.alpha,
                        p.beta, p.dout, p.dq, p.dk, p.dalpha, p.dbeta, p.T, p.H, NC, p.scale, ws);
   return hipGetLastError();
 }
