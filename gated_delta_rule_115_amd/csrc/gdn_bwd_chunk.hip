@@ -295,18 +295,89 @@ __device__ __forceinline__ void load_gates(Gates& gs, const float* rec, const fl
   }
 }
 
+// Per-chunk inputs of the sequential kernels, one chunk ahead in registers
+// (512 threads): K (and Q) tiles in the input type, the record's Tm (and P),
+// the gates' log cumsum and beta (threads 0..63).
+template <class TIn>
+struct TileRegs {
+  typedef typename Vec16<TIn>::type vec;
+  static constexpr int VN = Vec16<TIn>::N;
+  static constexpr int KV = C * D / VN / 512;  // K-tile vectors per thread
+  vec x[KV];
+  __device__ __forceinline__ void issue(const TIn* src, int b, int t0, int h, int T, int H) {
+#pragma unroll
+    for (int u = 0; u < KV; ++u) {
+      const int i = threadIdx.x + 512 * u, r = i / (D / VN), cv = i % (D / VN);
+      if (t0 + r < T) {
+        x[u] = *reinterpret_cast<const vec*>(src + tok_off(b, t0 + r, h, T, H) + cv * VN);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) x[u][e] = from_f32<TIn>(0.f);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(TIn* dst, int ld) const {
+#pragma unroll
+    for (int u = 0; u < KV; ++u) {
+      const int i = threadIdx.x + 512 * u, r = i / (D / VN), cv = i % (D / VN);
+      *reinterpret_cast<vec*>(dst + r * ld + cv * VN) = x[u];
+    }
+  }
+};
+// A C x C f32 record matrix: 2 vectors per thread.
+struct RecRegs {
+  f32x4 x[2];
+  __device__ __forceinline__ void issue(const float* src) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = threadIdx.x + 512 * u;
+      x[u] = *reinterpret_cast<const f32x4*>(src + (i >> 4) * C + (i & 15) * 4);
+    }
+  }
+  __device__ __forceinline__ void store(float* dst) const {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = threadIdx.x + 512 * u;
+      *reinterpret_cast<f32x4*>(dst + (i >> 4) * LC + (i & 15) * 4) = x[u];
+    }
+  }
+};
+struct GateRegs {
+  float gm = 0.f, bt = 0.f;
+  __device__ __forceinline__ void issue(const float* rec, const float* beta, int b, int t0, int h,
+                                        int T, int H) {
+    const int tid = threadIdx.x;
+    if (tid < C) {
+      gm = rec[3 * C * C + tid];
+      bt = (t0 + tid < T) ? beta[((size_t)b * T + t0 + tid) * H + h] : 0.f;
+    }
+  }
+  // Threads 0..63 are wave 0: the last row's log gate by a lane broadcast.
+  __device__ __forceinline__ void store(Gates& gs) const {
+    const int tid = threadIdx.x;
+    if (tid < C) {
+      const float gl = __shfl(gm, C - 1);
+      gs.g[tid] = __expf(gm);
+      gs.d[tid] = __expf(gl - gm);
+      gs.bet[tid] = bt;
+      if (tid == 0) gs.gC = __expf(gl);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // forward: S entering every chunk, Vm and U (value slice of DVS columns).
-// Wave w: token rows 16 w .. 16 w + 15 of the C x DVS products, state key
-// rows 32 w .. 32 w + 31.
+// Wave w (8 waves): state key rows 16 w .. 16 w + 15; token rows 16 (w >> 1)
+// .. + 15 and column tiles (w & 1) NT / 2 + {0 .. NT / 2 - 1} of the C x DVS
+// products.
 // ---------------------------------------------------------------------------
 template <class TIn, int DVS>
-__global__ __launch_bounds__(256) void bwdc_fwd_kernel(const TIn* __restrict__ k,
+__global__ __launch_bounds__(512) void bwdc_fwd_kernel(const TIn* __restrict__ k,
                                                        const TIn* __restrict__ v,
                                                        const float* __restrict__ beta,
                                                        const float* __restrict__ state_in, int T,
                                                        int H, int NC, int NS, float* __restrict__ wsb) {
-  constexpr int NT = DVS / 16;
+  constexpr int NT = DVS / 16, NH = NT / 2;
   constexpr int LK = D + 8;        // K tile stride (input type)
   constexpr int LS = DVS + 16;     // [rows][DVS] tiles read m-contiguous
   __shared__ __align__(16) TIn Ks[C * LK];
@@ -316,127 +387,150 @@ __global__ __launch_bounds__(256) void bwdc_fwd_kernel(const TIn* __restrict__ k
   __shared__ __align__(16) float Us[C * LS];
   __shared__ Gates gs;
 
-  const int tid = threadIdx.x, w = wave_index(), l = lane_id();
+  const int w = wave_index(), l = lane_id();
   int bh, slice;
   xcd_group_map(blockIdx.x, gridDim.x / NS, NS, &bh, &slice);
   const int b = bh / H, h = bh % H, col0 = slice * DVS;
+  const int rt = w >> 1, ct0 = (w & 1) * NH;
   const Ws ws = ws_split(wsb, (size_t)gridDim.x / NS * NC);
 
-  f32x4 S[2][NT];
+  f32x4 S[NT];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int n = 0; n < NT; ++n) {
+    S[n] = zero4();
+    if (state_in) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      S[m][n] = zero4();
-      if (state_in) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          S[m][n][i] = state_in[((size_t)bh * D + (2 * w + m) * 16 + 4 * (l >> 4) + i) * D + col0 +
-                                n * 16 + (l & 15)];
-      }
+      for (int i = 0; i < 4; ++i)
+        S[n][i] = state_in[((size_t)bh * D + 16 * w + 4 * (l >> 4) + i) * D + col0 + n * 16 +
+                           (l & 15)];
     }
+  }
+
+  TileRegs<TIn> kr;
+  RecRegs tr;
+  GateRegs gr;
+  uint32_t vr[NH][4];
+  auto issue = [&](int c) {
+    const int t0 = c * C;
+    const float* rec = ws.rec + ((size_t)bh * NC + c) * REC;
+    kr.issue(k, b, t0, h, T, H);
+    tr.issue(rec);
+    gr.issue(rec, beta, b, t0, h, T, H);
+#pragma unroll
+    for (int n = 0; n < NH; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * rt + 4 * (l >> 4) + i;
+        vr[n][i] = t < T ? load_raw32(v + tok_off(b, t, h, T, H) + col0 + (ct0 + n) * 16 +
+                                      (l & 15))
+                         : 0u;
+      }
+  };
+  if (NC > 0) issue(0);
 
   for (int c = 0; c < NC; ++c) {
     const int t0 = c * C;
     const size_t ch = (size_t)bh * NC + c;
-    const float* rec = ws.rec + ch * REC;
     __syncthreads();  // the previous chunk's readers are done with LDS
-    load_tile(Ks, LK, k, b, t0, h, T, H);
-    load_f32<C, C>(Ts, LC, rec, C);
-    load_gates(gs, rec, beta, b, t0, h, T, H);
+    kr.store(Ks, LK);
+    tr.store(Ts);
+    gr.store(gs);
+    float vv[NH][4];
+#pragma unroll
+    for (int n = 0; n < NH; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[n][i] = raw32_to_f32<TIn>(vr[n][i]);
     float* Sg = ws.S + ch * D * D;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = (2 * w + m) * 16 + 4 * (l >> 4) + i, cc = n * 16 + (l & 15);
-          Ss[r * LS + cc] = S[m][n][i];
-          Sg[r * D + col0 + cc] = S[m][n][i];
-        }
-    __syncthreads();
-
-    // X = K S -> Vm = V - g X, Y = beta Vm.
-    f32x4 X[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) X[n] = zero4();
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int kk = k0 + (l >> 4);
-      const float a = to_f32(Ks[(16 * w + (l & 15)) * LK + kk]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) X[n] = mma4(a, Ss[kk * LS + n * 16 + (l & 15)], X[n]);
-    }
-    float* Vg = ws.Vm + ch * C * D;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * (l >> 4) + i, cc = n * 16 + (l & 15);
-        const int t = t0 + r;
-        const float vv = t < T ? to_f32(v[tok_off(b, t, h, T, H) + col0 + cc]) : 0.f;
-        const float vm = vv - gs.g[r] * X[n][i];
+        Ss[r * LS + cc] = S[n][i];
+        Sg[r * D + col0 + cc] = S[n][i];
+      }
+    __syncthreads();
+    if (c + 1 < NC) issue(c + 1);
+
+    // X = K S -> Vm = V - g X, Y = beta Vm.
+    f32x4 X[NH];
+#pragma unroll
+    for (int n = 0; n < NH; ++n) X[n] = zero4();
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const int kk = k0 + (l >> 4);
+      const float a = to_f32(Ks[(16 * rt + (l & 15)) * LK + kk]);
+#pragma unroll
+      for (int n = 0; n < NH; ++n)
+        X[n] = mma4(a, Ss[kk * LS + (ct0 + n) * 16 + (l & 15)], X[n]);
+    }
+    float* Vg = ws.Vm + ch * C * D;
+#pragma unroll
+    for (int n = 0; n < NH; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * (l >> 4) + i, cc = (ct0 + n) * 16 + (l & 15);
+        const float vm = vv[n][i] - gs.g[r] * X[n][i];
         Vg[r * D + col0 + cc] = vm;
         Ys[r * LS + cc] = gs.bet[r] * vm;
       }
     __syncthreads();
 
-    // U = Tm Y (Tm lower triangular: tokens i < 16 (w + 1)).
-    f32x4 Uc[NT];
+    // U = Tm Y (Tm lower triangular: tokens i < 16 (rt + 1)).
+    f32x4 Uc[NH];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) Uc[n] = zero4();
-    for (int k0 = 0; k0 < 16 * (w + 1); k0 += 4) {
+    for (int n = 0; n < NH; ++n) Uc[n] = zero4();
+    for (int k0 = 0; k0 < 16 * (rt + 1); k0 += 4) {
       const int kk = k0 + (l >> 4);
-      const float a = Ts[(16 * w + (l & 15)) * LC + kk];
+      const float a = Ts[(16 * rt + (l & 15)) * LC + kk];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) Uc[n] = mma4(a, Ys[kk * LS + n * 16 + (l & 15)], Uc[n]);
+      for (int n = 0; n < NH; ++n)
+        Uc[n] = mma4(a, Ys[kk * LS + (ct0 + n) * 16 + (l & 15)], Uc[n]);
     }
     float* Ug = ws.U + ch * C * D;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+    for (int n = 0; n < NH; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * (l >> 4) + i, cc = n * 16 + (l & 15);
+        const int r = 16 * rt + 4 * (l >> 4) + i, cc = (ct0 + n) * 16 + (l & 15);
         Ug[r * D + col0 + cc] = Uc[n][i];
         Us[r * LS + cc] = gs.d[r] * Uc[n][i];
       }
     __syncthreads();
 
-    // S <- g_{C-1} S + K^T diag(d) U.
+    // S <- g_{C-1} S + K^T diag(d) U (key tile w).
     const float gC = gs.gC;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) S[m][n] *= gC;
+    for (int n = 0; n < NT; ++n) S[n] *= gC;
 #pragma unroll 4
     for (int k0 = 0; k0 < C; k0 += 4) {
       const int kk = k0 + (l >> 4);
-      float a[2];
+      const float a = to_f32(Ks[kk * LK + 16 * w + (l & 15)]);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) a[m] = to_f32(Ks[kk * LK + (2 * w + m) * 16 + (l & 15)]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const float bb = Us[kk * LS + n * 16 + (l & 15)];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) S[m][n] = mma4(a[m], bb, S[m][n]);
-      }
+      for (int n = 0; n < NT; ++n) S[n] = mma4(a, Us[kk * LS + n * 16 + (l & 15)], S[n]);
     }
+    (void)t0;
   }
 }
 
 // ---------------------------------------------------------------------------
-// dstate: the gradient of the state, chunks in reverse (value slice).
+// dstate: the gradient of the state, chunks in reverse (value slice).  Wave
+// w: gradient key rows 16 w .. 16 w + 15; token rows 16 (w >> 1) .. + 15 and
+// column tiles (w & 1) NT / 2 + {0 .. NT / 2 - 1} of dU, dY.
 // ---------------------------------------------------------------------------
 template <class TIn, int DVS>
-__global__ __launch_bounds__(256) void bwdc_dstate_kernel(
+__global__ __launch_bounds__(512) void bwdc_dstate_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
     const float* __restrict__ dout, const float* __restrict__ dstate_out, float* __restrict__ dv,
     float* __restrict__ dstate_in, int T, int H, int NC, int NS, float scale,
     float* __restrict__ wsb) {
-  constexpr int NT = DVS / 16;
+  constexpr int NT = DVS / 16, NH = NT / 2;
   constexpr int LK = D + 8;
   constexpr int LS = DVS + 16;
+  constexpr int LX = DVS + 4;
+  constexpr int OV = C * DVS / 4 / 512;  // dO vectors per thread
+  static_assert(LX <= LC, "dX fits in the P tile");
+  static_assert(OV >= 1, "dO slice covers the work-group");
   __shared__ __align__(16) TIn Ks[C * LK];
   __shared__ __align__(16) TIn Qs[C * LK];
   __shared__ __align__(16) float Ts[C * LC];
@@ -445,84 +539,101 @@ __global__ __launch_bounds__(256) void bwdc_dstate_kernel(
   __shared__ __align__(16) float dSs[D * LS];
   __shared__ __align__(16) float dUs[C * LS];
   __shared__ Gates gs;
-  constexpr int LX = DVS + 4;
-  static_assert(LX <= LC, "dX fits in the P tile");
 
   const int tid = threadIdx.x, w = wave_index(), l = lane_id();
   int bh, slice;
   xcd_group_map(blockIdx.x, gridDim.x / NS, NS, &bh, &slice);
   const int b = bh / H, h = bh % H, col0 = slice * DVS;
+  const int rt = w >> 1, ct0 = (w & 1) * NH;
   const Ws ws = ws_split(wsb, (size_t)gridDim.x / NS * NC);
   float* dXs = Ps;
 
-  f32x4 G[2][NT];
+  f32x4 G[NT];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int n = 0; n < NT; ++n) {
+    G[n] = zero4();
+    if (dstate_out) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      G[m][n] = zero4();
-      if (dstate_out) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          G[m][n][i] = dstate_out[((size_t)bh * D + (2 * w + m) * 16 + 4 * (l >> 4) + i) * D +
-                                  col0 + n * 16 + (l & 15)];
-      }
+      for (int i = 0; i < 4; ++i)
+        G[n][i] = dstate_out[((size_t)bh * D + 16 * w + 4 * (l >> 4) + i) * D + col0 + n * 16 +
+                             (l & 15)];
     }
+  }
+
+  TileRegs<TIn> kr, qr;
+  RecRegs tr, pr;
+  GateRegs gr;
+  f32x4 orr[OV];
+  auto issue = [&](int c) {
+    const int t0 = c * C;
+    const float* rec = ws.rec + ((size_t)bh * NC + c) * REC;
+    kr.issue(k, b, t0, h, T, H);
+    qr.issue(q, b, t0, h, T, H);
+    tr.issue(rec);
+    pr.issue(rec + C * C);
+    gr.issue(rec, beta, b, t0, h, T, H);
+#pragma unroll
+    for (int u = 0; u < OV; ++u) {
+      const int i = tid + 512 * u, r = i / (DVS / 4), c4 = i % (DVS / 4);
+      orr[u] = zero4();
+      if (t0 + r < T)
+        orr[u] = *reinterpret_cast<const f32x4*>(dout + tok_off(b, t0 + r, h, T, H) + col0 +
+                                                 c4 * 4);
+    }
+  };
+  if (NC > 0) issue(NC - 1);
 
   for (int c = NC - 1; c >= 0; --c) {
     const int t0 = c * C;
     const size_t ch = (size_t)bh * NC + c;
-    const float* rec = ws.rec + ch * REC;
     __syncthreads();
-    load_tile(Ks, LK, k, b, t0, h, T, H);
-    load_tile(Qs, LK, q, b, t0, h, T, H);
-    load_f32<C, C>(Ts, LC, rec, C);
-    load_f32<C, C>(Ps, LC, rec + C * C, C);
-    load_gates(gs, rec, beta, b, t0, h, T, H);
-    for (int i = tid; i < C * DVS / 4; i += 256) {
-      const int r = i / (DVS / 4), c4 = i % (DVS / 4);
-      f32x4 x = zero4();
-      if (t0 + r < T)
-        x = *reinterpret_cast<const f32x4*>(dout + tok_off(b, t0 + r, h, T, H) + col0 +
-                                            c4 * 4);
-      *reinterpret_cast<f32x4*>(dOs + r * LS + c4 * 4) = x;
+    kr.store(Ks, LK);
+    qr.store(Qs, LK);
+    tr.store(Ts);
+    pr.store(Ps);
+    gr.store(gs);
+#pragma unroll
+    for (int u = 0; u < OV; ++u) {
+      const int i = tid + 512 * u, r = i / (DVS / 4), c4 = i % (DVS / 4);
+      *reinterpret_cast<f32x4*>(dOs + r * LS + c4 * 4) = orr[u];
     }
     float* dSg = ws.dS + ch * D * D;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = (2 * w + m) * 16 + 4 * (l >> 4) + i, cc = n * 16 + (l & 15);
-          dSs[r * LS + cc] = G[m][n][i];
-          dSg[r * D + col0 + cc] = G[m][n][i];
-        }
-    __syncthreads();
-
-    // dU = P^T dO + diag(d) K dSn   (P^T: tokens r >= 16 w).
-    f32x4 du[NT], kd[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) du[n] = kd[n] = zero4();
-    for (int k0 = 16 * w; k0 < C; k0 += 4) {
-      const int kk = k0 + (l >> 4);
-      const float a = Ps[kk * LC + 16 * w + (l & 15)];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) du[n] = mma4(a, dOs[kk * LS + n * 16 + (l & 15)], du[n]);
-    }
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int kk = k0 + (l >> 4);
-      const float a = to_f32(Ks[(16 * w + (l & 15)) * LK + kk]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) kd[n] = mma4(a, dSs[kk * LS + n * 16 + (l & 15)], kd[n]);
-    }
-    float* dUg = ws.dU + ch * C * D;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * (l >> 4) + i, cc = n * 16 + (l & 15);
+        dSs[r * LS + cc] = G[n][i];
+        dSg[r * D + col0 + cc] = G[n][i];
+      }
+    __syncthreads();
+    if (c > 0) issue(c - 1);
+
+    // dU = P^T dO + diag(d) K dSn   (P^T: tokens r >= 16 rt).
+    f32x4 du[NH], kd[NH];
+#pragma unroll
+    for (int n = 0; n < NH; ++n) du[n] = kd[n] = zero4();
+    for (int k0 = 16 * rt; k0 < C; k0 += 4) {
+      const int kk = k0 + (l >> 4);
+      const float a = Ps[kk * LC + 16 * rt + (l & 15)];
+#pragma unroll
+      for (int n = 0; n < NH; ++n)
+        du[n] = mma4(a, dOs[kk * LS + (ct0 + n) * 16 + (l & 15)], du[n]);
+    }
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const int kk = k0 + (l >> 4);
+      const float a = to_f32(Ks[(16 * rt + (l & 15)) * LK + kk]);
+#pragma unroll
+      for (int n = 0; n < NH; ++n)
+        kd[n] = mma4(a, dSs[kk * LS + (ct0 + n) * 16 + (l & 15)], kd[n]);
+    }
+    float* dUg = ws.dU + ch * C * D;
+#pragma unroll
+    for (int n = 0; n < NH; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * (l >> 4) + i, cc = (ct0 + n) * 16 + (l & 15);
         const float x = du[n][i] + gs.d[r] * kd[n][i];
         dUg[r * D + col0 + cc] = x;
         dUs[r * LS + cc] = x;
@@ -530,21 +641,22 @@ __global__ __launch_bounds__(256) void bwdc_dstate_kernel(
     __syncthreads();
 
     // dY = Tm^T dU; dv = beta dY; dX = -beta g dY (into the P tile).
-    f32x4 dy[NT];
+    f32x4 dy[NH];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) dy[n] = zero4();
-    for (int k0 = 16 * w; k0 < C; k0 += 4) {
+    for (int n = 0; n < NH; ++n) dy[n] = zero4();
+    for (int k0 = 16 * rt; k0 < C; k0 += 4) {
       const int kk = k0 + (l >> 4);
-      const float a = Ts[kk * LC + 16 * w + (l & 15)];
+      const float a = Ts[kk * LC + 16 * rt + (l & 15)];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) dy[n] = mma4(a, dUs[kk * LS + n * 16 + (l & 15)], dy[n]);
+      for (int n = 0; n < NH; ++n)
+        dy[n] = mma4(a, dUs[kk * LS + (ct0 + n) * 16 + (l & 15)], dy[n]);
     }
     float* dYg = ws.dY + ch * C * D;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+    for (int n = 0; n < NH; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * (l >> 4) + i, cc = n * 16 + (l & 15);
+        const int r = 16 * rt + 4 * (l >> 4) + i, cc = (ct0 + n) * 16 + (l & 15);
         const int t = t0 + r;
         dYg[r * D + col0 + cc] = dy[n][i];
         if (t < T) dv[tok_off(b, t, h, T, H) + col0 + cc] = gs.bet[r] * dy[n][i];
@@ -552,39 +664,29 @@ __global__ __launch_bounds__(256) void bwdc_dstate_kernel(
       }
     __syncthreads();
 
-    // dS <- g_{C-1} dS + Q^T diag(scale g) dO + K^T dX.
+    // dS <- g_{C-1} dS + Q^T diag(scale g) dO + K^T dX (key tile w).
     const float gC = gs.gC;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) G[m][n] *= gC;
+    for (int n = 0; n < NT; ++n) G[n] *= gC;
 #pragma unroll 2
     for (int k0 = 0; k0 < C; k0 += 4) {
       const int kk = k0 + (l >> 4);
-      const float sg = scale * gs.g[kk];
-      float aq[2], ak[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        aq[m] = sg * to_f32(Qs[kk * LK + (2 * w + m) * 16 + (l & 15)]);
-        ak[m] = to_f32(Ks[kk * LK + (2 * w + m) * 16 + (l & 15)]);
-      }
+      const float aq = scale * gs.g[kk] * to_f32(Qs[kk * LK + 16 * w + (l & 15)]);
+      const float ak = to_f32(Ks[kk * LK + 16 * w + (l & 15)]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const float bo = dOs[kk * LS + n * 16 + (l & 15)];
         const float bx = dXs[kk * LX + n * 16 + (l & 15)];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) G[m][n] = mma4(ak[m], bx, mma4(aq[m], bo, G[m][n]));
+        G[n] = mma4(ak, bx, mma4(aq, bo, G[n]));
       }
     }
   }
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dstate_in[((size_t)bh * D + (2 * w + m) * 16 + 4 * (l >> 4) + i) * D + col0 + n * 16 +
-                  (l & 15)] = G[m][n][i];
+    for (int i = 0; i < 4; ++i)
+      dstate_in[((size_t)bh * D + 16 * w + 4 * (l >> 4) + i) * D + col0 + n * 16 + (l & 15)] =
+          G[n][i];
 }
 
 // ---------------------------------------------------------------------------
@@ -978,10 +1080,10 @@ hipError_t launch_bwdc_t(const BwdArgs& p) {
   if (NC > 0) {
     hipLaunchKernelGGL(bwdc_prep_kernel<TIn>, dim3(BH * NC), dim3(256), 0, st, q, k, p.alpha,
                        p.beta, p.T, p.H, NC, p.scale, ws_split(ws, (size_t)BH * NC).rec);
-    hipLaunchKernelGGL((bwdc_fwd_kernel<TIn, DVS>), dim3(BH * NS), dim3(256), 0, st, k, v, p.beta,
+    hipLaunchKernelGGL((bwdc_fwd_kernel<TIn, DVS>), dim3(BH * NS), dim3(512), 0, st, k, v, p.beta,
                        p.state_in, p.T, p.H, NC, NS, ws);
   }
-  hipLaunchKernelGGL((bwdc_dstate_kernel<TIn, DVS>), dim3(BH * NS), dim3(256), 0, st, q, k,
+  hipLaunchKernelGGL((bwdc_dstate_kernel<TIn, DVS>), dim3(BH * NS), dim3(512), 0, st, q, k,
                      p.beta, p.dout, p.dstate_out, p.dv, p.dstate_in, p.T, p.H, NC, NS, p.scale,
                      ws);
   if (NC > 0)
