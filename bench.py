@@ -23,6 +23,7 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   leg "backward_t1024":  gradients of the scalar-gate prefill (dq, dk, dv,
                          dalpha, dbeta, dS0) for B=4, H=32, T=1024, d=128,
                          bf16 inputs, f32 gradients: gdn_prefill_backward
+                         (chunked reverse mode, f32 MFMA)
   leg "conv_qwen32b":    Qwen-32B-shaped layer with projection adaptation,
                          B=2, H=40, T=16384: gdn_prefill_chunked_conv (short
                          convolution + SiLU on the raw q, k, v and the L2 norm
@@ -61,9 +62,6 @@ import synthetic  # noqa: E402
 PEAK_BF16_FLOPS = 2.5e15   # bf16 and f16 MFMA
 PEAK_F32_MFMA_FLOPS = 157.3e12
 PEAK_HBM_BPS = 8.0e12
-# f32 VALU without packed-f32 instructions (the library is built with them
-# off): 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz.
-PEAK_F32_VALU_FLOPS = 78.6e12
 
 # Algorithmic work per unit (fixed definitions; d = Dk = Dv, chunk C = 64):
 #   prefill flops per token-head: dense-tile count of the chunked form
@@ -103,13 +101,18 @@ def chgate_bytes(B, T, H, dk, dv, esize=2):
     return B * T * H * (esize * (2 * dk + 2 * dv) + 4 * dk + 4) + B * H * dk * dv * 4
 
 
-# Backward (direct adjoint with recompute) per token-head: the forward state
-# update twice (checkpoint sweep and recompute from the checkpoints, ~5 dk dv
-# each) and
-# the adjoint step (~19 dk dv: G += q do^T, S do, G v, G^T k, P^T k, P g,
-# <G, P>, G p, the carry of G).
-def backward_flops_per_token_head(dk, dv):
-    return 29 * dk * dv
+# Backward per token-head at d = d_k = d_v, chunk C = 64: dense-tile count of
+# the chunked reverse mode (products on lower block triangles counted at
+# 10/16 of the square):
+#   C d^2 products (2 C d^2 flops each): K S and K^T (d U) in the state
+#   sweep; K dSn and Q^T dO + K^T dX (two) in the reverse sweep; dO S^T,
+#   dX S^T, (d U) dSn^T in the gradient pass -> 16 C d^2;
+#   C^2 d products: K K^T, Q K^T (lower), Tm Y, P^T dO, Tm^T dU, dO U^T,
+#   dU Y^T (lower), E1 K, E1^T Q, (E2 + E2^T) K -> 14.75 C^2 d;
+#   C^3 products: dTm Tm^T and Tm^T M1 -> 4 C^3;
+# divided by C: 16 d^2 + 14.75 C d + 4 C^2 = 399,360 at d = 128.
+def backward_flops_per_token_head(d, C=64):
+    return int(16 * d * d + 14.75 * C * d + 4 * C * C)
 
 
 def swa_set_sizes(T, n_sink, window):
@@ -149,8 +152,10 @@ PREFILL_CONV_KERNELS = ("prefill_lead_kernel<bf16,conv> + segment_combine_kernel
                         "prefill_out_kernel<bf16,conv>")
 CHGATE_KERNELS = ("chgate_prep_kernel (f32) + chgate_recur_tile_kernel (bf16 inputs: f16 MFMA "
                   "operands, f32 accumulation and state)")
-# The backward call launches the adjoint kernel and the slice-partial sum.
-BWD_KERNELS = "gdn_bwd_kernel<bf16,128,128,32> + bwd_reduce_kernel (f32)"
+# The backward call (d = 128) launches the chunked reverse mode's four kernels,
+# every product on f32 MFMA.
+BWD_KERNELS = ("bwdc_prep_kernel + bwdc_fwd_kernel + bwdc_dstate_kernel + bwdc_grad_kernel "
+               "(bf16 inputs, f32 MFMA)")
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
@@ -181,9 +186,9 @@ COUNTERS = {
         sha1="d919a99ca61702a2b04a8647f6725c5fd6fcad7c",
         fetch_kib=264783 + 394320, write_kib=395285 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
-        src="gated_delta_rule_115_amd/csrc/gdn_bwd.hip",
-        sha1="c17595e858a5302d13a5199bfbb3355398e23a48",
-        fetch_kib=1348643 + 264212, write_kib=2703971 + 132096, profile=PROFILE),
+        src="gated_delta_rule_115_amd/csrc/gdn_bwd_chunk.hip",
+        sha1="0",
+        fetch_kib=0, write_kib=0, profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
@@ -364,7 +369,7 @@ def make_backward_leg():
         mark("backward")
 
     info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
-                alu_flops=backward_flops_per_token_head(d, d) * B * T * H,
+                flops=backward_flops_per_token_head(d) * B * T * H,
                 bytes=B * T * H * (2 * 3 * d + 8 + 4 * d + 4 * (3 * d + 2)))
     return run, info
 
@@ -673,12 +678,14 @@ def main():
         inf = infos["backward_t1024"]
         ms = seg_ms[("backward_t1024", "backward")]
         sec = ms / 1e3
-        roof_bwd = dict(bound="alu", kernel=BWD_KERNELS,
-                        achieved=inf["alu_flops"] / sec / 1e12,
-                        peak=PEAK_F32_VALU_FLOPS / 1e12, unit="TFLOP/s",
-                        frac=inf["alu_flops"] / sec / PEAK_F32_VALU_FLOPS,
+        roof_bwd = dict(bound="mfma", kernel=BWD_KERNELS,
+                        achieved=inf["flops"] / sec / 1e12,
+                        peak=PEAK_F32_MFMA_FLOPS / 1e12, unit="TFLOP/s",
+                        frac=inf["flops"] / sec / PEAK_F32_MFMA_FLOPS,
                         traffic=traffic_bytes(BWD_KERNELS),
-                        ms_per_launch=ms, flops_per_launch=inf["alu_flops"])
+                        ms_per_launch=ms, flops_per_launch=inf["flops"],
+                        hbm_bytes_algorithmic=inf["bytes"],
+                        hbm_frac_algorithmic=inf["bytes"] / sec / PEAK_HBM_BPS)
     roof_conv = None
     if "conv_qwen32b" in out_legs:
         inf = infos["conv_qwen32b"]

@@ -323,6 +323,16 @@ struct TileRegs {
       *reinterpret_cast<vec*>(dst + r * ld + cv * VN) = x[u];
     }
   }
+  __device__ __forceinline__ void store_f32(float* dst, int ld) const {
+#pragma unroll
+    for (int u = 0; u < KV; ++u) {
+      const int i = threadIdx.x + 512 * u, r = i / (D / VN), cv = i % (D / VN);
+#pragma unroll
+      for (int e = 0; e < VN; e += 4)
+        *reinterpret_cast<f32x4*>(dst + r * ld + cv * VN + e) =
+            f32x4{to_f32(x[u][e]), to_f32(x[u][e + 1]), to_f32(x[u][e + 2]), to_f32(x[u][e + 3])};
+    }
+  }
 };
 // A C x C f32 record matrix: 2 vectors per thread.
 struct RecRegs {
@@ -767,7 +777,8 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
   __shared__ __align__(16) char smem[sizeof(GradV) > sizeof(GradK) ? sizeof(GradV)
                                                                     : sizeof(GradK)];
   __shared__ Gates gs;
-  __shared__ float gam[C], red[4][C], redz[4][C], dbY[C], dgam[C], dbA[C], colF[C], wsum[8];
+  __shared__ float gam[C], red[4][C], redz[4][C], dbY[C], dgam[C], dbA[C], colF[C], zrow[C],
+      wsum[8];
   GradV& sv = *reinterpret_cast<GradV*>(smem);
   GradK& sk = *reinterpret_cast<GradK*>(smem);
 
@@ -793,12 +804,41 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
   float dbY_acc = 0.f, dgc_acc = 0.f;
 
   PassRegs pr;
+  TileRegs<TIn> kx, qx;  // K and Q of the chunk, loaded during the last pass
+  RecRegs tx;            // Tm, likewise
+  float pv[2][4], gv[2][4];  // P and K K^T on this wave's dA / dP tiles, likewise
   pass_issue(pr, ws, ch, dout, b, t0, h, T, H, 0);
+  __syncthreads();  // gates in LDS
+  // Per-row factors of this wave's A fragments (token rows 16 (tr0 + t) + l % 16).
+  float fo[2], fy[2], fu[2], fb[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int tok = (tr0 + t) * 16 + (l & 15);
+    fo[t] = scale * gs.g[tok];
+    fy[t] = -gs.bet[tok] * gs.g[tok];
+    fu[t] = gs.d[tok];
+    fb[t] = t < nT ? gs.bet[16 * low_ct(yT0 + 8 * t) + (l & 15)] : 0.f;
+  }
   for (int pass = 0; pass < D / QV; ++pass) {
-    __syncthreads();  // the previous pass's readers are done
+    if (pass) __syncthreads();  // the previous pass's readers are done
     pass_store(pr, sv);
     __syncthreads();
-    if (pass + 1 < D / QV) pass_issue(pr, ws, ch, dout, b, t0, h, T, H, (pass + 1) * QV);
+    if (pass + 1 < D / QV) {
+      pass_issue(pr, ws, ch, dout, b, t0, h, T, H, (pass + 1) * QV);
+    } else {
+      kx.issue(k, b, t0, h, T, H);
+      qx.issue(q, b, t0, h, T, H);
+      tx.issue(rec);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int y = w + 8 * (t < nP ? t : 0);
+          const int o = (16 * low_rt(y) + 4 * (l >> 4) + i) * C + 16 * low_ct(y) + (l & 15);
+          pv[t][i] = rec[C * C + o];
+          gv[t][i] = rec[2 * C * C + o];
+        }
+    }
 
     // dY . Vm per row (thread: row tid / 8, 4 columns) and <dSn, S>.
     {
@@ -825,9 +865,9 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int tok = (tr0 + t) * 16 + (l & 15);
-        const float ao = scale * gs.g[tok] * sv.dO[tok * LV + kk];
-        const float ay = -gs.bet[tok] * gs.g[tok] * sv.dY[tok * LV + kk];
-        const float au = gs.d[tok] * sv.U[tok * LV + kk];
+        const float ao = fo[t] * sv.dO[tok * LV + kk];
+        const float ay = fy[t] * sv.dY[tok * LV + kk];
+        const float au = fu[t] * sv.U[tok * LV + kk];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           aQ[t][m] = mma4(ao, bS[m], aQ[t][m]);
@@ -846,7 +886,7 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
           const int y = yT0 + 8 * t;
           const int i = 16 * low_ct(y) + (l & 15);
           const float a = sv.dU[(16 * low_rt(y) + (l & 15)) * LV + kk];
-          aT[t] = mma4(a, gs.bet[i] * sv.Vm[i * LV + kk], aT[t]);
+          aT[t] = mma4(a, fb[t] * sv.Vm[i * LV + kk], aT[t]);
         }
       }
     }
@@ -861,13 +901,9 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
   __syncthreads();  // value passes done: the LDS becomes the key-side tiles
   if ((tid & 7) == 0) dbY[tid >> 3] = dbY_acc;
 
-  load_tile<TIn, float, 512>(sk.K, LKF, k, b, t0, h, T, H);
-  load_tile<TIn, float, 512>(sk.Q, LKF, q, b, t0, h, T, H);
-  for (int i = tid; i < C * C / 4; i += 512) {
-    const int r = i / (C / 4), c4 = i % (C / 4);
-    *reinterpret_cast<f32x4*>(sk.Tm + r * LC + c4 * 4) =
-        *reinterpret_cast<const f32x4*>(rec + r * C + c4 * 4);
-  }
+  kx.store_f32(sk.K, LKF);
+  qx.store_f32(sk.Q, LKF);
+  tx.store(sk.Tm);
   // dTm, strictly lower part (the only part that reaches dA); zeros above.
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -944,8 +980,6 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
 
   // E2 = diag(beta) (G o dA) -> dT tile; H = dA o G o Gk (row sums: dbeta's
   // A part) -> M1 tile; F = dP o P + dA o A -> Ep; E1 = scale G o dP -> Tm tile.
-  const float* Pg = rec + C * C;
-  const float* Gg = rec + 2 * C * C;
   float* E2s = sk.dT;
   float* Hs = sk.M1;
   float* E1s = sk.Tm;
@@ -960,13 +994,13 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
       float e2 = 0.f, hh = 0.f, e1 = 0.f, f = 0.f;
       if (cc < r) {
         const float a = -da[t][i] * gr;  // dA_ri G_ri
-        hh = a * Gg[r * C + cc];
+        hh = a * gv[t][i];
         e2 = gs.bet[r] * a;
         f = gs.bet[r] * hh;
       }
       if (cc <= r) {
         e1 = scale * gr * aP[t][i];
-        f += aP[t][i] * Pg[r * C + cc];
+        f += aP[t][i] * pv[t][i];
       }
       st_lds(&E2s[r * LC + cc], e2);
       st_lds(&Hs[r * LC + cc], hh);
@@ -985,22 +1019,28 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
   }
   __syncthreads();
 
-  // Row sums of F and H (threads 0..63) and column sums of F (64..127).
-  if (tid < C) {
-    float fr = 0.f, hr = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < C; ++i) {
-      fr += sk.Ep[tid * LC + i];
-      hr += Hs[tid * LC + i];
+  // Row sums of F and H and column sums of F, 8 threads per row / column.
+  {
+    const int x = tid >> 3, p0 = (tid & 7) * 8;
+    float fr = 0.f, hr = 0.f, fc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      fr += sk.Ep[x * LC + p0 + e];
+      hr += Hs[x * LC + p0 + e];
+      fc += sk.Ep[(p0 + e) * LC + x];
     }
-    dgam[tid] = fr + red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-    dbA[tid] = dbY[tid] + hr;
-  } else if (tid < 2 * C) {
-    const int c = tid - C;
-    float fc = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < C; ++r) fc += sk.Ep[r * LC + c];
-    colF[c] = fc;
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      fr += __shfl_xor(fr, off);
+      hr += __shfl_xor(hr, off);
+      fc += __shfl_xor(fc, off);
+    }
+    if ((tid & 7) == 0) {
+      dgam[x] = fr + red[0][x] + red[1][x] + red[2][x] + red[3][x];
+      dbA[x] = dbY[x] + hr;
+      colF[x] = fc;
+      zrow[x] = redz[0][x] + redz[1][x] + redz[2][x] + redz[3][x];
+    }
   }
 
   // dq += E1 K; dk += E1^T Q + (E2 + E2^T) K.
@@ -1034,9 +1074,11 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
   if (w == 0) {
     const int r = C - 1 - l, t = t0 + r;
     float x = dgam[r] - colF[r];
+    float zs = zrow[l];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) zs += __shfl_xor(zs, off);
     if (r == C - 1) {
-      float zs = 0.f, ws8 = 0.f;
-      for (int i = 0; i < C; ++i) zs += redz[0][i] + redz[1][i] + redz[2][i] + redz[3][i];
+      float ws8 = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) ws8 += wsum[i];
       x += gs.gC * ws8 + zs;
