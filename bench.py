@@ -159,13 +159,13 @@ BWD_KERNELS = ("bwdc_prep_kernel + bwdc_fwd_kernel + bwdc_dstate_kernel + bwdc_g
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="d2735030a2461d9e01aa1bea23c3f5e2c211ce93",
-        fetch_kib=248635 + 73759 + 372913, write_kib=55312 + 14336 + 239617,
+        sha1="0adb6d06d71ed12add2b507a58ca6806ba269228",
+        fetch_kib=248642 + 15420 + 371933, write_kib=55306 + 14336 + 239616,
         profile=PROFILE),
     PREFILL_CONV_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="d2735030a2461d9e01aa1bea23c3f5e2c211ce93",
-        fetch_kib=313718 + 56352 + 423459, write_kib=102720 + 10240 + 258846,
+        sha1="0adb6d06d71ed12add2b507a58ca6806ba269228",
+        fetch_kib=316775 + 12856 + 423986, write_kib=102722 + 10240 + 258823,
         profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
@@ -187,8 +187,9 @@ COUNTERS = {
         fetch_kib=264783 + 394320, write_kib=395285 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd_chunk.hip",
-        sha1="0",
-        fetch_kib=0, write_kib=0, profile=PROFILE),
+        sha1="f8b2d1a94b1511aba0bc32ac2fcdb75501e20ff1",
+        fetch_kib=33368 + 51532 + 100691 + 370187, write_kib=99058 + 262144 + 335885 + 132141,
+        profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
@@ -370,6 +371,7 @@ def make_backward_leg():
 
     info = dict(B=B, T=T, H=H, d=d, tokens=B * T,
                 flops=backward_flops_per_token_head(d) * B * T * H,
+                peak_flops=PEAK_F32_MFMA_FLOPS,
                 bytes=B * T * H * (2 * 3 * d + 8 + 4 * d + 4 * (3 * d + 2)))
     return run, info
 
@@ -596,7 +598,7 @@ def main():
         rec = dict(ms_avg=avg, ms_min=min(ms), tokens_per_s=inf["tokens"] / sec)
         if "flops" in inf:
             rec["tflops"] = inf["flops"] / sec / 1e12
-            rec["mfma_frac"] = inf["flops"] / sec / PEAK_BF16_FLOPS
+            rec["mfma_frac"] = inf["flops"] / sec / inf.get("peak_flops", PEAK_BF16_FLOPS)
             rec["hbm_gbps_algorithmic"] = inf["bytes"] / sec / 1e9
             rec["hbm_frac"] = inf["bytes"] / sec / PEAK_HBM_BPS
         else:

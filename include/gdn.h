@@ -401,12 +401,16 @@ int gdn_decode_step_kgla(const void* q, const void* k, const void* v, const floa
  *   Outputs (f32, caller-owned): dq, dk [B,T,H,Dk], dv [B,T,H,Dv],
  *   dalpha, dbeta [B,T,H], dstate_in [B,H,Dk,Dv].
  *   workspace: gdn_prefill_backward_workspace_bytes(B, T, H, Dk, Dv) bytes,
- *   256-byte aligned (the forward state every 4 tokens per head and column
- *   slice, plus per-slice partial sums of dq, dk, dalpha, dbeta when
- *   Dv > 32).
- * One work-group per (b, h, slice of 32 state columns), sequential over
- * tokens, f32 arithmetic; a second kernel sums the slices' partials in a
- * fixed order, so results are deterministic.
+ *   256-byte aligned; its contents are scratch (overwritten by every call).
+ * Dk = Dv = 128 takes the chunked reverse mode (chunks of 64 tokens, every
+ * product on f32 MFMA): a per-chunk pass (gates, Gram matrices, triangular
+ * inverse), a forward pass over the chunks storing the state entering each,
+ * a reverse pass carrying the state gradient, and a per-chunk pass forming
+ * dq, dk, dalpha, dbeta; the workspace holds ~304 KiB per (b, h, chunk).
+ * Other head sizes take the token loop above directly: one work-group per
+ * (b, h, slice of 32 state columns) with the state every 4 tokens in the
+ * workspace and per-slice partials summed by a second kernel.  Both forms
+ * are f32 throughout and sum in a fixed order (deterministic results).
  * Limits: Dk and Dv in {16, 32, 64, 128}.
  */
 size_t gdn_prefill_backward_workspace_bytes(int B, int T, int H, int Dk, int Dv);
