@@ -187,7 +187,7 @@ COUNTERS = {
         fetch_kib=264783 + 394320, write_kib=395285 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd_chunk.hip",
-        sha1="f8b2d1a94b1511aba0bc32ac2fcdb75501e20ff1",
+        sha1="0d6f6e7f8c3df6b6b05c847b3fecb401391d67d1",
         fetch_kib=33368 + 51532 + 100691 + 370187, write_kib=99058 + 262144 + 335885 + 132141,
         profile=PROFILE),
     # the three projections of the leg together

@@ -114,14 +114,14 @@ __device__ __forceinline__ size_t tok_off(int b, int t, int h, int T, int H) {
 }
 
 // Rows t0 .. t0 + C - 1 of a [B, T, H, D] tensor into an LDS tile [C][ld]
-// of type TL (zeros past T), NTH threads.
-template <class TIn, class TL, int NTH = 256>
+// of type TL (zeros past T), 256 threads.
+template <class TIn, class TL>
 __device__ __forceinline__ void load_tile(TL* dst, int ld, const TIn* src, int b, int t0, int h,
                                           int T, int H) {
   typedef typename Vec16<TIn>::type vec;
   constexpr int VN = Vec16<TIn>::N;
   constexpr int VPR = D / VN;
-  for (int i = threadIdx.x; i < C * VPR; i += NTH) {
+  for (int i = threadIdx.x; i < C * VPR; i += 256) {
     const int r = i / VPR, cv = i % VPR;
     const int t = t0 + r;
     vec x;
@@ -133,17 +133,6 @@ __device__ __forceinline__ void load_tile(TL* dst, int ld, const TIn* src, int b
     }
 #pragma unroll
     for (int e = 0; e < VN; ++e) dst[r * ld + cv * VN + e] = from_f32<TL>(to_f32(x[e]));
-  }
-}
-
-// An f32 block [R][W] from global (row stride gs floats) into LDS [R][ld].
-template <int R, int W>
-__device__ __forceinline__ void load_f32(float* dst, int ld, const float* src, size_t gs) {
-  constexpr int VPR = W / 4;
-  for (int i = threadIdx.x; i < R * VPR; i += 256) {
-    const int r = i / VPR, cv = i % VPR;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(src + r * gs + cv * 4);
-    *reinterpret_cast<f32x4*>(dst + r * ld + cv * 4) = x;
   }
 }
 
@@ -439,7 +428,6 @@ __global__ __launch_bounds__(512) void bwdc_fwd_kernel(const TIn* __restrict__ k
   if (NC > 0) issue(0);
 
   for (int c = 0; c < NC; ++c) {
-    const int t0 = c * C;
     const size_t ch = (size_t)bh * NC + c;
     __syncthreads();  // the previous chunk's readers are done with LDS
     kr.store(Ks, LK);
@@ -519,7 +507,6 @@ __global__ __launch_bounds__(512) void bwdc_fwd_kernel(const TIn* __restrict__ k
 #pragma unroll
       for (int n = 0; n < NT; ++n) S[n] = mma4(a, Us[kk * LS + n * 16 + (l & 15)], S[n]);
     }
-    (void)t0;
   }
 }
 
