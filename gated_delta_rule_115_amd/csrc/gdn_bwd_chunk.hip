@@ -148,11 +148,16 @@ __global__ __launch_bounds__(256) void bwdc_prep_kernel(const TIn* __restrict__ 
                                                         float* __restrict__ rec_all) {
   typedef Mfma<TIn> M;
   constexpr int LK = D + Vec16<TIn>::N;
+  // The A matrix and the block-substitution scratch reuse the Q and K tiles'
+  // LDS once the Gram products are in registers (35 KB per work-group with
+  // bf16 inputs, so four work-groups share a CU).
   __shared__ __align__(16) TIn Ks[C * LK];
   __shared__ __align__(16) TIn Qs[C * LK];
-  __shared__ __align__(16) float Am[C * LC];
-  __shared__ __align__(16) float Xs[4][16 * 16];
   __shared__ float gam[C], bet[C];
+  static_assert(sizeof(TIn) * C * LK >= sizeof(float) * C * LC, "A fits in the Q tile");
+  static_assert(sizeof(TIn) * C * LK >= sizeof(float) * 4 * 16 * 16, "scratch fits in the K tile");
+  float* Am = reinterpret_cast<float*>(Qs);
+  float (*Xs)[16 * 16] = reinterpret_cast<float (*)[16 * 16]>(Ks);
 
   const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
   const int chunk = blockIdx.x % NC, bh = blockIdx.x / NC;
@@ -182,6 +187,7 @@ __global__ __launch_bounds__(256) void bwdc_prep_kernel(const TIn* __restrict__ 
   // Lower block triangle of K K^T (x < 10) and Q K^T (x >= 10): 20 tiles.
   float* Pg = rec + C * C;
   float* Gg = rec + 2 * C * C;
+  f32x4 accs[5];
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     const int x = wave + 4 * j;
@@ -190,10 +196,19 @@ __global__ __launch_bounds__(256) void bwdc_prep_kernel(const TIn* __restrict__ 
     const int tj = y - ti * (ti + 1) / 2;
     const TIn* Arow = (which ? Qs : Ks) + ti * 16 * LK;
     const TIn* Brow = Ks + tj * 16 * LK;
-    f32x4 acc = zero4();
+    accs[j] = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += M::KSTEP)
-      acc = M::mma(frag_k(Arow, LK, k0, D), frag_k(Brow, LK, k0, D), acc);
+      accs[j] = M::mma(frag_k(Arow, LK, k0, D), frag_k(Brow, LK, k0, D), accs[j]);
+  }
+  __syncthreads();  // K and Q tiles no longer read: their LDS takes A and the scratch
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int x = wave + 4 * j;
+    const int which = x / 10, y = x % 10;
+    const int ti = y < 1 ? 0 : y < 3 ? 1 : y < 6 ? 2 : 3;
+    const int tj = y - ti * (ti + 1) / 2;
+    const f32x4 acc = accs[j];
     const int col = tj * 16 + (l & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
