@@ -187,8 +187,8 @@ COUNTERS = {
         fetch_kib=264783 + 394320, write_kib=395285 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd_chunk.hip",
-        sha1="0d6f6e7f8c3df6b6b05c847b3fecb401391d67d1",
-        fetch_kib=33368 + 51532 + 100691 + 370187, write_kib=99058 + 262144 + 335885 + 132141,
+        sha1="daf661de2c10c59c1d4d3a3abd4ccc71ff187d41",
+        fetch_kib=33369 + 51538 + 100697 + 370193, write_kib=101661 + 262144 + 335897 + 132185,
         profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
