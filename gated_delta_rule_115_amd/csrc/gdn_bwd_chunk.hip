@@ -32,8 +32,9 @@
 //   prep     (work-group per (b, h, chunk)): gam, Tm (diagonal 16 x 16 blocks
 //            by forward substitution, the rest by block substitution), P and
 //            the key Gram matrix K K^T, to a per-chunk record;
-//   forward  (work-group per (b, h, value slice), sequential): S entering
-//            every chunk, Vm and U of every chunk;
+//   forward  (work-group per (b, h, value slice of 64 columns, 32 with f32
+//            inputs), sequential): S entering every chunk, Vm and U of every
+//            chunk;
 //   dstate   (work-group per (b, h, value slice), sequential in reverse):
 //            dSn of every chunk, dU and dY; dv, and dstate_in at the end;
 //   grads    (work-group per (b, h, chunk)): everything else, over the full
