@@ -187,7 +187,7 @@ COUNTERS = {
         fetch_kib=264783 + 394320, write_kib=395285 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd_chunk.hip",
-        sha1="daf661de2c10c59c1d4d3a3abd4ccc71ff187d41",
+        sha1="76eb7eb3a498a8418a2184466bde8005362ddcf4",
         fetch_kib=33369 + 51538 + 100697 + 370193, write_kib=101661 + 262144 + 335897 + 132185,
         profile=PROFILE),
     # the three projections of the leg together
