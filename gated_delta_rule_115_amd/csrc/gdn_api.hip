@@ -15,7 +15,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int code, const char* fmt, ...) {
+gdn_status fail(gdn_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -25,12 +25,12 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+gdn_status ok() {
   g_last_error.clear();
   return GDN_OK;
 }
 
-int hip_status(hipError_t e, const char* what) {
+gdn_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -39,7 +39,7 @@ bool is_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // dtype of the token inputs and of the output: (bf16, bf16), (bf16, f32) or
 // (f32, f32).
-int check_dtypes(int dtype, int out_dtype) {
+gdn_status check_dtypes(int dtype, int out_dtype) {
   if (dtype != GDN_BF16 && dtype != GDN_F32)
     return fail(GDN_ERR_INVALID_ARG, "dtype %d is neither GDN_BF16 nor GDN_F32", dtype);
   if (out_dtype != GDN_BF16 && out_dtype != GDN_F32)
@@ -59,7 +59,7 @@ size_t esize(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
 
 #define REQUIRE_DTYPES(dt, odt)                 \
   do {                                          \
-    const int st_ = check_dtypes((dt), (odt));  \
+    const gdn_status st_ = check_dtypes((dt), (odt));  \
     if (st_ != GDN_OK) return st_;              \
   } while (0)
 
@@ -100,10 +100,10 @@ namespace {
 // with a caller workspace and the one with the static scratch.  On success
 // returns GDN_OK, fills p (without workspace and stream) and sets *need to
 // the scratch bytes the launch uses.
-int check_prefill(const void* q, const void* k, const void* v, const float* alpha,
-                  const float* beta, const float* state_in, float* state_out, void* out,
-                  int B, int T, int H, int Dk, int Dv, int chunk, int dtype, int out_dtype,
-                  float scale, gdn::PrefillArgs* p, size_t* need) {
+gdn_status check_prefill(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* state_in, float* state_out, void* out,
+                         int B, int T, int H, int Dk, int Dv, int chunk, int dtype, int out_dtype,
+                         float scale, gdn::PrefillArgs* p, size_t* need) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG,
           "bad sizes B=%d T=%d H=%d", B, T, H);
@@ -150,7 +150,7 @@ void* scratch_addr[kMaxDevices] = {};
 
 // Device address of `scratch` on the current device (nullptr and an error
 // message on failure).
-void* scratch_on_current_device(int* status) {
+void* scratch_on_current_device(gdn_status* status) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
@@ -180,15 +180,15 @@ void* scratch_on_current_device(int* status) {
 
 extern "C" {
 
-int gdn_prefill_chunked(const void* q, const void* k, const void* v,
-                        const float* alpha, const float* beta,
-                        const float* state_in, float* state_out, void* out,
-                        int B, int T, int H, int Dk, int Dv, int chunk,
-                        int dtype, int out_dtype, float scale, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta,
+                               const float* state_in, float* state_out, void* out,
+                               int B, int T, int H, int Dk, int Dv, int chunk,
+                               int dtype, int out_dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   gdn::PrefillArgs p;
   size_t need = 0;
-  const int st = check_prefill(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk,
+  const gdn_status st = check_prefill(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk,
                                Dv, chunk, dtype, out_dtype, scale, &p, &need);
   if (st != GDN_OK) return st;
   if ((long long)B * H == 0) return ok();
@@ -203,14 +203,14 @@ int gdn_prefill_chunked(const void* q, const void* k, const void* v,
   return hip_status(gdn::launch_prefill(p), "gdn_prefill_chunked launch");
 }
 
-int gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
-                                const float* alpha, const float* beta,
-                                const float* state_in, float* state_out, void* out,
-                                int B, int T, int H, int Dk, int Dv, int chunk,
-                                int dtype, int out_dtype, float scale, void* stream) {
+gdn_status gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const float* state_in, float* state_out, void* out,
+                                       int B, int T, int H, int Dk, int Dv, int chunk,
+                                       int dtype, int out_dtype, float scale, void* stream) {
   gdn::PrefillArgs p;
   size_t need = 0;
-  int st = check_prefill(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk, Dv,
+  gdn_status st = check_prefill(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk, Dv,
                          chunk, dtype, out_dtype, scale, &p, &need);
   if (st != GDN_OK) return st;
   if ((long long)B * H == 0) return ok();
@@ -224,16 +224,16 @@ int gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
   return hip_status(gdn::launch_prefill(p), "gdn_prefill_chunked_noalloc launch");
 }
 
-int gdn_prefill_chunked_conv(const void* xq, const void* xk, const void* xv,
-                             const float* taps_q, const float* taps_k, const float* taps_v,
-                             int conv_kernel, float conv_eps, const float* alpha,
-                             const float* beta, const float* state_in, float* state_out,
-                             void* out, int B, int T, int H, int Dk, int Dv, int chunk,
-                             int dtype, int out_dtype, float scale, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+gdn_status gdn_prefill_chunked_conv(const void* xq, const void* xk, const void* xv,
+                                    const float* taps_q, const float* taps_k, const float* taps_v,
+                                    int conv_kernel, float conv_eps, const float* alpha,
+                                    const float* beta, const float* state_in, float* state_out,
+                                    void* out, int B, int T, int H, int Dk, int Dv, int chunk,
+                                    int dtype, int out_dtype, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   gdn::PrefillArgs p;
   size_t need = 0;
-  const int st = check_prefill(xq, xk, xv, alpha, beta, state_in, state_out, out, B, T, H, Dk,
+  const gdn_status st = check_prefill(xq, xk, xv, alpha, beta, state_in, state_out, out, B, T, H, Dk,
                                Dv, chunk, dtype, out_dtype, scale, &p, &need);
   if (st != GDN_OK) return st;
   REQUIRE(conv_kernel == 4, GDN_ERR_UNSUPPORTED,
@@ -259,11 +259,11 @@ int gdn_prefill_chunked_conv(const void* xq, const void* xk, const void* xv,
   return hip_status(gdn::launch_prefill(p), "gdn_prefill_chunked_conv launch");
 }
 
-int gdn_decode_step(const void* q, const void* k, const void* v,
-                    const float* alpha, const float* beta,
-                    const float* state_in, float* state_out, void* out, int B,
-                    int H, int Dk, int Dv, int dtype, int out_dtype,
-                    float scale, void* stream) {
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta,
+                           const float* state_in, float* state_out, void* out, int B,
+                           int H, int Dk, int Dv, int dtype, int out_dtype,
+                           float scale, void* stream) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d H=%d", B, H);
   REQUIRE(is_head_dim(Dk) && is_head_dim(Dv), GDN_ERR_UNSUPPORTED,
@@ -287,9 +287,9 @@ int gdn_decode_step(const void* q, const void* k, const void* v,
   return hip_status(gdn::launch_decode(p), "gdn_decode_step launch");
 }
 
-int gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
-                        int T, int Ch, int K, int l2norm_group, float eps,
-                        int dtype, int out_dtype, void* stream) {
+gdn_status gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
+                               int T, int Ch, int K, int l2norm_group, float eps,
+                               int dtype, int out_dtype, void* stream) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && T >= 0 && Ch >= 1, GDN_ERR_INVALID_ARG,
           "bad sizes B=%d T=%d Ch=%d", B, T, Ch);
@@ -318,9 +318,9 @@ int gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
   return hip_status(gdn::launch_conv(p), "gdn_short_conv_silu launch");
 }
 
-int gdn_short_conv_step(const void* x, const float* taps, void* conv_state, void* y,
-                        int B, int Ch, int K, int l2norm_group, float eps, int dtype,
-                        int out_dtype, void* stream) {
+gdn_status gdn_short_conv_step(const void* x, const float* taps, void* conv_state, void* y,
+                               int B, int Ch, int K, int l2norm_group, float eps, int dtype,
+                               int out_dtype, void* stream) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && Ch >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d Ch=%d", B, Ch);
   REQUIRE(K >= 1 && K <= 8, GDN_ERR_UNSUPPORTED, "kernel size %d not in 1..8", K);
@@ -353,11 +353,11 @@ int gdn_short_conv_step(const void* x, const float* taps, void* conv_state, void
   return hip_status(gdn::launch_conv_step(p, conv_state), "gdn_short_conv_step launch");
 }
 
-int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
-                        void* k_cache, void* v_cache, const int* n_tokens,
-                        int B, int H, int D, int n_sink, int window,
-                        float softmax_scale, int accumulate, void* out,
-                        int dtype, int out_dtype, void* stream) {
+gdn_status gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, const int* n_tokens,
+                               int B, int H, int D, int n_sink, int window,
+                               float softmax_scale, int accumulate, void* out,
+                               int dtype, int out_dtype, void* stream) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d H=%d", B, H);
   REQUIRE(D == 64 || D == 128, GDN_ERR_UNSUPPORTED, "head dim %d not in {64,128}", D);
@@ -387,9 +387,9 @@ int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
   return hip_status(gdn::launch_swa(p), "gdn_swa_sink_decode launch");
 }
 
-int gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out, int B,
-                         int T, int H, int D, int n_sink, int window, float softmax_scale,
-                         int accumulate_from, int dtype, int out_dtype, void* stream) {
+gdn_status gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out, int B,
+                                int T, int H, int D, int n_sink, int window, float softmax_scale,
+                                int accumulate_from, int dtype, int out_dtype, void* stream) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
           H);
@@ -415,8 +415,8 @@ int gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out,
   return hip_status(gdn::launch_swa_prefill(p), "gdn_swa_sink_prefill launch");
 }
 
-int gdn_swa_cache_fill(const void* k, const void* v, void* k_cache, void* v_cache, int B,
-                       int T, int H, int D, int n_sink, int window, int dtype, void* stream) {
+gdn_status gdn_swa_cache_fill(const void* k, const void* v, void* k_cache, void* v_cache, int B,
+                              int T, int H, int D, int n_sink, int window, int dtype, void* stream) {
   REQUIRE(dtype == GDN_BF16 || dtype == GDN_F32, GDN_ERR_INVALID_ARG, "bad dtype %d", dtype);
   REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
           H);
@@ -443,12 +443,12 @@ size_t gdn_hybrid_prefill_workspace_bytes(int B, int T, int H, int D, int n_sink
   return gdn::prefill_workspace_bytes(B, (int)t_lin, H, D, D, 64, true);
 }
 
-int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
-                       const float* alpha, const float* beta, const void* q_swa,
-                       const void* k_swa, const void* v_swa, float* state_out, void* out,
-                       void* k_cache, void* v_cache, int B, int T, int H, int D, int n_sink,
-                       int window, float lin_scale, float softmax_scale, int dtype,
-                       int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+gdn_status gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
+                              const float* alpha, const float* beta, const void* q_swa,
+                              const void* k_swa, const void* v_swa, float* state_out, void* out,
+                              void* k_cache, void* v_cache, int B, int T, int H, int D, int n_sink,
+                              int window, float lin_scale, float softmax_scale, int dtype,
+                              int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
           H);
@@ -507,7 +507,7 @@ int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
     p.B = B; p.T = (int)n; p.H = H; p.Dk = D; p.Dv = D; p.chunk = 64;
     p.bf16 = true; p.out_bf16 = out_dtype == GDN_BF16; p.scale = lin_scale;
     p.workspace = workspace; p.stream = stream; p.seq_stride = T;
-    const int st = hip_status(gdn::launch_prefill(p), "gdn_hybrid_prefill linear path");
+    const gdn_status st = hip_status(gdn::launch_prefill(p), "gdn_hybrid_prefill linear path");
     if (st != GDN_OK) return st;
   }
   if (T > 0) {
@@ -516,7 +516,7 @@ int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
     p.B = B; p.T = T; p.H = H; p.n_sink = n_sink; p.window = window;
     p.acc_from = t_lin > 0 ? n_sink + window : T;
     p.softmax_scale = softmax_scale; p.out_bf16 = out_dtype == GDN_BF16; p.stream = stream;
-    const int st = hip_status(gdn::launch_swa_prefill(p), "gdn_hybrid_prefill softmax path");
+    const gdn_status st = hip_status(gdn::launch_swa_prefill(p), "gdn_hybrid_prefill softmax path");
     if (st != GDN_OK) return st;
   }
   if (k_cache != nullptr && T > 0) {
@@ -539,11 +539,11 @@ size_t gdn_prefill_chgate_workspace_bytes(int B, int T, int H) {
 namespace {
 
 // The channel-gate prefill and decode step, and kGLA on the same kernels.
-int prefill_chgate_call(const void* q, const void* k, const void* v, const float* alpha,
-                        const float* beta, const float* state_in, float* state_out, void* out,
-                        int B, int T, int H, int Dk, int Dv, int dtype, int out_dtype,
-                        float scale, void* workspace, size_t workspace_bytes, void* stream,
-                        bool kgla, const char* name) {
+gdn_status prefill_chgate_call(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* state_in, float* state_out, void* out,
+                               int B, int T, int H, int Dk, int Dv, int dtype, int out_dtype,
+                               float scale, void* workspace, size_t workspace_bytes, void* stream,
+                               bool kgla, const char* name) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
           H);
@@ -577,10 +577,10 @@ int prefill_chgate_call(const void* q, const void* k, const void* v, const float
   return hip_status(gdn::launch_prefill_chgate(p), name);
 }
 
-int decode_chgate_call(const void* q, const void* k, const void* v, const float* alpha,
-                       const float* beta, const float* state_in, float* state_out, void* out,
-                       int B, int H, int Dk, int Dv, int dtype, int out_dtype, float scale,
-                       void* stream, bool kgla, const char* name) {
+gdn_status decode_chgate_call(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const float* state_in, float* state_out, void* out,
+                              int B, int H, int Dk, int Dv, int dtype, int out_dtype, float scale,
+                              void* stream, bool kgla, const char* name) {
   REQUIRE_DTYPES(dtype, out_dtype);
   REQUIRE(B >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d H=%d", B, H);
   REQUIRE(is_head_dim(Dk) && is_head_dim(Dv), GDN_ERR_UNSUPPORTED,
@@ -607,38 +607,38 @@ int decode_chgate_call(const void* q, const void* k, const void* v, const float*
 
 extern "C" {
 
-int gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
-                               const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
-                               int dtype, int out_dtype, float scale, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+gdn_status gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta, const float* state_in,
+                                      float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
+                                      int dtype, int out_dtype, float scale, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   return prefill_chgate_call(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk, Dv,
                              dtype, out_dtype, scale, workspace, workspace_bytes, stream, false,
                              "gdn_prefill_chunked_chgate launch");
 }
 
-int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* state_in, float* state_out,
-                           void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
-                           float scale, void* stream) {
+gdn_status gdn_decode_step_chgate(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* state_in, float* state_out,
+                                  void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
+                                  float scale, void* stream) {
   return decode_chgate_call(q, k, v, alpha, beta, state_in, state_out, out, B, H, Dk, Dv, dtype,
                             out_dtype, scale, stream, false, "gdn_decode_step_chgate launch");
 }
 
-int gdn_prefill_chunked_kgla(const void* q, const void* k, const void* v,
-                             const float* alpha, const float* beta, const float* state_in,
-                             float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
-                             int dtype, int out_dtype, float scale, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+gdn_status gdn_prefill_chunked_kgla(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta, const float* state_in,
+                                    float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
+                                    int dtype, int out_dtype, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   return prefill_chgate_call(q, k, v, alpha, beta, state_in, state_out, out, B, T, H, Dk, Dv,
                              dtype, out_dtype, scale, workspace, workspace_bytes, stream, true,
                              "gdn_prefill_chunked_kgla launch");
 }
 
-int gdn_decode_step_kgla(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, const float* state_in, float* state_out, void* out,
-                         int B, int H, int Dk, int Dv, int dtype, int out_dtype, float scale,
-                         void* stream) {
+gdn_status gdn_decode_step_kgla(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* state_in, float* state_out, void* out,
+                                int B, int H, int Dk, int Dv, int dtype, int out_dtype, float scale,
+                                void* stream) {
   return decode_chgate_call(q, k, v, alpha, beta, state_in, state_out, out, B, H, Dk, Dv, dtype,
                             out_dtype, scale, stream, true, "gdn_decode_step_kgla launch");
 }
@@ -648,12 +648,12 @@ size_t gdn_prefill_backward_workspace_bytes(int B, int T, int H, int Dk, int Dv)
   return gdn::backward_workspace_bytes(B, T, H, Dk, Dv);
 }
 
-int gdn_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, const float* state_in, const float* dout,
-                         const float* dstate_out, float* dq, float* dk, float* dv,
-                         float* dalpha, float* dbeta, float* dstate_in, int B, int T, int H,
-                         int Dk, int Dv, int dtype, float scale, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+gdn_status gdn_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* state_in, const float* dout,
+                                const float* dstate_out, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* dstate_in, int B, int T, int H,
+                                int Dk, int Dv, int dtype, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   REQUIRE(dtype == GDN_BF16 || dtype == GDN_F32, GDN_ERR_INVALID_ARG, "bad dtype %d", dtype);
   REQUIRE(B >= 0 && T >= 0 && H >= 1, GDN_ERR_INVALID_ARG, "bad sizes B=%d T=%d H=%d", B, T,
           H);

@@ -106,12 +106,12 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int Dk, int Dv,
  * copies state_in (or zeros) to state_out.  alpha must be > 0 (the kernels
  * work with log alpha).
  */
-int gdn_prefill_chunked(const void* q, const void* k, const void* v,
-                        const float* alpha, const float* beta,
-                        const float* state_in, float* state_out, void* out,
-                        int B, int T, int H, int Dk, int Dv, int chunk,
-                        int dtype, int out_dtype, float scale, void* workspace,
-                        size_t workspace_bytes, void* stream);
+gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta,
+                               const float* state_in, float* state_out, void* out,
+                               int B, int T, int H, int Dk, int Dv, int chunk,
+                               int dtype, int out_dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * gdn_prefill_chunked without a workspace argument, for callers that cannot
@@ -132,12 +132,12 @@ int gdn_prefill_chunked(const void* q, const void* k, const void* v,
  *     wrong results; order them on one stream.
  */
 #define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
-int gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
-                                const float* alpha, const float* beta,
-                                const float* state_in, float* state_out,
-                                void* out, int B, int T, int H, int Dk, int Dv,
-                                int chunk, int dtype, int out_dtype, float scale,
-                                void* stream);
+gdn_status gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const float* state_in, float* state_out,
+                                       void* out, int B, int T, int H, int Dk, int Dv,
+                                       int chunk, int dtype, int out_dtype, float scale,
+                                       void* stream);
 
 /*
  * gdn_prefill_chunked on the raw q, k, v projections, with the projection
@@ -162,15 +162,15 @@ int gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
  * normalised, so the f16 operand range holds for them; v's SiLU output must
  * stay below 65504 in magnitude, as gdn_prefill_chunked's v.
  */
-int gdn_prefill_chunked_conv(const void* xq, const void* xk, const void* xv,
-                             const float* taps_q, const float* taps_k,
-                             const float* taps_v, int conv_kernel,
-                             float conv_eps, const float* alpha,
-                             const float* beta, const float* state_in,
-                             float* state_out, void* out, int B, int T, int H,
-                             int Dk, int Dv, int chunk, int dtype,
-                             int out_dtype, float scale, void* workspace,
-                             size_t workspace_bytes, void* stream);
+gdn_status gdn_prefill_chunked_conv(const void* xq, const void* xk, const void* xv,
+                                    const float* taps_q, const float* taps_k,
+                                    const float* taps_v, int conv_kernel,
+                                    float conv_eps, const float* alpha,
+                                    const float* beta, const float* state_in,
+                                    float* state_out, void* out, int B, int T, int H,
+                                    int Dk, int Dv, int chunk, int dtype,
+                                    int out_dtype, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * One recurrence step for a batch of sequences (section 3.1.2 at a single
@@ -180,11 +180,11 @@ int gdn_prefill_chunked_conv(const void* xq, const void* xk, const void* xv,
  *   out [B, H, Dv] out_dtype:   out = scale * S'^T q
  * Each state is read once and written once.  Limits as for the prefill.
  */
-int gdn_decode_step(const void* q, const void* k, const void* v,
-                    const float* alpha, const float* beta,
-                    const float* state_in, float* state_out, void* out, int B,
-                    int H, int Dk, int Dv, int dtype, int out_dtype,
-                    float scale, void* stream);
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta,
+                           const float* state_in, float* state_out, void* out, int B,
+                           int H, int Dk, int Dv, int dtype, int out_dtype,
+                           float scale, void* stream);
 
 /*
  * Causal depthwise short convolution + SiLU on one projection output
@@ -197,9 +197,9 @@ int gdn_decode_step(const void* q, const void* k, const void* v,
  * Limits: K in 1..8; Ch a multiple of 8; l2norm_group 0 (off) or a power of
  * two in 8..512 dividing Ch.  y must not overlap x.
  */
-int gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
-                        int T, int Ch, int K, int l2norm_group, float eps,
-                        int dtype, int out_dtype, void* stream);
+gdn_status gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
+                               int T, int Ch, int K, int l2norm_group, float eps,
+                               int dtype, int out_dtype, void* stream);
 
 /*
  * One decode step of the same short convolution (section 4, "Adapting
@@ -218,9 +218,9 @@ int gdn_short_conv_silu(const void* x, const float* taps, void* y, int B,
  *   y          [B, Ch] out_dtype
  * Limits as gdn_short_conv_silu.  x, y and conv_state must not overlap.
  */
-int gdn_short_conv_step(const void* x, const float* taps, void* conv_state,
-                        void* y, int B, int Ch, int K, int l2norm_group,
-                        float eps, int dtype, int out_dtype, void* stream);
+gdn_status gdn_short_conv_step(const void* x, const float* taps, void* conv_state,
+                               void* y, int B, int Ch, int K, int l2norm_group,
+                               float eps, int dtype, int out_dtype, void* stream);
 
 /*
  * Softmax decode step over sink tokens and a sliding window (section 4,
@@ -243,11 +243,11 @@ int gdn_short_conv_step(const void* x, const float* taps, void* conv_state,
  *   out      [B, H, D] out_dtype.
  * Limits: D in {64, 128}; n_sink >= 0; window >= 1.
  */
-int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
-                        void* k_cache, void* v_cache, const int* n_tokens,
-                        int B, int H, int D, int n_sink, int window,
-                        float softmax_scale, int accumulate, void* out,
-                        int dtype, int out_dtype, void* stream);
+gdn_status gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, const int* n_tokens,
+                               int B, int H, int D, int n_sink, int window,
+                               float softmax_scale, int accumulate, void* out,
+                               int dtype, int out_dtype, void* stream);
 
 /*
  * Softmax over sink tokens and a sliding window at every position of a
@@ -261,9 +261,9 @@ int gdn_swa_sink_decode(const void* q, const void* k_new, const void* v_new,
  * Limits: dtype GDN_BF16 and D = 128 (else GDN_ERR_UNSUPPORTED); n_sink >= 0;
  * window >= 1; softmax_scale > 0 and finite.  out must not overlap q, k or v.
  */
-int gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out, int B,
-                         int T, int H, int D, int n_sink, int window, float softmax_scale,
-                         int accumulate_from, int dtype, int out_dtype, void* stream);
+gdn_status gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out, int B,
+                                int T, int H, int D, int n_sink, int window, float softmax_scale,
+                                int accumulate_from, int dtype, int out_dtype, void* stream);
 
 /*
  * Fill the decode-time KV cache of gdn_swa_sink_decode from a sequence's
@@ -276,8 +276,8 @@ int gdn_swa_sink_prefill(const void* q, const void* k, const void* v, void* out,
  * After it, gdn_swa_sink_decode with n_tokens = T + 1 attends the right set.
  * Limits: D in {64, 128}; n_sink >= 0; window >= 1.
  */
-int gdn_swa_cache_fill(const void* k, const void* v, void* k_cache, void* v_cache, int B,
-                       int T, int H, int D, int n_sink, int window, int dtype, void* stream);
+gdn_status gdn_swa_cache_fill(const void* k, const void* v, void* k_cache, void* v_cache, int B,
+                              int T, int H, int D, int n_sink, int window, int dtype, void* stream);
 
 /*
  * Workspace (bytes) that gdn_hybrid_prefill needs for these sizes (0 = none;
@@ -314,12 +314,12 @@ size_t gdn_hybrid_prefill_workspace_bytes(int B, int T, int H, int D, int n_sink
  * GDN_BF16 and D = 128 (else GDN_ERR_UNSUPPORTED).  No output may overlap
  * an input.
  */
-int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
-                       const float* alpha, const float* beta, const void* q_swa,
-                       const void* k_swa, const void* v_swa, float* state_out, void* out,
-                       void* k_cache, void* v_cache, int B, int T, int H, int D, int n_sink,
-                       int window, float lin_scale, float softmax_scale, int dtype,
-                       int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+gdn_status gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
+                              const float* alpha, const float* beta, const void* q_swa,
+                              const void* k_swa, const void* v_swa, float* state_out, void* out,
+                              void* k_cache, void* v_cache, int B, int T, int H, int D, int n_sink,
+                              int window, float lin_scale, float softmax_scale, int dtype,
+                              int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Channel-wise gate (section 3.2's diagonal gates prod_j diag(alpha_j) in
@@ -340,15 +340,15 @@ int gdn_hybrid_prefill(const void* q_lin, const void* k_lin, const void* v_lin,
  *   [B, H, Dk] f32.  Limits as gdn_decode_step.
  */
 size_t gdn_prefill_chgate_workspace_bytes(int B, int T, int H);
-int gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
-                               const float* alpha, const float* beta, const float* state_in,
-                               float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
-                               int dtype, int out_dtype, float scale, void* workspace,
-                               size_t workspace_bytes, void* stream);
-int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* state_in, float* state_out,
-                           void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
-                           float scale, void* stream);
+gdn_status gdn_prefill_chunked_chgate(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta, const float* state_in,
+                                      float* state_out, void* out, int B, int T, int H, int Dk, int Dv,
+                                      int dtype, int out_dtype, float scale, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+gdn_status gdn_decode_step_chgate(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* state_in, float* state_out,
+                                  void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
+                                  float scale, void* stream);
 
 /*
  * Gated linear attention with a key-dependent gate (kGLA, section 3.2.2,
@@ -365,12 +365,12 @@ int gdn_decode_step_chgate(const void* q, const void* k, const void* v, const fl
  * and beta k[c]^2 < 1 for every channel (the kernels work with the log of
  * the gate, which must be positive).
  */
-int gdn_prefill_chunked_kgla(const void* q, const void* k, const void* v,
-                             const float* alpha, const float* beta,
-                             const float* state_in, float* state_out, void* out,
-                             int B, int T, int H, int Dk, int Dv, int dtype,
-                             int out_dtype, float scale, void* workspace,
-                             size_t workspace_bytes, void* stream);
+gdn_status gdn_prefill_chunked_kgla(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta,
+                                    const float* state_in, float* state_out, void* out,
+                                    int B, int T, int H, int Dk, int Dv, int dtype,
+                                    int out_dtype, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * One kGLA step per (b, h) (section 3.2.2 at a single token):
@@ -379,10 +379,10 @@ int gdn_prefill_chunked_kgla(const void* q, const void* k, const void* v,
  * gdn_decode_step_chgate (may alias).  No precondition on the gate's sign:
  * the step multiplies by it directly.
  */
-int gdn_decode_step_kgla(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, const float* state_in, float* state_out,
-                         void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
-                         float scale, void* stream);
+gdn_status gdn_decode_step_kgla(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* state_in, float* state_out,
+                                void* out, int B, int H, int Dk, int Dv, int dtype, int out_dtype,
+                                float scale, void* stream);
 
 /*
  * Backward pass of gdn_prefill_chunked (scalar gate; section 3.1.2 update,
@@ -414,12 +414,12 @@ int gdn_decode_step_kgla(const void* q, const void* k, const void* v, const floa
  * Limits: Dk and Dv in {16, 32, 64, 128}.
  */
 size_t gdn_prefill_backward_workspace_bytes(int B, int T, int H, int Dk, int Dv);
-int gdn_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, const float* state_in, const float* dout,
-                         const float* dstate_out, float* dq, float* dk, float* dv,
-                         float* dalpha, float* dbeta, float* dstate_in, int B, int T, int H,
-                         int Dk, int Dv, int dtype, float scale, void* workspace,
-                         size_t workspace_bytes, void* stream);
+gdn_status gdn_prefill_backward(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* state_in, const float* dout,
+                                const float* dstate_out, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* dstate_in, int B, int T, int H,
+                                int Dk, int Dv, int dtype, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }
