@@ -88,12 +88,29 @@ __global__ __launch_bounds__(PNT, 2) void swa_sink_prefill_kernel(
   const size_t base = ((size_t)b * T * H + h) * PD;
 
   // Key blocks: the sink blocks below the first window block, then every
-  // block from the earliest window start to the last query.
+  // block from the earliest window start to the last query.  The window
+  // blocks are visited in the order of their index modulo npd, the most
+  // window blocks a work-group can have: the work-groups of one (b, h) start
+  // together and move one block per step, so at step j all of them read the
+  // blocks congruent to j -- a block's five or so readers fetch it at about
+  // the same time and its later reads hit in L2.  (In index order, each
+  // work-group would read a different block at every step and the whole
+  // sequence's K and V would be live in L2 at once.)  The softmax is the
+  // same in any order.
   const int kb_lo = max(0, t0 - window + 1) / PK;
   const int kb_hi = (min(T, t0 + PQ) - 1) / PK;
   const int nsb = min((n_sink + PK - 1) / PK, kb_lo);
-  const int nblk = nsb + (kb_hi - kb_lo + 1);
-  auto blk = [&](int i) { return i < nsb ? i : kb_lo + (i - nsb); };
+  const int nwin = kb_hi - kb_lo + 1;
+  const int nblk = nsb + nwin;
+  const int npd = PQ / PK + (window - 1 + PK - 1) / PK;
+  int rot = (npd - kb_lo % npd) % npd;  // position of the first block congruent to 0
+  if (rot >= nwin) rot = 0;
+  auto blk = [&](int i) {
+    if (i < nsb) return i;
+    int j = i - nsb + rot;
+    if (j >= nwin) j -= nwin;
+    return kb_lo + j;
+  };
 
   // Q^T operand of this wave (query r, dims 32 j + 8 g .. + 7).
   bf16x8 qf[4];
