@@ -1402,7 +1402,10 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
 // (inline asm, 24 loads per lane, two register slots) before the current
 // product, and each step's result is written with 8 vector stores (inline
 // asm): at the end of a step the loads are complete once at most those 8
-// stores are outstanding, so no wait covers a store.
+// stores are outstanding, so no wait covers a store.  When the grid has more
+// work-groups than fit two per CU, nothing is prefetched: one register slot
+// keeps the kernel under 128 VGPRs, so four work-groups fit per CU and the
+// grid runs in one round (each step then waits for its own loads).
 __device__ __forceinline__ void cb_ld4(f32x4& r, const float* p) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
 }
@@ -1429,6 +1432,7 @@ __device__ __forceinline__ void cb_wait(CombLoads& x) {
                : "memory");
 }
 
+template <bool PF>
 __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
   __shared__ __align__(16) float St[16][HD + 4];  // S slice transposed: [column][key]
   // The 8 slices of a head on one XCD (when the head count is a multiple of
@@ -1457,13 +1461,13 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
         cb_ld1(x.b[t][i], Bs + (size_t)(16 * (2 * w + t) + 4 * lq + i) * HD + col0 + lr);
     }
   };
-  CombLoads ld[2];
+  CombLoads ld[PF ? 2 : 1];
   issue(ld[0], 1);
   cb_wait<0>(ld[0]);  // also covers the compiler's loads of S_1 above
   lds_barrier();
   auto step = [&](int sg, auto Par) {
     constexpr int p = decltype(Par)::value;  // (sg - 1) & 1
-    issue(ld[p ^ 1], sg + 1);
+    if constexpr (PF) issue(ld[p ^ 1], sg + 1);
     f32x4 acc[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -1489,17 +1493,27 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
       for (int i = 0; i < 4; ++i) cb_st1(dst + (size_t)(r0 + i) * HD + col0 + lr, a[i]);
     }
     lds_barrier();
-    cb_wait<8>(ld[p ^ 1]);
+    if constexpr (PF) cb_wait<8>(ld[p ^ 1]);
   };
-  int sg = 1;
-  for (; sg + 1 <= last; sg += 2) {
-    step(sg, ic<0>());
-    step(sg + 1, ic<1>());
+  if constexpr (PF) {
+    int sg = 1;
+    for (; sg + 1 <= last; sg += 2) {
+      step(sg, ic<0>());
+      step(sg + 1, ic<1>());
+    }
+    if (sg <= last) step(sg, ic<0>());
+  } else {
+    for (int sg = 1; sg <= last; ++sg) {
+      if (sg > 1) {
+        issue(ld[0], sg);
+        cb_wait<0>(ld[0]);
+      }
+      step(sg, ic<0>());
+    }
   }
-  if (sg <= last) step(sg, ic<0>());
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last stores
   cb_wait<0>(ld[0]);
-  cb_wait<0>(ld[1]);
+  if constexpr (PF) cb_wait<0>(ld[1]);
 }
 
 }  // namespace
@@ -1571,8 +1585,12 @@ static hipError_t launch_head_t(const PrefillArgs& p) {
     hipLaunchKernelGGL((prefill_lead_kernel<TOut, CV>), dim3(BH * (g.P - 1)), dim3(HNT), 0, st, q,
                        k, v, p.alpha, p.beta, p.state_in, (TOut*)p.out, ws, g, p.T, TS, p.H,
                        p.scale, ct);
-    if (g.P > 2)
-      hipLaunchKernelGGL(segment_combine_kernel, dim3(BH * 8), dim3(256), 0, st, ws, g.P);
+    if (g.P > 2) {
+      if (BH * 8 <= 2 * kCUs)
+        hipLaunchKernelGGL(segment_combine_kernel<true>, dim3(BH * 8), dim3(256), 0, st, ws, g.P);
+      else
+        hipLaunchKernelGGL(segment_combine_kernel<false>, dim3(BH * 8), dim3(256), 0, st, ws, g.P);
+    }
     s_first = 1;
   }
   hipLaunchKernelGGL((prefill_out_kernel<TOut, CV>), dim3(BH * (g.P - s_first)), dim3(HNT), 0, st,

@@ -37,7 +37,7 @@ def test_per_head_kernels_have_no_inflight_hazard(asm):
     names = [k for k in kernels(asm) if "prefill_" in k]
     assert len(names) == 8  # lead and output kernels x {bf16, f32 out} x {fused conv, not}
     names += [k for k in kernels(asm) if "segment_combine_kernel" in k]
-    assert len(names) == 9
+    assert len(names) == 10  # + the combine with and without prefetch
     for k in names:
         rep = check_kernel(asm, k)
         assert rep == [], (k, rep[:5])

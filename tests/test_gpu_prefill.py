@@ -104,6 +104,7 @@ def test_bf16_dk128_prefill_matches_oracle(B, T, H, Dv, state0):
     (2, 2048 + 5, 1, "randn", 1),   # 4 segments, short ragged last one
     (1, 1536, 2, "randn", 3),       # steeper gates: some chunks take the wide path
     (1, 1536, 2, "randn", 8),       # most chunks wide
+    (1, 2048, 72, "randn", 1),      # 4 segments over 72 heads: the combine pass without prefetch
 ])
 def test_segmented_prefill_matches_oracle(B, T, H, state0, gate_pow):
     """bf16, Dk = Dv = 128, chunk 64 and few heads: the sequence is split into
