@@ -1393,19 +1393,21 @@ __global__ __launch_bounds__(HNT) void prefill_out_kernel(
 
 // Initial states of segments 2 .. P - 1: from S_1 (left in the workspace by
 // the output pass of segment 0), S_{s+1} = M_s S_s + B_s, in f32.  One
-// work-group of 4 waves per (head, 16-column slice); wave w forms row tiles
-// 2 w, 2 w + 1 (16 rows each) of every step with v_mfma_f32_16x16x4_f32: in
-// the 16-key block jj, product i takes key 16 jj + 4 q + i in lane group q,
-// so each lane reads its 4 keys of M with one 16-byte load and S (kept
-// transposed in LDS) with one 16-byte read; each row tile accumulates in two
-// chains (even and odd key blocks).  The next segment's M and B are requested
-// (inline asm, 24 loads per lane, two register slots) before the current
-// product, and each step's result is written with 8 vector stores (inline
-// asm): at the end of a step the loads are complete once at most those 8
-// stores are outstanding, so no wait covers a store.  When the grid has more
-// work-groups than fit two per CU, nothing is prefetched: one register slot
-// keeps the kernel under 128 VGPRs, so four work-groups fit per CU and the
-// grid runs in one round (each step then waits for its own loads).
+// work-group per (head, 16-column slice); wave w forms RT row tiles (16 rows
+// each, tiles RT w .. RT w + RT - 1) of every step with
+// v_mfma_f32_16x16x4_f32: in the 16-key block jj, product i takes key 16 jj
+// + 4 q + i in lane group q, so each lane reads its 4 keys of M with one
+// 16-byte load and S (kept transposed in LDS) with one 16-byte read; each
+// row tile accumulates in two chains (even and odd key blocks).
+//   - PF (the grid fits two work-groups per CU): 8 waves, one row tile each;
+//     the next segment's M and B are requested (inline asm, 12 loads per
+//     lane, two register slots) before the current product, and each step's
+//     result is written with 4 vector stores (inline asm): at the end of a
+//     step the loads are complete once at most those 4 stores are
+//     outstanding, so no wait covers a store.
+//   - otherwise: 4 waves, two row tiles each, one register slot (under 128
+//     VGPRs, so four work-groups fit per CU and the grid runs in one round);
+//     each step waits for its own loads.
 __device__ __forceinline__ void cb_ld4(f32x4& r, const float* p) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
 }
@@ -1415,12 +1417,22 @@ __device__ __forceinline__ void cb_ld1(float& r, const float* p) {
 __device__ __forceinline__ void cb_st1(float* p, float v) {
   asm volatile("global_store_dword %0, %1, off" : : "v"(p), "v"(v) : "memory");
 }
+template <int RT>
 struct CombLoads {
-  f32x4 m[2][8];  // M rows 16 (2 w + t) + lr, keys 16 jj + 4 lq .. + 3
-  float b[2][4];  // B in accumulator layout: rows 16 (2 w + t) + 4 lq + i, column lr
+  f32x4 m[RT][8];  // M rows 16 (RT w + t) + lr, keys 16 jj + 4 lq .. + 3
+  float b[RT][4];  // B in accumulator layout: rows 16 (RT w + t) + 4 lq + i, column lr
 };
 template <int N>
-__device__ __forceinline__ void cb_wait(CombLoads& x) {
+__device__ __forceinline__ void cb_wait(CombLoads<1>& x) {
+  asm volatile("s_waitcnt vmcnt(%12)"
+               : "+v"(x.m[0][0]), "+v"(x.m[0][1]), "+v"(x.m[0][2]), "+v"(x.m[0][3]),
+                 "+v"(x.m[0][4]), "+v"(x.m[0][5]), "+v"(x.m[0][6]), "+v"(x.m[0][7]),
+                 "+v"(x.b[0][0]), "+v"(x.b[0][1]), "+v"(x.b[0][2]), "+v"(x.b[0][3])
+               : "n"(N)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void cb_wait(CombLoads<2>& x) {
   asm volatile("s_waitcnt vmcnt(%24)"
                : "+v"(x.m[0][0]), "+v"(x.m[0][1]), "+v"(x.m[0][2]), "+v"(x.m[0][3]),
                  "+v"(x.m[0][4]), "+v"(x.m[0][5]), "+v"(x.m[0][6]), "+v"(x.m[0][7]),
@@ -1433,7 +1445,9 @@ __device__ __forceinline__ void cb_wait(CombLoads& x) {
 }
 
 template <bool PF>
-__global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
+__global__ __launch_bounds__(PF ? 512 : 256) void segment_combine_kernel(SegWs ws, int P) {
+  constexpr int RT = PF ? 1 : 2;   // row tiles per wave
+  constexpr int NT = 64 * 8 / RT;  // threads
   __shared__ __align__(16) float St[16][HD + 4];  // S slice transposed: [column][key]
   // The 8 slices of a head on one XCD (when the head count is a multiple of
   // 8), so M_s comes from HBM into one L2 once and is read from there 8 times.
@@ -1442,35 +1456,35 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
   const int col0 = 16 * sl;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
   const float* s1 = ws.S + ws.at(bh, 0, P);
-  for (int i = tid; i < HD * 16; i += 256) {
+  for (int i = tid; i < HD * 16; i += NT) {
     const int r = i >> 4, c = i & 15;
     St[c][r] = s1[r * HD + col0 + c];
   }
   const int last = P - 2;  // steps sg = 1 .. last
-  auto issue = [&](CombLoads& x, int sg) {
+  auto issue = [&](CombLoads<RT>& x, int sg) {
     sg = min(sg, last);
     const float* M = ws.M + ws.at(bh, sg, P);
     const float* Bs = ws.B + ws.at(bh, sg, P);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = 16 * (2 * w + t) + lr;
+    for (int t = 0; t < RT; ++t) {
+      const int row = 16 * (RT * w + t) + lr;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) cb_ld4(x.m[t][jj], M + (size_t)row * HD + 16 * jj + 4 * lq);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        cb_ld1(x.b[t][i], Bs + (size_t)(16 * (2 * w + t) + 4 * lq + i) * HD + col0 + lr);
+        cb_ld1(x.b[t][i], Bs + (size_t)(16 * (RT * w + t) + 4 * lq + i) * HD + col0 + lr);
     }
   };
-  CombLoads ld[PF ? 2 : 1];
+  CombLoads<RT> ld[PF ? 2 : 1];
   issue(ld[0], 1);
   cb_wait<0>(ld[0]);  // also covers the compiler's loads of S_1 above
   lds_barrier();
   auto step = [&](int sg, auto Par) {
     constexpr int p = decltype(Par)::value;  // (sg - 1) & 1
     if constexpr (PF) issue(ld[p ^ 1], sg + 1);
-    f32x4 acc[2][2];
+    f32x4 acc[RT][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < RT; ++t) {
       acc[t][0] = f32x4{ld[p].b[t][0], ld[p].b[t][1], ld[p].b[t][2], ld[p].b[t][3]};
       acc[t][1] = zero4();
 #pragma unroll
@@ -1485,15 +1499,15 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(SegWs ws, int P) {
     lds_barrier();  // every wave has read St
     float* dst = ws.S + ws.at(bh, sg, P);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < RT; ++t) {
       const f32x4 a = acc[t][0] + acc[t][1];
-      const int r0 = 16 * (2 * w + t) + 4 * lq;
+      const int r0 = 16 * (RT * w + t) + 4 * lq;
       *reinterpret_cast<f32x4*>(&St[lr][r0]) = a;
 #pragma unroll
       for (int i = 0; i < 4; ++i) cb_st1(dst + (size_t)(r0 + i) * HD + col0 + lr, a[i]);
     }
     lds_barrier();
-    if constexpr (PF) cb_wait<8>(ld[p ^ 1]);
+    if constexpr (PF) cb_wait<4 * RT>(ld[p ^ 1]);
   };
   if constexpr (PF) {
     int sg = 1;
@@ -1587,7 +1601,7 @@ static hipError_t launch_head_t(const PrefillArgs& p) {
                        p.scale, ct);
     if (g.P > 2) {
       if (BH * 8 <= 2 * kCUs)
-        hipLaunchKernelGGL(segment_combine_kernel<true>, dim3(BH * 8), dim3(256), 0, st, ws, g.P);
+        hipLaunchKernelGGL(segment_combine_kernel<true>, dim3(BH * 8), dim3(512), 0, st, ws, g.P);
       else
         hipLaunchKernelGGL(segment_combine_kernel<false>, dim3(BH * 8), dim3(256), 0, st, ws, g.P);
     }
