@@ -159,18 +159,18 @@ BWD_KERNELS = ("bwdc_prep_kernel + bwdc_fwd_kernel + bwdc_dstate_kernel + bwdc_g
 COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="0adb6d06d71ed12add2b507a58ca6806ba269228",
-        fetch_kib=248642 + 15420 + 371933, write_kib=55306 + 14336 + 239616,
+        sha1="7d272a8c4a3e61df3fc2b8b4e2b998427123eb32",
+        fetch_kib=248678 + 15389 + 371487, write_kib=55318 + 14336 + 239616,
         profile=PROFILE),
     PREFILL_CONV_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
-        sha1="0adb6d06d71ed12add2b507a58ca6806ba269228",
-        fetch_kib=316775 + 12856 + 423986, write_kib=102722 + 10240 + 258823,
+        sha1="7d272a8c4a3e61df3fc2b8b4e2b998427123eb32",
+        fetch_kib=318844 + 12834 + 424178, write_kib=102722 + 10240 + 258828,
         profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
         sha1="d0e70d0a01d4633fac0a955eda54f3bd69f01b62",
-        fetch_kib=265758, write_kib=526634, profile=PROFILE),
+        fetch_kib=265757, write_kib=526665, profile=PROFILE),
     "swa_sink_decode_kernel<bf16,bf16,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa.hip",
         sha1="afa1a0eccd2a4fdf0d91fdc379ee91e97784c24f",
@@ -178,8 +178,8 @@ COUNTERS = {
     # mean of the three launches of the counter run (same inputs)
     "swa_sink_prefill_kernel<bf16>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa_prefill.hip",
-        sha1="22b363dac7d447a545132a0e123c8b66d2eff229",
-        fetch_kib=(444899 + 441849 + 439651) / 3, write_kib=(133848 + 133726 + 133661) / 3,
+        sha1="574a282283f29c6e63b6756b722bf61d901a095e",
+        fetch_kib=(254812 + 254878 + 255096) / 3, write_kib=(131860 + 132186 + 132122) / 3,
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
