@@ -248,19 +248,24 @@ __global__ __launch_bounds__(PNT, 2) void swa_sink_prefill_kernel(
 // Decode-cache fill from a sequence's keys and values: slot j < n_sink holds
 // position j, the position p >= n_sink lives in slot n_sink + (p - n_sink) %
 // window; after T tokens the cache holds the sinks and the last `window`
-// non-sink positions.  One work-group per (b, h); 16 lanes per row.
+// non-sink positions.  kFillParts work-groups per (b, h), each taking every
+// kFillParts-th 256-piece stretch of its rows (one work-group per (b, h)
+// left half of the CUs idle at B4 H32); 16-byte pieces, D / 8 or D / 4 per
+// row.
+constexpr int kFillParts = 8;
 template <class T_>
 __global__ __launch_bounds__(256) void swa_cache_fill_kernel(
     const T_* __restrict__ k, const T_* __restrict__ v, T_* __restrict__ kc,
     T_* __restrict__ vc, int T, int H, int D, int n_sink, int window) {
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int bh = blockIdx.x / kFillParts, part = blockIdx.x % kFillParts;
+  const int b = bh / H, h = bh % H;
   const int ns = min(n_sink, T);
   const int p_lo = max(n_sink, T - window);
   const int nw = max(0, T - p_lo);
   const int rows = ns + nw;
   constexpr int E = 16 / sizeof(T_);  // elements per 16-byte piece
   const int ppr = D / E;              // pieces per row
-  for (int c = threadIdx.x; c < rows * ppr; c += blockDim.x) {
+  for (int c = part * blockDim.x + threadIdx.x; c < rows * ppr; c += kFillParts * blockDim.x) {
     const int row = c / ppr, e = (c % ppr) * E;
     const int p = row < ns ? row : p_lo + (row - ns);
     const int slot = p < n_sink ? p : n_sink + (p - n_sink) % window;
@@ -292,7 +297,7 @@ hipError_t launch_swa_prefill(const SwaPrefillArgs& p) {
 
 hipError_t launch_swa_cache_fill(const SwaCacheFillArgs& p) {
   if ((long long)p.B * p.H * p.T == 0) return hipSuccess;
-  const dim3 grid(p.B * p.H), block(256);
+  const dim3 grid(p.B * p.H * kFillParts), block(256);
   const hipStream_t st = (hipStream_t)p.stream;
   if (p.bf16)
     hipLaunchKernelGGL(swa_cache_fill_kernel<bf16>, grid, block, 0, st, (const bf16*)p.k,
