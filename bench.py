@@ -178,8 +178,8 @@ COUNTERS = {
     # mean of the three launches of the counter run (same inputs)
     "swa_sink_prefill_kernel<bf16>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa_prefill.hip",
-        sha1="574a282283f29c6e63b6756b722bf61d901a095e",
-        fetch_kib=(254812 + 254878 + 255096) / 3, write_kib=(131860 + 132186 + 132122) / 3,
+        sha1="37b818d402e8140a9ccfde193dc53fe2b22252c0",
+        fetch_kib=(254970 + 254725 + 254841) / 3, write_kib=(131901 + 132097 + 131943) / 3,
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
