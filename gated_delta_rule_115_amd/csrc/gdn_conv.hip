@@ -55,16 +55,6 @@ __device__ __forceinline__ Raw8<TIn> load_raw8(const TIn* p) {
   return r;
 }
 template <class TIn>
-__device__ __forceinline__ void zero_raw8(Raw8<TIn>& r) {
-  if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.v[e] = (bf16)0.f;
-  } else {
-    r.a = zero4();
-    r.b = zero4();
-  }
-}
-template <class TIn>
 __device__ __forceinline__ float raw8_at(const Raw8<TIn>& r, int e) {
   if constexpr (sizeof(TIn) == 2) {
     return (float)r.v[e];
@@ -196,34 +186,32 @@ static hipError_t launch_conv_k(const ConvArgs& p) {
 // (oldest row first), which is then shifted by one row with the new token
 // appended.  A thread owns 8 channels of one sequence: it reads the token and
 // its history rows, writes y and the shifted history (every thread reads its
-// own channels before writing them, so the update is in place).  L2 groups
-// are consecutive lanes of one wave (a group's channels are consecutive and
-// groups do not straddle sequences).
+// own channels before writing them, so the update is in place).  The
+// work-groups of a sequence are consecutive (no per-thread division), and
+// every load is unconditional (lanes past the last channel vector read the
+// last one and store nothing), so all of a thread's loads are in flight
+// together.  L2 groups are consecutive lanes of one wave (a group's channels
+// are consecutive, and a work-group's 128 vectors start at a multiple of 128).
 template <class TIn, class TOut, int K>
 __global__ __launch_bounds__(kConvThreads) void short_conv_step_kernel(
     const TIn* __restrict__ x, const float* __restrict__ taps, TIn* __restrict__ state,
     TOut* __restrict__ y, int B, int Ch, int group, float eps) {
   const int nvec = Ch / 8;
-  const long long gi = (long long)blockIdx.x * kConvThreads + threadIdx.x;
-  const bool active = gi < (long long)B * nvec;
-  const int b = active ? (int)(gi / nvec) : 0;
-  const int c0 = (active ? (int)(gi % nvec) : 0) * 8;
+  const int nblk = (nvec + kConvThreads - 1) / kConvThreads;  // work-groups per sequence
+  const int b = blockIdx.x / nblk;
+  const int vi = (blockIdx.x - b * nblk) * kConvThreads + threadIdx.x;
+  const bool active = vi < nvec;
+  const int c0 = min(vi, nvec - 1) * 8;
   float w[8][K];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int j = 0; j < K; ++j) w[e][j] = active ? taps[(size_t)(c0 + e) * K + j] : 0.f;
+    for (int j = 0; j < K; ++j) w[e][j] = taps[(size_t)(c0 + e) * K + j];
   Raw8<TIn> rows[K];  // history rows 0 .. K - 2, then the new token
   TIn* sb = state + (size_t)b * (K - 1) * Ch + c0;
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    if (!active)
-      zero_raw8(rows[j]);
-    else if (j < K - 1)
-      rows[j] = load_raw8(sb + (size_t)j * Ch);
-    else
-      rows[j] = load_raw8(x + (size_t)b * Ch + c0);
-  }
+  for (int j = 0; j < K; ++j)
+    rows[j] = load_raw8(j < K - 1 ? sb + (size_t)j * Ch : x + (size_t)b * Ch + c0);
   float o[8], ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -235,6 +223,7 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_step_kernel(
   }
   const int gl = group / 8;
   if (gl > 0) {
+    if (!active) ss = 0.f;
     for (int m = 1; m < gl; m <<= 1) ss += __shfl_xor(ss, m);
     const float inv = __builtin_amdgcn_rcpf(sqrtf(ss) + eps);
 #pragma unroll
@@ -253,9 +242,8 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_step_kernel(
 
 template <class TIn, class TOut, int K>
 static hipError_t launch_conv_step_t(const ConvArgs& p, void* state) {
-  const long long n = (long long)p.B * (p.Ch / 8);
-  hipLaunchKernelGGL((short_conv_step_kernel<TIn, TOut, K>),
-                     dim3((unsigned)((n + kConvThreads - 1) / kConvThreads)), dim3(kConvThreads), 0,
+  const long long n = (long long)p.B * ((p.Ch / 8 + kConvThreads - 1) / kConvThreads);
+  hipLaunchKernelGGL((short_conv_step_kernel<TIn, TOut, K>), dim3((unsigned)n), dim3(kConvThreads), 0,
                      (hipStream_t)p.stream, (const TIn*)p.x, p.taps, (TIn*)state, (TOut*)p.y, p.B,
                      p.Ch, p.group, p.eps);
   return hipGetLastError();
