@@ -77,29 +77,27 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_silu_kernel(
   const int b = blockIdx.z;
   const int tb = blockIdx.y * kConvRun;
   const int te = min(T, tb + kConvRun);
-  const int c0 = (active ? vi : 0) * 8;
+  const int c0 = (active ? vi : nvec - 1) * 8;
   const TIn* xb = x + (size_t)b * T * Ch + c0;
   TOut* yb = y + (size_t)b * T * Ch + c0;
 
+  // Taps and history loads are unconditional (an inactive thread reads the
+  // last channel vector; rows before the sequence read row 0 and are zeroed
+  // after the load), so they are all in flight together.
   float w[8][K];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int j = 0; j < K; ++j) w[e][j] = active ? taps[(size_t)(c0 + e) * K + j] : 0.f;
+    for (int j = 0; j < K; ++j) w[e][j] = taps[(size_t)(c0 + e) * K + j];
 
   // History rows x_{t-K+1} .. x_{t-1} (oldest first).
   float hist[K > 1 ? K - 1 : 1][8];
 #pragma unroll
   for (int j = 0; j < K - 1; ++j) {
     const int ts = tb - (K - 1) + j;
-    if (active && ts >= 0) {
-      const Raw8<TIn> r = load_raw8(xb + (size_t)ts * Ch);
+    const Raw8<TIn> r = load_raw8(xb + (size_t)max(ts, 0) * Ch);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hist[j][e] = raw8_at(r, e);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hist[j][e] = 0.f;
-    }
+    for (int e = 0; e < 8; ++e) hist[j][e] = ts >= 0 ? raw8_at(r, e) : 0.f;
   }
 
   const int gl = group / 8;  // lanes per L2 group (0 = no normalisation)
