@@ -328,14 +328,28 @@ struct TileRegs {
       *reinterpret_cast<vec*>(dst + r * ld + cv * VN) = x[u];
     }
   }
-  __device__ __forceinline__ void store_f32(float* dst, int ld) const {
+  // Unconditional loads (rows past T read row T - 1; store_f32_rows zeroes
+  // them): with no load under a branch the compiler does not wait for the
+  // loads at the branch's end, so they stay in flight.
+  __device__ __forceinline__ void issue_clamped(const TIn* src, int b, int t0, int h, int T,
+                                                int H) {
 #pragma unroll
     for (int u = 0; u < KV; ++u) {
       const int i = threadIdx.x + 512 * u, r = i / (D / VN), cv = i % (D / VN);
+      x[u] = *reinterpret_cast<const vec*>(src + tok_off(b, min(t0 + r, T - 1), h, T, H) + cv * VN);
+    }
+  }
+  __device__ __forceinline__ void store_f32_rows(float* dst, int ld, int t0, int T) const {
+#pragma unroll
+    for (int u = 0; u < KV; ++u) {
+      const int i = threadIdx.x + 512 * u, r = i / (D / VN), cv = i % (D / VN);
+      const bool in = t0 + r < T;
 #pragma unroll
       for (int e = 0; e < VN; e += 4)
         *reinterpret_cast<f32x4*>(dst + r * ld + cv * VN + e) =
-            f32x4{to_f32(x[u][e]), to_f32(x[u][e + 1]), to_f32(x[u][e + 2]), to_f32(x[u][e + 3])};
+            in ? f32x4{to_f32(x[u][e]), to_f32(x[u][e + 1]), to_f32(x[u][e + 2]),
+                       to_f32(x[u][e + 3])}
+               : zero4();
     }
   }
 };
@@ -742,16 +756,16 @@ __device__ __forceinline__ void pass_issue(PassRegs& pr, const Ws& ws, size_t ch
     pr.x[2 + u] = *reinterpret_cast<const f32x4*>(dS + r * D + c4 * 4);
   }
   const int r = tid >> 3, c4 = tid & 7;
-  pr.x[4] = zero4();
-  if (t0 + r < T)
-    pr.x[4] = *reinterpret_cast<const f32x4*>(dout + tok_off(b, t0 + r, h, T, H) + c0 + c4 * 4);
+  // (unconditional: rows past T read row T - 1 and are zeroed in pass_store)
+  pr.x[4] = *reinterpret_cast<const f32x4*>(dout + tok_off(b, min(t0 + r, T - 1), h, T, H) + c0 +
+                                            c4 * 4);
   const size_t o = ch * C * D + r * D + c0 + c4 * 4;
   pr.x[5] = *reinterpret_cast<const f32x4*>(ws.dY + o);
   pr.x[6] = *reinterpret_cast<const f32x4*>(ws.U + o);
   pr.x[7] = *reinterpret_cast<const f32x4*>(ws.Vm + o);
   pr.x[8] = *reinterpret_cast<const f32x4*>(ws.dU + o);
 }
-__device__ __forceinline__ void pass_store(const PassRegs& pr, GradV& sv) {
+__device__ __forceinline__ void pass_store(const PassRegs& pr, GradV& sv, int t0, int T) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -760,7 +774,7 @@ __device__ __forceinline__ void pass_store(const PassRegs& pr, GradV& sv) {
     *reinterpret_cast<f32x4*>(sv.dS + r * LV + c4 * 4) = pr.x[2 + u];
   }
   const int o = (tid >> 3) * LV + (tid & 7) * 4;
-  *reinterpret_cast<f32x4*>(sv.dO + o) = pr.x[4];
+  *reinterpret_cast<f32x4*>(sv.dO + o) = t0 + (tid >> 3) < T ? pr.x[4] : zero4();
   *reinterpret_cast<f32x4*>(sv.dY + o) = pr.x[5];
   *reinterpret_cast<f32x4*>(sv.U + o) = pr.x[6];
   *reinterpret_cast<f32x4*>(sv.Vm + o) = pr.x[7];
@@ -809,7 +823,7 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
   PassRegs pr;
   TileRegs<TIn> kx, qx;  // K and Q of the chunk, loaded during the last pass
   RecRegs tx;            // Tm, likewise
-  float pv[2][4], gv[2][4];  // P and K K^T on this wave's dA / dP tiles, likewise
+  float pv[2][4], gv[2][4];
   pass_issue(pr, ws, ch, dout, b, t0, h, T, H, 0);
   __syncthreads();  // gates in LDS
   // Per-row factors of this wave's A fragments (token rows 16 (tr0 + t) + l % 16).
@@ -824,23 +838,14 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
   }
   for (int pass = 0; pass < D / QV; ++pass) {
     if (pass) __syncthreads();  // the previous pass's readers are done
-    pass_store(pr, sv);
+    pass_store(pr, sv, t0, T);
     __syncthreads();
     if (pass + 1 < D / QV) {
       pass_issue(pr, ws, ch, dout, b, t0, h, T, H, (pass + 1) * QV);
     } else {
-      kx.issue(k, b, t0, h, T, H);
-      qx.issue(q, b, t0, h, T, H);
+      kx.issue_clamped(k, b, t0, h, T, H);
+      qx.issue_clamped(q, b, t0, h, T, H);
       tx.issue(rec);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int y = w + 8 * (t < nP ? t : 0);
-          const int o = (16 * low_rt(y) + 4 * (l >> 4) + i) * C + 16 * low_ct(y) + (l & 15);
-          pv[t][i] = rec[C * C + o];
-          gv[t][i] = rec[2 * C * C + o];
-        }
     }
 
     // dY . Vm per row (thread: row tid / 8, 4 columns) and <dSn, S>.
@@ -904,9 +909,19 @@ __global__ __launch_bounds__(512) void bwdc_grad_kernel(
   __syncthreads();  // value passes done: the LDS becomes the key-side tiles
   if ((tid & 7) == 0) dbY[tid >> 3] = dbY_acc;
 
-  kx.store_f32(sk.K, LKF);
-  qx.store_f32(sk.Q, LKF);
+  kx.store_f32_rows(sk.K, LKF, t0, T);
+  qx.store_f32_rows(sk.Q, LKF, t0, T);
   tx.store(sk.Tm);
+  // P and K K^T on this wave's dA / dP tiles (used at the dA stage below).
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int y = w + 8 * (t < nP ? t : 0);
+      const int o = (16 * low_rt(y) + 4 * (l >> 4) + i) * C + 16 * low_ct(y) + (l & 15);
+      pv[t][i] = rec[C * C + o];
+      gv[t][i] = rec[2 * C * C + o];
+    }
   // dTm, strictly lower part (the only part that reaches dA); zeros above.
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
