@@ -160,46 +160,46 @@ COUNTERS = {
     PREFILL_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
         sha1="7d272a8c4a3e61df3fc2b8b4e2b998427123eb32",
-        fetch_kib=248678 + 15389 + 371487, write_kib=55318 + 14336 + 239616,
+        fetch_kib=248642 + 15389 + 371797, write_kib=55305 + 14336 + 239618,
         profile=PROFILE),
     PREFILL_CONV_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_prefill_head.hip",
         sha1="7d272a8c4a3e61df3fc2b8b4e2b998427123eb32",
-        fetch_kib=318844 + 12834 + 424178, write_kib=102722 + 10240 + 258828,
+        fetch_kib=318663 + 12834 + 423939, write_kib=102722 + 10240 + 258828,
         profile=PROFILE),
     "decode_step_kernel<bf16,bf16,128,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_decode.hip",
         sha1="d0e70d0a01d4633fac0a955eda54f3bd69f01b62",
-        fetch_kib=265757, write_kib=526665, profile=PROFILE),
+        fetch_kib=265758, write_kib=526637, profile=PROFILE),
     "swa_sink_decode_kernel<bf16,bf16,128>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa.hip",
         sha1="afa1a0eccd2a4fdf0d91fdc379ee91e97784c24f",
-        fetch_kib=1061936, write_kib=6144, profile=PROFILE),
+        fetch_kib=1062046, write_kib=6144, profile=PROFILE),
     # mean of the three launches of the counter run (same inputs)
     "swa_sink_prefill_kernel<bf16>": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_swa_prefill.hip",
         sha1="37b818d402e8140a9ccfde193dc53fe2b22252c0",
-        fetch_kib=(254970 + 254725 + 254841) / 3, write_kib=(131901 + 132097 + 131943) / 3,
+        fetch_kib=(254840 + 254984 + 255142) / 3, write_kib=(132055 + 132042 + 132151) / 3,
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
         sha1="d919a99ca61702a2b04a8647f6725c5fd6fcad7c",
-        fetch_kib=264783 + 394320, write_kib=395285 + 139264, profile=PROFILE),
+        fetch_kib=264738 + 394320, write_kib=395290 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd_chunk.hip",
-        sha1="76eb7eb3a498a8418a2184466bde8005362ddcf4",
-        fetch_kib=33369 + 51538 + 100697 + 370193, write_kib=101661 + 262144 + 335897 + 132185,
+        sha1="bad5dce9c0ea52a578d39c2b7f9c04dd69beec37",
+        fetch_kib=33369 + 51536 + 100695 + 370170, write_kib=101575 + 262145 + 335881 + 132178,
         profile=PROFILE),
     # the three projections of the leg together
     "short_conv_silu_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
-        sha1="92b6d24215239cccaa8a33d420f5e803ae0fe4a5",
-        fetch_kib=168112 + 168107 + 168109, write_kib=327681 + 327681 + 327687, profile=PROFILE),
+        sha1="26dcd19fe2422c955fb54847fe44d26b1569afa6",
+        fetch_kib=168102 + 168094 + 168099, write_kib=327682 + 327680 + 327702, profile=PROFILE),
     # the three projections' decode-time steps together
     "short_conv_step_kernel<bf16,bf16,4> (x3)": dict(
         src="gated_delta_rule_115_amd/csrc/gdn_conv.hip",
-        sha1="92b6d24215239cccaa8a33d420f5e803ae0fe4a5",
-        fetch_kib=5479 + 5478 + 5476, write_kib=10240 + 10240 + 10240, profile=PROFILE),
+        sha1="26dcd19fe2422c955fb54847fe44d26b1569afa6",
+        fetch_kib=5460 + 5460 + 5460, write_kib=10240 + 10240 + 10240, profile=PROFILE),
 }
 READ_FACTOR, WRITE_FACTOR = 2.00, 1.00
 
