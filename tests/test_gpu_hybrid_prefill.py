@@ -116,6 +116,26 @@ def test_hybrid_prefill_matches_oracle(B, T, H, s, w):
     assert bool(((ob - o).abs() <= bound).all())
 
 
+@pytest.mark.parametrize("T,s,w", [(300, 4, 64), (40, 4, 64), (66, 4, 64), (1000, 4, 512),
+                                   (1000, 0, 100), (129, 70, 30)])
+def test_hybrid_prefill_fills_caches_as_cache_fill(T, s, w):
+    """The hybrid call's decode caches equal gdn_swa_cache_fill's on the same
+    keys and values, bit for bit, and slots the sequence does not reach keep
+    their contents: short sequences (T < window, T < n_sink + window), no
+    sinks, sinks spanning a 64-key block, a full window."""
+    B, H = 2, 2
+    x, sw = _hybrid_inputs(B, T, H, seed=T + w)
+    kc = dev(torch.full((B, H, s + w, D), 7.0, dtype=torch.bfloat16))
+    vc = kc.clone()
+    _run_hybrid(x, sw, s, w, k_cache=kc, v_cache=vc)
+    rk = dev(torch.full((B, H, s + w, D), 7.0, dtype=torch.bfloat16))
+    rv = rk.clone()
+    gdn.gdn_swa_cache_fill(dev(sw[1]), dev(sw[2]), rk, rv, n_sink=s, window=w)
+    torch.cuda.synchronize()
+    say(f"cache fill T={T} n_sink={s} window={w}")
+    assert torch.equal(kc.cpu(), rk.cpu()) and torch.equal(vc.cpu(), rv.cpu())
+
+
 def test_hybrid_prefill_then_decode_step():
     """Prefill T tokens (state + decode caches), then one hybrid decode step
     for token T: equals the oracle's layer output at position T."""
