@@ -48,7 +48,9 @@ constexpr int kPrepGrid = 512;  // persistent per-chunk work-groups: two per CU
 constexpr float kFactorRange = 80.f;
 
 // Per-chunk record: T (C x C), Pm (C x C), beta (C), then from kGamOff the
-// cumulative log gates Gam (C x Dk, room for Dk = 128), all f32.
+// cumulative log gates Gam (C x Dk, room for Dk = 128), all f32; for the
+// tiled recurrence (which takes f16 operands) T and Pm are f16, T at byte 0
+// and Pm at byte 2 C^2, each rounded once from the f32 value.
 constexpr size_t kRecFloats = 2 * GC * GC + GC;
 constexpr size_t kGamOff = (kRecFloats * 4 + 255) / 256 * 256;  // bytes
 constexpr size_t kRecBytes = kGamOff + (size_t)GC * 128 * 4;
@@ -99,142 +101,216 @@ struct ChunkRegs {
   f32x4 g[NKQ][2], gl[NKQ][2], rec[NR];
 };
 
+// Four consecutive elements as loaded (bf16: one 8-byte load; f32: one
+// 16-byte load).
+template <class TIn>
+struct Raw4 {
+  bf16x4 v;
+};
+template <>
+struct Raw4<float> {
+  f32x4 v;
+};
+template <class TIn>
+__device__ __forceinline__ Raw4<TIn> ld4(const TIn* p) {
+  Raw4<TIn> r;
+  r.v = *reinterpret_cast<const decltype(r.v)*>(p);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
 // Kernel 1: a persistent grid; work-group w takes chunks (b, h, c) with
-// index w, w + gridDim.x, ... and loads the next one's q, k, alpha, beta into
-// registers while the current one is computed (barriers order LDS only, so
-// those loads stay in flight).
-template <class TIn, int DK, bool KG>
+// index w, w + gridDim.x, ...  Thread (grp, cq) owns channels 4 cq .. 4 cq + 3
+// of rows grp * RPG .. grp * RPG + RPG - 1 of the chunk: it holds their q, k,
+// alpha and beta in registers (loaded while the previous chunk is computed),
+// forms the cumulative log gates of its piece from one exchange of per-group
+// totals through LDS, writes its rows of Gam to the record, and writes the
+// gate-factored operands of the Gram blocks to LDS once.
+template <class TIn, int DK, bool KG, bool H16>
 __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, int T, int H, int NC, float scale, char* __restrict__ ws,
     int total) {
-  __shared__ float Ks[GC][DK + 1], Qs[GC][DK + 1], Gs[GC][DK + 1], Ki[GC][DK + 1];
-  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], bet[GC], rng[DK];
+  constexpr int NQ = DK / 4;    // channel quads per row
+  constexpr int NG = GNT / NQ;  // row groups
+  constexpr int RPG = GC / NG;  // rows per thread
+  // Row stride (floats) of the operand tiles: 4 mod 64 words, so the 16
+  // rows of an MFMA operand's 16-byte reads fall in distinct banks.
+  constexpr int LP = DK + 4;
+  static_assert(RPG >= 1 && NG * RPG == GC, "row groups must tile the chunk");
+  static_assert(GNT * 4 == GC * GC, "one 4-entry piece of T and Pm per thread");
+  __shared__ __align__(16) float Kg[GC * LP], Qg[GC * LP], Ki[GC * LP];
+  __shared__ __align__(16) float tot[NG * DK], g0s[DK];
+  __shared__ float As[GC][GC + 1], Ts[GC][GC + 1], Ps[GC][GC + 1], bet[GC], wmx[GNT / 64],
+      wrg[GNT / 64];
   __shared__ __align__(16) float Iv[2][f16ops::kInvScratch];
   const int tid = threadIdx.x;
-  typedef ChunkRegs<TIn, DK, GNT> R;
-  Raw8<TIn> kr[R::NKQ], qr[R::NKQ];
-  f32x4 ar[R::NA];
-  float br = 0.f;
-  const size_t tok = (size_t)H * DK;
+  const int cq = tid % NQ, grp = tid / NQ;
+  Raw4<TIn> kr[RPG], qr[RPG];
+  f32x4 ar[RPG];
+  float br[RPG];
   auto fetch = [&](int id) {
     const int c = id % NC, bh = id / NC, b = bh / H, h = bh % H;
-    const int t0 = c * GC;
 #pragma unroll
-    for (int u = 0; u < R::NKQ; ++u) {
-      const int pc = tid + GNT * u;
-      const int r = min(pc / (DK / 8), GC - 1), t = min(t0 + r, T - 1);
-      const size_t off = ((size_t)b * T + t) * tok + (size_t)h * DK + 8 * (pc % (DK / 8));
-      kr[u] = ld8(k + off);
-      qr[u] = ld8(q + off);
+    for (int i = 0; i < RPG; ++i) {
+      const size_t row = (size_t)b * T + min(c * GC + grp * RPG + i, T - 1);
+      const size_t off = (row * H + h) * DK + 4 * cq;
+      kr[i] = ld4(k + off);
+      qr[i] = ld4(q + off);
+      ar[i] = *reinterpret_cast<const f32x4*>(alpha + off);
+      br[i] = beta[row * H + h];
     }
-#pragma unroll
-    for (int u = 0; u < R::NA; ++u) {
-      const int pc = tid + GNT * u;
-      const int r = min(pc / (DK / 4), GC - 1), t = min(t0 + r, T - 1);
-      ar[u] = *reinterpret_cast<const f32x4*>(alpha + ((size_t)b * T + t) * tok +
-                                              (size_t)h * DK + 4 * (pc % (DK / 4)));
-    }
-    if (tid < GC) br = beta[((size_t)b * T + min(t0 + tid, T - 1)) * H + h];
   };
 
   if ((int)blockIdx.x < total) fetch(blockIdx.x);
   for (int id = blockIdx.x; id < total; id += gridDim.x) {
-    const int c = id % NC;
-    const int t0 = c * GC;
-    f16ops::lds_barrier();  // the previous chunk is done with every LDS buffer
+    const int t0 = (id % NC) * GC;
+    // This thread's piece; rows past T are identity tokens (k = q = 0,
+    // alpha = 1, beta = 0).  g: cumulative log gate within the piece; mx:
+    // the largest per-token log-gate decrease of the piece.
+    float kv[RPG][4], qv[RPG][4], g[RPG][4], bv[RPG];
+    float mx = 0.f;
 #pragma unroll
-    for (int u = 0; u < R::NKQ; ++u) {
-      const int pc = tid + GNT * u;
-      if (pc < GC * DK / 8) {
-        const int r = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
-        st8(&Ks[r][c8], kr[u], t0 + r < T);
-        st8(&Qs[r][c8], qr[u], t0 + r < T);
+    for (int i = 0; i < RPG; ++i) {
+      const bool ok = t0 + grp * RPG + i < T;
+      bv[i] = ok ? br[i] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv[i][e] = ok ? (float)kr[i].v[e] : 0.f;
+        qv[i][e] = ok ? (float)qr[i].v[e] : 0.f;
+        // (The log of the clamped row's alpha is taken either way, so the
+        // select stays branch-free.)
+        const float la = __logf(ar[i][e]);
+        float lgt = ok ? la : 0.f;
+        if constexpr (KG) lgt += log1pf(-bv[i] * kv[i][e] * kv[i][e]);
+        g[i][e] = (i > 0 ? g[i - 1][e] : 0.f) + lgt;
+        mx = fmaxf(mx, -lgt);
       }
     }
-#pragma unroll
-    for (int u = 0; u < R::NA; ++u) {
-      const int pc = tid + GNT * u;
-      if (pc < GC * DK / 4) {
-        const int r = pc / (DK / 4), c4 = 4 * (pc % (DK / 4));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Gs[r][c4 + e] = t0 + r < T ? __logf(ar[u][e]) : 0.f;
-      }
-    }
-    if (tid < GC) bet[tid] = t0 + tid < T ? br : 0.f;
     if (id + (int)gridDim.x < total) fetch(id + gridDim.x);
-    f16ops::lds_barrier();
-    // Cumulative log gate per channel, and its range over the chunk (kGLA:
-    // the gate is alpha o (1 - beta k o k); rows past T have k = beta = 0).
-    // (Each channel's 32 values are read into registers first, so the scan
-    // waits for one LDS round trip, not one per row.)
-    if (tid < DK) {
-      float g[GC];
+    mx = wave_max(mx);
+    f16ops::lds_barrier();  // the previous chunk is done with every LDS buffer
+    *reinterpret_cast<f32x4*>(&tot[grp * DK + 4 * cq]) =
+        f32x4{g[RPG - 1][0], g[RPG - 1][1], g[RPG - 1][2], g[RPG - 1][3]};
+    if (grp == 0) *reinterpret_cast<f32x4*>(&g0s[4 * cq]) = f32x4{g[0][0], g[0][1], g[0][2], g[0][3]};
+    if (cq == 0) {
 #pragma unroll
-      for (int r = 0; r < GC; ++r) {
-        g[r] = Gs[r][tid];
-        if constexpr (KG) g[r] += log1pf(-bet[r] * Ks[r][tid] * Ks[r][tid]);
-      }
-#pragma unroll
-      for (int r = 1; r < GC; ++r) g[r] += g[r - 1];
-#pragma unroll
-      for (int r = 0; r < GC; ++r) Gs[r][tid] = g[r];
-      rng[tid] = g[0] - g[GC - 1];
+      for (int i = 0; i < RPG; ++i) bet[grp * RPG + i] = bv[i];
     }
+    if ((tid & 63) == 0) wmx[tid >> 6] = mx;
     f16ops::lds_barrier();
-    {
-      float* gam = reinterpret_cast<float*>(ws + (size_t)id * kRecBytes + kGamOff);
-      for (int e = tid; e < GC * DK / 4; e += GNT) {
-        const int r = e / (DK / 4), c4 = 4 * (e % (DK / 4));
-        *reinterpret_cast<f32x4*>(gam + r * DK + c4) =
-            f32x4{Gs[r][c4], Gs[r][c4 + 1], Gs[r][c4 + 2], Gs[r][c4 + 3]};
-      }
-    }
-    // Largest range over the channels: lane l of every wave takes channels
-    // l, l + 64, ..., then a butterfly over the wave (ranges are >= 0).
-    float wide = 0.f;
-    for (int ch = tid & 63; ch < DK; ch += 64) wide = fmaxf(wide, rng[ch]);
+    // Gam of the piece = the totals of the earlier groups + g; Gam of the
+    // chunk's last row = the sum of all totals (summed in group order by
+    // every thread, so all threads of a channel agree bit for bit).
+    f32x4 pre = zero4(), all = zero4();
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) wide = fmaxf(wide, __shfl_xor(wide, m));
-
+    for (int gg = 0; gg < NG; ++gg) {
+      const f32x4 tv = *reinterpret_cast<const f32x4*>(&tot[gg * DK + 4 * cq]);
+      if (gg < grp) pre += tv;
+      all += tv;
+    }
+    const f32x4 gz = *reinterpret_cast<const f32x4*>(&g0s[4 * cq]);
     float* rec = reinterpret_cast<float*>(ws + (size_t)id * kRecBytes);
-    float* Tg = rec;
-    float* Pg = rec + GC * GC;
     float* Bg = rec + 2 * GC * GC;
-    if (wide <= kFactorRange) {
+    float* gam = reinterpret_cast<float*>(ws + (size_t)id * kRecBytes + kGamOff);
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[i][e] += pre[e];
+      *reinterpret_cast<f32x4*>(gam + (grp * RPG + i) * DK + 4 * cq) =
+          f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
+    }
+    // The chunk's largest per-channel log-gate range Gam_0 - Gam_last is at
+    // most (GC - 1) times the largest per-token decrease; only when that
+    // bound exceeds kFactorRange is the range itself taken (one more
+    // exchange).
+    float mm = wmx[0];
+#pragma unroll
+    for (int w = 1; w < GNT / 64; ++w) mm = fmaxf(mm, wmx[w]);
+    bool wide = false;
+    if ((GC - 1) * mm > kFactorRange) {
+      float rr = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rr = fmaxf(rr, gz[e] - all[e]);
+      rr = wave_max(rr);
+      if ((tid & 63) == 0) wrg[tid >> 6] = rr;
+      f16ops::lds_barrier();
+#pragma unroll
+      for (int w = 0; w < GNT / 64; ++w) wide = wide || wrg[w] > kFactorRange;
+    }
+    if (!wide) {
       // Gate factors about the chunk's per-channel midpoint Gam_m: with
       // Kg = K o e^(Gam - Gam_m), Ki = K o e^(Gam_m - Gam), Qg = Q o e^(Gam -
-      // Gam_m) every factor is at most e^(range / 2), and A = lower(Kg Ki^T),
-      // Pm = lower(Qg Ki^T) are two f32 MFMA products (each wave one 16 x 16
-      // tile of both).  Entries above the diagonal may overflow; they are not
-      // used.
-      for (int e = tid; e < GC * DK; e += GNT) {
-        const int r = e / DK, ch = e % DK;
-        const float gm = 0.5f * (Gs[0][ch] + Gs[GC - 1][ch]);
-        const float f = __expf(Gs[r][ch] - gm);
-        Ki[r][ch] = Ks[r][ch] * __expf(gm - Gs[r][ch]);
-        Ks[r][ch] *= f;
-        Qs[r][ch] *= f;
+      // Gam_m) every factor is at most e^(range / 2).
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        f32x4 fk, fq, fi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gm = 0.5f * (gz[e] + all[e]);
+          const float f = __expf(g[i][e] - gm);
+          fi[e] = kv[i][e] * __expf(gm - g[i][e]);
+          fk[e] = kv[i][e] * f;
+          fq[e] = qv[i][e] * f;
+        }
+        const int o = (grp * RPG + i) * LP + 4 * cq;
+        *reinterpret_cast<f32x4*>(&Kg[o]) = fk;
+        *reinterpret_cast<f32x4*>(&Qg[o]) = fq;
+        *reinterpret_cast<f32x4*>(&Ki[o]) = fi;
       }
-      f16ops::lds_barrier();
+    } else {
+      // Wide chunk: K, Q and Gam themselves (Gam in the Ki buffer).
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const int o = (grp * RPG + i) * LP + 4 * cq;
+        *reinterpret_cast<f32x4*>(&Kg[o]) = f32x4{kv[i][0], kv[i][1], kv[i][2], kv[i][3]};
+        *reinterpret_cast<f32x4*>(&Qg[o]) = f32x4{qv[i][0], qv[i][1], qv[i][2], qv[i][3]};
+        *reinterpret_cast<f32x4*>(&Ki[o]) = f32x4{g[i][0], g[i][1], g[i][2], g[i][3]};
+      }
+    }
+    f16ops::lds_barrier();
+    if (!wide) {
+      // A = lower(Kg Ki^T), Pm = lower(Qg Ki^T) on f32 MFMA: wave (tr, tc)
+      // forms 16 x 16 tile (tr, tc) of both; tile (0, 1) lies above the
+      // diagonal and is zero.  Lane (lg, lr) reads 4 consecutive channels
+      // of its row of each operand per 16-channel block and feeds them to 4
+      // MFMAs (the same channel order on both operands).  Entries above the
+      // diagonal may overflow; they are not used.
       const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
       const int tr = w >> 1, tc = w & 1;
-      f32x4 a0 = zero4(), a1 = zero4(), p0 = zero4(), p1 = zero4();
+      if (tr >= tc) {
+        f32x4 a0 = zero4(), a1 = zero4(), p0 = zero4(), p1 = zero4();
 #pragma unroll 4
-      for (int kk = 0; kk < DK; kk += 8) {
-        const float ki0 = Ki[16 * tc + lr][kk + lg], ki1 = Ki[16 * tc + lr][kk + 4 + lg];
-        if constexpr (!KG) {
-          a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[16 * tr + lr][kk + lg], ki0, a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[16 * tr + lr][kk + 4 + lg], ki1, a1, 0, 0, 0);
+        for (int kb = 0; kb < DK / 16; ++kb) {
+          const int oa = (16 * tr + lr) * LP + 16 * kb + 4 * lg;
+          const f32x4 ki = *reinterpret_cast<const f32x4*>(&Ki[(16 * tc + lr) * LP + 16 * kb + 4 * lg]);
+          const f32x4 qg = *reinterpret_cast<const f32x4*>(&Qg[oa]);
+          if constexpr (!KG) {
+            const f32x4 kg = *reinterpret_cast<const f32x4*>(&Kg[oa]);
+            a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kg[0], ki[0], a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kg[1], ki[1], a1, 0, 0, 0);
+            a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kg[2], ki[2], a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kg[3], ki[3], a1, 0, 0, 0);
+          }
+          p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qg[0], ki[0], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qg[1], ki[1], p1, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qg[2], ki[2], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qg[3], ki[3], p1, 0, 0, 0);
         }
-        p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[16 * tr + lr][kk + lg], ki0, p0, 0, 0, 0);
-        p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[16 * tr + lr][kk + 4 + lg], ki1, p1, 0, 0, 0);
-      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * tr + 4 * lg + j, i = 16 * tc + lr;
-        if constexpr (!KG) As[r][i] = (i < r) ? bet[r] * (a0[j] + a1[j]) : 0.f;
-        Pg[r * GC + i] = (i <= r) ? scale * (p0[j] + p1[j]) : 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * tr + 4 * lg + j, i = 16 * tc + lr;
+          if constexpr (!KG) As[r][i] = (i < r) ? bet[r] * (a0[j] + a1[j]) : 0.f;
+          Ps[r][i] = (i <= r) ? scale * (p0[j] + p1[j]) : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Ps[4 * lg + j][16 + lr] = 0.f;
       }
     } else {
       // Wide chunk: exact per-channel gate ratios, pairs (r, i), i <= r.
@@ -243,17 +319,28 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
         float a = 0.f, p = 0.f;
         if (i <= r) {
           for (int ch = 0; ch < DK; ++ch) {
-            const float e = __expf(Gs[r][ch] - Gs[i][ch]);
-            const float ki = Ks[i][ch] * e;
-            a += Ks[r][ch] * ki;
-            p += Qs[r][ch] * ki;
+            const float e = __expf(Ki[r * LP + ch] - Ki[i * LP + ch]);
+            const float kie = Kg[i * LP + ch] * e;
+            a += Kg[r * LP + ch] * kie;
+            p += Qg[r * LP + ch] * kie;
           }
         }
         if constexpr (!KG) As[r][i] = (i < r) ? bet[r] * a : 0.f;
-        Pg[r * GC + i] = (i <= r) ? scale * p : 0.f;
+        Ps[r][i] = (i <= r) ? scale * p : 0.f;
       }
     }
     f16ops::lds_barrier();
+    // T and Pm go to the record as one 4-entry piece of a row per thread.
+    const int wr = tid >> 3, wc = 4 * (tid & 7);
+    auto put_tile = [&](const float (*S)[GC + 1], int slot) {
+      const f32x4 x = {S[wr][wc], S[wr][wc + 1], S[wr][wc + 2], S[wr][wc + 3]};
+      if constexpr (H16)
+        *reinterpret_cast<f16ops::h16x4*>(reinterpret_cast<f16ops::h16*>(rec) + slot * GC * GC +
+                                          wr * GC + wc) = f16ops::cvt4(x);
+      else
+        *reinterpret_cast<f32x4*>(rec + slot * GC * GC + wr * GC + wc) = x;
+    };
+    put_tile(Ps, 1);
     if constexpr (KG) {  // no erase: T = I is implied, the recurrence uses U = V
       if (tid < GC) Bg[tid] = bet[tid];
       continue;
@@ -279,7 +366,7 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
       }
       f16ops::lds_barrier();
       if (w == 2) {
-        float* Xs = &Qs[0][0];  // X = A10 T00, [row][column], row stride GC + 1
+        float* Xs = Qg;  // X = A10 T00, [row][column], row stride GC + 1
         f32x4 X = zero4();
 #pragma unroll
         for (int kk = 0; kk < 16; kk += 4)
@@ -296,7 +383,7 @@ __global__ __launch_bounds__(GNT) void chgate_prep_kernel(
       }
       f16ops::lds_barrier();
     }
-    for (int e = tid; e < GC * GC; e += GNT) Tg[e] = Ts[e / GC][e % GC];
+    put_tile(Ts, 0);
     if (tid < GC) Bg[tid] = bet[tid];
   }
 }
@@ -531,10 +618,10 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
 }
 
 // Kernel 2 for bf16 inputs, Dk = Dv = 128, chgate (not kGLA): one
-// work-group of 12 waves per (b, h) walks its chunks with S in MFMA
+// work-group of 16 waves per (b, h) walks its chunks with S in MFMA
 // accumulator tiles.  Waves 0-7 each own 16 value columns of S (f32, all 128
 // keys: 8 tiles, key order kap below, so two stacked tiles form the B operand
-// of K S directly) and run the recurrence on f16 operands; waves 8-11 stream
+// of K S directly) and run the recurrence on f16 operands; waves 8-15 stream
 // the chunk's inputs and its record and write the f16 operand tiles to LDS:
 //   Kg = K o e^Gam,  Qg = Q o e^Gam,  Kd = K o e^(Gam_C - Gam)   [32 x 128]
 //   V [32 x 128], T and Pm with their columns in operand order, beta, e^Gam_C.
@@ -544,8 +631,8 @@ __global__ __launch_bounds__(GNTR) void chgate_recur_kernel(
 //   S <- diag(e^Gam_C) S + Kd^T U.
 // One work-group barrier per iteration.  The helpers' loads run two
 // iterations ahead (two register slots), as inline asm with fixed waits:
-// every iteration issues the same 14 loads per thread, so a slot's loads are
-// complete once vmcnt reaches 14.
+// every iteration issues the same 9 loads per thread, so a slot's loads are
+// complete once vmcnt reaches 9.
 namespace tile {
 
 constexpr int RS = 144;         // f16 row stride of the 128-wide tiles (288 bytes)
@@ -575,13 +662,17 @@ __device__ __forceinline__ void gld16(bf16x8& r, const void* p) {
 __device__ __forceinline__ void gld16f(f32x4& r, const void* p) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
 }
+__device__ __forceinline__ void gld8h(f16ops::h16x4& r, const void* p) {
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+}
 
 // One helper thread's loads of one chunk: K, Q and V at row pr and
 // channels pc .. pc + 7; Gam at that row and at the chunk's last row; 4
-// floats of T (threads 0-255) or of Pm (256-511), and 4 of beta.
+// f16 entries of T (threads 0-255) or of Pm (256-511), and 4 floats of beta.
 struct Loads {
   bf16x8 k, q, v;
-  f32x4 g[2], gl[2], tp, b;
+  f32x4 g[2], gl[2], b;
+  f16ops::h16x4 tp;
 };
 constexpr int kLoadsPerChunk = 3 + 2 + 2 + 1 + 1;  // 9
 
@@ -732,7 +823,8 @@ __global__ __launch_bounds__(NT) void chgate_recur_tile_kernel(
       for (int e = 0; e < 2; ++e) gld16f(x.g[e], gam + pr * DK + pc + 4 * e);
 #pragma unroll
       for (int e = 0; e < 2; ++e) gld16f(x.gl[e], gam + (GC - 1) * DK + pc + 4 * e);
-      gld16f(x.tp, rec + (ht < 256 ? 0 : GC * GC) + tr * GC + 4 * tc4);
+      gld8h(x.tp, reinterpret_cast<const f16ops::h16*>(rec) + (ht < 256 ? 0 : GC * GC) + tr * GC +
+                      4 * tc4);
       gld16f(x.b, rec + 2 * GC * GC + 4 * (ht & 7));
     };
     auto put = [&](const Loads& x, int c) {
@@ -760,7 +852,7 @@ __global__ __launch_bounds__(NT) void chgate_recur_tile_kernel(
         *reinterpret_cast<f32x4*>(&sm.gC[sl][pc]) = e0;
         *reinterpret_cast<f32x4*>(&sm.gC[sl][pc + 4]) = e1;
       }
-      *reinterpret_cast<h16x4*>((ht < 256 ? sm.Tp[sl] : sm.Pp[sl]) + tr * PRS + tslot) = cvt4(x.tp);
+      *reinterpret_cast<h16x4*>((ht < 256 ? sm.Tp[sl] : sm.Pp[sl]) + tr * PRS + tslot) = x.tp;
       if (ht < 8) *reinterpret_cast<f32x4*>(&sm.bet[sl][4 * ht]) = x.b;
     };
     Loads ld[2];
@@ -792,9 +884,15 @@ hipError_t launch_chgate_t(const PrefillArgs& p) {
   const hipStream_t st = (hipStream_t)p.stream;
   if (NC > 0) {
     const int total = p.B * p.H * NC;
-    hipLaunchKernelGGL((chgate_prep_kernel<TIn, DK, KG>), dim3(std::min(total, kPrepGrid)),
-                       dim3(GNT), 0, st, (const TIn*)p.q, (const TIn*)p.k, p.alpha, p.beta, p.T,
-                       p.H, NC, p.scale, (char*)p.workspace, total);
+    constexpr bool tiled = sizeof(TIn) == 2 && DK == 128 && !KG;
+    if (tiled && p.Dv == 128)
+      hipLaunchKernelGGL((chgate_prep_kernel<TIn, DK, KG, tiled>), dim3(std::min(total, kPrepGrid)),
+                         dim3(GNT), 0, st, (const TIn*)p.q, (const TIn*)p.k, p.alpha, p.beta, p.T,
+                         p.H, NC, p.scale, (char*)p.workspace, total);
+    else
+      hipLaunchKernelGGL((chgate_prep_kernel<TIn, DK, KG, false>), dim3(std::min(total, kPrepGrid)),
+                         dim3(GNT), 0, st, (const TIn*)p.q, (const TIn*)p.k, p.alpha, p.beta, p.T,
+                         p.H, NC, p.scale, (char*)p.workspace, total);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
