@@ -183,8 +183,8 @@ COUNTERS = {
         profile=PROFILE),
     CHGATE_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_chgate.hip",
-        sha1="d919a99ca61702a2b04a8647f6725c5fd6fcad7c",
-        fetch_kib=264738 + 394320, write_kib=395290 + 139264, profile=PROFILE),
+        sha1="c48cc347bf8361d2ce70ab62068c985f38dbf84f",
+        fetch_kib=264722 + 361550, write_kib=329728 + 139264, profile=PROFILE),
     BWD_KERNELS: dict(
         src="gated_delta_rule_115_amd/csrc/gdn_bwd_chunk.hip",
         sha1="bad5dce9c0ea52a578d39c2b7f9c04dd69beec37",
