@@ -35,6 +35,9 @@ def _ref(x, state_in=None, scale=1.0):
     ("bf16", 1, 200, 2, 128, 128, 2.0), ("f32", 1, 96, 2, 64, 64, 5.0),
     ("bf16", 2, 70, 2, 32, 32, 0.1), ("bf16", 1, 99, 2, 64, 128, 0.1),
     ("bf16", 1, 64, 2, 128, 32, 2.0),
+    # Dk = 32 (one row per thread of the per-chunk pass) with strong and very
+    # strong gates: the exact-range exchange and the per-element path
+    ("f32", 1, 70, 2, 32, 32, 2.0), ("bf16", 1, 96, 2, 32, 64, 5.0),
     # bf16, Dk = Dv = 128: the tiled recurrence (one work-group per head) --
     # one token, one chunk plus one token, very strong gates (exact path)
     ("bf16", 2, 1, 2, 128, 128, 0.1), ("bf16", 1, 33, 3, 128, 128, 0.1),

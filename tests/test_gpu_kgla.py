@@ -31,7 +31,8 @@ def _ref(x, state_in=None, scale=1.0):
     ("f32", 1, 96, 2, 128, 32, 0.1, None), ("bf16", 2, 130, 3, 128, 128, 0.1, None),
     ("bf16", 1, 1, 2, 128, 64, 0.1, None), ("f32", 2, 70, 2, 64, 64, 2.0, None),
     ("bf16", 1, 200, 2, 128, 128, 2.0, None), ("f32", 1, 96, 2, 64, 64, 5.0, None),
-    ("f32", 1, 300, 2, 128, 64, 0.1, 0.97), ("bf16", 1, 300, 2, 128, 128, 0.1, 0.9)])
+    ("f32", 1, 300, 2, 128, 64, 0.1, 0.97), ("bf16", 1, 300, 2, 128, 128, 0.1, 0.9),
+    ("f32", 1, 70, 2, 32, 32, 2.0, None), ("bf16", 1, 96, 2, 32, 64, 5.0, None)])
 def test_kgla_prefill_matches_oracle(dtype, B, T, H, Dk, Dv, gs, cos):
     say(f"kgla prefill {dtype} B{B} T{T} H{H} Dk{Dk} Dv{Dv} gate {gs} cos {cos}")
     x = synthetic.chgate_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=T + Dk + 1, state0="randn",
